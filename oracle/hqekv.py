@@ -1,0 +1,144 @@
+"""HqeKV five-tier assignment (oracle side).
+
+HqeKV notes:
+
+* section 3.2 -- key importance is the accumulated attention weight; value
+  importance multiplies it by the token's value range (max - min over the
+  channels).  Section 3.7's worked example ranks tokens by this joint product
+  and cuts the ranking by the tier shares; reading: one joint ranking per
+  token, keys and values share the tier.
+* section 3.3, Eq.(6) -- shares of FP16 / 4-bit / 2-bit / 1-bit / evicted;
+  the configuration fixes them (the TPE search that would choose them needs a
+  calibration model and dataset).
+* section 3.4 -- 4- and 2-bit use the uniform quantizer, 1-bit the normalized
+  one (``oracle.codec``).
+* section 3.5 -- every T generated tokens the cache is re-assigned, and a
+  token may only move to a lower precision (never back up).
+* section 3.8 / 3.10 -- prefill: importance from the last m = 20 prompt
+  queries, then the first assignment.
+
+Readings: granularity is per token (keys too: groups of 32 channels of one
+token); scores accumulate over every scoring query (prompt tail and all decode
+steps); at an event the tokens appended since the previous event keep full
+precision and are not ranked; share counts are floor(r_k * N) with N the
+number of tokens ever appended, cut in the order FP16, 4-bit, 2-bit, 1-bit,
+the rest evicted; a downgraded token is re-quantized from its current
+dequantized float32 values.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import attend
+from .codec import (int1_normal_dequantize, int1_normal_quantize, per_token_dequantize,
+                    per_token_quantize)
+from .numerics import FLT_MIN, bf16_to_f64
+from .rank import rank_tiers
+
+BF16, INT4, INT2, INT1, EVICT = 0, 1, 2, 3, 4
+
+
+def joint_metric(acc_attention, value_range):
+    return np.asarray(acc_attention, np.float64) * np.asarray(value_range, np.float64)
+
+
+def share_counts(ratios, n_total: int):
+    return [int(math.floor(r * n_total)) for r in ratios[:4]]
+
+
+def assign(metric, pos, eligible, counts):
+    """Target tier per token by rank of the joint metric (ties: newer first)."""
+    return rank_tiers(metric, pos, eligible, counts)
+
+
+class HqeKVGroup:
+    """HqeKV state of one (sequence, KV head): per-token tiers and contents."""
+
+    def __init__(self, k_rows, v_rows, *, G: int, ratios, period: int, group: int = 32):
+        self.korig = bf16_to_f64(k_rows)          # [T, d]
+        self.vorig = bf16_to_f64(v_rows)
+        self.T, self.d = self.korig.shape
+        self.G, self.ratios, self.period, self.group = G, tuple(ratios), period, group
+        self.kcur = self.korig.copy()
+        self.vcur = self.vorig.copy()
+        self.tier = np.full(self.T, 255, np.uint8)   # 255: not appended yet
+        self.score = np.zeros(self.T)
+        vr = self.vorig
+        self.range = vr.max(axis=1) - vr.min(axis=1)
+        self.N = 0
+        self.last_event_N = 0
+        self.codes: dict[int, tuple] = {}
+
+    def live(self):
+        return np.flatnonzero((self.tier != 255) & (self.tier != EVICT))
+
+    def _attend(self, q_bits, upto: int):
+        idx = self.live()
+        idx = idx[idx < upto]
+        q = bf16_to_f64(q_bits)
+        out, p = attend(q, self.kcur[idx][None], self.vcur[idx][None])
+        w = p.copy()
+        w[w < FLT_MIN] = 0.0
+        return out, idx, w.sum(axis=0)
+
+    def prefill(self, P: int, q_tail_bits):
+        """Prompt in full precision; the last m prompt queries (m = len of
+        q_tail_bits) are scored causally; then the first assignment."""
+        self.tier[:P] = BF16
+        self.N = P
+        m = len(q_tail_bits)
+        for i in range(m):
+            t = P - m + i
+            _, idx, w = self._attend(q_tail_bits[i], t + 1)
+            self.score[idx] += w
+        self.last_event_N = 0
+        self.event()
+
+    def step(self, s: int, t: int, q_bits):
+        self.tier[t] = BF16
+        self.N = t + 1
+        out, idx, w = self._attend(q_bits, self.N)
+        self.score[idx] += w
+        if (s + 1) % self.period == 0:
+            self.event()
+        return out, idx, w
+
+    def event(self):
+        N = self.N
+        live = self.live()
+        eligible = np.zeros(self.T, bool)
+        if self.last_event_N == 0:                 # first assignment: the whole prompt
+            eligible[live] = True
+        else:                                      # tokens appended before the previous event
+            eligible[live[live < self.last_event_N]] = True
+        metric = joint_metric(self.score, self.range)
+        target = assign(metric, np.arange(self.T), eligible, share_counts(self.ratios, N))
+        for t in np.flatnonzero(eligible):
+            new = max(int(self.tier[t]), int(target[t]))
+            if new > self.tier[t]:
+                self._requantize(t, new)
+        self.last_event_N = N
+
+    def _requantize(self, t: int, new: int):
+        if new == EVICT:
+            self.tier[t] = EVICT
+            self.codes.pop(t, None)
+            return
+        k32 = self.kcur[t].astype(np.float32)
+        v32 = self.vcur[t].astype(np.float32)
+        if new in (INT4, INT2):
+            bits = 4 if new == INT4 else 2
+            kc, ks, kz = per_token_quantize(k32, bits, self.group)
+            vc, vs, vz = per_token_quantize(v32, bits, self.group)
+            self.kcur[t] = per_token_dequantize(kc, ks, kz, self.group)
+            self.vcur[t] = per_token_dequantize(vc, vs, vz, self.group)
+            self.codes[t] = (new, kc, ks, kz, vc, vs, vz)
+        else:
+            kc, km, ksd = int1_normal_quantize(k32)
+            vc, vm, vsd = int1_normal_quantize(v32)
+            self.kcur[t] = int1_normal_dequantize(kc, km, ksd)
+            self.vcur[t] = int1_normal_dequantize(vc, vm, vsd)
+            self.codes[t] = (new, kc, km, ksd, vc, vm, vsd)
+        self.tier[t] = new

@@ -1,0 +1,248 @@
+"""The oracle pinned to what the pages and the mathematics fix (CPU only).
+
+Each test names the passage it checks.  The pins are chosen so that a
+plausible slip in the oracle -- a dropped term, a wrong sign or index, a
+transposed group axis, a wrong rounding or level count -- fails one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import budget, codec, h2o, hqekv, rank
+from oracle.attention import attend, attend_bruteforce
+from oracle.numerics import bf16_to_f64, round_to_bf16
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# H2O page, section 2.2: the capacity-6 worked step
+# ---------------------------------------------------------------------------
+
+def test_h2o_capacity6_example_scores_victim_cache():
+    g = gold("h2o_capacity6_example.json")
+    new, victim, kept = h2o.update_and_evict(g["positions"], g["scores_before"], g["weights"],
+                                             n_heavy=g["n_heavy"], n_recent=g["n_recent"],
+                                             n_sink=g["n_sink"], budget=g["budget"])
+    np.testing.assert_allclose(new, g["scores_after"], rtol=0, atol=1e-12)
+    assert victim == g["evicted"]
+    assert kept.tolist() == g["cache_after"]
+
+
+def test_h2o_capacity6_example_through_softmax():
+    """The same step with the weights produced by attention: logits ln(w)
+    (the printed weights sum to 1, so softmax returns them)."""
+    g = gold("h2o_capacity6_example.json")
+    w = np.array(g["weights"])
+    assert abs(w.sum() - 1.0) < 1e-12
+    q = np.array([[1.0]])
+    k = np.log(w)[None, :, None]                   # d = 1: logit_i = ln w_i
+    v = np.zeros_like(k)
+    _, p = attend(q, k, v)
+    new, victim, kept = h2o.update_and_evict(g["positions"], g["scores_before"], p[0],
+                                             n_heavy=3, n_recent=3, budget=6)
+    np.testing.assert_allclose(new, g["scores_after"], atol=1e-12)
+    assert victim == 8 and kept.tolist() == g["cache_after"]
+
+
+# ---------------------------------------------------------------------------
+# HqeKV notes, section 3.7: the 8-token ranking example
+# ---------------------------------------------------------------------------
+
+def test_hqekv_8token_joint_metric_order_and_tiers():
+    g = gold("hqekv_8token_example.json")
+    m = hqekv.joint_metric(g["acc_attention"], g["value_range"])
+    np.testing.assert_allclose(m, g["joint"], atol=5e-4)
+    pos = np.arange(8)
+    ranked = rank.order(m, pos)
+    assert (ranked + 1).tolist() == g["order_1based"]
+    counts = hqekv.share_counts(g["ratios"], 8)
+    assert counts == [0, 2, 2, 2]
+    t = hqekv.assign(m, pos, np.ones(8, bool), counts)
+    names = {hqekv.INT4: "int4", hqekv.INT2: "int2", hqekv.INT1: "int1_normal", hqekv.EVICT: "evicted"}
+    got = {v: sorted((np.flatnonzero(t == k) + 1).tolist()) for k, v in names.items()}
+    for k, v in g["tiers"].items():
+        assert got[k] == sorted(v), k
+
+
+def test_hqekv_example_attention_only_ranking_differs():
+    """The example's point: ranking by attention alone would evict t6 and keep
+    t7; the joint metric keeps t6 (1-bit) and evicts t7."""
+    g = gold("hqekv_8token_example.json")
+    a = np.array(g["acc_attention"])
+    t_att = hqekv.assign(a, np.arange(8), np.ones(8, bool), [0, 2, 2, 2])
+    assert t_att[5] == hqekv.EVICT and t_att[6] != hqekv.EVICT
+
+
+# ---------------------------------------------------------------------------
+# QEvict notes, section 4.5: Eq.(3) worked example; capacity arithmetic
+# ---------------------------------------------------------------------------
+
+def test_qevict_eq3_capacity_example():
+    g = gold("qevict_capacity_example.json")
+    assert budget.kv_bytes_per_token(1, 8, 128, 2) == g["bytes_per_token_per_layer"]
+    assert budget.kv_bytes_per_token(g["layers"], 8, 128, 2) == g["bytes_per_token"]
+    # M_f of an 8-token window across all layers = 8 * 128 KiB = 1 MiB
+    assert g["window"] * g["bytes_per_token"] == 1024 * 1024
+    kf, kq = budget.tier_capacities(g["b_hist_mb"], g["q"], g["m_full_mb"], g["m_quant_mb"])
+    assert (kf, kq) == (g["k_full"], g["k_quant"])
+    assert kf * g["window"] == g["full_tokens"] and kq * g["window"] == g["quant_tokens"]
+    # the page rounds M_q; the unrounded 1 MB * 2/16 * 1.05 gives one window fewer
+    assert budget.tier_capacities(100, 0.7, 1.0, 2 / 16 * 1.05)[1] == 533
+
+
+def test_kivi_payload_and_capacity_arithmetic():
+    g = gold("payload_examples.json")
+    bpe = budget.payload_bytes_per_elem(g["bits"], g["group"], g["param_bytes"])
+    assert bpe == g["bytes_per_elem"]
+    assert round(2.0 / bpe, 2) == g["compression_vs_bf16"]
+    # the oracle's own ledger layout carries exactly that payload at 32-token windows
+    assert budget.window_ledger_bytes(32, 128, 2) / (2 * 32 * 128) == g["bytes_per_elem"]
+    assert budget.kv_bytes_per_token(32, 8, 128, 2) == g["bytes_per_token"]
+    assert g["request_tokens"] * g["bytes_per_token"] == g["request_bytes"]
+    assert g["request_tokens"] * budget.kv_bytes_per_token(32, 32, 128, 2) == g["request_bytes_32kv"]
+    share = budget.residual_share(g["residual_T"], g["residual_R"], g["bytes_per_elem"])
+    assert round(100 * share, 1) == g["residual_share_pct"]
+    assert budget.last_page_waste(g["page_T"], 16) == g["waste_16"]
+    assert budget.last_page_waste(g["page_T"], 128) == g["waste_128"]
+    assert g["waste_16"] * g["bytes_per_token"] / 2 ** 20 == g["waste_16_mib"]
+    assert g["waste_128"] * g["bytes_per_token"] / 2 ** 20 == g["waste_128_mib"]
+
+
+def test_packed_sizes_match_payload():
+    """Packed canonical code streams have the bit counts of the payload arithmetic."""
+    rng = np.random.default_rng(0)
+    for bits in (1, 2, 4):
+        c = rng.integers(0, 2 ** bits, size=4096).astype(np.uint8)
+        p = codec.pack_codes(c, bits)
+        assert p.size == 4096 * bits // 8
+        np.testing.assert_array_equal(codec.unpack_codes(p, bits, 4096), c)
+    # explicit bit positions: element e at bit 2*(e mod 4) of byte e//4
+    p = codec.pack_codes(np.array([1, 2, 3, 0, 3], np.uint8), 2)
+    assert p.tolist() == [1 | (2 << 2) | (3 << 4), 3]
+    p4 = codec.pack_codes(np.array([0xA, 0x5], np.uint8), 4)
+    assert p4.tolist() == [0x5A]
+
+
+# ---------------------------------------------------------------------------
+# HqeKV notes, section 2.3, Eq.(2): the uniform quantizer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_uniform_quantizer_endpoints_and_error_bound(bits):
+    rng = np.random.default_rng(bits)
+    x = (rng.standard_normal((500, 32)) * rng.uniform(0.1, 20, (500, 1))).astype(np.float32)
+    x = bf16_to_f64(np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.float32)
+    c, s, z = codec.uniform_quantize(x, bits)
+    L = 2 ** bits - 1
+    assert c.max() <= L
+    # zero = min (Eq.2): the group minimum maps to code 0, the maximum to the top code
+    assert np.all(c[np.arange(500), x.argmin(1)] == 0)
+    assert np.all(c[np.arange(500), x.argmax(1)] == L)
+    xh = codec.uniform_dequantize(c, s, z).astype(np.float64)
+    step = (x.max(1) - x.min(1)) / L
+    # rounding to the nearest level: error <= step/2, plus the float16 parameter rounding
+    slack = np.abs(s.astype(np.float64) - step) * L + np.abs(z.astype(np.float64) - x.min(1)) + 1e-6
+    assert np.all(np.abs(xh - x).max(1) <= step / 2 + slack)
+
+
+def test_uniform_quantizer_degenerate_and_lossless_levels():
+    # a constant group: step 0, every code 0, exact reconstruction
+    x = np.full((3, 32), 1.5, np.float32)
+    c, s, z = codec.uniform_quantize(x, 2)
+    assert np.all(c == 0) and np.all(s == 0)
+    np.testing.assert_array_equal(codec.uniform_dequantize(c, s, z), x)
+    # data on the 4 levels z + k*s (s, z exact in float16): lossless at 2 bits
+    rng = np.random.default_rng(1)
+    k = rng.integers(0, 4, (64, 32))
+    k[:, 0], k[:, 1] = 0, 3
+    x = (-0.5 + 0.25 * k).astype(np.float32)
+    c, s, z = codec.uniform_quantize(x, 2)
+    np.testing.assert_array_equal(c, k)
+    np.testing.assert_array_equal(codec.uniform_dequantize(c, s, z), x)
+
+
+def test_kivi_groups_keys_per_channel_values_per_token():
+    """KV-cache evolution page, section 5: per-channel key groups keep an
+    outlier channel from inflating the other channels' steps; values are
+    grouped per token."""
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((2, 16, 128)).astype(np.float32)
+    v = rng.standard_normal((2, 16, 128)).astype(np.float32)
+    k[:, :, 7] *= 50.0
+    q = codec.kivi_quantize_window(k, v, 2)
+    assert q["kscale"].shape == (2, 128, 1) and q["vscale"].shape == (2, 16, 4)
+    kh, vh = codec.kivi_dequantize_window(q)
+    err = np.abs(kh - k)
+    assert err[:, :, 7].max() > 5 * np.delete(err, 7, axis=2).max()
+    np.testing.assert_allclose(q["kscale"][:, 7, 0],
+                               ((k[:, :, 7].max(1) - k[:, :, 7].min(1)) / 3).astype(np.float16), rtol=1e-3)
+    np.testing.assert_allclose(q["vscale"][0, 3, 1],
+                               np.float16((v[0, 3, 32:64].max() - v[0, 3, 32:64].min()) / 3), rtol=1e-3)
+    # 32-token windows: one key group per channel; 48-token window: two chunks
+    q48 = codec.kivi_quantize_window(np.tile(k, (1, 3, 1)), np.tile(v, (1, 3, 1)), 2)
+    assert q48["kscale"].shape == (2, 128, 2)
+
+
+# ---------------------------------------------------------------------------
+# HqeKV notes, section 2.3, Eq.(3)-(4) and section 3.4
+# ---------------------------------------------------------------------------
+
+def test_normal_quantizer_one_bit_is_sign_test_with_quartile_centres():
+    assert abs(0.5 * (1 + math.erf(float(codec.KAPPA1) / math.sqrt(2))) - 0.75) < 1e-7
+    rng = np.random.default_rng(3)
+    x = bf16_to_f64(np.asarray(rng.standard_normal((200, 128)), np.float32).view(np.uint32) >> 16).astype(np.float32)
+    c, m, sd = codec.int1_normal_quantize(x)
+    np.testing.assert_array_equal(c, (x > x.astype(np.float64).mean(1, keepdims=True)).astype(np.uint8))
+    xh = codec.int1_normal_dequantize(c, m, sd).astype(np.float64)
+    lvl = m.astype(np.float64)[:, None] + np.where(c > 0, 1, -1) * 0.6744897501960817 * sd.astype(np.float64)[:, None]
+    np.testing.assert_allclose(xh, lvl, rtol=1e-6, atol=1e-6)
+    # the general-b quantizer reduces to the same codes at b = 1
+    c1, *_ = codec.normal_quantize(x, 1)
+    np.testing.assert_array_equal(c1, c)
+
+
+def test_uniform_vs_normalized_reversal_on_gaussian_vectors():
+    """Section 3.4: on Gaussian vectors the normalized quantizer wins at 1 bit
+    and the uniform one wins at 4 bits."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2000, 128))
+    for bits, uniform_better in ((1, False), (4, True)):
+        e_u = np.mean((codec.uniform_roundtrip64(x, bits) - x) ** 2)
+        e_n = np.mean((codec.normal_quantize(x, bits)[3] - x) ** 2)
+        assert (e_u < e_n) == uniform_better, (bits, e_u, e_n)
+
+
+# ---------------------------------------------------------------------------
+# attention (QEvict 4.1; H2O 1.1)
+# ---------------------------------------------------------------------------
+
+def test_attention_matches_bruteforce_and_rows_sum_to_one():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 8))
+    k = rng.standard_normal((2, 11, 8))
+    v = rng.standard_normal((2, 11, 8))
+    mask = rng.random(11) > 0.3
+    o, p = attend(q, k, v, mask)
+    ob, pb = attend_bruteforce(q, k, v, mask)
+    np.testing.assert_allclose(o, ob, atol=1e-12)
+    np.testing.assert_allclose(p, pb, atol=1e-12)
+    np.testing.assert_allclose(p.sum(1), 1.0, atol=1e-12)
+    assert np.all(p[:, ~mask] == 0)
+    # removing a position renormalizes the rest (H2O 1.1): masked == gathered subset
+    o2, p2 = attend(q, k[:, mask], v[:, mask])
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    np.testing.assert_allclose(p[:, mask], p2, atol=1e-12)
+
+
+def test_round_to_bf16_nearest_even():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7 + 2 ** -9, -3.0], np.float32)
+    np.testing.assert_array_equal(round_to_bf16(x), [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -3.0])
