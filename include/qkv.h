@@ -1,0 +1,216 @@
+/*
+ * qkv.h -- C ABI of the tiered KV-cache decode path for MI355X (gfx950).
+ *
+ * One cache object holds one transformer layer's KV state for a batch of
+ * sequences that advance in lockstep.  Its memory is a single caller-owned
+ * device workspace; the library never allocates device memory after
+ * qkv_create and never frees caller memory.  Every call that takes a stream
+ * only enqueues work on that stream (NULL = the null stream) and returns;
+ * routing decisions, transition lists and live-unit lists stay on the device,
+ * so no call waits for the GPU.  All tensor arguments are device pointers,
+ * row-major, densely packed.  bfloat16 tensors are passed as uint16 storage.
+ *
+ * Error convention: every int-returning call returns QKV_OK (0) or a negative
+ * QKV_E* code; arguments are validated on the host before anything is
+ * enqueued, so a call that fails leaves the cache unchanged.  A device-side
+ * condition (a quantization parameter outside float16 range) is latched in
+ * the cache and reported by qkv_status().  No call throws.  A cache is not
+ * thread-safe: use one cache per stream.
+ *
+ * Notation follows the pages: H_q query heads, H_kv KV heads, G = H_q/H_kv,
+ * d = head dim, window = tokens per window (omega_w), omega = routing period
+ * (Omega), K_f / K_q = windows kept in full precision / quantized.
+ */
+#ifndef QKV_H
+#define QKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qkv_cache qkv_cache;
+typedef void *qkv_stream; /* a hipStream_t */
+
+enum {
+  QKV_OK = 0,
+  QKV_EINVAL = -1,    /* bad shape, argument or configuration               */
+  QKV_ECAPACITY = -2, /* max_ctx, list or workspace capacity exceeded       */
+  QKV_ERANGE = -3,    /* a quantization parameter does not fit float16      */
+  QKV_EHIP = -4,      /* HIP runtime error                                  */
+  QKV_ESTATE = -5,    /* call out of order for the cache's policy or state  */
+};
+
+enum { QKV_POLICY_QEVICT = 0, QKV_POLICY_H2O = 1, QKV_POLICY_HQEKV = 2 };
+
+/* Quantizer kinds of qkv_quantize_window. */
+enum {
+  QKV_KIND_K_PER_CHANNEL = 0, /* keys: one group per channel along tokens     */
+  QKV_KIND_PER_TOKEN = 1,     /* values (and HqeKV keys): per token, channel groups */
+  QKV_KIND_INT1_NORMAL = 2,   /* one-bit normalized quantizer per token       */
+};
+
+enum { QKV_DTYPE_BF16 = 0, QKV_DTYPE_F32 = 1 };
+
+/* Unit tiers as exported by qkv_export(QKV_EXPORT_TIERS). */
+enum {
+  QKV_TIER_EMPTY = 0,   /* not yet appended                                  */
+  QKV_TIER_SINK = 1,    /* protected prefix, always full precision            */
+  QKV_TIER_RECENT = 2,  /* full precision, not yet ranked                     */
+  QKV_TIER_FULL = 3,    /* ranked into the full-precision tier               */
+  QKV_TIER_QUANT = 4,   /* ranked into the quantized (recoverable) tier      */
+  QKV_TIER_EVICTED = 5, /* dropped for good                                  */
+};
+
+typedef struct qkv_config {
+  int32_t batch;      /* sequences                                          */
+  int32_t n_q_heads;  /* H_q                                                */
+  int32_t n_kv_heads; /* H_kv; H_q % H_kv == 0, G = H_q / H_kv <= 8          */
+  int32_t head_dim;   /* d in {64, 128}                                     */
+  int32_t policy;     /* QKV_POLICY_*                                       */
+  int32_t window;     /* tokens per window: 8, 16 or 32 (QEvict)            */
+  int32_t omega;      /* routing period in decode steps                     */
+  int32_t n_sink;     /* protected prefix tokens (<= 16)                    */
+  int32_t n_recent;   /* protected recent tokens                            */
+  int32_t k_full;     /* K_f: windows kept in full precision                */
+  int32_t k_quant;    /* K_q: windows kept quantized                        */
+  float ratios[5];    /* HqeKV shares: BF16, INT4, INT2, INT1-normal, evict */
+  int32_t quant_bits; /* bits of the recoverable tier (2)                    */
+  int32_t group;      /* quantization group (32)                            */
+  int32_t max_ctx;    /* capacity in tokens per sequence                    */
+  int32_t n_splits;   /* attention splits per (sequence, KV head); 0 = auto */
+} qkv_config;
+
+/* Bytes of device workspace a cache with this configuration needs, or 0 if
+ * the configuration is invalid (see qkv_check_config for the reason). */
+size_t qkv_workspace_bytes(const qkv_config *cfg);
+
+/* QKV_OK if the configuration is supported, else QKV_EINVAL. */
+int qkv_check_config(const qkv_config *cfg);
+
+/* Create a cache over `workspace` (device memory, at least
+ * qkv_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller and
+ * kept alive until qkv_destroy).  The workspace is cleared on `stream`. */
+int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream,
+               qkv_cache **out);
+
+/* Release the host-side handle (the workspace stays the caller's). */
+int qkv_destroy(qkv_cache *cache);
+
+/*
+ * Append n_tokens new positions to every sequence.
+ *   k, v: bfloat16 [batch, n_kv_heads, n_tokens, head_dim].
+ * QEvict: positions go to their windows (the first n_sink positions form the
+ * sink unit); every appended window is full precision and not yet ranked
+ * (QEvict notes, Fig.1 stage 1: all windows start in full precision).
+ * Errors: QKV_ECAPACITY if the total would exceed max_ctx.
+ */
+int qkv_append(qkv_cache *cache, const void *k, const void *v, int32_t n_tokens, qkv_stream stream);
+
+/*
+ * One decode step of single-query attention over the accessible cache, with
+ * the attention mass each unit receives accumulated into its score.
+ *   q:        bfloat16 [batch, n_q_heads, head_dim]
+ *   out:      float32  [batch, n_q_heads, head_dim]
+ *   mass_out: optional float32 [batch, n_kv_heads, n_units]: this step's mass
+ *             per unit summed over the G query heads of each KV head (0 for
+ *             units that were not accessible).  n_units: qkv_info(QKV_INFO_UNITS).
+ * Attention is softmax(q K^T / sqrt(d)) V over sinks, not-yet-ranked windows,
+ * full-precision windows and dequantized quantized windows (QEvict notes
+ * section 4.1, Eq. attention); each head's mass on a unit below FLT_MIN counts
+ * as 0; QEvict scores add the mass of all query heads (section 4.2, Eq.(1),
+ * without its constant 1/H_q).
+ */
+int qkv_decode_attend(qkv_cache *cache, const void *q, float *out, float *mass_out, qkv_stream stream);
+
+/*
+ * Routing event (QEvict notes section 4.4, Eq.(4)-(6), Algorithm 1): the
+ * previous full and quantized windows and the windows that aged out of the
+ * recent region are ranked by score (descending, ties to the later window);
+ * the first k_full are full precision, the next k_quant quantized, the rest
+ * evicted.  A window demoted for the first time is packed (keys per channel,
+ * values per token, float16 scale/zero per group) into its persistent ledger;
+ * later demotions reuse those codes; a promoted window is rebuilt in
+ * full precision from its ledger.
+ */
+int qkv_route(qkv_cache *cache, qkv_stream stream);
+
+/*
+ * Stateless quantizer (HqeKV notes section 2.3 Eq.(2) uniform; Eq.(3)-(4)
+ * one-bit normalized) over n_blocks independent blocks of [tokens, head_dim].
+ *   x:      [n_blocks, tokens, head_dim], bfloat16 or float32 (x_dtype)
+ *   codes:  uint8, canonical packed layout, codes_bytes(kind) per block:
+ *           K_PER_CHANNEL: element (channel c, token t) has index c*tokens+t;
+ *           PER_TOKEN / INT1_NORMAL: index t*head_dim+c; element e sits at bit
+ *           bits*(e mod (8/bits)) of byte e*bits/8.
+ *   params: float16 pairs per group, per block:
+ *           K_PER_CHANNEL: [head_dim][ceil(tokens/group)][scale, zero]
+ *           PER_TOKEN:     [tokens][head_dim/group][scale, zero]
+ *           INT1_NORMAL:   [tokens][mean, std]
+ * bits: 2 or 4 for the uniform kinds, 1 for INT1_NORMAL.  Groups are `group`
+ * tokens (K_PER_CHANNEL) or channels (PER_TOKEN).  A parameter outside float16
+ * range latches QKV_ERANGE, reported by qkv_quantize_status().
+ */
+int qkv_quantize_window(const void *x, int32_t x_dtype, int32_t n_blocks, int32_t tokens, int32_t head_dim,
+                        int32_t bits, int32_t group, int32_t kind, uint8_t *codes, uint16_t *params,
+                        qkv_stream stream);
+
+/*
+ * Stateless multi-tier ranking: entries with eligible[i] != 0 are ordered by
+ * (score descending, pos descending); the first tier_counts[0] get tier 0, the
+ * next tier_counts[1] tier 1, ..., the remaining eligible entries tier n_tiers,
+ * ineligible entries 255.  All pointers are device memory; n <= 8192.
+ */
+int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int32_t n,
+                   const int32_t *tier_counts, int32_t n_tiers, uint8_t *tier_out, qkv_stream stream);
+
+/* Export state into device memory `dst` (`bytes` must equal the size below).
+ *   QKV_EXPORT_TIERS   uint8   [batch, n_units]
+ *   QKV_EXPORT_SCORES  float32 [batch, n_units]
+ *   QKV_EXPORT_LEDGER  uint8   [batch, n_units]   1 if the unit holds ledger codes
+ *   QKV_EXPORT_KCODES  uint8   [batch, n_units, n_kv_heads, window*head_dim*bits/8] canonical
+ *   QKV_EXPORT_VCODES  uint8   [batch, n_units, n_kv_heads, window*head_dim*bits/8] canonical
+ *   QKV_EXPORT_KPARAMS uint16  [batch, n_units, n_kv_heads, head_dim, 1, 2]
+ *   QKV_EXPORT_VPARAMS uint16  [batch, n_units, n_kv_heads, window, head_dim/group, 2]
+ *   QKV_EXPORT_KEYS    uint16  [batch, n_kv_heads, max_ctx, head_dim]  full-precision content
+ *   QKV_EXPORT_VALUES  uint16  [batch, n_kv_heads, max_ctx, head_dim]
+ * (units without a ledger export zero codes and parameters).
+ */
+enum {
+  QKV_EXPORT_TIERS = 0,
+  QKV_EXPORT_SCORES = 1,
+  QKV_EXPORT_LEDGER = 2,
+  QKV_EXPORT_KCODES = 3,
+  QKV_EXPORT_VCODES = 4,
+  QKV_EXPORT_KPARAMS = 5,
+  QKV_EXPORT_VPARAMS = 6,
+  QKV_EXPORT_KEYS = 7,
+  QKV_EXPORT_VALUES = 8,
+};
+int qkv_export(const qkv_cache *cache, int32_t what, void *dst, size_t bytes, qkv_stream stream);
+size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);
+
+/* Host-side counters. */
+enum {
+  QKV_INFO_TOKENS = 0,      /* positions appended per sequence               */
+  QKV_INFO_UNITS = 1,       /* units per sequence (sink unit + windows)      */
+  QKV_INFO_STEPS = 2,       /* decode steps attended                         */
+  QKV_INFO_ROUTES = 3,      /* routing events                                */
+  QKV_INFO_SPLITS = 4,      /* attention splits per (sequence, KV head)      */
+  QKV_INFO_WORKSPACE = 5,   /* workspace bytes in use                        */
+};
+int qkv_info(const qkv_cache *cache, int32_t what, int64_t *value);
+
+/* Device-latched status: waits for `stream`, returns QKV_OK or QKV_ERANGE. */
+int qkv_status(qkv_cache *cache, qkv_stream stream);
+/* Status latched by qkv_quantize_window calls since the last query (same rule). */
+int qkv_quantize_status(qkv_stream stream);
+
+const char *qkv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKV_H */

@@ -18,7 +18,7 @@ Follows the QEvict notes:
   demotion, keys per channel / values per token, and the codes are kept in a
   persistent ledger that later demotions reuse; a promoted window is rebuilt
   from the ledger.
-* Fig.1 -- all windows start in full precision.
+* Fig.1 -- all windows start in full precision (and unranked).
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -112,12 +112,14 @@ class QEvictSequence:
 
     # -- prefill ------------------------------------------------------------
     def prefill(self, P: int) -> None:
-        """All prompt windows start in full precision: windows already older
-        than the recent region are Full, the others Recent; scores are 0."""
+        """All prompt windows start in full precision and unranked (Recent);
+        scores are 0.  The first event's candidate pool is then every window
+        that has aged out of the recent region, which is the pool Eq.(4) gives
+        when the aged prompt windows are counted as the previous Full set."""
         self.P = self.N = P
         self.tier[0] = SINK
         for u in range(1, self.unit_of_pos[P - 1] + 1):
-            self.tier[u] = FULL if self.last(u) < P - self.n_recent else RECENT
+            self.tier[u] = RECENT
 
     # -- one decode step ----------------------------------------------------
     def accessible_mask(self) -> np.ndarray:

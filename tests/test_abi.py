@@ -1,0 +1,81 @@
+"""The C ABI library loads and exports what include/qkv.h declares; host-side
+configuration checks (CPU only: no call here touches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from tiered_quantization_eviction_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        from tiered_quantization_eviction_amd import build
+        build.build()
+    return L, L.lib()
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(qkv_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("qkv_append", "qkv_decode_attend", "qkv_route", "qkv_quantize_window", "qkv_create",
+                 "qkv_destroy", "qkv_rank_tiers", "qkv_export", "qkv_workspace_bytes"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    _, lib = _lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_config_checks_on_host():
+    L, lib = _lib()
+    for cfg in (W.TINY, W.DRIFT, W.STRESS):
+        c = L.make_config(cfg)
+        assert lib.qkv_check_config(ctypes.byref(c)) == 0, cfg.name
+        assert L.workspace_bytes(c) > 0
+    bad = [dict(n_q_heads=12, n_kv_heads=4),     # G = 3
+           dict(head_dim=96),
+           dict(window=12),
+           dict(n_sink=17),
+           dict(quant_bits=3),
+           dict(max_ctx=0)]
+    for kw in bad:
+        c = L.make_config(W.TINY, **kw) if "max_ctx" not in kw else L.make_config(W.TINY, max_ctx=0)
+        if "max_ctx" not in kw:
+            for k, v in kw.items():
+                setattr(c, k, v)
+        assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL, kw
+        assert L.workspace_bytes(c) == 0
+
+
+def test_strerror_and_info_arguments():
+    L, lib = _lib()
+    assert lib.qkv_strerror(L.ERANGE).decode().startswith("quantization parameter")
+    assert lib.qkv_create(None, None, 0, None, None) == L.EINVAL
+    assert lib.qkv_append(None, None, None, 1, None) == L.EINVAL
+    assert lib.qkv_route(None, None) == L.EINVAL
+
+
+def test_workspace_holds_payload_of_config3():
+    """Unit-indexed pages and ledger of the 32K x 16 workload."""
+    L, _ = _lib()
+    c = L.make_config(W.DRIFT)
+    U = 1 + -(-(W.DRIFT.total_tokens - 5) // 16)
+    pages = 16 * U * 8 * 2 * 16 * 128 * 2
+    ledger = 16 * U * 8 * (512 + 512 + 512 + 256)
+    assert pages + ledger <= L.workspace_bytes(c) <= pages + ledger + 64 * 2 ** 20

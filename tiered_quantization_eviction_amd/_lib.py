@@ -1,0 +1,219 @@
+"""ctypes binding of libqkv.so (argument marshalling only).
+
+Every step of the decode path runs in the HIP library; this module only turns
+torch tensors into device pointers and the current torch stream into the
+stream argument.  Importing it on a host without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqkv.so")
+
+OK, EINVAL, ECAPACITY, ERANGE, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+POLICY = {"qevict": 0, "h2o": 1, "hqekv": 2}
+KIND_K_PER_CHANNEL, KIND_PER_TOKEN, KIND_INT1_NORMAL = 0, 1, 2
+DTYPE_BF16, DTYPE_F32 = 0, 1
+TIER_EMPTY, TIER_SINK, TIER_RECENT, TIER_FULL, TIER_QUANT, TIER_EVICTED = range(6)
+EXPORT = {"tiers": 0, "scores": 1, "ledger": 2, "kcodes": 3, "vcodes": 4, "kparams": 5, "vparams": 6,
+          "keys": 7, "values": 8}
+INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5}
+
+
+class QkvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {_lib().qkv_strerror(code).decode()} ({code})")
+
+
+class QkvConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("policy", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("omega", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+        ("k_full", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("ratios", ctypes.c_float * 5),
+        ("quant_bits", ctypes.c_int32), ("group", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+        ("n_splits", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libqkv.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.qkv_strerror.restype = ctypes.c_char_p
+        L.qkv_strerror.argtypes = [ctypes.c_int]
+        L.qkv_workspace_bytes.restype = _sz
+        L.qkv_workspace_bytes.argtypes = [ctypes.POINTER(QkvConfig)]
+        L.qkv_check_config.argtypes = [ctypes.POINTER(QkvConfig)]
+        L.qkv_create.argtypes = [ctypes.POINTER(QkvConfig), _vp, _sz, _vp, ctypes.POINTER(_vp)]
+        L.qkv_destroy.argtypes = [_vp]
+        L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
+        L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
+        L.qkv_route.argtypes = [_vp, _vp]
+        L.qkv_quantize_window.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+        L.qkv_quantize_status.argtypes = [_vp]
+        L.qkv_rank_tiers.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]
+        L.qkv_export.argtypes = [_vp, _i32, _vp, _sz, _vp]
+        L.qkv_export_bytes.restype = _sz
+        L.qkv_export_bytes.argtypes = [_vp, _i32]
+        L.qkv_info.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qkv_status.argtypes = [_vp, _vp]
+        _LIB = L
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    return _lib()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise QkvError(rc, what)
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor required")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor required")
+    return t.data_ptr()
+
+
+def make_config(cfg=None, *, n_splits: int = 0, max_ctx: int | None = None, **kw) -> QkvConfig:
+    """Build the C configuration from an object with the workload attributes
+    (batch, n_q_heads, ..., prefill, steps) or from keyword arguments."""
+    src = dict(kw)
+    if cfg is not None:
+        for f, _ in QkvConfig._fields_:
+            if hasattr(cfg, f) and f not in src:
+                src[f] = getattr(cfg, f)
+        if max_ctx is None and hasattr(cfg, "prefill"):
+            max_ctx = cfg.prefill + cfg.steps
+        if "policy" in src and isinstance(src["policy"], str):
+            src["policy"] = POLICY[src["policy"]]
+    c = QkvConfig()
+    for f, _ in QkvConfig._fields_:
+        if f == "ratios":
+            r = src.get("ratios", (0, 0, 0, 0, 0))
+            for i in range(5):
+                c.ratios[i] = float(r[i])
+        elif f == "max_ctx":
+            c.max_ctx = int(max_ctx if max_ctx is not None else src.get("max_ctx", 0))
+        elif f == "n_splits":
+            c.n_splits = int(n_splits)
+        elif f == "policy":
+            p = src.get("policy", 0)
+            c.policy = POLICY[p] if isinstance(p, str) else int(p)
+        else:
+            setattr(c, f, int(src.get(f, 32 if f == "group" else (2 if f == "quant_bits" else 0))))
+    return c
+
+
+def workspace_bytes(c: QkvConfig) -> int:
+    return int(_lib().qkv_workspace_bytes(ctypes.byref(c)))
+
+
+class Cache:
+    """One layer's tiered KV cache for a batch of sequences (device state)."""
+
+    def __init__(self, c: QkvConfig, device="cuda", stream=None):
+        import torch
+        self.c = c
+        n = workspace_bytes(c)
+        if n == 0:
+            raise QkvError(_lib().qkv_check_config(ctypes.byref(c)), "qkv config")
+        self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self._base = (base + 255) // 256 * 256
+        h = _vp()
+        _check(_lib().qkv_create(ctypes.byref(c), self._base, n, _stream(stream), ctypes.byref(h)), "qkv_create")
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            _lib().qkv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, k, v, stream=None):
+        """k, v: bf16 [B, Hkv, n, d] device tensors."""
+        n = int(k.shape[2])
+        _check(_lib().qkv_append(self.h, _ptr(k), _ptr(v), n, _stream(stream)), "qkv_append")
+
+    def decode_attend(self, q, out, mass_out=None, stream=None):
+        _check(_lib().qkv_decode_attend(self.h, _ptr(q), _ptr(out), _ptr(mass_out), _stream(stream)),
+               "qkv_decode_attend")
+
+    def route(self, stream=None):
+        _check(_lib().qkv_route(self.h, _stream(stream)), "qkv_route")
+
+    def export(self, what: str, stream=None):
+        import torch
+        code = EXPORT[what]
+        nbytes = int(_lib().qkv_export_bytes(self.h, code))
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=self.workspace.device)
+        _check(_lib().qkv_export(self.h, code, _ptr(dst), nbytes, _stream(stream)), "qkv_export")
+        return dst
+
+    def info(self, what: str) -> int:
+        v = ctypes.c_int64()
+        _check(_lib().qkv_info(self.h, INFO[what], ctypes.byref(v)), "qkv_info")
+        return int(v.value)
+
+    def status(self, stream=None) -> int:
+        return int(_lib().qkv_status(self.h, _stream(stream)))
+
+
+def quantize_window(x, kind: int, bits: int, group: int = 32, stream=None):
+    """x: [n_blocks, tokens, d] bf16 (as int16/uint16/bfloat16) or float32 device tensor.
+    Returns (codes uint8 [n_blocks, code_bytes], params uint16 [n_blocks, ...])."""
+    import torch
+    n_blocks, tokens, d = (int(s) for s in x.shape)
+    dtype = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
+    code_bytes = (tokens * d * bits + 7) // 8
+    if kind == KIND_K_PER_CHANNEL:
+        n_params = d * ((tokens + group - 1) // group) * 2
+    elif kind == KIND_PER_TOKEN:
+        n_params = tokens * (d // group) * 2
+    else:
+        n_params = tokens * 2
+    codes = torch.zeros((n_blocks, code_bytes), dtype=torch.uint8, device=x.device)
+    params = torch.zeros((n_blocks, n_params), dtype=torch.int16, device=x.device)
+    _check(_lib().qkv_quantize_window(_ptr(x), dtype, n_blocks, tokens, d, bits, group, kind, _ptr(codes),
+                                      _ptr(params), _stream(stream)), "qkv_quantize_window")
+    return codes, params
+
+
+def quantize_status(stream=None) -> int:
+    return int(_lib().qkv_quantize_status(_stream(stream)))
+
+
+def rank_tiers(score, pos, eligible, counts, stream=None):
+    import torch
+    n = int(score.numel())
+    out = torch.empty(n, dtype=torch.uint8, device=score.device)
+    _check(_lib().qkv_rank_tiers(_ptr(score), _ptr(pos), _ptr(eligible), n, _ptr(counts), int(counts.numel()),
+                                 _ptr(out), _stream(stream)), "qkv_rank_tiers")
+    return out

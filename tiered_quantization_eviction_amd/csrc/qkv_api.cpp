@@ -1,0 +1,307 @@
+// Host side of the qkv C ABI: configuration checks, geometry, workspace
+// carving, and the per-step scalars (token count, recent range) that the host
+// tracks so that no call has to read device state.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <string.h>
+
+#include "qkv_internal.h"
+
+using namespace qkv;
+
+struct qkv_cache {
+  qkv_config cfg;
+  Geom g;
+  State st;
+  void *ws;
+  size_t ws_bytes;
+  int N;          // tokens appended per sequence
+  int r0;         // first window not yet ranked
+  int routed;     // ranked windows held (same for every sequence)
+  long long steps;
+  long long routes;
+};
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int validate(const qkv_config *c) {
+  if (!c) return QKV_EINVAL;
+  if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1) return QKV_EINVAL;
+  if (c->n_q_heads % c->n_kv_heads) return QKV_EINVAL;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 4 && G != 8) return QKV_EINVAL;            // query heads per KV head: 4 or 8
+  if (c->n_q_heads > 128) return QKV_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return QKV_EINVAL;
+  if (c->max_ctx < 1) return QKV_EINVAL;
+  if (c->n_splits < 0 || c->n_splits > 256) return QKV_EINVAL;
+  if (c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;   // per-token policies: separate caches (not here)
+  if (c->window != 8 && c->window != 16 && c->window != 32) return QKV_EINVAL;
+  if (c->omega < 1) return QKV_EINVAL;
+  if (c->n_sink < 0 || c->n_sink > TS || c->n_recent < 0) return QKV_EINVAL;
+  if (c->k_full < 0 || c->k_quant < 0) return QKV_EINVAL;
+  if (c->quant_bits != 2 || c->group != 32) return QKV_EINVAL;
+  const long long U = 1 + ((long long)c->max_ctx - c->n_sink + c->window - 1) / c->window;
+  if (U + 1 > SORT_MAX) return QKV_EINVAL;            // routing candidates are ranked in LDS
+  return QKV_OK;
+}
+
+void make_geom(const qkv_config *c, Geom &g) {
+  memset(&g, 0, sizeof g);
+  g.B = c->batch;
+  g.Hq = c->n_q_heads;
+  g.Hkv = c->n_kv_heads;
+  g.G = c->n_q_heads / c->n_kv_heads;
+  g.d = c->head_dim;
+  g.window = c->window;
+  g.omega = c->omega;
+  g.n_sink = c->n_sink;
+  g.n_recent = c->n_recent;
+  g.k_full = c->k_full;
+  g.k_quant = c->k_quant;
+  g.bits = c->quant_bits;
+  g.group = c->group;
+  g.max_ctx = c->max_ctx;
+  g.U = 1 + (c->max_ctx - c->n_sink + c->window - 1) / c->window;
+  if (g.U < 1) g.U = 1;
+  g.tpw = (c->window + TS - 1) / TS;
+  g.page_unit_elems = g.tpw * 2 * TS * g.d;
+  g.kparam_bytes = 4 * g.d;
+  g.tile_kcode_bytes = TS * g.d / 4;
+  g.tile_vcode_bytes = TS * g.d / 4;
+  g.tile_vparam_bytes = 4 * (g.d / 32) * 16;
+  g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
+  g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;
+  g.cost_full = g.page_unit_elems * 2;
+  g.cost_quant = g.ledger_unit_bytes;
+  int S = c->n_splits;
+  if (S == 0) {   // enough workgroups to fill 256 compute units several times over
+    const int pairs = g.B * g.Hkv;
+    S = (2048 + pairs - 1) / pairs;
+    const int cap = g.U / 4 > 1 ? g.U / 4 : 1;
+    if (S > cap) S = cap;
+    if (S > 64) S = 64;
+    if (S < 1) S = 1;
+  }
+  g.n_splits = S;
+}
+
+// workspace carving; with base == nullptr only sizes are computed
+size_t carve(const Geom &g, char *base, State &st) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *p = base ? base + off : nullptr;
+    off = align_up(off + bytes);
+    return (void *)p;
+  };
+  const size_t BU = (size_t)g.B * g.U;
+  st.pages = (uint16_t *)take(BU * g.Hkv * (size_t)g.page_unit_elems * 2);
+  st.ledger = (uint8_t *)take(BU * g.Hkv * (size_t)g.ledger_unit_bytes);
+  st.tier = (uint8_t *)take(BU);
+  st.has_ledger = (uint8_t *)take(BU);
+  st.score = (float *)take(BU * 4);
+  st.routed = (int32_t *)take(BU * 4);
+  st.routed_nf = (int32_t *)take((size_t)g.B * 4);
+  st.routed_nq = (int32_t *)take((size_t)g.B * 4);
+  st.pack_list = (int32_t *)take(BU * 4);
+  st.pack_count = (int32_t *)take((size_t)g.B * 4);
+  st.promote_list = (int32_t *)take(BU * 4);
+  st.promote_count = (int32_t *)take((size_t)g.B * 4);
+  st.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
+  st.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
+  st.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
+  st.status = (int32_t *)take(16);
+  return off;
+}
+
+int hip_err(hipError_t e) { return e == hipSuccess ? QKV_OK : QKV_EHIP; }
+
+StepInfo step_info(const qkv_cache *c) {
+  StepInfo si;
+  si.N = c->N;
+  si.has_sink = (c->g.n_sink > 0 && c->N > 0) ? 1 : 0;
+  si.r0 = c->r0;
+  si.r1 = c->N > c->g.n_sink ? unit_of(c->g, c->N - 1) : 0;
+  return si;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qkv_strerror(int code) {
+  switch (code) {
+    case QKV_OK: return "ok";
+    case QKV_EINVAL: return "invalid argument or configuration";
+    case QKV_ECAPACITY: return "capacity exceeded";
+    case QKV_ERANGE: return "quantization parameter outside float16 range";
+    case QKV_EHIP: return "HIP runtime error";
+    case QKV_ESTATE: return "call out of order";
+    default: return "unknown error";
+  }
+}
+
+int qkv_check_config(const qkv_config *cfg) { return validate(cfg); }
+
+size_t qkv_workspace_bytes(const qkv_config *cfg) {
+  if (validate(cfg) != QKV_OK) return 0;
+  Geom g;
+  make_geom(cfg, g);
+  State st;
+  return carve(g, nullptr, st);
+}
+
+int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream, qkv_cache **out) {
+  if (!out) return QKV_EINVAL;
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc != QKV_OK) return rc;
+  if (!workspace || ((uintptr_t)workspace % ALIGN)) return QKV_EINVAL;
+  qkv_cache *c = new (std::nothrow) qkv_cache;
+  if (!c) return QKV_ECAPACITY;
+  memset(c, 0, sizeof *c);
+  c->cfg = *cfg;
+  make_geom(cfg, c->g);
+  size_t need = carve(c->g, (char *)workspace, c->st);
+  if (bytes < need) {
+    delete c;
+    return QKV_ECAPACITY;
+  }
+  c->ws = workspace;
+  c->ws_bytes = need;
+  c->r0 = 1;
+  rc = hip_err(launch_clear(workspace, need, (hipStream_t)stream));
+  if (rc != QKV_OK) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return QKV_OK;
+}
+
+int qkv_destroy(qkv_cache *cache) {
+  delete cache;
+  return QKV_OK;
+}
+
+int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv_stream stream) {
+  if (!c || !k || !v || n_tokens < 1) return QKV_EINVAL;
+  if ((long long)c->N + n_tokens > c->g.max_ctx) return QKV_ECAPACITY;
+  int rc = hip_err(launch_append(c->g, c->st, (const uint16_t *)k, (const uint16_t *)v, n_tokens, c->N,
+                                 (hipStream_t)stream));
+  if (rc != QKV_OK) return rc;
+  c->N += n_tokens;
+  return QKV_OK;
+}
+
+int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, qkv_stream stream) {
+  if (!c || !q || !out) return QKV_EINVAL;
+  if (c->N < 1) return QKV_ESTATE;
+  int rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream));
+  if (rc != QKV_OK) return rc;
+  c->steps++;
+  return QKV_OK;
+}
+
+int qkv_route(qkv_cache *c, qkv_stream stream) {
+  if (!c) return QKV_EINVAL;
+  if (c->N < 1) return QKV_ESTATE;
+  const Geom &g = c->g;
+  // windows whose last position is older than the newest n_recent positions
+  const long long limit = (long long)c->N - g.n_recent;
+  const long long aged = limit > g.n_sink ? (limit - g.n_sink) / g.window : 0;
+  const int a0 = c->r0;
+  const int a1 = (int)(aged + 1 > a0 ? aged + 1 : a0);
+  const int n_cand = c->routed + (a1 - a0);
+  int rc = hip_err(launch_route(g, c->st, step_info(c), a0, a1, n_cand, (hipStream_t)stream));
+  if (rc != QKV_OK) return rc;
+  c->r0 = a1;
+  const int kfq = g.k_full + g.k_quant;
+  c->routed = n_cand < kfq ? n_cand : kfq;
+  c->routes++;
+  return QKV_OK;
+}
+
+int qkv_quantize_window(const void *x, int32_t x_dtype, int32_t n_blocks, int32_t tokens, int32_t head_dim,
+                        int32_t bits, int32_t group, int32_t kind, uint8_t *codes, uint16_t *params,
+                        qkv_stream stream) {
+  if (!x || !codes || !params || n_blocks < 1 || tokens < 1 || head_dim < 8 || head_dim % 8) return QKV_EINVAL;
+  if (x_dtype != QKV_DTYPE_BF16 && x_dtype != QKV_DTYPE_F32) return QKV_EINVAL;
+  if (kind == QKV_KIND_K_PER_CHANNEL || kind == QKV_KIND_PER_TOKEN) {
+    if (bits != 2 && bits != 4) return QKV_EINVAL;
+    if (group < 8 || group % 8) return QKV_EINVAL;
+    if (kind == QKV_KIND_K_PER_CHANNEL && tokens % 8) return QKV_EINVAL;   // whole bytes per channel run
+    if (kind == QKV_KIND_PER_TOKEN && head_dim % group) return QKV_EINVAL;
+  } else if (kind == QKV_KIND_INT1_NORMAL) {
+    if (bits != 1) return QKV_EINVAL;
+  } else {
+    return QKV_EINVAL;
+  }
+  return hip_err(launch_quantize_window(x, x_dtype, n_blocks, tokens, head_dim, bits, group, kind, codes, params,
+                                        (hipStream_t)stream));
+}
+
+int qkv_quantize_status(qkv_stream stream) {
+  int flag = 0;
+  int rc = hip_err(read_quantize_status(&flag, (hipStream_t)stream));
+  if (rc != QKV_OK) return rc;
+  return flag ? QKV_ERANGE : QKV_OK;
+}
+
+int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int32_t n,
+                   const int32_t *tier_counts, int32_t n_tiers, uint8_t *tier_out, qkv_stream stream) {
+  if (!score || !pos || !eligible || !tier_counts || !tier_out) return QKV_EINVAL;
+  if (n < 1 || n > 4096 || n_tiers < 0 || n_tiers > 254) return QKV_EINVAL;
+  return hip_err(launch_rank_tiers(score, pos, eligible, n, tier_counts, n_tiers, tier_out, (hipStream_t)stream));
+}
+
+size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
+  if (!c) return 0;
+  const Geom &g = c->g;
+  const size_t BU = (size_t)g.B * g.U;
+  switch (what) {
+    case QKV_EXPORT_TIERS:
+    case QKV_EXPORT_LEDGER: return BU;
+    case QKV_EXPORT_SCORES: return BU * 4;
+    case QKV_EXPORT_KCODES:
+    case QKV_EXPORT_VCODES: return BU * g.Hkv * (size_t)(g.window * g.d * g.bits / 8);
+    case QKV_EXPORT_KPARAMS: return BU * g.Hkv * (size_t)g.d * 2 * 2;
+    case QKV_EXPORT_VPARAMS: return BU * g.Hkv * (size_t)g.window * (g.d / g.group) * 2 * 2;
+    case QKV_EXPORT_KEYS:
+    case QKV_EXPORT_VALUES: return (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2;
+    default: return 0;
+  }
+}
+
+int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_stream stream) {
+  if (!c || !dst) return QKV_EINVAL;
+  const size_t need = qkv_export_bytes(c, what);
+  if (need == 0 || bytes != need) return QKV_EINVAL;
+  return hip_err(launch_export(c->g, c->st, what, dst, (hipStream_t)stream));
+}
+
+int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
+  if (!c || !value) return QKV_EINVAL;
+  switch (what) {
+    case QKV_INFO_TOKENS: *value = c->N; return QKV_OK;
+    case QKV_INFO_UNITS: *value = c->g.U; return QKV_OK;
+    case QKV_INFO_STEPS: *value = c->steps; return QKV_OK;
+    case QKV_INFO_ROUTES: *value = c->routes; return QKV_OK;
+    case QKV_INFO_SPLITS: *value = c->g.n_splits; return QKV_OK;
+    case QKV_INFO_WORKSPACE: *value = (int64_t)c->ws_bytes; return QKV_OK;
+    default: return QKV_EINVAL;
+  }
+}
+
+int qkv_status(qkv_cache *c, qkv_stream stream) {
+  if (!c) return QKV_EINVAL;
+  int32_t flag = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return QKV_EHIP;
+  if (hipMemcpy(&flag, c->st.status, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess) return QKV_EHIP;
+  return flag ? QKV_ERANGE : QKV_OK;
+}
+
+}  // extern "C"

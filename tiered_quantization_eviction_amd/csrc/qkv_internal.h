@@ -1,0 +1,160 @@
+// Internal geometry, device state and layout helpers of the qkv library.
+//
+// Memory layout in HBM (one workspace, carved at create time):
+//
+//   pages    bf16  [B][U][Hkv][tpw][2][TS*d]   full-precision content of every unit
+//                  (unit 0 = sink prefix, unit 1+j = window j), tiles of TS=16
+//                  token slots; K tiles and V tiles are stored in the order
+//                  the matrix-core operands are read (see k_tile_index /
+//                  v_tile_index), so each wavefront load is one contiguous block.
+//   ledger   u8    [B][U][Hkv][ledger_unit_bytes]  persistent quantized codes
+//                  of every window ever demoted (pack-once ledger).
+//   tier, has_ledger u8 [B][U]; score f32 [B][U]
+//   routed   i32   [B][U]  ranked unit ids: full-precision windows first, then
+//                  quantized windows (rank order); counts in routed_nf/nq.
+//   pack/promote lists i32 [B][U] + counts; attention partials; mass partials.
+//
+// Units are addressed by their stable window id; a window's position span is
+// fixed by its id, independent of its tier (the stable window <-> span map the
+// routing recurrence needs).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qkv.h"
+
+namespace qkv {
+
+constexpr int TS = 16;           // token slots per tile
+constexpr int WAVE = 64;
+constexpr int ATT_WAVES = 4;     // waves per attention workgroup
+constexpr int SORT_MAX = 8192;   // largest routing candidate set (LDS sort)
+
+enum : uint8_t { T_EMPTY = 0, T_SINK = 1, T_RECENT = 2, T_FULL = 3, T_QUANT = 4, T_EVICTED = 5 };
+
+struct Geom {
+  int B, Hq, Hkv, G, d;
+  int window, omega, n_sink, n_recent, k_full, k_quant, bits, group, max_ctx;
+  int U;                 // units per sequence
+  int tpw;               // tiles per unit
+  int n_splits;
+  // per (b,u,g) sizes
+  int page_unit_elems;   // bf16 elements: tpw * 2 * TS * d
+  int ledger_unit_bytes; // kparams + tpw * tile block
+  int kparam_bytes;      // s[d], z[d] fp16
+  int tile_kcode_bytes;  // TS * d / 4
+  int tile_vcode_bytes;
+  int tile_vparam_bytes; // 4 token quads * d/32 groups * 16 B
+  int tile_block_bytes;
+  // bytes one KV head reads for one unit (split balancing)
+  int cost_full, cost_quant;
+};
+
+struct State {
+  uint16_t *pages;
+  uint8_t *ledger;
+  uint8_t *tier;
+  uint8_t *has_ledger;
+  float *score;
+  int32_t *routed;
+  int32_t *routed_nf;
+  int32_t *routed_nq;
+  int32_t *pack_list;
+  int32_t *pack_count;
+  int32_t *promote_list;
+  int32_t *promote_count;
+  float *part_o;     // [B][Hkv][S][G][d]
+  float *part_ml;    // [B][Hkv][S][G][2]  (max in log2 units, sum)
+  float *mass_part;  // [B][Hkv][U+1][G][2] (partial mass, reference max)
+  int32_t *status;   // [4] latched device errors
+};
+
+// Per-step scalars the host knows without reading the device.
+struct StepInfo {
+  int N;        // tokens appended per sequence
+  int r0, r1;   // recent (not yet ranked) windows: units r0..r1 (r1 < r0: none)
+  int has_sink; // sink entry present
+};
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// position span of unit u
+__host__ __device__ inline int unit_start(const Geom &g, int u) { return u == 0 ? 0 : g.n_sink + (u - 1) * g.window; }
+__host__ __device__ inline int unit_len(const Geom &g, int u) { return u == 0 ? g.n_sink : g.window; }
+__host__ __device__ inline int unit_of(const Geom &g, int pos) {
+  return pos < g.n_sink ? 0 : 1 + (pos - g.n_sink) / g.window;
+}
+
+// Swizzled element index inside a K tile [TS tokens x d]: the A operand of a
+// 16x16x32 matrix op reads, for k-block kb, lane l = token + 16*q, the 8
+// channels kb*32 + 8q .. +7 -- stored as 16 contiguous bytes at (kb*64+l)*8.
+__host__ __device__ inline int k_tile_index(int t, int c) {
+  return ((c >> 5) * 64 + ((c & 31) >> 3) * 16 + t) * 8 + (c & 7);
+}
+// V tile: the B operand of a 16x16x16 op reads, for column tile ct, lane
+// l = (t/4)*16 + c%16 the 4 tokens 4q..4q+3 of channel c -- 8 contiguous bytes.
+__host__ __device__ inline int v_tile_index(int t, int c) {
+  return ((c >> 4) * 64 + (t >> 2) * 16 + (c & 15)) * 4 + (t & 3);
+}
+
+// Ledger code placement (2-bit codes, 16 per dword).
+// Keys: dword (j*64 + l) of a tile, j = kb/2, l = ((c%32)/8)*16 + t, pair
+// i = (kb%2)*4 + (c%8)/2, slot p = i + 8*(c%2): bits [2p, 2p+1].
+__host__ __device__ inline void kcode_slot(int t, int c, int &dword, int &shift) {
+  int kb = c >> 5, l = ((c & 31) >> 3) * 16 + t, e = c & 7;
+  int i = (kb & 1) * 4 + (e >> 1);
+  int p = i + 8 * (e & 1);
+  dword = (kb >> 1) * 64 + l;
+  shift = 2 * p;
+}
+// Values: dword (j*64 + l), j = ct/4, l = (t/4)*16 + c%16, pair
+// i = (ct%4)*2 + (t%4)/2, slot p = i + 8*(t%2).
+__host__ __device__ inline void vcode_slot(int t, int c, int &dword, int &shift) {
+  int ct = c >> 4, l = (t >> 2) * 16 + (c & 15);
+  int i = (ct & 3) * 2 + ((t & 3) >> 1);
+  int p = i + 8 * (t & 1);
+  dword = (ct >> 2) * 64 + l;
+  shift = 2 * p;
+}
+// V params of a tile: [token quad tq][group g][s x4, z x4] fp16
+__host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int which /*0 s,1 z*/) {
+  return ((t >> 2) * (g.d / 32) + grp) * 8 + which * 4 + (t & 3);
+}
+
+__host__ __device__ inline size_t page_offset(const Geom &g, int b, int u, int h) {
+  return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.page_unit_elems;
+}
+__host__ __device__ inline size_t ledger_offset(const Geom &g, int b, int u, int h) {
+  return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.ledger_unit_bytes;
+}
+
+// bf16 helpers
+__host__ __device__ inline float bf16_to_f32(uint16_t h) {
+  union { uint32_t u; float f; } x;
+  x.u = (uint32_t)h << 16;
+  return x.f;
+}
+__host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
+  union { uint32_t u; float f; } x;
+  x.f = f;
+  uint32_t lsb = (x.u >> 16) & 1u;
+  return (uint16_t)((x.u + 0x7FFFu + lsb) >> 16);
+}
+
+// ---- launchers (defined in qkv_kernels.hip) ----
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
+                         int pos0, hipStream_t s);
+hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
+                         float *mass_out, hipStream_t s);
+hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
+                        hipStream_t s);
+hipError_t launch_quantize_window(const void *x, int x_dtype, int n_blocks, int tokens, int d, int bits, int group,
+                                  int kind, uint8_t *codes, uint16_t *params, hipStream_t s);
+hipError_t launch_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int n,
+                             const int32_t *counts, int n_tiers, uint8_t *out, hipStream_t s);
+hipError_t launch_export(const Geom &g, const State &st, int what, void *dst, hipStream_t s);
+hipError_t read_quantize_status(int *flag, hipStream_t s);
+
+}  // namespace qkv

@@ -1,0 +1,1061 @@
+// HIP kernels of the tiered decode path for gfx950 (CDNA4).
+//
+// Decode attention (QEvict notes section 4.1, Eq. attention) runs split-K over
+// each (sequence, KV head): a workgroup of 4 waves streams a contiguous range
+// of live units; scores S^T = K Q^T and the output P V use 16x16 matrix-core
+// ops with the G query heads of the KV head as the narrow dimension.  Full
+// precision tiles feed bf16 operands straight from HBM; quantized tiles are
+// unpacked to exact fp16 integers in registers with the per-channel key scale
+// folded into the query (q' = q*s split into two fp16 limbs) and the
+// per-token value scale folded into the probabilities -- so no dequantized
+// tile is ever materialized.  Each wave keeps an online softmax and emits,
+// per unit, the head's partial mass with the reference maximum it is relative
+// to; the merge kernel normalizes those with the global (max, sum) and adds
+// them into the window scores (QEvict Eq.(1)) in a fixed order (no atomics).
+#include "qkv_internal.h"
+
+#include <math.h>
+
+namespace qkv {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ int g_quant_status;   // latched by the stateless quantizer
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__device__ inline floatx4 mfma_bf16_k32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_f16_k32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_bf16_k16(short4v a, short4v b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_f16_k16(half4 a, half4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// two 2-bit codes (slots i and i+8 of a dword) as an exact fp16 pair
+__device__ inline uint32_t code_pair_bits(uint32_t x, int i) {
+  return ((x >> (2 * i)) & 0x00030003u) | 0x64006400u;   // (1024 + c_lo, 1024 + c_hi)
+}
+__device__ inline half8 unpack8(uint32_t x, int i0) {
+  union { uint32_t u[4]; half8 h; } r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.u[k] = code_pair_bits(x, i0 + k);
+  const half8 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024,
+                     (half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
+  return r.h - off;
+}
+__device__ inline half4 unpack4(uint32_t x, int i0) {
+  union { uint32_t u[2]; half4 h; } r;
+  r.u[0] = code_pair_bits(x, i0);
+  r.u[1] = code_pair_bits(x, i0 + 1);
+  const half4 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
+  return r.h - off;
+}
+
+__device__ inline float neg_inf() { return -__builtin_inff(); }
+
+// uniform quantizer of one value (see the codec definition): code of x in a
+// group with float16 step s16 and zero z16
+__device__ inline uint32_t quant_code(float x, half_t s16, half_t z16, float levels) {
+  float s = (float)s16;
+  if (s == 0.0f) return 0u;
+  float r = (x - (float)z16) / s;
+  r = rintf(r);
+  r = fminf(fmaxf(r, 0.0f), levels);
+  return (uint32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+// fill
+// ---------------------------------------------------------------------------
+
+__global__ void fill_zero_kernel(uint32_t *p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  size_t words = bytes / 4;
+  int grid = (int)((words + 255) / 256);
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint32_t *)p, words);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// append: new positions into their unit's page (swizzled tiles)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void append_kernel(Geom g, State st, const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v, int n_tokens, int pos0) {
+  const int chunks = g.d / 8;
+  long long total = (long long)g.B * g.Hkv * n_tokens * chunks;
+  for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < total;
+       it += (long long)gridDim.x * blockDim.x) {
+    int ch = (int)(it % chunks);
+    long long r = it / chunks;
+    int tok = (int)(r % n_tokens);
+    r /= n_tokens;
+    int h = (int)(r % g.Hkv);
+    int b = (int)(r / g.Hkv);
+    int pos = pos0 + tok;
+    int u = unit_of(g, pos);
+    int slot = pos - unit_start(g, u);
+    int tile = slot / TS, t = slot % TS;
+    uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)tile * 2 * TS * g.d;
+    uint16_t *vt = kt + TS * g.d;
+    size_t src = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d + ch * 8;
+    uint4 kk = *(const uint4 *)(k + src);
+    int c0 = ch * 8;
+    *(uint4 *)(kt + k_tile_index(t, c0)) = kk;
+    const uint16_t *vs = v + src;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = vs[j];
+    if (h == 0 && ch == 0 && (slot == 0 || tok == 0)) st.tier[b * g.U + u] = (u == 0) ? T_SINK : T_RECENT;
+  }
+}
+
+hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
+                         int pos0, hipStream_t s) {
+  long long total = (long long)g.B * g.Hkv * n_tokens * (g.d / 8);
+  int grid = (int)((total + 255) / 256);
+  if (grid > 16384) grid = 16384;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(256), 0, s, g, st, k, v, n_tokens, pos0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// live-entry list of one sequence (sink, ranked full, ranked quantized, recent)
+// ---------------------------------------------------------------------------
+
+struct EntryList {
+  int s0, nF, nQ, nR, r0;
+  long long cF, cQ;
+  __device__ int count() const { return s0 + nF + nQ + nR; }
+  __device__ long long total_cost() const { return (long long)(s0 + nF + nR) * cF + (long long)nQ * cQ; }
+  // first entry whose cost-start is >= x
+  __device__ int first_at(long long x) const {
+    int E = count();
+    if (x <= 0) return 0;
+    long long A = s0 + nF;
+    if (x <= A * cF) return (int)((x + cF - 1) / cF);
+    long long x2 = x - A * cF;
+    if (x2 <= (long long)nQ * cQ) return (int)(A + (x2 + cQ - 1) / cQ);
+    long long x3 = x2 - (long long)nQ * cQ;
+    long long e = A + nQ + (x3 + cF - 1) / cF;
+    return (int)(e < E ? e : E);
+  }
+};
+
+__device__ inline EntryList make_list(const Geom &g, const State &st, const StepInfo &si, int b) {
+  EntryList L;
+  L.s0 = si.has_sink;
+  L.nF = st.routed_nf[b];
+  L.nQ = st.routed_nq[b];
+  L.nR = si.r1 >= si.r0 ? si.r1 - si.r0 + 1 : 0;
+  L.r0 = si.r0;
+  L.cF = g.cost_full;
+  L.cQ = g.cost_quant;
+  return L;
+}
+
+// entry -> unit, quantized?, valid tokens
+__device__ inline int entry_unit(const Geom &g, const State &st, const StepInfo &si, const EntryList &L, int b,
+                                 int e, bool &quant, int &n_valid) {
+  quant = false;
+  if (e < L.s0) {
+    n_valid = min(si.N, g.n_sink);
+    return 0;
+  }
+  int r = e - L.s0;
+  if (r < L.nF + L.nQ) {
+    quant = r >= L.nF;
+    n_valid = g.window;
+    return st.routed[b * g.U + r];
+  }
+  int u = L.r0 + (r - L.nF - L.nQ);
+  int rem = si.N - unit_start(g, u);
+  n_valid = rem < g.window ? rem : g.window;
+  return u;
+}
+
+// ---------------------------------------------------------------------------
+// attention: one workgroup per (sequence, KV head, split)
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct WaveState {
+  floatx4 acc[D / 16];   // output rows (head, limb) x columns of each 16-channel tile
+  floatx4 zacc;          // value-zero term per (row, channel group) of quantized tiles
+  float m;               // running max of this lane's column (log2 units)
+  float l;               // partial sum of probabilities over this lane's tokens
+};
+
+// online-softmax update for one 16-token tile of scores (C layout: lane holds
+// column col = lane%16, tokens 4*(lane/16)+i); returns probabilities in p[]
+template <int D>
+__device__ inline float softmax_tile(WaveState<D> &ws, floatx4 s, float sc, int n_valid, int lq, float &rho,
+                                     float p[4]) {
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (4 * lq + i < n_valid) ? s[i] * sc : neg_inf();
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float m_new = fmaxf(ws.m, mx);
+  bool grow = m_new > ws.m;
+  if (__any(grow)) {
+    float alpha = grow ? (ws.m == neg_inf() ? 0.0f : exp2f(ws.m - m_new)) : 1.0f;
+    ws.l *= alpha;
+    rho *= alpha;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i (= column of lane 4*lq+i)
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
+      ws.zacc[i] *= ar;
+    }
+    (void)lane;
+    ws.m = m_new;
+  }
+  float ts = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = (ws.m == neg_inf()) ? 0.0f : exp2f(x[i] - ws.m);
+    ts += p[i];
+  }
+  ws.l += ts;
+  ts += __shfl_xor(ts, 16);
+  ts += __shfl_xor(ts, 32);
+  rho += ts;
+  return ts;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, StepInfo si,
+                                                            const uint16_t *__restrict__ q, float scale_log2) {
+  constexpr int KB = D / 32;
+  constexpr int CT = D / 16;
+  const int S = g.n_splits;
+  const int split = blockIdx.x % S;
+  const int bh = blockIdx.x / S;
+  const int h = bh % g.Hkv;
+  const int b = bh / g.Hkv;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int lq = lane >> 4;
+  const int G = g.G;
+  const bool is_hi = col < G;
+  const bool is_lo = col >= G && col < 2 * G;
+  const int hc = is_hi ? col : (is_lo ? col - G : 0);
+
+  // ---- query operands (columns h and G+h both carry head h) ----
+  bf16x8 bq[KB];
+  half8 bqh[KB];
+  const uint16_t *qrow = q + ((size_t)b * g.Hq + (size_t)h * G + hc) * D;
+  float amax = 0.0f;
+  float qv[KB][8];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    uint4 raw = *(const uint4 *)(qrow + kb * 32 + lq * 8);
+    const uint16_t *e = (const uint16_t *)&raw;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = (is_hi || is_lo) ? bf16_to_f32(e[j]) : 0.0f;
+      qv[kb][j] = f;
+      amax = fmaxf(amax, fabsf(f));
+    }
+    union { uint4 u; bf16x8 v; } cv;
+    cv.u = (is_hi || is_lo) ? raw : make_uint4(0, 0, 0, 0);
+    bq[kb] = cv.v;
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int qexp = 0;
+  if (amax > 0.0f) frexpf(amax, &qexp);        // amax * 2^-qexp < 1
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bqh[kb][j] = (half_t)ldexpf(qv[kb][j], -qexp);
+  const float sc_full = scale_log2;
+  const float sc_quant = ldexpf(scale_log2, qexp);
+
+  // ---- this split's entry range ----
+  const EntryList L = make_list(g, st, si, b);
+  const long long C = L.total_cost();
+  const int e_begin = L.first_at(C * split / S);
+  const int e_end = L.first_at(C * (split + 1) / S);
+
+  WaveState<D> ws;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  ws.zacc = floatx4{0.f, 0.f, 0.f, 0.f};
+  ws.m = neg_inf();
+  ws.l = 0.0f;
+
+  float *mass_row = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1)) * G * 2;
+
+  for (int e = e_begin + wave; e < e_end; e += ATT_WAVES) {
+    bool quant;
+    int n_valid;
+    const int u = entry_unit(g, st, si, L, b, e, quant, n_valid);
+    float rho = 0.0f;
+    const int n_tiles = (n_valid + TS - 1) / TS;
+    if (!quant) {
+      const uint16_t *base = st.pages + page_offset(g, b, u, h);
+      for (int tile = 0; tile < n_tiles; ++tile) {
+        const uint16_t *kt = base + (size_t)tile * 2 * TS * D;
+        const uint16_t *vt = kt + TS * D;
+        floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          bf16x8 a = *(const bf16x8 *)(kt + (kb * 64 + lane) * 8);
+          s = mfma_bf16_k32(a, bq[kb], s);
+        }
+        float p[4];
+        softmax_tile<D>(ws, s, sc_full, n_valid - tile * TS, lq, rho, p);
+        short4v ap;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint16_t hi = f32_to_bf16_rne(p[i]);
+          uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
+          ap[i] = (short)(is_hi ? hi : (is_lo ? lo : (uint16_t)0));
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          short4v bv = *(const short4v *)(vt + (ct * 64 + lane) * 4);
+          ws.acc[ct] = mfma_bf16_k16(ap, bv, ws.acc[ct]);
+        }
+      }
+    } else {
+      const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+      const half_t *ks = (const half_t *)Lb;
+      const half_t *kz = ks + D;
+      half8 qhi[KB], qlo[KB], z8[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        half8 s8 = *(const half8 *)(ks + kb * 32 + lq * 8);
+        z8[kb] = *(const half8 *)(kz + kb * 32 + lq * 8);
+        qhi[kb] = bqh[kb] * s8;
+        qlo[kb] = __builtin_elementwise_fma(bqh[kb], s8, -qhi[kb]);   // exact remainder of q*s
+      }
+      for (int tile = 0; tile < n_tiles; ++tile) {
+        const uint8_t *T = Lb + g.kparam_bytes + (size_t)tile * g.tile_block_bytes;
+        const uint32_t *kc = (const uint32_t *)T;
+        const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
+        const half_t *vp = (const half_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes);
+        uint32_t kd[KB / 2], vd[D / 64];
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j) kd[j] = kc[j * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) vd[j] = vc[j * 64 + lane];
+        floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          half8 a = unpack8(kd[kb >> 1], (kb & 1) * 4);
+          s = mfma_f16_k32(a, qhi[kb], s);
+          s = mfma_f16_k32(a, qlo[kb], s);
+          s = mfma_f16_k32(z8[kb], bqh[kb], s);    // sum_c q_c z_c
+        }
+        float p[4];
+        softmax_tile<D>(ws, s, sc_quant, n_valid - tile * TS, lq, rho, p);
+        half4 phi, plo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          phi[i] = (half_t)p[i];
+          plo[i] = (half_t)(p[i] - (float)phi[i]);
+        }
+        const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+#pragma unroll
+        for (int grp = 0; grp < D / 32; ++grp) {
+          half4 s4 = *(const half4 *)(vp + (lq * (D / 32) + grp) * 8);
+          half4 th = phi * s4;
+          half4 tl = __builtin_elementwise_fma(phi, s4, -th);
+          tl = __builtin_elementwise_fma(plo, s4, tl);
+          half4 ag = is_hi ? th : (is_lo ? tl : zero4);
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const int ct = grp * 2 + c2;
+            half4 bc = unpack4(vd[ct >> 2], (ct & 3) * 2);
+            ws.acc[ct] = mfma_f16_k16(ag, bc, ws.acc[ct]);
+          }
+        }
+        half4 apz = is_hi ? phi : (is_lo ? plo : zero4);
+        half4 bz = zero4;
+        if (col < D / 32) bz = *(const half4 *)(vp + (lq * (D / 32) + col) * 8 + 4);
+        ws.zacc = mfma_f16_k16(apz, bz, ws.zacc);
+      }
+    }
+    // this unit's partial mass per head, relative to the current running max
+    if (lq == 0 && col < G) {
+      float *mp = mass_row + ((size_t)e * G + col) * 2;
+      mp[0] = rho;
+      mp[1] = ws.m;
+    }
+  }
+
+  // ---- wave epilogue: fold value-zero term and limbs ----
+  float l_tot = ws.l + __shfl_xor(ws.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl(ws.zacc[i], lq * 16 + (ct >> 1));
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl_down(ws.acc[ct][i], 4 * G);
+
+  // ---- workgroup merge ----
+  __shared__ float sm_m[ATT_WAVES][8];
+  __shared__ float sm_l[ATT_WAVES][8];
+  __shared__ float sm_o[ATT_WAVES][8][D];
+  if (lq == 0 && col < G) {
+    sm_m[wave][col] = ws.m;
+    sm_l[wave][col] = l_tot;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * lq + i;
+    if (r < G) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) sm_o[wave][r][ct * 16 + col] = ws.acc[ct][i];
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)(b * g.Hkv + h) * S + split) * G;
+  for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
+    const int hh = it / D, c = it % D;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w)
+      if (sm_m[w][hh] != neg_inf()) o += sm_o[w][hh][c] * exp2f(sm_m[w][hh] - M);
+    st.part_o[(pbase + hh) * D + c] = o;
+    if (c == 0) {
+      float l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < ATT_WAVES; ++w)
+        if (sm_m[w][hh] != neg_inf()) l += sm_l[w][hh] * exp2f(sm_m[w][hh] - M);
+      st.part_ml[(pbase + hh) * 2 + 0] = M;
+      st.part_ml[(pbase + hh) * 2 + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: outputs per (sequence, KV head); masses -> window scores per sequence
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, StepInfo si, float *__restrict__ out,
+                                                           float *__restrict__ mass_out, int n_chunks) {
+  const int S = g.n_splits, G = g.G, D = g.d;
+  const int n_out_blocks = g.B * g.Hkv;
+  __shared__ float sM[128], sInvL[128];   // Hkv*G = Hq <= 128
+  if ((int)blockIdx.x < n_out_blocks) {
+    const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
+    const size_t base = (size_t)(b * g.Hkv + h) * S;
+    for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
+      const int hh = it / D, c = it % D;
+      float M = neg_inf();
+      for (int s = 0; s < S; ++s) M = fmaxf(M, st.part_ml[((base + s) * G + hh) * 2]);
+      float l = 0.0f, o = 0.0f;
+      for (int s = 0; s < S; ++s) {
+        const float ms = st.part_ml[((base + s) * G + hh) * 2];
+        if (ms == neg_inf()) continue;
+        const float f = exp2f(ms - M);
+        l += st.part_ml[((base + s) * G + hh) * 2 + 1] * f;
+        o += st.part_o[((base + s) * G + hh) * D + c] * f;
+      }
+      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o / l;
+    }
+    return;
+  }
+  // mass chunk
+  const int mb = blockIdx.x - n_out_blocks;
+  const int b = mb / n_chunks, chunk = mb % n_chunks;
+  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) {
+    const int h = it / G, hh = it % G;
+    const size_t base = (size_t)(b * g.Hkv + h) * S;
+    float M = neg_inf();
+    for (int s = 0; s < S; ++s) M = fmaxf(M, st.part_ml[((base + s) * G + hh) * 2]);
+    float l = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = st.part_ml[((base + s) * G + hh) * 2];
+      if (ms != neg_inf()) l += st.part_ml[((base + s) * G + hh) * 2 + 1] * exp2f(ms - M);
+    }
+    sM[it] = M;
+    sInvL[it] = 1.0f / l;
+  }
+  __syncthreads();
+  const EntryList L = make_list(g, st, si, b);
+  const int E = L.count();
+  const int e = chunk * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  bool quant;
+  int n_valid;
+  const int u = entry_unit(g, st, si, L, b, e, quant, n_valid);
+  float total = 0.0f;
+  for (int h = 0; h < g.Hkv; ++h) {
+    const float *mp = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1) + e) * G * 2;
+    float gs = 0.0f;
+    for (int hh = 0; hh < G; ++hh) {
+      const float rho = mp[hh * 2], ms = mp[hh * 2 + 1];
+      float v = (ms == neg_inf()) ? 0.0f : rho * exp2f(ms - sM[h * G + hh]) * sInvL[h * G + hh];
+      if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's mass below FLT_MIN counts as 0
+      gs += v;
+    }
+    if (mass_out) mass_out[((size_t)b * g.Hkv + h) * g.U + u] = gs;
+    total += gs;
+  }
+  st.score[b * g.U + u] += total;
+}
+
+hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
+                         float *mass_out, hipStream_t s) {
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+  const int grid = g.B * g.Hkv * g.n_splits;
+  if (g.d == 128)
+    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
+  else
+    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mass_out) {
+    e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.U * sizeof(float), s);
+    if (e != hipSuccess) return e;
+  }
+  const int n_chunks = (g.U + 1 + 255) / 256;
+  hipLaunchKernelGGL(merge_qevict_kernel, dim3(g.B * g.Hkv + g.B * n_chunks), dim3(256), 0, s, g, st, si, out,
+                     mass_out, n_chunks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// routing event: rank candidates per sequence in LDS (bitonic), assign tiers
+// ---------------------------------------------------------------------------
+
+__device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = keys[i], c = keys[ixj];
+          const bool desc = (i & k) == 0;
+          if ((a < c) == desc) {
+            keys[i] = c;
+            keys[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, int a0, int a1, int npow) {
+  extern __shared__ unsigned long long keys[];
+  __shared__ int n_pack, n_prom;
+  const int b = blockIdx.x;
+  const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
+  const int RC = nF + nQ;
+  const int n = RC + (a1 > a0 ? a1 - a0 : 0);
+  if (threadIdx.x == 0) {
+    n_pack = 0;
+    n_prom = 0;
+  }
+  for (int i = threadIdx.x; i < npow; i += blockDim.x) {
+    unsigned long long key = 0ull;
+    if (i < n) {
+      const int u = i < RC ? st.routed[b * g.U + i] : a0 + (i - RC);
+      const uint32_t sb = __float_as_uint(st.score[b * g.U + u]);    // scores are >= 0: bits are monotone
+      key = ((unsigned long long)sb << 32) | (unsigned long long)(uint32_t)(unit_start(g, u) + 1);
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  bitonic_desc_u64(keys, npow);
+  const int KFQ = g.k_full + g.k_quant;
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    const int start = (int)(uint32_t)(keys[r] & 0xffffffffull) - 1;
+    const int u = unit_of(g, start);
+    const int idx = b * g.U + u;
+    const uint8_t old = st.tier[idx];
+    const uint8_t nt = r < g.k_full ? T_FULL : (r < KFQ ? T_QUANT : T_EVICTED);
+    if (nt == T_QUANT && !st.has_ledger[idx]) {
+      const int p = atomicAdd(&n_pack, 1);
+      st.pack_list[b * g.U + p] = u;
+      st.has_ledger[idx] = 1;
+    }
+    if (nt == T_FULL && old == T_QUANT) {
+      const int p = atomicAdd(&n_prom, 1);
+      st.promote_list[b * g.U + p] = u;
+    }
+    if (nt == T_EVICTED) st.has_ledger[idx] = 0;
+    st.tier[idx] = nt;
+    if (r < KFQ) st.routed[b * g.U + r] = u;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    st.routed_nf[b] = min(n, g.k_full);
+    st.routed_nq[b] = max(0, min(n - g.k_full, g.k_quant));
+    st.pack_count[b] = n_pack;
+    st.promote_count[b] = n_prom;
+  }
+}
+
+// pack (first demotion) and promote (quantized -> full) of listed windows
+template <int D>
+__global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State st, int per_seq) {
+  __shared__ float sk[32][D];
+  __shared__ float sv[32][D];
+  __shared__ half_t s_ks[D], s_kz[D];
+  __shared__ half_t s_vs[32][D / 32], s_vz[32][D / 32];
+  const int b = blockIdx.x / per_seq;
+  const int w0 = blockIdx.x % per_seq;
+  const int npk = st.pack_count[b];
+  const int npr = st.promote_count[b];
+  const int items = (npk + npr) * g.Hkv;
+  const int W = g.window;
+  const float levels = 3.0f;
+  for (int it = w0; it < items; it += per_seq) {
+    const int i = it / g.Hkv, h = it % g.Hkv;
+    const bool pack = i < npk;
+    const int u = pack ? st.pack_list[b * g.U + i] : st.promote_list[b * g.U + (i - npk)];
+    uint16_t *pg = st.pages + page_offset(g, b, u, h);
+    uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+    half_t *kparam = (half_t *)Lb;
+    if (pack) {
+      // 1. tiles -> LDS in logical order
+      for (int tile = 0; tile < g.tpw; ++tile) {
+        const uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
+        const uint16_t *vt = kt + TS * D;
+        for (int ci = threadIdx.x; ci < TS * D / 8; ci += blockDim.x) {
+          const int kb = ci / 64, l = ci % 64;
+          const int t = l % 16, c0 = kb * 32 + (l / 16) * 8;
+          const uint16_t *src = kt + ci * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sk[tile * TS + t][c0 + j] = bf16_to_f32(src[j]);
+        }
+        for (int ci = threadIdx.x; ci < TS * D / 4; ci += blockDim.x) {
+          const int ct = ci / 64, l = ci % 64;
+          const int c = ct * 16 + l % 16, t0 = (l / 16) * 4;
+          const uint16_t *src = vt + ci * 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[tile * TS + t0 + j][c] = bf16_to_f32(src[j]);
+        }
+      }
+      __syncthreads();
+      // 2. key parameters per channel over the window's tokens
+      for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        float mn = sk[0][c], mx = sk[0][c];
+        for (int t = 1; t < W; ++t) {
+          mn = fminf(mn, sk[t][c]);
+          mx = fmaxf(mx, sk[t][c]);
+        }
+        const half_t s16 = (half_t)((mx - mn) / levels);
+        const half_t z16 = (half_t)mn;
+        if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
+        s_ks[c] = s16;
+        s_kz[c] = z16;
+        kparam[c] = s16;
+        kparam[D + c] = z16;
+      }
+      // value parameters per token per 32-channel group
+      for (int it2 = threadIdx.x; it2 < W * (D / 32); it2 += blockDim.x) {
+        const int t = it2 / (D / 32), grp = it2 % (D / 32);
+        float mn = sv[t][grp * 32], mx = mn;
+        for (int c = 1; c < 32; ++c) {
+          mn = fminf(mn, sv[t][grp * 32 + c]);
+          mx = fmaxf(mx, sv[t][grp * 32 + c]);
+        }
+        const half_t s16 = (half_t)((mx - mn) / levels);
+        const half_t z16 = (half_t)mn;
+        if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
+        s_vs[t][grp] = s16;
+        s_vz[t][grp] = z16;
+        half_t *vp = (half_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes + g.tile_kcode_bytes +
+                                g.tile_vcode_bytes);
+        vp[vparam_index(g, t % TS, grp, 0)] = s16;
+        vp[vparam_index(g, t % TS, grp, 1)] = z16;
+      }
+      __syncthreads();
+      // 3. codes in the matrix-core operand order
+      for (int tile = 0; tile < g.tpw; ++tile) {
+        uint32_t *kc = (uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes);
+        uint32_t *vc = (uint32_t *)((uint8_t *)kc + g.tile_kcode_bytes);
+        for (int dw = threadIdx.x; dw < (D / 64) * 64; dw += blockDim.x) {
+          const int j = dw / 64, l = dw % 64;
+          uint32_t kword = 0u, vword = 0u;
+#pragma unroll
+          for (int p = 0; p < 16; ++p) {
+            const int i = p & 7, hi = p >> 3;
+            // key slot p: pair i of k-blocks 2j, 2j+1
+            {
+              const int kb = 2 * j + (i >> 2), e = 2 * (i & 3) + hi;
+              const int c = kb * 32 + (l / 16) * 8 + e, t = l % 16;
+              const int tt = tile * TS + t;
+              uint32_t code = tt < W ? quant_code(sk[tt][c], s_ks[c], s_kz[c], levels) : 0u;
+              kword |= code << (2 * p);
+            }
+            // value slot p: pair i of column tiles 4j..4j+3
+            {
+              const int ct = 4 * j + (i >> 1);
+              const int t = 4 * (l / 16) + 2 * (i & 1) + hi, c = ct * 16 + l % 16;
+              const int tt = tile * TS + t;
+              uint32_t code = tt < W ? quant_code(sv[tt][c], s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u;
+              vword |= code << (2 * p);
+            }
+          }
+          kc[dw] = kword;
+          vc[dw] = vword;
+        }
+      }
+      __syncthreads();
+    } else {
+      // promote: rebuild the full-precision tiles from the ledger
+      for (int tile = 0; tile < g.tpw; ++tile) {
+        const uint8_t *T = Lb + g.kparam_bytes + tile * g.tile_block_bytes;
+        const uint32_t *kc = (const uint32_t *)T;
+        const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
+        const half_t *vp = (const half_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes);
+        uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
+        uint16_t *vt = kt + TS * D;
+        for (int el = threadIdx.x; el < TS * D; el += blockDim.x) {
+          const int t = el / D, c = el % D;
+          int dw, sh;
+          kcode_slot(t, c, dw, sh);
+          const float kcode = (float)((kc[dw] >> sh) & 3u);
+          const float kx = __builtin_fmaf(kcode, (float)kparam[c], (float)kparam[D + c]);
+          kt[k_tile_index(t, c)] = f32_to_bf16_rne(kx);
+          vcode_slot(t, c, dw, sh);
+          const float vcode = (float)((vc[dw] >> sh) & 3u);
+          const float vx = __builtin_fmaf(vcode, (float)vp[vparam_index(g, t, c / 32, 0)],
+                                          (float)vp[vparam_index(g, t, c / 32, 1)]);
+          vt[v_tile_index(t, c)] = f32_to_bf16_rne(vx);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
+                        hipStream_t s) {
+  (void)si;
+  int bound = n_cand > 1 ? n_cand : 1;   // ranked windows + newly aged windows (same for every sequence)
+  int npow = 1;
+  while (npow < bound) npow <<= 1;
+  if (npow > SORT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_qevict_kernel, dim3(g.B), dim3(1024), npow * sizeof(unsigned long long), s, g, st, a0,
+                     a1, npow);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per_seq = 128;
+  if (g.d == 128)
+    hipLaunchKernelGGL(transitions_qevict_kernel<128>, dim3(g.B * per_seq), dim3(256), 0, s, g, st, per_seq);
+  else
+    hipLaunchKernelGGL(transitions_qevict_kernel<64>, dim3(g.B * per_seq), dim3(256), 0, s, g, st, per_seq);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// stateless quantizer (canonical layout)
+// ---------------------------------------------------------------------------
+
+__device__ inline float load_x(const void *x, int dtype, size_t i) {
+  return dtype == QKV_DTYPE_F32 ? ((const float *)x)[i] : bf16_to_f32(((const uint16_t *)x)[i]);
+}
+
+__global__ __launch_bounds__(256) void quantize_window_kernel(const void *__restrict__ x, int dtype, int n_blocks,
+                                                              int tokens, int D, int bits, int group, int kind,
+                                                              uint8_t *__restrict__ codes,
+                                                              uint16_t *__restrict__ params) {
+  const int per_byte = 8 / bits;
+  const float levels = (float)((1 << bits) - 1);
+  const size_t block_elems = (size_t)tokens * D;
+  const size_t block_code_bytes = (block_elems * bits + 7) / 8;
+  long long n_groups;
+  int n_chunks = (tokens + group - 1) / group;
+  if (kind == QKV_KIND_K_PER_CHANNEL) n_groups = (long long)D * n_chunks;
+  else if (kind == QKV_KIND_PER_TOKEN) n_groups = (long long)tokens * (D / group);
+  else n_groups = tokens;
+  const long long total = n_groups * n_blocks;
+  for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < total;
+       it += (long long)gridDim.x * blockDim.x) {
+    const int blk = (int)(it / n_groups);
+    const long long gi = it % n_groups;
+    const size_t xb = (size_t)blk * block_elems;
+    uint8_t *cb = codes + (size_t)blk * block_code_bytes;
+    if (kind == QKV_KIND_K_PER_CHANNEL) {
+      const int c = (int)(gi / n_chunks), ch = (int)(gi % n_chunks);
+      const int t0 = ch * group, t1 = min(tokens, t0 + group);
+      float mn = load_x(x, dtype, xb + (size_t)t0 * D + c), mx = mn;
+      for (int t = t0 + 1; t < t1; ++t) {
+        const float v = load_x(x, dtype, xb + (size_t)t * D + c);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      const half_t s16 = (half_t)((mx - mn) / levels), z16 = (half_t)mn;
+      if (!isfinite((float)s16) || !isfinite((float)z16)) g_quant_status = QKV_ERANGE;
+      uint16_t *pp = params + (((size_t)blk * D + c) * n_chunks + ch) * 2;
+      pp[0] = __builtin_bit_cast(uint16_t, s16);
+      pp[1] = __builtin_bit_cast(uint16_t, z16);
+      for (int t = t0; t < t1; t += per_byte) {
+        uint32_t byte = 0;
+        for (int k = 0; k < per_byte && t + k < t1; ++k)
+          byte |= quant_code(load_x(x, dtype, xb + (size_t)(t + k) * D + c), s16, z16, levels) << (bits * k);
+        cb[((size_t)c * tokens + t) / per_byte] = (uint8_t)byte;
+      }
+    } else if (kind == QKV_KIND_PER_TOKEN) {
+      const int t = (int)(gi / (D / group)), grp = (int)(gi % (D / group));
+      const size_t row = xb + (size_t)t * D + (size_t)grp * group;
+      float mn = load_x(x, dtype, row), mx = mn;
+      for (int c = 1; c < group; ++c) {
+        const float v = load_x(x, dtype, row + c);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      const half_t s16 = (half_t)((mx - mn) / levels), z16 = (half_t)mn;
+      if (!isfinite((float)s16) || !isfinite((float)z16)) g_quant_status = QKV_ERANGE;
+      uint16_t *pp = params + (((size_t)blk * tokens + t) * (D / group) + grp) * 2;
+      pp[0] = __builtin_bit_cast(uint16_t, s16);
+      pp[1] = __builtin_bit_cast(uint16_t, z16);
+      for (int c = 0; c < group; c += per_byte) {
+        uint32_t byte = 0;
+        for (int k = 0; k < per_byte; ++k) byte |= quant_code(load_x(x, dtype, row + c + k), s16, z16, levels) << (bits * k);
+        cb[((size_t)t * D + grp * group + c) / per_byte] = (uint8_t)byte;
+      }
+    } else {
+      const int t = (int)gi;
+      const size_t row = xb + (size_t)t * D;
+      double sum = 0.0;
+      for (int c = 0; c < D; ++c) sum += (double)load_x(x, dtype, row + c);
+      const float m32 = (float)(sum / D);
+      double ss = 0.0;
+      for (int c = 0; c < D; ++c) {
+        const double dv = (double)load_x(x, dtype, row + c) - (double)m32;
+        ss += dv * dv;
+      }
+      const float sd32 = (float)sqrt(ss / D);
+      const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
+      if (!isfinite((float)m16) || !isfinite((float)sd16)) g_quant_status = QKV_ERANGE;
+      uint16_t *pp = params + ((size_t)blk * tokens + t) * 2;
+      pp[0] = __builtin_bit_cast(uint16_t, m16);
+      pp[1] = __builtin_bit_cast(uint16_t, sd16);
+      for (int c = 0; c < D; c += 8) {
+        uint32_t byte = 0;
+        for (int k = 0; k < 8; ++k) byte |= (load_x(x, dtype, row + c + k) > m32 ? 1u : 0u) << k;
+        cb[((size_t)t * D + c) / 8] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_window(const void *x, int x_dtype, int n_blocks, int tokens, int d, int bits, int group,
+                                  int kind, uint8_t *codes, uint16_t *params, hipStream_t s) {
+  long long groups = kind == QKV_KIND_K_PER_CHANNEL ? (long long)d * ((tokens + group - 1) / group)
+                     : kind == QKV_KIND_PER_TOKEN ? (long long)tokens * (d / group)
+                                                  : (long long)tokens;
+  long long total = groups * n_blocks;
+  int grid = (int)((total + 255) / 256);
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(quantize_window_kernel, dim3(grid), dim3(256), 0, s, x, x_dtype, n_blocks, tokens, d, bits,
+                     group, kind, codes, params);
+  return hipGetLastError();
+}
+
+hipError_t read_quantize_status(int *flag, hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(flag, HIP_SYMBOL(g_quant_status), sizeof(int), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_quant_status), &zero, sizeof(int), 0, hipMemcpyHostToDevice);
+}
+
+// ---------------------------------------------------------------------------
+// stateless multi-tier ranking
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void rank_tiers_kernel(const float *__restrict__ score,
+                                                          const int32_t *__restrict__ pos,
+                                                          const uint8_t *__restrict__ eligible, int n,
+                                                          const int32_t *__restrict__ counts, int n_tiers,
+                                                          uint8_t *__restrict__ out, int npow) {
+  extern __shared__ unsigned long long smem[];
+  unsigned long long *keys = smem;                // (score, pos) order key
+  int *idx = (int *)(smem + npow);
+  __shared__ int n_elig;
+  if (threadIdx.x == 0) n_elig = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    out[i] = 255;
+    if (eligible[i]) atomicAdd(&n_elig, 1);
+  }
+  // ordered-integer images of (score, pos); padding sorts last
+  for (int i = threadIdx.x; i < npow; i += blockDim.x) {
+    unsigned long long key = 0ull;
+    int id = -1;
+    if (i < n && eligible[i]) {
+      uint32_t sb = __float_as_uint(score[i]);
+      sb = (sb & 0x80000000u) ? ~sb : (sb | 0x80000000u);
+      const uint32_t pb = (uint32_t)pos[i] ^ 0x80000000u;
+      key = ((unsigned long long)sb << 32) | pb;
+      id = i;
+    }
+    keys[i] = key;
+    idx[i] = id;
+  }
+  __syncthreads();
+  // bitonic sort of (key, idx), key descending; padding (key 0) sorts last:
+  // a real key is never 0 (its score image or position image is non-zero)
+  for (int k = 2; k <= npow; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < npow; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = keys[i], c = keys[ixj];
+          const bool desc = (i & k) == 0;
+          if ((a < c) == desc && a != c) {
+            keys[i] = c;
+            keys[ixj] = a;
+            const int t = idx[i];
+            idx[i] = idx[ixj];
+            idx[ixj] = t;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const int ne = n_elig;
+  for (int r = threadIdx.x; r < ne; r += blockDim.x) {
+    int t = 0, acc = 0;
+    while (t < n_tiers && r >= acc + counts[t]) {
+      acc += counts[t];
+      ++t;
+    }
+    out[idx[r]] = (uint8_t)t;
+  }
+}
+
+hipError_t launch_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int n,
+                             const int32_t *counts, int n_tiers, uint8_t *out, hipStream_t s) {
+  int npow = 1;
+  while (npow < n) npow <<= 1;
+  size_t lds = (size_t)npow * (sizeof(unsigned long long) + sizeof(int));
+  hipLaunchKernelGGL(rank_tiers_kernel, dim3(1), dim3(1024), lds, s, score, pos, eligible, n, counts, n_tiers, out,
+                     npow);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// export in canonical layouts
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what, void *dst) {
+  const int W = g.window, D = g.d;
+  const size_t n_units = (size_t)g.B * g.U * g.Hkv;
+  if (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) {
+    const int bytes_per = W * D / 4;
+    const size_t total = n_units * bytes_per;
+    for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
+      const size_t blk = it / bytes_per;
+      const int byte = (int)(it % bytes_per);
+      const int h = (int)(blk % g.Hkv);
+      const int u = (int)((blk / g.Hkv) % g.U);
+      const int b = (int)(blk / ((size_t)g.Hkv * g.U));
+      uint32_t val = 0;
+      if (st.has_ledger[b * g.U + u]) {
+        const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+        for (int k = 0; k < 4; ++k) {
+          const int e = byte * 4 + k;
+          int t, c, dw, sh;
+          if (what == QKV_EXPORT_KCODES) {
+            c = e / W;
+            t = e % W;
+            kcode_slot(t % TS, c, dw, sh);
+            const uint32_t *kc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
+            val |= ((kc[dw] >> sh) & 3u) << (2 * k);
+          } else {
+            t = e / D;
+            c = e % D;
+            vcode_slot(t % TS, c, dw, sh);
+            const uint32_t *vc =
+                (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes + g.tile_kcode_bytes);
+            val |= ((vc[dw] >> sh) & 3u) << (2 * k);
+          }
+        }
+      }
+      ((uint8_t *)dst)[it] = (uint8_t)val;
+    }
+  } else if (what == QKV_EXPORT_KPARAMS || what == QKV_EXPORT_VPARAMS) {
+    const int per = what == QKV_EXPORT_KPARAMS ? D * 2 : W * (D / 32) * 2;
+    const size_t total = n_units * per;
+    for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
+      const size_t blk = it / per;
+      const int k = (int)(it % per);
+      const int h = (int)(blk % g.Hkv);
+      const int u = (int)((blk / g.Hkv) % g.U);
+      const int b = (int)(blk / ((size_t)g.Hkv * g.U));
+      uint16_t val = 0;
+      if (st.has_ledger[b * g.U + u]) {
+        const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+        if (what == QKV_EXPORT_KPARAMS) {
+          const int c = k / 2, which = k % 2;
+          val = ((const uint16_t *)Lb)[which * D + c];
+        } else {
+          const int which = k % 2, grp = (k / 2) % (D / 32), t = k / 2 / (D / 32);
+          const uint16_t *vp = (const uint16_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes +
+                                                  g.tile_kcode_bytes + g.tile_vcode_bytes);
+          val = vp[vparam_index(g, t % TS, grp, which)];
+        }
+      }
+      ((uint16_t *)dst)[it] = val;
+    }
+  } else {   // KEYS / VALUES
+    const size_t total = (size_t)g.B * g.Hkv * g.max_ctx * D;
+    for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
+      const int c = (int)(it % D);
+      const int pos = (int)((it / D) % g.max_ctx);
+      const int h = (int)((it / ((size_t)D * g.max_ctx)) % g.Hkv);
+      const int b = (int)(it / ((size_t)D * g.max_ctx * g.Hkv));
+      const int u = unit_of(g, pos);
+      const int slot = pos - unit_start(g, u);
+      const uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)(slot / TS) * 2 * TS * D;
+      const int t = slot % TS;
+      ((uint16_t *)dst)[it] = what == QKV_EXPORT_KEYS ? kt[k_tile_index(t, c)] : kt[TS * D + v_tile_index(t, c)];
+    }
+  }
+}
+
+hipError_t launch_export(const Geom &g, const State &st, int what, void *dst, hipStream_t s) {
+  if (what == QKV_EXPORT_TIERS)
+    return hipMemcpyAsync(dst, st.tier, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
+  if (what == QKV_EXPORT_SCORES)
+    return hipMemcpyAsync(dst, st.score, (size_t)g.B * g.U * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (what == QKV_EXPORT_LEDGER)
+    return hipMemcpyAsync(dst, st.has_ledger, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
+  hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, s, g, st, what, dst);
+  return hipGetLastError();
+}
+
+}  // namespace qkv
