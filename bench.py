@@ -1,0 +1,275 @@
+"""Decode benchmark of the tiered KV-cache path on one MI355X.
+
+Workload: the QEvict three-tier attention-drift layer -- batch 16, 32K-token
+prompt, H_q = 32, H_kv = 8, d = 128, 16-token windows routed every 16 steps,
+5 sinks + 64 recent tokens, K_f = 204 full-precision and K_q = 612 INT2 windows,
+512 decode steps (synthetic inputs, resident in HBM before timing).
+
+A step is one decode step of the whole path for the batch: append the new
+token, attention with fused mass emission and score accumulation, and -- every
+Omega steps -- the routing event (rank, pack, promote, evict).  The timed
+region is K consecutive decode steps starting right after the prompt (so it
+contains the heavy all-BF16 phase before the first routing event and every
+routing event); W warm-up steps run first on a separate cache.
+
+Prints one JSON line.  --gpus N with N > 1 is refused: this build measures
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", "qkv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+
+def _gen(args):
+    cfg, b = args
+    wl = W.Workload(cfg)
+    k, v = wl.kv(b)
+    return k, v, wl.queries(b)
+
+
+def make_inputs(cfg):
+    """K, V [B, Hkv, T, d], Q [B, steps, Hq, d] as bf16 bit patterns."""
+    from concurrent.futures import ProcessPoolExecutor
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), cfg.batch))
+    if workers > 1:
+        import multiprocessing as mp
+        with ProcessPoolExecutor(workers, mp_context=mp.get_context("fork")) as ex:
+            res = list(ex.map(_gen, [(cfg, b) for b in range(cfg.batch)]))
+    else:
+        res = [_gen((cfg, b)) for b in range(cfg.batch)]
+    return (np.stack([r[0] for r in res]), np.stack([r[1] for r in res]), np.stack([r[2] for r in res]))
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes of the live cache per step (what one attention launch must read)
+# ---------------------------------------------------------------------------
+
+def live_schedule(cfg, steps):
+    """Per decode step: (bf16 tokens per KV head, quantized windows per KV
+    head) of the live set, following the routing schedule (the counts are the
+    same for every sequence)."""
+    P, w, ns, nr = cfg.prefill, cfg.window, cfg.n_sink, cfg.n_recent
+    unit_of = lambda pos: 0 if pos < ns else 1 + (pos - ns) // w
+    start = lambda u: 0 if u == 0 else ns + (u - 1) * w
+    N, r0, nF, nQ = P, 1, 0, 0
+    out = []
+    for s in range(steps):
+        N += 1
+        r1 = unit_of(N - 1) if N > ns else 0
+        recent_tok = max(0, N - start(r0)) if r1 >= r0 else 0
+        out.append((min(N, ns) + nF * w + recent_tok, nQ))
+        if (s + 1) % cfg.omega == 0:
+            limit = N - nr
+            aged = (limit - ns) // w if limit > ns else 0
+            a1 = max(r0, aged + 1)
+            n_cand = nF + nQ + (a1 - r0)
+            nF, nQ = min(n_cand, cfg.k_full), min(max(n_cand - cfg.k_full, 0), cfg.k_quant)
+            r0 = a1
+    return out
+
+
+def quant_window_bytes(cfg):
+    w, d = cfg.window, cfg.head_dim
+    return 2 * w * d * cfg.quant_bits // 8 + d * 4 * -(-w // 32) + w * (d // 32) * 4
+
+
+def attend_bytes(cfg, sched):
+    """Algorithmic bytes per attention launch: every live BF16 token (K and V,
+    2 bytes each) and every quantized window's codes + parameters, per KV head,
+    plus the bf16 queries."""
+    per = []
+    for bf_tok, nq in sched:
+        kv = cfg.batch * cfg.n_kv_heads * (bf_tok * cfg.head_dim * 4 + nq * quant_window_bytes(cfg))
+        per.append(kv + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2)
+    return per
+
+
+# ---------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------
+
+def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
+    import torch
+    from tiered_quantization_eviction_amd import Cache, make_config
+    P = cfg.prefill
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    k_pre = dev(K[:, :, :P])
+    v_pre = dev(V[:, :, :P])
+    k_dec = dev(np.ascontiguousarray(K[:, :, P:].transpose(2, 0, 1, 3))[:, :, :, None, :])   # [S, B, Hkv, 1, d]
+    v_dec = dev(np.ascontiguousarray(V[:, :, P:].transpose(2, 0, 1, 3))[:, :, :, None, :])
+    q_dec = dev(np.ascontiguousarray(Q.transpose(1, 0, 2, 3)))                             # [S, B, Hq, d]
+    out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    conf = make_config(cfg, n_splits=n_splits)
+
+    def loop(cache, n, record=None):
+        for s in range(n):
+            cache.append(k_dec[s], v_dec[s])
+            cache.decode_attend(q_dec[s], out)
+            if (s + 1) % cfg.omega == 0:
+                cache.route()
+            if record is not None:
+                record.append(out.clone())
+
+    # warm-up on its own cache; keep its first outputs for the parity spot check
+    firsts = []
+    if warmup > 0:
+        cw = Cache(conf)
+        cw.append(k_pre, v_pre)
+        loop(cw, min(warmup, cfg.steps), firsts)
+        torch.cuda.synchronize()
+        cw.close()
+        del cw
+    cache = Cache(conf)
+    cache.append(k_pre, v_pre)
+    cache.profile_start(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop(cache, steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attend_ms = cache.profile_read(steps)
+    splits = cache.info("splits")
+    status = cache.status()
+    return (t1 - t0), attend_ms, [f[0].cpu().numpy() for f in firsts], splits, status
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(cfg, K, V, Q, sample_steps, firsts):
+    from oracle import qevict as oe
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    seq = oe.QEvictSequence(K[0], V[0], window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
+                            n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits,
+                            group=cfg.group, n_q_heads=cfg.n_q_heads)
+    seq.prefill(cfg.prefill)
+    worst = 0.0
+    t0 = time.perf_counter()
+    outs = []
+    for s in range(sample_steps):
+        o, _ = seq.step(s, Q[0, s])
+        outs.append(o)
+    dt = time.perf_counter() - t0
+    for s, o in enumerate(outs[:len(firsts)]):
+        worst = max(worst, float(np.abs(firsts[s] - o).max()))
+    return {"value": sample_steps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequence 0 of 16, decode steps 0..{sample_steps - 1} (incl. {sample_steps // cfg.omega} "
+                      f"routing events), float64 numpy on the host; {dt:.1f} s"}, worst
+
+
+def read_traffic(src_hash):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = t = None
+    for ln in txt.splitlines():
+        if ln.startswith("kernel_source_sha256:"):
+            h = ln.split(":", 1)[1].strip()
+        if ln.startswith("traffic_bytes_per_launch:"):
+            t = float(ln.split(":", 1)[1].strip())
+    return t if (h == src_hash and t is not None) else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--cpu-steps", type=int, default=256)
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
+              f"(the multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
+        sys.exit(2)
+    cfg = W.DRIFT
+    steps = min(a.steps, cfg.steps)
+    log(f"bench: generating inputs ({cfg.batch} x {cfg.total_tokens} tokens)")
+    t = time.perf_counter()
+    K, V, Q = make_inputs(cfg)
+    log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running {a.warmup} warm-up + {steps} timed steps")
+    wall, attend_ms, firsts, splits, status = run_gpu(cfg, K, V, Q, steps, a.warmup, a.splits)
+    if status != 0:
+        log(f"bench: device status {status}")
+    sched = live_schedule(cfg, steps)
+    abytes = attend_bytes(cfg, sched)
+    kv_bytes = sum(abytes)
+    tok_s = cfg.batch * steps / wall
+    att_avg_s = float(np.mean(attend_ms)) / 1e3
+    achieved = (kv_bytes / steps) / att_avg_s / 1e9
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    traffic = read_traffic(src_hash)
+    log(f"bench: {wall * 1e3:.1f} ms for {steps} steps; attention avg {att_avg_s * 1e6:.1f} us, "
+        f"{achieved:.0f} GB/s algorithmic")
+    cpu = None
+    worst = None
+    if not a.no_cpu:
+        log(f"bench: oracle baseline on {a.cpu_steps} steps of one sequence")
+        cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_steps, firsts)
+    res = {
+        "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": a.warmup,
+        "ms_per_step": wall * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+int2 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "QEvict three-tier attention drift: batch 16, 32768-token prompt + 512 decode steps, "
+                               "Hq=32 Hkv=8 d=128, window=Omega=16, 5 sinks + 64 recent, Kf=204 BF16 + Kq=612 INT2 "
+                               "windows (group 32), clusters A->B switch at step 100",
+                   "global_batch": cfg.batch, "seq_len": cfg.total_tokens, "parallelism": "single GPU",
+                   "attention_splits": splits},
+        "kv_read_GBps": kv_bytes / wall / 1e9,
+        "kv_read_pct_hbm_peak": 100.0 * kv_bytes / wall / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "attend_qevict_kernel<128>",
+                     "algorithmic_bytes_per_launch": kv_bytes / steps,
+                     "avg_launch_us": att_avg_s * 1e6},
+        "cpu_baseline": cpu,
+        "parity_spot_check_max_abs": worst,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,8 @@ def _lib() -> ctypes.CDLL:
         L.qkv_export_bytes.argtypes = [_vp, _i32]
         L.qkv_info.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_int64)]
         L.qkv_status.argtypes = [_vp, _vp]
+        L.qkv_profile_start.argtypes = [_vp, _i32]
+        L.qkv_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _i32]
         _LIB = L
     return _LIB
 
@@ -181,6 +183,14 @@ class Cache:
         v = ctypes.c_int64()
         _check(_lib().qkv_info(self.h, INFO[what], ctypes.byref(v)), "qkv_info")
         return int(v.value)
+
+    def profile_start(self, n: int) -> None:
+        _check(_lib().qkv_profile_start(self.h, int(n)), "qkv_profile_start")
+
+    def profile_read(self, n: int):
+        buf = (ctypes.c_float * n)()
+        _check(_lib().qkv_profile_read(self.h, buf, int(n)), "qkv_profile_read")
+        return list(buf)
 
     def status(self, stream=None) -> int:
         return int(_lib().qkv_status(self.h, _stream(stream)))

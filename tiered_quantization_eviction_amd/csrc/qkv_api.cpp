@@ -21,6 +21,9 @@ struct qkv_cache {
   int routed;     // ranked windows held (same for every sequence)
   long long steps;
   long long routes;
+  // kernel timing
+  hipEvent_t *ev;   // 2 * ev_n events
+  int ev_n, ev_next;
 };
 
 namespace {
@@ -182,8 +185,46 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
   return QKV_OK;
 }
 
+static void free_events(qkv_cache *c) {
+  if (c->ev) {
+    for (int i = 0; i < 2 * c->ev_n; ++i) hipEventDestroy(c->ev[i]);
+    delete[] c->ev;
+  }
+  c->ev = nullptr;
+  c->ev_n = c->ev_next = 0;
+}
+
 int qkv_destroy(qkv_cache *cache) {
+  if (cache) free_events(cache);
   delete cache;
+  return QKV_OK;
+}
+
+int qkv_profile_start(qkv_cache *c, int32_t n) {
+  if (!c || n < 0 || n > (1 << 20)) return QKV_EINVAL;
+  free_events(c);
+  if (n == 0) return QKV_OK;
+  c->ev = new (std::nothrow) hipEvent_t[2 * n];
+  if (!c->ev) return QKV_ECAPACITY;
+  for (int i = 0; i < 2 * n; ++i) {
+    if (hipEventCreate(&c->ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(c->ev[j]);
+      delete[] c->ev;
+      c->ev = nullptr;
+      return QKV_EHIP;
+    }
+  }
+  c->ev_n = n;
+  c->ev_next = 0;
+  return QKV_OK;
+}
+
+int qkv_profile_read(qkv_cache *c, float *ms, int32_t n) {
+  if (!c || !ms || n < 0 || n > c->ev_next) return QKV_EINVAL;
+  if (n == 0) return QKV_OK;
+  if (hipEventSynchronize(c->ev[2 * (c->ev_next - 1) + 1]) != hipSuccess) return QKV_EHIP;
+  for (int i = 0; i < n; ++i)
+    if (hipEventElapsedTime(&ms[i], c->ev[2 * i], c->ev[2 * i + 1]) != hipSuccess) return QKV_EHIP;
   return QKV_OK;
 }
 
@@ -200,7 +241,14 @@ int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv
 int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, qkv_stream stream) {
   if (!c || !q || !out) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
-  int rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (c->ev && c->ev_next < c->ev_n) {
+    e0 = c->ev[2 * c->ev_next];
+    e1 = c->ev[2 * c->ev_next + 1];
+    c->ev_next++;
+  }
+  int rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
+                                 e0, e1));
   if (rc != QKV_OK) return rc;
   c->steps++;
   return QKV_OK;

@@ -147,7 +147,7 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
                          int pos0, hipStream_t s);
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
-                         float *mass_out, hipStream_t s);
+                         float *mass_out, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
                         hipStream_t s);
 hipError_t launch_quantize_window(const void *x, int x_dtype, int n_blocks, int tokens, int d, int bits, int group,

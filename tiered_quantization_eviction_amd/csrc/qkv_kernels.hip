@@ -147,6 +147,13 @@ struct EntryList {
   long long cF, cQ;
   __device__ int count() const { return s0 + nF + nQ + nR; }
   __device__ long long total_cost() const { return (long long)(s0 + nF + nR) * cF + (long long)nQ * cQ; }
+  // cost position where entry e starts
+  __device__ long long cost_start(int e) const {
+    const long long A = s0 + nF;
+    if (e <= A) return e * cF;
+    if (e <= A + nQ) return A * cF + (e - A) * cQ;
+    return A * cF + (long long)nQ * cQ + (e - A - nQ) * cF;
+  }
   // first entry whose cost-start is >= x
   __device__ int first_at(long long x) const {
     int E = count();
@@ -208,29 +215,27 @@ struct WaveState {
 // online-softmax update for one 16-token tile of scores (C layout: lane holds
 // column col = lane%16, tokens 4*(lane/16)+i); returns probabilities in p[]
 template <int D>
-__device__ inline float softmax_tile(WaveState<D> &ws, floatx4 s, float sc, int n_valid, int lq, float &rho,
-                                     float p[4]) {
+__device__ inline void softmax_tile(WaveState<D> &ws, floatx4 s, float sc, int n_valid, int lq, float &rho,
+                                    float p[4]) {
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = (4 * lq + i < n_valid) ? s[i] * sc : neg_inf();
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float m_new = fmaxf(ws.m, mx);
-  bool grow = m_new > ws.m;
+  const float m_new = fmaxf(ws.m, mx);
+  const bool grow = m_new > ws.m;
   if (__any(grow)) {
-    float alpha = grow ? (ws.m == neg_inf() ? 0.0f : exp2f(ws.m - m_new)) : 1.0f;
+    const float alpha = grow ? (ws.m == neg_inf() ? 0.0f : exp2f(ws.m - m_new)) : 1.0f;
     ws.l *= alpha;
     rho *= alpha;
-    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i (= column of lane 4*lq+i)
+      const float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i
 #pragma unroll
       for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
       ws.zacc[i] *= ar;
     }
-    (void)lane;
     ws.m = m_new;
   }
   float ts = 0.0f;
@@ -243,7 +248,363 @@ __device__ inline float softmax_tile(WaveState<D> &ws, floatx4 s, float sc, int 
   ts += __shfl_xor(ts, 16);
   ts += __shfl_xor(ts, 32);
   rho += ts;
-  return ts;
+}
+
+// one full-precision tile whose K (D/32 x 16 B per lane) and V (D/16 x 8 B
+// per lane) operands are already in registers
+template <int D>
+__device__ inline void tile_full(WaveState<D> &ws, const bf16x8 *ka, const short4v *vb, const bf16x8 *bq, float sc,
+                                 int n_valid, int lq, bool is_hi, bool is_lo, float &rho) {
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) s = mfma_bf16_k32(ka[kb], bq[kb], s);
+  float p[4];
+  softmax_tile<D>(ws, s, sc, n_valid, lq, rho, p);
+  short4v ap;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t hi = f32_to_bf16_rne(p[i]);
+    const uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
+    ap[i] = (short)(is_hi ? hi : (is_lo ? lo : (uint16_t)0));
+  }
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct] = mfma_bf16_k16(ap, vb[ct], ws.acc[ct]);
+}
+
+// one quantized tile; the window's key params (s[D] then z[D]) and this
+// tile's value params are staged in the wave's LDS slots kp / vp
+template <int D>
+__device__ inline void tile_quant(WaveState<D> &ws, const uint32_t *kd, const uint32_t *vd, const half_t *kp,
+                                  const half_t *vp, const half8 *bqh, float sc, int n_valid, int lq, int col,
+                                  bool is_hi, bool is_lo, float &rho) {
+  constexpr int KB = D / 32, NG = D / 32;
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const half8 s8 = *(const half8 *)(kp + kb * 32 + lq * 8);
+    const half8 z8 = *(const half8 *)(kp + D + kb * 32 + lq * 8);
+    const half8 qhi = bqh[kb] * s8;
+    const half8 qlo = __builtin_elementwise_fma(bqh[kb], s8, -qhi);   // exact remainder of q*s
+    const half8 a = unpack8(kd[kb >> 1], (kb & 1) * 4);
+    s = mfma_f16_k32(a, qhi, s);
+    s = mfma_f16_k32(a, qlo, s);
+    s = mfma_f16_k32(z8, bqh[kb], s);                                   // sum_c q_c z_c
+  }
+  float p[4];
+  softmax_tile<D>(ws, s, sc, n_valid, lq, rho, p);
+  half4 phi, plo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    phi[i] = (half_t)p[i];
+    plo[i] = (half_t)(p[i] - (float)phi[i]);
+  }
+  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    const half4 s4 = *(const half4 *)(vp + (lq * NG + grp) * 8);
+    const half4 th = phi * s4;
+    half4 tl = __builtin_elementwise_fma(phi, s4, -th);
+    tl = __builtin_elementwise_fma(plo, s4, tl);
+    const half4 ag = is_hi ? th : (is_lo ? tl : zero4);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int ct = grp * 2 + c2;
+      ws.acc[ct] = mfma_f16_k16(ag, unpack4(vd[ct >> 2], (ct & 3) * 2), ws.acc[ct]);
+    }
+  }
+  const half4 apz = is_hi ? phi : (is_lo ? plo : zero4);
+  half4 bz = zero4;
+  if (col < NG) bz = *(const half4 *)(vp + (lq * NG + col) * 8 + 4);
+  ws.zacc = mfma_f16_k16(apz, bz, ws.zacc);
+}
+
+// order a wave's LDS writes before its own later LDS reads (no cross-wave sharing)
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
+constexpr int QBATCH = 2;   // quantized tiles per batch (two batches in flight per wave)
+
+// everything a wave needs while it walks its entries
+struct Ctx {
+  const Geom *g;
+  const State *st;
+  const StepInfo *si;
+  const EntryList *L;
+  const uint16_t *qrow;   // this lane's query row (head of its column)
+  int b, h, lane, col, lq, G;
+  bool is_hi, is_lo, has_q;
+  float scale_log2;
+  float *mass_row;
+  half_t *kp_lds;
+  half_t *vp_lds;
+};
+
+__device__ __forceinline__ void emit_mass(const Ctx &c, int e, float rho, float m) {
+  if (c.lq == 0 && c.col < c.G) {
+    float *mp = c.mass_row + ((size_t)e * c.G + c.col) * 2;
+    mp[0] = rho;
+    mp[1] = m;
+  }
+}
+
+// unit id and valid tokens of entries [tb, tb+64), one entry per lane
+__device__ __forceinline__ void load_table(const Ctx &c, int tb, int end, int &my_u, int &my_nv) {
+  const int e = tb + c.lane;
+  bool qq;
+  int nv = 0;
+  my_u = e < end ? entry_unit(*c.g, *c.st, *c.si, *c.L, c.b, e, qq, nv) : 0;
+  my_nv = nv;
+}
+
+struct Cursor {
+  int e, t, tb, my_u, my_nv;
+};
+
+// query B operands: bf16 as given (columns h and G+h carry head h)
+template <int D>
+__device__ __forceinline__ void query_bf16(const Ctx &c, bf16x8 (&bq)[D / 32]) {
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    const uint4 raw = c.has_q ? *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8) : make_uint4(0, 0, 0, 0);
+    bq[kb] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+// query as fp16 scaled by 2^-e (per head, |q| 2^-e < 1) so that q*s never leaves fp16
+template <int D>
+__device__ __forceinline__ float query_f16(const Ctx &c, half8 (&bqh)[D / 32]) {
+  uint4 raw[D / 32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    raw[kb] = c.has_q ? *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8) : make_uint4(0, 0, 0, 0);
+    const uint16_t *e = (const uint16_t *)&raw[kb];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  int qexp = 0;
+  if (amax > 0.0f) frexpf(amax, &qexp);
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    const uint16_t *e = (const uint16_t *)&raw[kb];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bqh[kb][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+  }
+  return ldexpf(c.scale_log2, qexp);
+}
+
+// ---- runs of full-precision units: tile by tile; the next tile's K loads
+// are issued right after this tile's QK, its V loads right after this PV ----
+
+struct FullItem {
+  int e, u, tile, nv;
+  bool last;
+};
+
+__device__ __forceinline__ bool full_next(const Ctx &c, int eb, Cursor &cu, FullItem &it) {
+  if (cu.e >= eb) return false;
+  if (cu.e >= cu.tb + 64) {
+    cu.tb = cu.e;
+    load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+  }
+  const int u = __shfl(cu.my_u, cu.e - cu.tb);
+  const int nv = __shfl(cu.my_nv, cu.e - cu.tb);
+  it.e = cu.e;
+  it.u = u;
+  it.tile = cu.t;
+  it.nv = nv - cu.t * TS;
+  it.last = (cu.t + 1) * TS >= nv;
+  if (it.last) {
+    ++cu.e;
+    cu.t = 0;
+  } else {
+    ++cu.t;
+  }
+  return true;
+}
+
+template <int D>
+__device__ __forceinline__ const uint16_t *tile_ptr(const Ctx &c, const FullItem &it) {
+  return c.st->pages + page_offset(*c.g, c.b, it.u, c.h) + (size_t)it.tile * 2 * TS * D;
+}
+
+template <int D>
+__device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
+  if (ea >= eb) return;
+  constexpr int KB = D / 32, CT = D / 16;
+  bf16x8 bq[KB];
+  query_bf16<D>(c, bq);
+  Cursor cu;
+  cu.e = ea;
+  cu.t = 0;
+  cu.tb = ea;
+  load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+  FullItem cur, nxt;
+  full_next(c, eb, cu, cur);
+  uint4 kr[KB];
+  uint2 vr[CT];
+  {
+    const uint16_t *kt = tile_ptr<D>(c, cur);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kr[kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) vr[ct] = *(const uint2 *)(kt + TS * D + (ct * 64 + c.lane) * 4);
+  }
+  float rho = 0.0f;
+  for (;;) {
+    const bool more = full_next(c, eb, cu, nxt);
+    if (!more) nxt = cur;            // the last step reloads its own tile: the same loads every step
+    const uint16_t *kn = tile_ptr<D>(c, nxt);
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[kb]), bq[kb], s);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kr[kb] = *(const uint4 *)(kn + (kb * 64 + c.lane) * 8);
+    float p[4];
+    softmax_tile<D>(ws, s, c.scale_log2, cur.nv, c.lq, rho, p);
+    short4v ap;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t hi = f32_to_bf16_rne(p[i]);
+      const uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
+      ap[i] = (short)(c.is_hi ? hi : (c.is_lo ? lo : (uint16_t)0));
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = mfma_bf16_k16(ap, __builtin_bit_cast(short4v, vr[ct]), ws.acc[ct]);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) vr[ct] = *(const uint2 *)(kn + TS * D + (ct * 64 + c.lane) * 4);
+    if (cur.last) {
+      emit_mass(c, cur.e, rho, ws.m);
+      rho = 0.0f;
+    }
+    if (!more) break;
+    cur = nxt;
+  }
+}
+
+// ---- runs of quantized windows: batches of QBATCH tiles; the next batch's
+// loads are in flight while the current batch computes ----
+
+struct QuantBuf {
+  uint4 k[QBATCH];      // (key code dwords, value code dwords) of each tile
+  uint2 p[QBATCH];      // this lane's 8 bytes of the window's key params
+  uint32_t vp[QBATCH];  // this lane's 4 bytes of the tile's value params
+};
+struct QuantItem {
+  int e, nb, u0, u1;
+};
+
+__device__ __forceinline__ bool quant_next(const Ctx &c, int eb, Cursor &cu, QuantItem &it) {
+  if (cu.e >= eb) return false;
+  const int per = QBATCH / c.g->tpw;
+  const int nb = min(per, eb - cu.e);
+  if (cu.e + nb > cu.tb + 64) {
+    cu.tb = cu.e;
+    load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+  }
+  it.e = cu.e;
+  it.nb = nb;
+  it.u0 = __shfl(cu.my_u, cu.e - cu.tb);
+  it.u1 = __shfl(cu.my_u, cu.e - cu.tb + (nb > 1 ? 1 : 0));
+  cu.e += nb;
+  return true;
+}
+
+template <int D>
+__device__ __forceinline__ void quant_load(const Ctx &c, const QuantItem &it, QuantBuf &qb) {
+  constexpr int NKD = D / 64;
+  const Geom &g = *c.g;
+  const int tpw = g.tpw;
+#pragma unroll
+  for (int j = 0; j < QBATCH; ++j) {
+    // slot j: window j of the batch (one tile each), or tile j of one two-tile window
+    const int u = (tpw == 1 && j == 1) ? it.u1 : it.u0;
+    const int tj = (tpw == 1) ? 0 : j;
+    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, u, c.h);
+    const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
+    const uint32_t *kc = (const uint32_t *)T;
+    const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
+    uint4 w;
+    w.x = kc[c.lane];
+    w.y = NKD > 1 ? kc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
+    w.z = vc[c.lane];
+    w.w = NKD > 1 ? vc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
+    qb.k[j] = w;
+    qb.p[j] = c.lane * 8 < g.kparam_bytes ? *(const uint2 *)(Lb + c.lane * 8) : make_uint2(0, 0);
+    qb.vp[j] = c.lane * 4 < g.tile_vparam_bytes
+                   ? ((const uint32_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes))[c.lane]
+                   : 0u;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&bqh)[D / 32],
+                                              float sc_quant, const QuantItem &it, const QuantBuf &qb) {
+  constexpr int NKD = D / 64;
+  const Geom &g = *c.g;
+  const int tpw = g.tpw;
+  const int n_tiles = it.nb * tpw;
+#pragma unroll
+  for (int j = 0; j < QBATCH; ++j) {
+    if (j < n_tiles) {
+      const int wj = tpw == 1 ? j : 0;   // window slot of tile j
+      if ((tpw == 1 || j == 0) && c.lane * 8 < g.kparam_bytes) *(uint2 *)(c.kp_lds + wj * 2 * D + c.lane * 4) = qb.p[j];
+      if (c.lane * 4 < g.tile_vparam_bytes) ((uint32_t *)(c.vp_lds + j * 2 * D))[c.lane] = qb.vp[j];
+    }
+  }
+  wave_lds_sync();
+  float rho = 0.0f;
+#pragma unroll
+  for (int j = 0; j < QBATCH; ++j) {
+    if (j < n_tiles) {
+      const int wj = tpw == 1 ? j : 0, tj = tpw == 1 ? 0 : j;
+      if (tj == 0) rho = 0.0f;
+      uint32_t kd[NKD], vd[NKD];
+      kd[0] = qb.k[j].x;
+      vd[0] = qb.k[j].z;
+      if (NKD > 1) {
+        kd[NKD - 1] = qb.k[j].y;
+        vd[NKD - 1] = qb.k[j].w;
+      }
+      tile_quant<D>(ws, kd, vd, c.kp_lds + wj * 2 * D, c.vp_lds + j * 2 * D, bqh, sc_quant, g.window - tj * TS,
+                    c.lq, c.col, c.is_hi, c.is_lo, rho);
+      if (tj == tpw - 1) emit_mass(c, it.e + wj, rho, ws.m);
+    }
+  }
+  wave_lds_sync();
+}
+
+template <int D>
+__device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
+  if (ea >= eb) return;
+  half8 bqh[D / 32];
+  const float sc_quant = query_f16<D>(c, bqh);
+  Cursor cu;
+  cu.e = ea;
+  cu.t = 0;
+  cu.tb = ea;
+  load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+  QuantItem i0, i1;
+  QuantBuf b0, b1;
+  quant_next(c, eb, cu, i0);
+  quant_load<D>(c, i0, b0);
+  for (;;) {
+    bool more = quant_next(c, eb, cu, i1);
+    if (!more) i1 = i0;
+    quant_load<D>(c, i1, b1);
+    quant_compute<D>(ws, c, bqh, sc_quant, i0, b0);
+    if (!more) break;
+    more = quant_next(c, eb, cu, i0);
+    if (!more) i0 = i1;
+    quant_load<D>(c, i0, b0);
+    quant_compute<D>(ws, c, bqh, sc_quant, i1, b1);
+    if (!more) break;
+  }
 }
 
 template <int D>
@@ -251,6 +612,7 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
   constexpr int CT = D / 16;
+  constexpr int NKD = D / 64;      // code dwords per lane per tile (keys, values)
   const int S = g.n_splits;
   const int split = blockIdx.x % S;
   const int bh = blockIdx.x / S;
@@ -265,42 +627,20 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
   const bool is_lo = col >= G && col < 2 * G;
   const int hc = is_hi ? col : (is_lo ? col - G : 0);
 
-  // ---- query operands (columns h and G+h both carry head h) ----
-  bf16x8 bq[KB];
-  half8 bqh[KB];
-  const uint16_t *qrow = q + ((size_t)b * g.Hq + (size_t)h * G + hc) * D;
-  float amax = 0.0f;
-  float qv[KB][8];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    uint4 raw = *(const uint4 *)(qrow + kb * 32 + lq * 8);
-    const uint16_t *e = (const uint16_t *)&raw;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float f = (is_hi || is_lo) ? bf16_to_f32(e[j]) : 0.0f;
-      qv[kb][j] = f;
-      amax = fmaxf(amax, fabsf(f));
-    }
-    union { uint4 u; bf16x8 v; } cv;
-    cv.u = (is_hi || is_lo) ? raw : make_uint4(0, 0, 0, 0);
-    bq[kb] = cv.v;
-  }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  int qexp = 0;
-  if (amax > 0.0f) frexpf(amax, &qexp);        // amax * 2^-qexp < 1
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bqh[kb][j] = (half_t)ldexpf(qv[kb][j], -qexp);
-  const float sc_full = scale_log2;
-  const float sc_quant = ldexpf(scale_log2, qexp);
+  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QBATCH][2 * D];   // key scale/zero per window
+  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QBATCH][2 * D];   // value params per tile
+  __shared__ float sm_m[ATT_WAVES][8];
+  __shared__ float sm_l[ATT_WAVES][8];
+  __shared__ float sm_o[ATT_WAVES][8][D];
 
-  // ---- this split's entry range ----
+  // ---- this split's entry range, cut into one contiguous sub-range per wave ----
   const EntryList L = make_list(g, st, si, b);
   const long long C = L.total_cost();
   const int e_begin = L.first_at(C * split / S);
   const int e_end = L.first_at(C * (split + 1) / S);
+  const long long c0 = L.cost_start(e_begin), c1 = L.cost_start(e_end);
+  const int w_begin = L.first_at(c0 + (c1 - c0) * wave / ATT_WAVES);
+  const int w_end = L.first_at(c0 + (c1 - c0) * (wave + 1) / ATT_WAVES);
 
   WaveState<D> ws;
 #pragma unroll
@@ -310,105 +650,32 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
   ws.l = 0.0f;
 
   float *mass_row = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1)) * G * 2;
+  half_t *kp_lds = &s_kp[wave][0][0];
+  half_t *vp_lds = &s_vp[wave][0][0];
 
-  for (int e = e_begin + wave; e < e_end; e += ATT_WAVES) {
-    bool quant;
-    int n_valid;
-    const int u = entry_unit(g, st, si, L, b, e, quant, n_valid);
-    float rho = 0.0f;
-    const int n_tiles = (n_valid + TS - 1) / TS;
-    if (!quant) {
-      const uint16_t *base = st.pages + page_offset(g, b, u, h);
-      for (int tile = 0; tile < n_tiles; ++tile) {
-        const uint16_t *kt = base + (size_t)tile * 2 * TS * D;
-        const uint16_t *vt = kt + TS * D;
-        floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          bf16x8 a = *(const bf16x8 *)(kt + (kb * 64 + lane) * 8);
-          s = mfma_bf16_k32(a, bq[kb], s);
-        }
-        float p[4];
-        softmax_tile<D>(ws, s, sc_full, n_valid - tile * TS, lq, rho, p);
-        short4v ap;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint16_t hi = f32_to_bf16_rne(p[i]);
-          uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
-          ap[i] = (short)(is_hi ? hi : (is_lo ? lo : (uint16_t)0));
-        }
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          short4v bv = *(const short4v *)(vt + (ct * 64 + lane) * 4);
-          ws.acc[ct] = mfma_bf16_k16(ap, bv, ws.acc[ct]);
-        }
-      }
-    } else {
-      const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
-      const half_t *ks = (const half_t *)Lb;
-      const half_t *kz = ks + D;
-      half8 qhi[KB], qlo[KB], z8[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        half8 s8 = *(const half8 *)(ks + kb * 32 + lq * 8);
-        z8[kb] = *(const half8 *)(kz + kb * 32 + lq * 8);
-        qhi[kb] = bqh[kb] * s8;
-        qlo[kb] = __builtin_elementwise_fma(bqh[kb], s8, -qhi[kb]);   // exact remainder of q*s
-      }
-      for (int tile = 0; tile < n_tiles; ++tile) {
-        const uint8_t *T = Lb + g.kparam_bytes + (size_t)tile * g.tile_block_bytes;
-        const uint32_t *kc = (const uint32_t *)T;
-        const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
-        const half_t *vp = (const half_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes);
-        uint32_t kd[KB / 2], vd[D / 64];
-#pragma unroll
-        for (int j = 0; j < KB / 2; ++j) kd[j] = kc[j * 64 + lane];
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j) vd[j] = vc[j * 64 + lane];
-        floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          half8 a = unpack8(kd[kb >> 1], (kb & 1) * 4);
-          s = mfma_f16_k32(a, qhi[kb], s);
-          s = mfma_f16_k32(a, qlo[kb], s);
-          s = mfma_f16_k32(z8[kb], bqh[kb], s);    // sum_c q_c z_c
-        }
-        float p[4];
-        softmax_tile<D>(ws, s, sc_quant, n_valid - tile * TS, lq, rho, p);
-        half4 phi, plo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          phi[i] = (half_t)p[i];
-          plo[i] = (half_t)(p[i] - (float)phi[i]);
-        }
-        const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
-#pragma unroll
-        for (int grp = 0; grp < D / 32; ++grp) {
-          half4 s4 = *(const half4 *)(vp + (lq * (D / 32) + grp) * 8);
-          half4 th = phi * s4;
-          half4 tl = __builtin_elementwise_fma(phi, s4, -th);
-          tl = __builtin_elementwise_fma(plo, s4, tl);
-          half4 ag = is_hi ? th : (is_lo ? tl : zero4);
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const int ct = grp * 2 + c2;
-            half4 bc = unpack4(vd[ct >> 2], (ct & 3) * 2);
-            ws.acc[ct] = mfma_f16_k16(ag, bc, ws.acc[ct]);
-          }
-        }
-        half4 apz = is_hi ? phi : (is_lo ? plo : zero4);
-        half4 bz = zero4;
-        if (col < D / 32) bz = *(const half4 *)(vp + (lq * (D / 32) + col) * 8 + 4);
-        ws.zacc = mfma_f16_k16(apz, bz, ws.zacc);
-      }
-    }
-    // this unit's partial mass per head, relative to the current running max
-    if (lq == 0 && col < G) {
-      float *mp = mass_row + ((size_t)e * G + col) * 2;
-      mp[0] = rho;
-      mp[1] = ws.m;
-    }
-  }
+  Ctx c;
+  c.g = &g;
+  c.st = &st;
+  c.si = &si;
+  c.L = &L;
+  c.qrow = q + ((size_t)b * g.Hq + (size_t)h * G + hc) * D;
+  c.b = b;
+  c.h = h;
+  c.lane = lane;
+  c.col = col;
+  c.lq = lq;
+  c.G = G;
+  c.is_hi = is_hi;
+  c.is_lo = is_lo;
+  c.has_q = is_hi || is_lo;
+  c.scale_log2 = scale_log2;
+  c.mass_row = mass_row;
+  c.kp_lds = kp_lds;
+  c.vp_lds = vp_lds;
+  const int A = L.s0 + L.nF, AQ = A + L.nQ;
+  run_full<D>(ws, c, w_begin, min(w_end, A));        // sink and ranked full-precision windows
+  run_quant<D>(ws, c, max(w_begin, A), min(w_end, AQ));
+  run_full<D>(ws, c, max(w_begin, AQ), w_end);        // windows not yet ranked
 
   // ---- wave epilogue: fold value-zero term and limbs ----
   float l_tot = ws.l + __shfl_xor(ws.l, 16);
@@ -423,9 +690,6 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
     for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl_down(ws.acc[ct][i], 4 * G);
 
   // ---- workgroup merge ----
-  __shared__ float sm_m[ATT_WAVES][8];
-  __shared__ float sm_l[ATT_WAVES][8];
-  __shared__ float sm_o[ATT_WAVES][8][D];
   if (lq == 0 && col < G) {
     sm_m[wave][col] = ws.m;
     sm_l[wave][col] = l_tot;
@@ -465,6 +729,23 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
 // merge: outputs per (sequence, KV head); masses -> window scores per sequence
 // ---------------------------------------------------------------------------
 
+// global (max, 1/sum) of head hh of KV head h over the splits
+__device__ inline void split_stats(const Geom &g, const State &st, int b, int h, int hh, float &M, float &invL) {
+  const int S = g.n_splits, G = g.G;
+  const float *ml = st.part_ml + ((size_t)(b * g.Hkv + h) * S * G + hh) * 2;
+  float m = neg_inf(), l = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+    const float ms = ml[(size_t)s * G * 2], ls = ml[(size_t)s * G * 2 + 1];
+    if (ms == neg_inf()) continue;
+    const float mn = fmaxf(m, ms);
+    l = (m == neg_inf() ? 0.0f : l * exp2f(m - mn)) + ls * exp2f(ms - mn);
+    m = mn;
+  }
+  M = m;
+  invL = 1.0f / l;
+}
+
 __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, StepInfo si, float *__restrict__ out,
                                                            float *__restrict__ mass_out, int n_chunks) {
   const int S = g.n_splits, G = g.G, D = g.d;
@@ -472,39 +753,27 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   __shared__ float sM[128], sInvL[128];   // Hkv*G = Hq <= 128
   if ((int)blockIdx.x < n_out_blocks) {
     const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
+    if ((int)threadIdx.x < G) split_stats(g, st, b, h, threadIdx.x, sM[threadIdx.x], sInvL[threadIdx.x]);
+    __syncthreads();
     const size_t base = (size_t)(b * g.Hkv + h) * S;
     for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
       const int hh = it / D, c = it % D;
-      float M = neg_inf();
-      for (int s = 0; s < S; ++s) M = fmaxf(M, st.part_ml[((base + s) * G + hh) * 2]);
-      float l = 0.0f, o = 0.0f;
+      const float M = sM[hh];
+      float o = 0.0f;
+#pragma unroll 8
       for (int s = 0; s < S; ++s) {
         const float ms = st.part_ml[((base + s) * G + hh) * 2];
-        if (ms == neg_inf()) continue;
-        const float f = exp2f(ms - M);
-        l += st.part_ml[((base + s) * G + hh) * 2 + 1] * f;
-        o += st.part_o[((base + s) * G + hh) * D + c] * f;
+        const float os = st.part_o[((base + s) * G + hh) * D + c];
+        if (ms != neg_inf()) o += os * exp2f(ms - M);
       }
-      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o / l;
+      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o * sInvL[hh];
     }
     return;
   }
   // mass chunk
   const int mb = blockIdx.x - n_out_blocks;
   const int b = mb / n_chunks, chunk = mb % n_chunks;
-  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) {
-    const int h = it / G, hh = it % G;
-    const size_t base = (size_t)(b * g.Hkv + h) * S;
-    float M = neg_inf();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, st.part_ml[((base + s) * G + hh) * 2]);
-    float l = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = st.part_ml[((base + s) * G + hh) * 2];
-      if (ms != neg_inf()) l += st.part_ml[((base + s) * G + hh) * 2 + 1] * exp2f(ms - M);
-    }
-    sM[it] = M;
-    sInvL[it] = 1.0f / l;
-  }
+  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
   __syncthreads();
   const EntryList L = make_list(g, st, si, b);
   const int E = L.count();
@@ -514,6 +783,7 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   int n_valid;
   const int u = entry_unit(g, st, si, L, b, e, quant, n_valid);
   float total = 0.0f;
+#pragma unroll 8
   for (int h = 0; h < g.Hkv; ++h) {
     const float *mp = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1) + e) * G * 2;
     float gs = 0.0f;
@@ -530,15 +800,17 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
 }
 
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
-                         float *mass_out, hipStream_t s) {
+                         float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
+  if (ev_start) hipEventRecord(ev_start, s);
   if (g.d == 128)
     hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
   else
     hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev_stop) hipEventRecord(ev_stop, s);
   if (mass_out) {
     e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.U * sizeof(float), s);
     if (e != hipSuccess) return e;
