@@ -44,24 +44,32 @@ __device__ inline floatx4 mfma_f16_k16(half4 a, half4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// two 2-bit codes (slots i and i+8 of a dword) as an exact fp16 pair
-__device__ inline uint32_t code_pair_bits(uint32_t x, int i) {
-  return ((x >> (2 * i)) & 0x00030003u) | 0x64006400u;   // (1024 + c_lo, 1024 + c_hi)
+// two 2-bit codes (slots i and i+8 of a dword) as an exact fp16 pair: the
+// codes land in the low mantissa bits of 1024.0 (0x6400), and 1024 is
+// subtracted exactly.  `magic` holds 0x64006400 in a VGPR so the mask-and-or
+// is a single v_and_or_b32.
+__device__ inline uint32_t code_pair_bits(uint32_t x, int i, uint32_t magic) {
+  return ((x >> (2 * i)) & 0x00030003u) | magic;
 }
-__device__ inline half8 unpack8(uint32_t x, int i0) {
+__device__ inline half8 unpack8(uint32_t x, int i0, uint32_t magic) {
   union { uint32_t u[4]; half8 h; } r;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r.u[k] = code_pair_bits(x, i0 + k);
+  for (int k = 0; k < 4; ++k) r.u[k] = code_pair_bits(x, i0 + k, magic);
   const half8 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024,
                      (half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
   return r.h - off;
 }
-__device__ inline half4 unpack4(uint32_t x, int i0) {
+__device__ inline half4 unpack4(uint32_t x, int i0, uint32_t magic) {
   union { uint32_t u[2]; half4 h; } r;
-  r.u[0] = code_pair_bits(x, i0);
-  r.u[1] = code_pair_bits(x, i0 + 1);
+  r.u[0] = code_pair_bits(x, i0, magic);
+  r.u[1] = code_pair_bits(x, i0 + 1, magic);
   const half4 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
   return r.h - off;
+}
+__device__ inline uint32_t magic_in_vgpr() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
 
 __device__ inline float neg_inf() { return -__builtin_inff(); }
@@ -212,112 +220,6 @@ struct WaveState {
   float l;               // partial sum of probabilities over this lane's tokens
 };
 
-// online-softmax update for one 16-token tile of scores (C layout: lane holds
-// column col = lane%16, tokens 4*(lane/16)+i); returns probabilities in p[]
-template <int D>
-__device__ inline void softmax_tile(WaveState<D> &ws, floatx4 s, float sc, int n_valid, int lq, float &rho,
-                                    float p[4]) {
-  float x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = (4 * lq + i < n_valid) ? s[i] * sc : neg_inf();
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(ws.m, mx);
-  const bool grow = m_new > ws.m;
-  if (__any(grow)) {
-    const float alpha = grow ? (ws.m == neg_inf() ? 0.0f : exp2f(ws.m - m_new)) : 1.0f;
-    ws.l *= alpha;
-    rho *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i
-#pragma unroll
-      for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
-      ws.zacc[i] *= ar;
-    }
-    ws.m = m_new;
-  }
-  float ts = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = (ws.m == neg_inf()) ? 0.0f : exp2f(x[i] - ws.m);
-    ts += p[i];
-  }
-  ws.l += ts;
-  ts += __shfl_xor(ts, 16);
-  ts += __shfl_xor(ts, 32);
-  rho += ts;
-}
-
-// one full-precision tile whose K (D/32 x 16 B per lane) and V (D/16 x 8 B
-// per lane) operands are already in registers
-template <int D>
-__device__ inline void tile_full(WaveState<D> &ws, const bf16x8 *ka, const short4v *vb, const bf16x8 *bq, float sc,
-                                 int n_valid, int lq, bool is_hi, bool is_lo, float &rho) {
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) s = mfma_bf16_k32(ka[kb], bq[kb], s);
-  float p[4];
-  softmax_tile<D>(ws, s, sc, n_valid, lq, rho, p);
-  short4v ap;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t hi = f32_to_bf16_rne(p[i]);
-    const uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
-    ap[i] = (short)(is_hi ? hi : (is_lo ? lo : (uint16_t)0));
-  }
-#pragma unroll
-  for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct] = mfma_bf16_k16(ap, vb[ct], ws.acc[ct]);
-}
-
-// one quantized tile; the window's key params (s[D] then z[D]) and this
-// tile's value params are staged in the wave's LDS slots kp / vp
-template <int D>
-__device__ inline void tile_quant(WaveState<D> &ws, const uint32_t *kd, const uint32_t *vd, const half_t *kp,
-                                  const half_t *vp, const half8 *bqh, float sc, int n_valid, int lq, int col,
-                                  bool is_hi, bool is_lo, float &rho) {
-  constexpr int KB = D / 32, NG = D / 32;
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const half8 s8 = *(const half8 *)(kp + kb * 32 + lq * 8);
-    const half8 z8 = *(const half8 *)(kp + D + kb * 32 + lq * 8);
-    const half8 qhi = bqh[kb] * s8;
-    const half8 qlo = __builtin_elementwise_fma(bqh[kb], s8, -qhi);   // exact remainder of q*s
-    const half8 a = unpack8(kd[kb >> 1], (kb & 1) * 4);
-    s = mfma_f16_k32(a, qhi, s);
-    s = mfma_f16_k32(a, qlo, s);
-    s = mfma_f16_k32(z8, bqh[kb], s);                                   // sum_c q_c z_c
-  }
-  float p[4];
-  softmax_tile<D>(ws, s, sc, n_valid, lq, rho, p);
-  half4 phi, plo;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    phi[i] = (half_t)p[i];
-    plo[i] = (half_t)(p[i] - (float)phi[i]);
-  }
-  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
-#pragma unroll
-  for (int grp = 0; grp < NG; ++grp) {
-    const half4 s4 = *(const half4 *)(vp + (lq * NG + grp) * 8);
-    const half4 th = phi * s4;
-    half4 tl = __builtin_elementwise_fma(phi, s4, -th);
-    tl = __builtin_elementwise_fma(plo, s4, tl);
-    const half4 ag = is_hi ? th : (is_lo ? tl : zero4);
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int ct = grp * 2 + c2;
-      ws.acc[ct] = mfma_f16_k16(ag, unpack4(vd[ct >> 2], (ct & 3) * 2), ws.acc[ct]);
-    }
-  }
-  const half4 apz = is_hi ? phi : (is_lo ? plo : zero4);
-  half4 bz = zero4;
-  if (col < NG) bz = *(const half4 *)(vp + (lq * NG + col) * 8 + 4);
-  ws.zacc = mfma_f16_k16(apz, bz, ws.zacc);
-}
-
 // order a wave's LDS writes before its own later LDS reads (no cross-wave sharing)
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -326,7 +228,6 @@ __device__ inline void wave_lds_sync() {
 }
 
 
-constexpr int QBATCH = 2;   // quantized tiles per batch (two batches in flight per wave)
 
 // everything a wave needs while it walks its entries
 struct Ctx {
@@ -337,6 +238,7 @@ struct Ctx {
   const uint16_t *qrow;   // this lane's query row (head of its column)
   int b, h, lane, col, lq, G;
   bool is_hi, is_lo, has_q;
+  uint32_t magic;
   float scale_log2;
   float *mass_row;
   half_t *kp_lds;
@@ -398,11 +300,64 @@ __device__ __forceinline__ float query_f16(const Ctx &c, half8 (&bqh)[D / 32]) {
   return ldexpf(c.scale_log2, qexp);
 }
 
-// ---- runs of full-precision units: tile by tile; the next tile's K loads
-// are issued right after this tile's QK, its V loads right after this PV ----
+// online-softmax update for a block of NT 16-token tiles (scores in C layout);
+// writes probabilities p[t][i] and each tile's probability sum ts[t] (summed
+// over the tile's 16 tokens), and rescales the running state -- including the
+// caller's partial unit mass rho -- when the running max grows.
+template <int D, int NT>
+__device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float sc, const int *nv, int lq,
+                                     float (*p)[4], float *ts, float &rho) {
+  float x[NT][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[t][i] = (4 * lq + i < nv[t]) ? s[t][i] * sc : neg_inf();
+      mx = fmaxf(mx, x[t][i]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(ws.m, mx);
+  const bool grow = m_new > ws.m;
+  if (__any(grow)) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;   // exp2(-inf) = 0 on the first block
+    ws.l *= alpha;
+    rho *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
+      ws.zacc[i] *= ar;
+    }
+    ws.m = m_new;
+  }
+  float lsum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    ts[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - ws.m);
+      ts[t] += p[t][i];
+    }
+    lsum += ts[t];
+  }
+  ws.l += lsum;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ts[t] += __shfl_xor(ts[t], 16);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ts[t] += __shfl_xor(ts[t], 32);
+}
+
+// ---- runs of full-precision units, two tiles (32 token slots) per block ----
+// A block's PV is one 16x16x32 op per column tile: the lane's eight k slots
+// are tokens 4*lq..4*lq+3 of the first tile and of the second tile, the same
+// order on the probability operand and on the value operand.
 
 struct FullItem {
-  int e, u, tile, nv;
+  int e, u, tile, nv;   // nv = 0: an empty slot (its address repeats a valid tile)
   bool last;
 };
 
@@ -428,6 +383,16 @@ __device__ __forceinline__ bool full_next(const Ctx &c, int eb, Cursor &cu, Full
   return true;
 }
 
+__device__ __forceinline__ bool full_block(const Ctx &c, int eb, Cursor &cu, FullItem (&it)[2]) {
+  if (!full_next(c, eb, cu, it[0])) return false;
+  if (!full_next(c, eb, cu, it[1])) {
+    it[1] = it[0];
+    it[1].nv = 0;
+    it[1].last = false;
+  }
+  return true;
+}
+
 template <int D>
 __device__ __forceinline__ const uint16_t *tile_ptr(const Ctx &c, const FullItem &it) {
   return c.st->pages + page_offset(*c.g, c.b, it.u, c.h) + (size_t)it.tile * 2 * TS * D;
@@ -444,76 +409,108 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   cu.t = 0;
   cu.tb = ea;
   load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
-  FullItem cur, nxt;
-  full_next(c, eb, cu, cur);
-  uint4 kr[KB];
-  uint2 vr[CT];
-  {
-    const uint16_t *kt = tile_ptr<D>(c, cur);
+  FullItem cur[2], nxt[2];
+  full_block(c, eb, cu, cur);
+  uint4 kr[2][KB];
+  uint2 vr[2][CT];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t *kt = tile_ptr<D>(c, cur[t]);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) vr[ct] = *(const uint2 *)(kt + TS * D + (ct * 64 + c.lane) * 4);
+    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) vr[t][ct] = *(const uint2 *)(kt + TS * D + (ct * 64 + c.lane) * 4);
   }
   float rho = 0.0f;
   for (;;) {
-    const bool more = full_next(c, eb, cu, nxt);
-    if (!more) nxt = cur;            // the last step reloads its own tile: the same loads every step
-    const uint16_t *kn = tile_ptr<D>(c, nxt);
-    floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[kb]), bq[kb], s);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[kb] = *(const uint4 *)(kn + (kb * 64 + c.lane) * 8);
-    float p[4];
-    softmax_tile<D>(ws, s, c.scale_log2, cur.nv, c.lq, rho, p);
-    short4v ap;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t hi = f32_to_bf16_rne(p[i]);
-      const uint16_t lo = f32_to_bf16_rne(p[i] - bf16_to_f32(hi));
-      ap[i] = (short)(c.is_hi ? hi : (c.is_lo ? lo : (uint16_t)0));
+    const bool more = full_block(c, eb, cu, nxt);
+    if (!more) {   // the last step reloads its own tiles: the same loads every step
+      nxt[0] = cur[0];
+      nxt[1] = cur[1];
     }
+    floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = mfma_bf16_k16(ap, __builtin_bit_cast(short4v, vr[ct]), ws.acc[ct]);
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) vr[ct] = *(const uint2 *)(kn + TS * D + (ct * 64 + c.lane) * 4);
-    if (cur.last) {
-      emit_mass(c, cur.e, rho, ws.m);
+      for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kn = tile_ptr<D>(c, nxt[t]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(kn + (kb * 64 + c.lane) * 8);
+    }
+    const int nv[2] = {c.has_q ? cur[0].nv : 0, c.has_q ? cur[1].nv : 0};
+    float p[2][4], ts[2];
+    softmax_block<D, 2>(ws, s, c.scale_log2, nv, c.lq, p, ts, rho);
+    rho += ts[0];
+    if (cur[0].last) {
+      emit_mass(c, cur[0].e, rho, ws.m);
       rho = 0.0f;
     }
+    rho += ts[1];
+    if (cur[1].nv > 0 && cur[1].last) {
+      emit_mass(c, cur[1].e, rho, ws.m);
+      rho = 0.0f;
+    }
+    // rows h carry bf16(p), rows G+h carry bf16(p - bf16(p))
+    bf16x8 ap;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float hi = (float)(__bf16)p[t][i];
+        ap[t * 4 + i] = (__bf16)(c.is_lo ? p[t][i] - hi : p[t][i]);
+      }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const uint4 vv = make_uint4(vr[0][ct].x, vr[0][ct].y, vr[1][ct].x, vr[1][ct].y);
+      ws.acc[ct] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, vv), ws.acc[ct]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kn = tile_ptr<D>(c, nxt[t]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) vr[t][ct] = *(const uint2 *)(kn + TS * D + (ct * 64 + c.lane) * 4);
+    }
     if (!more) break;
-    cur = nxt;
+    cur[0] = nxt[0];
+    cur[1] = nxt[1];
   }
 }
 
-// ---- runs of quantized windows: batches of QBATCH tiles; the next batch's
-// loads are in flight while the current batch computes ----
+// ---- runs of quantized windows, QT tiles per block; the next block is in
+// flight while one computes ----
+
+constexpr int QT = 4;   // quantized tiles per block
 
 struct QuantBuf {
-  uint4 k[QBATCH];      // (key code dwords, value code dwords) of each tile
-  uint2 p[QBATCH];      // this lane's 8 bytes of the window's key params
-  uint32_t vp[QBATCH];  // this lane's 4 bytes of the tile's value params
+  uint4 k[QT];      // (key code dwords, value code dwords) of each tile
+  uint2 p[QT];      // this lane's 8 bytes of the tile's window key params
+  uint32_t vp[QT];  // this lane's 4 bytes of the tile's value params
 };
 struct QuantItem {
-  int e, nb, u0, u1;
+  int e, nwin;
+  int u[QT];
 };
 
 __device__ __forceinline__ bool quant_next(const Ctx &c, int eb, Cursor &cu, QuantItem &it) {
   if (cu.e >= eb) return false;
-  const int per = QBATCH / c.g->tpw;
-  const int nb = min(per, eb - cu.e);
-  if (cu.e + nb > cu.tb + 64) {
+  const int per = QT / c.g->tpw;
+  const int nw = min(per, eb - cu.e);
+  if (cu.e + nw > cu.tb + 64) {
     cu.tb = cu.e;
     load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
   }
   it.e = cu.e;
-  it.nb = nb;
-  it.u0 = __shfl(cu.my_u, cu.e - cu.tb);
-  it.u1 = __shfl(cu.my_u, cu.e - cu.tb + (nb > 1 ? 1 : 0));
-  cu.e += nb;
+  it.nwin = nw;
+#pragma unroll
+  for (int j = 0; j < QT; ++j) it.u[j] = __shfl(cu.my_u, cu.e - cu.tb + (j < nw ? j : 0));
+  cu.e += nw;
   return true;
 }
+
+// window slot and tile-in-window of block tile j
+__device__ __forceinline__ int qt_win(int j, int tpw) { return tpw == 1 ? j : j >> 1; }
 
 template <int D>
 __device__ __forceinline__ void quant_load(const Ctx &c, const QuantItem &it, QuantBuf &qb) {
@@ -521,20 +518,20 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QuantItem &it, Qu
   const Geom &g = *c.g;
   const int tpw = g.tpw;
 #pragma unroll
-  for (int j = 0; j < QBATCH; ++j) {
-    // slot j: window j of the batch (one tile each), or tile j of one two-tile window
-    const int u = (tpw == 1 && j == 1) ? it.u1 : it.u0;
-    const int tj = (tpw == 1) ? 0 : j;
+  for (int j = 0; j < QT; ++j) {
+    const int w = qt_win(j, tpw);
+    const int tj = j - w * tpw;
+    const int u = w < it.nwin ? (tpw == 1 ? it.u[j] : it.u[j >> 1]) : it.u[0];   // spare slots repeat window 0
     const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, u, c.h);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
     const uint32_t *kc = (const uint32_t *)T;
     const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
-    uint4 w;
-    w.x = kc[c.lane];
-    w.y = NKD > 1 ? kc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
-    w.z = vc[c.lane];
-    w.w = NKD > 1 ? vc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
-    qb.k[j] = w;
+    uint4 wv;
+    wv.x = kc[c.lane];
+    wv.y = NKD > 1 ? kc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
+    wv.z = vc[c.lane];
+    wv.w = NKD > 1 ? vc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
+    qb.k[j] = wv;
     qb.p[j] = c.lane * 8 < g.kparam_bytes ? *(const uint2 *)(Lb + c.lane * 8) : make_uint2(0, 0);
     qb.vp[j] = c.lane * 4 < g.tile_vparam_bytes
                    ? ((const uint32_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes))[c.lane]
@@ -545,37 +542,101 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QuantItem &it, Qu
 template <int D>
 __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&bqh)[D / 32],
                                               float sc_quant, const QuantItem &it, const QuantBuf &qb) {
-  constexpr int NKD = D / 64;
+  constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
   const Geom &g = *c.g;
   const int tpw = g.tpw;
-  const int n_tiles = it.nb * tpw;
+  // stage key params (one slot per window) and value params (one slot per tile)
 #pragma unroll
-  for (int j = 0; j < QBATCH; ++j) {
-    if (j < n_tiles) {
-      const int wj = tpw == 1 ? j : 0;   // window slot of tile j
-      if ((tpw == 1 || j == 0) && c.lane * 8 < g.kparam_bytes) *(uint2 *)(c.kp_lds + wj * 2 * D + c.lane * 4) = qb.p[j];
-      if (c.lane * 4 < g.tile_vparam_bytes) ((uint32_t *)(c.vp_lds + j * 2 * D))[c.lane] = qb.vp[j];
-    }
+  for (int j = 0; j < QT; ++j) {
+    const int w = qt_win(j, tpw);
+    if (j - w * tpw == 0 && c.lane * 8 < g.kparam_bytes) *(uint2 *)(c.kp_lds + w * 2 * D + c.lane * 4) = qb.p[j];
+    if (c.lane * 4 < g.tile_vparam_bytes) ((uint32_t *)(c.vp_lds + j * 2 * D))[c.lane] = qb.vp[j];
   }
   wave_lds_sync();
-  float rho = 0.0f;
+  int nv[QT];
 #pragma unroll
-  for (int j = 0; j < QBATCH; ++j) {
-    if (j < n_tiles) {
-      const int wj = tpw == 1 ? j : 0, tj = tpw == 1 ? 0 : j;
-      if (tj == 0) rho = 0.0f;
-      uint32_t kd[NKD], vd[NKD];
-      kd[0] = qb.k[j].x;
-      vd[0] = qb.k[j].z;
-      if (NKD > 1) {
-        kd[NKD - 1] = qb.k[j].y;
-        vd[NKD - 1] = qb.k[j].w;
-      }
-      tile_quant<D>(ws, kd, vd, c.kp_lds + wj * 2 * D, c.vp_lds + j * 2 * D, bqh, sc_quant, g.window - tj * TS,
-                    c.lq, c.col, c.is_hi, c.is_lo, rho);
-      if (tj == tpw - 1) emit_mass(c, it.e + wj, rho, ws.m);
+  for (int j = 0; j < QT; ++j) {
+    const int w = qt_win(j, tpw);
+    nv[j] = (c.has_q && w < it.nwin) ? g.window - (j - w * tpw) * TS : 0;
+  }
+  // scores of the QT tiles, k-blocks outermost so the four MFMA chains interleave
+  floatx4 s[QT];
+#pragma unroll
+  for (int j = 0; j < QT; ++j) s[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < QT; ++j) {
+      const half_t *kp = c.kp_lds + qt_win(j, tpw) * 2 * D;
+      const half8 s8 = *(const half8 *)(kp + kb * 32 + c.lq * 8);
+      const half8 z8 = *(const half8 *)(kp + D + kb * 32 + c.lq * 8);
+      const half8 qhi = bqh[kb] * s8;
+      const half8 qlo = __builtin_elementwise_fma(bqh[kb], s8, -qhi);   // exact remainder of q*s
+      const uint32_t kw = (kb >> 1) == 0 ? qb.k[j].x : qb.k[j].y;
+      const half8 a = unpack8(kw, (kb & 1) * 4, c.magic);
+      s[j] = mfma_f16_k32(a, qhi, s[j]);
+      s[j] = mfma_f16_k32(a, qlo, s[j]);
+      s[j] = mfma_f16_k32(z8, bqh[kb], s[j]);                           // sum_c q_c z_c
+    }
+  float p[QT][4], ts[QT];
+  float rho = 0.0f;
+  softmax_block<D, QT>(ws, s, sc_quant, nv, c.lq, p, ts, rho);
+  // masses: window by window
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const int w = qt_win(j, tpw);
+    rho += ts[j];
+    if (j - w * tpw == tpw - 1) {
+      if (w < it.nwin) emit_mass(c, it.e + w, rho, ws.m);
+      rho = 0.0f;
     }
   }
+  // fp16 limbs of p; (P1, P2) = (0, phi) on hi lanes, (phi, plo) on lo lanes:
+  // one FMA chain then yields fp16(p*s) on hi rows and the remainder on lo rows
+  half4 P1[QT], P2[QT];
+  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    half4 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      phi[i] = (half_t)p[j][i];
+      plo[i] = (half_t)(p[j][i] - (float)phi[i]);
+    }
+    P1[j] = c.is_lo ? phi : zero4;
+    P2[j] = c.is_lo ? plo : phi;
+  }
+  // PV over tile pairs: k slots = tokens 4*lq..+3 of tile 2pp, then of tile 2pp+1
+#pragma unroll
+  for (int pp = 0; pp < QT / 2; ++pp) {
+    const int j0 = 2 * pp, j1 = 2 * pp + 1;
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp) {
+      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * 2 * D + (c.lq * NG + grp) * 8);
+      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * 2 * D + (c.lq * NG + grp) * 8);
+      const half4 t0 = P1[j0] * s40, t1 = P1[j1] * s41;
+      const half4 ag0 = __builtin_elementwise_fma(P2[j0], s40, __builtin_elementwise_fma(P1[j0], s40, -t0));
+      const half4 ag1 = __builtin_elementwise_fma(P2[j1], s41, __builtin_elementwise_fma(P1[j1], s41, -t1));
+      const half8 ag = __builtin_shufflevector(ag0, ag1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int ct = grp * 2 + c2;
+        const uint32_t v0 = (ct >> 2) == 0 ? qb.k[j0].z : qb.k[j0].w;
+        const uint32_t v1 = (ct >> 2) == 0 ? qb.k[j1].z : qb.k[j1].w;
+        const half8 bc = __builtin_shufflevector(unpack4(v0, (ct & 3) * 2, c.magic), unpack4(v1, (ct & 3) * 2, c.magic),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        ws.acc[ct] = mfma_f16_k32(ag, bc, ws.acc[ct]);
+      }
+    }
+    half4 bz0 = zero4, bz1 = zero4;
+    if (c.col < NG) {
+      bz0 = *(const half4 *)(c.vp_lds + j0 * 2 * D + (c.lq * NG + c.col) * 8 + 4);
+      bz1 = *(const half4 *)(c.vp_lds + j1 * 2 * D + (c.lq * NG + c.col) * 8 + 4);
+    }
+    ws.zacc = mfma_f16_k32(__builtin_shufflevector(P2[j0], P2[j1], 0, 1, 2, 3, 4, 5, 6, 7),
+                           __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
+  }
+  (void)NKD;
   wave_lds_sync();
 }
 
@@ -589,26 +650,28 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   cu.t = 0;
   cu.tb = ea;
   load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+  // two-slot ring: one block in flight while one computes; the slot past the
+  // end reloads the current block so that every step issues the same loads
   QuantItem i0, i1;
   QuantBuf b0, b1;
   quant_next(c, eb, cu, i0);
   quant_load<D>(c, i0, b0);
   for (;;) {
-    bool more = quant_next(c, eb, cu, i1);
-    if (!more) i1 = i0;
+    bool v1 = quant_next(c, eb, cu, i1);
+    if (!v1) i1 = i0;
     quant_load<D>(c, i1, b1);
     quant_compute<D>(ws, c, bqh, sc_quant, i0, b0);
-    if (!more) break;
-    more = quant_next(c, eb, cu, i0);
-    if (!more) i0 = i1;
+    if (!v1) break;
+    bool v0 = quant_next(c, eb, cu, i0);
+    if (!v0) i0 = i1;
     quant_load<D>(c, i0, b0);
     quant_compute<D>(ws, c, bqh, sc_quant, i1, b1);
-    if (!more) break;
+    if (!v0) break;
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, StepInfo si,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
   constexpr int CT = D / 16;
@@ -627,8 +690,8 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
   const bool is_lo = col >= G && col < 2 * G;
   const int hc = is_hi ? col : (is_lo ? col - G : 0);
 
-  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QBATCH][2 * D];   // key scale/zero per window
-  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QBATCH][2 * D];   // value params per tile
+  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QT][2 * D];   // key scale/zero per window
+  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QT][2 * D];   // value params per tile
   __shared__ float sm_m[ATT_WAVES][8];
   __shared__ float sm_l[ATT_WAVES][8];
   __shared__ float sm_o[ATT_WAVES][8][D];
@@ -646,7 +709,7 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
   ws.zacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  ws.m = neg_inf();
+  ws.m = (is_hi || is_lo) ? neg_inf() : 0.0f;   // columns without a head keep a finite reference
   ws.l = 0.0f;
 
   float *mass_row = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1)) * G * 2;
@@ -668,6 +731,7 @@ __global__ __launch_bounds__(256) void attend_qevict_kernel(Geom g, State st, St
   c.is_hi = is_hi;
   c.is_lo = is_lo;
   c.has_q = is_hi || is_lo;
+  c.magic = magic_in_vgpr();
   c.scale_log2 = scale_log2;
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
