@@ -162,29 +162,35 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg, K, V, Q, sample_steps, firsts):
+def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts):
+    """The oracle, as it stands, on the first n_seqs sequences for
+    sample_steps decode steps each (prompt handling untimed)."""
     from oracle import qevict as oe
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    seq = oe.QEvictSequence(K[0], V[0], window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
-                            n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits,
-                            group=cfg.group, n_q_heads=cfg.n_q_heads)
-    seq.prefill(cfg.prefill)
     worst = 0.0
-    t0 = time.perf_counter()
-    outs = []
-    for s in range(sample_steps):
-        o, _ = seq.step(s, Q[0, s])
-        outs.append(o)
-    dt = time.perf_counter() - t0
-    for s, o in enumerate(outs[:len(firsts)]):
-        worst = max(worst, float(np.abs(firsts[s] - o).max()))
-    return {"value": sample_steps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"sequence 0 of 16, decode steps 0..{sample_steps - 1} (incl. {sample_steps // cfg.omega} "
-                      f"routing events), float64 numpy on the host; {dt:.1f} s"}, worst
+    dt = 0.0
+    for b in range(n_seqs):
+        seq = oe.QEvictSequence(K[b], V[b], window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
+                                n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits,
+                                group=cfg.group, n_q_heads=cfg.n_q_heads)
+        seq.prefill(cfg.prefill)
+        outs = []
+        t0 = time.perf_counter()
+        for s in range(sample_steps):
+            o, _ = seq.step(s, Q[b, s])
+            outs.append(o)
+        dt += time.perf_counter() - t0
+        if b == 0:
+            for s, o in enumerate(outs[:len(firsts)]):
+                worst = max(worst, float(np.abs(firsts[s] - o).max()))
+    return {"value": n_seqs * sample_steps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"sequences 0..{n_seqs - 1} of {cfg.batch}, decode steps 0..{sample_steps - 1} each "
+                      f"({sample_steps // cfg.omega} routing events per sequence), float64 numpy on the host; "
+                      f"{dt:.1f} s"}, worst
 
 
 def read_traffic(src_hash):
@@ -203,15 +209,36 @@ def read_traffic(src_hash):
     return t if (h == src_hash and t is not None) else None
 
 
+def copy_probe(mib):
+    """Five plain device copies of a known size: the HBM byte counters of this
+    kernel (read MiB, write MiB per dispatch) calibrate those of the attention
+    kernel."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-steps", type=int, default=256)
+    ap.add_argument("--cpu-steps", type=int, default=512)
+    ap.add_argument("--cpu-seqs", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     a = ap.parse_args()
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
               f"(the multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
@@ -238,8 +265,9 @@ def main():
     cpu = None
     worst = None
     if not a.no_cpu:
-        log(f"bench: oracle baseline on {a.cpu_steps} steps of one sequence")
-        cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_steps, firsts)
+        n_cpu = min(a.cpu_steps, cfg.steps)
+        log(f"bench: oracle baseline on {n_cpu} steps of {a.cpu_seqs} sequences")
+        cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_seqs, n_cpu, firsts)
     res = {
         "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer",
         "value": tok_s,
