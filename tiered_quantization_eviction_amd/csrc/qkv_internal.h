@@ -92,30 +92,38 @@ __host__ __device__ inline int unit_of(const Geom &g, int pos) {
 __host__ __device__ inline int k_tile_index(int t, int c) {
   return ((c >> 5) * 64 + ((c & 31) >> 3) * 16 + t) * 8 + (c & 7);
 }
-// V tile: the B operand of a 16x16x16 op reads, for column tile ct, lane
-// l = (t/4)*16 + c%16 the 4 tokens 4q..4q+3 of channel c -- 8 contiguous bytes.
+// V tile: the B operand of a 16x16x32 op over a pair of tiles reads, for
+// column tile ct, lane l = (t/4)*16 + c%16 the 4 tokens 4q..4q+3 of channel c
+// of each tile; the column tiles 2p and 2p+1 of a lane sit side by side, so a
+// lane reads 16 contiguous bytes per column-tile pair.
 __host__ __device__ inline int v_tile_index(int t, int c) {
-  return ((c >> 4) * 64 + (t >> 2) * 16 + (c & 15)) * 4 + (t & 3);
+  return (((c >> 5) * 64 + (t >> 2) * 16 + (c & 15)) * 2 + ((c >> 4) & 1)) * 4 + (t & 3);
 }
 
-// Ledger code placement (2-bit codes, 16 per dword).
-// Keys: dword (j*64 + l) of a tile, j = kb/2, l = ((c%32)/8)*16 + t, pair
-// i = (kb%2)*4 + (c%8)/2, slot p = i + 8*(c%2): bits [2p, 2p+1].
-__host__ __device__ inline void kcode_slot(int t, int c, int &dword, int &shift) {
-  int kb = c >> 5, l = ((c & 31) >> 3) * 16 + t, e = c & 7;
-  int i = (kb & 1) * 4 + (e >> 1);
-  int p = i + 8 * (e & 1);
-  dword = (kb >> 1) * 64 + l;
-  shift = 2 * p;
+// Ledger code placement (2-bit codes, 16 per dword, slot p at bits [2p, 2p+1]).
+// A tile's codes are 2*nkd dwords per lane (nkd = d/64): the lane's nkd key
+// dwords, then its nkd value dwords, so one 16-byte load (d = 128) fetches all
+// of a lane's codes.  Slots are placed for the unpack in the attention
+// kernel: x & 0x33333333 keeps slots 4k and 4k+2 of byte k in the low bits of
+// its two nibbles, (x >> 2) & 0x33333333 slots 4k+1 and 4k+3, and a scaled
+// FP4 (e2m1) conversion of a byte then yields the two codes as an exact fp16
+// pair (a nibble 00cc is the e2m1 value cc/2).
+// Keys, for the A operand of k-block kb (lane l = ((c%32)/8)*16 + t holds the
+// 8 channels kb*32 + 8*(l/16) ..): dword l*2nkd + kb/2; channel e = c%8 sits
+// in byte e/2 of the kb%2 half: slot 4*(e/2) + kb%2 + 2*(e%2).
+__host__ __device__ inline void kcode_slot(int t, int c, int nkd, int &dword, int &shift) {
+  const int kb = c >> 5, l = ((c & 31) >> 3) * 16 + t, e = c & 7;
+  dword = l * 2 * nkd + (kb >> 1);
+  shift = 2 * (4 * (e >> 1) + (kb & 1) + 2 * (e & 1));
 }
-// Values: dword (j*64 + l), j = ct/4, l = (t/4)*16 + c%16, pair
-// i = (ct%4)*2 + (t%4)/2, slot p = i + 8*(t%2).
-__host__ __device__ inline void vcode_slot(int t, int c, int &dword, int &shift) {
-  int ct = c >> 4, l = (t >> 2) * 16 + (c & 15);
-  int i = (ct & 3) * 2 + ((t & 3) >> 1);
-  int p = i + 8 * (t & 1);
-  dword = (ct >> 2) * 64 + l;
-  shift = 2 * p;
+// Values, for the B operand of column tile ct (lane l = (t/4)*16 + c%16 holds
+// tokens 4*(l/16) .. +3 of channel ct*16 + l%16): dword l*2nkd + nkd + ct/4;
+// byte ct%4; tokens (0,1) of the quad in the first half, (2,3) in the second:
+// slot 4*(ct%4) + (t%4)/2 + 2*(t%2).
+__host__ __device__ inline void vcode_slot(int t, int c, int nkd, int &dword, int &shift) {
+  const int ct = c >> 4, l = (t >> 2) * 16 + (c & 15), tt = t & 3;
+  dword = l * 2 * nkd + nkd + (ct >> 2);
+  shift = 2 * (4 * (ct & 3) + (tt >> 1) + 2 * (tt & 1));
 }
 // V params of a tile: [token quad tq][group g][s x4, z x4] fp16
 __host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int which /*0 s,1 z*/) {

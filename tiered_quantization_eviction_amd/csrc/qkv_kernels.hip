@@ -44,32 +44,33 @@ __device__ inline floatx4 mfma_f16_k16(half4 a, half4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// two 2-bit codes (slots i and i+8 of a dword) as an exact fp16 pair: the
-// codes land in the low mantissa bits of 1024.0 (0x6400), and 1024 is
-// subtracted exactly.  `magic` holds 0x64006400 in a VGPR so the mask-and-or
-// is a single v_and_or_b32.
-__device__ inline uint32_t code_pair_bits(uint32_t x, int i, uint32_t magic) {
-  return ((x >> (2 * i)) & 0x00030003u) | magic;
+// 2-bit codes to exact fp16 operands.  A code dword is first masked to
+// 0x33333333 (directly, or after a shift by 2): every byte then holds two
+// nibbles 00cc, which are the e2m1 (FP4) values cc/2, and the scaled FP4
+// conversion with scale 2 turns byte b into the fp16 pair (low nibble, high
+// nibble) = two codes, exactly.  The slot placement of the ledger
+// (kcode_slot / vcode_slot) puts the codes an operand needs in these pairs.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+template <int B>
+__device__ __forceinline__ half2v fp4_pair(uint32_t m) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, B);
 }
-__device__ inline half8 unpack8(uint32_t x, int i0, uint32_t magic) {
-  union { uint32_t u[4]; half8 h; } r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) r.u[k] = code_pair_bits(x, i0 + k, magic);
-  const half8 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024,
-                     (half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
-  return r.h - off;
+__device__ __forceinline__ half2v fp4_pair_sel(uint32_t m, int b) {   // b is a constant after unrolling
+  switch (b & 3) {
+    case 0: return fp4_pair<0>(m);
+    case 1: return fp4_pair<1>(m);
+    case 2: return fp4_pair<2>(m);
+    default: return fp4_pair<3>(m);
+  }
 }
-__device__ inline half4 unpack4(uint32_t x, int i0, uint32_t magic) {
-  union { uint32_t u[2]; half4 h; } r;
-  r.u[0] = code_pair_bits(x, i0, magic);
-  r.u[1] = code_pair_bits(x, i0 + 1, magic);
-  const half4 off = {(half_t)1024, (half_t)1024, (half_t)1024, (half_t)1024};
-  return r.h - off;
+__device__ __forceinline__ uint32_t code_half(uint32_t x, int odd) {   // slots 4k+odd, 4k+odd+2 of each byte
+  return (odd ? (x >> 2) : x) & 0x33333333u;
 }
-__device__ inline uint32_t magic_in_vgpr() {
-  uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
-  return m;
+// the 8 codes of a masked dword (bytes 0..3) as one half8 operand
+__device__ __forceinline__ half8 codes8(uint32_t m) {
+  const half4 lo = __builtin_shufflevector(fp4_pair<0>(m), fp4_pair<1>(m), 0, 1, 2, 3);
+  const half4 hi = __builtin_shufflevector(fp4_pair<2>(m), fp4_pair<3>(m), 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ inline float neg_inf() { return -__builtin_inff(); }
@@ -188,29 +189,16 @@ __device__ inline EntryList make_list(const Geom &g, const State &st, const Step
   return L;
 }
 
-// entry -> unit, quantized?, valid tokens
-__device__ inline int entry_unit(const Geom &g, const State &st, const StepInfo &si, const EntryList &L, int b,
-                                 int e, bool &quant, int &n_valid) {
-  quant = false;
-  if (e < L.s0) {
-    n_valid = min(si.N, g.n_sink);
-    return 0;
-  }
-  int r = e - L.s0;
-  if (r < L.nF + L.nQ) {
-    quant = r >= L.nF;
-    n_valid = g.window;
-    return st.routed[b * g.U + r];
-  }
-  int u = L.r0 + (r - L.nF - L.nQ);
-  int rem = si.N - unit_start(g, u);
-  n_valid = rem < g.window ? rem : g.window;
-  return u;
-}
-
 // ---------------------------------------------------------------------------
 // attention: one workgroup per (sequence, KV head, split)
 // ---------------------------------------------------------------------------
+//
+// The steady-state loops below keep every memory operation out of branches:
+// a load or store under a branch makes the compiler wait for *all* loads in
+// flight at the join, which would serialize the prefetch of the next block
+// with the compute of the current one.  Unit ids are fetched two blocks
+// ahead with clamped (always valid) indices, spare slots re-read valid tiles,
+// and mass stores of unused lanes go to a spare slot.
 
 template <int D>
 struct WaveState {
@@ -227,7 +215,24 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-
+// reductions over lane pairs (l, l^16) and (l, l^32) with the row-swap
+// permutes of gfx950 (VALU, no LDS traffic); both lanes get identical bits
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // everything a wave needs while it walks its entries
 struct Ctx {
@@ -235,43 +240,63 @@ struct Ctx {
   const State *st;
   const StepInfo *si;
   const EntryList *L;
-  const uint16_t *qrow;   // this lane's query row (head of its column)
+  const uint16_t *qrow;   // this lane's query row (head of its column; head 0 for other lanes)
   int b, h, lane, col, lq, G;
   bool is_hi, is_lo, has_q;
-  uint32_t magic;
   float scale_log2;
-  float *mass_row;
+  float *mass_row;        // [(U+1)][G][2] of this (sequence, KV head); slot U is the spare
   half_t *kp_lds;
   half_t *vp_lds;
 };
 
-__device__ __forceinline__ void emit_mass(const Ctx &c, int e, float rho, float m) {
-  if (c.lq == 0 && c.col < c.G) {
-    float *mp = c.mass_row + ((size_t)e * c.G + c.col) * 2;
-    mp[0] = rho;
-    mp[1] = m;
+// unit id of entry e; `raw` is the routed-list value fetched for it (used
+// for ranked entries only)
+__device__ __forceinline__ int entry_id(const Ctx &c, int e, int raw) {
+  const EntryList &L = *c.L;
+  if (e < L.s0) return 0;
+  const int r = e - L.s0;
+  if (r < L.nF + L.nQ) return raw;
+  return L.r0 + (r - L.nF - L.nQ);
+}
+// valid tokens of entry e (unit u)
+__device__ __forceinline__ int entry_nv(const Ctx &c, int e, int u) {
+  const EntryList &L = *c.L;
+  if (e < L.s0) return min(c.si->N, c.g->n_sink);
+  if (e - L.s0 < L.nF + L.nQ) return c.g->window;
+  return min(c.si->N - unit_start(*c.g, u), c.g->window);
+}
+// routed-list values of entries e0 .. e0+3 in lanes j = 0..3 (mod 4); the
+// index is clamped into the list so the load is valid and unconditional
+__device__ __forceinline__ int ids_fetch(const Ctx &c, int e0) {
+  const int r = min(max(e0 + (c.lane & 3) - c.L->s0, 0), c.g->U - 1);
+  return c.st->routed[(size_t)c.b * c.g->U + r];
+}
+
+// Mass partials of up to 4 units of a block in one store: lanes of row q
+// (lq == q) and column h < G write unit slot q's (rho, m) when ok[q]; all
+// other lanes write the spare slot.
+template <int N>
+__device__ __forceinline__ void store_mass(const Ctx &c, const int *e, const bool *ok, const float *rho, float m) {
+  int slot = c.g->U;
+  float r = 0.0f;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const bool mine = (c.lq == q) && ok[q];
+    slot = mine ? e[q] : slot;
+    r = mine ? rho[q] : r;
   }
+  if (c.col >= c.G) slot = c.g->U;
+  *(float2 *)(c.mass_row + ((size_t)slot * c.G + (c.col & (c.G - 1))) * 2) = make_float2(r, m);
 }
-
-// unit id and valid tokens of entries [tb, tb+64), one entry per lane
-__device__ __forceinline__ void load_table(const Ctx &c, int tb, int end, int &my_u, int &my_nv) {
-  const int e = tb + c.lane;
-  bool qq;
-  int nv = 0;
-  my_u = e < end ? entry_unit(*c.g, *c.st, *c.si, *c.L, c.b, e, qq, nv) : 0;
-  my_nv = nv;
-}
-
-struct Cursor {
-  int e, t, tb, my_u, my_nv;
-};
 
 // query B operands: bf16 as given (columns h and G+h carry head h)
 template <int D>
 __device__ __forceinline__ void query_bf16(const Ctx &c, bf16x8 (&bq)[D / 32]) {
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) {
-    const uint4 raw = c.has_q ? *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t keep = c.has_q ? 0xffffffffu : 0u;   // lanes without a head get a zero query
+    uint4 raw = *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8);
+    raw = make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep);
     bq[kb] = __builtin_bit_cast(bf16x8, raw);
   }
 }
@@ -282,13 +307,15 @@ __device__ __forceinline__ float query_f16(const Ctx &c, half8 (&bqh)[D / 32]) {
   float amax = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) {
-    raw[kb] = c.has_q ? *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t keep = c.has_q ? 0xffffffffu : 0u;
+    const uint4 r = *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8);
+    raw[kb] = make_uint4(r.x & keep, r.y & keep, r.z & keep, r.w & keep);
     const uint16_t *e = (const uint16_t *)&raw[kb];
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax = max_x16(amax);
+  amax = max_x32(amax);
   int qexp = 0;
   if (amax > 0.0f) frexpf(amax, &qexp);
 #pragma unroll
@@ -302,11 +329,11 @@ __device__ __forceinline__ float query_f16(const Ctx &c, half8 (&bqh)[D / 32]) {
 
 // online-softmax update for a block of NT 16-token tiles (scores in C layout);
 // writes probabilities p[t][i] and each tile's probability sum ts[t] (summed
-// over the tile's 16 tokens), and rescales the running state -- including the
-// caller's partial unit mass rho -- when the running max grows.
+// over the tile's 16 tokens) and rescales the running state when the running
+// max grows.
 template <int D, int NT>
 __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float sc, const int *nv, int lq,
-                                     float (*p)[4], float *ts, float &rho) {
+                                     float (*p)[4], float *ts) {
   float x[NT][4];
   float mx = neg_inf();
 #pragma unroll
@@ -316,14 +343,13 @@ __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float s
       x[t][i] = (4 * lq + i < nv[t]) ? s[t][i] * sc : neg_inf();
       mx = fmaxf(mx, x[t][i]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_x16(mx);
+  mx = max_x32(mx);
   const float m_new = fmaxf(ws.m, mx);
   const bool grow = m_new > ws.m;
   if (__any(grow)) {
     const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;   // exp2(-inf) = 0 on the first block
     ws.l *= alpha;
-    rho *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i
@@ -346,88 +372,70 @@ __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float s
   }
   ws.l += lsum;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) ts[t] += __shfl_xor(ts[t], 16);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) ts[t] += __shfl_xor(ts[t], 32);
+  for (int t = 0; t < NT; ++t) ts[t] = sum_x32(sum_x16(ts[t]));
 }
 
 // ---- runs of full-precision units, two tiles (32 token slots) per block ----
-// A block's PV is one 16x16x32 op per column tile: the lane's eight k slots
-// are tokens 4*lq..4*lq+3 of the first tile and of the second tile, the same
-// order on the probability operand and on the value operand.
+// Tile k of a run is tile k % tpw of entry ea + k / tpw; block i holds tiles
+// 2i and 2i+1, so with at most two tiles per unit a unit never straddles
+// blocks.  A block's PV is one 16x16x32 op per column tile: the lane's eight
+// k slots are tokens 4*lq..4*lq+3 of the first tile and of the second tile,
+// the same order on the probability operand and on the value operand.
 
-struct FullItem {
-  int e, u, tile, nv;   // nv = 0: an empty slot (its address repeats a valid tile)
-  bool last;
+struct FBlock {
+  int e[2], u[2], tile[2], nv[2];   // nv <= 0: an empty slot (its address repeats slot 0)
 };
 
-__device__ __forceinline__ bool full_next(const Ctx &c, int eb, Cursor &cu, FullItem &it) {
-  if (cu.e >= eb) return false;
-  if (cu.e >= cu.tb + 64) {
-    cu.tb = cu.e;
-    load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
+__device__ __forceinline__ void fblock_make(const Ctx &c, int ea, int n_tiles, int i, int ids, FBlock &fb) {
+  const int tpw = c.g->tpw;
+  const int e_first = ea + (2 * i) / tpw;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = 2 * i + s;
+    const bool valid = k < n_tiles;
+    const int kk = valid ? k : 2 * i;
+    const int e = ea + kk / tpw;
+    const int t = kk - (kk / tpw) * tpw;
+    const int raw = __builtin_amdgcn_readlane(ids, e - e_first);
+    const int u = entry_id(c, e, raw);
+    fb.e[s] = e;
+    fb.u[s] = u;
+    fb.tile[s] = t;
+    fb.nv[s] = valid ? entry_nv(c, e, u) - t * TS : 0;
   }
-  const int u = __shfl(cu.my_u, cu.e - cu.tb);
-  const int nv = __shfl(cu.my_nv, cu.e - cu.tb);
-  it.e = cu.e;
-  it.u = u;
-  it.tile = cu.t;
-  it.nv = nv - cu.t * TS;
-  it.last = (cu.t + 1) * TS >= nv;
-  if (it.last) {
-    ++cu.e;
-    cu.t = 0;
-  } else {
-    ++cu.t;
-  }
-  return true;
-}
-
-__device__ __forceinline__ bool full_block(const Ctx &c, int eb, Cursor &cu, FullItem (&it)[2]) {
-  if (!full_next(c, eb, cu, it[0])) return false;
-  if (!full_next(c, eb, cu, it[1])) {
-    it[1] = it[0];
-    it[1].nv = 0;
-    it[1].last = false;
-  }
-  return true;
 }
 
 template <int D>
-__device__ __forceinline__ const uint16_t *tile_ptr(const Ctx &c, const FullItem &it) {
-  return c.st->pages + page_offset(*c.g, c.b, it.u, c.h) + (size_t)it.tile * 2 * TS * D;
+__device__ __forceinline__ const uint16_t *ftile_ptr(const Ctx &c, const FBlock &fb, int s) {
+  return c.st->pages + page_offset(*c.g, c.b, fb.u[s], c.h) + (size_t)fb.tile[s] * 2 * TS * D;
 }
 
 template <int D>
 __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
-  constexpr int KB = D / 32, CT = D / 16;
+  constexpr int KB = D / 32, CP = D / 32;
+  const int tpw = c.g->tpw;
+  const int n_tiles = (eb - ea) * tpw;
+  const int n_blocks = (n_tiles + 1) >> 1;
   bf16x8 bq[KB];
   query_bf16<D>(c, bq);
-  Cursor cu;
-  cu.e = ea;
-  cu.t = 0;
-  cu.tb = ea;
-  load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
-  FullItem cur[2], nxt[2];
-  full_block(c, eb, cu, cur);
-  uint4 kr[2][KB];
-  uint2 vr[2][CT];
+  int ids_a = ids_fetch(c, ea);
+  int ids_b = ids_fetch(c, ea + (2 * min(1, n_blocks - 1)) / tpw);
+  FBlock cur, nxt;
+  fblock_make(c, ea, n_tiles, 0, ids_a, cur);
+  uint4 kr[2][KB], vr[2][CP];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint16_t *kt = tile_ptr<D>(c, cur[t]);
+  for (int s = 0; s < 2; ++s) {
+    const uint16_t *kt = ftile_ptr<D>(c, cur, s);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) kr[s][kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) vr[t][ct] = *(const uint2 *)(kt + TS * D + (ct * 64 + c.lane) * 4);
+    for (int cp = 0; cp < CP; ++cp) vr[s][cp] = *(const uint4 *)(kt + TS * D + (cp * 64 + c.lane) * 8);
   }
-  float rho = 0.0f;
-  for (;;) {
-    const bool more = full_block(c, eb, cu, nxt);
-    if (!more) {   // the last step reloads its own tiles: the same loads every step
-      nxt[0] = cur[0];
-      nxt[1] = cur[1];
-    }
+  for (int i = 0; i < n_blocks; ++i) {
+    // unit ids two blocks ahead; the next block's tiles (the last block re-reads itself)
+    const int ids_c = ids_fetch(c, ea + (2 * min(i + 2, n_blocks - 1)) / tpw);
+    fblock_make(c, ea, n_tiles, min(i + 1, n_blocks - 1), ids_b, nxt);
     floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -435,46 +443,44 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
       for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t *kn = tile_ptr<D>(c, nxt[t]);
+      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(kn + (kb * 64 + c.lane) * 8);
     }
-    const int nv[2] = {c.has_q ? cur[0].nv : 0, c.has_q ? cur[1].nv : 0};
+    const int nv[2] = {c.has_q ? cur.nv[0] : 0, c.has_q ? cur.nv[1] : 0};
     float p[2][4], ts[2];
-    softmax_block<D, 2>(ws, s, c.scale_log2, nv, c.lq, p, ts, rho);
-    rho += ts[0];
-    if (cur[0].last) {
-      emit_mass(c, cur[0].e, rho, ws.m);
-      rho = 0.0f;
-    }
-    rho += ts[1];
-    if (cur[1].nv > 0 && cur[1].last) {
-      emit_mass(c, cur[1].e, rho, ws.m);
-      rho = 0.0f;
+    softmax_block<D, 2>(ws, s, c.scale_log2, nv, c.lq, p, ts);
+    {
+      // tpw == 1: each slot is a unit; tpw == 2: the block is one unit
+      const int e[2] = {cur.e[0], cur.e[1]};
+      const bool ok[2] = {true, tpw == 1 && cur.nv[1] > 0};
+      const float rho[2] = {tpw == 1 ? ts[0] : ts[0] + ts[1], ts[1]};
+      store_mass<2>(c, e, ok, rho, ws.m);
     }
     // rows h carry bf16(p), rows G+h carry bf16(p - bf16(p))
     bf16x8 ap;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float hi = (float)(__bf16)p[t][i];
-        ap[t * 4 + i] = (__bf16)(c.is_lo ? p[t][i] - hi : p[t][i]);
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float hi = (float)(__bf16)p[t][i2];
+        ap[t * 4 + i2] = (__bf16)(c.is_lo ? p[t][i2] - hi : p[t][i2]);
       }
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const uint4 vv = make_uint4(vr[0][ct].x, vr[0][ct].y, vr[1][ct].x, vr[1][ct].y);
-      ws.acc[ct] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, vv), ws.acc[ct]);
+    for (int cp = 0; cp < CP; ++cp) {
+      const uint4 v0 = make_uint4(vr[0][cp].x, vr[0][cp].y, vr[1][cp].x, vr[1][cp].y);
+      const uint4 v1 = make_uint4(vr[0][cp].z, vr[0][cp].w, vr[1][cp].z, vr[1][cp].w);
+      ws.acc[2 * cp] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * cp]);
+      ws.acc[2 * cp + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * cp + 1]);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t *kn = tile_ptr<D>(c, nxt[t]);
+      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) vr[t][ct] = *(const uint2 *)(kn + TS * D + (ct * 64 + c.lane) * 4);
+      for (int cp = 0; cp < CP; ++cp) vr[t][cp] = *(const uint4 *)(kn + TS * D + (cp * 64 + c.lane) * 8);
     }
-    if (!more) break;
-    cur[0] = nxt[0];
-    cur[1] = nxt[1];
+    cur = nxt;
+    ids_b = ids_c;
   }
 }
 
@@ -483,113 +489,118 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
 
 constexpr int QT = 4;   // quantized tiles per block
 
-struct QuantBuf {
-  uint4 k[QT];      // (key code dwords, value code dwords) of each tile
-  uint2 p[QT];      // this lane's 8 bytes of the tile's window key params
-  uint32_t vp[QT];  // this lane's 4 bytes of the tile's value params
+struct QBuf {
+  uint4 code[QT];   // the lane's key code dwords, then value code dwords, of each tile
+  uint2 kp[QT];     // the lane's 8 bytes of each window's key params (window slots)
+  uint32_t vp[QT];  // the lane's 4 bytes of each tile's value params
 };
-struct QuantItem {
+struct QBlock {
   int e, nwin;
-  int u[QT];
+  int u[QT];        // window slots; spare slots repeat slot 0
 };
-
-__device__ __forceinline__ bool quant_next(const Ctx &c, int eb, Cursor &cu, QuantItem &it) {
-  if (cu.e >= eb) return false;
-  const int per = QT / c.g->tpw;
-  const int nw = min(per, eb - cu.e);
-  if (cu.e + nw > cu.tb + 64) {
-    cu.tb = cu.e;
-    load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
-  }
-  it.e = cu.e;
-  it.nwin = nw;
-#pragma unroll
-  for (int j = 0; j < QT; ++j) it.u[j] = __shfl(cu.my_u, cu.e - cu.tb + (j < nw ? j : 0));
-  cu.e += nw;
-  return true;
-}
 
 // window slot and tile-in-window of block tile j
 __device__ __forceinline__ int qt_win(int j, int tpw) { return tpw == 1 ? j : j >> 1; }
 
-template <int D>
-__device__ __forceinline__ void quant_load(const Ctx &c, const QuantItem &it, QuantBuf &qb) {
-  constexpr int NKD = D / 64;
-  const Geom &g = *c.g;
-  const int tpw = g.tpw;
+__device__ __forceinline__ void qblock_make(const Ctx &c, int ea, int eb, int i, int ids, QBlock &qb) {
+  const int per = QT / c.g->tpw;
+  const int e0 = ea + i * per;
+  qb.e = e0;
+  qb.nwin = min(per, eb - e0);
 #pragma unroll
-  for (int j = 0; j < QT; ++j) {
-    const int w = qt_win(j, tpw);
-    const int tj = j - w * tpw;
-    const int u = w < it.nwin ? (tpw == 1 ? it.u[j] : it.u[j >> 1]) : it.u[0];   // spare slots repeat window 0
-    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, u, c.h);
-    const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
-    const uint32_t *kc = (const uint32_t *)T;
-    const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
-    uint4 wv;
-    wv.x = kc[c.lane];
-    wv.y = NKD > 1 ? kc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
-    wv.z = vc[c.lane];
-    wv.w = NKD > 1 ? vc[(NKD > 1 ? 64 : 0) + c.lane] : 0u;
-    qb.k[j] = wv;
-    qb.p[j] = c.lane * 8 < g.kparam_bytes ? *(const uint2 *)(Lb + c.lane * 8) : make_uint2(0, 0);
-    qb.vp[j] = c.lane * 4 < g.tile_vparam_bytes
-                   ? ((const uint32_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes))[c.lane]
-                   : 0u;
+  for (int w = 0; w < QT; ++w) {
+    const int ww = w < qb.nwin ? w : 0;
+    qb.u[w] = entry_id(c, e0 + ww, __builtin_amdgcn_readlane(ids, ww));
   }
 }
 
 template <int D>
-__device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&bqh)[D / 32],
-                                              float sc_quant, const QuantItem &it, const QuantBuf &qb) {
-  constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
+__device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf &buf) {
+  constexpr int NKD = D / 64;
   const Geom &g = *c.g;
   const int tpw = g.tpw;
-  // stage key params (one slot per window) and value params (one slot per tile)
+  const int kl = c.lane & (g.kparam_bytes / 8 - 1);       // lanes past the params repeat them
+  const int vl = c.lane & (g.tile_vparam_bytes / 4 - 1);
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const int w = qt_win(j, tpw);
-    if (j - w * tpw == 0 && c.lane * 8 < g.kparam_bytes) *(uint2 *)(c.kp_lds + w * 2 * D + c.lane * 4) = qb.p[j];
-    if (c.lane * 4 < g.tile_vparam_bytes) ((uint32_t *)(c.vp_lds + j * 2 * D))[c.lane] = qb.vp[j];
+    const int tj = j - w * tpw;
+    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h);
+    const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
+    if (NKD == 2) {
+      buf.code[j] = *(const uint4 *)(T + c.lane * 16);
+    } else {
+      const uint2 cw = *(const uint2 *)(T + c.lane * 8);
+      buf.code[j] = make_uint4(cw.x, cw.y, 0u, 0u);
+    }
+    buf.vp[j] = ((const uint32_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes))[vl];
+  }
+#pragma unroll
+  for (int w = 0; w < QT; ++w) buf.kp[w] = *(const uint2 *)(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
+}
+
+template <int D>
+__device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&bqh)[D / 32],
+                                              float sc_quant, const QBlock &qb, const QBuf &buf) {
+  constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
+  const Geom &g = *c.g;
+  const int tpw = g.tpw;
+  const int nws = QT / tpw;                                  // window slots per block
+  const int kl = c.lane & (g.kparam_bytes / 8 - 1);
+  const int vl = c.lane & (g.tile_vparam_bytes / 4 - 1);
+  // stage key params (one slot per window) and value params (one slot per tile)
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    *(uint2 *)(c.kp_lds + j * 2 * D + kl * 4) = buf.kp[j];
+    ((uint32_t *)(c.vp_lds + j * 2 * D))[vl] = buf.vp[j];
   }
   wave_lds_sync();
   int nv[QT];
 #pragma unroll
-  for (int j = 0; j < QT; ++j) {
-    const int w = qt_win(j, tpw);
-    nv[j] = (c.has_q && w < it.nwin) ? g.window - (j - w * tpw) * TS : 0;
+  for (int j = 0; j < QT; ++j) nv[j] = (c.has_q && qt_win(j, tpw) < qb.nwin) ? g.window - (j - qt_win(j, tpw) * tpw) * TS : 0;
+  // key-zero term sum_c q_c z_c of every window at once: A rows r are the
+  // zero vectors of window slot r % nws, so register i of every lane holds
+  // the term of window slot i % nws for the lane's column
+  floatx4 zb = {0.f, 0.f, 0.f, 0.f};
+  const int zr = (c.lane & 15) % nws;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const half8 z8 = *(const half8 *)(c.kp_lds + zr * 2 * D + D + kb * 32 + c.lq * 8);
+    zb = mfma_f16_k32(z8, bqh[kb], zb);
   }
   // scores of the QT tiles, k-blocks outermost so the four MFMA chains interleave
   floatx4 s[QT];
 #pragma unroll
-  for (int j = 0; j < QT; ++j) s[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < QT; ++j) {
+    const float z = tpw == 1 ? zb[j & 3] : zb[(j >> 1) & 3];
+    s[j] = floatx4{z, z, z, z};
+  }
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int j = 0; j < QT; ++j) {
       const half_t *kp = c.kp_lds + qt_win(j, tpw) * 2 * D;
       const half8 s8 = *(const half8 *)(kp + kb * 32 + c.lq * 8);
-      const half8 z8 = *(const half8 *)(kp + D + kb * 32 + c.lq * 8);
       const half8 qhi = bqh[kb] * s8;
       const half8 qlo = __builtin_elementwise_fma(bqh[kb], s8, -qhi);   // exact remainder of q*s
-      const uint32_t kw = (kb >> 1) == 0 ? qb.k[j].x : qb.k[j].y;
-      const half8 a = unpack8(kw, (kb & 1) * 4, c.magic);
+      const uint32_t kw = (kb >> 1) == 0 ? buf.code[j].x : buf.code[j].y;
+      const half8 a = codes8(code_half(kw, kb & 1));
       s[j] = mfma_f16_k32(a, qhi, s[j]);
       s[j] = mfma_f16_k32(a, qlo, s[j]);
-      s[j] = mfma_f16_k32(z8, bqh[kb], s[j]);                           // sum_c q_c z_c
     }
   float p[QT][4], ts[QT];
-  float rho = 0.0f;
-  softmax_block<D, QT>(ws, s, sc_quant, nv, c.lq, p, ts, rho);
-  // masses: window by window
+  softmax_block<D, QT>(ws, s, sc_quant, nv, c.lq, p, ts);
+  {
+    int e[QT];
+    bool ok[QT];
+    float rho[QT];
 #pragma unroll
-  for (int j = 0; j < QT; ++j) {
-    const int w = qt_win(j, tpw);
-    rho += ts[j];
-    if (j - w * tpw == tpw - 1) {
-      if (w < it.nwin) emit_mass(c, it.e + w, rho, ws.m);
-      rho = 0.0f;
+    for (int w = 0; w < QT; ++w) {
+      e[w] = qb.e + w;
+      ok[w] = w < qb.nwin;
+      rho[w] = tpw == 1 ? ts[w] : (w < 2 ? ts[2 * w] + ts[2 * w + 1] : 0.0f);
     }
+    store_mass<QT>(c, e, ok, rho, ws.m);
   }
   // fp16 limbs of p; (P1, P2) = (0, phi) on hi lanes, (phi, plo) on lo lanes:
   // one FMA chain then yields fp16(p*s) on hi rows and the remainder on lo rows
@@ -621,10 +632,16 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const int ct = grp * 2 + c2;
-        const uint32_t v0 = (ct >> 2) == 0 ? qb.k[j0].z : qb.k[j0].w;
-        const uint32_t v1 = (ct >> 2) == 0 ? qb.k[j1].z : qb.k[j1].w;
-        const half8 bc = __builtin_shufflevector(unpack4(v0, (ct & 3) * 2, c.magic), unpack4(v1, (ct & 3) * 2, c.magic),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint32_t v0 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j0].z : buf.code[j0].y)
+                                           : buf.code[j0].w;
+        const uint32_t v1 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j1].z : buf.code[j1].y)
+                                           : buf.code[j1].w;
+        // tokens (0,1) of the lane's quad from the low half, (2,3) from the high half; byte = ct % 4
+        const half4 b0 = __builtin_shufflevector(fp4_pair_sel(code_half(v0, 0), ct), fp4_pair_sel(code_half(v0, 1), ct),
+                                                 0, 1, 2, 3);
+        const half4 b1 = __builtin_shufflevector(fp4_pair_sel(code_half(v1, 0), ct), fp4_pair_sel(code_half(v1, 1), ct),
+                                                 0, 1, 2, 3);
+        const half8 bc = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
         ws.acc[ct] = mfma_f16_k32(ag, bc, ws.acc[ct]);
       }
     }
@@ -636,7 +653,6 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     ws.zacc = mfma_f16_k32(__builtin_shufflevector(P2[j0], P2[j1], 0, 1, 2, 3, 4, 5, 6, 7),
                            __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
   }
-  (void)NKD;
   wave_lds_sync();
 }
 
@@ -645,28 +661,28 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
   half8 bqh[D / 32];
   const float sc_quant = query_f16<D>(c, bqh);
-  Cursor cu;
-  cu.e = ea;
-  cu.t = 0;
-  cu.tb = ea;
-  load_table(c, cu.tb, eb, cu.my_u, cu.my_nv);
-  // two-slot ring: one block in flight while one computes; the slot past the
-  // end reloads the current block so that every step issues the same loads
-  QuantItem i0, i1;
-  QuantBuf b0, b1;
-  quant_next(c, eb, cu, i0);
-  quant_load<D>(c, i0, b0);
-  for (;;) {
-    bool v1 = quant_next(c, eb, cu, i1);
-    if (!v1) i1 = i0;
-    quant_load<D>(c, i1, b1);
-    quant_compute<D>(ws, c, bqh, sc_quant, i0, b0);
-    if (!v1) break;
-    bool v0 = quant_next(c, eb, cu, i0);
-    if (!v0) i0 = i1;
-    quant_load<D>(c, i0, b0);
-    quant_compute<D>(ws, c, bqh, sc_quant, i1, b1);
-    if (!v0) break;
+  const int per = QT / c.g->tpw;
+  const int n_blocks = (eb - ea + per - 1) / per;
+  // two-slot ring: one block in flight while one computes; unit ids two
+  // blocks ahead; past the end the last block is re-read, so every step
+  // issues the same loads
+  QBlock k0, k1;
+  QBuf b0, b1;
+  const int ids0 = ids_fetch(c, ea);
+  int ids1 = ids_fetch(c, ea + min(1, n_blocks - 1) * per);
+  qblock_make(c, ea, eb, 0, ids0, k0);
+  quant_load<D>(c, k0, b0);
+  for (int i = 0;; i += 2) {
+    const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
+    qblock_make(c, ea, eb, min(i + 1, n_blocks - 1), ids1, k1);
+    quant_load<D>(c, k1, b1);
+    quant_compute<D>(ws, c, bqh, sc_quant, k0, b0);
+    if (i + 1 >= n_blocks) break;
+    ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
+    qblock_make(c, ea, eb, min(i + 2, n_blocks - 1), ids2, k0);
+    quant_load<D>(c, k0, b0);
+    quant_compute<D>(ws, c, bqh, sc_quant, k1, b1);
+    if (i + 2 >= n_blocks) break;
   }
 }
 
@@ -681,7 +697,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = blockIdx.x / S;
   const int h = bh % g.Hkv;
   const int b = bh / g.Hkv;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: ranges and loops stay scalar
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int lq = lane >> 4;
@@ -731,7 +747,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.is_hi = is_hi;
   c.is_lo = is_lo;
   c.has_q = is_hi || is_lo;
-  c.magic = magic_in_vgpr();
   c.scale_log2 = scale_log2;
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
@@ -843,9 +858,13 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   const int E = L.count();
   const int e = chunk * blockDim.x + threadIdx.x;
   if (e >= E) return;
-  bool quant;
-  int n_valid;
-  const int u = entry_unit(g, st, si, L, b, e, quant, n_valid);
+  int u;
+  if (e < L.s0)
+    u = 0;
+  else if (e - L.s0 < L.nF + L.nQ)
+    u = st.routed[b * g.U + (e - L.s0)];
+  else
+    u = L.r0 + (e - L.s0 - L.nF - L.nQ);
   float total = 0.0f;
 #pragma unroll 8
   for (int h = 0; h < g.Hkv; ++h) {
@@ -991,12 +1010,9 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
 #pragma unroll
           for (int j = 0; j < 8; ++j) sk[tile * TS + t][c0 + j] = bf16_to_f32(src[j]);
         }
-        for (int ci = threadIdx.x; ci < TS * D / 4; ci += blockDim.x) {
-          const int ct = ci / 64, l = ci % 64;
-          const int c = ct * 16 + l % 16, t0 = (l / 16) * 4;
-          const uint16_t *src = vt + ci * 4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sv[tile * TS + t0 + j][c] = bf16_to_f32(src[j]);
+        for (int el = threadIdx.x; el < TS * D; el += blockDim.x) {
+          const int t = el / D, c = el % D;
+          sv[tile * TS + t][c] = bf16_to_f32(vt[v_tile_index(t, c)]);
         }
       }
       __syncthreads();
@@ -1034,35 +1050,30 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
         vp[vparam_index(g, t % TS, grp, 1)] = z16;
       }
       __syncthreads();
-      // 3. codes in the matrix-core operand order
+      // 3. codes in the matrix-core operand order: one thread per code dword,
+      // walking its 16 slots (the inverse of kcode_slot / vcode_slot)
       for (int tile = 0; tile < g.tpw; ++tile) {
-        uint32_t *kc = (uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes);
-        uint32_t *vc = (uint32_t *)((uint8_t *)kc + g.tile_kcode_bytes);
-        for (int dw = threadIdx.x; dw < (D / 64) * 64; dw += blockDim.x) {
+        uint32_t *tc = (uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes);
+        constexpr int NKD = D / 64;
+        for (int dw = threadIdx.x; dw < NKD * 64; dw += blockDim.x) {
           const int j = dw / 64, l = dw % 64;
           uint32_t kword = 0u, vword = 0u;
 #pragma unroll
           for (int p = 0; p < 16; ++p) {
-            const int i = p & 7, hi = p >> 3;
-            // key slot p: pair i of k-blocks 2j, 2j+1
-            {
-              const int kb = 2 * j + (i >> 2), e = 2 * (i & 3) + hi;
-              const int c = kb * 32 + (l / 16) * 8 + e, t = l % 16;
+            const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
+            {  // key slot p: k-block 2j+par, channel pair m, element hi
+              const int c = (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi, t = l % 16;
               const int tt = tile * TS + t;
-              uint32_t code = tt < W ? quant_code(sk[tt][c], s_ks[c], s_kz[c], levels) : 0u;
-              kword |= code << (2 * p);
+              kword |= (tt < W ? quant_code(sk[tt][c], s_ks[c], s_kz[c], levels) : 0u) << (2 * p);
             }
-            // value slot p: pair i of column tiles 4j..4j+3
-            {
-              const int ct = 4 * j + (i >> 1);
-              const int t = 4 * (l / 16) + 2 * (i & 1) + hi, c = ct * 16 + l % 16;
+            {  // value slot p: column tile 4j+m, token pair par of the quad, element hi
+              const int c = (4 * j + m) * 16 + l % 16, t = 4 * (l / 16) + 2 * par + hi;
               const int tt = tile * TS + t;
-              uint32_t code = tt < W ? quant_code(sv[tt][c], s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u;
-              vword |= code << (2 * p);
+              vword |= (tt < W ? quant_code(sv[tt][c], s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u) << (2 * p);
             }
           }
-          kc[dw] = kword;
-          vc[dw] = vword;
+          tc[l * 2 * NKD + j] = kword;
+          tc[l * 2 * NKD + NKD + j] = vword;
         }
       }
       __syncthreads();
@@ -1070,20 +1081,19 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
       // promote: rebuild the full-precision tiles from the ledger
       for (int tile = 0; tile < g.tpw; ++tile) {
         const uint8_t *T = Lb + g.kparam_bytes + tile * g.tile_block_bytes;
-        const uint32_t *kc = (const uint32_t *)T;
-        const uint32_t *vc = (const uint32_t *)(T + g.tile_kcode_bytes);
+        const uint32_t *tc = (const uint32_t *)T;
         const half_t *vp = (const half_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes);
         uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
         uint16_t *vt = kt + TS * D;
         for (int el = threadIdx.x; el < TS * D; el += blockDim.x) {
           const int t = el / D, c = el % D;
           int dw, sh;
-          kcode_slot(t, c, dw, sh);
-          const float kcode = (float)((kc[dw] >> sh) & 3u);
+          kcode_slot(t, c, D / 64, dw, sh);
+          const float kcode = (float)((tc[dw] >> sh) & 3u);
           const float kx = __builtin_fmaf(kcode, (float)kparam[c], (float)kparam[D + c]);
           kt[k_tile_index(t, c)] = f32_to_bf16_rne(kx);
-          vcode_slot(t, c, dw, sh);
-          const float vcode = (float)((vc[dw] >> sh) & 3u);
+          vcode_slot(t, c, D / 64, dw, sh);
+          const float vcode = (float)((tc[dw] >> sh) & 3u);
           const float vx = __builtin_fmaf(vcode, (float)vp[vparam_index(g, t, c / 32, 0)],
                                           (float)vp[vparam_index(g, t, c / 32, 1)]);
           vt[v_tile_index(t, c)] = f32_to_bf16_rne(vx);
@@ -1328,15 +1338,14 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
           if (what == QKV_EXPORT_KCODES) {
             c = e / W;
             t = e % W;
-            kcode_slot(t % TS, c, dw, sh);
+            kcode_slot(t % TS, c, D / 64, dw, sh);
             const uint32_t *kc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
             val |= ((kc[dw] >> sh) & 3u) << (2 * k);
           } else {
             t = e / D;
             c = e % D;
-            vcode_slot(t % TS, c, dw, sh);
-            const uint32_t *vc =
-                (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes + g.tile_kcode_bytes);
+            vcode_slot(t % TS, c, D / 64, dw, sh);
+            const uint32_t *vc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
             val |= ((vc[dw] >> sh) & 3u) << (2 * k);
           }
         }
