@@ -78,12 +78,10 @@ void make_geom(const qkv_config *c, Geom &g) {
   g.tile_vparam_bytes = 4 * (g.d / 32) * 16;
   g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
   g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;
-  g.cost_full = g.page_unit_elems * 2;
-  g.cost_quant = g.ledger_unit_bytes;
   int S = c->n_splits;
-  if (S == 0) {   // enough workgroups to fill 256 compute units several times over
+  if (S == 0) {   // one resident round: 512 workgroups = 2 per compute unit at 2 waves per SIMD
     const int pairs = g.B * g.Hkv;
-    S = (2048 + pairs - 1) / pairs;
+    S = (512 + pairs - 1) / pairs;
     const int cap = g.U / 4 > 1 ? g.U / 4 : 1;
     if (S > cap) S = cap;
     if (S > 64) S = 64;

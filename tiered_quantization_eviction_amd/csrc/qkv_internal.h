@@ -47,8 +47,6 @@ struct Geom {
   int tile_vcode_bytes;
   int tile_vparam_bytes; // 4 token quads * d/32 groups * 16 B
   int tile_block_bytes;
-  // bytes one KV head reads for one unit (split balancing)
-  int cost_full, cost_quant;
 };
 
 struct State {

@@ -153,28 +153,7 @@ hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, cons
 
 struct EntryList {
   int s0, nF, nQ, nR, r0;
-  long long cF, cQ;
   __device__ int count() const { return s0 + nF + nQ + nR; }
-  __device__ long long total_cost() const { return (long long)(s0 + nF + nR) * cF + (long long)nQ * cQ; }
-  // cost position where entry e starts
-  __device__ long long cost_start(int e) const {
-    const long long A = s0 + nF;
-    if (e <= A) return e * cF;
-    if (e <= A + nQ) return A * cF + (e - A) * cQ;
-    return A * cF + (long long)nQ * cQ + (e - A - nQ) * cF;
-  }
-  // first entry whose cost-start is >= x
-  __device__ int first_at(long long x) const {
-    int E = count();
-    if (x <= 0) return 0;
-    long long A = s0 + nF;
-    if (x <= A * cF) return (int)((x + cF - 1) / cF);
-    long long x2 = x - A * cF;
-    if (x2 <= (long long)nQ * cQ) return (int)(A + (x2 + cQ - 1) / cQ);
-    long long x3 = x2 - (long long)nQ * cQ;
-    long long e = A + nQ + (x3 + cF - 1) / cF;
-    return (int)(e < E ? e : E);
-  }
 };
 
 __device__ inline EntryList make_list(const Geom &g, const State &st, const StepInfo &si, int b) {
@@ -184,8 +163,6 @@ __device__ inline EntryList make_list(const Geom &g, const State &st, const Step
   L.nQ = st.routed_nq[b];
   L.nR = si.r1 >= si.r0 ? si.r1 - si.r0 + 1 : 0;
   L.r0 = si.r0;
-  L.cF = g.cost_full;
-  L.cQ = g.cost_quant;
   return L;
 }
 
@@ -712,14 +689,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float sm_l[ATT_WAVES][8];
   __shared__ float sm_o[ATT_WAVES][8][D];
 
-  // ---- this split's entry range, cut into one contiguous sub-range per wave ----
+  // ---- this wave's share: slice gi of 4*S of the full-precision entries
+  // (sink, ranked full, recent) and the same slice of the quantized windows,
+  // so every workgroup (and so every XCD and CU) gets the same mix of
+  // bandwidth-bound and arithmetic-bound work ----
   const EntryList L = make_list(g, st, si, b);
-  const long long C = L.total_cost();
-  const int e_begin = L.first_at(C * split / S);
-  const int e_end = L.first_at(C * (split + 1) / S);
-  const long long c0 = L.cost_start(e_begin), c1 = L.cost_start(e_end);
-  const int w_begin = L.first_at(c0 + (c1 - c0) * wave / ATT_WAVES);
-  const int w_end = L.first_at(c0 + (c1 - c0) * (wave + 1) / ATT_WAVES);
+  const int A = L.s0 + L.nF, AQ = A + L.nQ, E = L.count();
+  const int nB = A + (E - AQ);
+  const int NS = 4 * S, gi = split * 4 + wave;
+  const int vb0 = (int)((long long)nB * gi / NS), vb1 = (int)((long long)nB * (gi + 1) / NS);
+  const int q0 = A + (int)((long long)L.nQ * gi / NS), q1 = A + (int)((long long)L.nQ * (gi + 1) / NS);
+  // full-precision virtual range [vb0, vb1) -> entries [f0, f1) below A and [r0e, r1e) from AQ on
+  const int f0 = min(vb0, A), f1 = min(vb1, A);
+  const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
 
   WaveState<D> ws;
 #pragma unroll
@@ -751,10 +733,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
-  const int A = L.s0 + L.nF, AQ = A + L.nQ;
-  run_full<D>(ws, c, w_begin, min(w_end, A));        // sink and ranked full-precision windows
-  run_quant<D>(ws, c, max(w_begin, A), min(w_end, AQ));
-  run_full<D>(ws, c, max(w_begin, AQ), w_end);        // windows not yet ranked
+  if (gi & 1) {   // alternate the order so that neighbouring waves are in different phases
+    run_quant<D>(ws, c, q0, q1);
+    run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
+    run_full<D>(ws, c, r0e, r1e);    // windows not yet ranked
+  } else {
+    run_full<D>(ws, c, f0, f1);
+    run_full<D>(ws, c, r0e, r1e);
+    run_quant<D>(ws, c, q0, q1);
+  }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
   float l_tot = ws.l + __shfl_xor(ws.l, 16);
