@@ -203,13 +203,15 @@ enum {
 };
 int qkv_info(const qkv_cache *cache, int32_t what, int64_t *value);
 
-/* Kernel timing: after qkv_profile_start(cache, n), the next n qkv_decode_attend
- * calls record a pair of HIP events on their stream around the attention
- * kernel (not the merge).  qkv_profile_read waits for the last pair and writes
- * the recorded durations in milliseconds (n entries, at most as many as were
- * started).  Events are created by qkv_profile_start (no device memory) and
- * released by the next start or by qkv_destroy. */
-int qkv_profile_start(qkv_cache *cache, int32_t n);
+/* Kernel timing: after qkv_profile_start(cache, n, stride), every stride-th of
+ * the following qkv_decode_attend calls (the 1st, the (1+stride)-th, ...)
+ * records a pair of HIP events on its stream around the attention kernel (not
+ * the merge), n pairs in all.  Sampling keeps the event packets, which delay
+ * the next launch, out of most steps.  qkv_profile_read waits for the last pair
+ * and writes the recorded durations in milliseconds (n entries, at most as many
+ * as were recorded).  Events are created by qkv_profile_start (no device
+ * memory) and released by the next start or by qkv_destroy.  stride >= 1. */
+int qkv_profile_start(qkv_cache *cache, int32_t n, int32_t stride);
 int qkv_profile_read(qkv_cache *cache, float *ms, int32_t n);
 
 /* Device-latched status: waits for `stream`, returns QKV_OK or QKV_ERANGE. */

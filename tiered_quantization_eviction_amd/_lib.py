@@ -67,7 +67,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_export_bytes.argtypes = [_vp, _i32]
         L.qkv_info.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_int64)]
         L.qkv_status.argtypes = [_vp, _vp]
-        L.qkv_profile_start.argtypes = [_vp, _i32]
+        L.qkv_profile_start.argtypes = [_vp, _i32, _i32]
         L.qkv_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _i32]
         _LIB = L
     return _LIB
@@ -184,8 +184,9 @@ class Cache:
         _check(_lib().qkv_info(self.h, INFO[what], ctypes.byref(v)), "qkv_info")
         return int(v.value)
 
-    def profile_start(self, n: int) -> None:
-        _check(_lib().qkv_profile_start(self.h, int(n)), "qkv_profile_start")
+    def profile_start(self, n: int, stride: int = 1) -> None:
+        """Time every stride-th of the next attention launches, n in all."""
+        _check(_lib().qkv_profile_start(self.h, int(n), int(stride)), "qkv_profile_start")
 
     def profile_read(self, n: int):
         buf = (ctypes.c_float * n)()

@@ -23,7 +23,7 @@ struct qkv_cache {
   long long routes;
   // kernel timing
   hipEvent_t *ev;   // 2 * ev_n events
-  int ev_n, ev_next;
+  int ev_n, ev_next, ev_stride, ev_calls;
 };
 
 namespace {
@@ -126,6 +126,7 @@ StepInfo step_info(const qkv_cache *c) {
   si.has_sink = (c->g.n_sink > 0 && c->N > 0) ? 1 : 0;
   si.r0 = c->r0;
   si.r1 = c->N > c->g.n_sink ? unit_of(c->g, c->N - 1) : 0;
+  si.n_routed = c->routed;
   return si;
 }
 
@@ -198,8 +199,8 @@ int qkv_destroy(qkv_cache *cache) {
   return QKV_OK;
 }
 
-int qkv_profile_start(qkv_cache *c, int32_t n) {
-  if (!c || n < 0 || n > (1 << 20)) return QKV_EINVAL;
+int qkv_profile_start(qkv_cache *c, int32_t n, int32_t stride) {
+  if (!c || n < 0 || n > (1 << 20) || stride < 1) return QKV_EINVAL;
   free_events(c);
   if (n == 0) return QKV_OK;
   c->ev = new (std::nothrow) hipEvent_t[2 * n];
@@ -214,6 +215,8 @@ int qkv_profile_start(qkv_cache *c, int32_t n) {
   }
   c->ev_n = n;
   c->ev_next = 0;
+  c->ev_stride = stride;
+  c->ev_calls = 0;
   return QKV_OK;
 }
 
@@ -240,7 +243,7 @@ int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, 
   if (!c || !q || !out) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (c->ev && c->ev_next < c->ev_n) {
+  if (c->ev && c->ev_next < c->ev_n && c->ev_calls++ % c->ev_stride == 0) {
     e0 = c->ev[2 * c->ev_next];
     e1 = c->ev[2 * c->ev_next + 1];
     c->ev_next++;

@@ -73,6 +73,7 @@ struct StepInfo {
   int N;        // tokens appended per sequence
   int r0, r1;   // recent (not yet ranked) windows: units r0..r1 (r1 < r0: none)
   int has_sink; // sink entry present
+  int n_routed; // ranked (full + quantized) windows per sequence after the last routing event
 };
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -218,12 +218,14 @@ struct Ctx {
   const StepInfo *si;
   const EntryList *L;
   const uint16_t *qrow;   // this lane's query row (head of its column; head 0 for other lanes)
-  int b, h, lane, col, lq, G;
+  const uint16_t *qbase;  // query rows of the KV head's G heads
+  int b, h, lane, col, lq, G, hc;
   bool is_hi, is_lo, has_q;
   float scale_log2;
   float *mass_row;        // [(U+1)][G][2] of this (sequence, KV head); slot U is the spare
   half_t *kp_lds;
   half_t *vp_lds;
+  half_t *qs_lds;         // per window slot: q*s limbs [2][G][d] (fp16)
 };
 
 // unit id of entry e; `raw` is the routed-list value fetched for it (used
@@ -277,31 +279,56 @@ __device__ __forceinline__ void query_bf16(const Ctx &c, bf16x8 (&bq)[D / 32]) {
     bq[kb] = __builtin_bit_cast(bf16x8, raw);
   }
 }
-// query as fp16 scaled by 2^-e (per head, |q| 2^-e < 1) so that q*s never leaves fp16
+// Query for quantized tiles, as fp16 scaled by 2^-e (one e for the KV head's
+// G heads, |q| 2^-e < 1, so q*s never leaves fp16).  qc: the compact operand
+// of lane L -- heads (L/16) + 4r, channels 8*(L%16) .. +7 -- from which each
+// window's q*s limbs are formed; bz: the B operand of the key-zero term
+// (head h in column h, zero elsewhere).  Returns the softmax scale of the
+// scores so formed.
 template <int D>
-__device__ __forceinline__ float query_f16(const Ctx &c, half8 (&bqh)[D / 32]) {
-  uint4 raw[D / 32];
+__device__ __forceinline__ float query_f16(const Ctx &c, half8 (&qc)[2], half8 (&bz)[D / 32]) {
+  constexpr int KB = D / 32;
+  const int c0 = 8 * ((c.lane & 15) % (D / 8));
+  uint4 rc[2];
   float amax = 0.0f;
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) {
-    const uint32_t keep = c.has_q ? 0xffffffffu : 0u;
-    const uint4 r = *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8);
-    raw[kb] = make_uint4(r.x & keep, r.y & keep, r.z & keep, r.w & keep);
-    const uint16_t *e = (const uint16_t *)&raw[kb];
+  for (int r = 0; r < 2; ++r) {
+    const int hh = min((c.lane >> 4) + 4 * r, c.G - 1);
+    rc[r] = *(const uint4 *)(c.qbase + (size_t)hh * D + c0);
+    const uint16_t *e = (const uint16_t *)&rc[r];
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
   }
   amax = max_x16(amax);
   amax = max_x32(amax);
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
   int qexp = 0;
   if (amax > 0.0f) frexpf(amax, &qexp);
 #pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) {
-    const uint16_t *e = (const uint16_t *)&raw[kb];
+  for (int r = 0; r < 2; ++r) {
+    const uint16_t *e = (const uint16_t *)&rc[r];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bqh[kb][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+    for (int j = 0; j < 8; ++j) qc[r][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+  }
+  const uint32_t keep = c.is_hi ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const uint4 r = *(const uint4 *)(c.qrow + kb * 32 + c.lq * 8);
+    const uint16_t *e = (const uint16_t *)&r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bz[kb][j] = (half_t)ldexpf(bf16_to_f32(keep ? e[j] : (uint16_t)0), -qexp);
   }
   return ldexpf(c.scale_log2, qexp);
+}
+
+// s + (s of the lane 8 columns away): folds the low-limb column 8+h into
+// column h and vice versa (a row rotation by 8, so both get the same sum)
+__device__ __forceinline__ float fold8(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));   // row_ror:8
+  return x + y;
 }
 
 // online-softmax update for a block of NT 16-token tiles (scores in C layout);
@@ -465,6 +492,10 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
 // flight while one computes ----
 
 constexpr int QT = 4;   // quantized tiles per block
+// LDS strides (halfs), padded by 16 bytes so that rows and slots that are read
+// together fall on different banks
+template <int D> constexpr int PSTR = 2 * D + 8;   // parameter slot: [s(d), z(d)]
+template <int D> constexpr int QSTR = D + 8;       // one q*s row
 
 struct QBuf {
   uint4 code[QT];   // the lane's key code dwords, then value code dwords, of each tile
@@ -517,19 +548,44 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
 }
 
 template <int D>
-__device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&bqh)[D / 32],
-                                              float sc_quant, const QBlock &qb, const QBuf &buf) {
+__device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&qc)[2],
+                                              const half8 (&bz)[D / 32], float sc_quant, const QBlock &qb,
+                                              const QBuf &buf) {
   constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
   const Geom &g = *c.g;
   const int tpw = g.tpw;
   const int nws = QT / tpw;                                  // window slots per block
+  const int G = c.G;
   const int kl = c.lane & (g.kparam_bytes / 8 - 1);
   const int vl = c.lane & (g.tile_vparam_bytes / 4 - 1);
   // stage key params (one slot per window) and value params (one slot per tile)
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
-    *(uint2 *)(c.kp_lds + j * 2 * D + kl * 4) = buf.kp[j];
-    ((uint32_t *)(c.vp_lds + j * 2 * D))[vl] = buf.vp[j];
+    *(uint2 *)(c.kp_lds + j * PSTR<D> + kl * 4) = buf.kp[j];
+    ((uint32_t *)(c.vp_lds + j * PSTR<D>))[vl] = buf.vp[j];
+  }
+  wave_lds_sync();
+  // q*s of each window as two fp16 limbs (high, exact remainder), computed
+  // once per (head, channel) in the compact layout and stored [limb][head][c]
+  {
+    const int c0 = 8 * ((c.lane & 15) % (D / 8));
+#pragma unroll
+    for (int w = 0; w < QT; ++w) {
+      if (w < nws) {
+        const half8 s8 = *(const half8 *)(c.kp_lds + w * PSTR<D> + c0);
+        half_t *qs = c.qs_lds + w * 2 * G * QSTR<D>;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (4 * r < G) {
+            const int hh = (c.lane >> 4) + 4 * r;
+            const half8 hi = qc[r] * s8;
+            const half8 lo = __builtin_elementwise_fma(qc[r], s8, -hi);
+            *(half8 *)(qs + hh * QSTR<D> + c0) = hi;
+            *(half8 *)(qs + (G + hh) * QSTR<D> + c0) = lo;
+          }
+        }
+      }
+    }
   }
   wave_lds_sync();
   int nv[QT];
@@ -537,34 +593,35 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   for (int j = 0; j < QT; ++j) nv[j] = (c.has_q && qt_win(j, tpw) < qb.nwin) ? g.window - (j - qt_win(j, tpw) * tpw) * TS : 0;
   // key-zero term sum_c q_c z_c of every window at once: A rows r are the
   // zero vectors of window slot r % nws, so register i of every lane holds
-  // the term of window slot i % nws for the lane's column
+  // the term of window slot i % nws for the lane's column (high columns only)
   floatx4 zb = {0.f, 0.f, 0.f, 0.f};
   const int zr = (c.lane & 15) % nws;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const half8 z8 = *(const half8 *)(c.kp_lds + zr * 2 * D + D + kb * 32 + c.lq * 8);
-    zb = mfma_f16_k32(z8, bqh[kb], zb);
+    const half8 z8 = *(const half8 *)(c.kp_lds + zr * PSTR<D> + D + kb * 32 + c.lq * 8);
+    zb = mfma_f16_k32(z8, bz[kb], zb);
   }
-  // scores of the QT tiles, k-blocks outermost so the four MFMA chains interleave
+  // scores of the QT tiles: column h takes the high limb, column 8+h the low
+  // limb, one MFMA per k-block; the two are folded after the last k-block
   floatx4 s[QT];
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const float z = tpw == 1 ? zb[j & 3] : zb[(j >> 1) & 3];
     s[j] = floatx4{z, z, z, z};
   }
+  const int qrow = (c.is_lo ? G : 0) + c.hc;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int j = 0; j < QT; ++j) {
-      const half_t *kp = c.kp_lds + qt_win(j, tpw) * 2 * D;
-      const half8 s8 = *(const half8 *)(kp + kb * 32 + c.lq * 8);
-      const half8 qhi = bqh[kb] * s8;
-      const half8 qlo = __builtin_elementwise_fma(bqh[kb], s8, -qhi);   // exact remainder of q*s
+      const half8 bq = *(const half8 *)(c.qs_lds + (qt_win(j, tpw) * 2 * G + qrow) * QSTR<D> + kb * 32 + c.lq * 8);
       const uint32_t kw = (kb >> 1) == 0 ? buf.code[j].x : buf.code[j].y;
-      const half8 a = codes8(code_half(kw, kb & 1));
-      s[j] = mfma_f16_k32(a, qhi, s[j]);
-      s[j] = mfma_f16_k32(a, qlo, s[j]);
+      s[j] = mfma_f16_k32(codes8(code_half(kw, kb & 1)), bq, s[j]);
     }
+#pragma unroll
+  for (int j = 0; j < QT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[j][i] = fold8(s[j][i]);
   float p[QT][4], ts[QT];
   softmax_block<D, QT>(ws, s, sc_quant, nv, c.lq, p, ts);
   {
@@ -600,8 +657,8 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     const int j0 = 2 * pp, j1 = 2 * pp + 1;
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
-      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * 2 * D + (c.lq * NG + grp) * 8);
-      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * 2 * D + (c.lq * NG + grp) * 8);
+      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + grp) * 8);
+      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + grp) * 8);
       const half4 t0 = P1[j0] * s40, t1 = P1[j1] * s41;
       const half4 ag0 = __builtin_elementwise_fma(P2[j0], s40, __builtin_elementwise_fma(P1[j0], s40, -t0));
       const half4 ag1 = __builtin_elementwise_fma(P2[j1], s41, __builtin_elementwise_fma(P1[j1], s41, -t1));
@@ -624,8 +681,8 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     }
     half4 bz0 = zero4, bz1 = zero4;
     if (c.col < NG) {
-      bz0 = *(const half4 *)(c.vp_lds + j0 * 2 * D + (c.lq * NG + c.col) * 8 + 4);
-      bz1 = *(const half4 *)(c.vp_lds + j1 * 2 * D + (c.lq * NG + c.col) * 8 + 4);
+      bz0 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + c.col) * 8 + 4);
+      bz1 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + c.col) * 8 + 4);
     }
     ws.zacc = mfma_f16_k32(__builtin_shufflevector(P2[j0], P2[j1], 0, 1, 2, 3, 4, 5, 6, 7),
                            __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
@@ -636,8 +693,8 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
 template <int D>
 __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
-  half8 bqh[D / 32];
-  const float sc_quant = query_f16<D>(c, bqh);
+  half8 qc[2], bz[D / 32];
+  const float sc_quant = query_f16<D>(c, qc, bz);
   const int per = QT / c.g->tpw;
   const int n_blocks = (eb - ea + per - 1) / per;
   // two-slot ring: one block in flight while one computes; unit ids two
@@ -653,12 +710,12 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
     const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 1, n_blocks - 1), ids1, k1);
     quant_load<D>(c, k1, b1);
-    quant_compute<D>(ws, c, bqh, sc_quant, k0, b0);
+    quant_compute<D>(ws, c, qc, bz, sc_quant, k0, b0);
     if (i + 1 >= n_blocks) break;
     ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 2, n_blocks - 1), ids2, k0);
     quant_load<D>(c, k0, b0);
-    quant_compute<D>(ws, c, bqh, sc_quant, k1, b1);
+    quant_compute<D>(ws, c, qc, bz, sc_quant, k1, b1);
     if (i + 2 >= n_blocks) break;
   }
 }
@@ -679,15 +736,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int col = lane & 15;
   const int lq = lane >> 4;
   const int G = g.G;
-  const bool is_hi = col < G;
-  const bool is_lo = col >= G && col < 2 * G;
-  const int hc = is_hi ? col : (is_lo ? col - G : 0);
+  const bool is_hi = col < G;                   // column h: head h (high limb of quantized-tile scores)
+  const bool is_lo = col >= 8 && col < 8 + G;   // column 8+h: head h again (low limb)
+  const int hc = is_hi ? col : (is_lo ? col - 8 : 0);
 
-  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QT][2 * D];   // key scale/zero per window
-  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QT][2 * D];   // value params per tile
+  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QT][PSTR<D>];   // key scale/zero per window
+  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QT][PSTR<D>];   // value params per tile
   __shared__ float sm_m[ATT_WAVES][8];
   __shared__ float sm_l[ATT_WAVES][8];
   __shared__ float sm_o[ATT_WAVES][8][D];
+  extern __shared__ __attribute__((aligned(16))) half_t s_qs[];   // [ATT_WAVES][window slots][2][G][D+8]
 
   // ---- this wave's share: slice gi of 4*S of the full-precision entries
   // (sink, ranked full, recent) and the same slice of the quantized windows,
@@ -720,6 +778,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.si = &si;
   c.L = &L;
   c.qrow = q + ((size_t)b * g.Hq + (size_t)h * G + hc) * D;
+  c.qbase = q + ((size_t)b * g.Hq + (size_t)h * G) * D;
+  c.hc = hc;
   c.b = b;
   c.h = h;
   c.lane = lane;
@@ -733,6 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
+  c.qs_lds = s_qs + (size_t)wave * (QT / g.tpw) * 2 * G * QSTR<D>;
   if (gi & 1) {   // alternate the order so that neighbouring waves are in different phases
     run_quant<D>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
@@ -753,7 +814,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl_down(ws.acc[ct][i], 4 * G);
+    for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl_down(ws.acc[ct][i], 32);   // rows 8+h onto rows h
 
   // ---- workgroup merge ----
   if (lq == 0 && col < G) {
@@ -812,61 +873,94 @@ __device__ inline void split_stats(const Geom &g, const State &st, int b, int h,
   invL = 1.0f / l;
 }
 
+template <int G>
 __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, StepInfo si, float *__restrict__ out,
                                                            float *__restrict__ mass_out, int n_chunks) {
-  const int S = g.n_splits, G = g.G, D = g.d;
+  constexpr int CH = 8;   // splits / KV heads whose loads are issued together
+  const int S = g.n_splits, D = g.d;
   const int n_out_blocks = g.B * g.Hkv;
   __shared__ float sM[128], sInvL[128];   // Hkv*G = Hq <= 128
   if ((int)blockIdx.x < n_out_blocks) {
+    // outputs of one (sequence, KV head): each thread folds the split
+    // partials of its outputs with the LSE rule on its own
     const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
-    if ((int)threadIdx.x < G) split_stats(g, st, b, h, threadIdx.x, sM[threadIdx.x], sInvL[threadIdx.x]);
-    __syncthreads();
-    const size_t base = (size_t)(b * g.Hkv + h) * S;
+    const float2 *ml = (const float2 *)st.part_ml + (size_t)(b * g.Hkv + h) * S * G;
+    const float *po = st.part_o + (size_t)(b * g.Hkv + h) * S * G * D;
     for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
       const int hh = it / D, c = it % D;
-      const float M = sM[hh];
-      float o = 0.0f;
-#pragma unroll 8
-      for (int s = 0; s < S; ++s) {
-        const float ms = st.part_ml[((base + s) * G + hh) * 2];
-        const float os = st.part_o[((base + s) * G + hh) * D + c];
-        if (ms != neg_inf()) o += os * exp2f(ms - M);
+      float m = neg_inf(), l = 0.0f, o = 0.0f;
+      for (int s0 = 0; s0 < S; s0 += CH) {
+        float2 mls[CH];
+        float os[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const int sp = min(s0 + k, S - 1);
+          mls[k] = ml[sp * G + hh];
+          os[k] = po[(size_t)(sp * G + hh) * D + c];
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          if (s0 + k >= S || mls[k].x == neg_inf()) continue;
+          const float mn = fmaxf(m, mls[k].x);
+          const float a = m == neg_inf() ? 0.0f : exp2f(m - mn), w = exp2f(mls[k].x - mn);
+          l = l * a + mls[k].y * w;
+          o = o * a + os[k] * w;
+          m = mn;
+        }
       }
-      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o * sInvL[hh];
+      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o / l;
     }
     return;
   }
-  // mass chunk
+  // masses of up to 256 live entries of one sequence -> window scores
   const int mb = blockIdx.x - n_out_blocks;
   const int b = mb / n_chunks, chunk = mb % n_chunks;
-  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
-  __syncthreads();
   const EntryList L = make_list(g, st, si, b);
   const int E = L.count();
   const int e = chunk * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+  const int ee = min(e, E - 1);
+  const int raw = st.routed[b * g.U + min(max(ee - L.s0, 0), g.U - 1)];   // issued before the stats wait
+  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
+  __syncthreads();
   int u;
-  if (e < L.s0)
+  if (ee < L.s0)
     u = 0;
-  else if (e - L.s0 < L.nF + L.nQ)
-    u = st.routed[b * g.U + (e - L.s0)];
+  else if (ee - L.s0 < L.nF + L.nQ)
+    u = raw;
   else
-    u = L.r0 + (e - L.s0 - L.nF - L.nQ);
+    u = L.r0 + (ee - L.s0 - L.nF - L.nQ);
+  const float old = st.score[b * g.U + u];
   float total = 0.0f;
-#pragma unroll 8
-  for (int h = 0; h < g.Hkv; ++h) {
-    const float *mp = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1) + e) * G * 2;
-    float gs = 0.0f;
-    for (int hh = 0; hh < G; ++hh) {
-      const float rho = mp[hh * 2], ms = mp[hh * 2 + 1];
-      float v = (ms == neg_inf()) ? 0.0f : rho * exp2f(ms - sM[h * G + hh]) * sInvL[h * G + hh];
-      if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's mass below FLT_MIN counts as 0
-      gs += v;
+  for (int h0 = 0; h0 < g.Hkv; h0 += CH) {
+    float4 mp[CH][G / 2];   // (rho, m) of the G heads, per KV head
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int h = min(h0 + k, g.Hkv - 1);
+      const float4 *src = (const float4 *)(st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1) + ee) * G * 2);
+#pragma unroll
+      for (int q = 0; q < G / 2; ++q) mp[k][q] = src[q];
     }
-    if (mass_out) mass_out[((size_t)b * g.Hkv + h) * g.U + u] = gs;
-    total += gs;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int h = h0 + k;
+      if (h >= g.Hkv) break;
+      float gs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < G / 2; ++q) {
+        const float r2[2] = {mp[k][q].x, mp[k][q].z}, m2[2] = {mp[k][q].y, mp[k][q].w};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int hh = 2 * q + t;
+          float v = (m2[t] == neg_inf()) ? 0.0f : r2[t] * exp2f(m2[t] - sM[h * G + hh]) * sInvL[h * G + hh];
+          if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's mass below FLT_MIN counts as 0
+          gs += v;
+        }
+      }
+      if (mass_out && e < E) mass_out[((size_t)b * g.Hkv + h) * g.U + u] = gs;
+      total += gs;
+    }
   }
-  st.score[b * g.U + u] += total;
+  if (e < E) st.score[b * g.U + u] = old + total;
 }
 
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
@@ -874,10 +968,11 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
   if (ev_start) hipEventRecord(ev_start, s);
+  const size_t qs_bytes = (size_t)ATT_WAVES * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
   if (g.d == 128)
-    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
+    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(256), qs_bytes, s, g, st, si, q, scale_log2);
   else
-    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(256), 0, s, g, st, si, q, scale_log2);
+    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(256), qs_bytes, s, g, st, si, q, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_stop) hipEventRecord(ev_stop, s);
@@ -885,9 +980,13 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
     e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.U * sizeof(float), s);
     if (e != hipSuccess) return e;
   }
-  const int n_chunks = (g.U + 1 + 255) / 256;
-  hipLaunchKernelGGL(merge_qevict_kernel, dim3(g.B * g.Hkv + g.B * n_chunks), dim3(256), 0, s, g, st, si, out,
-                     mass_out, n_chunks);
+  const int n_live = si.has_sink + si.n_routed + (si.r1 >= si.r0 ? si.r1 - si.r0 + 1 : 0);   // entries this step
+  const int n_chunks = (n_live + 255) / 256;
+  const dim3 mgrid(g.B * g.Hkv + g.B * n_chunks);
+  if (g.G == 4)
+    hipLaunchKernelGGL(merge_qevict_kernel<4>, mgrid, dim3(256), 0, s, g, st, si, out, mass_out, n_chunks);
+  else
+    hipLaunchKernelGGL(merge_qevict_kernel<8>, mgrid, dim3(256), 0, s, g, st, si, out, mass_out, n_chunks);
   return hipGetLastError();
 }
 
