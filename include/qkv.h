@@ -100,6 +100,20 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
 int qkv_destroy(qkv_cache *cache);
 
 /*
+ * Policies.
+ * QKV_POLICY_QEVICT: window units (window = 8, 16 or 32 tokens), one score
+ *   per (sequence, window) summed over all query heads, three tiers (full
+ *   precision, INT2 ledger, evicted); routing every omega steps.
+ * QKV_POLICY_H2O (H2O notes, sections 1.1-2.1 and the GQA paragraph): token
+ *   units (window = 1, k_quant = 0), one score per (sequence, KV head, token)
+ *   summed over the G query heads of that KV head; k_full is the heavy-hitter
+ *   budget B_h, n_recent the recent budget B_r, n_sink protected sinks; call
+ *   qkv_route after every decode step (omega = 1) to evict down to the budget.
+ *   The scored prompt (section 3.3): append it, qkv_prefill_score with its
+ *   queries, then one qkv_route trims it.  max_ctx <= 8192.
+ */
+
+/*
  * Append n_tokens new positions to every sequence.
  *   k, v: bfloat16 [batch, n_kv_heads, n_tokens, head_dim].
  * QEvict: positions go to their windows (the first n_sink positions form the
@@ -136,6 +150,21 @@ int qkv_decode_attend(qkv_cache *cache, const void *q, float *out, float *mass_o
  * full precision from its ledger.
  */
 int qkv_route(qkv_cache *cache, qkv_stream stream);
+/* H2O: the same call is the per-step eviction: tokens older than the newest
+ * n_recent join the kept older tokens, and of those the k_full best by
+ * (score descending, position descending) stay, the rest are evicted for
+ * good (H2O notes section 2.1; the tie rule is this library's reading). */
+
+/*
+ * Scored prompt (H2O notes section 3.3): the queries of the last n_queries
+ * appended positions, each attending causally to the live tokens at or before
+ * its own position, add their weights (summed over each KV head's query
+ * heads, each below FLT_MIN counting as 0) to the token scores; no output.
+ *   q: bfloat16 [batch, n_queries, n_q_heads, head_dim]
+ * Errors: QKV_ESTATE for the window policy, or when a scored position is
+ * older than a token already ranked and kept by qkv_route.
+ */
+int qkv_prefill_score(qkv_cache *cache, const void *q, int32_t n_queries, qkv_stream stream);
 
 /*
  * Stateless quantizer (HqeKV notes section 2.3 Eq.(2) uniform; Eq.(3)-(4)
@@ -177,6 +206,8 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *   QKV_EXPORT_KEYS    uint16  [batch, n_kv_heads, max_ctx, head_dim]  full-precision content
  *   QKV_EXPORT_VALUES  uint16  [batch, n_kv_heads, max_ctx, head_dim]
  * (units without a ledger export zero codes and parameters).
+ * Token policies (H2O) export TIERS as uint8 [batch, n_kv_heads, max_ctx] and
+ * SCORES as float32 [batch, n_kv_heads, max_ctx]; the other kinds are EINVAL.
  */
 enum {
   QKV_EXPORT_TIERS = 0,

@@ -59,6 +59,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
         L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.qkv_route.argtypes = [_vp, _vp]
+        L.qkv_prefill_score.argtypes = [_vp, _vp, _i32, _vp]
         L.qkv_quantize_window.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
         L.qkv_quantize_status.argtypes = [_vp]
         L.qkv_rank_tiers.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]
@@ -170,6 +171,10 @@ class Cache:
 
     def route(self, stream=None):
         _check(_lib().qkv_route(self.h, _stream(stream)), "qkv_route")
+
+    def prefill_score(self, q, stream=None):
+        """q: bf16 [B, n_queries, Hq, d] queries of the last appended positions."""
+        _check(_lib().qkv_prefill_score(self.h, _ptr(q), int(q.shape[1]), _stream(stream)), "qkv_prefill_score")
 
     def export(self, what: str, stream=None):
         import torch

@@ -12,8 +12,13 @@ using namespace qkv;
 
 struct qkv_cache {
   qkv_config cfg;
+  bool tok;       // token mode (H2O): per-token units, per-(sequence, KV head) scores
   Geom g;
   State st;
+  TokGeom tg;
+  TokState ts;
+  int r_tok;      // token mode: first position not yet ranked
+  int n_cmp;      // token mode: kept older tokens per (sequence, KV head)
   void *ws;
   size_t ws_bytes;
   int N;          // tokens appended per sequence
@@ -41,7 +46,14 @@ int validate(const qkv_config *c) {
   if (c->head_dim != 64 && c->head_dim != 128) return QKV_EINVAL;
   if (c->max_ctx < 1) return QKV_EINVAL;
   if (c->n_splits < 0 || c->n_splits > 256) return QKV_EINVAL;
-  if (c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;   // per-token policies: separate caches (not here)
+  if (c->policy == QKV_POLICY_H2O) {
+    // per-token heavy hitters: window 1, no quantized tier, scores per KV head
+    if (c->window != 1 || c->omega < 1 || c->k_quant != 0 || c->k_full < 0 || c->n_recent < 0) return QKV_EINVAL;
+    if (c->n_sink < 0 || c->n_sink > TS) return QKV_EINVAL;
+    if (c->max_ctx > SORT_MAX) return QKV_EINVAL;    // routing candidates are ranked in LDS
+    return QKV_OK;
+  }
+  if (c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;
   if (c->window != 8 && c->window != 16 && c->window != 32) return QKV_EINVAL;
   if (c->omega < 1) return QKV_EINVAL;
   if (c->n_sink < 0 || c->n_sink > TS || c->n_recent < 0) return QKV_EINVAL;
@@ -86,6 +98,33 @@ void make_geom(const qkv_config *c, Geom &g) {
     if (S > cap) S = cap;
     if (S > 64) S = 64;
     if (S < 1) S = 1;
+  }
+  g.n_splits = S;
+}
+
+void make_tok_geom(const qkv_config *c, TokGeom &g) {
+  memset(&g, 0, sizeof g);
+  g.B = c->batch;
+  g.Hq = c->n_q_heads;
+  g.Hkv = c->n_kv_heads;
+  g.G = c->n_q_heads / c->n_kv_heads;
+  g.d = c->head_dim;
+  g.policy = c->policy;
+  g.T = c->max_ctx;
+  g.NPT = (c->max_ctx + TS - 1) / TS;
+  g.NCT = c->k_full > 0 ? (c->k_full + TS - 1) / TS : 1;
+  g.TILES = 1 + g.NCT + g.NPT;
+  g.n_sink = c->n_sink;
+  g.n_recent = c->n_recent;
+  g.k_heavy = c->k_full;
+  g.omega = c->omega;
+  int S = c->n_splits;
+  if (S == 0) {   // one resident round of workgroups, at least two tiles per wave
+    const int pairs = g.B * g.Hkv;
+    S = (512 + pairs - 1) / pairs;
+    const int cap = g.TILES / 8 > 1 ? g.TILES / 8 : 1;
+    if (S > cap) S = cap;
+    if (S > 64) S = 64;
   }
   g.n_splits = S;
 }
@@ -150,6 +189,12 @@ int qkv_check_config(const qkv_config *cfg) { return validate(cfg); }
 
 size_t qkv_workspace_bytes(const qkv_config *cfg) {
   if (validate(cfg) != QKV_OK) return 0;
+  if (cfg->policy == QKV_POLICY_H2O) {
+    TokGeom tg;
+    make_tok_geom(cfg, tg);
+    TokState ts;
+    return tok_carve(tg, nullptr, ts);
+  }
   Geom g;
   make_geom(cfg, g);
   State st;
@@ -166,8 +211,16 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
   if (!c) return QKV_ECAPACITY;
   memset(c, 0, sizeof *c);
   c->cfg = *cfg;
-  make_geom(cfg, c->g);
-  size_t need = carve(c->g, (char *)workspace, c->st);
+  c->tok = cfg->policy == QKV_POLICY_H2O;
+  size_t need;
+  if (c->tok) {
+    make_tok_geom(cfg, c->tg);
+    need = tok_carve(c->tg, (char *)workspace, c->ts);
+    c->r_tok = cfg->n_sink;
+  } else {
+    make_geom(cfg, c->g);
+    need = carve(c->g, (char *)workspace, c->st);
+  }
   if (bytes < need) {
     delete c;
     return QKV_ECAPACITY;
@@ -231,9 +284,11 @@ int qkv_profile_read(qkv_cache *c, float *ms, int32_t n) {
 
 int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv_stream stream) {
   if (!c || !k || !v || n_tokens < 1) return QKV_EINVAL;
-  if ((long long)c->N + n_tokens > c->g.max_ctx) return QKV_ECAPACITY;
-  int rc = hip_err(launch_append(c->g, c->st, (const uint16_t *)k, (const uint16_t *)v, n_tokens, c->N,
-                                 (hipStream_t)stream));
+  if ((long long)c->N + n_tokens > c->cfg.max_ctx) return QKV_ECAPACITY;
+  int rc = c->tok ? hip_err(tok_launch_append(c->tg, c->ts, (const uint16_t *)k, (const uint16_t *)v, n_tokens,
+                                              c->N, (hipStream_t)stream))
+                  : hip_err(launch_append(c->g, c->st, (const uint16_t *)k, (const uint16_t *)v, n_tokens, c->N,
+                                          (hipStream_t)stream));
   if (rc != QKV_OK) return rc;
   c->N += n_tokens;
   return QKV_OK;
@@ -248,16 +303,56 @@ int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, 
     e1 = c->ev[2 * c->ev_next + 1];
     c->ev_next++;
   }
-  int rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
-                                 e0, e1));
+  int rc;
+  if (c->tok) {
+    const TokStep ts = {c->N, c->r_tok, c->n_cmp};
+    rc = hip_err(tok_launch_attend(c->tg, c->ts, ts, (const uint16_t *)q, (size_t)c->tg.Hq * c->tg.d, out, mass_out,
+                                   (hipStream_t)stream, e0, e1));
+  } else {
+    rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
+                               e0, e1));
+  }
   if (rc != QKV_OK) return rc;
   c->steps++;
+  return QKV_OK;
+}
+
+int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream stream) {
+  if (!c || !q || n_queries < 1) return QKV_EINVAL;
+  if (!c->tok) return QKV_ESTATE;                        // window mode does not score the prompt
+  if (n_queries > c->N) return QKV_EINVAL;
+  // a scored position must not be older than a kept ranked token (it would see it)
+  if (c->n_cmp > 0 && c->N - n_queries < c->r_tok) return QKV_ESTATE;
+  const TokGeom &g = c->tg;
+  const size_t row = (size_t)g.Hq * g.d;
+  for (int i = 0; i < n_queries; ++i) {
+    const TokStep ts = {c->N - n_queries + i + 1, c->r_tok, c->n_cmp};   // causal: positions <= its own
+    int rc = hip_err(tok_launch_attend(g, c->ts, ts, (const uint16_t *)q + (size_t)i * row, (size_t)n_queries * row,
+                                       c->ts.scratch_out, nullptr, (hipStream_t)stream));
+    if (rc != QKV_OK) return rc;
+  }
   return QKV_OK;
 }
 
 int qkv_route(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
+  if (c->tok) {
+    // tokens older than the newest n_recent join the kept ones; the best k_full stay
+    const TokGeom &tg = c->tg;
+    const int limit = c->N - tg.n_recent;
+    const int a0 = c->r_tok, a1 = limit > a0 ? limit : a0;
+    const int n_cand = c->n_cmp + (a1 - a0);
+    if (n_cand > 0) {
+      const TokStep ts = {c->N, c->r_tok, c->n_cmp};
+      int rc = hip_err(tok_launch_route(tg, c->ts, ts, a0, a1, n_cand, (hipStream_t)stream));
+      if (rc != QKV_OK) return rc;
+    }
+    c->r_tok = a1;
+    c->n_cmp = n_cand < tg.k_heavy ? n_cand : tg.k_heavy;
+    c->routes++;
+    return QKV_OK;
+  }
   const Geom &g = c->g;
   // windows whose last position is older than the newest n_recent positions
   const long long limit = (long long)c->N - g.n_recent;
@@ -309,6 +404,10 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
 
 size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
   if (!c) return 0;
+  if (c->tok) {
+    const size_t n = (size_t)c->tg.B * c->tg.Hkv * c->tg.T;
+    return what == QKV_EXPORT_TIERS ? n : (what == QKV_EXPORT_SCORES ? n * 4 : 0);
+  }
   const Geom &g = c->g;
   const size_t BU = (size_t)g.B * g.U;
   switch (what) {
@@ -329,6 +428,7 @@ int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_st
   if (!c || !dst) return QKV_EINVAL;
   const size_t need = qkv_export_bytes(c, what);
   if (need == 0 || bytes != need) return QKV_EINVAL;
+  if (c->tok) return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
   return hip_err(launch_export(c->g, c->st, what, dst, (hipStream_t)stream));
 }
 
@@ -336,10 +436,10 @@ int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
   if (!c || !value) return QKV_EINVAL;
   switch (what) {
     case QKV_INFO_TOKENS: *value = c->N; return QKV_OK;
-    case QKV_INFO_UNITS: *value = c->g.U; return QKV_OK;
+    case QKV_INFO_UNITS: *value = c->tok ? c->tg.T : c->g.U; return QKV_OK;
     case QKV_INFO_STEPS: *value = c->steps; return QKV_OK;
     case QKV_INFO_ROUTES: *value = c->routes; return QKV_OK;
-    case QKV_INFO_SPLITS: *value = c->g.n_splits; return QKV_OK;
+    case QKV_INFO_SPLITS: *value = c->tok ? c->tg.n_splits : c->g.n_splits; return QKV_OK;
     case QKV_INFO_WORKSPACE: *value = (int64_t)c->ws_bytes; return QKV_OK;
     default: return QKV_EINVAL;
   }
@@ -349,7 +449,8 @@ int qkv_status(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   int32_t flag = 0;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return QKV_EHIP;
-  if (hipMemcpy(&flag, c->st.status, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess) return QKV_EHIP;
+  if (hipMemcpy(&flag, c->tok ? c->ts.status : c->st.status, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
+    return QKV_EHIP;
   return flag ? QKV_ERANGE : QKV_OK;
 }
 

@@ -1,0 +1,166 @@
+// Device helpers shared by the window-mode and token-mode kernels of the qkv
+// library (gfx950): operand types, matrix-core wrappers, the exact unpack of
+// 2-bit codes, cross-lane reductions and the online-softmax block update.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "qkv_internal.h"
+
+namespace qkv {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline floatx4 mfma_bf16_k32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_f16_k32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_bf16_k16(short4v a, short4v b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma_f16_k16(half4 a, half4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// 2-bit codes to exact fp16 operands.  A code dword is first masked to
+// 0x33333333 (directly, or after a shift by 2): every byte then holds two
+// nibbles 00cc, which are the e2m1 (FP4) values cc/2, and the scaled FP4
+// conversion with scale 2 turns byte b into the fp16 pair (low nibble, high
+// nibble) = two codes, exactly.  The slot placement of the ledger
+// (kcode_slot / vcode_slot) puts the codes an operand needs in these pairs.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+template <int B>
+__device__ __forceinline__ half2v fp4_pair(uint32_t m) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, B);
+}
+__device__ __forceinline__ half2v fp4_pair_sel(uint32_t m, int b) {   // b is a constant after unrolling
+  switch (b & 3) {
+    case 0: return fp4_pair<0>(m);
+    case 1: return fp4_pair<1>(m);
+    case 2: return fp4_pair<2>(m);
+    default: return fp4_pair<3>(m);
+  }
+}
+__device__ __forceinline__ uint32_t code_half(uint32_t x, int odd) {   // slots 4k+odd, 4k+odd+2 of each byte
+  return (odd ? (x >> 2) : x) & 0x33333333u;
+}
+// the 8 codes of a masked dword (bytes 0..3) as one half8 operand
+__device__ __forceinline__ half8 codes8(uint32_t m) {
+  const half4 lo = __builtin_shufflevector(fp4_pair<0>(m), fp4_pair<1>(m), 0, 1, 2, 3);
+  const half4 hi = __builtin_shufflevector(fp4_pair<2>(m), fp4_pair<3>(m), 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ inline float neg_inf() { return -__builtin_inff(); }
+
+// uniform quantizer of one value (see the codec definition): code of x in a
+// group with float16 step s16 and zero z16
+__device__ inline uint32_t quant_code(float x, half_t s16, half_t z16, float levels) {
+  float s = (float)s16;
+  if (s == 0.0f) return 0u;
+  float r = (x - (float)z16) / s;
+  r = rintf(r);
+  r = fminf(fmaxf(r, 0.0f), levels);
+  return (uint32_t)r;
+}
+
+template <int D>
+struct WaveState {
+  floatx4 acc[D / 16];   // output rows (head, limb) x columns of each 16-channel tile
+  floatx4 zacc;          // value-zero term per (row, channel group) of quantized tiles
+  float m;               // running max of this lane's column (log2 units)
+  float l;               // partial sum of probabilities over this lane's tokens
+};
+
+// order a wave's LDS writes before its own later LDS reads (no cross-wave sharing)
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// reductions over lane pairs (l, l^16) and (l, l^32) with the row-swap
+// permutes of gfx950 (VALU, no LDS traffic); both lanes get identical bits
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// s + (s of the lane 8 columns away): folds the low-limb column 8+h into
+// column h and vice versa (a row rotation by 8, so both get the same sum)
+__device__ __forceinline__ float fold8(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));   // row_ror:8
+  return x + y;
+}
+
+// online-softmax update for a block of NT 16-token tiles (scores in C layout;
+// rows lo[t] <= r < hi[t] of tile t are valid); writes probabilities p[t][i]
+// and each tile's probability sum ts[t] (summed over the tile's 16 tokens) and
+// rescales the running state when the running max grows.
+template <int D, int NT>
+__device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float sc, const int *lo, const int *hi,
+                                     int lq, float (*p)[4], float *ts) {
+  float x[NT][4];
+  float mx = neg_inf();
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lq + i;
+      x[t][i] = (row >= lo[t] && row < hi[t]) ? s[t][i] * sc : neg_inf();
+      mx = fmaxf(mx, x[t][i]);
+    }
+  mx = max_x16(mx);
+  mx = max_x32(mx);
+  const float m_new = fmaxf(ws.m, mx);
+  const bool grow = m_new > ws.m;
+  if (__any(grow)) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;   // exp2(-inf) = 0 on the first block
+    ws.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ar = __shfl(alpha, 4 * lq + i);   // factor of output row 4*lq+i
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
+      ws.zacc[i] *= ar;
+    }
+    ws.m = m_new;
+  }
+  float lsum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    ts[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - ws.m);
+      ts[t] += p[t][i];
+    }
+    lsum += ts[t];
+  }
+  ws.l += lsum;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ts[t] = sum_x32(sum_x16(ts[t]));
+}
+
+}  // namespace qkv

@@ -149,6 +149,58 @@ __host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((x.u + 0x7FFFu + lsb) >> 16);
 }
 
+// ---------------------------------------------------------------------------
+// Token mode (H2O, HqeKV): every token is its own scoring unit, scores are
+// per (sequence, KV head), and the kept tokens are gathered into compact tiles.
+//
+//   pages   bf16 [B][Hkv][NPT][2][TS*d]  every appended token at its position
+//                (tile pos/16, slot pos%16; same swizzle as the window pages)
+//   cpages  bf16 [B][Hkv][NCT][2][TS*d]  compact full-precision tiles: kept
+//                tokens in rank order; cpos [B][Hkv][NCT*TS] their positions
+//   tier u8, score f32 [B][Hkv][T]       per token
+//   mrho f32 [B][Hkv][TILES+1][G][TS]    per live tile and head: p of each slot
+//   mref f32 [B][Hkv][TILES+1][G]        ... and the running max it is relative
+//                to (row TILES is the spare row unused lanes write to)
+// ---------------------------------------------------------------------------
+
+struct TokGeom {
+  int B, Hq, Hkv, G, d;
+  int policy;
+  int T;            // token capacity per (sequence, KV head)
+  int NPT;          // position tiles: ceil(T / TS)
+  int NCT;          // compact tiles per (sequence, KV head)
+  int TILES;        // live tiles per (sequence, KV head), upper bound: 1 + NCT + NPT
+  int n_sink, n_recent, k_heavy, omega;
+  int n_splits;
+};
+
+struct TokState {
+  uint16_t *pages;
+  uint16_t *cpages;
+  int32_t *cpos;
+  uint8_t *tier;
+  float *score;
+  float *part_o;     // [B][Hkv][S][G][d]
+  float *part_ml;    // [B][Hkv][S][G][2]
+  float *mrho;
+  float *mref;
+  float *scratch_out;   // [B][Hq][d] outputs of scoring-only passes
+  int32_t *status;
+};
+
+// Per-call scalars the host knows: tokens so far, first position not yet
+// ranked (positions [rstart, N) are read from the position pages), kept tokens.
+struct TokStep {
+  int N, rstart, n_cmp;
+};
+
+__host__ __device__ inline size_t tok_page_offset(const TokGeom &g, int b, int h, int tile) {
+  return (((size_t)b * g.Hkv + h) * g.NPT + tile) * (size_t)(2 * TS * g.d);
+}
+__host__ __device__ inline size_t tok_cpage_offset(const TokGeom &g, int b, int h, int tile) {
+  return (((size_t)b * g.Hkv + h) * g.NCT + tile) * (size_t)(2 * TS * g.d);
+}
+
 // ---- launchers (defined in qkv_kernels.hip) ----
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
@@ -163,5 +215,16 @@ hipError_t launch_rank_tiers(const float *score, const int32_t *pos, const uint8
                              const int32_t *counts, int n_tiers, uint8_t *out, hipStream_t s);
 hipError_t launch_export(const Geom &g, const State &st, int what, void *dst, hipStream_t s);
 hipError_t read_quantize_status(int *flag, hipStream_t s);
+
+// ---- token-mode launchers (defined in qkv_token.hip) ----
+size_t tok_carve(const TokGeom &g, char *base, TokState &st);
+hipError_t tok_launch_append(const TokGeom &g, const TokState &st, const uint16_t *k, const uint16_t *v,
+                             int n_tokens, int pos0, hipStream_t s);
+hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep &ts, const uint16_t *q,
+                             size_t q_bstride, float *out, float *mass_out, hipStream_t s,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep &ts, int a0, int a1, int n_cand,
+                            hipStream_t s);
+hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, void *dst, hipStream_t s);
 
 }  // namespace qkv
