@@ -3,6 +3,7 @@
 // tracks so that no call has to read device state.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <new>
 #include <string.h>
 
@@ -18,7 +19,8 @@ struct qkv_cache {
   TokGeom tg;
   TokState ts;
   int r_tok;      // token mode: first position not yet ranked
-  int n_cmp;      // token mode: kept older tokens per (sequence, KV head)
+  int n_cmp;      // token mode (H2O): kept older tokens per (sequence, KV head)
+  int last_event_N;   // HqeKV: tokens at the previous assignment event (0: none yet)
   void *ws;
   size_t ws_bytes;
   int N;          // tokens appended per sequence
@@ -51,6 +53,17 @@ int validate(const qkv_config *c) {
     if (c->window != 1 || c->omega < 1 || c->k_quant != 0 || c->k_full < 0 || c->n_recent < 0) return QKV_EINVAL;
     if (c->n_sink < 0 || c->n_sink > TS) return QKV_EINVAL;
     if (c->max_ctx > SORT_MAX) return QKV_EINVAL;    // routing candidates are ranked in LDS
+    return QKV_OK;
+  }
+  if (c->policy == QKV_POLICY_HQEKV) {
+    // per-token five-tier assignment: window 1, no sinks, shares in [0, 1] summing to 1
+    if (c->window != 1 || c->omega < 1 || c->n_sink != 0) return QKV_EINVAL;
+    float sum = 0.0f;
+    for (int k = 0; k < 5; ++k) {
+      if (!(c->ratios[k] >= 0.0f && c->ratios[k] <= 1.0f)) return QKV_EINVAL;
+      sum += c->ratios[k];
+    }
+    if (sum < 0.999f || sum > 1.001f) return QKV_EINVAL;
     return QKV_OK;
   }
   if (c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;
@@ -112,8 +125,21 @@ void make_tok_geom(const qkv_config *c, TokGeom &g) {
   g.policy = c->policy;
   g.T = c->max_ctx;
   g.NPT = (c->max_ctx + TS - 1) / TS;
-  g.NCT = c->k_full > 0 ? (c->k_full + TS - 1) / TS : 1;
-  g.TILES = 1 + g.NCT + g.NPT;
+  if (c->policy == QKV_POLICY_HQEKV) {
+    g.NCT = g.NPT;                 // any tier may hold every token
+    g.TILES = 2 * g.NPT + 5;       // ranked tiles (one partial per tier) + recent tiles
+    g.rec_bytes = g.d + (g.d / 32) * 8;
+    const int KB = g.d / 32;
+    const int bits[3] = {4, 2, 1};
+    for (int f = 0; f < 3; ++f) {
+      const int lb = KB * bits[f] < 4 ? 4 : KB * bits[f];
+      const int pb = f == 2 ? 4 : KB * 4;
+      g.qtile_bytes[f] = 128 * lb + 32 * pb;
+    }
+  } else {
+    g.NCT = c->k_full > 0 ? (c->k_full + TS - 1) / TS : 1;
+    g.TILES = 1 + g.NCT + g.NPT;
+  }
   g.n_sink = c->n_sink;
   g.n_recent = c->n_recent;
   g.k_heavy = c->k_full;
@@ -189,7 +215,7 @@ int qkv_check_config(const qkv_config *cfg) { return validate(cfg); }
 
 size_t qkv_workspace_bytes(const qkv_config *cfg) {
   if (validate(cfg) != QKV_OK) return 0;
-  if (cfg->policy == QKV_POLICY_H2O) {
+  if (cfg->policy == QKV_POLICY_H2O || cfg->policy == QKV_POLICY_HQEKV) {
     TokGeom tg;
     make_tok_geom(cfg, tg);
     TokState ts;
@@ -211,7 +237,7 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
   if (!c) return QKV_ECAPACITY;
   memset(c, 0, sizeof *c);
   c->cfg = *cfg;
-  c->tok = cfg->policy == QKV_POLICY_H2O;
+  c->tok = cfg->policy == QKV_POLICY_H2O || cfg->policy == QKV_POLICY_HQEKV;
   size_t need;
   if (c->tok) {
     make_tok_geom(cfg, c->tg);
@@ -337,6 +363,20 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
 int qkv_route(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
+  if (c->tok && c->tg.policy == QKV_POLICY_HQEKV) {
+    // assignment event: tokens ranked before (all live ones at the first
+    // event) get target tiers by their rank; shares floor(r_k * N) of all
+    // tokens ever appended, in the order BF16, INT4, INT2, INT1
+    const int elig_end = c->last_event_N == 0 ? c->N : c->last_event_N;
+    int counts[4];
+    for (int k = 0; k < 4; ++k) counts[k] = (int)floor((double)c->cfg.ratios[k] * (double)c->N);
+    int rc = hip_err(hq_launch_event(c->tg, c->ts, c->N, elig_end, counts, (hipStream_t)stream));
+    if (rc != QKV_OK) return rc;
+    c->r_tok = elig_end;
+    c->last_event_N = c->N;
+    c->routes++;
+    return QKV_OK;
+  }
   if (c->tok) {
     // tokens older than the newest n_recent join the kept ones; the best k_full stay
     const TokGeom &tg = c->tg;
@@ -406,7 +446,15 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
   if (!c) return 0;
   if (c->tok) {
     const size_t n = (size_t)c->tg.B * c->tg.Hkv * c->tg.T;
-    return what == QKV_EXPORT_TIERS ? n : (what == QKV_EXPORT_SCORES ? n * 4 : 0);
+    switch (what) {
+      case QKV_EXPORT_TIERS: return n;
+      case QKV_EXPORT_SCORES: return n * 4;
+      case QKV_EXPORT_KCODES:
+      case QKV_EXPORT_VCODES: return c->tg.policy == QKV_POLICY_HQEKV ? n * (c->tg.d / 2) : 0;
+      case QKV_EXPORT_KPARAMS:
+      case QKV_EXPORT_VPARAMS: return c->tg.policy == QKV_POLICY_HQEKV ? n * (c->tg.d / 32) * 4 : 0;
+      default: return 0;
+    }
   }
   const Geom &g = c->g;
   const size_t BU = (size_t)g.B * g.U;

@@ -163,15 +163,25 @@ __host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 //                to (row TILES is the spare row unused lanes write to)
 // ---------------------------------------------------------------------------
 
+// HqeKV tiers of a ranked token (the per-token state of the five-tier method)
+enum : int { HQ_BF16 = 0, HQ_INT4 = 1, HQ_INT2 = 2, HQ_INT1 = 3, HQ_EVICT = 4 };
+// exported tier codes of token-mode tokens
+enum : uint8_t { T_INT4 = 6, T_INT1 = 7 };   // besides T_FULL (BF16), T_QUANT (INT2), T_EVICTED
+
 struct TokGeom {
   int B, Hq, Hkv, G, d;
   int policy;
   int T;            // token capacity per (sequence, KV head)
   int NPT;          // position tiles: ceil(T / TS)
-  int NCT;          // compact tiles per (sequence, KV head)
-  int TILES;        // live tiles per (sequence, KV head), upper bound: 1 + NCT + NPT
+  int NCT;          // compact tiles per (sequence, KV head) of each tier
+  int TILES;        // live tiles per (sequence, KV head), upper bound
   int n_sink, n_recent, k_heavy, omega;
   int n_splits;
+  // HqeKV: per-position record of a quantized token (canonical per-token
+  // packing): K codes [d/2 B], V codes [d/2 B], K params [d/32][2] fp16,
+  // V params [d/32][2] fp16 (INT1: [mean, std] in the first pair)
+  int rec_bytes;
+  int qtile_bytes[3];   // compact tile bytes of INT4, INT2, INT1
 };
 
 struct TokState {
@@ -186,6 +196,13 @@ struct TokState {
   float *mref;
   float *scratch_out;   // [B][Hq][d] outputs of scoring-only passes
   int32_t *status;
+  // HqeKV
+  float *vrange;        // [B][Hkv][T] max - min of the token's original value row
+  uint8_t *qrec;        // [B][Hkv][T][rec_bytes]
+  uint8_t *qtiles[3];   // [B][Hkv][NCT][qtile_bytes] compact INT4 / INT2 / INT1 tiles
+  int32_t *qpos[3];     // [B][Hkv][NCT*TS] their positions
+  int32_t *cnt;         // [B][Hkv][4] tokens per ranked tier (BF16, INT4, INT2, INT1)
+  unsigned long long *cuts;   // [B][Hkv][4] cut keys of the last assignment
 };
 
 // Per-call scalars the host knows: tokens so far, first position not yet
@@ -226,5 +243,7 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
 hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep &ts, int a0, int a1, int n_cand,
                             hipStream_t s);
 hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, void *dst, hipStream_t s);
+hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
+                           hipStream_t s);
 
 }  // namespace qkv

@@ -1,21 +1,28 @@
 // Token-mode kernels of the tiered decode path (gfx950): H2O heavy-hitter
-// eviction, where every token is its own unit and scores are kept per
-// (sequence, KV head).
+// eviction and HqeKV five-tier assignment, where every token is its own unit
+// and scores are kept per (sequence, KV head).
 //
 // H2O notes, sections 1.1-2.1 and the GQA paragraph: append the new token,
 // attend over the kept set plus the new token, add each kept token's weight
 // (summed over the query heads that share the KV head) to its score, keep the
 // newest B_r tokens and the sinks, and evict from the older tokens the
-// lowest-scored ones so that B_h heavy hitters remain (one per step once the
-// budget is reached; the whole surplus when the scored prompt is trimmed).
+// lowest-scored ones so that B_h heavy hitters remain.
 //
-// Kept older tokens live in compact tiles gathered at each routing call; the
-// sinks and the tokens not yet ranked are read from the position pages.  The
-// attention kernel streams [sink tile][compact tiles][recent position tiles]
-// with the same 16x16x32 bf16 matrix-core tiling as the window mode, and emits
-// per token slot the head's probability relative to the running maximum; the
-// merge kernel normalizes those with the global (max, sum) of each head and
-// adds them into the per-token scores in a fixed order (no atomics).
+// HqeKV notes, sections 3.2-3.5: every T steps the tokens ranked so far are
+// ordered by accumulated attention times value range and cut by the tier
+// shares into BF16 / INT4 / INT2 / INT1 (normalized) / evicted; a token only
+// moves to a lower precision, re-quantized from its current values (keys and
+// values per token, groups of 32 channels; INT1: mean and deviation).
+//
+// Ranked tokens live in compact tiles per tier, gathered at each routing
+// call; tokens not yet ranked (and H2O's sinks) are read from the position
+// pages.  The attention kernel streams [sink][BF16 compact][INT4][INT2][INT1]
+// [recent] tiles: full-precision tiles feed bf16 matrix-core operands;
+// quantized tiles are dequantized in registers to exact float32 values and
+// split into two fp16 limbs, so the 16x16x32 fp16 operations keep about 22
+// bits.  Each token slot's probability is emitted relative to the running
+// maximum; the merge kernel normalizes those with the global (max, sum) of
+// each head and adds them into the per-token scores in a fixed order.
 #include "qkv_device.h"
 
 namespace qkv {
@@ -24,6 +31,8 @@ namespace {
 
 constexpr size_t TOK_ALIGN = 256;
 inline size_t tok_align(size_t x) { return (x + TOK_ALIGN - 1) / TOK_ALIGN * TOK_ALIGN; }
+constexpr int QBITS[3] = {4, 2, 1};   // INT4, INT2, INT1
+constexpr float KAPPA1 = 0.6744897501960817f;   // Phi^-1(3/4): INT1 centres are mean -/+ KAPPA1 * std
 
 }  // namespace
 
@@ -47,11 +56,29 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.mref = (float *)take(BH * (g.TILES + 1) * g.G * 4);
   st.scratch_out = (float *)take((size_t)g.B * g.Hq * g.d * 4);
   st.status = (int32_t *)take(16);
+  st.vrange = nullptr;
+  st.qrec = nullptr;
+  st.cnt = nullptr;
+  st.cuts = nullptr;
+  for (int k = 0; k < 3; ++k) {
+    st.qtiles[k] = nullptr;
+    st.qpos[k] = nullptr;
+  }
+  if (g.policy == QKV_POLICY_HQEKV) {
+    st.vrange = (float *)take(BH * g.T * 4);
+    st.qrec = (uint8_t *)take(BH * g.T * g.rec_bytes);
+    for (int k = 0; k < 3; ++k) {
+      st.qtiles[k] = (uint8_t *)take(BH * g.NCT * g.qtile_bytes[k]);
+      st.qpos[k] = (int32_t *)take(BH * g.NCT * TS * 4);
+    }
+    st.cnt = (int32_t *)take(BH * 4 * 4);
+    st.cuts = (unsigned long long *)take(BH * 4 * 8);
+  }
   return off;
 }
 
 // ---------------------------------------------------------------------------
-// append: new tokens into the position pages
+// append: new tokens into the position pages (HqeKV: and their value range)
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void tok_append_kernel(TokGeom g, TokState st, const uint16_t *__restrict__ k,
@@ -70,14 +97,23 @@ __global__ __launch_bounds__(256) void tok_append_kernel(TokGeom g, TokState st,
     uint16_t *kt = st.pages + tok_page_offset(g, b, h, pos / TS);
     uint16_t *vt = kt + TS * g.d;
     const int t = pos % TS, c0 = ch * 8;
-    const size_t src = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d + c0;
-    *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + src);
+    const size_t row = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d;
+    *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + row + c0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = v[src + j];
+    for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = v[row + c0 + j];
     if (ch == 0) {
       const size_t u = ((size_t)b * g.Hkv + h) * g.T + pos;
       st.tier[u] = pos < g.n_sink ? T_SINK : T_RECENT;
       st.score[u] = 0.0f;
+      if (st.vrange) {   // value range over the token's channels (HqeKV section 3.2)
+        float mn = bf16_to_f32(v[row]), mx = mn;
+        for (int c = 1; c < g.d; ++c) {
+          const float x = bf16_to_f32(v[row + c]);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+        st.vrange[u] = mx - mn;
+      }
     }
   }
 }
@@ -92,26 +128,42 @@ hipError_t tok_launch_append(const TokGeom &g, const TokState &st, const uint16_
 }
 
 // ---------------------------------------------------------------------------
-// attention over [sink tile][compact tiles][recent position tiles]
+// live tiles of one (sequence, KV head):
+//   [sink][BF16 compact][INT4][INT2][INT1][recent position tiles]
 // ---------------------------------------------------------------------------
 
 struct TokList {
-  int s0, nC, nR, rt0;   // sink tile present, compact tiles, recent tiles, first recent tile
-  __device__ int count() const { return s0 + nC + nR; }
+  int s0, nC, nQ[3], nR, rt0;   // tiles of each part; first recent position tile
+  int nCtok, nQtok[3];          // tokens in the compact lists
+  __device__ int base_q(int k) const {
+    int b = s0 + nC;
+    for (int j = 0; j < k; ++j) b += nQ[j];
+    return b;
+  }
+  __device__ int base_r() const { return s0 + nC + nQ[0] + nQ[1] + nQ[2]; }
+  __device__ int count() const { return base_r() + nR; }
 };
 
-__device__ __forceinline__ TokList tok_list(const TokGeom &g, const TokStep &ts) {
+__device__ __forceinline__ TokList tok_list(const TokGeom &g, const TokState &st, const TokStep &ts, int bh) {
   TokList L;
   L.s0 = (g.n_sink > 0 && ts.N > 0) ? 1 : 0;
-  L.nC = (ts.n_cmp + TS - 1) / TS;
+  if (g.policy == QKV_POLICY_HQEKV) {
+    L.nCtok = st.cnt[bh * 4 + 0];
+    for (int k = 0; k < 3; ++k) L.nQtok[k] = st.cnt[bh * 4 + 1 + k];
+  } else {
+    L.nCtok = ts.n_cmp;
+    for (int k = 0; k < 3; ++k) L.nQtok[k] = 0;
+  }
+  L.nC = (L.nCtok + TS - 1) / TS;
+  for (int k = 0; k < 3; ++k) L.nQ[k] = (L.nQtok[k] + TS - 1) / TS;
   L.rt0 = ts.rstart / TS;
   L.nR = ts.N > ts.rstart ? (ts.N - 1) / TS - L.rt0 + 1 : 0;
   return L;
 }
 
-// tile k of the list: page address and valid rows [lo, hi)
-__device__ __forceinline__ const uint16_t *tok_tile(const TokGeom &g, const TokState &st, const TokStep &ts,
-                                                    const TokList &L, int b, int h, int k, int &lo, int &hi) {
+// full-precision tile k of the list (sink, compact or recent): page address, valid rows [lo, hi)
+__device__ __forceinline__ const uint16_t *tok_ftile(const TokGeom &g, const TokState &st, const TokStep &ts,
+                                                     const TokList &L, int b, int h, int k, int &lo, int &hi) {
   if (k < L.s0) {
     lo = 0;
     hi = min(ts.N, g.n_sink);
@@ -120,19 +172,290 @@ __device__ __forceinline__ const uint16_t *tok_tile(const TokGeom &g, const TokS
   if (k < L.s0 + L.nC) {
     const int c = k - L.s0;
     lo = 0;
-    hi = min(TS, ts.n_cmp - c * TS);
+    hi = min(TS, L.nCtok - c * TS);
     return st.cpages + tok_cpage_offset(g, b, h, c);
   }
-  const int rt = L.rt0 + (k - L.s0 - L.nC);
+  const int rt = L.rt0 + (k - L.base_r());
   lo = max(ts.rstart - rt * TS, 0);
   hi = min(ts.N - rt * TS, TS);
   return st.pages + tok_page_offset(g, b, h, rt);
 }
 
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+
+struct TokCtx {
+  const TokGeom *g;
+  const TokState *st;
+  const TokStep *ts;
+  const TokList *L;
+  int b, h, bh, lane, col, lq, G;
+  bool is_hi, is_lo, has_q;
+  float *mrho, *mref;
+};
+
+// per-slot probabilities of a tile (lanes of column h < G hold rows 4*lq..+3)
+// and the running max they are relative to; other lanes write the spare row
+__device__ __forceinline__ void tok_store_mass(const TokCtx &c, int e, const float *p, float m) {
+  const int G = c.G, TILES = c.g->TILES;
+  const int er = c.is_hi ? e : TILES;
+  *(float4 *)(c.mrho + ((size_t)er * G + (c.col & (G - 1))) * TS + 4 * c.lq) = make_float4(p[0], p[1], p[2], p[3]);
+  const int em = (c.is_hi && c.lq == 0) ? e : TILES;
+  c.mref[(size_t)em * G + (c.col & (G - 1))] = m;
+}
+
+// full-precision tiles (sink, compact, recent) of virtual range [ea, eb);
+// virtual index v < s0 + nC is list tile v, above it list tile v + (quantized tiles)
+template <int D>
+__device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&bq)[D / 32], float sc, int ea,
+                             int eb) {
+  if (ea >= eb) return;
+  constexpr int KB = D / 32, CP = D / 32;
+  const TokList &L = *c.L;
+  const int skip = L.base_r() - (L.s0 + L.nC);   // quantized tiles between compact and recent
+  const int n_blocks = (eb - ea + 1) >> 1;
+  auto block = [&](int i, const uint16_t *(&ptr)[2], int (&lo)[2], int (&hi)[2], int (&e)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int vk = ea + 2 * i + t;
+      const bool valid = vk < eb;
+      const int v = valid ? vk : ea + 2 * i;
+      const int k = v < L.s0 + L.nC ? v : v + skip;
+      ptr[t] = tok_ftile(*c.g, *c.st, *c.ts, L, c.b, c.h, k, lo[t], hi[t]);
+      if (!valid || !c.has_q) {
+        lo[t] = 0;
+        hi[t] = 0;
+      }
+      e[t] = valid ? k : c.g->TILES;
+    }
+  };
+  const uint16_t *cp[2], *np[2];
+  int clo[2], chi[2], ce[2], nlo[2], nhi[2], ne[2];
+  block(0, cp, clo, chi, ce);
+  uint4 kr[2][KB], vr[2][CP];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(cp[t] + (kb * 64 + c.lane) * 8);
+#pragma unroll
+    for (int p = 0; p < CP; ++p) vr[t][p] = *(const uint4 *)(cp[t] + TS * D + (p * 64 + c.lane) * 8);
+  }
+  for (int i = 0; i < n_blocks; ++i) {
+    block(min(i + 1, n_blocks - 1), np, nlo, nhi, ne);   // the last block re-reads itself
+    floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(np[t] + (kb * 64 + c.lane) * 8);
+    float p[2][4], tsum[2];
+    softmax_block<D, 2>(ws, s, sc, clo, chi, c.lq, p, tsum);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    // rows h carry bf16(p), rows 8+h carry bf16(p - bf16(p))
+    bf16x8 ap;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const float hi_ = (float)(__bf16)p[t][i2];
+        ap[t * 4 + i2] = (__bf16)(c.is_lo ? p[t][i2] - hi_ : p[t][i2]);
+      }
+#pragma unroll
+    for (int p2 = 0; p2 < CP; ++p2) {
+      const uint4 v0 = make_uint4(vr[0][p2].x, vr[0][p2].y, vr[1][p2].x, vr[1][p2].y);
+      const uint4 v1 = make_uint4(vr[0][p2].z, vr[0][p2].w, vr[1][p2].z, vr[1][p2].w);
+      ws.acc[2 * p2] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * p2]);
+      ws.acc[2 * p2 + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * p2 + 1]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = *(const uint4 *)(np[t] + TS * D + (p2 * 64 + c.lane) * 8);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      cp[t] = np[t];
+      clo[t] = nlo[t];
+      chi[t] = nhi[t];
+      ce[t] = ne[t];
+    }
+  }
+}
+
+// Compact quantized tile of format F (0 INT4, 1 INT2, 2 INT1), bits b:
+//   K codes  [64 lanes][KB*b bytes]: lane l (token l%16) holds, for k-block kb,
+//            channels kb*32 + 8*(l/16) + e at bit (kb*8 + e)*b
+//   V codes  [64 lanes][KB*b bytes]: lane l (channel column l%16) holds, for
+//            column tile ct, tokens 4*(l/16) + tt at bit (ct*4 + tt)*b
+//   K params [16 tokens][PB bytes], V params [16 tokens][PB bytes]:
+//            INT4/INT2 (scale, zero) fp16 per group of 32 channels,
+//            INT1 (mean, std) fp16
+template <int D, int F>
+struct QTile {
+  static constexpr int BITS = F == 0 ? 4 : (F == 1 ? 2 : 1);
+  static constexpr int LB = (D / 32) * BITS < 4 ? 4 : (D / 32) * BITS;   // code bytes per lane (dword padded)
+  static constexpr int PB = F == 2 ? 4 : (D / 32) * 4;
+  static constexpr int KC = 0, VC = 64 * LB, KP = 128 * LB, VP = 128 * LB + 16 * PB;
+  static constexpr int BYTES = 128 * LB + 32 * PB;
+  static constexpr int NW = (LB + 3) / 4;      // code dwords per lane
+};
+
+template <int D, int F>
+struct QBufT {
+  uint32_t kc[QTile<D, F>::NW];
+  uint32_t vc[QTile<D, F>::NW];
+  uint32_t kp[QTile<D, F>::PB / 4];            // this lane's token
+  uint32_t vp[QTile<D, F>::PB];                // this lane's four tokens (4 * PB bytes)
+};
+
+template <int D, int F>
+__device__ __forceinline__ void qt_load(const uint8_t *tile, int lane, QBufT<D, F> &q) {
+  using Q = QTile<D, F>;
+  const int t = lane & 15, lq = lane >> 4;
+  const uint32_t *kc = (const uint32_t *)(tile + Q::KC + lane * Q::LB);
+  const uint32_t *vc = (const uint32_t *)(tile + Q::VC + lane * Q::LB);
+#pragma unroll
+  for (int w = 0; w < Q::NW; ++w) {
+    q.kc[w] = kc[w];
+    q.vc[w] = vc[w];
+  }
+  const uint32_t *kp = (const uint32_t *)(tile + Q::KP + t * Q::PB);
+#pragma unroll
+  for (int w = 0; w < Q::PB / 4; ++w) q.kp[w] = kp[w];
+  const uint32_t *vp = (const uint32_t *)(tile + Q::VP + 4 * lq * Q::PB);
+#pragma unroll
+  for (int w = 0; w < Q::PB; ++w) q.vp[w] = vp[w];
+}
+
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16)); }
+
+template <int D, int F>
+__device__ __forceinline__ uint32_t qt_code(const uint32_t *w, int idx) {   // idx-th code of a lane's bits
+  constexpr int B = QTile<D, F>::BITS;
+  const int bit = idx * B;
+  return (w[bit >> 5] >> (bit & 31)) & ((1u << B) - 1u);
+}
+
+// dequantized value of a code: fma(code, s, z) for INT4/INT2; INT1 the
+// centre m -/+ KAPPA1 * std, both one float32 rounding
+template <int F>
+__device__ __forceinline__ float qt_deq(uint32_t code, float s_or_sd, float z_or_m) {
+  if (F == 2) return __builtin_fmaf(code ? KAPPA1 : -KAPPA1, s_or_sd, z_or_m);
+  return __builtin_fmaf((float)code, s_or_sd, z_or_m);
+}
+
+template <int D, int F>
+__device__ void tok_run_quant(WaveState<D> &ws, const TokCtx &c, const half8 (&bqf)[D / 32], float sc, int ea,
+                              int eb) {
+  if (ea >= eb) return;
+  using Q = QTile<D, F>;
+  constexpr int KB = D / 32, CT = D / 16;
+  const TokList &L = *c.L;
+  const int base = L.base_q(F);
+  const int ntok = L.nQtok[F];
+  const uint8_t *tiles = c.st->qtiles[F] + (size_t)c.bh * c.g->NCT * Q::BYTES;
+  const int n_blocks = (eb - ea + 1) >> 1;
+  auto block = [&](int i, const uint8_t *(&ptr)[2], int (&hi)[2], int (&e)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qk = ea + 2 * i + t;
+      const bool valid = qk < eb;
+      const int qq = valid ? qk : ea + 2 * i;
+      ptr[t] = tiles + (size_t)qq * Q::BYTES;
+      hi[t] = (valid && c.has_q) ? min(TS, ntok - qq * TS) : 0;
+      e[t] = valid ? base + qq : c.g->TILES;
+    }
+  };
+  const uint8_t *cp[2], *np[2];
+  int chi[2], ce[2], nhi[2], ne[2];
+  block(0, cp, chi, ce);
+  QBufT<D, F> qb[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) qt_load<D, F>(cp[t], c.lane, qb[t]);
+  const int lo[2] = {0, 0};
+  for (int i = 0; i < n_blocks; ++i) {
+    block(min(i + 1, n_blocks - 1), np, nhi, ne);
+    // keys: exact float32 values, as two fp16 limbs, for each k-block
+    floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float ks, kz;
+        if (F == 2) {
+          ks = h_hi(qb[t].kp[0]);
+          kz = h_lo(qb[t].kp[0]);
+        } else {
+          ks = h_lo(qb[t].kp[kb]);
+          kz = h_hi(qb[t].kp[kb]);
+        }
+        half8 ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = qt_deq<F>(qt_code<D, F>(qb[t].kc, kb * 8 + e), ks, kz);
+          ahi[e] = (half_t)x;
+          alo[e] = (half_t)(x - (float)ahi[e]);
+        }
+        s[t] = mfma_f16_k32(ahi, bqf[kb], s[t]);
+        s[t] = mfma_f16_k32(alo, bqf[kb], s[t]);
+      }
+    float p[2][4], tsum[2];
+    softmax_block<D, 2>(ws, s, sc, lo, chi, c.lq, p, tsum);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    // rows h carry fp16(p), rows 8+h carry fp16(p - fp16(p))
+    half8 ap;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const half_t hp = (half_t)p[t][i2];
+        ap[t * 4 + i2] = c.is_lo ? (half_t)(p[t][i2] - (float)hp) : hp;
+      }
+    // values of the lane's four tokens of each tile, exact, as two fp16 limbs
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      half8 bhi, blo;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          float vs, vz;
+          if (F == 2) {
+            vs = h_hi(qb[t].vp[tt]);
+            vz = h_lo(qb[t].vp[tt]);
+          } else {
+            const uint32_t w = qb[t].vp[tt * (Q::PB / 4) + (ct >> 1)];   // group ct*16/32
+            vs = h_lo(w);
+            vz = h_hi(w);
+          }
+          const float x = qt_deq<F>(qt_code<D, F>(qb[t].vc, ct * 4 + tt), vs, vz);
+          const half_t xh = (half_t)x;
+          bhi[t * 4 + tt] = xh;
+          blo[t * 4 + tt] = (half_t)(x - (float)xh);
+        }
+      ws.acc[ct] = mfma_f16_k32(ap, bhi, ws.acc[ct]);
+      ws.acc[ct] = mfma_f16_k32(ap, blo, ws.acc[ct]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      qt_load<D, F>(np[t], c.lane, qb[t]);
+      cp[t] = np[t];
+      chi[t] = nhi[t];
+      ce[t] = ne[t];
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tok_attend_kernel(
     TokGeom g, TokState st, TokStep ts, const uint16_t *__restrict__ q, size_t q_bstride, float scale_log2) {
-  constexpr int KB = D / 32, CT = D / 16, CP = D / 32;
+  constexpr int KB = D / 32, CT = D / 16;
   const int S = g.n_splits;
   const int split = blockIdx.x % S;
   const int bh = blockIdx.x / S;
@@ -152,10 +475,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float sm_l[ATT_WAVES][8];
   __shared__ float sm_o[ATT_WAVES][8][D];
 
-  const TokList L = tok_list(g, ts);
-  const int E = L.count();
-  const int NS = 4 * S, gi = split * 4 + wave;
-  const int ea = (int)((long long)E * gi / NS), eb = (int)((long long)E * (gi + 1) / NS);
+  const TokList L = tok_list(g, st, ts, bh);
+  TokCtx c;
+  c.g = &g;
+  c.st = &st;
+  c.ts = &ts;
+  c.L = &L;
+  c.b = b;
+  c.h = h;
+  c.bh = bh;
+  c.lane = lane;
+  c.col = col;
+  c.lq = lq;
+  c.G = G;
+  c.is_hi = is_hi;
+  c.is_lo = is_lo;
+  c.has_q = has_q;
+  c.mrho = st.mrho + (size_t)bh * (g.TILES + 1) * G * TS;
+  c.mref = st.mref + (size_t)bh * (g.TILES + 1) * G;
 
   WaveState<D> ws;
 #pragma unroll
@@ -164,101 +501,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   ws.m = has_q ? neg_inf() : 0.0f;   // columns without a head keep a finite reference
   ws.l = 0.0f;
 
-  // query B operands (columns h and 8+h carry head h)
+  // query operands: bf16 for full-precision tiles; fp16 scaled by 2^-e (one e
+  // per KV head) for quantized ones.  Columns h and 8+h carry head h.
   bf16x8 bq[KB];
+  half8 bqf[KB];
+  float scq = scale_log2;
   {
     const uint16_t *qrow = q + (size_t)b * q_bstride + ((size_t)h * G + hc) * D;
     const uint32_t keep = has_q ? 0xffffffffu : 0u;
+    float amax = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 r = *(const uint4 *)(qrow + kb * 32 + lq * 8);
-      bq[kb] = __builtin_bit_cast(bf16x8, make_uint4(r.x & keep, r.y & keep, r.z & keep, r.w & keep));
+      const uint4 rk = make_uint4(r.x & keep, r.y & keep, r.z & keep, r.w & keep);
+      bq[kb] = __builtin_bit_cast(bf16x8, rk);
+      const uint16_t *e = (const uint16_t *)&rk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
     }
+    amax = max_x32(max_x16(amax));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 8));
+    int qexp = 0;
+    if (amax > 0.0f) frexpf(amax, &qexp);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint16_t *e = (const uint16_t *)&bq[kb];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bqf[kb][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+    }
+    scq = ldexpf(scale_log2, qexp);
   }
-  float *mrho = st.mrho + (size_t)bh * (g.TILES + 1) * G * TS;
-  float *mref = st.mref + (size_t)bh * (g.TILES + 1) * G;
 
-  if (ea < eb) {
-    const int n_blocks = (eb - ea + 1) >> 1;
-    // block i = tiles ea+2i, ea+2i+1 (a missing second tile repeats the first, masked)
-    auto block = [&](int i, const uint16_t *(&ptr)[2], int (&lo)[2], int (&hi)[2], int (&e)[2]) {
+  // this wave's share: slice gi of 4*S of every part of the list
+  const int NS = 4 * S, gi = split * 4 + wave;
+  auto slice = [&](int n, int &a, int &z) {
+    a = (int)((long long)n * gi / NS);
+    z = (int)((long long)n * (gi + 1) / NS);
+  };
+  int fa, fz;
+  slice(L.s0 + L.nC + L.nR, fa, fz);   // full-precision tiles (virtual order: sink, compact, recent)
+  int qa[3], qz[3];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int k = ea + 2 * i + t;
-        const bool valid = k < eb;
-        ptr[t] = tok_tile(g, st, ts, L, b, h, valid ? k : ea + 2 * i, lo[t], hi[t]);
-        if (!valid || !has_q) {
-          lo[t] = 0;
-          hi[t] = 0;
-        }
-        e[t] = valid ? k : g.TILES;
-      }
-    };
-    const uint16_t *cp[2], *np[2];
-    int clo[2], chi[2], ce[2], nlo[2], nhi[2], ne[2];
-    block(0, cp, clo, chi, ce);
-    uint4 kr[2][KB], vr[2][CP];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(cp[t] + (kb * 64 + lane) * 8);
-#pragma unroll
-      for (int p = 0; p < CP; ++p) vr[t][p] = *(const uint4 *)(cp[t] + TS * D + (p * 64 + lane) * 8);
-    }
-    for (int i = 0; i < n_blocks; ++i) {
-      block(min(i + 1, n_blocks - 1), np, nlo, nhi, ne);   // the last block re-reads itself
-      floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(np[t] + (kb * 64 + lane) * 8);
-      float p[2][4], tsum[2];
-      softmax_block<D, 2>(ws, s, scale_log2, clo, chi, lq, p, tsum);
-      // per-slot probabilities of the heads (lanes of column h < G hold rows 4*lq..+3)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int er = is_hi ? ce[t] : g.TILES;
-        *(float4 *)(mrho + ((size_t)er * G + (col & (G - 1))) * TS + 4 * lq) =
-            make_float4(p[t][0], p[t][1], p[t][2], p[t][3]);
-        const int em = (is_hi && lq == 0) ? ce[t] : g.TILES;
-        mref[(size_t)em * G + (col & (G - 1))] = ws.m;
-      }
-      // rows h carry bf16(p), rows 8+h carry bf16(p - bf16(p))
-      bf16x8 ap;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          const float hi_ = (float)(__bf16)p[t][i2];
-          ap[t * 4 + i2] = (__bf16)(is_lo ? p[t][i2] - hi_ : p[t][i2]);
-        }
-#pragma unroll
-      for (int p2 = 0; p2 < CP; ++p2) {
-        const uint4 v0 = make_uint4(vr[0][p2].x, vr[0][p2].y, vr[1][p2].x, vr[1][p2].y);
-        const uint4 v1 = make_uint4(vr[0][p2].z, vr[0][p2].w, vr[1][p2].z, vr[1][p2].w);
-        ws.acc[2 * p2] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * p2]);
-        ws.acc[2 * p2 + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * p2 + 1]);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = *(const uint4 *)(np[t] + TS * D + (p2 * 64 + lane) * 8);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        cp[t] = np[t];
-        clo[t] = nlo[t];
-        chi[t] = nhi[t];
-        ce[t] = ne[t];
-      }
-    }
+  for (int k = 0; k < 3; ++k) slice(L.nQ[k], qa[k], qz[k]);
+  tok_run_bf16<D>(ws, c, bq, scale_log2, fa, fz);
+  if (g.policy == QKV_POLICY_HQEKV) {
+    tok_run_quant<D, 0>(ws, c, bqf, scq, qa[0], qz[0]);
+    tok_run_quant<D, 1>(ws, c, bqf, scq, qa[1], qz[1]);
+    tok_run_quant<D, 2>(ws, c, bqf, scq, qa[2], qz[2]);
   }
 
   // ---- wave epilogue: fold the low-limb rows 8+h onto rows h ----
-  float l_tot = sum_x32(sum_x16(ws.l));
+  const float l_tot = sum_x32(sum_x16(ws.l));
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -280,16 +576,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   const size_t pbase = ((size_t)bh * S + split) * G;
   for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
-    const int hh = it / D, c = it % D;
+    const int hh = it / D, cc = it % D;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
     float o = 0.0f;
 #pragma unroll
     for (int w = 0; w < ATT_WAVES; ++w)
-      if (sm_m[w][hh] != neg_inf()) o += sm_o[w][hh][c] * exp2f(sm_m[w][hh] - M);
-    st.part_o[(pbase + hh) * D + c] = o;
-    if (c == 0) {
+      if (sm_m[w][hh] != neg_inf()) o += sm_o[w][hh][cc] * exp2f(sm_m[w][hh] - M);
+    st.part_o[(pbase + hh) * D + cc] = o;
+    if (cc == 0) {
       float l = 0.0f;
 #pragma unroll
       for (int w = 0; w < ATT_WAVES; ++w)
@@ -331,7 +627,7 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
     const float2 *ml = (const float2 *)st.part_ml + (size_t)bh * S * G;
     const float *po = st.part_o + (size_t)bh * S * G * D;
     for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
-      const int hh = it / D, c = it % D;
+      const int hh = it / D, cc = it % D;
       float m = neg_inf(), l = 0.0f, o = 0.0f;
       for (int s0 = 0; s0 < S; s0 += CH) {
         float2 mls[CH];
@@ -340,7 +636,7 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
         for (int k = 0; k < CH; ++k) {
           const int sp = min(s0 + k, S - 1);
           mls[k] = ml[sp * G + hh];
-          os[k] = po[(size_t)(sp * G + hh) * D + c];
+          os[k] = po[(size_t)(sp * G + hh) * D + cc];
         }
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
@@ -352,7 +648,7 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
           m = mn;
         }
       }
-      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o / l;
+      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + cc] = o / l;
     }
     return;
   }
@@ -361,22 +657,30 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
   const int mb = blockIdx.x - n_out_blocks;
   const int bh = mb / n_chunks, chunk = mb % n_chunks;
   const int b = bh / g.Hkv, h = bh % g.Hkv;
-  const TokList L = tok_list(g, ts);
+  const TokList L = tok_list(g, st, ts, bh);
   const int k = chunk * (256 / TS) + (int)threadIdx.x / TS;   // tile
   const int slot = threadIdx.x % TS;
   if ((int)threadIdx.x < G) tok_split_stats(g, st, bh, threadIdx.x, sM[threadIdx.x], sInvL[threadIdx.x]);
   __syncthreads();
   if (k >= L.count()) return;
-  int lo, hi;
-  (void)tok_tile(g, st, ts, L, b, h, k, lo, hi);
-  if (slot < lo || slot >= hi) return;
-  int pos;
-  if (k < L.s0)
-    pos = slot;
-  else if (k < L.s0 + L.nC)
-    pos = st.cpos[(size_t)bh * g.NCT * TS + (k - L.s0) * TS + slot];
-  else
-    pos = (L.rt0 + (k - L.s0 - L.nC)) * TS + slot;
+  int pos = -1;
+  if (k < L.s0 + L.nC || k >= L.base_r()) {
+    int lo, hi;
+    (void)tok_ftile(g, st, ts, L, b, h, k, lo, hi);
+    if (slot < lo || slot >= hi) return;
+    if (k < L.s0)
+      pos = slot;
+    else if (k < L.s0 + L.nC)
+      pos = st.cpos[(size_t)bh * g.NCT * TS + (k - L.s0) * TS + slot];
+    else
+      pos = (L.rt0 + (k - L.base_r())) * TS + slot;
+  } else {
+    int f = 0;
+    while (k >= L.base_q(f + 1)) ++f;
+    const int idx = (k - L.base_q(f)) * TS + slot;
+    if (idx >= L.nQtok[f]) return;
+    pos = st.qpos[f][(size_t)bh * g.NCT * TS + idx];
+  }
   const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + k) * G * TS;
   const float *ref = st.mref + ((size_t)bh * (g.TILES + 1) + k) * G;
   float mass = 0.0f;
@@ -405,8 +709,12 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
   if (mass_out && (e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.T * sizeof(float), s)) != hipSuccess) return e;
-  const int n_tiles = (g.n_sink > 0 ? 1 : 0) + (ts.n_cmp + TS - 1) / TS +
-                      (ts.N > ts.rstart ? (ts.N - 1) / TS - ts.rstart / TS + 1 : 0);
+  // live tiles per (sequence, KV head): at most the ranked tokens' tiles
+  // (one partial tile per tier) plus the sink and recent tiles
+  const int ranked = g.policy == QKV_POLICY_HQEKV ? ts.rstart : ts.n_cmp;
+  int n_tiles = (g.n_sink > 0 ? 1 : 0) + (ranked + TS - 1) / TS + (g.policy == QKV_POLICY_HQEKV ? 4 : 0) +
+                (ts.N > ts.rstart ? (ts.N - 1) / TS - ts.rstart / TS + 1 : 0);
+  if (n_tiles > g.TILES) n_tiles = g.TILES;
   const int n_chunks = (n_tiles * TS + 255) / 256;
   const dim3 mgrid(g.B * g.Hkv + g.B * g.Hkv * n_chunks);
   if (g.G == 4)
@@ -439,6 +747,20 @@ __device__ inline void tok_bitonic_desc(unsigned long long *keys, int n) {
     }
 }
 
+// copy token `pos` of the position pages into slot i of compact tiles `dst`
+__device__ __forceinline__ void tok_copy_token(const TokGeom &g, const uint16_t *pages_bh, uint16_t *dst_bh, int pos,
+                                               int i, int c0) {
+  const int D = g.d;
+  const uint16_t *sk = pages_bh + (size_t)(pos / TS) * 2 * TS * D;
+  const uint16_t *sv = sk + TS * D;
+  uint16_t *dk = dst_bh + (size_t)(i / TS) * 2 * TS * D;
+  uint16_t *dv = dk + TS * D;
+  const int ts_ = pos % TS, td = i % TS;
+  *(uint4 *)(dk + k_tile_index(td, c0)) = *(const uint4 *)(sk + k_tile_index(ts_, c0));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dv[v_tile_index(td, c0 + j)] = sv[v_tile_index(ts_, c0 + j)];
+}
+
 __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState st, int n_old, int a0, int a1,
                                                              int npow) {
   extern __shared__ unsigned long long keys[];
@@ -465,18 +787,12 @@ __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState
     if (i < keep) cpos[i] = pos;
   }
   // gather the kept tokens (rank order) into the compact tiles
-  const int D = g.d, chunks = D / 8;
+  const int chunks = g.d / 8;
+  const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
+  uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
   for (int it = threadIdx.x; it < keep * chunks; it += blockDim.x) {
-    const int i = it / chunks, c0 = (it % chunks) * 8;
-    const int pos = (int)(keys[i] & 0xffffffffull) - 1;
-    const uint16_t *sk = st.pages + tok_page_offset(g, b, h, pos / TS);
-    const uint16_t *sv = sk + TS * D;
-    uint16_t *dk = st.cpages + tok_cpage_offset(g, b, h, i / TS);
-    uint16_t *dv = dk + TS * D;
-    const int ts_ = pos % TS, td = i % TS;
-    *(uint4 *)(dk + k_tile_index(td, c0)) = *(const uint4 *)(sk + k_tile_index(ts_, c0));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dv[v_tile_index(td, c0 + j)] = sv[v_tile_index(ts_, c0 + j)];
+    const int i = it / chunks;
+    tok_copy_token(g, pages_bh, cpages_bh, (int)(keys[i] & 0xffffffffull) - 1, i, (it % chunks) * 8);
   }
 }
 
@@ -490,17 +806,377 @@ hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep 
 }
 
 // ---------------------------------------------------------------------------
-// export: tiers and scores per (sequence, KV head, position)
+// HqeKV assignment event, one workgroup of 1024 threads per (sequence, KV head)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int hq_level(uint8_t t) {
+  switch (t) {
+    case T_INT4: return HQ_INT4;
+    case T_QUANT: return HQ_INT2;
+    case T_INT1: return HQ_INT1;
+    case T_EVICTED: return HQ_EVICT;
+    default: return HQ_BF16;   // ranked or not-yet-ranked full precision
+  }
+}
+__device__ __forceinline__ uint8_t hq_code(int level) {
+  switch (level) {
+    case HQ_INT4: return T_INT4;
+    case HQ_INT2: return T_QUANT;
+    case HQ_INT1: return T_INT1;
+    case HQ_EVICT: return T_EVICTED;
+    default: return T_FULL;
+  }
+}
+
+// Record of a quantized token (canonical per-token packing, element c of a
+// b-bit code stream at bit b*(c mod (8/b)) of byte c*b/8):
+//   [K codes, d/2 B][V codes, d/2 B][K params d/32 x (s, z) fp16][V params]
+// INT1 keeps (mean, std) fp16 in the first params pair.
+__device__ __forceinline__ int rec_kc(const TokGeom &) { return 0; }
+__device__ __forceinline__ int rec_vc(const TokGeom &g) { return g.d / 2; }
+__device__ __forceinline__ int rec_kp(const TokGeom &g) { return g.d; }
+__device__ __forceinline__ int rec_vp(const TokGeom &g) { return g.d + (g.d / 32) * 4; }
+
+// current float32 value of channel c of a token's key (w = 0) or value (w = 1) row
+__device__ float hq_current(const TokGeom &g, const TokState &st, int b, int h, int pos, int level, int w, int c) {
+  if (level == HQ_BF16) {
+    const uint16_t *t = st.pages + tok_page_offset(g, b, h, pos / TS) + (w ? TS * g.d : 0);
+    return bf16_to_f32(t[w ? v_tile_index(pos % TS, c) : k_tile_index(pos % TS, c)]);
+  }
+  const uint8_t *rec = st.qrec + (((size_t)b * g.Hkv + h) * g.T + pos) * g.rec_bytes;
+  const uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
+  const uint16_t *par = (const uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
+  if (level == HQ_INT1) {
+    const uint32_t bit = (codes[c >> 3] >> (c & 7)) & 1u;
+    const float m = (float)__builtin_bit_cast(half_t, par[0]), sd = (float)__builtin_bit_cast(half_t, par[1]);
+    return __builtin_fmaf(bit ? KAPPA1 : -KAPPA1, sd, m);
+  }
+  const int bits = level == HQ_INT4 ? 4 : 2;
+  const int per = 8 / bits;
+  const uint32_t code = (codes[c / per] >> (bits * (c % per))) & ((1u << bits) - 1u);
+  const int grp = c / 32;
+  const float s = (float)__builtin_bit_cast(half_t, par[2 * grp]), z = (float)__builtin_bit_cast(half_t, par[2 * grp + 1]);
+  return __builtin_fmaf((float)code, s, z);
+}
+
+// Re-quantize one token row (keys w = 0, values w = 1) from `old` to `level`,
+// one wave per row: lane l handles channels l and l + 64.  The current values
+// are read first (all of them), then the record is written.
+__device__ void hq_requant_row(const TokGeom &g, TokState &st, int b, int h, int pos, int old, int level, int w,
+                               int lane) {
+  const int D = g.d;
+  const int n_per = D / 64;   // channels per lane: 1 or 2
+  float x[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) x[j] = j < n_per ? hq_current(g, st, b, h, pos, old, w, lane + 64 * j) : 0.0f;
+  __builtin_amdgcn_wave_barrier();
+  uint8_t *rec = st.qrec + (((size_t)b * g.Hkv + h) * g.T + pos) * g.rec_bytes;
+  uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
+  uint16_t *par = (uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
+  if (level == HQ_INT1) {
+    // mean and population deviation in float64, rounded to float32, then fp16
+    double sum = 0.0;
+    for (int j = 0; j < n_per; ++j) sum += (double)x[j];
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    const float m32 = (float)(sum / D);
+    double ss = 0.0;
+    for (int j = 0; j < n_per; ++j) {
+      const double dv = (double)x[j] - (double)m32;
+      ss += dv * dv;
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    const float sd32 = (float)sqrt(ss / D);
+    const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
+    if (!isfinite((float)m16) || !isfinite((float)sd16)) st.status[0] = QKV_ERANGE;
+    // codes: bit c = x_c > mean; bytes assembled by ballots
+    for (int j = 0; j < n_per; ++j) {
+      const unsigned long long bal = __ballot((double)x[j] > (double)m32);
+      if (lane < 8) codes[8 * j + lane] = (uint8_t)(bal >> (8 * lane));
+    }
+    if (lane == 0) {
+      par[0] = __builtin_bit_cast(uint16_t, m16);
+      par[1] = __builtin_bit_cast(uint16_t, sd16);
+    }
+    return;
+  }
+  const int bits = level == HQ_INT4 ? 4 : 2;
+  const float levels = (float)((1 << bits) - 1);
+  for (int j = 0; j < n_per; ++j) {
+    // group of 32 channels: lanes 32*(lane/32) .. +31 of channel chunk j
+    float mn = x[j], mx = x[j];
+    for (int off = 16; off > 0; off >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off));
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    const half_t s16 = (half_t)((mx - mn) / levels);
+    const half_t z16 = (half_t)mn;
+    if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
+    const uint32_t code = quant_code(x[j], s16, z16, levels);
+    // pack: element c at bit bits*(c mod per) of byte c/per
+    const int c = lane + 64 * j;
+    const int per = 8 / bits;
+    uint32_t byte = code << (bits * (c % per));
+    // combine the per lanes of one byte (lanes c/per*per .. +per-1 are adjacent)
+    for (int off = 1; off < per; off <<= 1) byte |= __shfl_xor(byte, off);
+    if (c % per == 0) codes[c / per] = (uint8_t)byte;
+    const int grp = c / 32;
+    if (c % 32 == 0) {
+      par[2 * grp] = __builtin_bit_cast(uint16_t, s16);
+      par[2 * grp + 1] = __builtin_bit_cast(uint16_t, z16);
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, int N, int elig_end, int c0, int c1,
+                                                        int c2, int c3) {
+  const int bh = blockIdx.x;
+  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const size_t tb = (size_t)bh * g.T;
+  const int tid = threadIdx.x;
+  __shared__ unsigned int hist[4][256];
+  __shared__ unsigned long long prefix[4];
+  __shared__ long long rem[4];
+  __shared__ int n_elig;
+  __shared__ unsigned long long thr[4];
+  auto eligible = [&](int pos) {
+    const uint8_t t = st.tier[tb + pos];
+    return t != T_EVICTED && t != T_EMPTY;
+  };
+  auto keyof = [&](int pos) {
+    const float metric = st.score[tb + pos] * st.vrange[tb + pos];   // accumulated attention x value range
+    return ((unsigned long long)__float_as_uint(metric) << 32) | (unsigned)(pos + 1);
+  };
+  // eligible count
+  if (tid == 0) n_elig = 0;
+  __syncthreads();
+  {
+    int cnt = 0;
+    for (int pos = tid; pos < elig_end; pos += blockDim.x) cnt += eligible(pos) ? 1 : 0;
+    atomicAdd(&n_elig, cnt);
+  }
+  __syncthreads();
+  const long long E = n_elig;
+  const long long cum[4] = {c0, (long long)c0 + c1, (long long)c0 + c1 + c2, (long long)c0 + c1 + c2 + c3};
+  // radix select of the four cut keys: the key with exactly cum[j]-1 keys above it
+  if (tid < 4) {
+    prefix[tid] = 0ull;
+    rem[tid] = cum[tid] - 1;
+  }
+  for (int byte = 7; byte >= 0; --byte) {
+    for (int i = tid; i < 4 * 256; i += blockDim.x) hist[i / 256][i % 256] = 0u;
+    __syncthreads();
+    const int sh = 8 * byte;
+    const unsigned long long hmask = byte == 7 ? 0ull : (~0ull << (sh + 8));
+    for (int pos = tid; pos < elig_end; pos += blockDim.x) {
+      if (!eligible(pos)) continue;
+      const unsigned long long key = keyof(pos);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (rem[j] >= 0 && rem[j] < E && (key & hmask) == (prefix[j] & hmask))
+          atomicAdd(&hist[j][(key >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 4 && rem[tid] >= 0 && rem[tid] < E) {
+      long long acc = 0;
+      for (int v = 255; v >= 0; --v) {
+        const unsigned int c = hist[tid][v];
+        if (acc + c > rem[tid]) {
+          prefix[tid] |= (unsigned long long)v << sh;
+          rem[tid] -= acc;
+          break;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < 4) {
+    // keys >= thr[j] have rank < cum[j]: all of them when cum[j] >= E, none when cum[j] == 0
+    thr[tid] = cum[tid] >= E ? 0ull : (cum[tid] <= 0 ? ~0ull : prefix[tid]);
+    st.cuts[bh * 4 + tid] = thr[tid];
+  }
+  __syncthreads();
+  // targets, downgrade only, re-quantization (one wave per changed token)
+  const int wave = tid >> 6, lane = tid & 63, n_waves = blockDim.x >> 6;
+  for (int base = 0; base < elig_end; base += 64 * n_waves) {
+    const int pos = base + wave * 64 + lane;
+    int old = HQ_EVICT, nw = HQ_EVICT;
+    if (pos < elig_end && eligible(pos)) {
+      const unsigned long long key = keyof(pos);
+      int target = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
+      old = hq_level(st.tier[tb + pos]);
+      nw = max(old, target);
+    }
+    // the wave walks its changed tokens one by one
+    unsigned long long todo = __ballot(pos < elig_end && nw > old);
+    while (todo) {
+      const int l = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int p = __shfl(pos, l), o = __shfl(old, l), n2 = __shfl(nw, l);
+      if (n2 != HQ_EVICT) {
+        hq_requant_row(g, st, b, h, p, o, n2, 0, lane);
+        hq_requant_row(g, st, b, h, p, o, n2, 1, lane);
+      }
+      if (lane == 0) st.tier[tb + p] = hq_code(n2);
+    }
+  }
+  __syncthreads();
+  // ranked tokens (pos < elig_end) per tier, in position order -> position lists
+  __shared__ int run[4];
+  __shared__ int wsum[16][4];
+  if (tid < 4) run[tid] = 0;
+  __syncthreads();
+  for (int base = 0; base < elig_end; base += blockDim.x) {
+    const int pos = base + tid;
+    int lvl = HQ_EVICT;
+    if (pos < elig_end) lvl = hq_level(st.tier[tb + pos]);
+    // block prefix sums of the four tier flags
+    int incl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned long long bal = __ballot(lvl == k);
+      incl[k] = __popcll(bal & ((2ull << lane) - 1ull));   // inclusive within the wave
+      if (lane == 63) wsum[wave][k] = __popcll(bal);
+    }
+    __syncthreads();
+    if (pos < elig_end && lvl < 4) {
+      int off = run[lvl] + incl[lvl] - 1;
+      for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2][lvl];
+      if (lvl == HQ_BF16)
+        st.cpos[(size_t)bh * g.NCT * TS + off] = pos;
+      else
+        st.qpos[lvl - 1][(size_t)bh * g.NCT * TS + off] = pos;
+    }
+    __syncthreads();
+    if (tid < 4) {
+      int t = 0;
+      for (int w2 = 0; w2 < n_waves; ++w2) t += wsum[w2][tid];
+      run[tid] += t;
+    }
+    __syncthreads();
+  }
+  if (tid < 4) st.cnt[bh * 4 + tid] = run[tid];
+  (void)N;
+}
+
+__device__ __forceinline__ size_t tb_of(const TokGeom &g, int bh) { return (size_t)bh * g.T; }
+
+// compact tiles of every tier from the position lists: one thread per
+// (token slot, 8-channel chunk) for BF16, per (token slot) for quantized tiers
+template <int D>
+__global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) {
+  const int bh = blockIdx.y;
+  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const int chunks = D / 8;
+  const int nb = st.cnt[bh * 4 + 0];
+  const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
+  uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < nb * chunks; it += gridDim.x * blockDim.x) {
+    const int i = it / chunks;
+    tok_copy_token(g, pages_bh, cpages_bh, st.cpos[(size_t)bh * g.NCT * TS + i], i, (it % chunks) * 8);
+  }
+  // quantized tiers: one thread per (slot, lane of the tile layout)
+  constexpr int KB = D / 32, CT = D / 16;
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
+    const int bits = QBITS[f];
+    const int LB = KB * bits < 4 ? 4 : KB * bits, PB = f == 2 ? 4 : KB * 4, BYTES = 128 * LB + 32 * PB;
+    const int nq = st.cnt[bh * 4 + 1 + f];
+    const int ntiles = (nq + TS - 1) / TS;
+    uint8_t *tiles = st.qtiles[f] + (size_t)bh * g.NCT * BYTES;
+    const int32_t *qpos = st.qpos[f] + (size_t)bh * g.NCT * TS;
+    for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
+      const int tile = it / 64, lane = it % 64;
+      uint8_t *T = tiles + (size_t)tile * BYTES;
+      const int t = lane & 15, lq = lane >> 4;
+      // keys: this lane's token is slot t
+      const int ks = tile * TS + t;
+      uint32_t kw[4] = {0u, 0u, 0u, 0u};
+      if (ks < nq) {
+        const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[ks]) * g.rec_bytes;
+        for (int kb = 0; kb < KB; ++kb)
+          for (int e = 0; e < 8; ++e) {
+            const int cch = kb * 32 + 8 * lq + e;
+            uint32_t code;
+            if (bits == 1)
+              code = (rec[cch >> 3] >> (cch & 7)) & 1u;
+            else
+              code = (rec[cch * bits / 8] >> (bits * (cch % (8 / bits)))) & ((1u << bits) - 1u);
+            const int bit = (kb * 8 + e) * bits;
+            kw[bit >> 5] |= code << (bit & 31);
+          }
+      }
+      for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + lane * LB))[w] = kw[w];
+      // values: this lane's column l%16, tokens 4*lq .. +3
+      uint32_t vw[4] = {0u, 0u, 0u, 0u};
+      for (int tt = 0; tt < 4; ++tt) {
+        const int vs = tile * TS + 4 * lq + tt;
+        if (vs >= nq) continue;
+        const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[vs]) * g.rec_bytes + g.d / 2;
+        for (int ct = 0; ct < CT; ++ct) {
+          const int cch = ct * 16 + t;
+          uint32_t code;
+          if (bits == 1)
+            code = (rec[cch >> 3] >> (cch & 7)) & 1u;
+          else
+            code = (rec[cch * bits / 8] >> (bits * (cch % (8 / bits)))) & ((1u << bits) - 1u);
+          const int bit = (ct * 4 + tt) * bits;
+          vw[bit >> 5] |= code << (bit & 31);
+        }
+      }
+      for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + 64 * LB + lane * LB))[w] = vw[w];
+      // params of slot t (keys then values), written by the lanes of row lq == 0
+      if (lq == 0) {
+        const int sl = tile * TS + t;
+        const uint8_t *rec = sl < nq ? st.qrec + (tb_of(g, bh) + qpos[sl]) * g.rec_bytes : nullptr;
+        for (int bb = 0; bb < PB; ++bb) {
+          T[128 * LB + t * PB + bb] = rec ? rec[g.d + bb] : 0;
+          T[128 * LB + 16 * PB + t * PB + bb] = rec ? rec[g.d + (g.d / 32) * 4 + bb] : 0;
+        }
+      }
+    }
+  }
+}
+
+hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(hq_event_kernel, dim3(g.B * g.Hkv), dim3(1024), 0, s, g, st, N, elig_end, counts[0], counts[1],
+                     counts[2], counts[3]);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(64, g.B * g.Hkv);
+  if (g.d == 128)
+    hipLaunchKernelGGL(hq_gather_kernel<128>, grid, dim3(256), 0, s, g, st);
+  else
+    hipLaunchKernelGGL(hq_gather_kernel<64>, grid, dim3(256), 0, s, g, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// export: tiers and scores per (sequence, KV head, position); HqeKV records
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void tok_export_kernel(TokGeom g, TokState st, int what, void *dst) {
   const size_t n = (size_t)g.B * g.Hkv * g.T;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    if (what == QKV_EXPORT_TIERS)
-      ((uint8_t *)dst)[i] = st.tier[i];
-    else
-      ((float *)dst)[i] = st.score[i];
+  if (what == QKV_EXPORT_TIERS || what == QKV_EXPORT_SCORES) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+      if (what == QKV_EXPORT_TIERS)
+        ((uint8_t *)dst)[i] = st.tier[i];
+      else
+        ((float *)dst)[i] = st.score[i];
+    }
+    return;
   }
+  // records: KCODES / VCODES [.., d/2] bytes, KPARAMS / VPARAMS [.., d/32, 2] fp16
+  const int off = what == QKV_EXPORT_KCODES ? 0 : what == QKV_EXPORT_VCODES ? g.d / 2
+                : what == QKV_EXPORT_KPARAMS ? g.d : g.d + (g.d / 32) * 4;
+  const int len = (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) ? g.d / 2 : (g.d / 32) * 4;
+  const size_t total = n * len;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x)
+    ((uint8_t *)dst)[i] = st.qrec[(i / len) * g.rec_bytes + off + (i % len)];
 }
 
 hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, void *dst, hipStream_t s) {
