@@ -1,0 +1,156 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (default splits), on sampled sequences / KV heads that the
+oracle follows step by step.
+
+* QEvict drift layer: batch 16, 32768-token prompt, Kf = 204, Kq = 612;
+  160 steps (ten routing events, the query switch at step 100).
+* QEvict stress layer: batch 32, 131072-token prompt, Hq = 64 (G = 8),
+  32-token windows; the first routing event and the steps around it.
+* HqeKV layer: batch 8, 65536-token prompt, two assignment events.
+
+Bars as in the small parity tests: outputs 2e-3, scores 1e-4 relative,
+tiers exact (codes and parameters are compared bit for bit in the small
+parity tests, which export them).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import hqekv as oq
+from oracle import qevict as oe
+
+from _harness import QEvictGPURun, gpu_inputs_parallel, gpu_inputs_sampled, log
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-3
+SCORE_RTOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiered_quantization_eviction_amd  # noqa: F401  (raises if the library is missing)
+    return torch
+
+
+def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True):
+    log(f"[{label}] generating {cfg.batch} x {cfg.total_tokens} tokens")
+    K, V, Q = gpu_inputs_parallel(cfg) if all_real else gpu_inputs_sampled(cfg, seq_ids)
+    run = QEvictGPURun(cfg, K, V, Q)
+    log(f"[{label}] GPU cache ready ({run.cache.info('splits')} splits); oracle sequences {seq_ids}")
+    wl = W.Workload(cfg)
+    seqs, qs = {}, {}
+    for b in seq_ids:
+        k, v = wl.kv(b)
+        seqs[b] = oe.QEvictSequence(k, v, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
+                                    n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
+                                    bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads)
+        seqs[b].prefill(cfg.prefill)
+        qs[b] = wl.queries(b)
+    worst, routes = 0.0, 0
+    for s in range(cfg.steps):
+        routed = run.step(want_mass=False)
+        torch.cuda.synchronize()
+        out = run.out.cpu().numpy()
+        scores = run.scores()
+        for b in seq_ids:
+            o, _ = seqs[b].step(s, qs[b][s])
+            err = float(np.abs(out[b] - o).max())
+            worst = max(worst, err)
+            assert err <= OUT_TOL, f"step {s} seq {b}: out err {err}"
+            np.testing.assert_allclose(scores[b], seqs[b].score, rtol=SCORE_RTOL, atol=1e-7,
+                                       err_msg=f"scores step {s} seq {b}")
+        if routed:
+            routes += 1
+            tiers = run.tiers()
+            for b in seq_ids:
+                np.testing.assert_array_equal(tiers[b], seqs[b].tier,
+                                              err_msg=f"tiers after event {routes} (step {s}) seq {b}, "
+                                                      f"margins {seqs[b].events[-1].margins}")
+        if s % 16 == 15:
+            log(f"[{label}] step {s + 1}: worst out err {worst:.2e}, routes {routes}")
+    promoted = sum(len(e.promoted) for sq in seqs.values() for e in sq.events)
+    log(f"[{label}] done: worst out err {worst:.3e}, routes {routes}, promotions {promoted}")
+    return seqs
+
+
+def test_drift_fullsize_sampled(torch_cuda):
+    _qevict_sampled(W.DRIFT.replace(steps=160), torch_cuda, [0, 11], "drift-full")
+
+
+def test_stress_fullsize_sampled(torch_cuda):
+    """Batch 32 at 131072 tokens; sequence 5 follows the clustered recipe and
+    the oracle, the other 31 are normal filler of the same shape."""
+    _qevict_sampled(W.STRESS.replace(steps=36), torch_cuda, [5], "stress-full", all_real=False)
+
+
+def test_hqekv_fullsize_sampled(torch_cuda):
+    """Config of the HqeKV layer at full size, two KV heads followed by the oracle."""
+    from tiered_quantization_eviction_amd import Cache, make_config
+    torch = torch_cuda
+    cfg = W.HQEKV.replace(steps=128)
+    B, Hkv, G, d, P, T = cfg.batch, cfg.n_kv_heads, cfg.group_size, cfg.head_dim, cfg.prefill, cfg.total_tokens
+    m = cfg.init_queries
+    label = "hqekv-full"
+    sampled = [(0, 0), (5, 3)]
+    log(f"[{label}] generating {B} x {T} tokens")
+    K, V, Q = gpu_inputs_sampled(cfg, sorted({b for b, _ in sampled}))
+    wl = W.Workload(cfg)
+    qt = np.stack([wl.prefill_queries(b, P - m, P) if b in (0, 5) else
+                   np.zeros((m, cfg.n_q_heads, d), np.uint16) for b in range(B)])
+    log(f"[{label}] prompt queries ready")
+    cache = Cache(make_config(cfg))
+    out = torch.zeros((B, cfg.n_q_heads, d), dtype=torch.float32, device="cuda")
+    cache.append(K[:, :, :P].contiguous(), V[:, :, :P].contiguous())
+    cache.prefill_score(torch.from_numpy(qt.view(np.int16)).cuda())
+    cache.route()
+    log(f"[{label}] GPU prompt scored and assigned")
+    ratios32 = tuple(float(np.float32(r)) for r in cfg.ratios)
+    groups = {}
+    for b, g in sampled:
+        k, v = wl.kv(b)
+        grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group)
+        grp.prefill(P, qt[b][:, g * G:(g + 1) * G])
+        groups[b, g] = grp
+        log(f"[{label}] oracle (seq {b}, head {g}) prompt assigned")
+    qs = {b: wl.queries(b) for b, _ in sampled}
+    log(f"[{label}] first assignment done on both sides")
+    to_o = {2: oq.BF16, 3: oq.BF16, 6: oq.INT4, 4: oq.INT2, 7: oq.INT1, 5: oq.EVICT, 0: 255}
+
+    def check(tag):
+        torch.cuda.synchronize()
+        tiers = cache.export("tiers").cpu().numpy().reshape(B, Hkv, T)
+        scores = cache.export("scores").cpu().numpy().view(np.float32).reshape(B, Hkv, T)
+        for (b, g), grp in groups.items():
+            got = np.vectorize(to_o.get)(tiers[b, g]).astype(np.uint8)
+            np.testing.assert_array_equal(got, grp.tier, err_msg=f"{tag}: tiers (seq {b}, head {g})")
+            live = np.flatnonzero((grp.tier != 255) & (grp.tier != oq.EVICT))
+            np.testing.assert_allclose(scores[b, g, live], grp.score[live], rtol=SCORE_RTOL, atol=1e-7,
+                                       err_msg=f"{tag}: scores (seq {b}, head {g})")
+        log(f"[{label}] {tag}: tiers and scores agree")
+
+    check("first assignment")
+    worst = 0.0
+    for s in range(cfg.steps):
+        t = P + s
+        cache.append(K[:, :, t:t + 1].contiguous(), V[:, :, t:t + 1].contiguous())
+        cache.decode_attend(Q[:, s].contiguous(), out)
+        event = (s + 1) % cfg.omega == 0
+        if event:
+            cache.route()
+        torch.cuda.synchronize()
+        o_gpu = out.cpu().numpy()
+        for (b, g), grp in groups.items():
+            o, _, _ = grp.step(s, t, qs[b][s][g * G:(g + 1) * G])
+            err = float(np.abs(o_gpu[b, g * G:(g + 1) * G] - o).max())
+            worst = max(worst, err)
+            assert err <= OUT_TOL, f"step {s} (seq {b}, head {g}): out err {err}"
+        if event:
+            check(f"event after step {s}")
+        if s % 16 == 15:
+            log(f"[{label}] step {s + 1}: worst out err {worst:.2e}")
+    log(f"[{label}] done: worst out err {worst:.3e}")
+

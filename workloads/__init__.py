@@ -249,14 +249,13 @@ class Workload:
         """q_h = 2 k_j + N(0,1), j uniform over positions <= the query's own."""
         cfg = self.cfg
         kb, _ = self.kv(b)
-        kf = bf16_bits_to_f32(kb)
         rng = _rng(cfg, b, tensor)
         n = len(positions)
         hq, d, G = cfg.n_q_heads, cfg.head_dim, cfg.group_size
         j = np.floor(rng.random((n, hq)) * (positions[:, None] + 1)).astype(np.int64)
         noise = rng.standard_normal((n, hq, d), dtype=np.float32)
         g = np.arange(hq) // G
-        q = np.float32(2.0) * kf[g[None, :], j, :] + noise
+        q = np.float32(2.0) * bf16_bits_to_f32(kb[g[None, :], j, :]) + noise   # only the target keys
         return f32_to_bf16_bits(q)
 
     def queries(self, b: int) -> np.ndarray:
