@@ -31,15 +31,19 @@ def _gen_seq(args):
 
 
 def gpu_inputs_parallel(cfg: W.Config, workers: int = 16):
-    """Like gpu_inputs for large workloads: sequences generated in forked
-    worker processes (each sequence has its own streams)."""
+    """Like gpu_inputs for large workloads: sequences generated in worker
+    processes (each sequence has its own streams).  Workers are spawned, not
+    forked: the test process has already initialized the GPU runtime."""
     import multiprocessing as mp
     import os
     from concurrent.futures import ProcessPoolExecutor
     import torch
     n = max(1, min(workers, len(os.sched_getaffinity(0)), cfg.batch))
-    with ProcessPoolExecutor(n, mp_context=mp.get_context("fork")) as ex:
-        res = list(ex.map(_gen_seq, [(cfg, b) for b in range(cfg.batch)]))
+    with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as ex:
+        res = []
+        for b, r in enumerate(ex.map(_gen_seq, [(cfg, b) for b in range(cfg.batch)])):
+            res.append(r)
+            log(f"  sequence {b} generated")
     K = torch.from_numpy(np.stack([r[0] for r in res]).view(np.int16)).cuda()
     V = torch.from_numpy(np.stack([r[1] for r in res]).view(np.int16)).cuda()
     Q = torch.from_numpy(np.stack([r[2] for r in res]).view(np.int16)).cuda()
@@ -62,7 +66,7 @@ def gpu_inputs_sampled(cfg: W.Config, real, seed: int = 1234):
     V = torch.randn((B, Hkv, T, d), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
     Q = (2.0 * torch.randn((B, S, Hq, d), generator=gen, device="cuda")).to(torch.bfloat16).view(torch.int16)
     n = max(1, min(16, len(os.sched_getaffinity(0)), len(real)))
-    with ProcessPoolExecutor(n, mp_context=mp.get_context("fork")) as ex:
+    with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as ex:   # no fork after GPU init
         for b, (k, v, q) in zip(real, ex.map(_gen_seq, [(cfg, b) for b in real])):
             K[b] = torch.from_numpy(k.view(np.int16)).cuda()
             V[b] = torch.from_numpy(v.view(np.int16)).cuda()

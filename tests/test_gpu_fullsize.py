@@ -3,9 +3,10 @@ benchmark times (default splits), on sampled sequences / KV heads that the
 oracle follows step by step.
 
 * QEvict drift layer: batch 16, 32768-token prompt, Kf = 204, Kq = 612;
-  160 steps (ten routing events, the query switch at step 100).
+  160 steps (ten routing events, the query switch at step 100 and the
+  promotions that follow it).
 * QEvict stress layer: batch 32, 131072-token prompt, Hq = 64 (G = 8),
-  32-token windows; the first routing event and the steps around it.
+  32-token windows; two routing events.
 * HqeKV layer: batch 8, 65536-token prompt, two assignment events.
 
 Bars as in the small parity tests: outputs 2e-3, scores 1e-4 relative,
@@ -78,13 +79,15 @@ def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True):
 
 
 def test_drift_fullsize_sampled(torch_cuda):
-    _qevict_sampled(W.DRIFT.replace(steps=160), torch_cuda, [0, 11], "drift-full")
+    seqs = _qevict_sampled(W.DRIFT.replace(steps=160), torch_cuda, [0, 11], "drift-full")
+    assert sum(len(e.promoted) for sq in seqs.values() for e in sq.events) > 0, \
+        "no INT2 -> BF16 promotion after the query switch"
 
 
 def test_stress_fullsize_sampled(torch_cuda):
     """Batch 32 at 131072 tokens; sequence 5 follows the clustered recipe and
     the oracle, the other 31 are normal filler of the same shape."""
-    _qevict_sampled(W.STRESS.replace(steps=36), torch_cuda, [5], "stress-full", all_real=False)
+    _qevict_sampled(W.STRESS.replace(steps=65), torch_cuda, [5], "stress-full", all_real=False)
 
 
 def test_hqekv_fullsize_sampled(torch_cuda):
