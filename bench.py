@@ -38,7 +38,10 @@ HBM_PEAK_GBPS = 8000.0
 # pair delays the following launch by a few microseconds, so timing every step
 # would slow the very loop whose throughput is reported.
 PROFILE_STRIDE = 8
-KERNEL_SRC = os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", "qkv_kernels.hip")
+# The attention kernel is built from these sources; the counter summary is
+# only used while their hash matches the one it was taken on.
+KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
+               for f in ("qkv_kernels.hip", "qkv_device.h", "qkv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
@@ -199,6 +202,13 @@ def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts):
                       f"{dt:.1f} s"}, worst
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def read_traffic(src_hash):
     """HBM bytes per attention launch from the committed counter summary, if
     it was taken on the current kernel source."""
@@ -266,7 +276,7 @@ def main():
     att_avg_s = float(np.mean(attend_ms)) / 1e3
     bytes_per_launch = float(np.mean(sampled))
     achieved = bytes_per_launch / att_avg_s / 1e9
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    src_hash = kernel_source_hash()
     traffic = read_traffic(src_hash)
     log(f"bench: {wall * 1e3:.1f} ms for {steps} steps; attention avg {att_avg_s * 1e6:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")

@@ -377,7 +377,9 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
   for (int j = 0; j < QT; ++j) {
     const int w = qt_win(j, tpw);
     const int tj = j - w * tpw;
-    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h);
+    // both candidates are fixed indices: a run-time index would put u[] in scratch memory
+    const int uw = tpw == 1 ? qb.u[j] : qb.u[j >> 1];
+    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, uw, c.h);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
     if (NKD == 2) {
       buf.code[j] = *(const uint4 *)(T + c.lane * 16);
