@@ -110,8 +110,61 @@ __device__ __forceinline__ float max_x32(float x) {
 // s + (s of the lane 8 columns away): folds the low-limb column 8+h into
 // column h and vice versa (a row rotation by 8, so both get the same sum)
 __device__ __forceinline__ float fold8(float x) {
-  const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));   // row_ror:8
+  // row_ror:8 reads inside the row for every lane, so bound_ctrl changes
+  // nothing; with it the move folds into the add (one DPP add)
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, true));
   return x + y;
+}
+
+// Four per-lane values a, b, c, d -> lane group g (lanes 16g .. 16g+15) gets
+// the sum of the g-th value over the four lane groups of its column
+// (a reduce-scatter: three row-swap permutes and three adds)
+__device__ __forceinline__ float reduce_scatter4(float a, float b, float c, float d) {
+  // lanes 0-31 keep a (b) summed with lanes 32-63; lanes 32-63 keep c (d)
+  const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(d), false, false);
+  const float u = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+  const float v = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+  // within each half: lanes of the lower 16 keep u, the upper 16 keep v
+  const auto r3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(r3[0]) + __uint_as_float(r3[1]);
+}
+
+// Online-softmax update for NT 16-token tiles of log2-domain logits x in C
+// layout (empty rows hold -inf): writes the probabilities p and each lane's
+// per-tile sums ts (over its own 4 rows), and rescales the running state when
+// the running max grows.
+template <int D, int NT>
+__device__ inline void softmax_rows(WaveState<D> &ws, const float (*x)[4], float (*p)[4], float *ts) {
+  float mx = neg_inf();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) mx = fmaxf(mx, fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3])));
+  mx = max_x16(mx);
+  mx = max_x32(mx);
+  const float m_new = fmaxf(ws.m, mx);
+  const bool grow = m_new > ws.m;
+  if (__any(grow)) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f(ws.m - m_new) : 1.0f;
+    ws.l *= alpha;
+    const int lq = (int)(__lane_id() >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ar = __shfl(alpha, 4 * lq + i);
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) ws.acc[ct][i] *= ar;
+      ws.zacc[i] *= ar;
+    }
+    ws.m = m_new;
+  }
+  float lsum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - ws.m);
+    ts[t] = (p[t][0] + p[t][1]) + (p[t][2] + p[t][3]);
+    lsum += ts[t];
+  }
+  ws.l += lsum;
 }
 
 // online-softmax update for a block of NT 16-token tiles (scores in C layout;

@@ -395,8 +395,8 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
 
 template <int D>
 __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&qc)[2],
-                                              const half8 (&bz)[D / 32], float sc_quant, const QBlock &qb,
-                                              const QBuf &buf) {
+                                              const half8 (&bz)[D / 32], float sc_quant, const float (&row_bias)[4],
+                                              const QBlock &qb, const QBuf &buf) {
   constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
   const Geom &g = *c.g;
   const int tpw = g.tpw;
@@ -434,9 +434,6 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     }
   }
   wave_lds_sync();
-  int nv[QT];
-#pragma unroll
-  for (int j = 0; j < QT; ++j) nv[j] = (c.has_q && qt_win(j, tpw) < qb.nwin) ? g.window - (j - qt_win(j, tpw) * tpw) * TS : 0;
   // key-zero term sum_c q_c z_c of every window at once: A rows r are the
   // zero vectors of window slot r % nws, so register i of every lane holds
   // the term of window slot i % nws for the lane's column (high columns only)
@@ -453,7 +450,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const float z = tpw == 1 ? zb[j & 3] : zb[(j >> 1) & 3];
-    s[j] = floatx4{z, z, z, z};
+    s[j] = floatx4{z + row_bias[0], z + row_bias[1], z + row_bias[2], z + row_bias[3]};
   }
   const int qrow = (c.is_lo ? G : 0) + c.hc;
 #pragma unroll
@@ -468,35 +465,51 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   for (int j = 0; j < QT; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[j][i] = fold8(s[j][i]);
-  const int lo[QT] = {0, 0, 0, 0};
-  float p[QT][4], ts[QT];
-  softmax_block<D, QT>(ws, s, sc_quant, lo, nv, c.lq, p, ts);
-  {
-    int e[QT];
-    bool ok[QT];
-    float rho[QT];
+  // log2-domain logits.  Whether a tile holds tokens is uniform over the
+  // wave, so an empty slot costs one scalar bias (-inf) instead of a
+  // per-value mask; rows past a window shorter than a tile start from -inf
+  // in the accumulator.  Columns without a head carry finite duplicates that
+  // nothing reads.
+  float x[QT][4];
 #pragma unroll
-    for (int w = 0; w < QT; ++w) {
-      e[w] = qb.e + w;
-      ok[w] = w < qb.nwin;
-      rho[w] = tpw == 1 ? ts[w] : (w < 2 ? ts[2 * w] + ts[2 * w + 1] : 0.0f);
-    }
-    store_mass<QT>(c, e, ok, rho, ws.m);
+  for (int j = 0; j < QT; ++j) {
+    const float bias = qt_win(j, tpw) < qb.nwin ? 0.0f : neg_inf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[j][i] = __builtin_fmaf(s[j][i], sc_quant, bias);
+  }
+  float p[QT][4], ts[QT];
+  softmax_rows<D, QT>(ws, x, p, ts);
+  // window masses: lane group lq ends with the sum over the 16 rows of
+  // window slot lq (reduce-scatter over the four lane groups), which is the
+  // slot its lanes store
+  {
+    const float a = tpw == 1 ? ts[0] : ts[0] + ts[1];
+    const float b = tpw == 1 ? ts[1] : ts[2] + ts[3];
+    const float cc = tpw == 1 ? ts[2] : 0.0f;
+    const float d = tpw == 1 ? ts[3] : 0.0f;
+    const float rho = reduce_scatter4(a, b, cc, d);
+    const int slot = (c.lq < qb.nwin && c.col < G) ? qb.e + c.lq : g.U;
+    *(float2 *)(c.mass_row + ((size_t)slot * G + (c.col & (G - 1))) * 2) = make_float2(rho, ws.m);
   }
   // fp16 limbs of p; (P1, P2) = (0, phi) on hi lanes, (phi, plo) on lo lanes:
   // one FMA chain then yields fp16(p*s) on hi rows and the remainder on lo rows
   half4 P1[QT], P2[QT];
   const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+  const uint32_t lo_keep = c.is_lo ? 0xffffffffu : 0u;
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
+    // phi: p cut to 11 significant bits (exact in fp16 for p >= 2^-14);
+    // plo: the exact fp32 remainder, rounded to fp16
     half4 phi, plo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      phi[i] = (half_t)p[j][i];
-      plo[i] = (half_t)(p[j][i] - (float)phi[i]);
+      const float ph = __uint_as_float(__float_as_uint(p[j][i]) & 0xffffe000u);
+      phi[i] = (half_t)ph;
+      plo[i] = (half_t)(p[j][i] - ph);
     }
-    P1[j] = c.is_lo ? phi : zero4;
-    P2[j] = c.is_lo ? plo : phi;
+    const uint2 ph = __builtin_bit_cast(uint2, phi), pl = __builtin_bit_cast(uint2, plo);
+    P1[j] = __builtin_bit_cast(half4, make_uint2(ph.x & lo_keep, ph.y & lo_keep));
+    P2[j] = __builtin_bit_cast(half4, make_uint2(c.is_lo ? pl.x : ph.x, c.is_lo ? pl.y : ph.y));
   }
   // PV over tile pairs: k slots = tokens 4*lq..+3 of tile 2pp, then of tile 2pp+1
 #pragma unroll
@@ -542,6 +555,10 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
   half8 qc[2], bz[D / 32];
   const float sc_quant = query_f16<D>(c, qc, bz);
+  // rows of a tile past a window shorter than the tile hold no token
+  float row_bias[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) row_bias[i] = 4 * c.lq + i < c.g->window ? 0.0f : neg_inf();
   const int per = QT / c.g->tpw;
   const int n_blocks = (eb - ea + per - 1) / per;
   // two-slot ring: one block in flight while one computes; unit ids two
@@ -557,12 +574,12 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
     const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 1, n_blocks - 1), ids1, k1);
     quant_load<D>(c, k1, b1);
-    quant_compute<D>(ws, c, qc, bz, sc_quant, k0, b0);
+    quant_compute<D>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
     if (i + 1 >= n_blocks) break;
     ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 2, n_blocks - 1), ids2, k0);
     quant_load<D>(c, k0, b0);
-    quant_compute<D>(ws, c, qc, bz, sc_quant, k1, b1);
+    quant_compute<D>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
     if (i + 2 >= n_blocks) break;
   }
 }
