@@ -104,10 +104,10 @@ void make_geom(const qkv_config *c, Geom &g) {
   g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
   g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;
   int S = c->n_splits;
-  if (S == 0) {   // one resident round: 512 workgroups = 2 per compute unit at 2 waves per SIMD
+  if (S == 0) {   // one resident round: 256 workgroups of 8 waves = 1 per compute unit, 2 waves per SIMD
     const int pairs = g.B * g.Hkv;
-    S = (512 + pairs - 1) / pairs;
-    const int cap = g.U / 4 > 1 ? g.U / 4 : 1;
+    S = (256 + pairs - 1) / pairs;
+    const int cap = g.U / 8 > 1 ? g.U / 8 : 1;
     if (S > cap) S = cap;
     if (S > 64) S = 64;
     if (S < 1) S = 1;

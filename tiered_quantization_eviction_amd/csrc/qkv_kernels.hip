@@ -584,8 +584,12 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   }
 }
 
+// Waves per attention workgroup: one 8-wave workgroup per compute unit
+// holds two waves on each SIMD.
+constexpr int QW = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
+__global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
   constexpr int CT = D / 16;
@@ -604,21 +608,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool is_lo = col >= 8 && col < 8 + G;   // column 8+h: head h again (low limb)
   const int hc = is_hi ? col : (is_lo ? col - 8 : 0);
 
-  __shared__ __attribute__((aligned(16))) half_t s_kp[ATT_WAVES][QT][PSTR<D>];   // key scale/zero per window
-  __shared__ __attribute__((aligned(16))) half_t s_vp[ATT_WAVES][QT][PSTR<D>];   // value params per tile
-  __shared__ float sm_m[ATT_WAVES][8];
-  __shared__ float sm_l[ATT_WAVES][8];
-  __shared__ float sm_o[ATT_WAVES][8][D];
-  extern __shared__ __attribute__((aligned(16))) half_t s_qs[];   // [ATT_WAVES][window slots][2][G][D+8]
+  __shared__ __attribute__((aligned(16))) half_t s_kp[QW][QT][PSTR<D>];   // key scale/zero per window
+  __shared__ __attribute__((aligned(16))) half_t s_vp[QW][QT][PSTR<D>];   // value params per tile
+  __shared__ float sm_m[QW][8];
+  __shared__ float sm_l[QW][8];
+  __shared__ float sm_o[QW][8][D];
+  extern __shared__ __attribute__((aligned(16))) half_t s_qs[];   // [QW][window slots][2][G][D+8]
 
-  // ---- this wave's share: slice gi of 4*S of the full-precision entries
+  // ---- this wave's share: slice gi of QW*S of the full-precision entries
   // (sink, ranked full, recent) and the same slice of the quantized windows,
   // so every workgroup (and so every XCD and CU) gets the same mix of
   // bandwidth-bound and arithmetic-bound work ----
   const EntryList L = make_list(g, st, si, b);
   const int A = L.s0 + L.nF, AQ = A + L.nQ, E = L.count();
   const int nB = A + (E - AQ);
-  const int NS = 4 * S, gi = split * 4 + wave;
+  const int NS = QW * S, gi = split * QW + wave;
   const int vb0 = (int)((long long)nB * gi / NS), vb1 = (int)((long long)nB * (gi + 1) / NS);
   const int q0 = A + (int)((long long)L.nQ * gi / NS), q1 = A + (int)((long long)L.nQ * (gi + 1) / NS);
   // full-precision virtual range [vb0, vb1) -> entries [f0, f1) below A and [r0e, r1e) from AQ on
@@ -658,7 +662,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
   c.qs_lds = s_qs + (size_t)wave * (QT / g.tpw) * 2 * G * QSTR<D>;
-  if (gi & 1) {   // alternate the order so that neighbouring waves are in different phases
+  // Opposite orders for the two waves that share a SIMD, whether the
+  // workgroup's waves are dealt to the SIMDs round-robin (w, w+4) or in
+  // pairs (2k, 2k+1): one streams full-precision tiles while the other
+  // unpacks quantized ones.
+  if (((wave & 1) ^ (wave >> 2)) & 1) {
     run_quant<D>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
     run_full<D>(ws, c, r0e, r1e);    // windows not yet ranked
@@ -699,16 +707,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int hh = it / D, c = it % D;
     float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 0; w < QW; ++w) M = fmaxf(M, sm_m[w][hh]);
     float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w)
+    for (int w = 0; w < QW; ++w)
       if (sm_m[w][hh] != neg_inf()) o += sm_o[w][hh][c] * exp2f(sm_m[w][hh] - M);
     st.part_o[(pbase + hh) * D + c] = o;
     if (c == 0) {
       float l = 0.0f;
 #pragma unroll
-      for (int w = 0; w < ATT_WAVES; ++w)
+      for (int w = 0; w < QW; ++w)
         if (sm_m[w][hh] != neg_inf()) l += sm_l[w][hh] * exp2f(sm_m[w][hh] - M);
       st.part_ml[(pbase + hh) * 2 + 0] = M;
       st.part_ml[(pbase + hh) * 2 + 1] = l;
@@ -832,11 +840,11 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
   if (ev_start) hipEventRecord(ev_start, s);
-  const size_t qs_bytes = (size_t)ATT_WAVES * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+  const size_t qs_bytes = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
   if (g.d == 128)
-    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(256), qs_bytes, s, g, st, si, q, scale_log2);
+    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
   else
-    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(256), qs_bytes, s, g, st, si, q, scale_log2);
+    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_stop) hipEventRecord(ev_stop, s);
