@@ -62,6 +62,23 @@ __device__ __forceinline__ half8 codes8(uint32_t m) {
 
 __device__ inline float neg_inf() { return -__builtin_inff(); }
 
+// Streaming loads of cache tiles: read once per decode step, so they are
+// issued nontemporal (they do not displace reused lines in the caches, and
+// HBM read throughput is measurably higher than with ordinary loads).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+  const u32x4v v = __builtin_nontemporal_load((const u32x4v *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void *p) {
+  const u32x2v v = __builtin_nontemporal_load((const u32x2v *)p);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const void *p) {
+  return __builtin_nontemporal_load((const uint32_t *)p);
+}
+
 // uniform quantizer of one value (see the codec definition): code of x in a
 // group with float16 step s16 and zero z16
 __device__ inline uint32_t quant_code(float x, half_t s16, half_t z16, float levels) {

@@ -275,9 +275,9 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   for (int s = 0; s < 2; ++s) {
     const uint16_t *kt = ftile_ptr<D>(c, cur, s);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[s][kb] = *(const uint4 *)(kt + (kb * 64 + c.lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) kr[s][kb] = ld_stream16(kt + (kb * 64 + c.lane) * 8);
 #pragma unroll
-    for (int cp = 0; cp < CP; ++cp) vr[s][cp] = *(const uint4 *)(kt + TS * D + (cp * 64 + c.lane) * 8);
+    for (int cp = 0; cp < CP; ++cp) vr[s][cp] = ld_stream16(kt + TS * D + (cp * 64 + c.lane) * 8);
   }
   for (int i = 0; i < n_blocks; ++i) {
     // unit ids two blocks ahead; the next block's tiles (the last block re-reads itself)
@@ -292,7 +292,7 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
     for (int t = 0; t < 2; ++t) {
       const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(kn + (kb * 64 + c.lane) * 8);
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(kn + (kb * 64 + c.lane) * 8);
     }
     const int lo[2] = {0, 0};
     const int hi[2] = {c.has_q ? cur.nv[0] : 0, c.has_q ? cur.nv[1] : 0};
@@ -325,7 +325,7 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
     for (int t = 0; t < 2; ++t) {
       const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
 #pragma unroll
-      for (int cp = 0; cp < CP; ++cp) vr[t][cp] = *(const uint4 *)(kn + TS * D + (cp * 64 + c.lane) * 8);
+      for (int cp = 0; cp < CP; ++cp) vr[t][cp] = ld_stream16(kn + TS * D + (cp * 64 + c.lane) * 8);
     }
     cur = nxt;
     ids_b = ids_c;
@@ -382,15 +382,15 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, uw, c.h);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
     if (NKD == 2) {
-      buf.code[j] = *(const uint4 *)(T + c.lane * 16);
+      buf.code[j] = ld_stream16(T + c.lane * 16);
     } else {
-      const uint2 cw = *(const uint2 *)(T + c.lane * 8);
+      const uint2 cw = ld_stream8(T + c.lane * 8);
       buf.code[j] = make_uint4(cw.x, cw.y, 0u, 0u);
     }
-    buf.vp[j] = ((const uint32_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes))[vl];
+    buf.vp[j] = ld_stream4(T + g.tile_kcode_bytes + g.tile_vcode_bytes + 4 * vl);
   }
 #pragma unroll
-  for (int w = 0; w < QT; ++w) buf.kp[w] = *(const uint2 *)(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
+  for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
 }
 
 template <int D>
