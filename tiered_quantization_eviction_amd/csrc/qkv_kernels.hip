@@ -119,6 +119,7 @@ struct Ctx {
   const uint16_t *qbase;  // query rows of the KV head's G heads
   int b, h, lane, col, lq, G, hc;
   bool is_hi, is_lo, has_q;
+  int slot;               // channel-group slot of this lane's A row in the paired value product
   float scale_log2;
   float *mass_row;        // [(U+1)][G][2] of this (sequence, KV head); slot U is the spare
   half_t *kp_lds;
@@ -393,7 +394,7 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
   for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
 }
 
-template <int D>
+template <int D, int GP>
 __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&qc)[2],
                                               const half8 (&bz)[D / 32], float sc_quant, const float (&row_bias)[4],
                                               const QBlock &qb, const QBuf &buf) {
@@ -511,21 +512,26 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     P1[j] = __builtin_bit_cast(half4, make_uint2(ph.x & lo_keep, ph.y & lo_keep));
     P2[j] = __builtin_bit_cast(half4, make_uint2(c.is_lo ? pl.x : ph.x, c.is_lo ? pl.y : ph.y));
   }
-  // PV over tile pairs: k slots = tokens 4*lq..+3 of tile 2pp, then of tile 2pp+1
+  // PV over tile pairs: k slots = tokens 4*lq..+3 of tile 2pp, then of tile
+  // 2pp+1.  The A operand scales p by the value step of one channel group;
+  // with GP = 2 (four heads, each in two columns per limb) rows slot*G + h
+  // take group gb + slot, so one operand serves two groups and each group's
+  // MFMAs use its own rows.
 #pragma unroll
   for (int pp = 0; pp < QT / 2; ++pp) {
     const int j0 = 2 * pp, j1 = 2 * pp + 1;
 #pragma unroll
-    for (int grp = 0; grp < NG; ++grp) {
-      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + grp) * 8);
-      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + grp) * 8);
+    for (int gb = 0; gb < NG; gb += GP) {
+      const int grp_l = gb + (GP == 1 ? 0 : c.slot);
+      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + grp_l) * 8);
+      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + grp_l) * 8);
       const half4 t0 = P1[j0] * s40, t1 = P1[j1] * s41;
       const half4 ag0 = __builtin_elementwise_fma(P2[j0], s40, __builtin_elementwise_fma(P1[j0], s40, -t0));
       const half4 ag1 = __builtin_elementwise_fma(P2[j1], s41, __builtin_elementwise_fma(P1[j1], s41, -t1));
       const half8 ag = __builtin_shufflevector(ag0, ag1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int ct = grp * 2 + c2;
+      for (int c2 = 0; c2 < 2 * GP; ++c2) {
+        const int ct = gb * 2 + c2;
         const uint32_t v0 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j0].z : buf.code[j0].y)
                                            : buf.code[j0].w;
         const uint32_t v1 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j1].z : buf.code[j1].y)
@@ -550,7 +556,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   wave_lds_sync();
 }
 
-template <int D>
+template <int D, int GP>
 __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
   half8 qc[2], bz[D / 32];
@@ -574,12 +580,12 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
     const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 1, n_blocks - 1), ids1, k1);
     quant_load<D>(c, k1, b1);
-    quant_compute<D>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
     if (i + 1 >= n_blocks) break;
     ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
     qblock_make(c, ea, eb, min(i + 2, n_blocks - 1), ids2, k0);
     quant_load<D>(c, k0, b0);
-    quant_compute<D>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
     if (i + 2 >= n_blocks) break;
   }
 }
@@ -588,7 +594,7 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
 // holds two waves on each SIMD.
 constexpr int QW = 8;
 
-template <int D>
+template <int D, int GP>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
@@ -604,9 +610,13 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int col = lane & 15;
   const int lq = lane >> 4;
   const int G = g.G;
-  const bool is_hi = col < G;                   // column h: head h (high limb of quantized-tile scores)
-  const bool is_lo = col >= 8 && col < 8 + G;   // column 8+h: head h again (low limb)
-  const int hc = is_hi ? col : (is_lo ? col - 8 : 0);
+  // Columns 0..7 take the high limb of quantized-tile scores, 8..15 the low
+  // limb; within each half column c serves head (c mod 8) mod G, so with
+  // fewer than 8 heads every head appears in several columns (identical
+  // values) and no lane idles.
+  const bool is_hi = col < 8;
+  const bool is_lo = col >= 8;
+  const int hc = (col & 7) & (G - 1);
 
   __shared__ __attribute__((aligned(16))) half_t s_kp[QW][QT][PSTR<D>];   // key scale/zero per window
   __shared__ __attribute__((aligned(16))) half_t s_vp[QW][QT][PSTR<D>];   // value params per tile
@@ -633,7 +643,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
   ws.zacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  ws.m = (is_hi || is_lo) ? neg_inf() : 0.0f;   // columns without a head keep a finite reference
+  ws.m = neg_inf();
   ws.l = 0.0f;
 
   float *mass_row = st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1)) * G * 2;
@@ -656,7 +666,8 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   c.G = G;
   c.is_hi = is_hi;
   c.is_lo = is_lo;
-  c.has_q = is_hi || is_lo;
+  c.has_q = true;
+  c.slot = min((col & 7) / G, GP - 1);
   c.scale_log2 = scale_log2;
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
@@ -667,13 +678,13 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // pairs (2k, 2k+1): one streams full-precision tiles while the other
   // unpacks quantized ones.
   if (((wave & 1) ^ (wave >> 2)) & 1) {
-    run_quant<D>(ws, c, q0, q1);
+    run_quant<D, GP>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
     run_full<D>(ws, c, r0e, r1e);    // windows not yet ranked
   } else {
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
-    run_quant<D>(ws, c, q0, q1);
+    run_quant<D, GP>(ws, c, q0, q1);
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -693,12 +704,15 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     sm_m[wave][col] = ws.m;
     sm_l[wave][col] = l_tot;
   }
+  // row r < 8 holds head r mod G; a channel tile's values are read from the
+  // rows of its group's slot (r / G == group mod GP)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * lq + i;
-    if (r < G) {
+    if (r < 8) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) sm_o[wave][r][ct * 16 + col] = ws.acc[ct][i];
+      for (int ct = 0; ct < CT; ++ct)
+        if (r / G == ((ct >> 1) % GP)) sm_o[wave][r & (G - 1)][ct * 16 + col] = ws.acc[ct][i];
     }
   }
   __syncthreads();
@@ -841,10 +855,16 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
   const int grid = g.B * g.Hkv * g.n_splits;
   if (ev_start) hipEventRecord(ev_start, s);
   const size_t qs_bytes = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
-  if (g.d == 128)
-    hipLaunchKernelGGL(attend_qevict_kernel<128>, dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+  // four heads per KV head: value operands shared by channel-group pairs
+  const bool pair = g.G == 4;
+  if (g.d == 128 && pair)
+    hipLaunchKernelGGL((attend_qevict_kernel<128, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+  else if (g.d == 128)
+    hipLaunchKernelGGL((attend_qevict_kernel<128, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+  else if (pair)
+    hipLaunchKernelGGL((attend_qevict_kernel<64, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
   else
-    hipLaunchKernelGGL(attend_qevict_kernel<64>, dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+    hipLaunchKernelGGL((attend_qevict_kernel<64, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_stop) hipEventRecord(ev_stop, s);
