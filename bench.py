@@ -308,7 +308,7 @@ def main():
         "kv_read_pct_hbm_peak": 100.0 * kv_bytes / wall / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "attend_qevict_kernel<128>",
+                     "kernel": "attend_qevict_kernel<128, 2>",
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": att_avg_s * 1e6,
                      "timed_launches": f"{len(attend_ms)} of {steps} (every {PROFILE_STRIDE}th step)"},

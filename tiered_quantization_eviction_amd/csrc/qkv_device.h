@@ -71,6 +71,7 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p) {
   const u32x4v v = __builtin_nontemporal_load((const u32x4v *)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ u32x4v ld_stream16v(const void *p) { return __builtin_nontemporal_load((const u32x4v *)p); }
 __device__ __forceinline__ uint2 ld_stream8(const void *p) {
   const u32x2v v = __builtin_nontemporal_load((const u32x2v *)p);
   return make_uint2(v.x, v.y);

@@ -258,6 +258,67 @@ __device__ __forceinline__ const uint16_t *ftile_ptr(const Ctx &c, const FBlock 
   return c.st->pages + page_offset(*c.g, c.b, fb.u[s], c.h) + (size_t)fb.tile[s] * 2 * TS * D;
 }
 
+// Attend over block `cur` (tiles in kr, vr); with PF the tiles of block
+// `nxt` are loaded into kr and vr as soon as each has been consumed.
+template <int D, bool PF>
+__device__ __forceinline__ void full_step(WaveState<D> &ws, const Ctx &c, const bf16x8 (&bq)[D / 32],
+                                          const FBlock &cur, const FBlock &nxt, u32x4v (&kr)[2][D / 32],
+                                          u32x4v (&vr)[2][D / 32]) {
+  constexpr int KB = D / 32, CP = D / 32;
+  const int tpw = c.g->tpw;
+  floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
+  if (PF) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16v(kn + (kb * 64 + c.lane) * 8);
+    }
+  }
+  const int lo[2] = {0, 0};
+  const int hi[2] = {c.has_q ? cur.nv[0] : 0, c.has_q ? cur.nv[1] : 0};
+  float p[2][4], ts[2];
+  softmax_block<D, 2>(ws, s, c.scale_log2, lo, hi, c.lq, p, ts);
+  {
+    // tpw == 1: each slot is a unit; tpw == 2: the block is one unit
+    const int e[2] = {cur.e[0], cur.e[1]};
+    const bool ok[2] = {true, tpw == 1 && cur.nv[1] > 0};
+    const float rho[2] = {tpw == 1 ? ts[0] : ts[0] + ts[1], ts[1]};
+    store_mass<2>(c, e, ok, rho, ws.m);
+  }
+  // rows h carry bf16(p), rows G+h carry bf16(p - bf16(p))
+  bf16x8 ap;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const float hi = (float)(__bf16)p[t][i2];
+      ap[t * 4 + i2] = (__bf16)(c.is_lo ? p[t][i2] - hi : p[t][i2]);
+    }
+#pragma unroll
+  for (int cp = 0; cp < CP; ++cp) {
+    const u32x4v v0 = __builtin_shufflevector(vr[0][cp], vr[1][cp], 0, 1, 4, 5);
+    const u32x4v v1 = __builtin_shufflevector(vr[0][cp], vr[1][cp], 2, 3, 6, 7);
+    ws.acc[2 * cp] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * cp]);
+    ws.acc[2 * cp + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * cp + 1]);
+  }
+  if (PF) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
+#pragma unroll
+      for (int cp = 0; cp < CP; ++cp) vr[t][cp] = ld_stream16v(kn + TS * D + (cp * 64 + c.lane) * 8);
+    }
+  }
+}
+
+// Run of full-precision entries [ea, eb), two tiles per block; the next
+// block is in flight while one computes, and the last block is peeled off so
+// that nothing past the run is read.
 template <int D>
 __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
@@ -271,66 +332,24 @@ __device__ void run_full(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   int ids_b = ids_fetch(c, ea + (2 * min(1, n_blocks - 1)) / tpw);
   FBlock cur, nxt;
   fblock_make(c, ea, n_tiles, 0, ids_a, cur);
-  uint4 kr[2][KB], vr[2][CP];
+  u32x4v kr[2][KB], vr[2][CP];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const uint16_t *kt = ftile_ptr<D>(c, cur, s);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[s][kb] = ld_stream16(kt + (kb * 64 + c.lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) kr[s][kb] = ld_stream16v(kt + (kb * 64 + c.lane) * 8);
 #pragma unroll
-    for (int cp = 0; cp < CP; ++cp) vr[s][cp] = ld_stream16(kt + TS * D + (cp * 64 + c.lane) * 8);
+    for (int cp = 0; cp < CP; ++cp) vr[s][cp] = ld_stream16v(kt + TS * D + (cp * 64 + c.lane) * 8);
   }
-  for (int i = 0; i < n_blocks; ++i) {
-    // unit ids two blocks ahead; the next block's tiles (the last block re-reads itself)
+  for (int i = 0; i + 1 < n_blocks; ++i) {
+    // unit ids two blocks ahead (clamped), the next block's tiles
     const int ids_c = ids_fetch(c, ea + (2 * min(i + 2, n_blocks - 1)) / tpw);
-    fblock_make(c, ea, n_tiles, min(i + 1, n_blocks - 1), ids_b, nxt);
-    floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s[t] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, kr[t][kb]), bq[kb], s[t]);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(kn + (kb * 64 + c.lane) * 8);
-    }
-    const int lo[2] = {0, 0};
-    const int hi[2] = {c.has_q ? cur.nv[0] : 0, c.has_q ? cur.nv[1] : 0};
-    float p[2][4], ts[2];
-    softmax_block<D, 2>(ws, s, c.scale_log2, lo, hi, c.lq, p, ts);
-    {
-      // tpw == 1: each slot is a unit; tpw == 2: the block is one unit
-      const int e[2] = {cur.e[0], cur.e[1]};
-      const bool ok[2] = {true, tpw == 1 && cur.nv[1] > 0};
-      const float rho[2] = {tpw == 1 ? ts[0] : ts[0] + ts[1], ts[1]};
-      store_mass<2>(c, e, ok, rho, ws.m);
-    }
-    // rows h carry bf16(p), rows G+h carry bf16(p - bf16(p))
-    bf16x8 ap;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const float hi = (float)(__bf16)p[t][i2];
-        ap[t * 4 + i2] = (__bf16)(c.is_lo ? p[t][i2] - hi : p[t][i2]);
-      }
-#pragma unroll
-    for (int cp = 0; cp < CP; ++cp) {
-      const uint4 v0 = make_uint4(vr[0][cp].x, vr[0][cp].y, vr[1][cp].x, vr[1][cp].y);
-      const uint4 v1 = make_uint4(vr[0][cp].z, vr[0][cp].w, vr[1][cp].z, vr[1][cp].w);
-      ws.acc[2 * cp] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * cp]);
-      ws.acc[2 * cp + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * cp + 1]);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t *kn = ftile_ptr<D>(c, nxt, t);
-#pragma unroll
-      for (int cp = 0; cp < CP; ++cp) vr[t][cp] = ld_stream16(kn + TS * D + (cp * 64 + c.lane) * 8);
-    }
+    fblock_make(c, ea, n_tiles, i + 1, ids_b, nxt);
+    full_step<D, true>(ws, c, bq, cur, nxt, kr, vr);
     cur = nxt;
     ids_b = ids_c;
   }
+  full_step<D, false>(ws, c, bq, cur, cur, kr, vr);
 }
 
 // ---- runs of quantized windows, QT tiles per block; the next block is in
@@ -568,25 +587,34 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   const int per = QT / c.g->tpw;
   const int n_blocks = (eb - ea + per - 1) / per;
   // two-slot ring: one block in flight while one computes; unit ids two
-  // blocks ahead; past the end the last block is re-read, so every step
-  // issues the same loads
+  // blocks ahead (clamped, always valid); the loop body issues the same
+  // loads on every trip, and the tail reads nothing past the run
   QBlock k0, k1;
   QBuf b0, b1;
   const int ids0 = ids_fetch(c, ea);
   int ids1 = ids_fetch(c, ea + min(1, n_blocks - 1) * per);
   qblock_make(c, ea, eb, 0, ids0, k0);
   quant_load<D>(c, k0, b0);
-  for (int i = 0;; i += 2) {
+  // steady state: two blocks per trip, the following block always in flight
+  int i = 0;
+  for (; i + 2 < n_blocks; i += 2) {
     const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
-    qblock_make(c, ea, eb, min(i + 1, n_blocks - 1), ids1, k1);
+    qblock_make(c, ea, eb, i + 1, ids1, k1);
     quant_load<D>(c, k1, b1);
     quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
-    if (i + 1 >= n_blocks) break;
     ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
-    qblock_make(c, ea, eb, min(i + 2, n_blocks - 1), ids2, k0);
+    qblock_make(c, ea, eb, i + 2, ids2, k0);
     quant_load<D>(c, k0, b0);
     quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
-    if (i + 2 >= n_blocks) break;
+  }
+  // the last one or two blocks: nothing past the run is read
+  if (i + 1 < n_blocks) {
+    qblock_make(c, ea, eb, i + 1, ids1, k1);
+    quant_load<D>(c, k1, b1);
+    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+  } else {
+    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
   }
 }
 
