@@ -285,7 +285,8 @@ int qkv_profile_start(qkv_cache *c, int32_t n, int32_t stride) {
   c->ev = new (std::nothrow) hipEvent_t[2 * n];
   if (!c->ev) return QKV_ECAPACITY;
   for (int i = 0; i < 2 * n; ++i) {
-    if (hipEventCreate(&c->ev[i]) != hipSuccess) {
+    // timing only: no system-scope fence (cache writeback) when recorded
+    if (hipEventCreateWithFlags(&c->ev[i], hipEventDisableSystemFence) != hipSuccess) {
       for (int j = 0; j < i; ++j) hipEventDestroy(c->ev[j]);
       delete[] c->ev;
       c->ev = nullptr;

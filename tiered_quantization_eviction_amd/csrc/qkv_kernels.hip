@@ -12,6 +12,8 @@
 // per unit, the head's partial mass with the reference maximum it is relative
 // to; the merge kernel normalizes those with the global (max, sum) and adds
 // them into the window scores (QEvict Eq.(1)) in a fixed order (no atomics).
+#include <hip/hip_ext.h>
+
 #include "qkv_device.h"
 
 namespace qkv {
@@ -881,21 +883,25 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
                          float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
-  if (ev_start) hipEventRecord(ev_start, s);
   const size_t qs_bytes = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
-  // four heads per KV head: value operands shared by channel-group pairs
+  // four heads per KV head: value operands shared by channel-group pairs.
+  // The optional events are attached to the dispatch itself, so they time
+  // the kernel's execution (no launch gap).
   const bool pair = g.G == 4;
   if (g.d == 128 && pair)
-    hipLaunchKernelGGL((attend_qevict_kernel<128, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+    hipExtLaunchKernelGGL((attend_qevict_kernel<128, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
+                          g, st, si, q, scale_log2);
   else if (g.d == 128)
-    hipLaunchKernelGGL((attend_qevict_kernel<128, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+    hipExtLaunchKernelGGL((attend_qevict_kernel<128, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
+                          g, st, si, q, scale_log2);
   else if (pair)
-    hipLaunchKernelGGL((attend_qevict_kernel<64, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+    hipExtLaunchKernelGGL((attend_qevict_kernel<64, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
+                          g, st, si, q, scale_log2);
   else
-    hipLaunchKernelGGL((attend_qevict_kernel<64, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, g, st, si, q, scale_log2);
+    hipExtLaunchKernelGGL((attend_qevict_kernel<64, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
+                          g, st, si, q, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev_stop) hipEventRecord(ev_stop, s);
   if (mass_out) {
     e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.U * sizeof(float), s);
     if (e != hipSuccess) return e;

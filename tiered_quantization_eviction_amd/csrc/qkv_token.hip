@@ -23,6 +23,8 @@
 // bits.  Each token slot's probability is emitted relative to the running
 // maximum; the merge kernel normalizes those with the global (max, sum) of
 // each head and adds them into the per-token scores in a fixed order.
+#include <hip/hip_ext.h>
+
 #include "qkv_device.h"
 
 namespace qkv {
@@ -701,13 +703,14 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
   hipError_t e;
-  if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
+  // the optional events are attached to the dispatch (kernel execution time)
   if (g.d == 128)
-    hipLaunchKernelGGL(tok_attend_kernel<128>, dim3(grid), dim3(256), 0, s, g, st, ts, q, q_bstride, scale_log2);
+    hipExtLaunchKernelGGL(tok_attend_kernel<128>, dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts, q,
+                          q_bstride, scale_log2);
   else
-    hipLaunchKernelGGL(tok_attend_kernel<64>, dim3(grid), dim3(256), 0, s, g, st, ts, q, q_bstride, scale_log2);
+    hipExtLaunchKernelGGL(tok_attend_kernel<64>, dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts, q,
+                          q_bstride, scale_log2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
   if (mass_out && (e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.T * sizeof(float), s)) != hipSuccess) return e;
   // live tiles per (sequence, KV head): at most the ranked tokens' tiles
   // (one partial tile per tier) plus the sink and recent tiles
