@@ -14,6 +14,13 @@ routing event); W warm-up steps run first on a separate cache.
 
 Prints one JSON line.  --gpus N with N > 1 is refused: this build measures
 one GPU.
+
+--workload selects another layer of the same path (the default is the one
+above): `stress` (QEvict, batch 32, 128K prompt, G = 8, 32-token windows),
+`hqekv` (five-tier per-token assignment, batch 8, 64K prompt), `h2o`
+(per-token heavy hitters, batch 1, 512-token scored prompt) or `tiny`.  Their
+lines carry the same fields; the oracle baseline is taken on the default
+workload only.
 """
 from __future__ import annotations
 
@@ -43,6 +50,28 @@ PROFILE_STRIDE = 8
 KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
                for f in ("qkv_kernels.hip", "qkv_device.h", "qkv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
+
+
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.STRESS, W.HQEKV, W.H2O, W.TINY)}
+DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
+          W.POLICY_H2O: "bf16 (fp32 accumulate)",
+          W.POLICY_HQEKV: "bf16+int4+int2+int1 (fp32 accumulate)"}
+
+
+def describe(cfg, steps):
+    head = (f"batch {cfg.batch}, {cfg.prefill}-token prompt + {steps} decode steps, "
+            f"Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim}")
+    if cfg.name == "drift":
+        return ("QEvict three-tier attention drift: " + head + ", window=Omega=16, 5 sinks + 64 recent, "
+                "Kf=204 BF16 + Kq=612 INT2 windows (group 32), clusters A->B switch at step 100")
+    if cfg.policy == W.POLICY_QEVICT:
+        return (f"QEvict three-tier ({cfg.name}): " + head + f", window={cfg.window} Omega={cfg.omega}, "
+                f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} INT2 windows")
+    if cfg.policy == W.POLICY_H2O:
+        return (f"H2O heavy hitters: " + head + f", scored prompt, {cfg.n_sink} sinks + {cfg.k_full} heavy + "
+                f"{cfg.n_recent} recent tokens per KV head, eviction every step")
+    return (f"HqeKV five-tier: " + head + f", shares {'/'.join(str(r) for r in cfg.ratios)} "
+            f"BF16/INT4/INT2/INT1/evicted by attention x value range, events every {cfg.omega} steps")
 
 
 def log(msg):
@@ -167,6 +196,102 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
     return (t1 - t0), attend_ms, [f[0].cpu().numpy() for f in firsts], splits, status
 
 
+# token modes (H2O, HqeKV): every token is a unit, decisions per (sequence, KV head)
+T_SINK, T_RECENT, T_FULL, T_QUANT, T_EVICTED, T_INT4, T_INT1 = 1, 2, 3, 4, 5, 6, 7
+
+
+def token_bytes_per_token(cfg):
+    """Bytes one live token of each tier costs per KV head: bf16 K and V;
+    per-token records of codes plus (scale, zero) per 32 channels, or INT1's
+    (mean, std), for K and V."""
+    d = cfg.head_dim
+    return {T_SINK: 4 * d, T_RECENT: 4 * d, T_FULL: 4 * d,
+            T_INT4: d + 2 * (d // 32) * 4, T_QUANT: d // 2 + 2 * (d // 32) * 4, T_INT1: d // 4 + 2 * 4}
+
+
+def prompt_queries(cfg, wl, b):
+    """Prompt queries that score the prompt: every position (H2O) or the last
+    init_queries positions (HqeKV)."""
+    P = cfg.prefill
+    m = P if cfg.policy == W.POLICY_H2O else cfg.init_queries
+    return wl.prefill_queries(b, P - m, P)
+
+
+def run_gpu_tok(cfg, K, V, Q, QP, steps, n_splits):
+    """Prompt appended, scored and routed before timing; then `steps` decode
+    steps (append, attend, route every omega steps) timed.  An untimed pass
+    over the same calls on its own cache records the tier histogram after
+    every routing call, from which the bytes each attention launch reads are
+    counted."""
+    import torch
+    from tiered_quantization_eviction_amd import Cache, make_config
+    P = cfg.prefill
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    k_pre, v_pre = dev(K[:, :, :P]), dev(V[:, :, :P])
+    k_dec = dev(np.ascontiguousarray(K[:, :, P:].transpose(2, 0, 1, 3))[:, :, :, None, :])
+    v_dec = dev(np.ascontiguousarray(V[:, :, P:].transpose(2, 0, 1, 3))[:, :, :, None, :])
+    q_dec = dev(np.ascontiguousarray(Q.transpose(1, 0, 2, 3)))
+    qp = dev(QP)
+    out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    conf = make_config(cfg, n_splits=n_splits)
+    T = cfg.total_tokens
+
+    def start(cache):
+        cache.append(k_pre, v_pre)
+        cache.prefill_score(qp)
+        cache.route()
+
+    def loop(cache, n, on_route=None):
+        for s in range(n):
+            cache.append(k_dec[s], v_dec[s])
+            cache.decode_attend(q_dec[s], out)
+            if (s + 1) % cfg.omega == 0:
+                cache.route()
+                if on_route is not None:
+                    on_route(s)
+
+    def hist(cache):
+        t = cache.export("tiers").cpu().numpy().reshape(cfg.batch * cfg.n_kv_heads, T)
+        return {code: int((t == code).sum()) for code in (T_SINK, T_RECENT, T_FULL, T_INT4, T_QUANT, T_INT1)}
+
+    # counting pass: live tokens per tier before each attention launch
+    cc = Cache(conf)
+    start(cc)
+    per_tok = token_bytes_per_token(cfg)
+    state = {"h": hist(cc), "since": 0}
+    launch_bytes = []
+
+    def on_route(s):
+        state["h"] = hist(cc)
+        state["since"] = 0
+
+    for s in range(steps):
+        cc.append(k_dec[s], v_dec[s])
+        state["since"] += 1
+        kv = sum(n * per_tok[code] for code, n in state["h"].items())
+        kv += cfg.batch * cfg.n_kv_heads * state["since"] * per_tok[T_RECENT]   # appended since the last route
+        launch_bytes.append(kv + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2)
+        cc.decode_attend(q_dec[s], out)
+        if (s + 1) % cfg.omega == 0:
+            cc.route()
+            on_route(s)
+    torch.cuda.synchronize()
+    cc.close()
+    del cc
+
+    cache = Cache(conf)
+    start(cache)
+    n_prof = (steps + PROFILE_STRIDE - 1) // PROFILE_STRIDE
+    cache.profile_start(n_prof, PROFILE_STRIDE)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop(cache, steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attend_ms = cache.profile_read(n_prof)
+    return (t1 - t0), attend_ms, launch_bytes, cache.info("splits"), cache.status()
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
@@ -243,6 +368,7 @@ def copy_probe(mib):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="drift", choices=sorted(WORKLOADS))
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--splits", type=int, default=0)
@@ -259,17 +385,24 @@ def main():
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
               f"(the multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
         sys.exit(2)
-    cfg = W.DRIFT
+    cfg = WORKLOADS[a.workload]
     steps = min(a.steps, cfg.steps)
+    token_mode = cfg.policy != W.POLICY_QEVICT
     log(f"bench: generating inputs ({cfg.batch} x {cfg.total_tokens} tokens)")
     t = time.perf_counter()
     K, V, Q = make_inputs(cfg)
-    log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running {a.warmup} warm-up + {steps} timed steps")
-    wall, attend_ms, firsts, splits, status = run_gpu(cfg, K, V, Q, steps, a.warmup, a.splits)
+    log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running "
+        f"{'a counting pass' if token_mode else f'{a.warmup} warm-up'} + {steps} timed steps")
+    firsts = []
+    if token_mode:
+        wl = W.Workload(cfg)
+        QP = np.stack([prompt_queries(cfg, wl, b) for b in range(cfg.batch)])
+        wall, attend_ms, abytes, splits, status = run_gpu_tok(cfg, K, V, Q, QP, steps, a.splits)
+    else:
+        wall, attend_ms, firsts, splits, status = run_gpu(cfg, K, V, Q, steps, a.warmup, a.splits)
+        abytes = attend_bytes(cfg, live_schedule(cfg, steps))
     if status != 0:
         log(f"bench: device status {status}")
-    sched = live_schedule(cfg, steps)
-    abytes = attend_bytes(cfg, sched)
     kv_bytes = sum(abytes)
     tok_s = cfg.batch * steps / wall
     sampled = abytes[::PROFILE_STRIDE][:len(attend_ms)]          # the launches that were timed
@@ -277,38 +410,38 @@ def main():
     bytes_per_launch = float(np.mean(sampled))
     achieved = bytes_per_launch / att_avg_s / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_traffic(src_hash)
+    traffic = read_traffic(src_hash) if a.workload == "drift" else None
     log(f"bench: {wall * 1e3:.1f} ms for {steps} steps; attention avg {att_avg_s * 1e6:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
     cpu = None
     worst = None
-    if not a.no_cpu:
+    if not a.no_cpu and a.workload == "drift":
         n_cpu = min(a.cpu_steps, cfg.steps)
         log(f"bench: oracle baseline on {n_cpu} steps of {a.cpu_seqs} sequences")
         cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_seqs, n_cpu, firsts)
+    kernel = ("tok_attend_kernel<%d>" % cfg.head_dim if token_mode else
+              "attend_qevict_kernel<%d, %d>" % (cfg.head_dim, 2 if cfg.group_size == 4 else 1))
     res = {
-        "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer",
+        "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer"
+                  if a.workload == "drift" else "decode tokens/s + KV-read GB/s (% of HBM peak), 1 layer",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": a.warmup,
+        "warmup": 0 if token_mode else a.warmup,
         "ms_per_step": wall * 1e3 / steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+int2 (fp32 accumulate)",
+        "dtype": DTYPES[cfg.policy],
         "data": "synthetic",
-        "config": {"workload": "QEvict three-tier attention drift: batch 16, 32768-token prompt + 512 decode steps, "
-                               "Hq=32 Hkv=8 d=128, window=Omega=16, 5 sinks + 64 recent, Kf=204 BF16 + Kq=612 INT2 "
-                               "windows (group 32), clusters A->B switch at step 100",
-                   "global_batch": cfg.batch, "seq_len": cfg.total_tokens, "parallelism": "single GPU",
-                   "attention_splits": splits},
+        "config": {"workload": describe(cfg, steps), "global_batch": cfg.batch, "seq_len": cfg.total_tokens,
+                   "parallelism": "single GPU", "attention_splits": splits},
         "kv_read_GBps": kv_bytes / wall / 1e9,
         "kv_read_pct_hbm_peak": 100.0 * kv_bytes / wall / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "attend_qevict_kernel<128, 2>",
+                     "kernel": kernel,
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": att_avg_s * 1e6,
                      "timed_launches": f"{len(attend_ms)} of {steps} (every {PROFILE_STRIDE}th step)"},
