@@ -109,8 +109,16 @@ int qkv_destroy(qkv_cache *cache);
  *   summed over the G query heads of that KV head; k_full is the heavy-hitter
  *   budget B_h, n_recent the recent budget B_r, n_sink protected sinks; call
  *   qkv_route after every decode step (omega = 1) to evict down to the budget.
- *   The scored prompt (section 3.3): append it, qkv_prefill_score with its
+ *   The scored prompt (section 1.2, each position accumulates from its own
+ *   causal row): append it, qkv_prefill_score with its
  *   queries, then one qkv_route trims it.  max_ctx <= 8192.
+ * QKV_POLICY_HQEKV (HqeKV notes, sections 3.2-3.5 and 3.8): token units
+ *   (window = 1, n_sink = 0), one score per (sequence, KV head, token) summed
+ *   over the G query heads; ratios[0..4] are the shares of full precision,
+ *   INT4, INT2, INT1 (normalized quantizer) and evicted tokens, summing to 1;
+ *   omega is the assignment period in decode steps.  The prompt: append it,
+ *   qkv_prefill_score with its last 20 queries (section 3.10, m = 20), then
+ *   qkv_route makes the first assignment.
  */
 
 /*
@@ -153,10 +161,22 @@ int qkv_route(qkv_cache *cache, qkv_stream stream);
 /* H2O: the same call is the per-step eviction: tokens older than the newest
  * n_recent join the kept older tokens, and of those the k_full best by
  * (score descending, position descending) stay, the rest are evicted for
- * good (H2O notes section 2.1; the tie rule is this library's reading). */
+ * good (H2O notes section 2.1; the tie rule is this library's reading).
+ * HqeKV: the same call is an assignment event (HqeKV notes sections 3.2, 3.3
+ * and 3.5): the tokens appended before the previous event (all tokens at the
+ * first event) are ordered by accumulated score times the value range of
+ * their original value row (max - min over head_dim), float32, descending,
+ * ties to the later position; the first floor(ratios[k] * N) of them (N =
+ * tokens appended so far, shares taken as float32) target tier k in the
+ * order full precision, INT4, INT2, INT1, and the rest are evicted.  A
+ * token's tier only moves down (new = max(old, target)); a token that moves
+ * to a quantized tier is re-quantized from its current values, keys and
+ * values per token in groups of 32 channels with float16 scale and zero
+ * (INT4, INT2) or as signs around the row mean with float16 mean and
+ * standard deviation (INT1). */
 
 /*
- * Scored prompt (H2O notes section 3.3): the queries of the last n_queries
+ * Scored prompt (H2O notes section 1.2; HqeKV notes sections 3.8 and 3.10): the queries of the last n_queries
  * appended positions, each attending causally to the live tokens at or before
  * its own position, add their weights (summed over each KV head's query
  * heads, each below FLT_MIN counting as 0) to the token scores; no output.

@@ -15,10 +15,11 @@ H2O page:
 * "multi-head and GQA" paragraph and section 5 kernel notes -- with grouped
   query attention the weights of the query heads of one KV group are summed
   into one score per KV head; victims are chosen per (request, KV head).
-* section 3.3 -- prefill: either score the full prompt and trim once, or
-  stream; the choice must be stated.  Reading: the prompt is scored token by
-  token (query t attends to positions <= t, no eviction), then trimmed once to
-  sinks + newest B_r + best B_h.
+* prefill: the page leaves open how the prompt enters the budget; from
+  section 1.2 (a position accumulates from its own causal row on) the reading
+  here is that the prompt is scored token by token (query t attends to
+  positions <= t, no eviction), then trimmed once to sinks + newest B_r +
+  best B_h.
 
 Sinks (a protected prefix, as in StreamingLLM and the QEvict setup) are never
 evicted.  Victim order: lowest score, ties to the oldest position (the

@@ -1,8 +1,8 @@
 """The ranking order shared by every router (oracle side).
 
 QEvict Eq.(5) ranks candidates by accumulated score, highest first; the H2O
-page (section 3.3, "sort-free two budgets"; section 5 test advice) asks for a
-fixed tie rule keyed on the original position.  Reading (the pages give the
+page (section 5.1, small-shape correctness) asks for a fixed tie rule keyed
+on the original position.  Reading (the pages give the
 key but not its direction): one total order everywhere -- score descending,
 then start position descending, so among equal scores the newer unit ranks
 higher.  When scores carry no information this degenerates to recency.
