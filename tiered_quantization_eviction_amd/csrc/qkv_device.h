@@ -53,6 +53,24 @@ __device__ __forceinline__ half2v fp4_pair_sel(uint32_t m, int b) {   // b is a 
 __device__ __forceinline__ uint32_t code_half(uint32_t x, int odd) {   // slots 4k+odd, 4k+odd+2 of each byte
   return (odd ? (x >> 2) : x) & 0x33333333u;
 }
+// 4-bit codes to exact fp16 operands: a code dword is masked to 0x0F0F0F0F
+// (directly, or after a shift by 4), so every byte is 0000cccc, which as an
+// E4M3 FP8 value is cccc * 2^-9 (the subnormal and first normal binade are
+// one linear range); the scaled FP8 conversion with scale 2^9 turns bytes
+// (2w, 2w+1) into the fp16 pair (cccc, cccc) exactly.
+template <bool W>
+__device__ __forceinline__ half2v fp8_pair(uint32_t m) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m, 512.0f, W);
+}
+// the 8 codes of one 4-bit code dword whose code e sits at nibble 2e (e < 4)
+// or 2(e-4)+1 (e >= 4), in order e = 0..7
+__device__ __forceinline__ half8 codes8_int4(uint32_t x) {
+  const uint32_t m0 = x & 0x0F0F0F0Fu, m1 = (x >> 4) & 0x0F0F0F0Fu;
+  const half4 lo = __builtin_shufflevector(fp8_pair<false>(m0), fp8_pair<true>(m0), 0, 1, 2, 3);
+  const half4 hi = __builtin_shufflevector(fp8_pair<false>(m1), fp8_pair<true>(m1), 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // the 8 codes of a masked dword (bytes 0..3) as one half8 operand
 __device__ __forceinline__ half8 codes8(uint32_t m) {
   const half4 lo = __builtin_shufflevector(fp4_pair<0>(m), fp4_pair<1>(m), 0, 1, 2, 3);

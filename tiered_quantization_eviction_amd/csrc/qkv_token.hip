@@ -101,21 +101,30 @@ __global__ __launch_bounds__(256) void tok_append_kernel(TokGeom g, TokState st,
     const int t = pos % TS, c0 = ch * 8;
     const size_t row = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d;
     *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + row + c0);
+    const uint4 vq = *(const uint4 *)(v + row + c0);
+    const uint16_t *vs = (const uint16_t *)&vq;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = v[row + c0 + j];
+    for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = vs[j];
+    const size_t u = ((size_t)b * g.Hkv + h) * g.T + pos;
     if (ch == 0) {
-      const size_t u = ((size_t)b * g.Hkv + h) * g.T + pos;
       st.tier[u] = pos < g.n_sink ? T_SINK : T_RECENT;
       st.score[u] = 0.0f;
-      if (st.vrange) {   // value range over the token's channels (HqeKV section 3.2)
-        float mn = bf16_to_f32(v[row]), mx = mn;
-        for (int c = 1; c < g.d; ++c) {
-          const float x = bf16_to_f32(v[row + c]);
-          mn = fminf(mn, x);
-          mx = fmaxf(mx, x);
-        }
-        st.vrange[u] = mx - mn;
+    }
+    if (st.vrange) {
+      // value range over the token's channels (HqeKV section 3.2): the token's
+      // d/8 chunks are adjacent lanes of one wave (the grid stride is a
+      // multiple of 64 and the chunk count divides 64), reduced by shuffles
+      float mn = bf16_to_f32(vs[0]), mx = mn;
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        mn = fminf(mn, bf16_to_f32(vs[j]));
+        mx = fmaxf(mx, bf16_to_f32(vs[j]));
       }
+      for (int off = 1; off < chunks; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      if (ch == 0) st.vrange[u] = mx - mn;
     }
   }
 }
@@ -194,16 +203,20 @@ struct TokCtx {
   const TokList *L;
   int b, h, bh, lane, col, lq, G;
   bool is_hi, is_lo, has_q;
+  bool mass_lane;         // column col < G: the lane that stores its head's probabilities
+  int slot;               // channel-group slot of this lane's A row in the paired value product
   float *mrho, *mref;
+  uint32_t *lds_par;      // per wave: raw params of a block's two quantized tiles
+  float *lds_ks;          // per wave: their key scales as float32 [2][groups][16]
 };
 
 // per-slot probabilities of a tile (lanes of column h < G hold rows 4*lq..+3)
 // and the running max they are relative to; other lanes write the spare row
 __device__ __forceinline__ void tok_store_mass(const TokCtx &c, int e, const float *p, float m) {
   const int G = c.G, TILES = c.g->TILES;
-  const int er = c.is_hi ? e : TILES;
+  const int er = c.mass_lane ? e : TILES;
   *(float4 *)(c.mrho + ((size_t)er * G + (c.col & (G - 1))) * TS + 4 * c.lq) = make_float4(p[0], p[1], p[2], p[3]);
-  const int em = (c.is_hi && c.lq == 0) ? e : TILES;
+  const int em = (c.mass_lane && c.lq == 0) ? e : TILES;
   c.mref[(size_t)em * G + (c.col & (G - 1))] = m;
 }
 
@@ -305,6 +318,48 @@ struct QTile {
   static constexpr int BYTES = 128 * LB + 32 * PB;
   static constexpr int NW = (LB + 3) / 4;      // code dwords per lane
 };
+
+// INT4 and INT2 compact tiles (F = 0, 1) are laid out in the order the
+// matrix-core operands are built, so that the attention kernel never
+// dequantizes an element:
+//   K codes  [64 lanes][CW dwords]: lane l holds token l%16, channels
+//            kb*32 + 8*(l/16) + e (e < 8) of every k-block kb (ql_kslot)
+//   V codes  [64 lanes][CW dwords]: lane l holds channel ct*16 + l%16 of
+//            every column tile ct, tokens 4*(l/16) + tt (tt < 4) (ql_vslot)
+//   params   K scale [NG][16], K zero [16][NG] (token-major), V scale [NG][16],
+//            V zero [NG][16], fp16, one (scale, zero) per 32-channel group
+// INT2 places codes as the window ledger does (two 2-bit codes per byte
+// nibble pair, unpacked by the FP4 conversion); INT4 puts code e of a k-block
+// at nibble 2e (e < 4) or 2(e-4)+1, and value token tt of column tile ct at
+// nibble 2tt + ct%2 of dword ct/2 (unpacked by the FP8 conversion).
+template <int D, int F>
+struct QL {
+  static constexpr int KB = D / 32, CT = D / 16, NG = D / 32, NKD = D / 64;
+  static constexpr int CW = F == 0 ? KB : NKD;   // code dwords per lane, keys and values alike
+  static constexpr int VC = 256 * CW, PAR = 512 * CW;
+  static constexpr int KS = PAR, KZ = PAR + 32 * NG, VS = PAR + 64 * NG, VZ = PAR + 96 * NG;
+  static constexpr int BYTES = PAR + 128 * NG;
+};
+template <int F>
+__host__ __device__ inline void ql_kslot(int kb, int e, int &dw, int &bit) {
+  if (F == 0) {
+    dw = kb;
+    bit = 4 * (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+  } else {
+    dw = kb >> 1;
+    bit = 2 * (4 * (e >> 1) + (kb & 1) + 2 * (e & 1));
+  }
+}
+template <int F>
+__host__ __device__ inline void ql_vslot(int ct, int tt, int &dw, int &bit) {
+  if (F == 0) {
+    dw = ct >> 1;
+    bit = 4 * (2 * tt + (ct & 1));
+  } else {
+    dw = ct >> 2;
+    bit = 2 * (4 * (ct & 3) + (tt >> 1) + 2 * (tt & 1));
+  }
+}
 
 template <int D, int F>
 struct QBufT {
@@ -454,10 +509,197 @@ __device__ void tok_run_quant(WaveState<D> &ws, const TokCtx &c, const half8 (&b
   }
 }
 
-template <int D>
+// INT4 / INT2 tiles (QL layout), two per block.  Keys: one MFMA per k-block
+// on the exact integer codes against the fp16 query (high columns only), kept
+// per k-block and combined with each token's group scales in float32; the
+// key-zero term sum_g z[t][g] * (sum of q over group g) is one 16x16x16 MFMA
+// whose B operand holds the group sums as two fp16 limbs (high columns, low
+// columns), folded with the rest by one DPP add.  Values: the value step is
+// folded into the probabilities (fp16(p*s) on high rows, the exact remainder
+// on low rows), against the exact integer codes; the value-zero term is one
+// MFMA per block.
+template <int D, int F, int GP>
+__device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], half4 bQ, float sc,
+                           int ea, int eb) {
+  if (ea >= eb) return;
+  using Q = QL<D, F>;
+  constexpr int KB = Q::KB, NG = Q::NG, CW = Q::CW;
+  const TokList &L = *c.L;
+  const int base = L.base_q(F);
+  const int ntok = L.nQtok[F];
+  const uint8_t *tiles = c.st->qtiles[F] + (size_t)c.bh * c.g->NCT * Q::BYTES;
+  const int n_blocks = (eb - ea + 1) >> 1;
+  auto block = [&](int i, const uint8_t *(&ptr)[2], int (&hi)[2], int (&e)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qk = ea + 2 * i + t;
+      const bool valid = qk < eb;
+      const int qq = valid ? qk : ea + 2 * i;
+      ptr[t] = tiles + (size_t)qq * Q::BYTES;
+      hi[t] = valid ? min(TS, ntok - qq * TS) : 0;
+      e[t] = valid ? base + qq : c.g->TILES;
+    }
+  };
+  struct Buf {
+    uint32_t kc[2][CW], vc[2][CW];
+    uint32_t par[NG];   // this lane's 4*NG bytes of the params of tile lane/32
+  };
+  auto load = [&](const uint8_t *const (&ptr)[2], Buf &bf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t *kc = (const uint32_t *)(ptr[t] + c.lane * 4 * CW);
+      const uint32_t *vc = (const uint32_t *)(ptr[t] + Q::VC + c.lane * 4 * CW);
+#pragma unroll
+      for (int w = 0; w < CW; ++w) {
+        bf.kc[t][w] = ld_stream4(kc + w);
+        bf.vc[t][w] = ld_stream4(vc + w);
+      }
+    }
+    // both tiles' params: lanes 0-31 the first tile's, 32-63 the second's
+    const uint8_t *pp = (c.lane < 32 ? ptr[0] : ptr[1]) + Q::PAR + (c.lane & 31) * 4 * NG;
+#pragma unroll
+    for (int w = 0; w < NG; ++w) bf.par[w] = ld_stream4(pp + 4 * w);
+  };
+  const uint8_t *cp[2], *np[2];
+  int chi[2], ce[2], nhi[2], ne[2];
+  block(0, cp, chi, ce);
+  Buf cur, nxt;
+  load(cp, cur);
+  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+  for (int i = 0; i < n_blocks; ++i) {
+    block(min(i + 1, n_blocks - 1), np, nhi, ne);   // the last block re-reads itself
+    load(np, nxt);
+    // stage params: raw bytes, and the key scales as float32
+    {
+      uint32_t *dst = c.lds_par + (c.lane >> 5) * 32 * NG + (c.lane & 31) * NG;
+#pragma unroll
+      for (int w = 0; w < NG; ++w) dst[w] = cur.par[w];
+      if ((c.lane & 31) < 8) {   // these lanes hold the key scales [NG][16]
+        float *ks = c.lds_ks + (c.lane >> 5) * 16 * NG + (c.lane & 31) * 2 * NG;
+#pragma unroll
+        for (int w = 0; w < NG; ++w) {
+          ks[2 * w] = h_lo(cur.par[w]);
+          ks[2 * w + 1] = h_hi(cur.par[w]);
+        }
+      }
+    }
+    wave_lds_sync();
+    // ---- keys ----
+    float x[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const half8 a = F == 0 ? codes8_int4(cur.kc[t][kb]) : codes8(code_half(cur.kc[t][kb >> 1], kb & 1));
+        acc[kb] = mfma_f16_k32(a, bqk[kb], floatx4{0.f, 0.f, 0.f, 0.f});
+      }
+      // key-zero term: A row = token (lanes 0-15), k = group
+      half4 za = zero4;
+      {
+        const half_t *kz = (const half_t *)((const uint8_t *)c.lds_par + t * 128 * NG + (Q::KZ - Q::PAR)) +
+                           (c.lane & 15) * NG;
+        half4 zr;
+        if (NG == 4) {
+          zr = *(const half4 *)kz;
+        } else {
+          zr = half4{kz[0], kz[1], (half_t)0, (half_t)0};
+        }
+        za = c.lane < 16 ? zr : zero4;
+      }
+      floatx4 sco = mfma_f16_k16(za, bQ, floatx4{0.f, 0.f, 0.f, 0.f});
+      const float *ks = c.lds_ks + t * 16 * NG;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float4 s4 = *(const float4 *)(ks + kb * 16 + 4 * c.lq);
+        sco[0] = __builtin_fmaf(s4.x, acc[kb][0], sco[0]);
+        sco[1] = __builtin_fmaf(s4.y, acc[kb][1], sco[1]);
+        sco[2] = __builtin_fmaf(s4.z, acc[kb][2], sco[2]);
+        sco[3] = __builtin_fmaf(s4.w, acc[kb][3], sco[3]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = fold8(sco[r]);
+        x[t][r] = 4 * c.lq + r < chi[t] ? f * sc : neg_inf();
+      }
+    }
+    float p[2][4], tsum[2];
+    softmax_rows<D, 2>(ws, x, p, tsum);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    // ---- values ----
+    // fp16 limbs of p (p cut to 11 bits, exact remainder); (P1, P2) = (0, phi)
+    // on high rows, (phi, plo) on low rows
+    half4 P1[2], P2[2];
+    const uint32_t lo_keep = c.is_lo ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      half4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ph = __uint_as_float(__float_as_uint(p[t][r]) & 0xffffe000u);
+        phi[r] = (half_t)ph;
+        plo[r] = (half_t)(p[t][r] - ph);
+      }
+      const uint2 hb = __builtin_bit_cast(uint2, phi), lb = __builtin_bit_cast(uint2, plo);
+      P1[t] = __builtin_bit_cast(half4, make_uint2(hb.x & lo_keep, hb.y & lo_keep));
+      P2[t] = __builtin_bit_cast(half4, make_uint2(c.is_lo ? lb.x : hb.x, c.is_lo ? lb.y : hb.y));
+    }
+    const half_t *vs = (const half_t *)((const uint8_t *)c.lds_par + (Q::VS - Q::PAR));
+    const half_t *vz = (const half_t *)((const uint8_t *)c.lds_par + (Q::VZ - Q::PAR));
+#pragma unroll
+    for (int gb = 0; gb < NG; gb += GP) {
+      const int grp_l = gb + (GP == 1 ? 0 : c.slot);
+      const half4 s40 = *(const half4 *)(vs + grp_l * TS + 4 * c.lq);
+      const half4 s41 = *(const half4 *)(vs + 64 * NG + grp_l * TS + 4 * c.lq);
+      const half4 t0 = P1[0] * s40, t1 = P1[1] * s41;
+      const half4 ag0 = __builtin_elementwise_fma(P2[0], s40, __builtin_elementwise_fma(P1[0], s40, -t0));
+      const half4 ag1 = __builtin_elementwise_fma(P2[1], s41, __builtin_elementwise_fma(P1[1], s41, -t1));
+      const half8 ag = __builtin_shufflevector(ag0, ag1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c2 = 0; c2 < 2 * GP; ++c2) {
+        const int ct = gb * 2 + c2;
+        half4 b0, b1;
+        if (F == 0) {
+          const uint32_t x0 = cur.vc[0][ct >> 1], x1 = cur.vc[1][ct >> 1];
+          const uint32_t m0 = ((ct & 1) ? (x0 >> 4) : x0) & 0x0F0F0F0Fu;
+          const uint32_t m1 = ((ct & 1) ? (x1 >> 4) : x1) & 0x0F0F0F0Fu;
+          b0 = __builtin_shufflevector(fp8_pair<false>(m0), fp8_pair<true>(m0), 0, 1, 2, 3);
+          b1 = __builtin_shufflevector(fp8_pair<false>(m1), fp8_pair<true>(m1), 0, 1, 2, 3);
+        } else {
+          const uint32_t v0 = cur.vc[0][ct >> 2], v1 = cur.vc[1][ct >> 2];
+          b0 = __builtin_shufflevector(fp4_pair_sel(code_half(v0, 0), ct), fp4_pair_sel(code_half(v0, 1), ct), 0, 1,
+                                       2, 3);
+          b1 = __builtin_shufflevector(fp4_pair_sel(code_half(v1, 0), ct), fp4_pair_sel(code_half(v1, 1), ct), 0, 1,
+                                       2, 3);
+        }
+        ws.acc[ct] = mfma_f16_k32(ag, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), ws.acc[ct]);
+      }
+    }
+    {
+      // value-zero term: B column = group (col < NG), k = the lane's four tokens of each tile
+      const int zc = c.col < NG ? c.col : 0;
+      const half4 z0 = *(const half4 *)(vz + zc * TS + 4 * c.lq);
+      const half4 z1 = *(const half4 *)(vz + 64 * NG + zc * TS + 4 * c.lq);
+      const half4 bz0 = c.col < NG ? z0 : zero4, bz1 = c.col < NG ? z1 : zero4;
+      ws.zacc = mfma_f16_k32(__builtin_shufflevector(P2[0], P2[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                             __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
+    }
+    wave_lds_sync();
+    cur = nxt;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      cp[t] = np[t];
+      chi[t] = nhi[t];
+      ce[t] = ne[t];
+    }
+  }
+}
+
+template <int D, int GP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tok_attend_kernel(
     TokGeom g, TokState st, TokStep ts, const uint16_t *__restrict__ q, size_t q_bstride, float scale_log2) {
-  constexpr int KB = D / 32, CT = D / 16;
+  constexpr int KB = D / 32, CT = D / 16, NG = D / 32;
   const int S = g.n_splits;
   const int split = blockIdx.x % S;
   const int bh = blockIdx.x / S;
@@ -468,14 +710,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int col = lane & 15;
   const int lq = lane >> 4;
   const int G = g.G;
-  const bool is_hi = col < G;
-  const bool is_lo = col >= 8 && col < 8 + G;
-  const bool has_q = is_hi || is_lo;
-  const int hc = is_hi ? col : (is_lo ? col - 8 : 0);
+  // columns 0..7 take high limbs, 8..15 low limbs; within each half column c
+  // serves head (c mod 8) mod G, so every lane carries a head
+  const bool is_hi = col < 8;
+  const bool is_lo = col >= 8;
+  const int hc = (col & 7) & (G - 1);
 
   __shared__ float sm_m[ATT_WAVES][8];
   __shared__ float sm_l[ATT_WAVES][8];
   __shared__ float sm_o[ATT_WAVES][8][D];
+  __shared__ __attribute__((aligned(16))) uint32_t s_par[ATT_WAVES][2 * 32 * NG];
+  __shared__ __attribute__((aligned(16))) float s_ks[ATT_WAVES][2 * 16 * NG];
 
   const TokList L = tok_list(g, st, ts, bh);
   TokCtx c;
@@ -492,32 +737,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.G = G;
   c.is_hi = is_hi;
   c.is_lo = is_lo;
-  c.has_q = has_q;
+  c.has_q = true;
+  c.mass_lane = col < G;
+  c.slot = min((col & 7) / G, GP - 1);
   c.mrho = st.mrho + (size_t)bh * (g.TILES + 1) * G * TS;
   c.mref = st.mref + (size_t)bh * (g.TILES + 1) * G;
+  c.lds_par = &s_par[wave][0];
+  c.lds_ks = &s_ks[wave][0];
 
   WaveState<D> ws;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) ws.acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
   ws.zacc = floatx4{0.f, 0.f, 0.f, 0.f};
-  ws.m = has_q ? neg_inf() : 0.0f;   // columns without a head keep a finite reference
+  ws.m = neg_inf();
   ws.l = 0.0f;
 
   // query operands: bf16 for full-precision tiles; fp16 scaled by 2^-e (one e
-  // per KV head) for quantized ones.  Columns h and 8+h carry head h.
+  // per KV head, exact) for quantized ones -- in every column for INT1 tiles,
+  // in the high columns only for INT4 / INT2 tiles, whose key-zero term takes
+  // the per-group sums of the scaled query as two fp16 limbs (bQ: lanes 0-15,
+  // k = group; high limb in the high columns, low limb in the low ones).
   bf16x8 bq[KB];
-  half8 bqf[KB];
+  half8 bqf[KB], bqk[KB];
+  half4 bQ;
   float scq = scale_log2;
   {
     const uint16_t *qrow = q + (size_t)b * q_bstride + ((size_t)h * G + hc) * D;
-    const uint32_t keep = has_q ? 0xffffffffu : 0u;
     float amax = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint4 r = *(const uint4 *)(qrow + kb * 32 + lq * 8);
-      const uint4 rk = make_uint4(r.x & keep, r.y & keep, r.z & keep, r.w & keep);
-      bq[kb] = __builtin_bit_cast(bf16x8, rk);
-      const uint16_t *e = (const uint16_t *)&rk;
+      bq[kb] = __builtin_bit_cast(bf16x8, r);
+      const uint16_t *e = (const uint16_t *)&r;
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(bf16_to_f32(e[j])));
     }
@@ -528,11 +779,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     amax = fmaxf(amax, __shfl_xor(amax, 8));
     int qexp = 0;
     if (amax > 0.0f) frexpf(amax, &qexp);
+    const half8 zero8 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0};
+    float gsum[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint16_t *e = (const uint16_t *)&bq[kb];
+      float sum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bqf[kb][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+      for (int j = 0; j < 8; ++j) {
+        bqf[kb][j] = (half_t)ldexpf(bf16_to_f32(e[j]), -qexp);
+        sum += (float)bqf[kb][j];
+      }
+      gsum[kb] = sum_x32(sum_x16(sum));   // the 32 channels of group kb, for this lane's head
+      bqk[kb] = is_hi ? bqf[kb] : zero8;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float qs = k < KB ? gsum[k < KB ? k : 0] : 0.0f;
+      const half_t qh = (half_t)qs;
+      const half_t ql = (half_t)(qs - (float)qh);
+      bQ[k] = lq == 0 ? (is_hi ? qh : ql) : (half_t)0;
     }
     scq = ldexpf(scale_log2, qexp);
   }
@@ -550,13 +816,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int k = 0; k < 3; ++k) slice(L.nQ[k], qa[k], qz[k]);
   tok_run_bf16<D>(ws, c, bq, scale_log2, fa, fz);
   if (g.policy == QKV_POLICY_HQEKV) {
-    tok_run_quant<D, 0>(ws, c, bqf, scq, qa[0], qz[0]);
-    tok_run_quant<D, 1>(ws, c, bqf, scq, qa[1], qz[1]);
+    tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
+    tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
     tok_run_quant<D, 2>(ws, c, bqf, scq, qa[2], qz[2]);
   }
 
-  // ---- wave epilogue: fold the low-limb rows 8+h onto rows h ----
+  // ---- wave epilogue: value-zero term, then the low-limb rows 8+h onto rows h ----
   const float l_tot = sum_x32(sum_x16(ws.l));
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.acc[ct][i] += __shfl(ws.zacc[i], lq * 16 + (ct >> 1));
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -567,12 +837,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sm_m[wave][col] = ws.m;
     sm_l[wave][col] = l_tot;
   }
+  // row r < 8 holds head r mod G; a channel tile's values are read from the
+  // rows of its group's slot (r / G == group mod GP)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * lq + i;
-    if (r < G) {
+    if (r < 8) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) sm_o[wave][r][ct * 16 + col] = ws.acc[ct][i];
+      for (int ct = 0; ct < CT; ++ct)
+        if (r / G == ((ct >> 1) % GP)) sm_o[wave][r & (G - 1)][ct * 16 + col] = ws.acc[ct][i];
     }
   }
   __syncthreads();
@@ -703,13 +976,21 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
   hipError_t e;
-  // the optional events are attached to the dispatch (kernel execution time)
-  if (g.d == 128)
-    hipExtLaunchKernelGGL(tok_attend_kernel<128>, dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts, q,
-                          q_bstride, scale_log2);
+  // the optional events are attached to the dispatch (kernel execution time);
+  // four heads per KV head: value operands shared by channel-group pairs
+  const bool pair = g.G == 4;
+  if (g.d == 128 && pair)
+    hipExtLaunchKernelGGL((tok_attend_kernel<128, 2>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
+                          q, q_bstride, scale_log2);
+  else if (g.d == 128)
+    hipExtLaunchKernelGGL((tok_attend_kernel<128, 1>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
+                          q, q_bstride, scale_log2);
+  else if (pair)
+    hipExtLaunchKernelGGL((tok_attend_kernel<64, 2>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
+                          q, q_bstride, scale_log2);
   else
-    hipExtLaunchKernelGGL(tok_attend_kernel<64>, dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts, q,
-                          q_bstride, scale_log2);
+    hipExtLaunchKernelGGL((tok_attend_kernel<64, 1>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
+                          q, q_bstride, scale_log2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mass_out && (e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.T * sizeof(float), s)) != hipSuccess) return e;
   // live tiles per (sequence, KV head): at most the ranked tokens' tiles
@@ -1067,6 +1348,124 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
 
 __device__ __forceinline__ size_t tb_of(const TokGeom &g, int bh) { return (size_t)bh * g.T; }
 
+// code of channel c of a per-token record's code stream (bits b)
+__device__ __forceinline__ uint32_t rec_code(const uint8_t *codes, int c, int bits) {
+  if (bits == 1) return (codes[c >> 3] >> (c & 7)) & 1u;
+  return (codes[c * bits / 8] >> (bits * (c % (8 / bits)))) & ((1u << bits) - 1u);
+}
+
+// INT4 / INT2 tiles of one (sequence, KV head) in operand order (QL)
+template <int D, int F>
+__device__ void hq_gather_ql(const TokGeom &g, const TokState &st, int bh) {
+  using Q = QL<D, F>;
+  const int bits = F == 0 ? 4 : 2;
+  const int nq = st.cnt[bh * 4 + 1 + F];
+  const int ntiles = (nq + TS - 1) / TS;
+  uint8_t *tiles = st.qtiles[F] + (size_t)bh * g.NCT * Q::BYTES;
+  const int32_t *qpos = st.qpos[F] + (size_t)bh * g.NCT * TS;
+  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * g.rec_bytes;
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
+    const int tile = it / 64, lane = it % 64;
+    uint8_t *T = tiles + (size_t)tile * Q::BYTES;
+    const int t = lane & 15, lq = lane >> 4;
+    // keys: token slot t, channels kb*32 + 8*lq + e
+    uint32_t kw[Q::CW];
+#pragma unroll
+    for (int w = 0; w < Q::CW; ++w) kw[w] = 0u;
+    const int ks = tile * TS + t;
+    if (ks < nq) {
+      const uint8_t *rec = rec0 + (size_t)qpos[ks] * g.rec_bytes;
+      for (int kb = 0; kb < Q::KB; ++kb)
+        for (int e = 0; e < 8; ++e) {
+          int dw, bit;
+          ql_kslot<F>(kb, e, dw, bit);
+          kw[dw] |= rec_code(rec, kb * 32 + 8 * lq + e, bits) << bit;
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < Q::CW; ++w) ((uint32_t *)(T + lane * 4 * Q::CW))[w] = kw[w];
+    // values: channel ct*16 + t, token slots 4*lq + tt
+    uint32_t vw[Q::CW];
+#pragma unroll
+    for (int w = 0; w < Q::CW; ++w) vw[w] = 0u;
+    for (int tt = 0; tt < 4; ++tt) {
+      const int vs = tile * TS + 4 * lq + tt;
+      if (vs >= nq) continue;
+      const uint8_t *rec = rec0 + (size_t)qpos[vs] * g.rec_bytes + D / 2;
+      for (int ct = 0; ct < Q::CT; ++ct) {
+        int dw, bit;
+        ql_vslot<F>(ct, tt, dw, bit);
+        vw[dw] |= rec_code(rec, ct * 16 + t, bits) << bit;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < Q::CW; ++w) ((uint32_t *)(T + Q::VC + lane * 4 * Q::CW))[w] = vw[w];
+    // params of token slot t, written by the lanes of row lq == 0
+    if (lq == 0) {
+      const int sl = tile * TS + t;
+      const uint16_t *par = sl < nq ? (const uint16_t *)(rec0 + (size_t)qpos[sl] * g.rec_bytes + D) : nullptr;
+      uint16_t *ksc = (uint16_t *)(T + Q::KS), *kzr = (uint16_t *)(T + Q::KZ);
+      uint16_t *vsc = (uint16_t *)(T + Q::VS), *vzr = (uint16_t *)(T + Q::VZ);
+      for (int gi = 0; gi < Q::NG; ++gi) {
+        ksc[gi * TS + t] = par ? par[2 * gi] : 0;
+        kzr[t * Q::NG + gi] = par ? par[2 * gi + 1] : 0;
+        vsc[gi * TS + t] = par ? par[2 * Q::NG + 2 * gi] : 0;
+        vzr[gi * TS + t] = par ? par[2 * Q::NG + 2 * gi + 1] : 0;
+      }
+    }
+  }
+}
+
+// INT1 tiles (QTile layout: codes by lane, params by token)
+template <int D>
+__device__ void hq_gather_int1(const TokGeom &g, const TokState &st, int bh) {
+  constexpr int KB = D / 32, CT = D / 16;
+  constexpr int f = 2, bits = 1;
+  const int LB = KB * bits < 4 ? 4 : KB * bits, PB = 4, BYTES = 128 * LB + 32 * PB;
+  const int nq = st.cnt[bh * 4 + 1 + f];
+  const int ntiles = (nq + TS - 1) / TS;
+  uint8_t *tiles = st.qtiles[f] + (size_t)bh * g.NCT * BYTES;
+  const int32_t *qpos = st.qpos[f] + (size_t)bh * g.NCT * TS;
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
+    const int tile = it / 64, lane = it % 64;
+    uint8_t *T = tiles + (size_t)tile * BYTES;
+    const int t = lane & 15, lq = lane >> 4;
+    // keys: this lane's token is slot t
+    const int ks = tile * TS + t;
+    uint32_t kw[4] = {0u, 0u, 0u, 0u};
+    if (ks < nq) {
+      const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[ks]) * g.rec_bytes;
+      for (int kb = 0; kb < KB; ++kb)
+        for (int e = 0; e < 8; ++e) {
+          const int bit = (kb * 8 + e) * bits;
+          kw[bit >> 5] |= rec_code(rec, kb * 32 + 8 * lq + e, bits) << (bit & 31);
+        }
+    }
+    for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + lane * LB))[w] = kw[w];
+    // values: this lane's column l%16, tokens 4*lq .. +3
+    uint32_t vw[4] = {0u, 0u, 0u, 0u};
+    for (int tt = 0; tt < 4; ++tt) {
+      const int vs = tile * TS + 4 * lq + tt;
+      if (vs >= nq) continue;
+      const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[vs]) * g.rec_bytes + g.d / 2;
+      for (int ct = 0; ct < CT; ++ct) {
+        const int bit = (ct * 4 + tt) * bits;
+        vw[bit >> 5] |= rec_code(rec, ct * 16 + t, bits) << (bit & 31);
+      }
+    }
+    for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + 64 * LB + lane * LB))[w] = vw[w];
+    // params of slot t (keys then values), written by the lanes of row lq == 0
+    if (lq == 0) {
+      const int sl = tile * TS + t;
+      const uint8_t *rec = sl < nq ? st.qrec + (tb_of(g, bh) + qpos[sl]) * g.rec_bytes : nullptr;
+      for (int bb = 0; bb < PB; ++bb) {
+        T[128 * LB + t * PB + bb] = rec ? rec[g.d + bb] : 0;
+        T[128 * LB + 16 * PB + t * PB + bb] = rec ? rec[g.d + (g.d / 32) * 4 + bb] : 0;
+      }
+    }
+  }
+}
+
 // compact tiles of every tier from the position lists: one thread per
 // (token slot, 8-channel chunk) for BF16, per (token slot) for quantized tiers
 template <int D>
@@ -1082,66 +1481,9 @@ __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) 
     tok_copy_token(g, pages_bh, cpages_bh, st.cpos[(size_t)bh * g.NCT * TS + i], i, (it % chunks) * 8);
   }
   // quantized tiers: one thread per (slot, lane of the tile layout)
-  constexpr int KB = D / 32, CT = D / 16;
-#pragma unroll
-  for (int f = 0; f < 3; ++f) {
-    const int bits = QBITS[f];
-    const int LB = KB * bits < 4 ? 4 : KB * bits, PB = f == 2 ? 4 : KB * 4, BYTES = 128 * LB + 32 * PB;
-    const int nq = st.cnt[bh * 4 + 1 + f];
-    const int ntiles = (nq + TS - 1) / TS;
-    uint8_t *tiles = st.qtiles[f] + (size_t)bh * g.NCT * BYTES;
-    const int32_t *qpos = st.qpos[f] + (size_t)bh * g.NCT * TS;
-    for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
-      const int tile = it / 64, lane = it % 64;
-      uint8_t *T = tiles + (size_t)tile * BYTES;
-      const int t = lane & 15, lq = lane >> 4;
-      // keys: this lane's token is slot t
-      const int ks = tile * TS + t;
-      uint32_t kw[4] = {0u, 0u, 0u, 0u};
-      if (ks < nq) {
-        const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[ks]) * g.rec_bytes;
-        for (int kb = 0; kb < KB; ++kb)
-          for (int e = 0; e < 8; ++e) {
-            const int cch = kb * 32 + 8 * lq + e;
-            uint32_t code;
-            if (bits == 1)
-              code = (rec[cch >> 3] >> (cch & 7)) & 1u;
-            else
-              code = (rec[cch * bits / 8] >> (bits * (cch % (8 / bits)))) & ((1u << bits) - 1u);
-            const int bit = (kb * 8 + e) * bits;
-            kw[bit >> 5] |= code << (bit & 31);
-          }
-      }
-      for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + lane * LB))[w] = kw[w];
-      // values: this lane's column l%16, tokens 4*lq .. +3
-      uint32_t vw[4] = {0u, 0u, 0u, 0u};
-      for (int tt = 0; tt < 4; ++tt) {
-        const int vs = tile * TS + 4 * lq + tt;
-        if (vs >= nq) continue;
-        const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[vs]) * g.rec_bytes + g.d / 2;
-        for (int ct = 0; ct < CT; ++ct) {
-          const int cch = ct * 16 + t;
-          uint32_t code;
-          if (bits == 1)
-            code = (rec[cch >> 3] >> (cch & 7)) & 1u;
-          else
-            code = (rec[cch * bits / 8] >> (bits * (cch % (8 / bits)))) & ((1u << bits) - 1u);
-          const int bit = (ct * 4 + tt) * bits;
-          vw[bit >> 5] |= code << (bit & 31);
-        }
-      }
-      for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + 64 * LB + lane * LB))[w] = vw[w];
-      // params of slot t (keys then values), written by the lanes of row lq == 0
-      if (lq == 0) {
-        const int sl = tile * TS + t;
-        const uint8_t *rec = sl < nq ? st.qrec + (tb_of(g, bh) + qpos[sl]) * g.rec_bytes : nullptr;
-        for (int bb = 0; bb < PB; ++bb) {
-          T[128 * LB + t * PB + bb] = rec ? rec[g.d + bb] : 0;
-          T[128 * LB + 16 * PB + t * PB + bb] = rec ? rec[g.d + (g.d / 32) * 4 + bb] : 0;
-        }
-      }
-    }
-  }
+  hq_gather_ql<D, 0>(g, st, bh);
+  hq_gather_ql<D, 1>(g, st, bh);
+  hq_gather_int1<D>(g, st, bh);
 }
 
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
