@@ -33,7 +33,6 @@ namespace {
 
 constexpr size_t TOK_ALIGN = 256;
 inline size_t tok_align(size_t x) { return (x + TOK_ALIGN - 1) / TOK_ALIGN * TOK_ALIGN; }
-constexpr int QBITS[3] = {4, 2, 1};   // INT4, INT2, INT1
 constexpr float KAPPA1 = 0.6744897501960817f;   // Phi^-1(3/4): INT1 centres are mean -/+ KAPPA1 * std
 
 }  // namespace
@@ -252,9 +251,9 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(cp[t] + (kb * 64 + c.lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(cp[t] + (kb * 64 + c.lane) * 8);
 #pragma unroll
-    for (int p = 0; p < CP; ++p) vr[t][p] = *(const uint4 *)(cp[t] + TS * D + (p * 64 + c.lane) * 8);
+    for (int p = 0; p < CP; ++p) vr[t][p] = ld_stream16(cp[t] + TS * D + (p * 64 + c.lane) * 8);
   }
   for (int i = 0; i < n_blocks; ++i) {
     block(min(i + 1, n_blocks - 1), np, nlo, nhi, ne);   // the last block re-reads itself
@@ -266,7 +265,7 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = *(const uint4 *)(np[t] + (kb * 64 + c.lane) * 8);
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(np[t] + (kb * 64 + c.lane) * 8);
     float p[2][4], tsum[2];
     softmax_block<D, 2>(ws, s, sc, clo, chi, c.lq, p, tsum);
 #pragma unroll
@@ -290,7 +289,7 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = *(const uint4 *)(np[t] + TS * D + (p2 * 64 + c.lane) * 8);
+      for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = ld_stream16(np[t] + TS * D + (p2 * 64 + c.lane) * 8);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       cp[t] = np[t];
@@ -300,24 +299,6 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
     }
   }
 }
-
-// Compact quantized tile of format F (0 INT4, 1 INT2, 2 INT1), bits b:
-//   K codes  [64 lanes][KB*b bytes]: lane l (token l%16) holds, for k-block kb,
-//            channels kb*32 + 8*(l/16) + e at bit (kb*8 + e)*b
-//   V codes  [64 lanes][KB*b bytes]: lane l (channel column l%16) holds, for
-//            column tile ct, tokens 4*(l/16) + tt at bit (ct*4 + tt)*b
-//   K params [16 tokens][PB bytes], V params [16 tokens][PB bytes]:
-//            INT4/INT2 (scale, zero) fp16 per group of 32 channels,
-//            INT1 (mean, std) fp16
-template <int D, int F>
-struct QTile {
-  static constexpr int BITS = F == 0 ? 4 : (F == 1 ? 2 : 1);
-  static constexpr int LB = (D / 32) * BITS < 4 ? 4 : (D / 32) * BITS;   // code bytes per lane (dword padded)
-  static constexpr int PB = F == 2 ? 4 : (D / 32) * 4;
-  static constexpr int KC = 0, VC = 64 * LB, KP = 128 * LB, VP = 128 * LB + 16 * PB;
-  static constexpr int BYTES = 128 * LB + 32 * PB;
-  static constexpr int NW = (LB + 3) / 4;      // code dwords per lane
-};
 
 // INT4 and INT2 compact tiles (F = 0, 1) are laid out in the order the
 // matrix-core operands are built, so that the attention kernel never
@@ -340,6 +321,23 @@ struct QL {
   static constexpr int KS = PAR, KZ = PAR + 32 * NG, VS = PAR + 64 * NG, VZ = PAR + 96 * NG;
   static constexpr int BYTES = PAR + 128 * NG;
 };
+
+// INT1 compact tiles: one code dword per lane for keys and one for values,
+// each bit a code, placed so that (x >> j) & 0x11111111 leaves eight codes as
+// the nibbles 000b of four bytes (the FP4 conversion then gives 0 or 1):
+//   keys: code of k-block kb, element e at bit 4e + kb
+//   values: column tile ct, token tt at bit 8*(2*(ct%2) + tt/2) + 4*(tt%2) + ct/2
+//   params: K std [16], K mean [16], V std [16], V mean [16], fp16
+template <int D>
+struct Q1 {
+  static constexpr int KB = D / 32, CT = D / 16, NG = D / 32;
+  static constexpr int VC = 256, PAR = 512;
+  static constexpr int KSD = PAR, KM = PAR + 32, VSD = PAR + 64, VM = PAR + 96;
+  static constexpr int BYTES = PAR + 128;
+};
+__host__ __device__ inline int q1_kbit(int kb, int e) { return 4 * e + kb; }
+__host__ __device__ inline int q1_vbit(int ct, int tt) { return 8 * (2 * (ct & 1) + (tt >> 1)) + 4 * (tt & 1) + (ct >> 1); }
+
 template <int F>
 __host__ __device__ inline void ql_kslot(int kb, int e, int &dw, int &bit) {
   if (F == 0) {
@@ -361,153 +359,8 @@ __host__ __device__ inline void ql_vslot(int ct, int tt, int &dw, int &bit) {
   }
 }
 
-template <int D, int F>
-struct QBufT {
-  uint32_t kc[QTile<D, F>::NW];
-  uint32_t vc[QTile<D, F>::NW];
-  uint32_t kp[QTile<D, F>::PB / 4];            // this lane's token
-  uint32_t vp[QTile<D, F>::PB];                // this lane's four tokens (4 * PB bytes)
-};
-
-template <int D, int F>
-__device__ __forceinline__ void qt_load(const uint8_t *tile, int lane, QBufT<D, F> &q) {
-  using Q = QTile<D, F>;
-  const int t = lane & 15, lq = lane >> 4;
-  const uint32_t *kc = (const uint32_t *)(tile + Q::KC + lane * Q::LB);
-  const uint32_t *vc = (const uint32_t *)(tile + Q::VC + lane * Q::LB);
-#pragma unroll
-  for (int w = 0; w < Q::NW; ++w) {
-    q.kc[w] = kc[w];
-    q.vc[w] = vc[w];
-  }
-  const uint32_t *kp = (const uint32_t *)(tile + Q::KP + t * Q::PB);
-#pragma unroll
-  for (int w = 0; w < Q::PB / 4; ++w) q.kp[w] = kp[w];
-  const uint32_t *vp = (const uint32_t *)(tile + Q::VP + 4 * lq * Q::PB);
-#pragma unroll
-  for (int w = 0; w < Q::PB; ++w) q.vp[w] = vp[w];
-}
-
 __device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16)); }
-
-template <int D, int F>
-__device__ __forceinline__ uint32_t qt_code(const uint32_t *w, int idx) {   // idx-th code of a lane's bits
-  constexpr int B = QTile<D, F>::BITS;
-  const int bit = idx * B;
-  return (w[bit >> 5] >> (bit & 31)) & ((1u << B) - 1u);
-}
-
-// dequantized value of a code: fma(code, s, z) for INT4/INT2; INT1 the
-// centre m -/+ KAPPA1 * std, both one float32 rounding
-template <int F>
-__device__ __forceinline__ float qt_deq(uint32_t code, float s_or_sd, float z_or_m) {
-  if (F == 2) return __builtin_fmaf(code ? KAPPA1 : -KAPPA1, s_or_sd, z_or_m);
-  return __builtin_fmaf((float)code, s_or_sd, z_or_m);
-}
-
-template <int D, int F>
-__device__ void tok_run_quant(WaveState<D> &ws, const TokCtx &c, const half8 (&bqf)[D / 32], float sc, int ea,
-                              int eb) {
-  if (ea >= eb) return;
-  using Q = QTile<D, F>;
-  constexpr int KB = D / 32, CT = D / 16;
-  const TokList &L = *c.L;
-  const int base = L.base_q(F);
-  const int ntok = L.nQtok[F];
-  const uint8_t *tiles = c.st->qtiles[F] + (size_t)c.bh * c.g->NCT * Q::BYTES;
-  const int n_blocks = (eb - ea + 1) >> 1;
-  auto block = [&](int i, const uint8_t *(&ptr)[2], int (&hi)[2], int (&e)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int qk = ea + 2 * i + t;
-      const bool valid = qk < eb;
-      const int qq = valid ? qk : ea + 2 * i;
-      ptr[t] = tiles + (size_t)qq * Q::BYTES;
-      hi[t] = (valid && c.has_q) ? min(TS, ntok - qq * TS) : 0;
-      e[t] = valid ? base + qq : c.g->TILES;
-    }
-  };
-  const uint8_t *cp[2], *np[2];
-  int chi[2], ce[2], nhi[2], ne[2];
-  block(0, cp, chi, ce);
-  QBufT<D, F> qb[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) qt_load<D, F>(cp[t], c.lane, qb[t]);
-  const int lo[2] = {0, 0};
-  for (int i = 0; i < n_blocks; ++i) {
-    block(min(i + 1, n_blocks - 1), np, nhi, ne);
-    // keys: exact float32 values, as two fp16 limbs, for each k-block
-    floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float ks, kz;
-        if (F == 2) {
-          ks = h_hi(qb[t].kp[0]);
-          kz = h_lo(qb[t].kp[0]);
-        } else {
-          ks = h_lo(qb[t].kp[kb]);
-          kz = h_hi(qb[t].kp[kb]);
-        }
-        half8 ahi, alo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = qt_deq<F>(qt_code<D, F>(qb[t].kc, kb * 8 + e), ks, kz);
-          ahi[e] = (half_t)x;
-          alo[e] = (half_t)(x - (float)ahi[e]);
-        }
-        s[t] = mfma_f16_k32(ahi, bqf[kb], s[t]);
-        s[t] = mfma_f16_k32(alo, bqf[kb], s[t]);
-      }
-    float p[2][4], tsum[2];
-    softmax_block<D, 2>(ws, s, sc, lo, chi, c.lq, p, tsum);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
-    // rows h carry fp16(p), rows 8+h carry fp16(p - fp16(p))
-    half8 ap;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const half_t hp = (half_t)p[t][i2];
-        ap[t * 4 + i2] = c.is_lo ? (half_t)(p[t][i2] - (float)hp) : hp;
-      }
-    // values of the lane's four tokens of each tile, exact, as two fp16 limbs
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      half8 bhi, blo;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          float vs, vz;
-          if (F == 2) {
-            vs = h_hi(qb[t].vp[tt]);
-            vz = h_lo(qb[t].vp[tt]);
-          } else {
-            const uint32_t w = qb[t].vp[tt * (Q::PB / 4) + (ct >> 1)];   // group ct*16/32
-            vs = h_lo(w);
-            vz = h_hi(w);
-          }
-          const float x = qt_deq<F>(qt_code<D, F>(qb[t].vc, ct * 4 + tt), vs, vz);
-          const half_t xh = (half_t)x;
-          bhi[t * 4 + tt] = xh;
-          blo[t * 4 + tt] = (half_t)(x - (float)xh);
-        }
-      ws.acc[ct] = mfma_f16_k32(ap, bhi, ws.acc[ct]);
-      ws.acc[ct] = mfma_f16_k32(ap, blo, ws.acc[ct]);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      qt_load<D, F>(np[t], c.lane, qb[t]);
-      cp[t] = np[t];
-      chi[t] = nhi[t];
-      ce[t] = ne[t];
-    }
-  }
-}
 
 // INT4 / INT2 tiles (QL layout), two per block.  Keys: one MFMA per k-block
 // on the exact integer codes against the fp16 query (high columns only), kept
@@ -696,6 +549,131 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
   }
 }
 
+// INT1 tiles (Q1 layout), two per block.  A token's values are
+// mean + KAPPA1 * std * (2b - 1), so with a = 2 KAPPA1 std and
+// c = mean - KAPPA1 std (float32, per token):
+//   keys:   score = a * sum_c q_c b_c + c * sum_c q_c, one MFMA chain over the
+//           0/1 codes against the fp16 query (high columns), then per row;
+//   values: o = sum_t (p_t a_t) b_t + sum_t p_t c_t, with p*a split into two
+//           fp16 limbs (high rows, low rows) against the 0/1 codes, and the
+//           zero term as two MFMAs over the fp16 limbs of c.
+template <int D>
+__device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], float qall, float sc,
+                           int ea, int eb) {
+  if (ea >= eb) return;
+  using Q = Q1<D>;
+  constexpr int KB = Q::KB, CT = Q::CT, NG = Q::NG;
+  const TokList &L = *c.L;
+  const int base = L.base_q(2);
+  const int ntok = L.nQtok[2];
+  const uint8_t *tiles = c.st->qtiles[2] + (size_t)c.bh * c.g->NCT * Q::BYTES;
+  const int n_blocks = (eb - ea + 1) >> 1;
+  auto block = [&](int i, const uint8_t *(&ptr)[2], int (&hi)[2], int (&e)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qk = ea + 2 * i + t;
+      const bool valid = qk < eb;
+      const int qq = valid ? qk : ea + 2 * i;
+      ptr[t] = tiles + (size_t)qq * Q::BYTES;
+      hi[t] = valid ? min(TS, ntok - qq * TS) : 0;
+      e[t] = valid ? base + qq : c.g->TILES;
+    }
+  };
+  struct Buf {
+    uint32_t kc[2], vc[2];
+    uint32_t par;   // this lane's 4 bytes of the params of tile lane/32
+  };
+  auto load = [&](const uint8_t *const (&ptr)[2], Buf &bf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf.kc[t] = ld_stream4(ptr[t] + 4 * c.lane);
+      bf.vc[t] = ld_stream4(ptr[t] + Q::VC + 4 * c.lane);
+    }
+    bf.par = ld_stream4((c.lane < 32 ? ptr[0] : ptr[1]) + Q::PAR + 4 * (c.lane & 31));
+  };
+  const uint8_t *cp[2], *np[2];
+  int chi[2], ce[2], nhi[2], ne[2];
+  block(0, cp, chi, ce);
+  Buf cur, nxt;
+  load(cp, cur);
+  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+  const half_t *par16 = (const half_t *)c.lds_par;   // [2 tiles][K std 16][K mean 16][V std 16][V mean 16]
+  for (int i = 0; i < n_blocks; ++i) {
+    block(min(i + 1, n_blocks - 1), np, nhi, ne);   // the last block re-reads itself
+    load(np, nxt);
+    c.lds_par[c.lane] = cur.par;
+    wave_lds_sync();
+    // ---- keys ----
+    float x[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = mfma_f16_k32(codes8((cur.kc[t] >> kb) & 0x11111111u), bqk[kb], acc);
+      const half4 sd = *(const half4 *)(par16 + t * 64 + 4 * c.lq);
+      const half4 mn = *(const half4 *)(par16 + t * 64 + 16 + 4 * c.lq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = 2.0f * KAPPA1 * (float)sd[r];
+        const float cz = __builtin_fmaf(-KAPPA1, (float)sd[r], (float)mn[r]);
+        const float f = fold8(__builtin_fmaf(a, acc[r], c.is_hi ? cz * qall : 0.0f));
+        x[t][r] = 4 * c.lq + r < chi[t] ? f * sc : neg_inf();
+      }
+    }
+    float p[2][4], tsum[2];
+    softmax_rows<D, 2>(ws, x, p, tsum);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    // ---- values ----
+    half8 ag, cz_hi, cz_lo;
+    half4 P2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const half4 sd = *(const half4 *)(par16 + t * 64 + 32 + 4 * c.lq);
+      const half4 mn = *(const half4 *)(par16 + t * 64 + 48 + 4 * c.lq);
+      half4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // p * a as a high part cut to 11 bits and the exact remainder
+        const float pa = p[t][r] * (2.0f * KAPPA1 * (float)sd[r]);
+        const float ah = __uint_as_float(__float_as_uint(pa) & 0xffffe000u);
+        ag[t * 4 + r] = c.is_lo ? (half_t)(pa - ah) : (half_t)ah;
+        const float ph = __uint_as_float(__float_as_uint(p[t][r]) & 0xffffe000u);
+        phi[r] = (half_t)ph;
+        plo[r] = (half_t)(p[t][r] - ph);
+        const float cz = __builtin_fmaf(-KAPPA1, (float)sd[r], (float)mn[r]);
+        const half_t czh = (half_t)cz;
+        cz_hi[t * 4 + r] = c.col < NG ? czh : (half_t)0;
+        cz_lo[t * 4 + r] = c.col < NG ? (half_t)(cz - (float)czh) : (half_t)0;
+      }
+      P2[t] = c.is_lo ? plo : phi;
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int B0 = 2 * (ct & 1);
+      const uint32_t m0 = (cur.vc[0] >> (ct >> 1)) & 0x11111111u;
+      const uint32_t m1 = (cur.vc[1] >> (ct >> 1)) & 0x11111111u;
+      const half4 b0 = __builtin_shufflevector(fp4_pair_sel(m0, B0), fp4_pair_sel(m0, B0 + 1), 0, 1, 2, 3);
+      const half4 b1 = __builtin_shufflevector(fp4_pair_sel(m1, B0), fp4_pair_sel(m1, B0 + 1), 0, 1, 2, 3);
+      ws.acc[ct] = mfma_f16_k32(ag, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), ws.acc[ct]);
+    }
+    {
+      const half8 pp = __builtin_shufflevector(P2[0], P2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      ws.zacc = mfma_f16_k32(pp, cz_hi, ws.zacc);
+      ws.zacc = mfma_f16_k32(pp, cz_lo, ws.zacc);
+    }
+    wave_lds_sync();
+    cur = nxt;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      cp[t] = np[t];
+      chi[t] = nhi[t];
+      ce[t] = ne[t];
+    }
+  }
+}
+
 template <int D, int GP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tok_attend_kernel(
     TokGeom g, TokState st, TokStep ts, const uint16_t *__restrict__ q, size_t q_bstride, float scale_log2) {
@@ -760,6 +738,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   bf16x8 bq[KB];
   half8 bqf[KB], bqk[KB];
   half4 bQ;
+  float qall;   // sum of the scaled query over all channels, for this lane's head
   float scq = scale_log2;
   {
     const uint16_t *qrow = q + (size_t)b * q_bstride + ((size_t)h * G + hc) * D;
@@ -781,6 +760,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (amax > 0.0f) frexpf(amax, &qexp);
     const half8 zero8 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0, (half_t)0};
     float gsum[KB];
+    qall = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint16_t *e = (const uint16_t *)&bq[kb];
@@ -791,6 +771,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sum += (float)bqf[kb][j];
       }
       gsum[kb] = sum_x32(sum_x16(sum));   // the 32 channels of group kb, for this lane's head
+      qall += gsum[kb];
       bqk[kb] = is_hi ? bqf[kb] : zero8;
     }
 #pragma unroll
@@ -818,7 +799,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (g.policy == QKV_POLICY_HQEKV) {
     tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
     tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
-    tok_run_quant<D, 2>(ws, c, bqf, scq, qa[2], qz[2]);
+    tok_run_q1<D>(ws, c, bqk, qall, scq, qa[2], qz[2]);
   }
 
   // ---- wave epilogue: value-zero term, then the low-limb rows 8+h onto rows h ----
@@ -1416,52 +1397,43 @@ __device__ void hq_gather_ql(const TokGeom &g, const TokState &st, int bh) {
   }
 }
 
-// INT1 tiles (QTile layout: codes by lane, params by token)
+// INT1 tiles of one (sequence, KV head) (Q1 layout)
 template <int D>
-__device__ void hq_gather_int1(const TokGeom &g, const TokState &st, int bh) {
-  constexpr int KB = D / 32, CT = D / 16;
-  constexpr int f = 2, bits = 1;
-  const int LB = KB * bits < 4 ? 4 : KB * bits, PB = 4, BYTES = 128 * LB + 32 * PB;
-  const int nq = st.cnt[bh * 4 + 1 + f];
+__device__ void hq_gather_q1(const TokGeom &g, const TokState &st, int bh) {
+  using Q = Q1<D>;
+  const int nq = st.cnt[bh * 4 + 3];
   const int ntiles = (nq + TS - 1) / TS;
-  uint8_t *tiles = st.qtiles[f] + (size_t)bh * g.NCT * BYTES;
-  const int32_t *qpos = st.qpos[f] + (size_t)bh * g.NCT * TS;
+  uint8_t *tiles = st.qtiles[2] + (size_t)bh * g.NCT * Q::BYTES;
+  const int32_t *qpos = st.qpos[2] + (size_t)bh * g.NCT * TS;
+  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * g.rec_bytes;
   for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
     const int tile = it / 64, lane = it % 64;
-    uint8_t *T = tiles + (size_t)tile * BYTES;
+    uint8_t *T = tiles + (size_t)tile * Q::BYTES;
     const int t = lane & 15, lq = lane >> 4;
-    // keys: this lane's token is slot t
+    uint32_t kw = 0u;
     const int ks = tile * TS + t;
-    uint32_t kw[4] = {0u, 0u, 0u, 0u};
     if (ks < nq) {
-      const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[ks]) * g.rec_bytes;
-      for (int kb = 0; kb < KB; ++kb)
-        for (int e = 0; e < 8; ++e) {
-          const int bit = (kb * 8 + e) * bits;
-          kw[bit >> 5] |= rec_code(rec, kb * 32 + 8 * lq + e, bits) << (bit & 31);
-        }
+      const uint8_t *rec = rec0 + (size_t)qpos[ks] * g.rec_bytes;
+      for (int kb = 0; kb < Q::KB; ++kb)
+        for (int e = 0; e < 8; ++e) kw |= rec_code(rec, kb * 32 + 8 * lq + e, 1) << q1_kbit(kb, e);
     }
-    for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + lane * LB))[w] = kw[w];
-    // values: this lane's column l%16, tokens 4*lq .. +3
-    uint32_t vw[4] = {0u, 0u, 0u, 0u};
+    ((uint32_t *)T)[lane] = kw;
+    uint32_t vw = 0u;
     for (int tt = 0; tt < 4; ++tt) {
       const int vs = tile * TS + 4 * lq + tt;
       if (vs >= nq) continue;
-      const uint8_t *rec = st.qrec + (tb_of(g, bh) + qpos[vs]) * g.rec_bytes + g.d / 2;
-      for (int ct = 0; ct < CT; ++ct) {
-        const int bit = (ct * 4 + tt) * bits;
-        vw[bit >> 5] |= rec_code(rec, ct * 16 + t, bits) << (bit & 31);
-      }
+      const uint8_t *rec = rec0 + (size_t)qpos[vs] * g.rec_bytes + D / 2;
+      for (int ct = 0; ct < Q::CT; ++ct) vw |= rec_code(rec, ct * 16 + t, 1) << q1_vbit(ct, tt);
     }
-    for (int w = 0; w < (LB + 3) / 4; ++w) ((uint32_t *)(T + 64 * LB + lane * LB))[w] = vw[w];
-    // params of slot t (keys then values), written by the lanes of row lq == 0
+    ((uint32_t *)(T + Q::VC))[lane] = vw;
     if (lq == 0) {
       const int sl = tile * TS + t;
-      const uint8_t *rec = sl < nq ? st.qrec + (tb_of(g, bh) + qpos[sl]) * g.rec_bytes : nullptr;
-      for (int bb = 0; bb < PB; ++bb) {
-        T[128 * LB + t * PB + bb] = rec ? rec[g.d + bb] : 0;
-        T[128 * LB + 16 * PB + t * PB + bb] = rec ? rec[g.d + (g.d / 32) * 4 + bb] : 0;
-      }
+      const uint16_t *par = sl < nq ? (const uint16_t *)(rec0 + (size_t)qpos[sl] * g.rec_bytes + D) : nullptr;
+      // records keep (mean, std) in the first params pair of keys and of values
+      ((uint16_t *)(T + Q::KSD))[t] = par ? par[1] : 0;
+      ((uint16_t *)(T + Q::KM))[t] = par ? par[0] : 0;
+      ((uint16_t *)(T + Q::VSD))[t] = par ? par[2 * Q::NG + 1] : 0;
+      ((uint16_t *)(T + Q::VM))[t] = par ? par[2 * Q::NG] : 0;
     }
   }
 }
@@ -1483,7 +1455,7 @@ __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) 
   // quantized tiers: one thread per (slot, lane of the tile layout)
   hq_gather_ql<D, 0>(g, st, bh);
   hq_gather_ql<D, 1>(g, st, bh);
-  hq_gather_int1<D>(g, st, bh);
+  hq_gather_q1<D>(g, st, bh);
 }
 
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
