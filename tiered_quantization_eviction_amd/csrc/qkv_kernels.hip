@@ -423,7 +423,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   const Geom &g = *c.g;
   const int tpw = g.tpw;
   const int nws = QT / tpw;                                  // window slots per block
-  const int G = c.G;
+  constexpr int G = GP == 2 ? 4 : 8;   // query heads per KV head (the launcher pairs groups for four)
   const int kl = c.lane & (g.kparam_bytes / 8 - 1);
   const int vl = c.lane & (g.tile_vparam_bytes / 4 - 1);
   // stage key params (one slot per window) and value params (one slot per tile)
@@ -475,14 +475,22 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     s[j] = floatx4{z + row_bias[0], z + row_bias[1], z + row_bias[2], z + row_bias[3]};
   }
   const int qrow = (c.is_lo ? G : 0) + c.hc;
+  // the q*s operands are read two steps ahead of their MFMA, so that LDS
+  // latency overlaps the matrix-core work instead of preceding every op
+  auto bq_at = [&](int idx) {
+    const int kb = idx / QT, j = idx % QT;
+    return *(const half8 *)(c.qs_lds + (qt_win(j, tpw) * 2 * G + qrow) * QSTR<D> + kb * 32 + c.lq * 8);
+  };
+  half8 bqa = bq_at(0), bqb = bq_at(1);
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int j = 0; j < QT; ++j) {
-      const half8 bq = *(const half8 *)(c.qs_lds + (qt_win(j, tpw) * 2 * G + qrow) * QSTR<D> + kb * 32 + c.lq * 8);
-      const uint32_t kw = (kb >> 1) == 0 ? buf.code[j].x : buf.code[j].y;
-      s[j] = mfma_f16_k32(codes8(code_half(kw, kb & 1)), bq, s[j]);
-    }
+  for (int idx = 0; idx < KB * QT; ++idx) {
+    const int kb = idx / QT, j = idx % QT;
+    const half8 bq = bqa;
+    bqa = bqb;
+    if (idx + 2 < KB * QT) bqb = bq_at(idx + 2);
+    const uint32_t kw = (kb >> 1) == 0 ? buf.code[j].x : buf.code[j].y;
+    s[j] = mfma_f16_k32(codes8(code_half(kw, kb & 1)), bq, s[j]);
+  }
 #pragma unroll
   for (int j = 0; j < QT; ++j)
 #pragma unroll
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int lq = lane >> 4;
-  const int G = g.G;
+  constexpr int G = GP == 2 ? 4 : 8;   // the launcher passes GP = 2 exactly when G = 4 (G is 4 or 8)
   // Columns 0..7 take the high limb of quantized-tile scores, 8..15 the low
   // limb; within each half column c serves head (c mod 8) mod G, so with
   // fewer than 8 heads every head appears in several columns (identical
