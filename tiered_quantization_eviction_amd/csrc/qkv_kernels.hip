@@ -437,17 +437,19 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   // once per (head, channel) in the compact layout and stored [limb][head][c]
   {
     const int c0 = 8 * ((c.lane & 15) % (D / 8));
+    half8 s8[QT];   // all slots are staged (spare ones repeat slot 0), so the reads go out together
+#pragma unroll
+    for (int w = 0; w < QT; ++w) s8[w] = *(const half8 *)(c.kp_lds + w * PSTR<D> + c0);
 #pragma unroll
     for (int w = 0; w < QT; ++w) {
       if (w < nws) {
-        const half8 s8 = *(const half8 *)(c.kp_lds + w * PSTR<D> + c0);
         half_t *qs = c.qs_lds + w * 2 * G * QSTR<D>;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           if (4 * r < G) {
             const int hh = (c.lane >> 4) + 4 * r;
-            const half8 hi = qc[r] * s8;
-            const half8 lo = __builtin_elementwise_fma(qc[r], s8, -hi);
+            const half8 hi = qc[r] * s8[w];
+            const half8 lo = __builtin_elementwise_fma(qc[r], s8[w], -hi);
             *(half8 *)(qs + hh * QSTR<D> + c0) = hi;
             *(half8 *)(qs + (G + hh) * QSTR<D> + c0) = lo;
           }
@@ -461,11 +463,11 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   // the term of window slot i % nws for the lane's column (high columns only)
   floatx4 zb = {0.f, 0.f, 0.f, 0.f};
   const int zr = (c.lane & 15) % nws;
+  half8 z8[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const half8 z8 = *(const half8 *)(c.kp_lds + zr * PSTR<D> + D + kb * 32 + c.lq * 8);
-    zb = mfma_f16_k32(z8, bz[kb], zb);
-  }
+  for (int kb = 0; kb < KB; ++kb) z8[kb] = *(const half8 *)(c.kp_lds + zr * PSTR<D> + D + kb * 32 + c.lq * 8);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) zb = mfma_f16_k32(z8[kb], bz[kb], zb);
   // scores of the QT tiles: column h takes the high limb, column 8+h the low
   // limb, one MFMA per k-block; the two are folded after the last k-block
   floatx4 s[QT];
@@ -521,10 +523,25 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     const int slot = (c.lq < qb.nwin && c.col < G) ? qb.e + c.lq : g.U;
     *(float2 *)(c.mass_row + ((size_t)slot * G + (c.col & (G - 1))) * 2) = make_float2(rho, ws.m);
   }
+  // value steps and zeros of the lane's tokens (all tiles, all group
+  // batches): the LDS reads go out before the limb arithmetic below
+  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
+  half4 sv[QT][NG / GP], zv[QT];
+  {
+    const int zc = c.col < NG ? c.col : 0;
+#pragma unroll
+    for (int j = 0; j < QT; ++j) {
+#pragma unroll
+      for (int gi = 0; gi < NG / GP; ++gi) {
+        const int grp_l = gi * GP + (GP == 1 ? 0 : c.slot);
+        sv[j][gi] = *(const half4 *)(c.vp_lds + j * PSTR<D> + (c.lq * NG + grp_l) * 8);
+      }
+      zv[j] = *(const half4 *)(c.vp_lds + j * PSTR<D> + (c.lq * NG + zc) * 8 + 4);
+    }
+  }
   // fp16 limbs of p; (P1, P2) = (0, phi) on hi lanes, (phi, plo) on lo lanes:
   // one FMA chain then yields fp16(p*s) on hi rows and the remainder on lo rows
   half4 P1[QT], P2[QT];
-  const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
   const uint32_t lo_keep = c.is_lo ? 0xffffffffu : 0u;
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
@@ -551,9 +568,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     const int j0 = 2 * pp, j1 = 2 * pp + 1;
 #pragma unroll
     for (int gb = 0; gb < NG; gb += GP) {
-      const int grp_l = gb + (GP == 1 ? 0 : c.slot);
-      const half4 s40 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + grp_l) * 8);
-      const half4 s41 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + grp_l) * 8);
+      const half4 s40 = sv[j0][gb / GP], s41 = sv[j1][gb / GP];
       const half4 t0 = P1[j0] * s40, t1 = P1[j1] * s41;
       const half4 ag0 = __builtin_elementwise_fma(P2[j0], s40, __builtin_elementwise_fma(P1[j0], s40, -t0));
       const half4 ag1 = __builtin_elementwise_fma(P2[j1], s41, __builtin_elementwise_fma(P1[j1], s41, -t1));
@@ -574,11 +589,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
         ws.acc[ct] = mfma_f16_k32(ag, bc, ws.acc[ct]);
       }
     }
-    half4 bz0 = zero4, bz1 = zero4;
-    if (c.col < NG) {
-      bz0 = *(const half4 *)(c.vp_lds + j0 * PSTR<D> + (c.lq * NG + c.col) * 8 + 4);
-      bz1 = *(const half4 *)(c.vp_lds + j1 * PSTR<D> + (c.lq * NG + c.col) * 8 + 4);
-    }
+    const half4 bz0 = c.col < NG ? zv[j0] : zero4, bz1 = c.col < NG ? zv[j1] : zero4;
     ws.zacc = mfma_f16_k32(__builtin_shufflevector(P2[j0], P2[j1], 0, 1, 2, 3, 4, 5, 6, 7),
                            __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
   }
