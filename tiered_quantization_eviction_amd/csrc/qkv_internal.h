@@ -199,6 +199,7 @@ struct TokState {
   // HqeKV
   float *vrange;        // [B][Hkv][T] max - min of the token's original value row
   uint8_t *qrec;        // [B][Hkv][T][rec_bytes]
+  uint8_t *hqold;       // [B][Hkv][T] level + 1 a token held before the last event, until it is re-quantized (0: none)
   uint8_t *qtiles[3];   // [B][Hkv][NCT][qtile_bytes] compact INT4 / INT2 / INT1 tiles
   int32_t *qpos[3];     // [B][Hkv][NCT*TS] their positions
   int32_t *cnt;         // [B][Hkv][4] tokens per ranked tier (BF16, INT4, INT2, INT1)

@@ -61,6 +61,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.qrec = nullptr;
   st.cnt = nullptr;
   st.cuts = nullptr;
+  st.hqold = nullptr;
   for (int k = 0; k < 3; ++k) {
     st.qtiles[k] = nullptr;
     st.qpos[k] = nullptr;
@@ -74,6 +75,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
     }
     st.cnt = (int32_t *)take(BH * 4 * 4);
     st.cuts = (unsigned long long *)take(BH * 4 * 8);
+    st.hqold = (uint8_t *)take(BH * g.T);
   }
   return off;
 }
@@ -1102,93 +1104,139 @@ __device__ __forceinline__ int rec_vc(const TokGeom &g) { return g.d / 2; }
 __device__ __forceinline__ int rec_kp(const TokGeom &g) { return g.d; }
 __device__ __forceinline__ int rec_vp(const TokGeom &g) { return g.d + (g.d / 32) * 4; }
 
-// current float32 value of channel c of a token's key (w = 0) or value (w = 1) row
-__device__ float hq_current(const TokGeom &g, const TokState &st, int b, int h, int pos, int level, int w, int c) {
-  if (level == HQ_BF16) {
-    const uint16_t *t = st.pages + tok_page_offset(g, b, h, pos / TS) + (w ? TS * g.d : 0);
-    return bf16_to_f32(t[w ? v_tile_index(pos % TS, c) : k_tile_index(pos % TS, c)]);
-  }
-  const uint8_t *rec = st.qrec + (((size_t)b * g.Hkv + h) * g.T + pos) * g.rec_bytes;
-  const uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
-  const uint16_t *par = (const uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
-  if (level == HQ_INT1) {
-    const uint32_t bit = (codes[c >> 3] >> (c & 7)) & 1u;
-    const float m = (float)__builtin_bit_cast(half_t, par[0]), sd = (float)__builtin_bit_cast(half_t, par[1]);
-    return __builtin_fmaf(bit ? KAPPA1 : -KAPPA1, sd, m);
-  }
-  const int bits = level == HQ_INT4 ? 4 : 2;
-  const int per = 8 / bits;
-  const uint32_t code = (codes[c / per] >> (bits * (c % per))) & ((1u << bits) - 1u);
-  const int grp = c / 32;
-  const float s = (float)__builtin_bit_cast(half_t, par[2 * grp]), z = (float)__builtin_bit_cast(half_t, par[2 * grp + 1]);
-  return __builtin_fmaf((float)code, s, z);
-}
-
-// Re-quantize one token row (keys w = 0, values w = 1) from `old` to `level`,
-// one wave per row: lane l handles channels l and l + 64.  The current values
-// are read first (all of them), then the record is written.
-__device__ void hq_requant_row(const TokGeom &g, TokState &st, int b, int h, int pos, int old, int level, int w,
-                               int lane) {
-  const int D = g.d;
-  const int n_per = D / 64;   // channels per lane: 1 or 2
-  float x[2];
+// Re-quantization of the tokens an assignment event moved to a quantized
+// tier.  Each token row (keys, values) is handled by 16 lanes, lane i owning
+// channels CPL*i .. CPL*i + CPL-1 (CPL = d/16), so a wave rebuilds two tokens
+// at a time and the whole grid works through the changed tokens of every
+// (sequence, KV head).  The current values are read first (float32: the bf16
+// page, or the dequantized record of the previous level), then the record is
+// written in canonical per-token packing.
+template <int D>
+__global__ __launch_bounds__(256) void hq_requant_kernel(TokGeom g, TokState st, int elig_end) {
+  constexpr int CPL = D / 16;                // channels per lane
+  constexpr int LPG = 32 / CPL;              // lanes per 32-channel group
+  const int bh = blockIdx.y;
+  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const size_t tb = (size_t)bh * g.T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp16 = lane >> 4, li = lane & 15;  // 16-lane group: token grp16/2, row grp16%2
+  const int w = grp16 & 1;
+  const int c0 = CPL * li;
+  const int base = (blockIdx.x * 4 + wave) * 64;
+  const int mypos = base + lane;
+  const bool pending = mypos < elig_end && st.hqold[tb + mypos] != 0;
+  unsigned long long todo = __ballot(pending);
+  while (todo) {
+    // two tokens per pass (the second may repeat the first when one is left)
+    const int l0 = __builtin_ctzll(todo);
+    todo &= todo - 1;
+    const int l1 = todo ? __builtin_ctzll(todo) : l0;
+    if (todo) todo &= todo - 1;
+    const int pos = base + ((grp16 >> 1) ? l1 : l0);
+    const int old = (int)st.hqold[tb + pos] - 1;
+    const int lvl = hq_level(st.tier[tb + pos]);
+    // ---- current values of this lane's channels ----
+    float x[CPL];
+    uint8_t *rec = st.qrec + (tb + pos) * g.rec_bytes;
+    if (old == HQ_BF16) {
+      const uint16_t *kt = st.pages + tok_page_offset(g, b, h, pos / TS);
+      const int t = pos % TS;
+      if (w == 0) {
+        const uint16_t *src = kt + k_tile_index(t, c0);   // CPL consecutive channels
 #pragma unroll
-  for (int j = 0; j < 2; ++j) x[j] = j < n_per ? hq_current(g, st, b, h, pos, old, w, lane + 64 * j) : 0.0f;
-  __builtin_amdgcn_wave_barrier();
-  uint8_t *rec = st.qrec + (((size_t)b * g.Hkv + h) * g.T + pos) * g.rec_bytes;
-  uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
-  uint16_t *par = (uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
-  if (level == HQ_INT1) {
-    // mean and population deviation in float64, rounded to float32, then fp16
-    double sum = 0.0;
-    for (int j = 0; j < n_per; ++j) sum += (double)x[j];
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    const float m32 = (float)(sum / D);
-    double ss = 0.0;
-    for (int j = 0; j < n_per; ++j) {
-      const double dv = (double)x[j] - (double)m32;
-      ss += dv * dv;
+        for (int e = 0; e < CPL; ++e) x[e] = bf16_to_f32(src[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) x[e] = bf16_to_f32(kt[TS * D + v_tile_index(t, c0 + e)]);
+      }
+    } else {
+      const uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
+      const uint16_t *par = (const uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
+      if (old == HQ_INT1) {
+        const uint32_t bits = codes[c0 >> 3] >> (c0 & 7);
+        const float m = (float)__builtin_bit_cast(half_t, par[0]), sd = (float)__builtin_bit_cast(half_t, par[1]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) x[e] = __builtin_fmaf(((bits >> e) & 1u) ? KAPPA1 : -KAPPA1, sd, m);
+      } else {
+        const int bits = old == HQ_INT4 ? 4 : 2;
+        uint32_t word = 0u;   // the lane's CPL codes, bits * CPL <= 32
+#pragma unroll
+        for (int k = 0; k < CPL * 4 / 8; ++k)
+          if (k * 8 < bits * CPL) word |= (uint32_t)codes[c0 * bits / 8 + k] << (8 * k);
+        const int gi = c0 >> 5;
+        const float sc = (float)__builtin_bit_cast(half_t, par[2 * gi]);
+        const float zc = (float)__builtin_bit_cast(half_t, par[2 * gi + 1]);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          x[e] = __builtin_fmaf((float)((word >> (bits * e)) & ((1u << bits) - 1u)), sc, zc);
+      }
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    const float sd32 = (float)sqrt(ss / D);
-    const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
-    if (!isfinite((float)m16) || !isfinite((float)sd16)) st.status[0] = QKV_ERANGE;
-    // codes: bit c = x_c > mean; bytes assembled by ballots
-    for (int j = 0; j < n_per; ++j) {
-      const unsigned long long bal = __ballot((double)x[j] > (double)m32);
-      if (lane < 8) codes[8 * j + lane] = (uint8_t)(bal >> (8 * lane));
+    __builtin_amdgcn_wave_barrier();
+    // ---- new record (all reads of this token are done) ----
+    uint8_t *codes = rec + (w ? rec_vc(g) : rec_kc(g));
+    uint16_t *par = (uint16_t *)(rec + (w ? rec_vp(g) : rec_kp(g)));
+    if (lvl == HQ_INT1) {
+      // mean and population deviation in float64 over the row, rounded to float32, then fp16
+      double sum = 0.0;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) sum += (double)x[e];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+      const float m32 = (float)(sum / D);
+      double ss = 0.0;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const double dv = (double)x[e] - (double)m32;
+        ss += dv * dv;
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
+      const float sd32 = (float)sqrt(ss / D);
+      const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
+      if (!isfinite((float)m16) || !isfinite((float)sd16)) st.status[0] = QKV_ERANGE;
+      uint32_t cb = 0u;   // bit c of the row: x_c > mean
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) cb |= ((double)x[e] > (double)m32 ? 1u : 0u) << e;
+      if (CPL == 8) {
+        codes[c0 >> 3] = (uint8_t)cb;
+      } else {   // four channels per lane: lane pairs share a byte
+        const uint32_t other = __shfl_xor(cb, 1);
+        if ((li & 1) == 0) codes[c0 >> 3] = (uint8_t)(cb | (other << 4));
+      }
+      if (li == 0) {
+        par[0] = __builtin_bit_cast(uint16_t, m16);
+        par[1] = __builtin_bit_cast(uint16_t, sd16);
+      }
+    } else {
+      const int bits = lvl == HQ_INT4 ? 4 : 2;
+      const float levels = (float)((1 << bits) - 1);
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int e = 1; e < CPL; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+      }
+#pragma unroll
+      for (int off = 1; off < LPG; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      const half_t s16 = (half_t)((mx - mn) / levels);
+      const half_t z16 = (half_t)mn;
+      if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
+      uint32_t word = 0u;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) word |= quant_code(x[e], s16, z16, levels) << (bits * e);
+#pragma unroll
+      for (int k = 0; k < CPL * 4 / 8; ++k)
+        if (k * 8 < bits * CPL) codes[c0 * bits / 8 + k] = (uint8_t)(word >> (8 * k));
+      if ((li % LPG) == 0) {
+        const int gi = c0 >> 5;
+        par[2 * gi] = __builtin_bit_cast(uint16_t, s16);
+        par[2 * gi + 1] = __builtin_bit_cast(uint16_t, z16);
+      }
     }
-    if (lane == 0) {
-      par[0] = __builtin_bit_cast(uint16_t, m16);
-      par[1] = __builtin_bit_cast(uint16_t, sd16);
-    }
-    return;
-  }
-  const int bits = level == HQ_INT4 ? 4 : 2;
-  const float levels = (float)((1 << bits) - 1);
-  for (int j = 0; j < n_per; ++j) {
-    // group of 32 channels: lanes 32*(lane/32) .. +31 of channel chunk j
-    float mn = x[j], mx = x[j];
-    for (int off = 16; off > 0; off >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
-    const half_t s16 = (half_t)((mx - mn) / levels);
-    const half_t z16 = (half_t)mn;
-    if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
-    const uint32_t code = quant_code(x[j], s16, z16, levels);
-    // pack: element c at bit bits*(c mod per) of byte c/per
-    const int c = lane + 64 * j;
-    const int per = 8 / bits;
-    uint32_t byte = code << (bits * (c % per));
-    // combine the per lanes of one byte (lanes c/per*per .. +per-1 are adjacent)
-    for (int off = 1; off < per; off <<= 1) byte |= __shfl_xor(byte, off);
-    if (c % per == 0) codes[c / per] = (uint8_t)byte;
-    const int grp = c / 32;
-    if (c % 32 == 0) {
-      par[2 * grp] = __builtin_bit_cast(uint16_t, s16);
-      par[2 * grp + 1] = __builtin_bit_cast(uint16_t, z16);
-    }
+    if (li == 0 && w == 0) st.hqold[tb + pos] = 0;
   }
 }
 
@@ -1261,31 +1309,22 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
     st.cuts[bh * 4 + tid] = thr[tid];
   }
   __syncthreads();
-  // targets, downgrade only, re-quantization (one wave per changed token)
+  // targets, downgrade only: a token that moves takes its new tier now; one
+  // that moves to a quantized tier keeps its previous level in hqold until
+  // hq_requant_kernel has rebuilt its record from its current values
   const int wave = tid >> 6, lane = tid & 63, n_waves = blockDim.x >> 6;
-  for (int base = 0; base < elig_end; base += 64 * n_waves) {
-    const int pos = base + wave * 64 + lane;
-    int old = HQ_EVICT, nw = HQ_EVICT;
-    if (pos < elig_end && eligible(pos)) {
-      const unsigned long long key = keyof(pos);
-      int target = 0;
+  for (int pos = tid; pos < elig_end; pos += blockDim.x) {
+    if (!eligible(pos)) continue;
+    const unsigned long long key = keyof(pos);
+    int target = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
-      old = hq_level(st.tier[tb + pos]);
-      nw = max(old, target);
-    }
-    // the wave walks its changed tokens one by one
-    unsigned long long todo = __ballot(pos < elig_end && nw > old);
-    while (todo) {
-      const int l = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const int p = __shfl(pos, l), o = __shfl(old, l), n2 = __shfl(nw, l);
-      if (n2 != HQ_EVICT) {
-        hq_requant_row(g, st, b, h, p, o, n2, 0, lane);
-        hq_requant_row(g, st, b, h, p, o, n2, 1, lane);
-      }
-      if (lane == 0) st.tier[tb + p] = hq_code(n2);
+    for (int j = 0; j < 4; ++j)
+      if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
+    const int old = hq_level(st.tier[tb + pos]);
+    const int nw = max(old, target);
+    if (nw > old) {
+      st.tier[tb + pos] = hq_code(nw);
+      if (nw != HQ_EVICT) st.hqold[tb + pos] = (uint8_t)(old + 1);
     }
   }
   __syncthreads();
@@ -1464,6 +1503,14 @@ hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig
                      counts[2], counts[3]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (elig_end > 0) {
+    const dim3 rgrid((elig_end + 255) / 256, g.B * g.Hkv);
+    if (g.d == 128)
+      hipLaunchKernelGGL(hq_requant_kernel<128>, rgrid, dim3(256), 0, s, g, st, elig_end);
+    else
+      hipLaunchKernelGGL(hq_requant_kernel<64>, rgrid, dim3(256), 0, s, g, st, elig_end);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const dim3 grid(64, g.B * g.Hkv);
   if (g.d == 128)
     hipLaunchKernelGGL(hq_gather_kernel<128>, grid, dim3(256), 0, s, g, st);
