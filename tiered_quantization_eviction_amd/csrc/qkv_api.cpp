@@ -364,6 +364,12 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
 int qkv_route(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
+  if (c->tok) {
+    // masses accumulated in list order reach the per-token scores first
+    const TokStep ts = {c->N, c->r_tok, c->n_cmp};
+    int rc = hip_err(tok_launch_flush(c->tg, c->ts, ts, (hipStream_t)stream));
+    if (rc != QKV_OK) return rc;
+  }
   if (c->tok && c->tg.policy == QKV_POLICY_HQEKV) {
     // assignment event: tokens ranked before (all live ones at the first
     // event) get target tiers by their rank; shares floor(r_k * N) of all
@@ -477,7 +483,14 @@ int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_st
   if (!c || !dst) return QKV_EINVAL;
   const size_t need = qkv_export_bytes(c, what);
   if (need == 0 || bytes != need) return QKV_EINVAL;
-  if (c->tok) return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
+  if (c->tok) {
+    if (what == QKV_EXPORT_SCORES && c->N > 0) {
+      const TokStep ts = {c->N, c->r_tok, c->n_cmp};
+      int rc = hip_err(tok_launch_flush(c->tg, c->ts, ts, (hipStream_t)stream));
+      if (rc != QKV_OK) return rc;
+    }
+    return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
+  }
   return hip_err(launch_export(c->g, c->st, what, dst, (hipStream_t)stream));
 }
 

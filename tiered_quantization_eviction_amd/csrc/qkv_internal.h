@@ -161,6 +161,8 @@ __host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 //   mrho f32 [B][Hkv][TILES+1][G][TS]    per live tile and head: p of each slot
 //   mref f32 [B][Hkv][TILES+1][G]        ... and the running max it is relative
 //                to (row TILES is the spare row unused lanes write to)
+//   tacc f32 [B][Hkv][TILES][TS]         masses summed in list order since the
+//                last flush into score (flushed before a route or an export)
 // ---------------------------------------------------------------------------
 
 // HqeKV tiers of a ranked token (the per-token state of the five-tier method)
@@ -194,6 +196,7 @@ struct TokState {
   float *part_ml;    // [B][Hkv][S][G][2]
   float *mrho;
   float *mref;
+  float *tacc;       // [B][Hkv][TILES][TS] masses added since the last flush, in list order
   float *scratch_out;   // [B][Hq][d] outputs of scoring-only passes
   int32_t *status;
   // HqeKV
@@ -244,6 +247,7 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
 hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep &ts, int a0, int a1, int n_cand,
                             hipStream_t s);
 hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, void *dst, hipStream_t s);
+hipError_t tok_launch_flush(const TokGeom &g, const TokState &st, const TokStep &ts, hipStream_t s);
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
                            hipStream_t s);
 

@@ -22,7 +22,10 @@
 // split into two fp16 limbs, so the 16x16x32 fp16 operations keep about 22
 // bits.  Each token slot's probability is emitted relative to the running
 // maximum; the merge kernel normalizes those with the global (max, sum) of
-// each head and adds them into the per-token scores in a fixed order.
+// each head and adds each token's mass into an accumulator kept in list order
+// (coalesced; the lists only change at routing calls).  Before a routing call
+// or an export of the scores, the accumulators are added into the per-token
+// scores and cleared.
 #include <hip/hip_ext.h>
 
 #include "qkv_device.h"
@@ -55,6 +58,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.part_ml = (float *)take(BH * g.n_splits * g.G * 2 * 4);
   st.mrho = (float *)take(BH * (g.TILES + 1) * g.G * TS * 4);
   st.mref = (float *)take(BH * (g.TILES + 1) * g.G * 4);
+  st.tacc = (float *)take(BH * g.TILES * TS * 4);
   st.scratch_out = (float *)take((size_t)g.B * g.Hq * g.d * 4);
   st.status = (int32_t *)take(16);
   st.vrange = nullptr;
@@ -191,6 +195,27 @@ __device__ __forceinline__ const uint16_t *tok_ftile(const TokGeom &g, const Tok
   lo = max(ts.rstart - rt * TS, 0);
   hi = min(ts.N - rt * TS, TS);
   return st.pages + tok_page_offset(g, b, h, rt);
+}
+
+// position of slot `slot` of list tile k of (sequence, KV head) bh; -1 when
+// the slot holds no token.  Without LOOKUP only validity is decided (0).
+template <bool LOOKUP>
+__device__ __forceinline__ int tok_slot_pos(const TokGeom &g, const TokState &st, const TokStep &ts, const TokList &L,
+                                            int bh, int k, int slot) {
+  if (k < L.s0 + L.nC || k >= L.base_r()) {
+    int lo, hi;
+    (void)tok_ftile(g, st, ts, L, bh / g.Hkv, bh % g.Hkv, k, lo, hi);
+    if (slot < lo || slot >= hi) return -1;
+    if (!LOOKUP) return 0;
+    if (k < L.s0) return slot;
+    if (k < L.s0 + L.nC) return st.cpos[(size_t)bh * g.NCT * TS + (k - L.s0) * TS + slot];
+    return (L.rt0 + (k - L.base_r())) * TS + slot;
+  }
+  int f = 0;
+  while (k >= L.base_q(f + 1)) ++f;
+  const int idx = (k - L.base_q(f)) * TS + slot;
+  if (idx >= L.nQtok[f]) return -1;
+  return LOOKUP ? st.qpos[f][(size_t)bh * g.NCT * TS + idx] : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -858,24 +883,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // merge: outputs per (sequence, KV head); per-token masses -> scores
 // ---------------------------------------------------------------------------
 
-__device__ inline void tok_split_stats(const TokGeom &g, const TokState &st, int bh, int hh, float &M, float &invL) {
-  const int S = g.n_splits, G = g.G;
-  const float *ml = st.part_ml + ((size_t)bh * S * G + hh) * 2;
+// global (max, 1/sum) of each head of (sequence, KV head) bh over the
+// splits, for the whole block: the splits' pairs are staged in LDS by all
+// threads at once, then combined in split order by thread hh < G
+template <int G>
+__device__ inline void tok_split_stats(const TokGeom &g, const TokState &st, int bh, float *sM, float *sInvL) {
+  __shared__ float2 sml[256];
+  constexpr int PER = 256 / G;   // splits staged per round
+  const int S = g.n_splits, tid = threadIdx.x;
+  const float2 *ml = (const float2 *)st.part_ml + (size_t)bh * S * G;
   float m = neg_inf(), l = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = ml[(size_t)s * G * 2], ls = ml[(size_t)s * G * 2 + 1];
-    if (ms == neg_inf()) continue;
-    const float mn = fmaxf(m, ms);
-    l = (m == neg_inf() ? 0.0f : l * exp2f(m - mn)) + ls * exp2f(ms - mn);
-    m = mn;
+  for (int r0 = 0; r0 < S; r0 += PER) {
+    const int ns = min(S - r0, PER);
+    if (tid < ns * G) sml[tid] = ml[(size_t)r0 * G + tid];
+    __syncthreads();
+    if (tid < G) {
+      for (int s = 0; s < ns; ++s) {
+        const float2 v = sml[s * G + tid];
+        if (v.x == neg_inf()) continue;
+        const float mn = fmaxf(m, v.x);
+        l = (m == neg_inf() ? 0.0f : l * exp2f(m - mn)) + v.y * exp2f(v.x - mn);
+        m = mn;
+      }
+    }
+    __syncthreads();
   }
-  M = m;
-  invL = 1.0f / l;
+  if (tid < G) {
+    sM[tid] = m;
+    sInvL[tid] = 1.0f / l;
+  }
+  __syncthreads();
 }
 
 template <int G>
 __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, TokStep ts, float *__restrict__ out,
-                                                        float *__restrict__ mass_out, int n_chunks) {
+                                                        float *__restrict__ mass_out, int n_parts) {
   constexpr int CH = 8;
   const int S = g.n_splits, D = g.d;
   const int n_out_blocks = g.B * g.Hkv;
@@ -910,47 +952,80 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
     }
     return;
   }
-  // masses: 256 token slots (16 tiles) of one (sequence, KV head) per block
+  // masses: block `part` of n_parts per (sequence, KV head) strides over its
+  // live tiles, four token slots per thread
   __shared__ float sM[G], sInvL[G];
   const int mb = blockIdx.x - n_out_blocks;
-  const int bh = mb / n_chunks, chunk = mb % n_chunks;
-  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const int bh = mb / n_parts, part = mb % n_parts;
+  tok_split_stats<G>(g, st, bh, sM, sInvL);
   const TokList L = tok_list(g, st, ts, bh);
-  const int k = chunk * (256 / TS) + (int)threadIdx.x / TS;   // tile
-  const int slot = threadIdx.x % TS;
-  if ((int)threadIdx.x < G) tok_split_stats(g, st, bh, threadIdx.x, sM[threadIdx.x], sInvL[threadIdx.x]);
-  __syncthreads();
-  if (k >= L.count()) return;
-  int pos = -1;
-  if (k < L.s0 + L.nC || k >= L.base_r()) {
-    int lo, hi;
-    (void)tok_ftile(g, st, ts, L, b, h, k, lo, hi);
-    if (slot < lo || slot >= hi) return;
-    if (k < L.s0)
-      pos = slot;
-    else if (k < L.s0 + L.nC)
-      pos = st.cpos[(size_t)bh * g.NCT * TS + (k - L.s0) * TS + slot];
-    else
-      pos = (L.rt0 + (k - L.base_r())) * TS + slot;
-  } else {
-    int f = 0;
-    while (k >= L.base_q(f + 1)) ++f;
-    const int idx = (k - L.base_q(f)) * TS + slot;
-    if (idx >= L.nQtok[f]) return;
-    pos = st.qpos[f][(size_t)bh * g.NCT * TS + idx];
-  }
-  const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + k) * G * TS;
-  const float *ref = st.mref + ((size_t)bh * (g.TILES + 1) + k) * G;
-  float mass = 0.0f;
+  const int n_live = min(L.count(), g.TILES);
+  const int s0 = ((int)threadIdx.x % (TS / 4)) * 4;
+  for (int k = part * (256 * 4 / TS) + (int)threadIdx.x / (TS / 4); k < n_live; k += n_parts * (256 * 4 / TS)) {
+    const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + k) * G * TS + s0;
+    const float *ref = st.mref + ((size_t)bh * (g.TILES + 1) + k) * G;
+    float4 *accp = (float4 *)(st.tacc + ((size_t)bh * g.TILES + k) * TS + s0);
+    float4 r[G];
+    float w[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float v = rho[hh * TS + slot] * exp2f(ref[hh] - sM[hh]) * sInvL[hh];
-    if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
-    mass += v;
+    for (int hh = 0; hh < G; ++hh) r[hh] = *(const float4 *)(rho + hh * TS);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) w[hh] = exp2f(ref[hh] - sM[hh]);
+    float4 acc = *accp;
+    float *ap = (float *)&acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = mass_out ? tok_slot_pos<true>(g, st, ts, L, bh, k, s0 + e)
+                               : tok_slot_pos<false>(g, st, ts, L, bh, k, s0 + e);
+      if (pos < 0) continue;
+      float mass = 0.0f;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float v = ((const float *)&r[hh])[e] * w[hh] * sInvL[hh];
+        if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
+        mass += v;
+      }
+      ap[e] += mass;
+      if (mass_out) mass_out[(size_t)bh * g.T + pos] = mass;
+    }
+    // list order: coalesced, and stable until the next route (which flushes first)
+    *accp = acc;
   }
-  const size_t u = (size_t)bh * g.T + pos;
-  if (mass_out) mass_out[u] = mass;
-  st.score[u] += mass;
+}
+
+// pending list-order masses -> per-token scores (before anything reads the
+// scores or a route changes the lists); the accumulators are cleared
+__global__ __launch_bounds__(256) void tok_flush_kernel(TokGeom g, TokState st, TokStep ts, int n_chunks) {
+  const int bh = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
+  const TokList L = tok_list(g, st, ts, bh);
+  const int k = chunk * (256 / TS) + (int)threadIdx.x / TS;
+  const int slot = threadIdx.x % TS;
+  if (k >= L.count() || k >= g.TILES) return;
+  float *acc = st.tacc + ((size_t)bh * g.TILES + k) * TS + slot;
+  const float a = *acc;
+  if (a == 0.0f) return;
+  const int pos = tok_slot_pos<true>(g, st, ts, L, bh, k, slot);
+  if (pos < 0) return;
+  st.score[(size_t)bh * g.T + pos] += a;
+  *acc = 0.0f;
+}
+
+namespace {
+// live tiles per (sequence, KV head): at most the ranked tokens' tiles (one
+// partial tile per tier) plus the sink and recent tiles
+int tok_live_tiles(const TokGeom &g, const TokStep &ts) {
+  const int ranked = g.policy == QKV_POLICY_HQEKV ? ts.rstart : ts.n_cmp;
+  const int n = (g.n_sink > 0 ? 1 : 0) + (ranked + TS - 1) / TS + (g.policy == QKV_POLICY_HQEKV ? 4 : 0) +
+                (ts.N > ts.rstart ? (ts.N - 1) / TS - ts.rstart / TS + 1 : 0);
+  return n > g.TILES ? g.TILES : n;
+}
+}  // namespace
+
+hipError_t tok_launch_flush(const TokGeom &g, const TokState &st, const TokStep &ts, hipStream_t s) {
+  const int n_chunks = (tok_live_tiles(g, ts) * TS + 255) / 256;
+  if (n_chunks < 1) return hipSuccess;
+  hipLaunchKernelGGL(tok_flush_kernel, dim3(g.B * g.Hkv * n_chunks), dim3(256), 0, s, g, st, ts, n_chunks);
+  return hipGetLastError();
 }
 
 hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep &ts, const uint16_t *q,
@@ -976,18 +1051,18 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
                           q, q_bstride, scale_log2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mass_out && (e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.T * sizeof(float), s)) != hipSuccess) return e;
-  // live tiles per (sequence, KV head): at most the ranked tokens' tiles
-  // (one partial tile per tier) plus the sink and recent tiles
-  const int ranked = g.policy == QKV_POLICY_HQEKV ? ts.rstart : ts.n_cmp;
-  int n_tiles = (g.n_sink > 0 ? 1 : 0) + (ranked + TS - 1) / TS + (g.policy == QKV_POLICY_HQEKV ? 4 : 0) +
-                (ts.N > ts.rstart ? (ts.N - 1) / TS - ts.rstart / TS + 1 : 0);
-  if (n_tiles > g.TILES) n_tiles = g.TILES;
-  const int n_chunks = (n_tiles * TS + 255) / 256;
-  const dim3 mgrid(g.B * g.Hkv + g.B * g.Hkv * n_chunks);
+  // mass blocks: about 2048 in all (a few per CU), at most one per 64 live tiles
+  const int BH = g.B * g.Hkv;
+  const int per_block = 256 * 4 / TS;
+  int n_parts = (tok_live_tiles(g, ts) + per_block - 1) / per_block;
+  const int want = (2048 + BH - 1) / BH;
+  if (n_parts > want) n_parts = want;
+  if (n_parts < 1) n_parts = 1;
+  const dim3 mgrid(BH + BH * n_parts);
   if (g.G == 4)
-    hipLaunchKernelGGL(tok_merge_kernel<4>, mgrid, dim3(256), 0, s, g, st, ts, out, mass_out, n_chunks);
+    hipLaunchKernelGGL(tok_merge_kernel<4>, mgrid, dim3(256), 0, s, g, st, ts, out, mass_out, n_parts);
   else
-    hipLaunchKernelGGL(tok_merge_kernel<8>, mgrid, dim3(256), 0, s, g, st, ts, out, mass_out, n_chunks);
+    hipLaunchKernelGGL(tok_merge_kernel<8>, mgrid, dim3(256), 0, s, g, st, ts, out, mass_out, n_parts);
   return hipGetLastError();
 }
 
@@ -1368,117 +1443,141 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
 
 __device__ __forceinline__ size_t tb_of(const TokGeom &g, int bh) { return (size_t)bh * g.T; }
 
-// code of channel c of a per-token record's code stream (bits b)
-__device__ __forceinline__ uint32_t rec_code(const uint8_t *codes, int c, int bits) {
-  if (bits == 1) return (codes[c >> 3] >> (c & 7)) & 1u;
-  return (codes[c * bits / 8] >> (bits * (c % (8 / bits)))) & ((1u << bits) - 1u);
+// The records (canonical per-token packing, see the re-quantization kernel)
+// of a compact tile's 16 token slots, staged in LDS by one wave with 16-byte
+// loads; slots past the tier's count read as zeros.
+template <int D>
+__device__ __forceinline__ void hq_stage_records(const uint8_t *rec0, const int32_t *qpos, int tile, int nq, int lane,
+                                                 uint8_t *lds) {
+  constexpr int R = D + (D / 32) * 8, NCH = R / 16;
+  for (int i = lane; i < TS * NCH; i += 64) {
+    const int tk = i / NCH, part = i - tk * NCH;
+    const int sl = tile * TS + tk;
+    u32x4v v = {0u, 0u, 0u, 0u};
+    if (sl < nq) v = *(const u32x4v *)(rec0 + (size_t)qpos[sl] * R + part * 16);
+    *(u32x4v *)(lds + tk * R + part * 16) = v;
+  }
+  wave_lds_sync();
 }
 
-// INT4 / INT2 tiles of one (sequence, KV head) in operand order (QL)
+template <int CW>
+__device__ __forceinline__ void store_words(uint8_t *dst, const uint32_t (&w)[CW]) {
+  if constexpr (CW == 4) {
+    *(u32x4v *)dst = u32x4v{w[0], w[1], w[2], w[3]};
+  } else if constexpr (CW == 2) {
+    *(u32x2v *)dst = u32x2v{w[0], w[1]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < CW; ++k) ((uint32_t *)dst)[k] = w[k];
+  }
+}
+
+// INT4 / INT2 tiles of one (sequence, KV head) in operand order (QL), one
+// wave per tile (tiles gw, gw + n_gw, ...)
 template <int D, int F>
-__device__ void hq_gather_ql(const TokGeom &g, const TokState &st, int bh) {
+__device__ void hq_gather_ql(const TokGeom &g, const TokState &st, int bh, uint8_t *lds, int gw, int n_gw, int lane) {
   using Q = QL<D, F>;
-  const int bits = F == 0 ? 4 : 2;
+  constexpr int R = D + (D / 32) * 8;
+  constexpr int bits = F == 0 ? 4 : 2;
+  constexpr uint32_t mask = (1u << bits) - 1u;
   const int nq = st.cnt[bh * 4 + 1 + F];
   const int ntiles = (nq + TS - 1) / TS;
   uint8_t *tiles = st.qtiles[F] + (size_t)bh * g.NCT * Q::BYTES;
   const int32_t *qpos = st.qpos[F] + (size_t)bh * g.NCT * TS;
-  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * g.rec_bytes;
-  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
-    const int tile = it / 64, lane = it % 64;
+  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * R;
+  const int t = lane & 15, lq = lane >> 4;
+  for (int tile = gw; tile < ntiles; tile += n_gw) {
+    hq_stage_records<D>(rec0, qpos, tile, nq, lane, lds);
     uint8_t *T = tiles + (size_t)tile * Q::BYTES;
-    const int t = lane & 15, lq = lane >> 4;
-    // keys: token slot t, channels kb*32 + 8*lq + e
-    uint32_t kw[Q::CW];
+    // keys: token slot t, channels kb*32 + 8*lq + e (one code word per k-block)
+    uint32_t kw[Q::CW], vw[Q::CW];
 #pragma unroll
-    for (int w = 0; w < Q::CW; ++w) kw[w] = 0u;
-    const int ks = tile * TS + t;
-    if (ks < nq) {
-      const uint8_t *rec = rec0 + (size_t)qpos[ks] * g.rec_bytes;
-      for (int kb = 0; kb < Q::KB; ++kb)
-        for (int e = 0; e < 8; ++e) {
-          int dw, bit;
-          ql_kslot<F>(kb, e, dw, bit);
-          kw[dw] |= rec_code(rec, kb * 32 + 8 * lq + e, bits) << bit;
-        }
+    for (int w = 0; w < Q::CW; ++w) kw[w] = vw[w] = 0u;
+#pragma unroll
+    for (int kb = 0; kb < Q::KB; ++kb) {
+      const uint32_t x = F == 0 ? *(const uint32_t *)(lds + t * R + 16 * kb + 4 * lq)
+                                : (uint32_t) * (const uint16_t *)(lds + t * R + 8 * kb + 2 * lq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int dw, bit;
+        ql_kslot<F>(kb, e, dw, bit);
+        kw[dw] |= ((x >> (bits * e)) & mask) << bit;
+      }
     }
+    // values: channel ct*16 + t of token slots 4*lq + tt
+    const int vsh = bits * (t % (8 / bits)), vby = t * bits / 8;
 #pragma unroll
-    for (int w = 0; w < Q::CW; ++w) ((uint32_t *)(T + lane * 4 * Q::CW))[w] = kw[w];
-    // values: channel ct*16 + t, token slots 4*lq + tt
-    uint32_t vw[Q::CW];
-#pragma unroll
-    for (int w = 0; w < Q::CW; ++w) vw[w] = 0u;
     for (int tt = 0; tt < 4; ++tt) {
-      const int vs = tile * TS + 4 * lq + tt;
-      if (vs >= nq) continue;
-      const uint8_t *rec = rec0 + (size_t)qpos[vs] * g.rec_bytes + D / 2;
+      const uint8_t *vr = lds + (4 * lq + tt) * R + D / 2 + vby;
+#pragma unroll
       for (int ct = 0; ct < Q::CT; ++ct) {
         int dw, bit;
         ql_vslot<F>(ct, tt, dw, bit);
-        vw[dw] |= rec_code(rec, ct * 16 + t, bits) << bit;
+        vw[dw] |= (((uint32_t)vr[ct * 16 * bits / 8] >> vsh) & mask) << bit;
       }
     }
-#pragma unroll
-    for (int w = 0; w < Q::CW; ++w) ((uint32_t *)(T + Q::VC + lane * 4 * Q::CW))[w] = vw[w];
+    store_words<Q::CW>(T + lane * 4 * Q::CW, kw);
+    store_words<Q::CW>(T + Q::VC + lane * 4 * Q::CW, vw);
     // params of token slot t, written by the lanes of row lq == 0
     if (lq == 0) {
-      const int sl = tile * TS + t;
-      const uint16_t *par = sl < nq ? (const uint16_t *)(rec0 + (size_t)qpos[sl] * g.rec_bytes + D) : nullptr;
+      const uint16_t *par = (const uint16_t *)(lds + t * R + D);
       uint16_t *ksc = (uint16_t *)(T + Q::KS), *kzr = (uint16_t *)(T + Q::KZ);
       uint16_t *vsc = (uint16_t *)(T + Q::VS), *vzr = (uint16_t *)(T + Q::VZ);
+#pragma unroll
       for (int gi = 0; gi < Q::NG; ++gi) {
-        ksc[gi * TS + t] = par ? par[2 * gi] : 0;
-        kzr[t * Q::NG + gi] = par ? par[2 * gi + 1] : 0;
-        vsc[gi * TS + t] = par ? par[2 * Q::NG + 2 * gi] : 0;
-        vzr[gi * TS + t] = par ? par[2 * Q::NG + 2 * gi + 1] : 0;
+        ksc[gi * TS + t] = par[2 * gi];
+        kzr[t * Q::NG + gi] = par[2 * gi + 1];
+        vsc[gi * TS + t] = par[2 * Q::NG + 2 * gi];
+        vzr[gi * TS + t] = par[2 * Q::NG + 2 * gi + 1];
       }
     }
+    wave_lds_sync();   // the next tile's records overwrite these
   }
 }
 
-// INT1 tiles of one (sequence, KV head) (Q1 layout)
+// INT1 tiles of one (sequence, KV head) (Q1 layout), one wave per tile
 template <int D>
-__device__ void hq_gather_q1(const TokGeom &g, const TokState &st, int bh) {
+__device__ void hq_gather_q1(const TokGeom &g, const TokState &st, int bh, uint8_t *lds, int gw, int n_gw, int lane) {
   using Q = Q1<D>;
+  constexpr int R = D + (D / 32) * 8;
   const int nq = st.cnt[bh * 4 + 3];
   const int ntiles = (nq + TS - 1) / TS;
   uint8_t *tiles = st.qtiles[2] + (size_t)bh * g.NCT * Q::BYTES;
   const int32_t *qpos = st.qpos[2] + (size_t)bh * g.NCT * TS;
-  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * g.rec_bytes;
-  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < ntiles * 64; it += gridDim.x * blockDim.x) {
-    const int tile = it / 64, lane = it % 64;
+  const uint8_t *rec0 = st.qrec + tb_of(g, bh) * R;
+  const int t = lane & 15, lq = lane >> 4;
+  for (int tile = gw; tile < ntiles; tile += n_gw) {
+    hq_stage_records<D>(rec0, qpos, tile, nq, lane, lds);
     uint8_t *T = tiles + (size_t)tile * Q::BYTES;
-    const int t = lane & 15, lq = lane >> 4;
-    uint32_t kw = 0u;
-    const int ks = tile * TS + t;
-    if (ks < nq) {
-      const uint8_t *rec = rec0 + (size_t)qpos[ks] * g.rec_bytes;
-      for (int kb = 0; kb < Q::KB; ++kb)
-        for (int e = 0; e < 8; ++e) kw |= rec_code(rec, kb * 32 + 8 * lq + e, 1) << q1_kbit(kb, e);
+    uint32_t kw = 0u, vw = 0u;
+#pragma unroll
+    for (int kb = 0; kb < Q::KB; ++kb) {
+      const uint32_t x = lds[t * R + 4 * kb + lq];   // channels kb*32 + 8*lq + e at bit e
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kw |= ((x >> e) & 1u) << q1_kbit(kb, e);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint8_t *vr = lds + (4 * lq + tt) * R + D / 2 + (t >> 3);
+#pragma unroll
+      for (int ct = 0; ct < Q::CT; ++ct) vw |= (((uint32_t)vr[2 * ct] >> (t & 7)) & 1u) << q1_vbit(ct, tt);
     }
     ((uint32_t *)T)[lane] = kw;
-    uint32_t vw = 0u;
-    for (int tt = 0; tt < 4; ++tt) {
-      const int vs = tile * TS + 4 * lq + tt;
-      if (vs >= nq) continue;
-      const uint8_t *rec = rec0 + (size_t)qpos[vs] * g.rec_bytes + D / 2;
-      for (int ct = 0; ct < Q::CT; ++ct) vw |= rec_code(rec, ct * 16 + t, 1) << q1_vbit(ct, tt);
-    }
     ((uint32_t *)(T + Q::VC))[lane] = vw;
     if (lq == 0) {
-      const int sl = tile * TS + t;
-      const uint16_t *par = sl < nq ? (const uint16_t *)(rec0 + (size_t)qpos[sl] * g.rec_bytes + D) : nullptr;
       // records keep (mean, std) in the first params pair of keys and of values
-      ((uint16_t *)(T + Q::KSD))[t] = par ? par[1] : 0;
-      ((uint16_t *)(T + Q::KM))[t] = par ? par[0] : 0;
-      ((uint16_t *)(T + Q::VSD))[t] = par ? par[2 * Q::NG + 1] : 0;
-      ((uint16_t *)(T + Q::VM))[t] = par ? par[2 * Q::NG] : 0;
+      const uint16_t *par = (const uint16_t *)(lds + t * R + D);
+      ((uint16_t *)(T + Q::KSD))[t] = par[1];
+      ((uint16_t *)(T + Q::KM))[t] = par[0];
+      ((uint16_t *)(T + Q::VSD))[t] = par[2 * Q::NG + 1];
+      ((uint16_t *)(T + Q::VM))[t] = par[2 * Q::NG];
     }
+    wave_lds_sync();
   }
 }
 
 // compact tiles of every tier from the position lists: one thread per
-// (token slot, 8-channel chunk) for BF16, per (token slot) for quantized tiers
+// (token slot, 8-channel chunk) for BF16, one wave per tile for quantized tiers
 template <int D>
 __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) {
   const int bh = blockIdx.y;
@@ -1491,10 +1590,13 @@ __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) 
     const int i = it / chunks;
     tok_copy_token(g, pages_bh, cpages_bh, st.cpos[(size_t)bh * g.NCT * TS + i], i, (it % chunks) * 8);
   }
-  // quantized tiers: one thread per (slot, lane of the tile layout)
-  hq_gather_ql<D, 0>(g, st, bh);
-  hq_gather_ql<D, 1>(g, st, bh);
-  hq_gather_q1<D>(g, st, bh);
+  // quantized tiers: one wave per tile
+  __shared__ __attribute__((aligned(16))) uint8_t s_rec[4][TS * (D + (D / 32) * 8)];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + wave, n_gw = gridDim.x * 4;
+  hq_gather_ql<D, 0>(g, st, bh, s_rec[wave], gw, n_gw, lane);
+  hq_gather_ql<D, 1>(g, st, bh, s_rec[wave], gw, n_gw, lane);
+  hq_gather_q1<D>(g, st, bh, s_rec[wave], gw, n_gw, lane);
 }
 
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
