@@ -51,9 +51,29 @@ def _canon(codes, bits):
     return oc.pack_codes(np.asarray(codes, np.uint8).reshape(-1), bits)
 
 
-def _run_hqekv(cfg, torch, n_splits=0, label=""):
+class _FlatValues:
+    """The workload with 70% of the tokens' value rows made constant: their
+    value range is 0, so is their joint metric, and every cut below the top
+    30% falls among equal metrics that only the positions order (newer
+    first)."""
+
+    def __init__(self, wl):
+        self.wl = wl
+
+    def kv(self, b):
+        k, v = self.wl.kv(b)
+        v = v.copy()
+        flat = (np.arange(v.shape[1]) % 10) < 7
+        v[:, flat, :] = v[:, flat, :1]
+        return k, v
+
+    def __getattr__(self, name):
+        return getattr(self.wl, name)
+
+
+def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
     from tiered_quantization_eviction_amd import Cache, make_config
-    wl = W.Workload(cfg)
+    wl = W.Workload(cfg) if wrap is None else wrap(W.Workload(cfg))
     B, Hkv, G, d, P, T = cfg.batch, cfg.n_kv_heads, cfg.group_size, cfg.head_dim, cfg.prefill, cfg.total_tokens
     m = cfg.init_queries
     ratios32 = tuple(float(np.float32(r)) for r in cfg.ratios)
@@ -157,3 +177,12 @@ def test_hqekv_d64_g8_splits_parity(torch_cuda):
     cfg = W.HQEKV.replace(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=64, prefill=700, steps=96, omega=32,
                           init_queries=8)
     _run_hqekv(cfg, torch_cuda, n_splits=3, label="hqekv-d64-g8")
+
+
+@pytest.mark.parametrize("prefill", [1024, 4096])
+def test_hqekv_equal_metrics_parity(torch_cuda, prefill):
+    """Thousands of tokens with metric 0 at three of the four cuts: about 700
+    tied tokens at a 1024-token prompt, about 2900 at 4096 (more than the
+    event kernel's in-LDS tie list holds, so the positions are radix-selected)."""
+    cfg = W.HQEKV.replace(batch=1, n_q_heads=8, n_kv_heads=2, prefill=prefill, steps=128)
+    _run_hqekv(cfg, torch_cuda, label=f"hqekv-ties-{prefill}", wrap=_FlatValues)

@@ -202,6 +202,7 @@ struct TokState {
   // HqeKV
   float *vrange;        // [B][Hkv][T] max - min of the token's original value row
   uint8_t *qrec;        // [B][Hkv][T][rec_bytes]
+  uint32_t *hqkey;      // [B][Hkv][hq_key_stride] metric keys of the last assignment event
   uint8_t *hqold;       // [B][Hkv][T] level + 1 a token held before the last event, until it is re-quantized (0: none)
   uint8_t *qtiles[3];   // [B][Hkv][NCT][qtile_bytes] compact INT4 / INT2 / INT1 tiles
   int32_t *qpos[3];     // [B][Hkv][NCT*TS] their positions
@@ -214,6 +215,9 @@ struct TokState {
 struct TokStep {
   int N, rstart, n_cmp;
 };
+
+// key slots per (sequence, KV head) of an assignment event (a multiple of 4)
+__host__ __device__ inline int hq_key_stride(const TokGeom &g) { return (g.T + 3) & ~3; }
 
 __host__ __device__ inline size_t tok_page_offset(const TokGeom &g, int b, int h, int tile) {
   return (((size_t)b * g.Hkv + h) * g.NPT + tile) * (size_t)(2 * TS * g.d);

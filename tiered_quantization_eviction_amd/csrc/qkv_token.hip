@@ -66,6 +66,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.cnt = nullptr;
   st.cuts = nullptr;
   st.hqold = nullptr;
+  st.hqkey = nullptr;
   for (int k = 0; k < 3; ++k) {
     st.qtiles[k] = nullptr;
     st.qpos[k] = nullptr;
@@ -80,6 +81,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
     st.cnt = (int32_t *)take(BH * 4 * 4);
     st.cuts = (unsigned long long *)take(BH * 4 * 8);
     st.hqold = (uint8_t *)take(BH * g.T);
+    st.hqkey = (uint32_t *)take(BH * hq_key_stride(g) * 4);
   }
   return off;
 }
@@ -1315,119 +1317,289 @@ __global__ __launch_bounds__(256) void hq_requant_kernel(TokGeom g, TokState st,
   }
 }
 
-__global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, int N, int elig_end, int c0, int c1,
-                                                        int c2, int c3) {
-  const int bh = blockIdx.x;
-  const int b = bh / g.Hkv, h = bh % g.Hkv;
-  const size_t tb = (size_t)bh * g.T;
-  const int tid = threadIdx.x;
-  __shared__ unsigned int hist[4][256];
-  __shared__ unsigned long long prefix[4];
-  __shared__ long long rem[4];
-  __shared__ int n_elig;
-  __shared__ unsigned long long thr[4];
-  auto eligible = [&](int pos) {
-    const uint8_t t = st.tier[tb + pos];
-    return t != T_EVICTED && t != T_EMPTY;
-  };
-  auto keyof = [&](int pos) {
-    const float metric = st.score[tb + pos] * st.vrange[tb + pos];   // accumulated attention x value range
-    return ((unsigned long long)__float_as_uint(metric) << 32) | (unsigned)(pos + 1);
-  };
-  // eligible count
-  if (tid == 0) n_elig = 0;
-  __syncthreads();
-  {
-    int cnt = 0;
-    for (int pos = tid; pos < elig_end; pos += blockDim.x) cnt += eligible(pos) ? 1 : 0;
-    atomicAdd(&n_elig, cnt);
-  }
-  __syncthreads();
-  const long long E = n_elig;
-  const long long cum[4] = {c0, (long long)c0 + c1, (long long)c0 + c1 + c2, (long long)c0 + c1 + c2 + c3};
-  // radix select of the four cut keys: the key with exactly cum[j]-1 keys above it
-  if (tid < 4) {
-    prefix[tid] = 0ull;
-    rem[tid] = cum[tid] - 1;
-  }
-  for (int byte = 7; byte >= 0; --byte) {
-    for (int i = tid; i < 4 * 256; i += blockDim.x) hist[i / 256][i % 256] = 0u;
-    __syncthreads();
-    const int sh = 8 * byte;
-    const unsigned long long hmask = byte == 7 ? 0ull : (~0ull << (sh + 8));
-    for (int pos = tid; pos < elig_end; pos += blockDim.x) {
-      if (!eligible(pos)) continue;
-      const unsigned long long key = keyof(pos);
+constexpr uint32_t HQ_KEY_NONE = 0xffffffffu;   // key slot of a token that is not ranked
+constexpr int HQ_TIE_CAP = 1024;                 // tied tokens at a cut resolved from one LDS list
+
+// One radix digit of every active cut, chosen by the whole block: count(j, b)
+// is the number of cut j's candidate keys whose digit is b (NB bins, a higher
+// bin ranking first).  The bin holding the key of rank rem[j] (0 = highest)
+// is or-ed into pref[j] at bit sh; rem[j] becomes the rank inside that bin
+// and bin_n[j] its key count.
+template <int NB, typename CountF>
+__device__ void hq_choose_digit(CountF count, int sh, uint32_t *pref, int *rem, int *bin_n, const bool *active,
+                                int (*wtot)[4]) {
+  constexpr int BPT = NB >= 1024 ? NB / 1024 : 1;   // bins per thread, thread order = descending bins
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool has = tid * BPT < NB;
+  int r[4], s[4], incl[4];
+  bool act[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (rem[j] >= 0 && rem[j] < E && (key & hmask) == (prefix[j] & hmask))
-          atomicAdd(&hist[j][(key >> sh) & 255u], 1u);
+  for (int j = 0; j < 4; ++j) {
+    act[j] = active[j];
+    r[j] = rem[j];
+    s[j] = 0;
+    if (act[j] && has)
+      for (int i = 0; i < BPT; ++i) s[j] += count(j, NB - 1 - (tid * BPT + i));
+    int v = s[j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off);
+      if (lane >= off) v += t;
     }
-    __syncthreads();
-    if (tid < 4 && rem[tid] >= 0 && rem[tid] < E) {
-      long long acc = 0;
-      for (int v = 255; v >= 0; --v) {
-        const unsigned int c = hist[tid][v];
-        if (acc + c > rem[tid]) {
-          prefix[tid] |= (unsigned long long)v << sh;
-          rem[tid] -= acc;
+    incl[j] = v;
+    if (lane == 63) wtot[wave][j] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    for (int w = 0; w < wave; ++w) incl[j] += wtot[w][j];
+    const int excl = incl[j] - s[j];
+    if (act[j] && s[j] > 0 && excl <= r[j] && r[j] < incl[j]) {
+      int acc = excl;
+      for (int i = 0; i < BPT; ++i) {
+        const int b = NB - 1 - (tid * BPT + i);
+        const int c = count(j, b);
+        if (acc + c > r[j]) {
+          pref[j] |= (uint32_t)b << sh;
+          rem[j] = r[j] - acc;
+          bin_n[j] = c;
           break;
         }
         acc += c;
       }
     }
-    __syncthreads();
-  }
-  if (tid < 4) {
-    // keys >= thr[j] have rank < cum[j]: all of them when cum[j] >= E, none when cum[j] == 0
-    thr[tid] = cum[tid] >= E ? 0ull : (cum[tid] <= 0 ? ~0ull : prefix[tid]);
-    st.cuts[bh * 4 + tid] = thr[tid];
   }
   __syncthreads();
-  // targets, downgrade only: a token that moves takes its new tier now; one
-  // that moves to a quantized tier keeps its previous level in hqold until
-  // hq_requant_kernel has rebuilt its record from its current values
-  const int wave = tid >> 6, lane = tid & 63, n_waves = blockDim.x >> 6;
-  for (int pos = tid; pos < elig_end; pos += blockDim.x) {
-    if (!eligible(pos)) continue;
-    const unsigned long long key = keyof(pos);
-    int target = 0;
+}
+
+// Assignment event of one (sequence, KV head) (HqeKV section 3.3 with the
+// shares of its tier table): the joint metric (accumulated attention x value
+// range) ranks every token appended before the previous event; the cuts at
+// ranks cum[j] = c0 + ... + cj are found by radix selection on the metric's
+// float bits (ties: the newer token first), each token moves down to its
+// target tier if that is lower (a token that moves to a quantized tier
+// keeps its previous level in hqold until hq_requant_kernel has rebuilt its
+// record), and the per-tier position lists are rebuilt in position order.
+__global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, int elig_end, int c0, int c1, int c2,
+                                                        int c3) {
+  const int bh = blockIdx.x;
+  const size_t tb = (size_t)bh * g.T;
+  uint32_t *keys = st.hqkey + (size_t)bh * hq_key_stride(g);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n_waves = blockDim.x >> 6;
+  const int nthr = blockDim.x;
+  __shared__ uint32_t hist[4][2048];
+  __shared__ int wtot[16][4];
+  __shared__ uint32_t pref[4], ppref[4];
+  __shared__ int rem[4], prem[4], bin_n[4], pbin_n[4], n_tie[4], pcut[4];
+  __shared__ bool active[4], big[4];
+  __shared__ int s_E;
+  __shared__ unsigned long long thr[4];
+  __shared__ int tie_pos[4][HQ_TIE_CAP];
+  __shared__ int run[4];
+
+  // ---- keys: metric bits of every eligible token, four positions per thread ----
+  if (tid == 0) s_E = 0;
+  __syncthreads();
+  {
+    int cnt = 0;
+    for (int p0 = 4 * tid; p0 < elig_end; p0 += 4 * nthr) {
+      uint32_t k4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = p0 + e;
+        k4[e] = HQ_KEY_NONE;
+        if (pos < elig_end) {
+          const uint8_t t = st.tier[tb + pos];
+          const float metric = st.score[tb + pos] * st.vrange[tb + pos];
+          if (t != T_EVICTED && t != T_EMPTY) {
+            const uint32_t k = __float_as_uint(metric);
+            k4[e] = k == HQ_KEY_NONE ? k - 1u : k;   // (an all-ones NaN keeps its place among NaNs)
+            ++cnt;
+          }
+        }
+      }
+      *(u32x4v *)(keys + p0) = u32x4v{k4[0], k4[1], k4[2], k4[3]};
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) atomicAdd(&s_E, cnt);
+  }
+  __syncthreads();
+  const long long E = s_E;
+  const long long cum[4] = {c0, (long long)c0 + c1, (long long)c0 + c1 + c2, (long long)c0 + c1 + c2 + c3};
+  if (tid < 4) {
+    const long long r = cum[tid] - 1;
+    active[tid] = r >= 0 && r < E;
+    rem[tid] = active[tid] ? (int)r : 0;
+    pref[tid] = 0u;
+    ppref[tid] = 0u;
+    bin_n[tid] = 0;
+    n_tie[tid] = 0;
+    pcut[tid] = -1;
+  }
+  // every key of the block's positions, 16 per thread per round (loads first)
+  auto for_keys = [&](auto fn) {
+    for (int p0 = 4 * tid; p0 < elig_end; p0 += 16 * nthr) {
+      u32x4v k4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = p0 + u * 4 * nthr;
+        k4[u] = q < elig_end ? *(const u32x4v *)(keys + q) : u32x4v{HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fn(k4[u][e], p0 + u * 4 * nthr + e);
+    }
+  };
+  auto clear_hist = [&]() {
+    for (int i = tid; i < 4 * 2048; i += nthr) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+  };
+  // ---- digit [31..21]: one histogram for all cuts (four copies against contention) ----
+  clear_hist();
+  for_keys([&](uint32_t k, int) {
+    if (k != HQ_KEY_NONE) atomicAdd(&hist[wave & 3][k >> 21], 1u);
+  });
+  __syncthreads();
+  hq_choose_digit<2048>([&](int, int b) { return (int)(hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b]); }, 21,
+                        pref, rem, bin_n, active, wtot);
+  // ---- digit [20..10], then [9..0], per cut among the keys of its prefix ----
+  clear_hist();
+  for_keys([&](uint32_t k, int) {
+    if (k == HQ_KEY_NONE) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
-    const int old = hq_level(st.tier[tb + pos]);
-    const int nw = max(old, target);
-    if (nw > old) {
-      st.tier[tb + pos] = hq_code(nw);
-      if (nw != HQ_EVICT) st.hqold[tb + pos] = (uint8_t)(old + 1);
+      if (active[j] && (k >> 21) == (pref[j] >> 21)) atomicAdd(&hist[j][(k >> 10) & 2047u], 1u);
+  });
+  __syncthreads();
+  hq_choose_digit<2048>([&](int j, int b) { return (int)hist[j][b]; }, 10, pref, rem, bin_n, active, wtot);
+  clear_hist();
+  for_keys([&](uint32_t k, int) {
+    if (k == HQ_KEY_NONE) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (active[j] && (k >> 10) == (pref[j] >> 10)) atomicAdd(&hist[j][k & 1023u], 1u);
+  });
+  __syncthreads();
+  hq_choose_digit<1024>([&](int j, int b) { return (int)hist[j][b]; }, 0, pref, rem, bin_n, active, wtot);
+  // ---- ties at each cut's metric: the newer token ranks first ----
+  if (tid < 4) big[tid] = active[tid] && bin_n[tid] > HQ_TIE_CAP;
+  __syncthreads();
+  for_keys([&](uint32_t k, int pos) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (active[j] && !big[j] && k == pref[j]) {
+        const int i = atomicAdd(&n_tie[j], 1);
+        if (i < HQ_TIE_CAP) tie_pos[j][i] = pos;
+      }
+  });
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!active[j] || big[j]) continue;
+    const int n = min(n_tie[j], HQ_TIE_CAP);
+    for (int i = tid; i < n; i += nthr) {
+      const int p = tie_pos[j][i];
+      int r = 0;
+      for (int q = 0; q < n; ++q) r += tie_pos[j][q] > p ? 1 : 0;
+      if (r == rem[j]) pcut[j] = p;
     }
   }
+  if (big[0] || big[1] || big[2] || big[3]) {
+    // many equal metrics: radix selection on the positions of the tied tokens
+    if (tid < 4) {
+      prem[tid] = rem[tid];
+      ppref[tid] = 0u;
+    }
+    __syncthreads();
+    const int shs[3] = {20, 9, 0};
+    for (int d = 0; d < 3; ++d) {
+      const int sh = shs[d], top = d == 0 ? 31 : shs[d - 1];
+      const uint32_t dmask = d == 2 ? 511u : 2047u;
+      clear_hist();
+      for_keys([&](uint32_t k, int pos) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (big[j] && k == pref[j] && ((uint32_t)pos >> top) == (ppref[j] >> top))
+            atomicAdd(&hist[j][((uint32_t)pos >> sh) & dmask], 1u);
+      });
+      __syncthreads();
+      if (d < 2)
+        hq_choose_digit<2048>([&](int j, int b) { return (int)hist[j][b]; }, sh, ppref, prem, pbin_n, big, wtot);
+      else
+        hq_choose_digit<512>([&](int j, int b) { return (int)hist[j][b]; }, sh, ppref, prem, pbin_n, big, wtot);
+    }
+    if (tid < 4 && big[tid]) pcut[tid] = (int)ppref[tid];
+  }
   __syncthreads();
-  // ranked tokens (pos < elig_end) per tier, in position order -> position lists
-  __shared__ int run[4];
+  if (tid < 4) {
+    // keys >= thr[j] have rank < cum[j]: all of them when cum[j] >= E, none when cum[j] <= 0
+    const long long c = cum[tid];
+    thr[tid] = c >= E ? 0ull
+             : (c <= 0 ? ~0ull : (((unsigned long long)pref[tid] << 32) | (unsigned)(pcut[tid] + 1)));
+    st.cuts[bh * 4 + tid] = thr[tid];
+    run[tid] = 0;
+  }
+  __syncthreads();
+  // ---- targets (downgrade only) and the per-tier position lists, in position order ----
   __shared__ int wsum[16][4];
-  if (tid < 4) run[tid] = 0;
-  __syncthreads();
-  for (int base = 0; base < elig_end; base += blockDim.x) {
-    const int pos = base + tid;
-    int lvl = HQ_EVICT;
-    if (pos < elig_end) lvl = hq_level(st.tier[tb + pos]);
-    // block prefix sums of the four tier flags
+  for (int base = 0; base < elig_end; base += 4 * nthr) {
+    const int p0 = base + 4 * tid;
+    int lv[4], cnt[4] = {0, 0, 0, 0};
+    const u32x4v k4 = p0 < elig_end ? *(const u32x4v *)(keys + p0)
+                                    : u32x4v{HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = p0 + e;
+      lv[e] = HQ_EVICT;
+      if (pos >= elig_end) continue;
+      const int old = hq_level(st.tier[tb + pos]);
+      lv[e] = old;
+      if (k4[e] != HQ_KEY_NONE) {
+        const unsigned long long key = ((unsigned long long)k4[e] << 32) | (unsigned)(pos + 1);
+        int target = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
+        if (target > old) {
+          st.tier[tb + pos] = hq_code(target);
+          if (target != HQ_EVICT) st.hqold[tb + pos] = (uint8_t)(old + 1);
+          lv[e] = target;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (lv[e] < 4) ++cnt[lv[e]];
     int incl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const unsigned long long bal = __ballot(lvl == k);
-      incl[k] = __popcll(bal & ((2ull << lane) - 1ull));   // inclusive within the wave
-      if (lane == 63) wsum[wave][k] = __popcll(bal);
+      int v = cnt[k];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+      }
+      incl[k] = v;
+      if (lane == 63) wsum[wave][k] = v;
     }
     __syncthreads();
-    if (pos < elig_end && lvl < 4) {
-      int off = run[lvl] + incl[lvl] - 1;
-      for (int w2 = 0; w2 < wave; ++w2) off += wsum[w2][lvl];
-      if (lvl == HQ_BF16)
-        st.cpos[(size_t)bh * g.NCT * TS + off] = pos;
+    int off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      off[k] = run[k] + incl[k] - cnt[k];
+      for (int w2 = 0; w2 < wave; ++w2) off[k] += wsum[w2][k];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int l = lv[e];
+      if (l >= 4) continue;
+      const int o = l == 0 ? off[0]++ : l == 1 ? off[1]++ : l == 2 ? off[2]++ : off[3]++;
+      if (l == HQ_BF16)
+        st.cpos[(size_t)bh * g.NCT * TS + o] = p0 + e;
       else
-        st.qpos[lvl - 1][(size_t)bh * g.NCT * TS + off] = pos;
+        st.qpos[l - 1][(size_t)bh * g.NCT * TS + o] = p0 + e;
     }
     __syncthreads();
     if (tid < 4) {
@@ -1438,7 +1610,6 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
     __syncthreads();
   }
   if (tid < 4) st.cnt[bh * 4 + tid] = run[tid];
-  (void)N;
 }
 
 __device__ __forceinline__ size_t tb_of(const TokGeom &g, int bh) { return (size_t)bh * g.T; }
@@ -1601,7 +1772,7 @@ __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) 
 
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
                            hipStream_t s) {
-  hipLaunchKernelGGL(hq_event_kernel, dim3(g.B * g.Hkv), dim3(1024), 0, s, g, st, N, elig_end, counts[0], counts[1],
+  hipLaunchKernelGGL(hq_event_kernel, dim3(g.B * g.Hkv), dim3(1024), 0, s, g, st, elig_end, counts[0], counts[1],
                      counts[2], counts[3]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
