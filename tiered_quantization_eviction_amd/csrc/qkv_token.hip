@@ -1747,24 +1747,61 @@ __device__ void hq_gather_q1(const TokGeom &g, const TokState &st, int bh, uint8
   }
 }
 
-// compact tiles of every tier from the position lists: one thread per
-// (token slot, 8-channel chunk) for BF16, one wave per tile for quantized tiers
+// Compact BF16 tiles of one (sequence, KV head) from the position pages, one
+// wave per tile, all accesses 16 bytes wide: key chunks (one token, eight
+// channels) are copied as they are; a value chunk of the tile layout (four
+// tokens of two channels c, c + 16) is assembled from the four source chunks
+// that hold those channels of each token.  Slots past the count are zeros.
+template <int D>
+__device__ void hq_gather_bf16(const TokGeom &g, const TokState &st, int bh, int gw, int n_gw, int lane) {
+  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const int nb = st.cnt[bh * 4 + 0];
+  const int ntiles = (nb + TS - 1) / TS;
+  const uint16_t *src = st.pages + tok_page_offset(g, b, h, 0);
+  const int32_t *cpos = st.cpos + (size_t)bh * g.NCT * TS;
+  const u32x4v zero = {0u, 0u, 0u, 0u};
+  for (int tile = gw; tile < ntiles; tile += n_gw) {
+    uint16_t *dk = st.cpages + tok_cpage_offset(g, b, h, tile);
+    uint16_t *dv = dk + TS * D;
+    for (int it = lane; it < TS * D / 8; it += 64) {
+      const int tk = it / (D / 8), c0 = (it % (D / 8)) * 8;
+      const int i = tile * TS + tk;
+      u32x4v v = zero;
+      if (i < nb) {
+        const int pos = cpos[i];
+        v = *(const u32x4v *)(src + (size_t)(pos / TS) * 2 * TS * D + k_tile_index(pos % TS, c0));
+      }
+      *(u32x4v *)(dk + k_tile_index(tk, c0)) = v;
+    }
+    for (int it = lane; it < 4 * (D / 2); it += 64) {
+      const int q = it / (D / 2), cp = it % (D / 2);
+      const int cb = (cp >> 4) * 32 + (cp & 15);   // channels cb and cb + 16
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        lo[tt] = hi[tt] = 0u;
+        const int i = tile * TS + 4 * q + tt;
+        if (i < nb) {
+          const int pos = cpos[i], ts = pos % TS, e = ts & 3;
+          const u32x4v sv = *(const u32x4v *)(src + (size_t)(pos / TS) * 2 * TS * D + TS * D + v_tile_index(ts & ~3, cb));
+          lo[tt] = ((e < 2 ? sv[0] : sv[1]) >> (16 * (e & 1))) & 0xffffu;
+          hi[tt] = ((e < 2 ? sv[2] : sv[3]) >> (16 * (e & 1))) & 0xffffu;
+        }
+      }
+      *(u32x4v *)(dv + v_tile_index(4 * q, cb)) =
+          u32x4v{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+    }
+  }
+}
+
+// compact tiles of every tier from the position lists, one wave per tile
 template <int D>
 __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) {
   const int bh = blockIdx.y;
-  const int b = bh / g.Hkv, h = bh % g.Hkv;
-  const int chunks = D / 8;
-  const int nb = st.cnt[bh * 4 + 0];
-  const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
-  uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
-  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < nb * chunks; it += gridDim.x * blockDim.x) {
-    const int i = it / chunks;
-    tok_copy_token(g, pages_bh, cpages_bh, st.cpos[(size_t)bh * g.NCT * TS + i], i, (it % chunks) * 8);
-  }
-  // quantized tiers: one wave per tile
   __shared__ __attribute__((aligned(16))) uint8_t s_rec[4][TS * (D + (D / 32) * 8)];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + wave, n_gw = gridDim.x * 4;
+  hq_gather_bf16<D>(g, st, bh, gw, n_gw, lane);
   hq_gather_ql<D, 0>(g, st, bh, s_rec[wave], gw, n_gw, lane);
   hq_gather_ql<D, 1>(g, st, bh, s_rec[wave], gw, n_gw, lane);
   hq_gather_q1<D>(g, st, bh, s_rec[wave], gw, n_gw, lane);
