@@ -42,42 +42,45 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
 // append: new positions into their unit's page (swizzled tiles)
 // ---------------------------------------------------------------------------
 
+// one block row per (sequence, KV head); thread it of the row copies 16-byte
+// chunk it % (D/8) of token it / (D/8) (32-bit indices: a prompt is far below 2^31 chunks)
+template <int D>
 __global__ __launch_bounds__(256) void append_kernel(Geom g, State st, const uint16_t *__restrict__ k,
                                                      const uint16_t *__restrict__ v, int n_tokens, int pos0) {
-  const int chunks = g.d / 8;
-  long long total = (long long)g.B * g.Hkv * n_tokens * chunks;
-  for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < total;
-       it += (long long)gridDim.x * blockDim.x) {
-    int ch = (int)(it % chunks);
-    long long r = it / chunks;
-    int tok = (int)(r % n_tokens);
-    r /= n_tokens;
-    int h = (int)(r % g.Hkv);
-    int b = (int)(r / g.Hkv);
-    int pos = pos0 + tok;
-    int u = unit_of(g, pos);
-    int slot = pos - unit_start(g, u);
-    int tile = slot / TS, t = slot % TS;
-    uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)tile * 2 * TS * g.d;
-    uint16_t *vt = kt + TS * g.d;
-    size_t src = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d + ch * 8;
-    uint4 kk = *(const uint4 *)(k + src);
-    int c0 = ch * 8;
-    *(uint4 *)(kt + k_tile_index(t, c0)) = kk;
-    const uint16_t *vs = v + src;
+  constexpr int CH = D / 8;
+  const int bh = blockIdx.x;
+  const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+  const int total = n_tokens * CH;
+  for (int it = blockIdx.y * blockDim.x + threadIdx.x; it < total; it += gridDim.y * blockDim.x) {
+    const int tok = it / CH, c0 = (it % CH) * 8;
+    const int pos = pos0 + tok;
+    const int u = unit_of(g, pos);
+    const int slot = pos - unit_start(g, u);
+    const int tile = slot / TS, t = slot % TS;
+    uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)tile * 2 * TS * D;
+    uint16_t *vt = kt + TS * D;
+    const size_t src = ((size_t)bh * n_tokens + tok) * D + c0;
+    *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + src);
+    const uint4 vq = *(const uint4 *)(v + src);
+    const uint16_t *vs = (const uint16_t *)&vq;
 #pragma unroll
     for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = vs[j];
-    if (h == 0 && ch == 0 && (slot == 0 || tok == 0)) st.tier[b * g.U + u] = (u == 0) ? T_SINK : T_RECENT;
+    if (h == 0 && c0 == 0 && (slot == 0 || tok == 0)) st.tier[b * g.U + u] = (u == 0) ? T_SINK : T_RECENT;
   }
 }
 
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
                          int pos0, hipStream_t s) {
-  long long total = (long long)g.B * g.Hkv * n_tokens * (g.d / 8);
-  int grid = (int)((total + 255) / 256);
-  if (grid > 16384) grid = 16384;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(256), 0, s, g, st, k, v, n_tokens, pos0);
+  if ((long long)n_tokens * (g.d / 8) > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int total = n_tokens * (g.d / 8);
+  const int threads = total <= 64 ? 64 : 256;
+  int rows = (total + threads - 1) / threads;
+  if (rows > 65535) rows = 65535;
+  const dim3 grid(g.B * g.Hkv, rows);
+  if (g.d == 128)
+    hipLaunchKernelGGL(append_kernel<128>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
   return hipGetLastError();
 }
 
@@ -847,16 +850,16 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     }
     return;
   }
-  // masses of up to 256 live entries of one sequence -> window scores
+  // masses of up to 256 live entries of one sequence -> window scores; the
+  // entry's unit, old score and first KV heads' (rho, m) pairs are loaded
+  // before the wait for the split statistics
   const int mb = blockIdx.x - n_out_blocks;
   const int b = mb / n_chunks, chunk = mb % n_chunks;
   const EntryList L = make_list(g, st, si, b);
   const int E = L.count();
   const int e = chunk * blockDim.x + threadIdx.x;
   const int ee = min(e, E - 1);
-  const int raw = st.routed[b * g.U + min(max(ee - L.s0, 0), g.U - 1)];   // issued before the stats wait
-  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
-  __syncthreads();
+  const int raw = st.routed[b * g.U + min(max(ee - L.s0, 0), g.U - 1)];
   int u;
   if (ee < L.s0)
     u = 0;
@@ -865,9 +868,8 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   else
     u = L.r0 + (ee - L.s0 - L.nF - L.nQ);
   const float old = st.score[b * g.U + u];
-  float total = 0.0f;
-  for (int h0 = 0; h0 < g.Hkv; h0 += CH) {
-    float4 mp[CH][G / 2];   // (rho, m) of the G heads, per KV head
+  float4 mp[CH][G / 2];   // (rho, m) of the G heads, per KV head
+  auto load_heads = [&](int h0) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int h = min(h0 + k, g.Hkv - 1);
@@ -875,6 +877,13 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
 #pragma unroll
       for (int q = 0; q < G / 2; ++q) mp[k][q] = src[q];
     }
+  };
+  load_heads(0);
+  for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
+  __syncthreads();
+  float total = 0.0f;
+  for (int h0 = 0; h0 < g.Hkv; h0 += CH) {
+    if (h0 > 0) load_heads(h0);
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int h = h0 + k;

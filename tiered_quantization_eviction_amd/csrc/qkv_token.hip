@@ -90,58 +90,64 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
 // append: new tokens into the position pages (HqeKV: and their value range)
 // ---------------------------------------------------------------------------
 
+// one block row per (sequence, KV head); thread it of the row copies 16-byte
+// chunk it % (D/8) of token it / (D/8)
+template <int D>
 __global__ __launch_bounds__(256) void tok_append_kernel(TokGeom g, TokState st, const uint16_t *__restrict__ k,
                                                          const uint16_t *__restrict__ v, int n_tokens, int pos0) {
-  const int chunks = g.d / 8;
-  const long long total = (long long)g.B * g.Hkv * n_tokens * chunks;
-  for (long long it = (long long)blockIdx.x * blockDim.x + threadIdx.x; it < total;
-       it += (long long)gridDim.x * blockDim.x) {
-    const int ch = (int)(it % chunks);
-    long long r = it / chunks;
-    const int tok = (int)(r % n_tokens);
-    r /= n_tokens;
-    const int h = (int)(r % g.Hkv);
-    const int b = (int)(r / g.Hkv);
+  constexpr int CH = D / 8;
+  const int bh = blockIdx.x;
+  const int b = bh / g.Hkv, h = bh - b * g.Hkv;
+  const int total = n_tokens * CH;
+  for (int it = blockIdx.y * blockDim.x + threadIdx.x; it < total; it += gridDim.y * blockDim.x) {
+    const int tok = it / CH, c0 = (it % CH) * 8;
     const int pos = pos0 + tok;
     uint16_t *kt = st.pages + tok_page_offset(g, b, h, pos / TS);
-    uint16_t *vt = kt + TS * g.d;
-    const int t = pos % TS, c0 = ch * 8;
-    const size_t row = (((size_t)b * g.Hkv + h) * n_tokens + tok) * g.d;
+    uint16_t *vt = kt + TS * D;
+    const int t = pos % TS;
+    const size_t row = ((size_t)bh * n_tokens + tok) * D;
     *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + row + c0);
     const uint4 vq = *(const uint4 *)(v + row + c0);
     const uint16_t *vs = (const uint16_t *)&vq;
 #pragma unroll
     for (int j = 0; j < 8; ++j) vt[v_tile_index(t, c0 + j)] = vs[j];
-    const size_t u = ((size_t)b * g.Hkv + h) * g.T + pos;
-    if (ch == 0) {
+    const size_t u = (size_t)bh * g.T + pos;
+    if (c0 == 0) {
       st.tier[u] = pos < g.n_sink ? T_SINK : T_RECENT;
       st.score[u] = 0.0f;
     }
     if (st.vrange) {
       // value range over the token's channels (HqeKV section 3.2): the token's
-      // d/8 chunks are adjacent lanes of one wave (the grid stride is a
-      // multiple of 64 and the chunk count divides 64), reduced by shuffles
+      // D/8 chunks are adjacent lanes of one wave (the stride is a multiple
+      // of 64 and the chunk count divides 64), reduced by shuffles
       float mn = bf16_to_f32(vs[0]), mx = mn;
 #pragma unroll
       for (int j = 1; j < 8; ++j) {
         mn = fminf(mn, bf16_to_f32(vs[j]));
         mx = fmaxf(mx, bf16_to_f32(vs[j]));
       }
-      for (int off = 1; off < chunks; off <<= 1) {
+#pragma unroll
+      for (int off = 1; off < CH; off <<= 1) {
         mn = fminf(mn, __shfl_xor(mn, off));
         mx = fmaxf(mx, __shfl_xor(mx, off));
       }
-      if (ch == 0) st.vrange[u] = mx - mn;
+      if (c0 == 0) st.vrange[u] = mx - mn;
     }
   }
 }
 
 hipError_t tok_launch_append(const TokGeom &g, const TokState &st, const uint16_t *k, const uint16_t *v,
                              int n_tokens, int pos0, hipStream_t s) {
-  const long long total = (long long)g.B * g.Hkv * n_tokens * (g.d / 8);
-  int grid = (int)((total + 255) / 256);
-  grid = grid > 16384 ? 16384 : (grid < 1 ? 1 : grid);
-  hipLaunchKernelGGL(tok_append_kernel, dim3(grid), dim3(256), 0, s, g, st, k, v, n_tokens, pos0);
+  if ((long long)n_tokens * (g.d / 8) > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int total = n_tokens * (g.d / 8);
+  const int threads = total <= 64 ? 64 : 256;
+  int rows = (total + threads - 1) / threads;
+  if (rows > 65535) rows = 65535;
+  const dim3 grid(g.B * g.Hkv, rows);
+  if (g.d == 128)
+    hipLaunchKernelGGL(tok_append_kernel<128>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+  else
+    hipLaunchKernelGGL(tok_append_kernel<64>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
   return hipGetLastError();
 }
 
