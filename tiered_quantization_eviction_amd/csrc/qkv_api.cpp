@@ -21,6 +21,9 @@ struct qkv_cache {
   int r_tok;      // token mode: first position not yet ranked
   int n_cmp;      // token mode (H2O): kept older tokens per (sequence, KV head)
   int last_event_N;   // HqeKV: tokens at the previous assignment event (0: none yet)
+  // token mode with a routing period above 1: masses wait in list order until
+  // a flush (before a route or a score export)
+  mutable bool tacc_dirty = false;
   void *ws;
   size_t ws_bytes;
   int N;          // tokens appended per sequence
@@ -335,6 +338,7 @@ int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, 
     const TokStep ts = {c->N, c->r_tok, c->n_cmp};
     rc = hip_err(tok_launch_attend(c->tg, c->ts, ts, (const uint16_t *)q, (size_t)c->tg.Hq * c->tg.d, out, mass_out,
                                    (hipStream_t)stream, e0, e1));
+    if (c->tg.omega > 1) c->tacc_dirty = true;
   } else {
     rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
                                e0, e1));
@@ -357,6 +361,7 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
     int rc = hip_err(tok_launch_attend(g, c->ts, ts, (const uint16_t *)q + (size_t)i * row, (size_t)n_queries * row,
                                        c->ts.scratch_out, nullptr, (hipStream_t)stream));
     if (rc != QKV_OK) return rc;
+    if (g.omega > 1) c->tacc_dirty = true;
   }
   return QKV_OK;
 }
@@ -364,11 +369,12 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
 int qkv_route(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
-  if (c->tok) {
+  if (c->tok && c->tacc_dirty) {
     // masses accumulated in list order reach the per-token scores first
     const TokStep ts = {c->N, c->r_tok, c->n_cmp};
     int rc = hip_err(tok_launch_flush(c->tg, c->ts, ts, (hipStream_t)stream));
     if (rc != QKV_OK) return rc;
+    c->tacc_dirty = false;
   }
   if (c->tok && c->tg.policy == QKV_POLICY_HQEKV) {
     // assignment event: tokens ranked before (all live ones at the first
@@ -484,10 +490,11 @@ int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_st
   const size_t need = qkv_export_bytes(c, what);
   if (need == 0 || bytes != need) return QKV_EINVAL;
   if (c->tok) {
-    if (what == QKV_EXPORT_SCORES && c->N > 0) {
+    if (what == QKV_EXPORT_SCORES && c->tacc_dirty) {
       const TokStep ts = {c->N, c->r_tok, c->n_cmp};
       int rc = hip_err(tok_launch_flush(c->tg, c->ts, ts, (hipStream_t)stream));
       if (rc != QKV_OK) return rc;
+      c->tacc_dirty = false;
     }
     return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
   }

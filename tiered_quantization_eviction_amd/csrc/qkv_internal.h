@@ -162,7 +162,8 @@ __host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 //   mref f32 [B][Hkv][TILES+1][G]        ... and the running max it is relative
 //                to (row TILES is the spare row unused lanes write to)
 //   tacc f32 [B][Hkv][TILES][TS]         masses summed in list order since the
-//                last flush into score (flushed before a route or an export)
+//                last flush into score (flushed before a route or an export;
+//                unused when the routing period is 1)
 // ---------------------------------------------------------------------------
 
 // HqeKV tiers of a ranked token (the per-token state of the five-tier method)

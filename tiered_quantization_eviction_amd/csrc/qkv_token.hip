@@ -25,7 +25,8 @@
 // each head and adds each token's mass into an accumulator kept in list order
 // (coalesced; the lists only change at routing calls).  Before a routing call
 // or an export of the scores, the accumulators are added into the per-token
-// scores and cleared.
+// scores and cleared.  With a routing period of 1 the merge adds into the
+// per-token scores directly.
 #include <hip/hip_ext.h>
 
 #include "qkv_device.h"
@@ -969,6 +970,7 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
   const TokList L = tok_list(g, st, ts, bh);
   const int n_live = min(L.count(), g.TILES);
   const int s0 = ((int)threadIdx.x % (TS / 4)) * 4;
+  const bool list_order = g.omega > 1;   // routing every step: straight into the scores
   for (int k = part * (256 * 4 / TS) + (int)threadIdx.x / (TS / 4); k < n_live; k += n_parts * (256 * 4 / TS)) {
     const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + k) * G * TS + s0;
     const float *ref = st.mref + ((size_t)bh * (g.TILES + 1) + k) * G;
@@ -979,12 +981,12 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
     for (int hh = 0; hh < G; ++hh) r[hh] = *(const float4 *)(rho + hh * TS);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) w[hh] = exp2f(ref[hh] - sM[hh]);
-    float4 acc = *accp;
+    float4 acc = list_order ? *accp : float4{0.f, 0.f, 0.f, 0.f};
     float *ap = (float *)&acc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int pos = mass_out ? tok_slot_pos<true>(g, st, ts, L, bh, k, s0 + e)
-                               : tok_slot_pos<false>(g, st, ts, L, bh, k, s0 + e);
+      const int pos = (mass_out || !list_order) ? tok_slot_pos<true>(g, st, ts, L, bh, k, s0 + e)
+                                                : tok_slot_pos<false>(g, st, ts, L, bh, k, s0 + e);
       if (pos < 0) continue;
       float mass = 0.0f;
 #pragma unroll
@@ -993,11 +995,14 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
         if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
         mass += v;
       }
-      ap[e] += mass;
+      if (list_order)
+        ap[e] += mass;
+      else
+        st.score[(size_t)bh * g.T + pos] += mass;
       if (mass_out) mass_out[(size_t)bh * g.T + pos] = mass;
     }
     // list order: coalesced, and stable until the next route (which flushes first)
-    *accp = acc;
+    if (list_order) *accp = acc;
   }
 }
 
