@@ -238,7 +238,6 @@ struct TokCtx {
   const TokList *L;
   int b, h, bh, lane, col, lq, G;
   bool is_hi, is_lo, has_q;
-  bool mass_lane;         // column col < G: the lane that stores its head's probabilities
   int slot;               // channel-group slot of this lane's A row in the paired value product
   float *mrho, *mref;
   uint32_t *lds_par;      // per wave: raw params of a block's two quantized tiles
@@ -247,17 +246,19 @@ struct TokCtx {
 
 // per-slot probabilities of a tile (lanes of column h < G hold rows 4*lq..+3)
 // and the running max they are relative to; other lanes write the spare row
+template <int GP>
 __device__ __forceinline__ void tok_store_mass(const TokCtx &c, int e, const float *p, float m) {
-  const int G = c.G, TILES = c.g->TILES;
-  const int er = c.mass_lane ? e : TILES;
+  constexpr int G = GP == 2 ? 4 : 8;
+  const bool mass_lane = c.col < G;
+  const int er = mass_lane ? e : c.g->TILES;
   *(float4 *)(c.mrho + ((size_t)er * G + (c.col & (G - 1))) * TS + 4 * c.lq) = make_float4(p[0], p[1], p[2], p[3]);
-  const int em = (c.mass_lane && c.lq == 0) ? e : TILES;
+  const int em = (mass_lane && c.lq == 0) ? e : c.g->TILES;
   c.mref[(size_t)em * G + (c.col & (G - 1))] = m;
 }
 
 // full-precision tiles (sink, compact, recent) of virtual range [ea, eb);
 // virtual index v < s0 + nC is list tile v, above it list tile v + (quantized tiles)
-template <int D>
+template <int D, int GP>
 __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&bq)[D / 32], float sc, int ea,
                              int eb) {
   if (ea >= eb) return;
@@ -283,13 +284,13 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
   const uint16_t *cp[2], *np[2];
   int clo[2], chi[2], ce[2], nlo[2], nhi[2], ne[2];
   block(0, cp, clo, chi, ce);
-  uint4 kr[2][KB], vr[2][CP];
+  u32x4v kr[2][KB], vr[2][CP];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(cp[t] + (kb * 64 + c.lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16v(cp[t] + (kb * 64 + c.lane) * 8);
 #pragma unroll
-    for (int p = 0; p < CP; ++p) vr[t][p] = ld_stream16(cp[t] + TS * D + (p * 64 + c.lane) * 8);
+    for (int p = 0; p < CP; ++p) vr[t][p] = ld_stream16v(cp[t] + TS * D + (p * 64 + c.lane) * 8);
   }
   for (int i = 0; i < n_blocks; ++i) {
     block(min(i + 1, n_blocks - 1), np, nlo, nhi, ne);   // the last block re-reads itself
@@ -301,11 +302,11 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16(np[t] + (kb * 64 + c.lane) * 8);
+      for (int kb = 0; kb < KB; ++kb) kr[t][kb] = ld_stream16v(np[t] + (kb * 64 + c.lane) * 8);
     float p[2][4], tsum[2];
     softmax_block<D, 2>(ws, s, sc, clo, chi, c.lq, p, tsum);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    for (int t = 0; t < 2; ++t) tok_store_mass<GP>(c, ce[t], p[t], ws.m);
     // rows h carry bf16(p), rows 8+h carry bf16(p - bf16(p))
     bf16x8 ap;
 #pragma unroll
@@ -317,15 +318,15 @@ __device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&b
       }
 #pragma unroll
     for (int p2 = 0; p2 < CP; ++p2) {
-      const uint4 v0 = make_uint4(vr[0][p2].x, vr[0][p2].y, vr[1][p2].x, vr[1][p2].y);
-      const uint4 v1 = make_uint4(vr[0][p2].z, vr[0][p2].w, vr[1][p2].z, vr[1][p2].w);
+      const u32x4v v0 = __builtin_shufflevector(vr[0][p2], vr[1][p2], 0, 1, 4, 5);
+      const u32x4v v1 = __builtin_shufflevector(vr[0][p2], vr[1][p2], 2, 3, 6, 7);
       ws.acc[2 * p2] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v0), ws.acc[2 * p2]);
       ws.acc[2 * p2 + 1] = mfma_bf16_k32(ap, __builtin_bit_cast(bf16x8, v1), ws.acc[2 * p2 + 1]);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = ld_stream16(np[t] + TS * D + (p2 * 64 + c.lane) * 8);
+      for (int p2 = 0; p2 < CP; ++p2) vr[t][p2] = ld_stream16v(np[t] + TS * D + (p2 * 64 + c.lane) * 8);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       cp[t] = np[t];
@@ -515,7 +516,7 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
     float p[2][4], tsum[2];
     softmax_rows<D, 2>(ws, x, p, tsum);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    for (int t = 0; t < 2; ++t) tok_store_mass<GP>(c, ce[t], p[t], ws.m);
     // ---- values ----
     // fp16 limbs of p (p cut to 11 bits, exact remainder); (P1, P2) = (0, phi)
     // on high rows, (phi, plo) on low rows
@@ -593,7 +594,7 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
 //   values: o = sum_t (p_t a_t) b_t + sum_t p_t c_t, with p*a split into two
 //           fp16 limbs (high rows, low rows) against the 0/1 codes, and the
 //           zero term as two MFMAs over the fp16 limbs of c.
-template <int D>
+template <int D, int GP>
 __device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], float qall, float sc,
                            int ea, int eb) {
   if (ea >= eb) return;
@@ -660,7 +661,7 @@ __device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
     float p[2][4], tsum[2];
     softmax_rows<D, 2>(ws, x, p, tsum);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tok_store_mass(c, ce[t], p[t], ws.m);
+    for (int t = 0; t < 2; ++t) tok_store_mass<GP>(c, ce[t], p[t], ws.m);
     // ---- values ----
     half8 ag, cz_hi, cz_lo;
     half4 P2[2];
@@ -752,7 +753,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   c.is_hi = is_hi;
   c.is_lo = is_lo;
   c.has_q = true;
-  c.mass_lane = col < G;
   c.slot = min((col & 7) / G, GP - 1);
   c.mrho = st.mrho + (size_t)bh * (g.TILES + 1) * G * TS;
   c.mref = st.mref + (size_t)bh * (g.TILES + 1) * G;
@@ -831,11 +831,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int qa[3], qz[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) slice(L.nQ[k], qa[k], qz[k]);
-  tok_run_bf16<D>(ws, c, bq, scale_log2, fa, fz);
+  tok_run_bf16<D, GP>(ws, c, bq, scale_log2, fa, fz);
   if (g.policy == QKV_POLICY_HQEKV) {
     tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
     tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
-    tok_run_q1<D>(ws, c, bqk, qall, scq, qa[2], qz[2]);
+    tok_run_q1<D, GP>(ws, c, bqk, qall, scq, qa[2], qz[2]);
   }
 
   // ---- wave epilogue: value-zero term, then the low-limb rows 8+h onto rows h ----
