@@ -453,10 +453,10 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
   const uint8_t *cp[2], *np[2];
   int chi[2], ce[2], nhi[2], ne[2];
   block(0, cp, chi, ce);
-  Buf cur, nxt;
-  load(cp, cur);
+  Buf buf0, buf1;
+  load(cp, buf0);
   const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
-  for (int i = 0; i < n_blocks; ++i) {
+  auto step = [&](const int i, Buf &cur, Buf &nxt) __attribute__((always_inline)) {
     block(min(i + 1, n_blocks - 1), np, nhi, ne);   // the last block re-reads itself
     load(np, nxt);
     // stage params: raw bytes, and the key scales as float32
@@ -576,14 +576,21 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
                              __builtin_shufflevector(bz0, bz1, 0, 1, 2, 3, 4, 5, 6, 7), ws.zacc);
     }
     wave_lds_sync();
-    cur = nxt;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       cp[t] = np[t];
       chi[t] = nhi[t];
       ce[t] = ne[t];
     }
+  };
+  // two blocks per trip with the buffers' roles swapped, so that no buffer
+  // whose loads are still in flight is copied at the end of a block
+  int i = 0;
+  for (; i + 1 < n_blocks; i += 2) {
+    step(i, buf0, buf1);
+    step(i + 1, buf1, buf0);
   }
+  if (i < n_blocks) step(i, buf0, buf1);
 }
 
 // INT1 tiles (Q1 layout), two per block.  A token's values are
@@ -631,11 +638,11 @@ __device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
   const uint8_t *cp[2], *np[2];
   int chi[2], ce[2], nhi[2], ne[2];
   block(0, cp, chi, ce);
-  Buf cur, nxt;
-  load(cp, cur);
+  Buf buf0, buf1;
+  load(cp, buf0);
   const half4 zero4 = {(half_t)0, (half_t)0, (half_t)0, (half_t)0};
   const half_t *par16 = (const half_t *)c.lds_par;   // [2 tiles][K std 16][K mean 16][V std 16][V mean 16]
-  for (int i = 0; i < n_blocks; ++i) {
+  auto step = [&](const int i, Buf &cur, Buf &nxt) __attribute__((always_inline)) {
     block(min(i + 1, n_blocks - 1), np, nhi, ne);   // the last block re-reads itself
     load(np, nxt);
     c.lds_par[c.lane] = cur.par;
@@ -701,14 +708,21 @@ __device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
       ws.zacc = mfma_f16_k32(pp, cz_lo, ws.zacc);
     }
     wave_lds_sync();
-    cur = nxt;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       cp[t] = np[t];
       chi[t] = nhi[t];
       ce[t] = ne[t];
     }
+  };
+  // two blocks per trip with the buffers' roles swapped, so that no buffer
+  // whose loads are still in flight is copied at the end of a block
+  int i = 0;
+  for (; i + 1 < n_blocks; i += 2) {
+    step(i, buf0, buf1);
+    step(i + 1, buf1, buf0);
   }
+  if (i < n_blocks) step(i, buf0, buf1);
 }
 
 template <int D, int GP>
