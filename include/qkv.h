@@ -87,12 +87,16 @@ typedef struct qkv_config {
  * the configuration is invalid (see qkv_check_config for the reason). */
 size_t qkv_workspace_bytes(const qkv_config *cfg);
 
-/* QKV_OK if the configuration is supported, else QKV_EINVAL. */
+/* QKV_OK if the configuration is supported, else QKV_EINVAL.  Besides the
+ * ranges above: QEvict with head_dim 128 and eight query heads per KV head
+ * needs 32-token windows (the attention workgroup's LDS would not fit). */
 int qkv_check_config(const qkv_config *cfg);
 
 /* Create a cache over `workspace` (device memory, at least
  * qkv_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller and
- * kept alive until qkv_destroy).  The workspace is cleared on `stream`. */
+ * kept alive until qkv_destroy).  The workspace is cleared on `stream`.
+ * QKV_EINVAL also when the attention workgroup of this configuration would
+ * not fit the current device's LDS. */
 int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream,
                qkv_cache **out);
 

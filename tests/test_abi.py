@@ -61,6 +61,11 @@ def test_config_checks_on_host():
                 setattr(c, k, v)
         assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL, kw
         assert L.workspace_bytes(c) == 0
+    # eight heads per KV head at d = 128 need 32-token windows (attention LDS)
+    for window, ok in ((16, False), (32, True)):
+        c = L.make_config(W.STRESS)
+        c.window = window
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, window
 
 
 def test_strerror_and_info_arguments():

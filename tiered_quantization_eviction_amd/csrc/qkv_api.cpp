@@ -75,6 +75,10 @@ int validate(const qkv_config *c) {
   if (c->n_sink < 0 || c->n_sink > TS || c->n_recent < 0) return QKV_EINVAL;
   if (c->k_full < 0 || c->k_quant < 0) return QKV_EINVAL;
   if (c->quant_bits != 2 || c->group != 32) return QKV_EINVAL;
+  // the attention workgroup's LDS (q*s limbs of every window slot of eight
+  // waves) exceeds the device's with d = 128, eight heads per KV head and
+  // windows of one tile
+  if (c->head_dim == 128 && G == 8 && c->window <= TS) return QKV_EINVAL;
   const long long U = 1 + ((long long)c->max_ctx - c->n_sink + c->window - 1) / c->window;
   if (U + 1 > SORT_MAX) return QKV_EINVAL;            // routing candidates are ranked in LDS
   return QKV_OK;
@@ -248,6 +252,12 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
     c->r_tok = cfg->n_sink;
   } else {
     make_geom(cfg, c->g);
+    bool fits = false;
+    rc = hip_err(attend_lds_fits(c->g, &fits));
+    if (rc != QKV_OK || !fits) {
+      delete c;
+      return rc != QKV_OK ? rc : QKV_EINVAL;   // (d = 128 with eight heads per KV head needs 32-token windows)
+    }
     need = carve(c->g, (char *)workspace, c->st);
   }
   if (bytes < need) {

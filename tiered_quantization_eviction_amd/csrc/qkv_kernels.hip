@@ -907,11 +907,30 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   if (e < E) st.score[b * g.U + u] = old + total;
 }
 
+// LDS of one attention workgroup beyond its static arrays: the q*s limbs of
+// every window slot of every wave
+static size_t attend_qs_bytes(const Geom &g) {
+  return (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+}
+
+hipError_t attend_lds_fits(const Geom &g, bool *fits) {
+  const void *f = g.d == 128 ? (g.G == 4 ? (const void *)attend_qevict_kernel<128, 2> : (const void *)attend_qevict_kernel<128, 1>)
+                             : (g.G == 4 ? (const void *)attend_qevict_kernel<64, 2> : (const void *)attend_qevict_kernel<64, 1>);
+  hipFuncAttributes a;
+  hipError_t e = hipFuncGetAttributes(&a, f);
+  if (e != hipSuccess) return e;
+  int dev = 0, max_lds = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return e;
+  *fits = a.sharedSizeBytes + attend_qs_bytes(g) <= (size_t)max_lds;
+  return hipSuccess;
+}
+
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
                          float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
-  const size_t qs_bytes = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+  const size_t qs_bytes = attend_qs_bytes(g);
   // four heads per KV head: value operands shared by channel-group pairs.
   // The optional events are attached to the dispatch itself, so they time
   // the kernel's execution (no launch gap).
