@@ -96,8 +96,11 @@ struct EntryList {
 __device__ inline EntryList make_list(const Geom &g, const State &st, const StepInfo &si, int b) {
   EntryList L;
   L.s0 = si.has_sink;
-  L.nF = st.routed_nf[b];
-  L.nQ = st.routed_nq[b];
+  // every sequence has the same candidate count, so the split of the ranked
+  // windows follows from the host's count (the routing kernel stores the same
+  // values in routed_nf / routed_nq)
+  L.nF = min(si.n_routed, g.k_full);
+  L.nQ = si.n_routed - L.nF;
   L.nR = si.r1 >= si.r0 ? si.r1 - si.r0 + 1 : 0;
   L.r0 = si.r0;
   return L;
