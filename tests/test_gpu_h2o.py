@@ -94,3 +94,10 @@ def test_h2o_small_g8_d64_parity(torch_cuda, splits):
     cfg = W.H2O.replace(batch=2, n_q_heads=16, n_kv_heads=2, head_dim=64, prefill=100, steps=60, n_sink=3,
                         k_full=20, n_recent=17)
     _run_h2o(cfg, torch_cuda, n_splits=splits, label=f"h2o-small-s{splits}")
+
+
+def test_h2o_no_heavy_hitters_parity(torch_cuda):
+    """No heavy-hitter budget: the cache keeps the sinks and the recent
+    window only (StreamingLLM)."""
+    cfg = W.H2O.replace(batch=1, prefill=200, steps=64, k_full=0)
+    _run_h2o(cfg, torch_cuda, label="h2o-kheavy0")

@@ -186,3 +186,13 @@ def test_hqekv_equal_metrics_parity(torch_cuda, prefill):
     event kernel's in-LDS tie list holds, so the positions are radix-selected)."""
     cfg = W.HQEKV.replace(batch=1, n_q_heads=8, n_kv_heads=2, prefill=prefill, steps=128)
     _run_hqekv(cfg, torch_cuda, label=f"hqekv-ties-{prefill}", wrap=_FlatValues)
+
+
+@pytest.mark.parametrize("ratios", [(1.0, 0.0, 0.0, 0.0, 0.0), (0.0, 0.0, 0.0, 1.0, 0.0), (0.0, 0.0, 0.0, 0.0, 1.0),
+                                    (0.0, 0.5, 0.5, 0.0, 0.0)])
+def test_hqekv_degenerate_shares_parity(torch_cuda, ratios):
+    """Single-tier and two-tier share vectors: everything BF16, everything
+    INT1, everything evicted after each event (attention over the tokens not
+    yet ranked only), and INT4/INT2 halves with no BF16 tier."""
+    cfg = W.HQEKV.replace(batch=1, n_q_heads=8, n_kv_heads=2, prefill=600, steps=128, ratios=ratios)
+    _run_hqekv(cfg, torch_cuda, label=f"hqekv-shares-{ratios}")

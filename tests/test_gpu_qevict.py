@@ -267,3 +267,13 @@ def test_qevict_window32_g8_parity(torch_cuda):
 def test_qevict_d64_window8_parity(torch_cuda):
     c = W.TINY.replace(batch=2, n_q_heads=8, n_kv_heads=2, prefill=515, steps=40, k_full=10, k_quant=20)
     _run_parity(c, torch_cuda, n_splits=4, label="d64w8")
+
+
+@pytest.mark.parametrize("kf,kq", [(0, 0), (0, 10 ** 6), (10 ** 6, 0), (3, 0), (0, 5)])
+def test_qevict_degenerate_capacities_parity(torch_cuda, kf, kq):
+    """The method's degenerate budgets: no ranked windows at all (sinks plus
+    recent, StreamingLLM at window granularity), every ranked window
+    quantized, nothing quantized (full attention over everything kept), and
+    small two-tier and quantized-only budgets that evict most windows."""
+    c = W.TINY.replace(k_full=kf, k_quant=kq, steps=40)
+    _run_parity(c, torch_cuda, label=f"degenerate kf={kf} kq={kq}")
