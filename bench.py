@@ -53,6 +53,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
 WORKLOADS = {c.name: c for c in (W.DRIFT, W.STRESS, W.HQEKV, W.H2O, W.TINY)}
+CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",
           W.POLICY_HQEKV: "bf16+int4+int2+int1 (fp32 accumulate)"}
@@ -296,17 +297,22 @@ def run_gpu_tok(cfg, K, V, Q, QP, steps, n_splits):
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts):
-    """The oracle, as it stands, on the first n_seqs sequences for
-    sample_steps decode steps each (prompt handling untimed)."""
-    from oracle import qevict as oe
+def _host_cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
-        cores = 1
+        return 1
+
+
+def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts, budget_s=None):
+    """The oracle, as it stands, on the first n_seqs sequences for
+    sample_steps decode steps each (prompt handling untimed); with budget_s,
+    one sequence for as many steps as fit in that many seconds."""
+    from oracle import qevict as oe
     worst = 0.0
     dt = 0.0
+    done = 0
     for b in range(n_seqs):
         seq = oe.QEvictSequence(K[b], V[b], window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
                                 n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits,
@@ -317,14 +323,52 @@ def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts):
         for s in range(sample_steps):
             o, _ = seq.step(s, Q[b, s])
             outs.append(o)
+            done += 1
+            if budget_s is not None and time.perf_counter() - t0 > budget_s:
+                break
         dt += time.perf_counter() - t0
         if b == 0:
             for s, o in enumerate(outs[:len(firsts)]):
                 worst = max(worst, float(np.abs(firsts[s] - o).max()))
-    return {"value": n_seqs * sample_steps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"sequences 0..{n_seqs - 1} of {cfg.batch}, decode steps 0..{sample_steps - 1} each "
-                      f"({sample_steps // cfg.omega} routing events per sequence), float64 numpy on the host; "
+    per_seq = done // n_seqs
+    return {"value": done / dt, "unit": "tokens/s", "cores": _host_cores(), "kind": "oracle",
+            "sample": f"sequences 0..{n_seqs - 1} of {cfg.batch}, decode steps 0..{per_seq - 1} each "
+                      f"({per_seq // cfg.omega} routing events per sequence), float64 numpy on the host; "
                       f"{dt:.1f} s"}, worst
+
+
+def cpu_baseline_tok(cfg, K, V, Q, QP, budget_s):
+    """The token-mode oracle (one group per KV head) on sequence 0: its
+    prompt scored and assigned untimed, then decode steps of all its KV-head
+    groups for as many steps as fit in budget_s seconds."""
+    G, P = cfg.group_size, cfg.prefill
+    groups = []
+    for g in range(cfg.n_kv_heads):
+        if cfg.policy == W.POLICY_H2O:
+            from oracle import h2o as oh
+            grp = oh.H2OGroup(K[0, g], V[0, g], G=G, n_sink=cfg.n_sink, n_heavy=cfg.k_full, n_recent=cfg.n_recent)
+        else:
+            from oracle import hqekv as oq
+            ratios32 = tuple(float(np.float32(r)) for r in cfg.ratios)
+            grp = oq.HqeKVGroup(K[0, g], V[0, g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group)
+        grp.prefill(P, QP[0][:, g * G:(g + 1) * G])
+        groups.append(grp)
+    done = 0
+    t0 = time.perf_counter()
+    for s in range(cfg.steps):
+        for g, grp in enumerate(groups):
+            q = Q[0, s][g * G:(g + 1) * G]
+            if cfg.policy == W.POLICY_H2O:
+                grp.step(P + s, q)
+            else:
+                grp.step(s, P + s, q)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": _host_cores(), "kind": "oracle",
+            "sample": f"sequence 0 of {cfg.batch} ({cfg.n_kv_heads} KV-head groups), decode steps 0..{done - 1} "
+                      f"({done // cfg.omega} events), float64 numpy on the host; {dt:.1f} s"}
 
 
 def kernel_source_hash():
@@ -419,6 +463,12 @@ def main():
         n_cpu = min(a.cpu_steps, cfg.steps)
         log(f"bench: oracle baseline on {n_cpu} steps of {a.cpu_seqs} sequences")
         cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_seqs, n_cpu, firsts)
+    elif not a.no_cpu and token_mode:
+        log(f"bench: oracle baseline on sequence 0, up to {CPU_BUDGET_S:.0f} s of decode steps")
+        cpu = cpu_baseline_tok(cfg, K, V, Q, QP, CPU_BUDGET_S)
+    elif not a.no_cpu:
+        log(f"bench: oracle baseline on sequence 0, up to {CPU_BUDGET_S:.0f} s of decode steps")
+        cpu, worst = cpu_baseline(cfg, K, V, Q, 1, cfg.steps, firsts, budget_s=CPU_BUDGET_S)
     kernel = ("tok_attend_kernel<%d>" % cfg.head_dim if token_mode else
               "attend_qevict_kernel<%d, %d>" % (cfg.head_dim, 2 if cfg.group_size == 4 else 1))
     res = {
