@@ -18,9 +18,10 @@
 // call; tokens not yet ranked (and H2O's sinks) are read from the position
 // pages.  The attention kernel streams [sink][BF16 compact][INT4][INT2][INT1]
 // [recent] tiles: full-precision tiles feed bf16 matrix-core operands;
-// quantized tiles are dequantized in registers to exact float32 values and
-// split into two fp16 limbs, so the 16x16x32 fp16 operations keep about 22
-// bits.  Each token slot's probability is emitted relative to the running
+// quantized tiles feed their integer codes to fp16 matrix-core operations
+// against the (exactly scaled) fp16 query, with the per-token scales and
+// zeros applied in float32 and the value scale folded into the probabilities
+// as two fp16 limbs (about 22 bits).  Each token slot's probability is emitted relative to the running
 // maximum; the merge kernel normalizes those with the global (max, sum) of
 // each head and adds each token's mass into an accumulator kept in list order
 // (coalesced; the lists only change at routing calls).  Before a routing call
