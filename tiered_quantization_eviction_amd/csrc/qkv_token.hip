@@ -228,6 +228,19 @@ __device__ __forceinline__ int tok_slot_pos(const TokGeom &g, const TokState &st
   return LOOKUP ? st.qpos[f][(size_t)bh * g.NCT * TS + idx] : 0;
 }
 
+// valid slots [lo, hi) of list tile k of (sequence, KV head) bh
+__device__ __forceinline__ void tok_tile_range(const TokGeom &g, const TokState &st, const TokStep &ts,
+                                               const TokList &L, int bh, int k, int &lo, int &hi) {
+  if (k < L.s0 + L.nC || k >= L.base_r()) {
+    (void)tok_ftile(g, st, ts, L, bh / g.Hkv, bh % g.Hkv, k, lo, hi);
+    return;
+  }
+  int f = 0;
+  while (k >= L.base_q(f + 1)) ++f;
+  lo = 0;
+  hi = min(TS, L.nQtok[f] - (k - L.base_q(f)) * TS);
+}
+
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
@@ -981,43 +994,60 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
   __shared__ float sM[G], sInvL[G];
   const int mb = blockIdx.x - n_out_blocks;
   const int bh = mb / n_parts, part = mb % n_parts;
-  tok_split_stats<G>(g, st, bh, sM, sInvL);
-  const TokList L = tok_list(g, st, ts, bh);
+  const TokList L = tok_list(g, st, ts, bh);   // issued ahead of the statistics wait
   const int n_live = min(L.count(), g.TILES);
+  tok_split_stats<G>(g, st, bh, sM, sInvL);
   const int s0 = ((int)threadIdx.x % (TS / 4)) * 4;
   const bool list_order = g.omega > 1;   // routing every step: straight into the scores
-  for (int k = part * (256 * 4 / TS) + (int)threadIdx.x / (TS / 4); k < n_live; k += n_parts * (256 * 4 / TS)) {
-    const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + k) * G * TS + s0;
-    const float *ref = st.mref + ((size_t)bh * (g.TILES + 1) + k) * G;
-    float4 *accp = (float4 *)(st.tacc + ((size_t)bh * g.TILES + k) * TS + s0);
-    float4 r[G];
-    float w[G];
+  const bool need_pos = mass_out || !list_order;
+  const int stride = n_parts * (256 * 4 / TS);
+  // two tiles per trip, all loads first (the second index is clamped so its
+  // loads stay valid; its results are dropped when it is past the list)
+  for (int k = part * (256 * 4 / TS) + (int)threadIdx.x / (TS / 4); k < n_live; k += 2 * stride) {
+    const int kt[2] = {k, min(k + stride, n_live - 1)};
+    const bool live[2] = {true, k + stride < n_live};
+    float4 r[2][G], acc[2];
+    float ref[2][G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) r[hh] = *(const float4 *)(rho + hh * TS);
+    for (int u = 0; u < 2; ++u) {
+      const float *rho = st.mrho + ((size_t)bh * (g.TILES + 1) + kt[u]) * G * TS + s0;
+      const float *rf = st.mref + ((size_t)bh * (g.TILES + 1) + kt[u]) * G;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) w[hh] = exp2f(ref[hh] - sM[hh]);
-    float4 acc = list_order ? *accp : float4{0.f, 0.f, 0.f, 0.f};
-    float *ap = (float *)&acc;
+      for (int hh = 0; hh < G; ++hh) r[u][hh] = *(const float4 *)(rho + hh * TS);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = (mass_out || !list_order) ? tok_slot_pos<true>(g, st, ts, L, bh, k, s0 + e)
-                                                : tok_slot_pos<false>(g, st, ts, L, bh, k, s0 + e);
-      if (pos < 0) continue;
-      float mass = 0.0f;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float v = ((const float *)&r[hh])[e] * w[hh] * sInvL[hh];
-        if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
-        mass += v;
-      }
-      if (list_order)
-        ap[e] += mass;
-      else
-        st.score[(size_t)bh * g.T + pos] += mass;
-      if (mass_out) mass_out[(size_t)bh * g.T + pos] = mass;
+      for (int hh = 0; hh < G; ++hh) ref[u][hh] = rf[hh];
+      acc[u] = list_order ? *(const float4 *)(st.tacc + ((size_t)bh * g.TILES + kt[u]) * TS + s0)
+                          : float4{0.f, 0.f, 0.f, 0.f};
     }
-    // list order: coalesced, and stable until the next route (which flushes first)
-    if (list_order) *accp = acc;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!live[u]) continue;
+      int lo, hi;
+      tok_tile_range(g, st, ts, L, bh, kt[u], lo, hi);
+      float w[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) w[hh] = exp2f(ref[u][hh] - sM[hh]);
+      float *ap = (float *)&acc[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (s0 + e < lo || s0 + e >= hi) continue;
+        float mass = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float v = ((const float *)&r[u][hh])[e] * w[hh] * sInvL[hh];
+          if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
+          mass += v;
+        }
+        if (list_order) ap[e] += mass;
+        if (need_pos) {
+          const int pos = tok_slot_pos<true>(g, st, ts, L, bh, kt[u], s0 + e);
+          if (!list_order) st.score[(size_t)bh * g.T + pos] += mass;
+          if (mass_out) mass_out[(size_t)bh * g.T + pos] = mass;
+        }
+      }
+      // list order: coalesced, and stable until the next route (which flushes first)
+      if (list_order) *(float4 *)(st.tacc + ((size_t)bh * g.TILES + kt[u]) * TS + s0) = acc[u];
+    }
   }
 }
 
