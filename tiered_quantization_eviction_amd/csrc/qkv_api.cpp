@@ -186,6 +186,7 @@ size_t carve(const Geom &g, char *base, State &st) {
   st.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
   st.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
   st.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
+  st.tail_next = (int32_t *)take((size_t)g.B * g.Hkv * 4);
   st.status = (int32_t *)take(16);
   return off;
 }

@@ -65,6 +65,8 @@ struct State {
   float *part_o;     // [B][Hkv][S][G][d]
   float *part_ml;    // [B][Hkv][S][G][2]  (max in log2 units, sum)
   float *mass_part;  // [B][Hkv][U+1][G][2] (partial mass, reference max)
+  int32_t *tail_next;   // [B][Hkv] next full-precision tail chunk of the attention launch
+                        // in flight; back to zero once the merge has run
   int32_t *status;   // [4] latched device errors
 };
 

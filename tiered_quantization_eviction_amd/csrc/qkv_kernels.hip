@@ -645,6 +645,12 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   }
 }
 
+// Tail of the attention work taken dynamically when every entry is full
+// precision: 1/TAIL_DIV of the entries, in about TAIL_CHUNKS chunks (at least
+// 8 entries each) per (sequence, KV head)
+constexpr int TAIL_DIV = 3;
+constexpr int TAIL_CHUNKS = 32;
+
 // Waves per attention workgroup: one 8-wave workgroup per compute unit
 // holds two waves on each SIMD.
 constexpr int QW = 8;
@@ -687,12 +693,17 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const EntryList L = make_list(g, st, si, b);
   const int A = L.s0 + L.nF, AQ = A + L.nQ, E = L.count();
   const int nB = A + (E - AQ);
+  // With no quantized windows (every entry streams in full precision), all
+  // but 1/TAIL_DIV of the entries are dealt out statically; the rest is a
+  // tail of chunks that the waves of this (sequence, KV head) take in turn
+  // once their static share is done, so that waves which stream slower finish
+  // with less work (wave times differ by tens of percent within a launch).
+  // With quantized windows the static deal stays whole: there, the pairing
+  // of streaming and arithmetic work on each SIMD matters more.
+  const int nBs = L.nQ == 0 ? nB - nB / TAIL_DIV : nB, nQs = L.nQ;
   const int NS = QW * S, gi = split * QW + wave;
-  const int vb0 = (int)((long long)nB * gi / NS), vb1 = (int)((long long)nB * (gi + 1) / NS);
-  const int q0 = A + (int)((long long)L.nQ * gi / NS), q1 = A + (int)((long long)L.nQ * (gi + 1) / NS);
-  // full-precision virtual range [vb0, vb1) -> entries [f0, f1) below A and [r0e, r1e) from AQ on
-  const int f0 = min(vb0, A), f1 = min(vb1, A);
-  const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
+  const int vb0 = (int)((long long)nBs * gi / NS), vb1 = (int)((long long)nBs * (gi + 1) / NS);
+  const int q0 = A + (int)((long long)nQs * gi / NS), q1 = A + (int)((long long)nQs * (gi + 1) / NS);
 
   WaveState<D> ws;
 #pragma unroll
@@ -732,6 +743,11 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // workgroup's waves are dealt to the SIMDs round-robin (w, w+4) or in
   // pairs (2k, 2k+1): one streams full-precision tiles while the other
   // unpacks quantized ones.
+  // tail chunks of full-precision virtual entries [nBs, nB)
+  int32_t *tail = st.tail_next + (b * g.Hkv + h);
+  const int fch = max(8, (nB - nBs + TAIL_CHUNKS - 1) / TAIL_CHUNKS);
+  const int f0 = min(vb0, A), f1 = min(vb1, A);
+  const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
   if (((wave & 1) ^ (wave >> 2)) & 1) {
     run_quant<D, GP>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
@@ -740,6 +756,18 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
     run_quant<D, GP>(ws, c, q0, q1);
+  }
+  // full-precision tail, chunk by chunk until taken (launches without one
+  // issue no atomic)
+  for (; nBs < nB;) {
+    int k = 0;
+    if (lane == 0) k = atomicAdd(tail, 1);
+    k = __builtin_amdgcn_readfirstlane(k);
+    const int lo = nBs + k * fch;
+    if (lo >= nB) break;
+    const int hi = min(lo + fch, nB);
+    run_full<D>(ws, c, min(lo, A), min(hi, A));
+    run_full<D>(ws, c, AQ + max(lo - A, 0), AQ + max(hi - A, 0));
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -825,6 +853,7 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     // outputs of one (sequence, KV head): each thread folds the split
     // partials of its outputs with the LSE rule on its own
     const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
+    if (threadIdx.x == 0) st.tail_next[blockIdx.x] = 0;   // for the next launch
     const float2 *ml = (const float2 *)st.part_ml + (size_t)(b * g.Hkv + h) * S * G;
     const float *po = st.part_o + (size_t)(b * g.Hkv + h) * S * G * D;
     for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
