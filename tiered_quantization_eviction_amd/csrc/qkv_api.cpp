@@ -187,6 +187,7 @@ size_t carve(const Geom &g, char *base, State &st) {
   st.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
   st.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
   st.tail_next = (int32_t *)take((size_t)g.B * g.Hkv * 4);
+  st.slist = (float *)take(BU * 4);
   st.status = (int32_t *)take(16);
   return off;
 }
@@ -509,7 +510,7 @@ int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_st
     }
     return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
   }
-  return hip_err(launch_export(c->g, c->st, what, dst, (hipStream_t)stream));
+  return hip_err(launch_export(c->g, c->st, step_info(c), what, dst, (hipStream_t)stream));
 }
 
 int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {

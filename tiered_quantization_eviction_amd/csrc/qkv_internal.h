@@ -54,7 +54,7 @@ struct State {
   uint8_t *ledger;
   uint8_t *tier;
   uint8_t *has_ledger;
-  float *score;
+  float *score;      // [B][U] per unit
   int32_t *routed;
   int32_t *routed_nf;
   int32_t *routed_nq;
@@ -67,6 +67,9 @@ struct State {
   float *mass_part;  // [B][Hkv][U+1][G][2] (partial mass, reference max)
   int32_t *tail_next;   // [B][Hkv] next full-precision tail chunk of the attention launch
                         // in flight; back to zero once the merge has run
+  float *slist;         // [B][U] scores of the live entries in list order (sink, ranked,
+                        // recent): the per-step merge updates these; score[] is brought up
+                        // to date from them by each routing event and before an export
   int32_t *status;   // [4] latched device errors
 };
 
@@ -242,7 +245,7 @@ hipError_t launch_quantize_window(const void *x, int x_dtype, int n_blocks, int 
                                   int kind, uint8_t *codes, uint16_t *params, hipStream_t s);
 hipError_t launch_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int n,
                              const int32_t *counts, int n_tiers, uint8_t *out, hipStream_t s);
-hipError_t launch_export(const Geom &g, const State &st, int what, void *dst, hipStream_t s);
+hipError_t launch_export(const Geom &g, const State &st, const StepInfo &si, int what, void *dst, hipStream_t s);
 hipError_t read_quantize_status(int *flag, hipStream_t s);
 
 // ---- token-mode launchers (defined in qkv_token.hip) ----

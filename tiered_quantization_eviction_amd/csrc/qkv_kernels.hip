@@ -106,6 +106,13 @@ __device__ inline EntryList make_list(const Geom &g, const State &st, const Step
   return L;
 }
 
+// unit of entry e of list L (routed: the sequence's ranked list)
+__device__ inline int entry_unit(const EntryList &L, const int32_t *routed, int e) {
+  if (e < L.s0) return 0;
+  const int r = e - L.s0;
+  return r < L.nF + L.nQ ? routed[r] : L.r0 + (r - L.nF - L.nQ);
+}
+
 // ---------------------------------------------------------------------------
 // attention: one workgroup per (sequence, KV head, split)
 // ---------------------------------------------------------------------------
@@ -882,24 +889,18 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     }
     return;
   }
-  // masses of up to 256 live entries of one sequence -> window scores; the
-  // entry's unit, old score and first KV heads' (rho, m) pairs are loaded
-  // before the wait for the split statistics
+  // masses of up to 256 live entries of one sequence -> window scores, kept
+  // in list order (the unit of an entry is needed only for mass_out); the
+  // old score and first KV heads' (rho, m) pairs are loaded before the wait
+  // for the split statistics
   const int mb = blockIdx.x - n_out_blocks;
   const int b = mb / n_chunks, chunk = mb % n_chunks;
   const EntryList L = make_list(g, st, si, b);
   const int E = L.count();
   const int e = chunk * blockDim.x + threadIdx.x;
   const int ee = min(e, E - 1);
-  const int raw = st.routed[b * g.U + min(max(ee - L.s0, 0), g.U - 1)];
-  int u;
-  if (ee < L.s0)
-    u = 0;
-  else if (ee - L.s0 < L.nF + L.nQ)
-    u = raw;
-  else
-    u = L.r0 + (ee - L.s0 - L.nF - L.nQ);
-  const float old = st.score[b * g.U + u];
+  const float old = st.slist[b * g.U + ee];
+  const int u_out = mass_out ? entry_unit(L, st.routed + b * g.U, ee) : 0;
   float4 mp[CH][G / 2];   // (rho, m) of the G heads, per KV head
   auto load_heads = [&](int h0) {
 #pragma unroll
@@ -932,11 +933,11 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
           gs += v;
         }
       }
-      if (mass_out && e < E) mass_out[((size_t)b * g.Hkv + h) * g.U + u] = gs;
+      if (mass_out && e < E) mass_out[((size_t)b * g.Hkv + h) * g.U + u_out] = gs;
       total += gs;
     }
   }
-  if (e < E) st.score[b * g.U + u] = old + total;
+  if (e < E) st.slist[b * g.U + e] = old + total;
 }
 
 // LDS of one attention workgroup beyond its static arrays: the q*s limbs of
@@ -1017,7 +1018,7 @@ __device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
     }
 }
 
-__global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, int a0, int a1, int npow) {
+__global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, StepInfo si, int a0, int a1, int npow) {
   extern __shared__ unsigned long long keys[];
   __shared__ int n_pack, n_prom;
   const int b = blockIdx.x;
@@ -1028,6 +1029,14 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, in
     n_pack = 0;
     n_prom = 0;
   }
+  // the list-order scores of the entries so far (sink, ranked, recent
+  // windows a0 .. r1) back to their units
+  {
+    const EntryList L = {si.has_sink, nF, nQ, si.r1 >= a0 ? si.r1 - a0 + 1 : 0, a0};
+    for (int e = threadIdx.x; e < L.count(); e += blockDim.x)
+      st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] = st.slist[b * g.U + e];
+  }
+  __syncthreads();
   for (int i = threadIdx.x; i < npow; i += blockDim.x) {
     unsigned long long key = 0ull;
     if (i < n) {
@@ -1060,28 +1069,60 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, in
     if (r < KFQ) st.routed[b * g.U + r] = u;
   }
   __syncthreads();
+  const int nF2 = min(n, g.k_full), nQ2 = max(0, min(n - g.k_full, g.k_quant));
   if (threadIdx.x == 0) {
-    st.routed_nf[b] = min(n, g.k_full);
-    st.routed_nq[b] = max(0, min(n - g.k_full, g.k_quant));
+    st.routed_nf[b] = nF2;
+    st.routed_nq[b] = nQ2;
     st.pack_count[b] = n_pack;
     st.promote_count[b] = n_prom;
   }
+  // list-order scores of the new list; the slots past it belong to windows
+  // not yet appended (score 0)
+  {
+    const EntryList L = {si.has_sink, nF2, nQ2, si.r1 >= a1 ? si.r1 - a1 + 1 : 0, a1};
+    const int E = L.count();
+    for (int e = threadIdx.x; e < g.U; e += blockDim.x)
+      st.slist[b * g.U + e] = e < E ? st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] : 0.0f;
+  }
 }
 
-// pack (first demotion) and promote (quantized -> full) of listed windows
+// list-order scores -> per-unit scores of the live entries (before an export)
+__global__ __launch_bounds__(256) void slist_sync_kernel(Geom g, State st, StepInfo si) {
+  const int b = blockIdx.y;
+  const EntryList L = make_list(g, st, si, b);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < L.count()) st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] = st.slist[b * g.U + e];
+}
+
+// pack (first demotion) and promote (quantized -> full) of listed windows;
+// one (window, KV head) item at a time per 256-thread workgroup.  Every
+// thread moves whole 16-byte tile chunks: a key chunk is 8 channels of one
+// token, a value chunk 4 tokens of two channels (c, c + 16).
+constexpr int TR_THREADS = 256;
+template <int D> constexpr int TR_ROW = D + 8;   // LDS row (bf16), 16-byte aligned, rows on distinct banks
+
 template <int D>
-__global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State st, int per_seq) {
-  __shared__ float sk[32][D];
-  __shared__ float sv[32][D];
+__global__ __launch_bounds__(TR_THREADS) void transitions_qevict_kernel(Geom g, State st, int per_seq) {
+  constexpr int NKD = D / 64;
+  constexpr int CHUNKS = TS * D / 8;   // 16-byte chunks per K (or V) tile
+  static_assert(CHUNKS <= TR_THREADS && D + 32 * (D / 32) <= TR_THREADS, "workgroup too small");
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2 * TS][TR_ROW<D>];   // bf16 of the window, [token][channel]
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2 * TS][TR_ROW<D>];
   __shared__ half_t s_ks[D], s_kz[D];
-  __shared__ half_t s_vs[32][D / 32], s_vz[32][D / 32];
+  __shared__ half_t s_vs[2 * TS][D / 32], s_vz[2 * TS][D / 32];
   const int b = blockIdx.x / per_seq;
   const int w0 = blockIdx.x % per_seq;
   const int npk = st.pack_count[b];
   const int npr = st.promote_count[b];
   const int items = (npk + npr) * g.Hkv;
-  const int W = g.window;
+  const int W = g.window, tpw = g.tpw;
   const float levels = 3.0f;
+  const int ci = threadIdx.x;
+  const bool own = ci < CHUNKS;   // threads with a key and a value chunk of each tile
+  // key chunk ci: token kt_t, channels kt_c .. +7; value chunk ci: tokens
+  // 4 vt_q .. +3 of channels vt_c and vt_c + 16
+  const int kt_t = ci % 16, kt_c = (ci / 64) * 32 + ((ci % 64) / 16) * 8;
+  const int vt_q = (ci % 64) / 16, vt_c = (ci / 64) * 32 + ci % 16;
   for (int it = w0; it < items; it += per_seq) {
     const int i = it / g.Hkv, h = it % g.Hkv;
     const bool pack = i < npk;
@@ -1090,30 +1131,40 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
     uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
     half_t *kparam = (half_t *)Lb;
     if (pack) {
-      // 1. tiles -> LDS in logical order
-      for (int tile = 0; tile < g.tpw; ++tile) {
-        const uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
-        const uint16_t *vt = kt + TS * D;
-        for (int ci = threadIdx.x; ci < TS * D / 8; ci += blockDim.x) {
-          const int kb = ci / 64, l = ci % 64;
-          const int t = l % 16, c0 = kb * 32 + (l / 16) * 8;
-          const uint16_t *src = kt + ci * 8;
+      // 1. tiles -> LDS in logical order (all loads issued before the stores)
+      if (own) {
+        uint4 kch[2], vch[2];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sk[tile * TS + t][c0 + j] = bf16_to_f32(src[j]);
+        for (int tile = 0; tile < 2; ++tile) {
+          const uint16_t *kt = pg + (size_t)min(tile, tpw - 1) * 2 * TS * D;
+          kch[tile] = *(const uint4 *)(kt + ci * 8);
+          vch[tile] = *(const uint4 *)(kt + TS * D + ci * 8);
         }
-        for (int el = threadIdx.x; el < TS * D; el += blockDim.x) {
-          const int t = el / D, c = el % D;
-          sv[tile * TS + t][c] = bf16_to_f32(vt[v_tile_index(t, c)]);
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          if (tile >= tpw) break;
+          *(uint4 *)&sk[tile * TS + kt_t][kt_c] = kch[tile];
+          const uint16_t *e = (const uint16_t *)&vch[tile];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[tile * TS + 4 * vt_q + j][vt_c + 16 * hf] = e[hf * 4 + j];
         }
       }
       __syncthreads();
-      // 2. key parameters per channel over the window's tokens
-      for (int c = threadIdx.x; c < D; c += blockDim.x) {
-        float mn = sk[0][c], mx = sk[0][c];
-        for (int t = 1; t < W; ++t) {
-          mn = fminf(mn, sk[t][c]);
-          mx = fmaxf(mx, sk[t][c]);
-        }
+      // 2. key parameters per channel over the window's tokens (threads
+      // 0 .. D-1); value parameters per token and 32-channel group (the
+      // upper half of the workgroup)
+      if (ci < D) {
+        const int c = ci;
+        float mn = bf16_to_f32(sk[0][c]), mx = mn;
+        for (int t0 = 0; t0 < W; t0 += 8)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float x = bf16_to_f32(sk[t0 + k][c]);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+          }
         const half_t s16 = (half_t)((mx - mn) / levels);
         const half_t z16 = (half_t)mn;
         if (!isfinite((float)s16) || !isfinite((float)z16)) st.status[0] = QKV_ERANGE;
@@ -1122,13 +1173,21 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
         kparam[c] = s16;
         kparam[D + c] = z16;
       }
-      // value parameters per token per 32-channel group
-      for (int it2 = threadIdx.x; it2 < W * (D / 32); it2 += blockDim.x) {
+      if (ci >= TR_THREADS - W * (D / 32)) {
+        const int it2 = ci - (TR_THREADS - W * (D / 32));
         const int t = it2 / (D / 32), grp = it2 % (D / 32);
-        float mn = sv[t][grp * 32], mx = mn;
-        for (int c = 1; c < 32; ++c) {
-          mn = fminf(mn, sv[t][grp * 32 + c]);
-          mx = fmaxf(mx, sv[t][grp * 32 + c]);
+        const uint4 *row = (const uint4 *)&sv[t][grp * 32];
+        float mn = bf16_to_f32(sv[t][grp * 32]), mx = mn;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint4 r = row[q4];
+          const uint16_t *e = (const uint16_t *)&r;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = bf16_to_f32(e[j]);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+          }
         }
         const half_t s16 = (half_t)((mx - mn) / levels);
         const half_t z16 = (half_t)mn;
@@ -1141,54 +1200,68 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
         vp[vparam_index(g, t % TS, grp, 1)] = z16;
       }
       __syncthreads();
-      // 3. codes in the matrix-core operand order: one thread per code dword,
-      // walking its 16 slots (the inverse of kcode_slot / vcode_slot)
-      for (int tile = 0; tile < g.tpw; ++tile) {
+      // 3. codes in the matrix-core operand order: one thread per (tile, code
+      // dword), walking its 16 slots (the inverse of kcode_slot / vcode_slot)
+      for (int dw2 = ci; dw2 < tpw * NKD * 64; dw2 += TR_THREADS) {
+        const int tile = dw2 / (NKD * 64), dw = dw2 % (NKD * 64);
         uint32_t *tc = (uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes);
-        constexpr int NKD = D / 64;
-        for (int dw = threadIdx.x; dw < NKD * 64; dw += blockDim.x) {
-          const int j = dw / 64, l = dw % 64;
-          uint32_t kword = 0u, vword = 0u;
+        const int j = dw / 64, l = dw % 64;
+        uint32_t kword = 0u, vword = 0u;
 #pragma unroll
-          for (int p = 0; p < 16; ++p) {
-            const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
-            {  // key slot p: k-block 2j+par, channel pair m, element hi
-              const int c = (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi, t = l % 16;
-              const int tt = tile * TS + t;
-              kword |= (tt < W ? quant_code(sk[tt][c], s_ks[c], s_kz[c], levels) : 0u) << (2 * p);
-            }
-            {  // value slot p: column tile 4j+m, token pair par of the quad, element hi
-              const int c = (4 * j + m) * 16 + l % 16, t = 4 * (l / 16) + 2 * par + hi;
-              const int tt = tile * TS + t;
-              vword |= (tt < W ? quant_code(sv[tt][c], s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u) << (2 * p);
-            }
+        for (int p = 0; p < 16; ++p) {
+          const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
+          {  // key slot p: k-block 2j+par, channel pair m, element hi
+            const int c = (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi, t = l % 16;
+            const int tt = tile * TS + t;
+            kword |= (tt < W ? quant_code(bf16_to_f32(sk[tt][c]), s_ks[c], s_kz[c], levels) : 0u) << (2 * p);
           }
-          tc[l * 2 * NKD + j] = kword;
-          tc[l * 2 * NKD + NKD + j] = vword;
+          {  // value slot p: column tile 4j+m, token pair par of the quad, element hi
+            const int c = (4 * j + m) * 16 + l % 16, t = 4 * (l / 16) + 2 * par + hi;
+            const int tt = tile * TS + t;
+            vword |= (tt < W ? quant_code(bf16_to_f32(sv[tt][c]), s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u)
+                     << (2 * p);
+          }
         }
+        tc[l * 2 * NKD + j] = kword;
+        tc[l * 2 * NKD + NKD + j] = vword;
       }
       __syncthreads();
     } else {
-      // promote: rebuild the full-precision tiles from the ledger
-      for (int tile = 0; tile < g.tpw; ++tile) {
+      // promote: rebuild the full-precision tiles from the ledger, one key
+      // chunk and one value chunk per thread and tile
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        if (tile >= tpw || !own) break;
         const uint8_t *T = Lb + g.kparam_bytes + tile * g.tile_block_bytes;
         const uint32_t *tc = (const uint32_t *)T;
         const half_t *vp = (const half_t *)(T + g.tile_kcode_bytes + g.tile_vcode_bytes);
         uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
-        uint16_t *vt = kt + TS * D;
-        for (int el = threadIdx.x; el < TS * D; el += blockDim.x) {
-          const int t = el / D, c = el % D;
-          int dw, sh;
-          kcode_slot(t, c, D / 64, dw, sh);
-          const float kcode = (float)((tc[dw] >> sh) & 3u);
-          const float kx = __builtin_fmaf(kcode, (float)kparam[c], (float)kparam[D + c]);
-          kt[k_tile_index(t, c)] = f32_to_bf16_rne(kx);
-          vcode_slot(t, c, D / 64, dw, sh);
-          const float vcode = (float)((tc[dw] >> sh) & 3u);
-          const float vx = __builtin_fmaf(vcode, (float)vp[vparam_index(g, t, c / 32, 0)],
-                                          (float)vp[vparam_index(g, t, c / 32, 1)]);
-          vt[v_tile_index(t, c)] = f32_to_bf16_rne(vx);
+        // keys: the chunk's 8 channels share one code dword (kcode_slot)
+        int kdw, vdw, sh;
+        kcode_slot(kt_t, kt_c, NKD, kdw, sh);
+        vcode_slot(4 * vt_q, vt_c, NKD, vdw, sh);
+        const uint32_t kw = tc[kdw], vw = tc[vdw];
+        const uint4 ks4 = *(const uint4 *)(kparam + kt_c), kz4 = *(const uint4 *)(kparam + D + kt_c);
+        const uint4 vpar = *(const uint4 *)(vp + vparam_index(g, 4 * vt_q, vt_c / 32, 0));
+        const half_t *ks = (const half_t *)&ks4, *kz = (const half_t *)&kz4, *vps = (const half_t *)&vpar;
+        uint4 ko, vo;
+        uint16_t *ke = (uint16_t *)&ko, *ve = (uint16_t *)&vo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kcode_slot(kt_t, kt_c + e, NKD, kdw, sh);
+          const float kcode = (float)((kw >> sh) & 3u);
+          ke[e] = f32_to_bf16_rne(__builtin_fmaf(kcode, (float)ks[e], (float)kz[e]));
         }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vcode_slot(4 * vt_q + j, vt_c + 16 * hf, NKD, vdw, sh);
+            const float vcode = (float)((vw >> sh) & 3u);
+            ve[hf * 4 + j] = f32_to_bf16_rne(__builtin_fmaf(vcode, (float)vps[j], (float)vps[4 + j]));
+          }
+        *(uint4 *)(kt + ci * 8) = ko;
+        *(uint4 *)(kt + TS * D + ci * 8) = vo;
       }
     }
   }
@@ -1196,20 +1269,19 @@ __global__ __launch_bounds__(256) void transitions_qevict_kernel(Geom g, State s
 
 hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
                         hipStream_t s) {
-  (void)si;
   int bound = n_cand > 1 ? n_cand : 1;   // ranked windows + newly aged windows (same for every sequence)
   int npow = 1;
   while (npow < bound) npow <<= 1;
   if (npow > SORT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(route_qevict_kernel, dim3(g.B), dim3(1024), npow * sizeof(unsigned long long), s, g, st, a0,
+  hipLaunchKernelGGL(route_qevict_kernel, dim3(g.B), dim3(1024), npow * sizeof(unsigned long long), s, g, st, si, a0,
                      a1, npow);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_seq = 128;
   if (g.d == 128)
-    hipLaunchKernelGGL(transitions_qevict_kernel<128>, dim3(g.B * per_seq), dim3(256), 0, s, g, st, per_seq);
+    hipLaunchKernelGGL(transitions_qevict_kernel<128>, dim3(g.B * per_seq), dim3(TR_THREADS), 0, s, g, st, per_seq);
   else
-    hipLaunchKernelGGL(transitions_qevict_kernel<64>, dim3(g.B * per_seq), dim3(256), 0, s, g, st, per_seq);
+    hipLaunchKernelGGL(transitions_qevict_kernel<64>, dim3(g.B * per_seq), dim3(TR_THREADS), 0, s, g, st, per_seq);
   return hipGetLastError();
 }
 
@@ -1483,11 +1555,15 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
   }
 }
 
-hipError_t launch_export(const Geom &g, const State &st, int what, void *dst, hipStream_t s) {
+hipError_t launch_export(const Geom &g, const State &st, const StepInfo &si, int what, void *dst, hipStream_t s) {
   if (what == QKV_EXPORT_TIERS)
     return hipMemcpyAsync(dst, st.tier, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
-  if (what == QKV_EXPORT_SCORES)
+  if (what == QKV_EXPORT_SCORES) {
+    hipLaunchKernelGGL(slist_sync_kernel, dim3((g.U + 255) / 256, g.B), dim3(256), 0, s, g, st, si);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     return hipMemcpyAsync(dst, st.score, (size_t)g.B * g.U * sizeof(float), hipMemcpyDeviceToDevice, s);
+  }
   if (what == QKV_EXPORT_LEDGER)
     return hipMemcpyAsync(dst, st.has_ledger, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
   hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, s, g, st, what, dst);
