@@ -260,6 +260,11 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
       delete c;
       return rc != QKV_OK ? rc : QKV_EINVAL;   // (d = 128 with eight heads per KV head needs 32-token windows)
     }
+    rc = hip_err(transitions_shape(c->g));
+    if (rc != QKV_OK) {
+      delete c;
+      return rc;
+    }
     need = carve(c->g, (char *)workspace, c->st);
   }
   if (bytes < need) {

@@ -47,6 +47,7 @@ struct Geom {
   int tile_vcode_bytes;
   int tile_vparam_bytes; // 4 token quads * d/32 groups * 16 B
   int tile_block_bytes;
+  int tr_per_seq;        // workgroups per sequence of the pack/promote launch (one resident round)
 };
 
 struct State {
@@ -241,6 +242,7 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
 hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
                         hipStream_t s);
 hipError_t attend_lds_fits(const Geom &g, bool *fits);   // the attention workgroup's LDS fits the device
+hipError_t transitions_shape(Geom &g);
 hipError_t launch_quantize_window(const void *x, int x_dtype, int n_blocks, int tokens, int d, int bits, int group,
                                   int kind, uint8_t *codes, uint16_t *params, hipStream_t s);
 hipError_t launch_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int n,

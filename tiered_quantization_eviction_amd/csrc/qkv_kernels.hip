@@ -834,16 +834,21 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // global (max, 1/sum) of head hh of KV head h over the splits
 __device__ inline void split_stats(const Geom &g, const State &st, int b, int h, int hh, float &M, float &invL) {
+  constexpr int CH = 8;   // splits whose (max, sum) loads are issued together
   const int S = g.n_splits, G = g.G;
-  const float *ml = st.part_ml + ((size_t)(b * g.Hkv + h) * S * G + hh) * 2;
+  const float2 *ml = (const float2 *)st.part_ml + (size_t)(b * g.Hkv + h) * S * G + hh;
   float m = neg_inf(), l = 0.0f;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float ms = ml[(size_t)s * G * 2], ls = ml[(size_t)s * G * 2 + 1];
-    if (ms == neg_inf()) continue;
-    const float mn = fmaxf(m, ms);
-    l = (m == neg_inf() ? 0.0f : l * exp2f(m - mn)) + ls * exp2f(ms - mn);
-    m = mn;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float2 p[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) p[k] = ml[(size_t)min(s0 + k, S - 1) * G];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (s0 + k >= S || p[k].x == neg_inf()) continue;
+      const float mn = fmaxf(m, p[k].x);
+      l = (m == neg_inf() ? 0.0f : l * exp2f(m - mn)) + p[k].y * exp2f(p[k].x - mn);
+      m = mn;
+    }
   }
   M = m;
   invL = 1.0f / l;
@@ -1102,7 +1107,8 @@ constexpr int TR_THREADS = 256;
 template <int D> constexpr int TR_ROW = D + 8;   // LDS row (bf16), 16-byte aligned, rows on distinct banks
 
 template <int D>
-__global__ __launch_bounds__(TR_THREADS) void transitions_qevict_kernel(Geom g, State st, int per_seq) {
+__global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void transitions_qevict_kernel(
+    Geom g, State st, int per_seq) {
   constexpr int NKD = D / 64;
   constexpr int CHUNKS = TS * D / 8;   // 16-byte chunks per K (or V) tile
   static_assert(CHUNKS <= TR_THREADS && D + 32 * (D / 32) <= TR_THREADS, "workgroup too small");
@@ -1123,10 +1129,17 @@ __global__ __launch_bounds__(TR_THREADS) void transitions_qevict_kernel(Geom g, 
   // 4 vt_q .. +3 of channels vt_c and vt_c + 16
   const int kt_t = ci % 16, kt_c = (ci / 64) * 32 + ((ci % 64) / 16) * 8;
   const int vt_q = (ci % 64) / 16, vt_c = (ci / 64) * 32 + ci % 16;
+  // window of item it (the next item's is fetched while this one is worked on)
+  auto item_unit = [&](int it) {
+    const int i = min(it, items - 1) / g.Hkv;
+    return i < npk ? st.pack_list[b * g.U + i] : st.promote_list[b * g.U + (i - npk)];
+  };
+  int u_next = items > w0 ? item_unit(w0) : 0;
   for (int it = w0; it < items; it += per_seq) {
     const int i = it / g.Hkv, h = it % g.Hkv;
     const bool pack = i < npk;
-    const int u = pack ? st.pack_list[b * g.U + i] : st.promote_list[b * g.U + (i - npk)];
+    const int u = u_next;
+    u_next = item_unit(it + per_seq);
     uint16_t *pg = st.pages + page_offset(g, b, u, h);
     uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
     half_t *kparam = (half_t *)Lb;
@@ -1267,6 +1280,19 @@ __global__ __launch_bounds__(TR_THREADS) void transitions_qevict_kernel(Geom g, 
   }
 }
 
+// pack/promote workgroups per sequence: as many as the device holds at once
+// (the lists of a routing event are short after the first one)
+hipError_t transitions_shape(Geom &g) {
+  int dev = 0, n_cu = 0, per_cu = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  const void *f = g.d == 128 ? (const void *)transitions_qevict_kernel<128> : (const void *)transitions_qevict_kernel<64>;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, TR_THREADS, 0)) != hipSuccess) return e;
+  g.tr_per_seq = per_cu * n_cu / g.B > 1 ? per_cu * n_cu / g.B : 1;
+  return hipSuccess;
+}
+
 hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
                         hipStream_t s) {
   int bound = n_cand > 1 ? n_cand : 1;   // ranked windows + newly aged windows (same for every sequence)
@@ -1277,7 +1303,7 @@ hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int 
                      a1, npow);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int per_seq = 128;
+  const int per_seq = g.tr_per_seq > 0 ? g.tr_per_seq : 128;
   if (g.d == 128)
     hipLaunchKernelGGL(transitions_qevict_kernel<128>, dim3(g.B * per_seq), dim3(TR_THREADS), 0, s, g, st, per_seq);
   else
