@@ -27,6 +27,9 @@ Modules and the passages they follow:
                    re-quantization (HqeKV notes sections 3.2-3.5, 3.7).
 * ``budget``    -- capacity and payload arithmetic (QEvict section 4.3/4.5;
                    KV-cache evolution page sections 2, 5, 10).
+* ``diagnostics`` -- future missed mass, mass by tier, selection churn and
+                   long-term importance recovery against full-cache attention
+                   (QEvict notes section 3).
 
 Readings of silent or ambiguous passages are stated where they are used.
 """

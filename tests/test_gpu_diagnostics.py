@@ -1,0 +1,126 @@
+"""Routing diagnostics of the GPU path against a full-cache oracle run.
+
+QEvict notes, section 3: future missed mass (FMM), the split of the
+full-cache attention over the tiers, selection churn and long-term importance
+recovery (LIR).  The tiers come from the library (exported after every
+routing event; they equal the oracle's bit for bit, which the parity tests
+check on the same configuration); the full-cache attention comes from the
+oracle, in float64, over every token appended so far.
+
+The workload is the drift recipe at a size the oracle follows quickly: a
+2048-token prompt, 160 decode steps, a query switch at step 64 after which
+the early cluster (held in INT2 by the three-tier policy) carries the
+attention.  The three-tier policy (K_f, K_q) is compared with a two-tier
+policy holding the same number of bytes in full precision only
+(K_f' = floor((K_f M_f + K_q M_q) / M_f), M = bytes of one window and KV
+head in each tier, QEvict notes section 4.3).  What the pages fix
+qualitatively, and the test asserts: at equal bytes the three-tier policy
+misses less future mass and evicts less of the full-cache attention; a
+two-tier policy never re-admits a window (LIR = 0), the three-tier one does
+after the switch (promotions).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import budget
+from oracle import diagnostics as dg
+from oracle.numerics import bf16_to_f64
+from oracle.qevict import EVICTED, FULL, QUANT, RECENT, SINK
+
+from _harness import QEvictGPURun, gpu_inputs, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiered_quantization_eviction_amd  # noqa: F401  (raises if the library is missing)
+    return torch
+
+
+def _three_tier():
+    c = W.DRIFT.replace(name="drift_diag", batch=2, n_q_heads=16, n_kv_heads=4, head_dim=128, prefill=2048,
+                        steps=160, window=16, omega=16, n_sink=5, n_recent=64, cluster_a=(60, 24),
+                        cluster_b=(4, 12), switch_step=64)
+    w0 = W.w0(c)
+    return c.replace(k_full=int(0.1 * w0), k_quant=int(0.3 * w0))
+
+
+def _two_tier(c3):
+    m_full = 2 * c3.window * c3.head_dim * 2
+    m_quant = budget.window_ledger_bytes(c3.window, c3.head_dim, c3.quant_bits, c3.group)
+    return c3.replace(k_full=(c3.k_full * m_full + c3.k_quant * m_quant) // m_full, k_quant=0)
+
+
+def _diagnose(cfg, torch, K, V, Q, full_attn, label):
+    """Step the GPU path; per step the FMM and tier shares of the full-cache
+    attention under the tiers in force at that step; per event the sets."""
+    run = QEvictGPURun(cfg, K, V, Q)
+    B, P = cfg.batch, cfg.prefill
+    pos = np.arange(cfg.total_tokens)
+    unit_of_pos = np.where(pos < cfg.n_sink, 0, 1 + (pos - cfg.n_sink) // cfg.window)
+    tiers = run.tiers()
+    fmm = {b: [] for b in range(B)}
+    shares = {b: [] for b in range(B)}
+    full_sets = {b: [] for b in range(B)}
+    kept_sets = {b: [] for b in range(B)}
+    for s in range(cfg.steps):
+        N = P + s + 1
+        for b in range(B):
+            t_pos = tiers[b][unit_of_pos[:N]].copy()
+            t_pos[t_pos == 0] = RECENT            # a window begun since the last export is recent
+            p = full_attn[b][s]
+            fmm[b].append(dg.future_missed_mass(p, t_pos != EVICTED))
+            sh = dg.tier_shares(p, t_pos, (SINK, RECENT, FULL, QUANT, EVICTED))
+            shares[b].append((sh[SINK] + sh[RECENT], sh[FULL], sh[QUANT], sh[EVICTED]))
+        if run.step(want_mass=False):
+            tiers = run.tiers()
+            for b in range(B):
+                full_sets[b].append(set(np.flatnonzero(tiers[b] == FULL).tolist()))
+                kept_sets[b].append(set(np.flatnonzero((tiers[b] == FULL) | (tiers[b] == QUANT)).tolist()))
+    first = cfg.omega               # steps after the first event
+    res = {
+        "fmm": float(np.mean([np.mean(fmm[b][first:]) for b in range(B)])),
+        "fmm_after_switch": float(np.mean([np.mean(fmm[b][cfg.switch_step + cfg.omega:]) for b in range(B)])),
+        "shares": np.mean([np.mean(shares[b][first:], axis=0) for b in range(B)], axis=0),
+        "churn_full": float(np.mean([np.mean(dg.churn(full_sets[b])) for b in range(B)])),
+        "churn_kept": float(np.mean([np.mean(dg.churn(kept_sets[b])) for b in range(B)])),
+        "recovery": [dg.recovery_counts(full_sets[b]) for b in range(B)],
+        "lir": float(np.mean([dg.lir(full_sets[b]) for b in range(B)])),
+    }
+    r, f, q, e = res["shares"]
+    log(f"[{label}] K_f={cfg.k_full} K_q={cfg.k_quant}: FMM {res['fmm']:.4f} (after the switch "
+        f"{res['fmm_after_switch']:.4f}); full-cache attention on recent/sink {r:.3f}, full {f:.3f}, "
+        f"INT2 {q:.3f}, evicted {e:.3f}; churn full {res['churn_full']:.4f}, kept {res['churn_kept']:.4f}; "
+        f"LIR {res['lir']:.4f} (re-entries, exits per sequence {res['recovery']})")
+    return res
+
+
+def test_diagnostics_three_tier_against_two_tier_at_equal_bytes(torch_cuda):
+    torch = torch_cuda
+    c3 = _three_tier()
+    c2 = _two_tier(c3)
+    wl = W.Workload(c3)
+    K, V, Q = gpu_inputs(c3, wl)
+    log(f"[diag] three-tier K_f={c3.k_full} K_q={c3.k_quant}; two-tier at equal bytes K_f={c2.k_full}")
+    full_attn = {}
+    for b in range(c3.batch):
+        k, _ = wl.kv(b)
+        kf = bf16_to_f64(k)
+        qs = bf16_to_f64(wl.queries(b))
+        full_attn[b] = [dg.full_attention(qs[s], kf[:, :c3.prefill + s + 1]) for s in range(c3.steps)]
+    log("[diag] full-cache attention of every step computed")
+    r3 = _diagnose(c3, torch, K, V, Q, full_attn, "three-tier")
+    r2 = _diagnose(c2, torch, K, V, Q, full_attn, "two-tier")
+    assert r3["fmm"] < r2["fmm"], (r3["fmm"], r2["fmm"])
+    assert r3["fmm_after_switch"] < r2["fmm_after_switch"]
+    assert r3["shares"][3] < r2["shares"][3]
+    assert r2["lir"] == 0.0 and all(re == 0 for re, _ in r2["recovery"])
+    assert r3["lir"] > 0.0, "no window came back into the full-precision set after the switch"
+    for r in (r2, r3):
+        assert abs(float(np.sum(r["shares"])) - 1.0) < 1e-9
+        assert r["fmm"] == pytest.approx(float(r["shares"][3]), abs=1e-12)
