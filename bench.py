@@ -350,7 +350,8 @@ def cpu_baseline_tok(cfg, K, V, Q, QP, budget_s):
         else:
             from oracle import hqekv as oq
             ratios32 = tuple(float(np.float32(r)) for r in cfg.ratios)
-            grp = oq.HqeKVGroup(K[0, g], V[0, g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group)
+            grp = oq.HqeKVGroup(K[0, g], V[0, g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
+                                window=cfg.score_window)
         grp.prefill(P, QP[0][:, g * G:(g + 1) * G])
         groups.append(grp)
     done = 0

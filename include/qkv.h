@@ -81,6 +81,11 @@ typedef struct qkv_config {
   int32_t group;      /* quantization group (32)                            */
   int32_t max_ctx;    /* capacity in tokens per sequence                    */
   int32_t n_splits;   /* attention splits per (sequence, KV head); 0 = auto */
+  int32_t score_window; /* HqeKV: 0 = every decode step adds to the scores;
+                         * m in [1, omega] = a rolling window of the last m
+                         * queries (HqeKV notes 3.8, 3.10): only the last m
+                         * decode steps before each event add, and the scores
+                         * restart from 0 after every event.  0 otherwise.   */
 } qkv_config;
 
 /* Bytes of device workspace a cache with this configuration needs, or 0 if

@@ -19,7 +19,10 @@ HqeKV notes:
 
 Readings: granularity is per token (keys too: groups of 32 channels of one
 token); scores accumulate over every scoring query (prompt tail and all decode
-steps); at an event the tokens appended since the previous event keep full
+steps), or, with a rolling window of m queries (sections 3.8 and 3.10: the
+metric is kept over the most recent m = 20 queries), over the prompt tail
+for the first assignment and then over the last m decode steps before each
+event only, the scores starting again from 0 after every event; at an event the tokens appended since the previous event keep full
 precision and are not ranked; share counts are floor(r_k * N) with N the
 number of tokens ever appended, cut in the order FP16, 4-bit, 2-bit, 1-bit,
 the rest evicted; a downgraded token is re-quantized from its current
@@ -56,11 +59,12 @@ def assign(metric, pos, eligible, counts):
 class HqeKVGroup:
     """HqeKV state of one (sequence, KV head): per-token tiers and contents."""
 
-    def __init__(self, k_rows, v_rows, *, G: int, ratios, period: int, group: int = 32):
+    def __init__(self, k_rows, v_rows, *, G: int, ratios, period: int, group: int = 32, window: int = 0):
         self.korig = bf16_to_f64(k_rows)          # [T, d]
         self.vorig = bf16_to_f64(v_rows)
         self.T, self.d = self.korig.shape
         self.G, self.ratios, self.period, self.group = G, tuple(ratios), period, group
+        self.window = window                       # 0: accumulate every step; m: the last m before an event
         self.kcur = self.korig.copy()
         self.vcur = self.vorig.copy()
         self.tier = np.full(self.T, 255, np.uint8)   # 255: not appended yet
@@ -100,7 +104,8 @@ class HqeKVGroup:
         self.tier[t] = BF16
         self.N = t + 1
         out, idx, w = self._attend(q_bits, self.N)
-        self.score[idx] += w
+        if self.window == 0 or s % self.period >= self.period - self.window:
+            self.score[idx] += w
         if (s + 1) % self.period == 0:
             self.event()
         return out, idx, w
@@ -120,6 +125,9 @@ class HqeKVGroup:
             if new > self.tier[t]:
                 self._requantize(t, new)
         self.last_event_N = N
+        self.last_metric = metric
+        if self.window:
+            self.score[:] = 0.0
 
     def _requantize(self, t: int, new: int):
         if new == EVICT:

@@ -68,6 +68,19 @@ def test_config_checks_on_host():
         assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, window
 
 
+def test_score_window_checks_on_host():
+    """A rolling score window belongs to HqeKV and spans at most one period."""
+    L, lib = _lib()
+    for window, ok in ((0, True), (20, True), (64, True), (65, False), (-1, False)):
+        c = L.make_config(W.HQEKV)
+        c.score_window = window
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, window
+    for cfg in (W.TINY, W.H2O):
+        c = L.make_config(cfg)
+        c.score_window = 1
+        assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL, cfg.name
+
+
 def test_strerror_and_info_arguments():
     L, lib = _lib()
     assert lib.qkv_strerror(L.ERANGE).decode().startswith("quantization parameter")

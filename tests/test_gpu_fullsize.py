@@ -115,7 +115,8 @@ def test_hqekv_fullsize_sampled(torch_cuda):
     groups = {}
     for b, g in sampled:
         k, v = wl.kv(b)
-        grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group)
+        grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
+                            window=cfg.score_window)
         grp.prefill(P, qt[b][:, g * G:(g + 1) * G])
         groups[b, g] = grp
         log(f"[{label}] oracle (seq {b}, head {g}) prompt assigned")

@@ -91,7 +91,8 @@ def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
     for b in range(B):
         k, v = wl.kv(b)
         for g in range(Hkv):
-            grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group)
+            grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
+                                window=cfg.score_window)
             grp.prefill(P, qt[b][:, g * G:(g + 1) * G])
             groups[b, g] = grp
 
@@ -177,6 +178,15 @@ def test_hqekv_d64_g8_splits_parity(torch_cuda):
     cfg = W.HQEKV.replace(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=64, prefill=700, steps=96, omega=32,
                           init_queries=8)
     _run_hqekv(cfg, torch_cuda, n_splits=3, label="hqekv-d64-g8")
+
+
+def test_hqekv_rolling_window_parity(torch_cuda):
+    """A rolling window of the last 20 queries (HqeKV notes 3.8 and 3.10) with
+    an event every 32 tokens: only the 20 decode steps before an event add to
+    the scores, which restart from 0 after it; tiers, codes and outputs
+    against the oracle over four events."""
+    cfg = W.HQEKV.replace(batch=2, n_q_heads=16, n_kv_heads=4, prefill=1024, steps=128, omega=32, score_window=20)
+    _run_hqekv(cfg, torch_cuda, label="hqekv-rolling")
 
 
 @pytest.mark.parametrize("prefill", [1024, 4096])

@@ -239,3 +239,40 @@ def test_hqekv_all_full_precision_is_exact_attention():
         out, _, _ = g.step(s, t, qb[s])
         ref, _ = attend(bf16_to_f64(qb[s]), K[:, :t + 1], V[:, :t + 1])
         np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+def test_hqekv_rolling_window_ranks_by_the_last_m_steps():
+    """HqeKV notes 3.8 and 3.10: with a rolling window of the last m queries
+    the metric of an event is the attention of the m decode steps before it.
+    Checked against an accumulating run of the same (sequence, KV head): both
+    runs share the first assignment (the same prompt queries) and so every
+    tier until the second event, so the rolling run's metric there must equal
+    the accumulating run's score growth over those m steps times the value
+    range; and the rolling scores restart from 0 after each event."""
+    cfg = W.HQEKV.replace(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, prefill=512, steps=64,
+                          omega=32, init_queries=20)
+    m, P, T = 20, cfg.prefill, cfg.omega
+    wl = W.Workload(cfg)
+    kb, vb = wl.kv(0)
+    acc = oq.HqeKVGroup(kb[0], vb[0], G=4, ratios=cfg.ratios, period=T)
+    rol = oq.HqeKVGroup(kb[0], vb[0], G=4, ratios=cfg.ratios, period=T, window=m)
+    pq = wl.prefill_queries(0, P - 20, P)
+    acc.prefill(P, pq)
+    rol.prefill(P, pq)
+    np.testing.assert_array_equal(acc.tier, rol.tier)
+    np.testing.assert_array_equal(rol.last_metric, acc.last_metric)
+    assert not rol.score.any()
+    qb = wl.queries(0)
+    for s in range(T):
+        if s == T - m:
+            start = acc.score.copy()
+        if s < T - m:
+            before = rol.score.copy()
+        acc.step(s, P + s, qb[s])
+        rol.step(s, P + s, qb[s])
+        if s < T - m:
+            np.testing.assert_array_equal(rol.score, before)    # outside the window: no change
+    grown = (acc.score - start) * rol.range
+    np.testing.assert_allclose(rol.last_metric, grown, rtol=1e-9, atol=1e-12 * float(np.max(acc.score)))
+    assert np.count_nonzero(rol.last_metric) > 0
+    assert not rol.score.any()

@@ -24,6 +24,7 @@ struct qkv_cache {
   // token mode with a routing period above 1: masses wait in list order until
   // a flush (before a route or a score export)
   mutable bool tacc_dirty = false;
+  int steps_since_route = 0;   // decode steps since the last routing / assignment event
   void *ws;
   size_t ws_bytes;
   int N;          // tokens appended per sequence
@@ -51,6 +52,9 @@ int validate(const qkv_config *c) {
   if (c->head_dim != 64 && c->head_dim != 128) return QKV_EINVAL;
   if (c->max_ctx < 1) return QKV_EINVAL;
   if (c->n_splits < 0 || c->n_splits > 256) return QKV_EINVAL;
+  // a rolling score window is HqeKV's, at most one routing period long
+  if (c->score_window < 0 || (c->score_window > 0 && (c->policy != QKV_POLICY_HQEKV || c->score_window > c->omega)))
+    return QKV_EINVAL;
   if (c->policy == QKV_POLICY_H2O) {
     // per-token heavy hitters: window 1, no quantized tier, scores per KV head
     if (c->window != 1 || c->omega < 1 || c->k_quant != 0 || c->k_full < 0 || c->n_recent < 0) return QKV_EINVAL;
@@ -352,10 +356,14 @@ int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, 
   }
   int rc;
   if (c->tok) {
-    const TokStep ts = {c->N, c->r_tok, c->n_cmp};
+    // with a rolling score window only the last score_window steps before
+    // the next event add to the scores
+    const int m = c->cfg.score_window;
+    const TokStep ts = {c->N, c->r_tok, c->n_cmp, (m > 0 && c->steps_since_route < c->tg.omega - m) ? 1 : 0};
     rc = hip_err(tok_launch_attend(c->tg, c->ts, ts, (const uint16_t *)q, (size_t)c->tg.Hq * c->tg.d, out, mass_out,
                                    (hipStream_t)stream, e0, e1));
     if (c->tg.omega > 1) c->tacc_dirty = true;
+    c->steps_since_route++;
   } else {
     rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
                                e0, e1));
@@ -402,9 +410,16 @@ int qkv_route(qkv_cache *c, qkv_stream stream) {
     for (int k = 0; k < 4; ++k) counts[k] = (int)floor((double)c->cfg.ratios[k] * (double)c->N);
     int rc = hip_err(hq_launch_event(c->tg, c->ts, c->N, elig_end, counts, (hipStream_t)stream));
     if (rc != QKV_OK) return rc;
+    if (c->cfg.score_window > 0) {
+      // rolling window: the next event ranks by the queries of its own window only
+      rc = hip_err(launch_clear(c->ts.score, (size_t)c->tg.B * c->tg.Hkv * c->tg.T * sizeof(float),
+                                (hipStream_t)stream));
+      if (rc != QKV_OK) return rc;
+    }
     c->r_tok = elig_end;
     c->last_event_N = c->N;
     c->routes++;
+    c->steps_since_route = 0;
     return QKV_OK;
   }
   if (c->tok) {
@@ -421,6 +436,7 @@ int qkv_route(qkv_cache *c, qkv_stream stream) {
     c->r_tok = a1;
     c->n_cmp = n_cand < tg.k_heavy ? n_cand : tg.k_heavy;
     c->routes++;
+    c->steps_since_route = 0;
     return QKV_OK;
   }
   const Geom &g = c->g;
@@ -436,6 +452,7 @@ int qkv_route(qkv_cache *c, qkv_stream stream) {
   const int kfq = g.k_full + g.k_quant;
   c->routed = n_cand < kfq ? n_cand : kfq;
   c->routes++;
+  c->steps_since_route = 0;
   return QKV_OK;
 }
 

@@ -221,6 +221,7 @@ struct TokState {
 // ranked (positions [rstart, N) are read from the position pages), kept tokens.
 struct TokStep {
   int N, rstart, n_cmp;
+  int skip;   // 1: this step's masses do not enter the scores (outside a rolling score window)
 };
 
 // key slots per (sequence, KV head) of an assignment event (a multiple of 4)

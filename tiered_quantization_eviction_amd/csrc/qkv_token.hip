@@ -1038,10 +1038,10 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
           if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's weight below FLT_MIN counts as 0
           mass += v;
         }
-        if (list_order) ap[e] += mass;
+        if (list_order && !ts.skip) ap[e] += mass;
         if (need_pos) {
           const int pos = tok_slot_pos<true>(g, st, ts, L, bh, kt[u], s0 + e);
-          if (!list_order) st.score[(size_t)bh * g.T + pos] += mass;
+          if (!list_order && !ts.skip) st.score[(size_t)bh * g.T + pos] += mass;
           if (mass_out) mass_out[(size_t)bh * g.T + pos] = mass;
         }
       }

@@ -81,6 +81,7 @@ class Config:
     # HqeKV: BF16 / INT4 / INT2 / INT1-normal / evict shares
     ratios: tuple = (0.0, 0.0, 0.0, 0.0, 0.0)
     init_queries: int = 0    # HqeKV: prompt queries scored before the first assignment
+    score_window: int = 0    # HqeKV: 0 = scores accumulate every step; m = only the last m steps before an event
     seed: int = 0
     # recipe knobs
     outlier_channels: int = 0
