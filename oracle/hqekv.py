@@ -22,7 +22,13 @@ token); scores accumulate over every scoring query (prompt tail and all decode
 steps), or, with a rolling window of m queries (sections 3.8 and 3.10: the
 metric is kept over the most recent m = 20 queries), over the prompt tail
 for the first assignment and then over the last m decode steps before each
-event only, the scores starting again from 0 after every event; at an event the tokens appended since the previous event keep full
+event only, the scores starting again from 0 after every event; with chunks
+of c tokens (section 3.3's implementation note: the cache is cut into groups
+of G = 32 tokens, a group's importance is the mean of its tokens', and the two
+most important groups always stay FP16) the eligible live tokens of each run
+of c positions form a chunk ranked by the mean of their joint metrics, share
+counts are floor(r_k * ceil(N / c)) chunks, the two best chunks get FP16
+whatever the shares say, and every token takes its chunk's target; at an event the tokens appended since the previous event keep full
 precision and are not ranked; share counts are floor(r_k * N) with N the
 number of tokens ever appended, cut in the order FP16, 4-bit, 2-bit, 1-bit,
 the rest evicted; a downgraded token is re-quantized from its current
@@ -38,7 +44,7 @@ from .attention import attend
 from .codec import (int1_normal_dequantize, int1_normal_quantize, per_token_dequantize,
                     per_token_quantize)
 from .numerics import FLT_MIN, bf16_to_f64
-from .rank import rank_tiers
+from .rank import order, rank_tiers
 
 BF16, INT4, INT2, INT1, EVICT = 0, 1, 2, 3, 4
 
@@ -59,12 +65,14 @@ def assign(metric, pos, eligible, counts):
 class HqeKVGroup:
     """HqeKV state of one (sequence, KV head): per-token tiers and contents."""
 
-    def __init__(self, k_rows, v_rows, *, G: int, ratios, period: int, group: int = 32, window: int = 0):
+    def __init__(self, k_rows, v_rows, *, G: int, ratios, period: int, group: int = 32, window: int = 0,
+                 chunk: int = 0):
         self.korig = bf16_to_f64(k_rows)          # [T, d]
         self.vorig = bf16_to_f64(v_rows)
         self.T, self.d = self.korig.shape
         self.G, self.ratios, self.period, self.group = G, tuple(ratios), period, group
         self.window = window                       # 0: accumulate every step; m: the last m before an event
+        self.chunk = chunk                         # 0: rank tokens; c: rank chunks of c positions
         self.kcur = self.korig.copy()
         self.vcur = self.vorig.copy()
         self.tier = np.full(self.T, 255, np.uint8)   # 255: not appended yet
@@ -119,7 +127,10 @@ class HqeKVGroup:
         else:                                      # tokens appended before the previous event
             eligible[live[live < self.last_event_N]] = True
         metric = joint_metric(self.score, self.range)
-        target = assign(metric, np.arange(self.T), eligible, share_counts(self.ratios, N))
+        if self.chunk:
+            target = self._chunk_targets(metric, eligible, N)
+        else:
+            target = assign(metric, np.arange(self.T), eligible, share_counts(self.ratios, N))
         for t in np.flatnonzero(eligible):
             new = max(int(self.tier[t]), int(target[t]))
             if new > self.tier[t]:
@@ -128,6 +139,25 @@ class HqeKVGroup:
         self.last_metric = metric
         if self.window:
             self.score[:] = 0.0
+
+    def _chunk_targets(self, metric, eligible, N):
+        """Target tier per token from the rank of its chunk's mean metric."""
+        c = self.chunk
+        n_chunks = -(-self.T // c)
+        cid = np.arange(self.T) // c
+        cnt = np.bincount(cid[eligible], minlength=n_chunks)
+        tot = np.bincount(cid[eligible], weights=metric[eligible], minlength=n_chunks)
+        ranked = cnt > 0
+        mean = np.zeros(n_chunks)
+        mean[ranked] = tot[ranked] / cnt[ranked]
+        self.chunk_mean = np.where(ranked, mean, np.nan)
+        tc = assign(mean, np.arange(n_chunks), ranked, share_counts(self.ratios, -(-N // c)))
+        idx = np.flatnonzero(ranked)
+        best = idx[order(mean[idx], idx)][:2]
+        tc[best] = BF16                             # the two most important chunks stay FP16
+        target = np.full(self.T, 255, np.uint8)
+        target[eligible] = tc[cid[eligible]]
+        return target
 
     def _requantize(self, t: int, new: int):
         if new == EVICT:

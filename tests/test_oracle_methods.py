@@ -276,3 +276,61 @@ def test_hqekv_rolling_window_ranks_by_the_last_m_steps():
     np.testing.assert_allclose(rol.last_metric, grown, rtol=1e-9, atol=1e-12 * float(np.max(acc.score)))
     assert np.count_nonzero(rol.last_metric) > 0
     assert not rol.score.any()
+
+
+def _bare_group(T, d=32, **kw):
+    rng = np.random.default_rng(5)
+    kb = (rng.standard_normal((T, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    g = oq.HqeKVGroup(kb, kb, G=4, **kw)
+    g.tier[:T] = oq.BF16
+    g.N = T
+    g.last_event_N = 0
+    return g
+
+
+def test_hqekv_chunk_ranking_hand_example():
+    """HqeKV notes 3.3 (implementation note): chunks ranked by the mean of
+    their tokens' metrics, ties to the newer chunk, shares counted in chunks,
+    the two best chunks FP16 whatever the shares say.  Chunks of 2 over 10
+    tokens, metric = score (range 1): means 2, 5, 2, 0, 7; order c4, c1, c2
+    (newer of the tie), c0, c3; one chunk per share -> c4 FP16, c1 INT4 but
+    pinned FP16, c2 INT2, c0 INT1, c3 evicted."""
+    g = _bare_group(10, ratios=(0.2, 0.2, 0.2, 0.2, 0.2), period=8, chunk=2)
+    g.score[:10] = [1, 3, 10, 0, 2, 2, 0, 0, 8, 6]
+    g.range[:] = 1.0
+    g.event()
+    B, I4, I2, I1, E = oq.BF16, oq.INT4, oq.INT2, oq.INT1, oq.EVICT
+    assert g.tier[:10].tolist() == [I1, I1, B, B, I2, I2, E, E, B, B]
+    np.testing.assert_array_equal(g.chunk_mean, [2, 5, 2, 0, 7])
+
+
+def test_hqekv_chunk_mean_skips_evicted_and_ineligible_tokens():
+    """A chunk's mean is over its live eligible tokens only: an evicted token
+    and the tokens appended since the previous event do not count."""
+    g = _bare_group(12, ratios=(0.5, 0.0, 0.0, 0.0, 0.5), period=8, chunk=4)
+    g.score[:12] = [4, 100, 4, 4, 1, 1, 1, 1, 9, 9, 50, 50]
+    g.range[:] = 1.0
+    g.tier[1] = oq.EVICT
+    g.last_event_N = 10            # tokens 10, 11 are not ranked at this event
+    g.event()
+    np.testing.assert_array_equal(g.chunk_mean, [4.0, 1.0, 9.0])
+    assert g.tier[1] == oq.EVICT and g.tier[10] == oq.BF16 and g.tier[11] == oq.BF16
+
+
+def test_hqekv_chunks_of_one_token_rank_like_tokens():
+    """Chunks of one position are the per-token ranking (the FP16 pin is void
+    when the FP16 share already holds two or more tokens)."""
+    cfg = W.HQEKV.replace(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, prefill=512, steps=96,
+                          omega=32, init_queries=20)
+    wl = W.Workload(cfg)
+    kb, vb = wl.kv(0)
+    tok = oq.HqeKVGroup(kb[0], vb[0], G=4, ratios=cfg.ratios, period=cfg.omega)
+    one = oq.HqeKVGroup(kb[0], vb[0], G=4, ratios=cfg.ratios, period=cfg.omega, chunk=1)
+    pq = wl.prefill_queries(0, cfg.prefill - 20, cfg.prefill)
+    tok.prefill(cfg.prefill, pq)
+    one.prefill(cfg.prefill, pq)
+    qb = wl.queries(0)
+    for s in range(cfg.steps):
+        tok.step(s, cfg.prefill + s, qb[s])
+        one.step(s, cfg.prefill + s, qb[s])
+        np.testing.assert_array_equal(tok.tier, one.tier)
