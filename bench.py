@@ -17,7 +17,9 @@ one GPU.
 
 --workload selects another layer of the same path (the default is the one
 above): `stress` (QEvict, batch 32, 128K prompt, G = 8, 32-token windows),
-`hqekv` (five-tier per-token assignment, batch 8, 64K prompt), `h2o`
+`hqekv` (five-tier per-token assignment, batch 8, 64K prompt), `hqekv_page`
+(the same layer with 32-position chunks, scores from the last 20 queries and
+an event every 32 tokens), `h2o`
 (per-token heavy hitters, batch 1, 512-token scored prompt) or `tiny`.  Their
 lines carry the same fields; the oracle baseline is taken on the default
 workload only.
@@ -52,7 +54,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
-WORKLOADS = {c.name: c for c in (W.DRIFT, W.STRESS, W.HQEKV, W.H2O, W.TINY)}
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O, W.TINY)}
 CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",
@@ -71,8 +73,11 @@ def describe(cfg, steps):
     if cfg.policy == W.POLICY_H2O:
         return (f"H2O heavy hitters: " + head + f", scored prompt, {cfg.n_sink} sinks + {cfg.k_full} heavy + "
                 f"{cfg.n_recent} recent tokens per KV head, eviction every step")
+    rank = (f"chunks of {cfg.chunk} ranked by mean metric (two best BF16)" if cfg.chunk else "per-token ranking")
+    scores = (f"scores from the last {cfg.score_window} queries" if cfg.score_window else "accumulated scores")
     return (f"HqeKV five-tier: " + head + f", shares {'/'.join(str(r) for r in cfg.ratios)} "
-            f"BF16/INT4/INT2/INT1/evicted by attention x value range, events every {cfg.omega} steps")
+            f"BF16/INT4/INT2/INT1/evicted by attention x value range, events every {cfg.omega} steps, "
+            f"{rank}, {scores}")
 
 
 def log(msg):
@@ -351,7 +356,7 @@ def cpu_baseline_tok(cfg, K, V, Q, QP, budget_s):
             from oracle import hqekv as oq
             ratios32 = tuple(float(np.float32(r)) for r in cfg.ratios)
             grp = oq.HqeKVGroup(K[0, g], V[0, g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
-                                window=cfg.score_window)
+                                window=cfg.score_window, chunk=cfg.chunk)
         grp.prefill(P, QP[0][:, g * G:(g + 1) * G])
         groups.append(grp)
     done = 0

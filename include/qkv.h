@@ -86,6 +86,11 @@ typedef struct qkv_config {
                          * queries (HqeKV notes 3.8, 3.10): only the last m
                          * decode steps before each event add, and the scores
                          * restart from 0 after every event.  0 otherwise.   */
+  int32_t chunk;      /* HqeKV: 0 = tokens are ranked one by one; c in [1, 64]
+                       * = positions are ranked in chunks of c by the mean of
+                       * their tokens' metrics, shares counted in chunks, the
+                       * two best chunks kept BF16 (HqeKV notes 3.3);
+                       * ceil(max_ctx / c) <= 4096.  0 otherwise.            */
 } qkv_config;
 
 /* Bytes of device workspace a cache with this configuration needs, or 0 if

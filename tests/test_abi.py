@@ -81,6 +81,20 @@ def test_score_window_checks_on_host():
         assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL, cfg.name
 
 
+def test_chunk_checks_on_host():
+    """Chunk ranking belongs to HqeKV: chunks of 1 to 64 positions, at most
+    4096 of them per (sequence, KV head)."""
+    L, lib = _lib()
+    for chunk, max_ctx, ok in ((0, 65792, True), (32, 65792, True), (64, 65792, True), (65, 65792, False),
+                               (16, 65792, False), (16, 65536, True), (-1, 65792, False)):
+        c = L.make_config(W.HQEKV, max_ctx=max_ctx)
+        c.chunk = chunk
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, (chunk, max_ctx)
+    c = L.make_config(W.TINY)
+    c.chunk = 32
+    assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL
+
+
 def test_strerror_and_info_arguments():
     L, lib = _lib()
     assert lib.qkv_strerror(L.ERANGE).decode().startswith("quantization parameter")

@@ -7,7 +7,9 @@ oracle follows step by step.
   promotions that follow it).
 * QEvict stress layer: batch 32, 131072-token prompt, Hq = 64 (G = 8),
   32-token windows; two routing events.
-* HqeKV layer: batch 8, 65536-token prompt, two assignment events.
+* HqeKV layer: batch 8, 65536-token prompt, two assignment events; and its
+  page variant (32-position chunks, scores from the last 20 queries, an
+  event every 32 tokens: four events).
 
 Bars as in the small parity tests: outputs 2e-3, scores 1e-4 relative,
 tiers exact (codes and parameters are compared bit for bit in the small
@@ -90,14 +92,17 @@ def test_stress_fullsize_sampled(torch_cuda):
     _qevict_sampled(W.STRESS.replace(steps=65), torch_cuda, [5], "stress-full", all_real=False)
 
 
-def test_hqekv_fullsize_sampled(torch_cuda):
-    """Config of the HqeKV layer at full size, two KV heads followed by the oracle."""
+@pytest.mark.parametrize("name", ["hqekv", "hqekv_page"])
+def test_hqekv_fullsize_sampled(torch_cuda, name):
+    """The HqeKV layer at full size (per-token ranking with accumulated
+    scores, and the page variant: 32-position chunks, scores from the last 20
+    queries, an event every 32 tokens), two KV heads followed by the oracle."""
     from tiered_quantization_eviction_amd import Cache, make_config
     torch = torch_cuda
-    cfg = W.HQEKV.replace(steps=128)
+    cfg = W.CONFIGS[name].replace(steps=128)
     B, Hkv, G, d, P, T = cfg.batch, cfg.n_kv_heads, cfg.group_size, cfg.head_dim, cfg.prefill, cfg.total_tokens
     m = cfg.init_queries
-    label = "hqekv-full"
+    label = f"{name}-full"
     sampled = [(0, 0), (5, 3)]
     log(f"[{label}] generating {B} x {T} tokens")
     K, V, Q = gpu_inputs_sampled(cfg, sorted({b for b, _ in sampled}))
@@ -116,7 +121,7 @@ def test_hqekv_fullsize_sampled(torch_cuda):
     for b, g in sampled:
         k, v = wl.kv(b)
         grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
-                            window=cfg.score_window)
+                            window=cfg.score_window, chunk=cfg.chunk)
         grp.prefill(P, qt[b][:, g * G:(g + 1) * G])
         groups[b, g] = grp
         log(f"[{label}] oracle (seq {b}, head {g}) prompt assigned")

@@ -92,7 +92,7 @@ def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
         k, v = wl.kv(b)
         for g in range(Hkv):
             grp = oq.HqeKVGroup(k[g], v[g], G=G, ratios=ratios32, period=cfg.omega, group=cfg.group,
-                                window=cfg.score_window)
+                                window=cfg.score_window, chunk=cfg.chunk)
             grp.prefill(P, qt[b][:, g * G:(g + 1) * G])
             groups[b, g] = grp
 
@@ -111,10 +111,20 @@ def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
             exp = grp.tier.copy()
             bad = np.flatnonzero(tiers[b, g] != exp)
             if len(bad):
-                metric = oq.joint_metric(grp.score, grp.range)
-                live = exp != 255
-                cuts = np.sort(metric[live])[::-1]
-                close = [np.min(np.abs(cuts - metric[t]) / max(metric[t], 1e-300)) for t in bad]
+                if cfg.chunk:
+                    # chunk ranking: the chunk's mean must be a near tie with another chunk's
+                    cm = grp.chunk_mean
+                    close = []
+                    for t in bad:
+                        c = t // cfg.chunk
+                        others = np.delete(cm, c)
+                        others = others[~np.isnan(others)]
+                        close.append(np.min(np.abs(others - cm[c])) / max(cm[c], 1e-300))
+                else:
+                    metric = oq.joint_metric(grp.score, grp.range)
+                    live = exp != 255
+                    cuts = np.sort(metric[live])[::-1]
+                    close = [np.min(np.abs(cuts - metric[t]) / max(metric[t], 1e-300)) for t in bad]
                 assert max(close) < 1e-5, (f"{tag}: tiers of (seq {b}, head {g}) differ at {bad[:8]} "
                                            f"(gpu {tiers[b, g][bad[:8]]}, oracle {exp[bad[:8]]})")
                 ambiguous += len(bad)
@@ -187,6 +197,17 @@ def test_hqekv_rolling_window_parity(torch_cuda):
     against the oracle over four events."""
     cfg = W.HQEKV.replace(batch=2, n_q_heads=16, n_kv_heads=4, prefill=1024, steps=128, omega=32, score_window=20)
     _run_hqekv(cfg, torch_cuda, label="hqekv-rolling")
+
+
+@pytest.mark.parametrize("chunk,window", [(32, 20), (16, 0)])
+def test_hqekv_chunk_ranking_parity(torch_cuda, chunk, window):
+    """HqeKV's page variant (notes 3.3 implementation note, 3.5, 3.8): chunks
+    of 32 positions ranked by their mean metric with the two best kept BF16,
+    a rolling window of the last 20 queries, an event every 32 tokens; and
+    16-position chunks with accumulated scores."""
+    cfg = W.HQEKV.replace(batch=2, n_q_heads=16, n_kv_heads=4, prefill=1024, steps=128, omega=32,
+                          score_window=window, chunk=chunk)
+    _run_hqekv(cfg, torch_cuda, label=f"hqekv-chunk{chunk}-w{window}")
 
 
 @pytest.mark.parametrize("prefill", [1024, 4096])

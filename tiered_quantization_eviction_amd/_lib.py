@@ -35,7 +35,7 @@ class QkvConfig(ctypes.Structure):
         ("omega", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
         ("k_full", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("ratios", ctypes.c_float * 5),
         ("quant_bits", ctypes.c_int32), ("group", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
-        ("n_splits", ctypes.c_int32), ("score_window", ctypes.c_int32),
+        ("n_splits", ctypes.c_int32), ("score_window", ctypes.c_int32), ("chunk", ctypes.c_int32),
     ]
 
 

@@ -55,6 +55,10 @@ int validate(const qkv_config *c) {
   // a rolling score window is HqeKV's, at most one routing period long
   if (c->score_window < 0 || (c->score_window > 0 && (c->policy != QKV_POLICY_HQEKV || c->score_window > c->omega)))
     return QKV_EINVAL;
+  // chunk ranking is HqeKV's, chunks of at most 64 positions, at most HQ_CHUNK_MAX of them
+  if (c->chunk < 0 || c->chunk > 64) return QKV_EINVAL;
+  if (c->chunk > 0 && (c->policy != QKV_POLICY_HQEKV || ((long long)c->max_ctx + c->chunk - 1) / c->chunk > HQ_CHUNK_MAX))
+    return QKV_EINVAL;
   if (c->policy == QKV_POLICY_H2O) {
     // per-token heavy hitters: window 1, no quantized tier, scores per KV head
     if (c->window != 1 || c->omega < 1 || c->k_quant != 0 || c->k_full < 0 || c->n_recent < 0) return QKV_EINVAL;
@@ -155,6 +159,7 @@ void make_tok_geom(const qkv_config *c, TokGeom &g) {
   g.n_recent = c->n_recent;
   g.k_heavy = c->k_full;
   g.omega = c->omega;
+  g.chunk = c->policy == QKV_POLICY_HQEKV ? c->chunk : 0;
   int S = c->n_splits;
   if (S == 0) {   // one resident round of workgroups, at least two tiles per wave
     const int pairs = g.B * g.Hkv;
@@ -406,8 +411,11 @@ int qkv_route(qkv_cache *c, qkv_stream stream) {
     // event) get target tiers by their rank; shares floor(r_k * N) of all
     // tokens ever appended, in the order BF16, INT4, INT2, INT1
     const int elig_end = c->last_event_N == 0 ? c->N : c->last_event_N;
+    // shares of all tokens ever appended, or of all chunks of them
+    const int chunk = c->tg.chunk;
+    const double units = chunk > 0 ? (double)((c->N + chunk - 1) / chunk) : (double)c->N;
     int counts[4];
-    for (int k = 0; k < 4; ++k) counts[k] = (int)floor((double)c->cfg.ratios[k] * (double)c->N);
+    for (int k = 0; k < 4; ++k) counts[k] = (int)floor((double)c->cfg.ratios[k] * units);
     int rc = hip_err(hq_launch_event(c->tg, c->ts, c->N, elig_end, counts, (hipStream_t)stream));
     if (rc != QKV_OK) return rc;
     if (c->cfg.score_window > 0) {

@@ -191,7 +191,10 @@ struct TokGeom {
   // V params [d/32][2] fp16 (INT1: [mean, std] in the first pair)
   int rec_bytes;
   int qtile_bytes[3];   // compact tile bytes of INT4, INT2, INT1
+  int chunk;            // HqeKV: positions per ranked chunk (0: tokens are ranked one by one)
 };
+
+constexpr int HQ_CHUNK_MAX = 4096;   // ranked chunks per (sequence, KV head), sorted in LDS
 
 struct TokState {
   uint16_t *pages;

@@ -1428,6 +1428,66 @@ __device__ void hq_choose_digit(CountF count, int sh, uint32_t *pref, int *rem, 
   __syncthreads();
 }
 
+// Chunk targets of an assignment event (HqeKV notes 3.3, implementation
+// note): chunk c holds positions [c*C, (c+1)*C) below elig_end and its metric
+// is the mean of its ranked tokens' keys (the fp32 joint metric), summed in
+// fp64 in position order; chunks are ordered by (mean desc, index desc), rank
+// r takes the tier of the cumulative chunk counts c0..c3 (the rest evicted),
+// and ranks 0 and 1 are BF16 whatever the counts.  ctgt[c] is left unset for
+// a chunk without a ranked token (no token reads it).
+__device__ void hq_rank_chunks(const TokGeom &g, const uint32_t *keys, int elig_end, int c0, int c1, int c2, int c3,
+                               uint8_t *ctgt) {
+  __shared__ double km[HQ_CHUNK_MAX];
+  __shared__ int ki[HQ_CHUNK_MAX];
+  const int C = g.chunk, tid = threadIdx.x, nthr = blockDim.x;
+  const int nC = (elig_end + C - 1) / C;   // at most HQ_CHUNK_MAX (checked at create)
+  int npow = 1;
+  while (npow < nC) npow <<= 1;
+  for (int c = tid; c < npow; c += nthr) {
+    double sum = 0.0;
+    int n = 0;
+    if (c < nC) {
+      const int p1 = min((c + 1) * C, elig_end);
+#pragma unroll 8
+      for (int p = c * C; p < p1; ++p) {
+        const uint32_t k = keys[p];
+        if (k != HQ_KEY_NONE) {
+          sum += (double)__uint_as_float(k);
+          ++n;
+        }
+      }
+    }
+    km[c] = n > 0 ? sum / n : -1.0;   // chunks without a ranked token sort last
+    ki[c] = c;
+  }
+  __syncthreads();
+  for (int k = 2; k <= npow; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < npow; i += nthr) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const double a = km[i], b = km[ixj];
+          const int ia = ki[i], ib = ki[ixj];
+          const bool a_first = a > b || (a == b && ia > ib);
+          if (a_first != ((i & k) == 0)) {
+            km[i] = b;
+            km[ixj] = a;
+            ki[i] = ib;
+            ki[ixj] = ia;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const int cum0 = c0, cum1 = c0 + c1, cum2 = cum1 + c2, cum3 = cum2 + c3;
+  for (int r = tid; r < nC; r += nthr) {
+    if (km[r] < 0.0) continue;
+    const int t = (r < 2 || r < cum0) ? HQ_BF16 : r < cum1 ? 1 : r < cum2 ? 2 : r < cum3 ? 3 : HQ_EVICT;
+    ctgt[ki[r]] = (uint8_t)t;
+  }
+  __syncthreads();
+}
+
 // Assignment event of one (sequence, KV head) (HqeKV section 3.3 with the
 // shares of its tier table): the joint metric (accumulated attention x value
 // range) ranks every token appended before the previous event; the cuts at
@@ -1512,6 +1572,10 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
     for (int i = tid; i < 4 * 2048; i += nthr) (&hist[0][0])[i] = 0u;
     __syncthreads();
   };
+  __shared__ uint8_t ctgt[HQ_CHUNK_MAX];
+  if (g.chunk > 0) {
+    hq_rank_chunks(g, keys, elig_end, c0, c1, c2, c3, ctgt);
+  } else {
   // ---- digit [31..21]: one histogram for all cuts (four copies against contention) ----
   clear_hist();
   for_keys([&](uint32_t k, int) {
@@ -1588,6 +1652,7 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
     }
     if (tid < 4 && big[tid]) pcut[tid] = (int)ppref[tid];
   }
+  }   // per-token ranking
   __syncthreads();
   if (tid < 4) {
     // keys >= thr[j] have rank < cum[j]: all of them when cum[j] >= E, none when cum[j] <= 0
@@ -1615,9 +1680,13 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
       if (k4[e] != HQ_KEY_NONE) {
         const unsigned long long key = ((unsigned long long)k4[e] << 32) | (unsigned)(pos + 1);
         int target = 0;
+        if (g.chunk > 0) {
+          target = ctgt[pos / g.chunk];
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
+          for (int j = 0; j < 4; ++j)
+            if (!(cum[j] >= E ? true : (cum[j] > 0 && key >= thr[j]))) ++target;
+        }
         if (target > old) {
           st.tier[tb + pos] = hq_code(target);
           if (target != HQ_EVICT) st.hqold[tb + pos] = (uint8_t)(old + 1);

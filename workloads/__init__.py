@@ -82,6 +82,7 @@ class Config:
     ratios: tuple = (0.0, 0.0, 0.0, 0.0, 0.0)
     init_queries: int = 0    # HqeKV: prompt queries scored before the first assignment
     score_window: int = 0    # HqeKV: 0 = scores accumulate every step; m = only the last m steps before an event
+    chunk: int = 0           # HqeKV: 0 = per-token ranking; c = chunks of c positions ranked by their mean metric
     seed: int = 0
     # recipe knobs
     outlier_channels: int = 0
@@ -152,6 +153,11 @@ HQEKV = _reg(Config(
     batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, prefill=65536, steps=256,
     window=1, omega=64, ratios=(0.20, 0.30, 0.30, 0.10, 0.10), init_queries=20,
     outlier_channels=4, outlier_scale=8.0, seed=0))
+
+# 4b: HqeKV's page variant: chunks of 32 positions ranked by their mean
+#     metric (the two best kept BF16), a rolling window of the last 20
+#     queries, an event every 32 tokens.
+HQEKV_PAGE = _reg(HQEKV.replace(name="hqekv_page", omega=32, score_window=20, chunk=32))
 
 # 5: long-context stress, G = 8, 32-token windows.
 _W0_STRESS = _w0(131072, 5, 32, 32)
