@@ -19,10 +19,9 @@ one GPU.
 above): `stress` (QEvict, batch 32, 128K prompt, G = 8, 32-token windows),
 `hqekv` (five-tier per-token assignment, batch 8, 64K prompt), `hqekv_page`
 (the same layer with 32-position chunks, scores from the last 20 queries and
-an event every 32 tokens), `h2o`
-(per-token heavy hitters, batch 1, 512-token scored prompt) or `tiny`.  Their
-lines carry the same fields; the oracle baseline is taken on the default
-workload only.
+an event every 32 tokens), `h2o` (per-token heavy hitters, batch 1,
+512-token scored prompt) or `tiny`.  Their lines carry the same fields; their
+oracle baseline runs sequence 0 for up to 15 s of decode steps.
 """
 from __future__ import annotations
 
