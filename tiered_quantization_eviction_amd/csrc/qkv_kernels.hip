@@ -1005,7 +1005,40 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
 // routing event: rank candidates per sequence in LDS (bitonic), assign tiers
 // ---------------------------------------------------------------------------
 
+// One key per thread (64 <= n <= blockDim.x, n a power of two): the
+// compare-exchange partner of a stage with distance j < 64 is in the same
+// wave and is read with a lane permute, so only the stages with j >= 64 go
+// through LDS and a workgroup barrier (10 of the 55 stages at n = 1024).
+__device__ inline void bitonic_desc_u64_regs(unsigned long long *keys, int n) {
+  const int i = threadIdx.x;
+  const bool mine = i < n;   // whole waves (n is a multiple of 64)
+  unsigned long long key = mine ? keys[i] : 0ull;
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      unsigned long long other;
+      if (j >= 64) {
+        __syncthreads();
+        if (mine) keys[i] = key;
+        __syncthreads();
+        other = mine ? keys[i ^ j] : 0ull;
+      } else {
+        const uint32_t lo = __shfl_xor((uint32_t)key, j), hi = __shfl_xor((uint32_t)(key >> 32), j);
+        other = ((unsigned long long)hi << 32) | lo;
+      }
+      // the lower index of a pair keeps the larger key in a descending run
+      const bool keep_max = ((i & j) == 0) == ((i & k) == 0);
+      key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
+    }
+  __syncthreads();
+  if (mine) keys[i] = key;
+  __syncthreads();
+}
+
 __device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
+  if (n >= 64 && n <= (int)blockDim.x) {
+    bitonic_desc_u64_regs(keys, n);
+    return;
+  }
   for (int k = 2; k <= n; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < n; i += blockDim.x) {
