@@ -97,6 +97,22 @@ typedef struct qkv_config {
  * the configuration is invalid (see qkv_check_config for the reason). */
 size_t qkv_workspace_bytes(const qkv_config *cfg);
 
+/* QEvict capacities from a byte budget (QEvict notes §4.3, Eq.(budget) and
+ * Eq.(3); §4.5 works the arithmetic for Llama-3.1-8B).  The budget
+ * `budget_bytes` covers `layers` layers of this configuration's KV geometry
+ * (per sequence); sinks and the recent region are held in BF16 and paid
+ * first; of the rest, a share q in [0, 1] buys quantized windows and 1 - q
+ * full-precision windows:
+ *   M_f = window * layers * 2 * n_kv_heads * head_dim * 2 bytes,
+ *   M_q = layers * n_kv_heads * (2 * window * head_dim * bits / 8
+ *         + head_dim * ceil(window / group) * 4 + window * (head_dim / group) * 4),
+ *   K_f = floor((1 - q) * B_hist / M_f),  K_q = floor(q * B_hist / M_q).
+ * Writes K_f and K_q (host pointers); QKV_EINVAL for a non-QEvict or invalid
+ * configuration, layers < 1, q outside [0, 1], a negative budget, or a budget
+ * that does not cover the sinks and the recent region. */
+int qkv_plan_capacities(const qkv_config *cfg, double budget_bytes, double q, int32_t layers, int32_t *k_full,
+                        int32_t *k_quant);
+
 /* QKV_OK if the configuration is supported, else QKV_EINVAL.  Besides the
  * ranges above: QEvict with head_dim 128 and eight query heads per KV head
  * needs 32-token windows (the attention workgroup's LDS would not fit). */

@@ -95,6 +95,42 @@ def test_chunk_checks_on_host():
     assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL
 
 
+def test_plan_capacities_matches_the_oracle_budget_arithmetic():
+    """QEvict notes 4.3 Eq.(3) through the library's planner against the
+    oracle's capacity and payload arithmetic (itself pinned to the pages'
+    100 MB example): Llama-3.1-8B geometry (32 layers, 8 KV heads, d = 128),
+    several windows, budgets and splits q."""
+    import math
+    from oracle import budget
+    L, lib = _lib()
+    for window in (8, 16, 32):
+        for q in (0.0, 0.3, 0.7, 1.0):
+            for mb in (40.0, 100.0, 1000.0):
+                c = L.make_config(W.DRIFT, window=window)
+                layers = 32
+                per_tok = budget.kv_bytes_per_token(layers, c.n_kv_heads, c.head_dim, 2)
+                b_hist = mb * 2 ** 20 - (c.n_sink + c.n_recent) * per_tok
+                m_full = window * per_tok
+                m_quant = layers * c.n_kv_heads * budget.window_ledger_bytes(window, c.head_dim, 2, 32)
+                want = budget.tier_capacities(b_hist, q, m_full, m_quant)
+                got = L.plan_capacities(c, mb * 2 ** 20, q, layers)
+                assert got == want, (window, q, mb, got, want)
+    c = L.make_config(W.DRIFT)
+    for bad in ((-1.0, 0.5, 1), (2 ** 30, 1.5, 1), (2 ** 30, 0.5, 0), (1000.0, 0.5, 1)):
+        with pytest.raises(ValueError):
+            L.plan_capacities(c, *bad)
+    with pytest.raises(ValueError):
+        L.plan_capacities(L.make_config(W.HQEKV), 2 ** 30, 0.5, 1)
+    # the single-layer drift capacities at the bytes they occupy
+    kf, kq = W.DRIFT.k_full, W.DRIFT.k_quant
+    per_tok = budget.kv_bytes_per_token(1, 8, 128, 2)
+    b = (5 + 64) * per_tok + kf * 16 * per_tok + kq * 8 * budget.window_ledger_bytes(16, 128, 2, 32)
+    q = kq * 8 * budget.window_ledger_bytes(16, 128, 2, 32) / (b - (5 + 64) * per_tok)
+    got = L.plan_capacities(c, b, q, 1)
+    assert abs(got[0] - kf) <= 1 and abs(got[1] - kq) <= 1, got
+    assert math.isfinite(q)
+
+
 def test_strerror_and_info_arguments():
     L, lib = _lib()
     assert lib.qkv_strerror(L.ERANGE).decode().startswith("quantization parameter")

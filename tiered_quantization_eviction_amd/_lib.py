@@ -54,6 +54,8 @@ def _lib() -> ctypes.CDLL:
         L.qkv_workspace_bytes.restype = _sz
         L.qkv_workspace_bytes.argtypes = [ctypes.POINTER(QkvConfig)]
         L.qkv_check_config.argtypes = [ctypes.POINTER(QkvConfig)]
+        L.qkv_plan_capacities.argtypes = [ctypes.POINTER(QkvConfig), ctypes.c_double, ctypes.c_double, _i32,
+                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.qkv_create.argtypes = [ctypes.POINTER(QkvConfig), _vp, _sz, _vp, ctypes.POINTER(_vp)]
         L.qkv_destroy.argtypes = [_vp]
         L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
@@ -127,6 +129,18 @@ def make_config(cfg=None, *, n_splits: int = 0, max_ctx: int | None = None, **kw
         else:
             setattr(c, f, int(src.get(f, 32 if f == "group" else (2 if f == "quant_bits" else 0))))
     return c
+
+
+def plan_capacities(c: QkvConfig, budget_bytes: float, q: float, layers: int = 1) -> tuple[int, int]:
+    """(K_f, K_q) that a byte budget buys over `layers` layers of this
+    configuration (QEvict Eq.(3)); raises ValueError where the C call
+    reports QKV_EINVAL."""
+    kf, kq = ctypes.c_int32(), ctypes.c_int32()
+    rc = _lib().qkv_plan_capacities(ctypes.byref(c), float(budget_bytes), float(q), int(layers),
+                                    ctypes.byref(kf), ctypes.byref(kq))
+    if rc != 0:
+        raise ValueError(_lib().qkv_strerror(rc).decode())
+    return kf.value, kq.value
 
 
 def workspace_bytes(c: QkvConfig) -> int:

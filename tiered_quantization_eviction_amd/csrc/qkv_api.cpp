@@ -231,6 +231,26 @@ const char *qkv_strerror(int code) {
 
 int qkv_check_config(const qkv_config *cfg) { return validate(cfg); }
 
+int qkv_plan_capacities(const qkv_config *cfg, double budget_bytes, double q, int32_t layers, int32_t *k_full,
+                        int32_t *k_quant) {
+  if (!cfg || !k_full || !k_quant || validate(cfg) != QKV_OK || cfg->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;
+  if (layers < 1 || !(q >= 0.0 && q <= 1.0) || !(budget_bytes >= 0.0)) return QKV_EINVAL;
+  const double per_token = (double)layers * 2.0 * cfg->n_kv_heads * cfg->head_dim * 2.0;   // K and V, BF16
+  const double fixed = (double)(cfg->n_sink + cfg->n_recent) * per_token;
+  const double b_hist = budget_bytes - fixed;
+  if (b_hist < 0.0) return QKV_EINVAL;
+  const int w = cfg->window, d = cfg->head_dim, grp = cfg->group;
+  const double m_f = (double)w * per_token;
+  const double ledger = 2.0 * w * d * cfg->quant_bits / 8.0 + (double)d * ((w + grp - 1) / grp) * 4.0 +
+                        (double)w * (d / grp) * 4.0;
+  const double m_q = (double)layers * cfg->n_kv_heads * ledger;
+  const double kf = floor((1.0 - q) * b_hist / m_f), kq = floor(q * b_hist / m_q);
+  if (kf > 2147483647.0 || kq > 2147483647.0) return QKV_EINVAL;
+  *k_full = (int32_t)kf;
+  *k_quant = (int32_t)kq;
+  return QKV_OK;
+}
+
 size_t qkv_workspace_bytes(const qkv_config *cfg) {
   if (validate(cfg) != QKV_OK) return 0;
   if (cfg->policy == QKV_POLICY_H2O || cfg->policy == QKV_POLICY_HQEKV) {
