@@ -1067,23 +1067,26 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     n_pack = 0;
     n_prom = 0;
   }
-  // the list-order scores of the entries so far (sink, ranked, recent
-  // windows a0 .. r1) back to their units
-  {
-    const EntryList L = {si.has_sink, nF, nQ, si.r1 >= a0 ? si.r1 - a0 + 1 : 0, a0};
-    for (int e = threadIdx.x; e < L.count(); e += blockDim.x)
-      st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] = st.slist[b * g.U + e];
-  }
-  __syncthreads();
+  // Candidate i sits at entry s0 + i of the list so far (the ranked windows,
+  // then the windows aged since the last event, which lead the recent ones):
+  // its list-order score is its key and goes back to its unit's score.  The
+  // sink and the windows that stay recent (a1 .. r1) go back too.
+  const int s0 = si.has_sink;
+  const float *sl = st.slist + (size_t)b * g.U;
+  const int n_keep = si.r1 >= a1 ? si.r1 - a1 + 1 : 0;
   for (int i = threadIdx.x; i < npow; i += blockDim.x) {
     unsigned long long key = 0ull;
     if (i < n) {
       const int u = i < RC ? st.routed[b * g.U + i] : a0 + (i - RC);
-      const uint32_t sb = __float_as_uint(st.score[b * g.U + u]);    // scores are >= 0: bits are monotone
-      key = ((unsigned long long)sb << 32) | (unsigned long long)(uint32_t)(unit_start(g, u) + 1);
+      const float sc = sl[s0 + i];
+      st.score[b * g.U + u] = sc;
+      key = ((unsigned long long)__float_as_uint(sc) << 32) |   // scores are >= 0: bits are monotone
+            (unsigned long long)(uint32_t)(unit_start(g, u) + 1);
     }
     keys[i] = key;
   }
+  for (int k = threadIdx.x; k < n_keep; k += blockDim.x) st.score[b * g.U + a1 + k] = sl[s0 + n + k];
+  if (s0 && threadIdx.x == 0) st.score[b * g.U] = sl[0];
   __syncthreads();
   bitonic_desc_u64(keys, npow);
   const int KFQ = g.k_full + g.k_quant;
@@ -1114,13 +1117,21 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     st.pack_count[b] = n_pack;
     st.promote_count[b] = n_prom;
   }
-  // list-order scores of the new list; the slots past it belong to windows
-  // not yet appended (score 0)
+  // list-order scores of the new list: the sink's is unchanged, the ranked
+  // windows' are in their sorted keys, the recent windows' were written back
+  // above; the slots past the list belong to windows not yet appended (0)
   {
-    const EntryList L = {si.has_sink, nF2, nQ2, si.r1 >= a1 ? si.r1 - a1 + 1 : 0, a1};
-    const int E = L.count();
-    for (int e = threadIdx.x; e < g.U; e += blockDim.x)
-      st.slist[b * g.U + e] = e < E ? st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] : 0.0f;
+    const int nFQ2 = nF2 + nQ2, E = s0 + nFQ2 + n_keep;
+    for (int e = threadIdx.x; e < g.U; e += blockDim.x) {
+      float v = 0.0f;
+      if (e < s0)
+        v = st.score[b * g.U];
+      else if (e - s0 < nFQ2)
+        v = __uint_as_float((uint32_t)(keys[e - s0] >> 32));
+      else if (e < E)
+        v = st.score[b * g.U + a1 + (e - s0 - nFQ2)];
+      st.slist[b * g.U + e] = v;
+    }
   }
 }
 
