@@ -98,9 +98,10 @@ def test_quantize_int1_normal_codes_bitexact(torch_cuda):
     for blk in range(2):
         c, m, sd = oc.int1_normal_quantize(x[blk])
         np.testing.assert_array_equal(codes[blk], oc.pack_codes(c.reshape(-1), 1))
-        np.testing.assert_array_equal(params[blk].reshape(-1, 2)[:, 0], m)
-        np.testing.assert_allclose(params[blk].reshape(-1, 2)[:, 1].astype(np.float32), sd.astype(np.float32),
-                                   rtol=1e-3)
+        # mean and deviation are both summed in float64 and rounded once to
+        # float32, then to float16, on both sides: compared bit for bit
+        np.testing.assert_array_equal(params[blk].reshape(-1, 2)[:, 0].view(np.uint16), m.view(np.uint16))
+        np.testing.assert_array_equal(params[blk].reshape(-1, 2)[:, 1].view(np.uint16), sd.view(np.uint16))
 
 
 def test_quantize_range_error_latched(torch_cuda):

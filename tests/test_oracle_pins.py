@@ -246,3 +246,125 @@ def test_attention_matches_bruteforce_and_rows_sum_to_one():
 def test_round_to_bf16_nearest_even():
     x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7 + 2 ** -9, -3.0], np.float32)
     np.testing.assert_array_equal(round_to_bf16(x), [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -3.0])
+
+
+# ---------------------------------------------------------------------------
+# HqeKV notes, section 2.3 Eq.(2) with the KIVI grouping of the KV-cache
+# evolution page, section 5: per-token quantization in groups of 32
+# consecutive channels
+# ---------------------------------------------------------------------------
+
+def _grid_token(bits):
+    """A 128-channel token whose four 32-channel groups lie on four different
+    grids z_j + k * s_j (s_j, z_j exact in float16), each group reaching its
+    lowest and highest level, so the expected codes and parameters are known
+    without running the quantizer."""
+    L = 2 ** bits - 1
+    z = np.array([-3.0, 0.5, 10.0, -40.0], np.float32)
+    s = np.array([0.25, 1.0, 0.125, 4.0], np.float32)
+    rng = np.random.default_rng(7 + bits)
+    k = rng.integers(0, L + 1, (4, 32))
+    k[:, 3], k[:, 17] = 0, L                       # every group spans its full range
+    x = (z[:, None] + k * s[:, None]).astype(np.float32).reshape(128)
+    return x, k.reshape(128), s, z
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_per_token_quantize_groups_of_32_channels(bits):
+    x, k, s, z = _grid_token(bits)
+    c, sc, zc = codec.per_token_quantize(x[None], bits)
+    np.testing.assert_array_equal(c[0], k)
+    # group j's parameters come from channels [32j, 32j + 32) and nothing else
+    np.testing.assert_array_equal(sc[0].astype(np.float32), s)
+    np.testing.assert_array_equal(zc[0].astype(np.float32), z)
+    np.testing.assert_array_equal(codec.per_token_dequantize(c, sc, zc)[0], x)
+    # the pin tells the grouping apart from a strided one (channel c in group c mod 4)
+    strided = x.reshape(32, 4).T
+    assert not np.array_equal(codec.uniform_quantize(strided, bits)[1].astype(np.float32), s)
+
+
+def test_per_token_quantize_rows_are_independent():
+    """A batch of tokens: each row's parameters depend on that row only."""
+    x2, k2, s2, z2 = _grid_token(2)
+    x4, k4, s4, z4 = _grid_token(4)
+    rows = np.stack([x2, x2 * np.float32(2.0)])
+    c, sc, zc = codec.per_token_quantize(rows, 2)
+    np.testing.assert_array_equal(c[0], k2)
+    np.testing.assert_array_equal(c[1], k2)
+    np.testing.assert_array_equal(sc[1].astype(np.float32), 2 * s2)
+    np.testing.assert_array_equal(zc[1].astype(np.float32), 2 * z2)
+
+
+# ---------------------------------------------------------------------------
+# HqeKV notes, sections 3.4-3.5: a token moving down re-quantizes its
+# current (dequantized) values -- the original is gone once it is quantized
+# ---------------------------------------------------------------------------
+
+def _bf16(a):
+    return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_hqekv_requantize_from_current_values():
+    """One 32-channel row [0, 3.0, 2.5, 0, ...] moved to INT4 and then INT2.
+
+    INT4: step fp32(3/15) -> float16 0.199951171875 (= 819/4096), zero 0;
+    codes 3/0.19995 = 15.004 -> 15 and 2.5/0.19995 = 12.503 -> 13; values
+    15*819/4096 = 2.999267578125 and 13*819/4096 = 2.599365234375.
+    INT2 from those: step 2.999267578125/3 = 1 - 2^-12, halfway between the
+    float16 neighbours 1 - 2^-11 and 1, rounds to even: 1.0; codes
+    rint(2.99927) = 3, rint(2.59937) = 3.
+    INT2 of the original row would give rint(2.5/1.0) = 2 (ties to even) at
+    channel 2 -- the value this pin rules out."""
+    row = np.zeros(32, np.float32)
+    row[1], row[2] = 3.0, 2.5
+    kb = _bf16(np.stack([row, row]))
+    grp = hqekv.HqeKVGroup(kb, kb, G=1, ratios=(1, 0, 0, 0, 0), period=1, group=32)
+    grp.tier[:] = hqekv.BF16
+    grp._requantize(0, hqekv.INT4)
+    tier, kc, ks, kz, vc, vs, vz = grp.codes[0]
+    assert tier == hqekv.INT4
+    assert kc[:3].tolist() == [0, 15, 13] and float(ks[0]) == 819 / 4096 and float(kz[0]) == 0.0
+    assert grp.kcur[0, 1] == 12285 / 4096 and grp.kcur[0, 2] == 10647 / 4096
+    grp._requantize(0, hqekv.INT2)
+    tier, kc, ks, kz, vc, vs, vz = grp.codes[0]
+    assert tier == hqekv.INT2
+    assert kc[:3].tolist() == [0, 3, 3] and vc[:3].tolist() == [0, 3, 3]
+    assert float(ks[0]) == 1.0 and float(vs[0]) == 1.0
+    assert grp.kcur[0, 2] == 3.0 and grp.vcur[0, 2] == 3.0
+    # straight from the original the same step gives code 2 at channel 2
+    assert codec.per_token_quantize(row, 2)[0][2] == 2
+    # a token going straight to INT2 (the other row) does quantize the original
+    grp._requantize(1, hqekv.INT2)
+    assert grp.codes[1][1][:3].tolist() == [0, 3, 2]
+
+
+# ---------------------------------------------------------------------------
+# FLT_MIN flush (a reading: a head's mass on a unit counts as 0 when the
+# unit's sum is below 2^-126; the flush is applied after the sum over the
+# unit's tokens, not to each probability)
+# ---------------------------------------------------------------------------
+
+def test_qevict_flush_applies_to_unit_sums():
+    """One query head, d = 4, q = e_0 (logit = k_0 / 2).  Position 0 holds the
+    largest logit 0; window 1 (positions 4..11) holds logits -88.5, each
+    probability e^-88.5 = 3.8e-39 below FLT_MIN = 1.18e-38, their sum over the
+    window 3.0e-38 above it; window 2 (positions 12..19) holds one token at
+    -88.5 (a sum below FLT_MIN).  Per-unit flushing keeps window 1's mass and
+    drops window 2's; flushing each probability would drop both."""
+    from oracle import qevict as oe
+    T, d = 21, 4
+    k = np.zeros((1, T, d), np.float32)
+    k[0, 1:, 0] = -400.0                       # everything else negligible
+    k[0, 4:12, 0] = -177.0                     # logit -88.5
+    k[0, 12, 0] = -177.0
+    v = np.zeros((1, T, d), np.float32)
+    seq = oe.QEvictSequence(_bf16(k), _bf16(v), window=8, omega=100, n_sink=4, n_recent=1,
+                            k_full=10, k_quant=10, n_q_heads=1)
+    seq.prefill(T - 1)
+    q = _bf16(np.array([[1.0, 0, 0, 0]], np.float32))
+    _, mass = seq.step(0, q)
+    p = math.exp(-88.5) / (1 + 9 * math.exp(-88.5))
+    assert p < np.finfo(np.float32).tiny < 8 * p
+    assert mass[0, 1] == pytest.approx(8 * p, rel=1e-12)
+    assert mass[0, 2] == 0.0
+    assert seq.score[1] == pytest.approx(8 * p, rel=1e-12) and seq.score[2] == 0.0
