@@ -7,10 +7,17 @@ prompt, H_q = 32, H_kv = 8, d = 128, 16-token windows routed every 16 steps,
 
 A step is one decode step of the whole path for the batch: append the new
 token, attention with fused mass emission and score accumulation, and -- every
-Omega steps -- the routing event (rank, pack, promote, evict).  The timed
-region is K consecutive decode steps starting right after the prompt (so it
-contains the heavy all-BF16 phase before the first routing event and every
-routing event); W warm-up steps run first on a separate cache.
+Omega steps -- the routing event (rank, pack, promote, evict).
+
+Phases (each timed on its own and reported under "phases"):
+* pre_route -- the first Omega steps after the prompt, which end with the
+  first routing event: every prompt window is still full precision (2.15 GB
+  read per attention step), and the first event packs 612 windows per
+  sequence.  A transient of the prompt, measured but not part of `value`.
+* steady -- W untimed warm-up steps, then the K timed steps: the routed
+  cache, with a routing event every Omega steps.  `value` is its tokens/s and
+  `roofline` is taken on its attention launches.
+* events -- the routing calls inside the timed steps (rank + pack/promote).
 
 Prints one JSON line.  --gpus N with N > 1 is refused: this build measures
 one GPU.
@@ -21,7 +28,9 @@ above): `stress` (QEvict, batch 32, 128K prompt, G = 8, 32-token windows),
 (the same layer with 32-position chunks, scores from the last 20 queries and
 an event every 32 tokens), `h2o` (per-token heavy hitters, batch 1,
 512-token scored prompt) or `tiny`.  Their lines carry the same fields; their
-oracle baseline runs sequence 0 for up to 15 s of decode steps.
+oracle baseline runs sequence 0 for up to 15 s of decode steps.  The token
+policies (H2O, HqeKV) make their first assignment at the end of the prompt,
+so their timed steps start routed (no pre_route phase).
 """
 from __future__ import annotations
 
@@ -42,10 +51,11 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 # The attention kernel is timed with HIP events on its own stream on every
-# PROFILE_STRIDE-th step of the timed region (steps 0, 8, 16, ...): an event
+# PROFILE_STRIDE-th step of the timed region (steps 0, 4, 8, ...): an event
 # pair delays the following launch by a few microseconds, so timing every step
-# would slow the very loop whose throughput is reported.
-PROFILE_STRIDE = 8
+# would slow the very loop whose throughput is reported.  The pre-route phase
+# is short and reported on its own, so all of its launches are timed.
+PROFILE_STRIDE = 4
 # The attention kernel is built from these sources; the counter summary is
 # only used while their hash matches the one it was taken on.
 KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
@@ -60,12 +70,16 @@ DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_HQEKV: "bf16+int4+int2+int1 (fp32 accumulate)"}
 
 
-def describe(cfg, steps):
-    head = (f"batch {cfg.batch}, {cfg.prefill}-token prompt + {steps} decode steps, "
+def describe(cfg, steps, first=0):
+    span = f"decode steps {first}..{first + steps - 1} timed" if first else f"{steps} decode steps timed"
+    head = (f"batch {cfg.batch}, {cfg.prefill}-token prompt, {span}, "
             f"Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim}")
     if cfg.name == "drift":
+        sw = cfg.switch_step
+        inside = ("inside the timed steps" if first <= sw < first + steps else
+                  "before the timed steps" if sw < first else "after the timed steps")
         return ("QEvict three-tier attention drift: " + head + ", window=Omega=16, 5 sinks + 64 recent, "
-                "Kf=204 BF16 + Kq=612 INT2 windows (group 32), clusters A->B switch at step 100")
+                f"Kf=204 BF16 + Kq=612 INT2 windows (group 32); query switch A->B at step {sw} ({inside})")
     if cfg.policy == W.POLICY_QEVICT:
         return (f"QEvict three-tier ({cfg.name}): " + head + f", window={cfg.window} Omega={cfg.omega}, "
                 f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} INT2 windows")
@@ -156,9 +170,14 @@ def attend_bytes(cfg, sched):
 # ---------------------------------------------------------------------------
 
 def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
+    """The pre-route phase (steps 0 .. Omega-1 and the first routing event),
+    W warm-up steps, then `steps` timed steps, all on one cache.  Attention
+    launches are timed with HIP events attached to the dispatch (every one in
+    the pre-route phase, every PROFILE_STRIDE-th in the timed steps); routing
+    calls with torch events on the same stream."""
     import torch
     from tiered_quantization_eviction_amd import Cache, make_config
-    P = cfg.prefill
+    P, om = cfg.prefill, cfg.omega
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     k_pre = dev(K[:, :, :P])
     v_pre = dev(V[:, :, :P])
@@ -166,39 +185,51 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
     v_dec = dev(np.ascontiguousarray(V[:, :, P:].transpose(2, 0, 1, 3))[:, :, :, None, :])
     q_dec = dev(np.ascontiguousarray(Q.transpose(1, 0, 2, 3)))                             # [S, B, Hq, d]
     out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
-    conf = make_config(cfg, n_splits=n_splits)
+    cache = Cache(make_config(cfg, n_splits=n_splits))
+    cache.append(k_pre, v_pre)
+    ev_route = []
 
-    def loop(cache, n, record=None):
-        for s in range(n):
+    def loop(s0, n, firsts=None):
+        for s in range(s0, s0 + n):
             cache.append(k_dec[s], v_dec[s])
             cache.decode_attend(q_dec[s], out)
-            if (s + 1) % cfg.omega == 0:
+            if firsts is not None and len(firsts) < 4:
+                firsts.append(out.clone())
+            if (s + 1) % om == 0:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
                 cache.route()
-            if record is not None:
-                record.append(out.clone())
+                e1.record()
+                ev_route.append((s, e0, e1))
 
-    # warm-up on its own cache; keep its first outputs for the parity spot check
+    # pre-route phase: the all-full-precision steps and the first routing event
     firsts = []
-    if warmup > 0:
-        cw = Cache(conf)
-        cw.append(k_pre, v_pre)
-        loop(cw, min(warmup, cfg.steps), firsts)
-        torch.cuda.synchronize()
-        cw.close()
-        del cw
-    cache = Cache(conf)
-    cache.append(k_pre, v_pre)
+    cache.profile_start(om, 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop(0, om, firsts)
+    torch.cuda.synchronize()
+    pre_wall = time.perf_counter() - t0
+    pre_att = cache.profile_read(om)
+    pre_route = [e0.elapsed_time(e1) for _, e0, e1 in ev_route]
+    ev_route.clear()
+    # warm-up on the routed cache, then the timed steps
+    loop(om, warmup)
+    s0 = om + warmup
     n_prof = (steps + PROFILE_STRIDE - 1) // PROFILE_STRIDE
     cache.profile_start(n_prof, PROFILE_STRIDE)
     torch.cuda.synchronize()
+    ev_route.clear()
     t0 = time.perf_counter()
-    loop(cache, steps)
+    loop(s0, steps)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    wall = time.perf_counter() - t0
     attend_ms = cache.profile_read(n_prof)
-    splits = cache.info("splits")
-    status = cache.status()
-    return (t1 - t0), attend_ms, [f[0].cpu().numpy() for f in firsts], splits, status
+    route_ms = [e0.elapsed_time(e1) for _, e0, e1 in ev_route]
+    return {"pre_wall": pre_wall, "pre_attend_ms": pre_att, "pre_route_ms": pre_route, "first": s0,
+            "wall": wall, "attend_ms": attend_ms, "route_ms": route_ms,
+            "firsts": [f[0].cpu().numpy() for f in firsts], "splits": cache.info("splits"),
+            "status": cache.status()}
 
 
 # token modes (H2O, HqeKV): every token is a unit, decisions per (sequence, KV head)
@@ -246,14 +277,18 @@ def run_gpu_tok(cfg, K, V, Q, QP, steps, n_splits):
         cache.prefill_score(qp)
         cache.route()
 
-    def loop(cache, n, on_route=None):
+    route_ev = []
+
+    def loop(cache, n):
         for s in range(n):
             cache.append(k_dec[s], v_dec[s])
             cache.decode_attend(q_dec[s], out)
             if (s + 1) % cfg.omega == 0:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
                 cache.route()
-                if on_route is not None:
-                    on_route(s)
+                e1.record()
+                route_ev.append((e0, e1))
 
     def hist(cache):
         t = cache.export("tiers").cpu().numpy().reshape(cfg.batch * cfg.n_kv_heads, T)
@@ -294,7 +329,8 @@ def run_gpu_tok(cfg, K, V, Q, QP, steps, n_splits):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     attend_ms = cache.profile_read(n_prof)
-    return (t1 - t0), attend_ms, launch_bytes, cache.info("splits"), cache.status()
+    route_ms = [e0.elapsed_time(e1) for e0, e1 in route_ev]
+    return (t1 - t0), attend_ms, launch_bytes, cache.info("splits"), cache.status(), route_ms
 
 
 # ---------------------------------------------------------------------------
@@ -383,20 +419,28 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def read_traffic(src_hash):
-    """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current kernel source."""
+def read_traffic(src_hash, workload, first, steps):
+    """HBM bytes per attention launch from the committed counter summary,
+    only if it was taken on the current kernel source, on this workload and
+    on the same launches the events time (the routed steps from `first`)."""
+    if workload != "drift":
+        return None
     try:
         txt = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    h = t = None
+    f = {}
     for ln in txt.splitlines():
-        if ln.startswith("kernel_source_sha256:"):
-            h = ln.split(":", 1)[1].strip()
-        if ln.startswith("traffic_bytes_per_launch:"):
-            t = float(ln.split(":", 1)[1].strip())
-    return t if (h == src_hash and t is not None) else None
+        if ":" in ln and not ln.startswith(("|", "#", " ")):
+            k, v = ln.split(":", 1)
+            f[k.strip()] = v.strip()
+    try:
+        ok = (f.get("kernel_source_sha256") == src_hash and f.get("launch_mix") == "routed" and
+              int(f.get("first_step", -1)) == first and int(f.get("stride", -1)) == PROFILE_STRIDE and
+              int(f.get("steps", -1)) >= steps)
+        return float(f["traffic_bytes_per_launch"]) if ok else None
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_probe(mib):
@@ -414,12 +458,21 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
 
 
+def _phase(bytes_list, ms_list):
+    """Average attention launch time (us), its algorithmic bytes and GB/s."""
+    if not ms_list:
+        return None, None, None
+    us = float(np.mean(ms_list)) * 1e3
+    b = float(np.mean(bytes_list))
+    return us, b, b / (us * 1e-6) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="drift", choices=sorted(WORKLOADS))
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--cpu-steps", type=int, default=512)
     ap.add_argument("--cpu-seqs", type=int, default=2)
@@ -435,32 +488,45 @@ def main():
               f"(the multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
         sys.exit(2)
     cfg = WORKLOADS[a.workload]
-    steps = min(a.steps, cfg.steps)
     token_mode = cfg.policy != W.POLICY_QEVICT
+    warmup = 0 if token_mode else max(0, min(a.warmup, cfg.steps - cfg.omega - 1))
+    lead = 0 if token_mode else cfg.omega + warmup       # decode steps before the timed ones
+    steps = max(1, min(a.steps, cfg.steps - lead))
     log(f"bench: generating inputs ({cfg.batch} x {cfg.total_tokens} tokens)")
     t = time.perf_counter()
     K, V, Q = make_inputs(cfg)
     log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running "
-        f"{'a counting pass' if token_mode else f'{a.warmup} warm-up'} + {steps} timed steps")
+        f"{'a counting pass' if token_mode else f'{cfg.omega} pre-route + {warmup} warm-up'} + {steps} timed steps")
     firsts = []
+    pre = None
     if token_mode:
         wl = W.Workload(cfg)
         QP = np.stack([prompt_queries(cfg, wl, b) for b in range(cfg.batch)])
-        wall, attend_ms, abytes, splits, status = run_gpu_tok(cfg, K, V, Q, QP, steps, a.splits)
+        wall, attend_ms, abytes, splits, status, route_ms = run_gpu_tok(cfg, K, V, Q, QP, steps, a.splits)
+        first = 0
     else:
-        wall, attend_ms, firsts, splits, status = run_gpu(cfg, K, V, Q, steps, a.warmup, a.splits)
-        abytes = attend_bytes(cfg, live_schedule(cfg, steps))
+        r = run_gpu(cfg, K, V, Q, steps, warmup, a.splits)
+        wall, attend_ms, firsts, splits, status, route_ms = (r["wall"], r["attend_ms"], r["firsts"], r["splits"],
+                                                             r["status"], r["route_ms"])
+        first = r["first"]
+        sched_bytes = attend_bytes(cfg, live_schedule(cfg, first + steps))
+        abytes = sched_bytes[first:]
+        pre_us, pre_b, pre_gbps = _phase(sched_bytes[:cfg.omega], r["pre_attend_ms"])
+        pre = {"steps": cfg.omega, "ms_per_step": r["pre_wall"] * 1e3 / cfg.omega,
+               "tokens_per_s": cfg.batch * cfg.omega / r["pre_wall"],
+               "attention_us": pre_us, "algorithmic_bytes_per_launch": pre_b, "attention_GBps": pre_gbps,
+               "attention_frac_of_peak": pre_gbps / HBM_PEAK_GBPS,
+               "first_event_us": r["pre_route_ms"][0] * 1e3 if r["pre_route_ms"] else None,
+               "timed_launches": f"all {len(r['pre_attend_ms'])}"}
     if status != 0:
         log(f"bench: device status {status}")
     kv_bytes = sum(abytes)
     tok_s = cfg.batch * steps / wall
     sampled = abytes[::PROFILE_STRIDE][:len(attend_ms)]          # the launches that were timed
-    att_avg_s = float(np.mean(attend_ms)) / 1e3
-    bytes_per_launch = float(np.mean(sampled))
-    achieved = bytes_per_launch / att_avg_s / 1e9
+    att_us, bytes_per_launch, achieved = _phase(sampled, attend_ms)
     src_hash = kernel_source_hash()
-    traffic = read_traffic(src_hash) if a.workload == "drift" else None
-    log(f"bench: {wall * 1e3:.1f} ms for {steps} steps; attention avg {att_avg_s * 1e6:.1f} us, "
+    traffic = read_traffic(src_hash, a.workload, first, steps)
+    log(f"bench: {wall * 1e3:.1f} ms for {steps} timed steps; attention avg {att_us:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
     cpu = None
     worst = None
@@ -476,6 +542,14 @@ def main():
         cpu, worst = cpu_baseline(cfg, K, V, Q, 1, cfg.steps, firsts, budget_s=CPU_BUDGET_S)
     kernel = ("tok_attend_kernel<%d>" % cfg.head_dim if token_mode else
               "attend_qevict_kernel<%d, %d>" % (cfg.head_dim, 2 if cfg.group_size == 4 else 1))
+    events = {"count": len(route_ms),
+              "avg_us": float(np.mean(route_ms)) * 1e3 if route_ms else None,
+              "max_us": float(np.max(route_ms)) * 1e3 if route_ms else None,
+              "share_of_timed_wall": float(np.sum(route_ms)) / 1e3 / wall if route_ms else 0.0}
+    steady = {"first_step": first, "steps": steps, "ms_per_step": wall * 1e3 / steps, "tokens_per_s": tok_s,
+              "attention_us": att_us, "algorithmic_bytes_per_launch": bytes_per_launch, "attention_GBps": achieved,
+              "attention_frac_of_peak": achieved / HBM_PEAK_GBPS,
+              "whole_loop_kv_GBps": kv_bytes / wall / 1e9}
     res = {
         "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer"
                   if a.workload == "drift" else "decode tokens/s + KV-read GB/s (% of HBM peak), 1 layer",
@@ -483,23 +557,25 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": 0 if token_mode else a.warmup,
+        "warmup": warmup,
         "ms_per_step": wall * 1e3 / steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPES[cfg.policy],
         "data": "synthetic",
-        "config": {"workload": describe(cfg, steps), "global_batch": cfg.batch, "seq_len": cfg.total_tokens,
-                   "parallelism": "single GPU", "attention_splits": splits},
+        "config": {"workload": describe(cfg, steps, first), "global_batch": cfg.batch,
+                   "seq_len": cfg.total_tokens, "parallelism": "single GPU", "attention_splits": splits},
         "kv_read_GBps": kv_bytes / wall / 1e9,
         "kv_read_pct_hbm_peak": 100.0 * kv_bytes / wall / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": kernel,
                      "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": att_avg_s * 1e6,
-                     "timed_launches": f"{len(attend_ms)} of {steps} (every {PROFILE_STRIDE}th step)"},
+                     "avg_launch_us": att_us,
+                     "timed_launches": f"{len(attend_ms)} of the {steps} timed steps (every "
+                                       f"{PROFILE_STRIDE}th, from decode step {first})"},
+        "phases": {"pre_route": pre, "steady": steady, "events": events},
         "cpu_baseline": cpu,
         "parity_spot_check_max_abs": worst,
     }

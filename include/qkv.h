@@ -237,15 +237,30 @@ int qkv_quantize_window(const void *x, int32_t x_dtype, int32_t n_blocks, int32_
                         qkv_stream stream);
 
 /*
- * Stateless multi-tier ranking: entries with eligible[i] != 0 are ordered by
- * (score descending, pos descending); the first tier_counts[0] get tier 0, the
- * next tier_counts[1] tier 1, ..., the remaining eligible entries tier n_tiers,
- * ineligible entries 255.  All pointers are device memory; n <= 8192.
+ * Stateless multi-tier ranking (HqeKV notes section 3.7, the 8-token worked
+ * example: tokens ordered by their importance and cut by the tier shares;
+ * H2O notes section 2.1 and section 5.1: one fixed order with position as the
+ * tie key).  Entries with eligible[i] != 0 are ordered by (score descending,
+ * pos descending); the first tier_counts[0] get tier 0, the next
+ * tier_counts[1] tier 1, ..., the remaining eligible entries tier n_tiers,
+ * ineligible entries 255.  score float32 [n], pos int32 [n], eligible uint8
+ * [n], tier_counts int32 [n_tiers] (non-negative), tier_out uint8 [n]; all
+ * device memory owned by the caller.  1 <= n <= 8192 (the ranking is one LDS
+ * sort), 0 <= n_tiers <= 254; QKV_EINVAL otherwise.
  */
 int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int32_t n,
                    const int32_t *tier_counts, int32_t n_tiers, uint8_t *tier_out, qkv_stream stream);
 
 /* Export state into device memory `dst` (`bytes` must equal the size below).
+ * The kinds are the pieces of a session's state that the pages name: the
+ * tier of every unit and its accumulated score (QEvict notes section 4.2
+ * Eq.(1), section 4.4 Eq.(4)-(6)), the pack-once ledger of codes and float16
+ * scale/zero (section 4.4, Algorithm 1 and its migration-stable quantization
+ * paragraph; section 10h asks for a ledger whose lifetime follows the
+ * window's), the content read in full precision, and -- for a session
+ * restore (H2O notes section 6.2: the heavy/recent boundary, scores,
+ * positions and the update step count) -- the ranked list order and the step
+ * scalars.  Codes and parameters are in the canonical packing:
  *   QKV_EXPORT_TIERS   uint8   [batch, n_units]
  *   QKV_EXPORT_SCORES  float32 [batch, n_units]
  *   QKV_EXPORT_LEDGER  uint8   [batch, n_units]   1 if the unit holds ledger codes
@@ -255,9 +270,22 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *   QKV_EXPORT_VPARAMS uint16  [batch, n_units, n_kv_heads, window, head_dim/group, 2]
  *   QKV_EXPORT_KEYS    uint16  [batch, n_kv_heads, max_ctx, head_dim]  full-precision content
  *   QKV_EXPORT_VALUES  uint16  [batch, n_kv_heads, max_ctx, head_dim]
+ *   QKV_EXPORT_ROUTED  int32   [batch, n_units]   ranked windows in rank order (full precision
+ *                                                  first, then quantized); entries past the
+ *                                                  ranked count are unspecified
+ *   QKV_EXPORT_STATE   int64   [16]               format tag, policy, geometry and step scalars
  * (units without a ledger export zero codes and parameters).
- * Token policies (H2O) export TIERS as uint8 [batch, n_kv_heads, max_ctx] and
- * SCORES as float32 [batch, n_kv_heads, max_ctx]; the other kinds are EINVAL.
+ * Token policies (H2O, HqeKV), per (sequence, KV head, position):
+ *   TIERS uint8 [batch, n_kv_heads, max_ctx]; SCORES float32 [same] (masses
+ *   pending in list order are added first); KEYS / VALUES uint16 [batch,
+ *   n_kv_heads, max_ctx, head_dim] (the appended originals); HqeKV also
+ *   KCODES / VCODES uint8 [batch, n_kv_heads, max_ctx, head_dim/2] and
+ *   KPARAMS / VPARAMS uint16 [batch, n_kv_heads, max_ctx, head_dim/32, 2]
+ *   (per-token records); ROUTED int32 [batch, n_kv_heads, 4 + 4*L]: the token
+ *   counts of the full-precision, INT4, INT2 and INT1 lists, then the four
+ *   lists of positions in list order, L = qkv_info(QKV_INFO_LIST_CAPACITY)
+ *   entries each (H2O: the kept heavy hitters in list 0); STATE as above.
+ * A kind a policy does not hold is QKV_EINVAL.
  */
 enum {
   QKV_EXPORT_TIERS = 0,
@@ -269,9 +297,35 @@ enum {
   QKV_EXPORT_VPARAMS = 6,
   QKV_EXPORT_KEYS = 7,
   QKV_EXPORT_VALUES = 8,
+  QKV_EXPORT_ROUTED = 9,
+  QKV_EXPORT_STATE = 10,
 };
 int qkv_export(const qkv_cache *cache, int32_t what, void *dst, size_t bytes, qkv_stream stream);
 size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);
+
+/*
+ * Session restore (H2O notes section 6.2: restoring a session needs the
+ * heavy/recent boundary, the scores, the positions and the update step
+ * count; QEvict notes section 10h: the ledger of codes and scale/zero lives
+ * as long as its window).  `src` is device memory in the layout qkv_export
+ * writes for the same kind and `bytes` must equal qkv_export_bytes(cache,
+ * what).  A full restore imports, into a cache created with the same
+ * configuration, every kind the policy exports:
+ *   QEvict: STATE, TIERS, SCORES, LEDGER, ROUTED, KCODES, VCODES, KPARAMS,
+ *           VPARAMS, KEYS, VALUES;
+ *   H2O:    STATE, TIERS, SCORES, ROUTED, KEYS, VALUES;
+ *   HqeKV:  the H2O kinds plus KCODES, VCODES, KPARAMS, VPARAMS.
+ * The order is free.  Structures derived from these (list-order scores, the
+ * compact tiles of the ranked lists, value ranges) are rebuilt on `stream`
+ * before the next append, attention, prompt scoring, routing or export, so a
+ * restored cache continues exactly as the exported one does (no pending
+ * masses are carried: SCORES already holds them).  STATE is read back to the
+ * host, so importing it waits for `stream`.  Errors: QKV_EINVAL for a kind
+ * the policy does not hold, a wrong size, or a STATE whose format tag,
+ * policy or geometry differs from the cache's or whose step scalars are out
+ * of range (the cache is then unchanged).
+ */
+int qkv_import(qkv_cache *cache, int32_t what, const void *src, size_t bytes, qkv_stream stream);
 
 /* Host-side counters. */
 enum {
@@ -281,6 +335,7 @@ enum {
   QKV_INFO_ROUTES = 3,      /* routing events                                */
   QKV_INFO_SPLITS = 4,      /* attention splits per (sequence, KV head)      */
   QKV_INFO_WORKSPACE = 5,   /* workspace bytes in use                        */
+  QKV_INFO_LIST_CAPACITY = 6, /* token policies: entries per list of QKV_EXPORT_ROUTED */
 };
 int qkv_info(const qkv_cache *cache, int32_t what, int64_t *value);
 

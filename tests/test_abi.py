@@ -147,3 +147,34 @@ def test_workspace_holds_payload_of_config3():
     pages = 16 * U * 8 * 2 * 16 * 128 * 2
     ledger = 16 * U * 8 * (512 + 512 + 512 + 256)
     assert pages + ledger <= L.workspace_bytes(c) <= pages + ledger + 64 * 2 ** 20
+
+
+def test_snapshot_and_ranking_arguments_checked_on_host():
+    """qkv_import / qkv_export refuse a missing cache or buffer, and the
+    stateless ranking refuses more entries than its LDS sort holds (8192),
+    all before any device work (the pointers below are never dereferenced)."""
+    L, lib = _lib()
+    assert "qkv_import" in declared_functions()
+    fake = ctypes.c_void_p(256)
+    assert lib.qkv_import(None, 0, fake, 1, None) == L.EINVAL
+    assert lib.qkv_export(None, 0, fake, 1, None) == L.EINVAL
+    assert lib.qkv_export_bytes(None, 0) == 0
+    assert lib.qkv_rank_tiers(fake, fake, fake, 8193, fake, 1, fake, None) == L.EINVAL
+    assert lib.qkv_rank_tiers(fake, fake, fake, 0, fake, 1, fake, None) == L.EINVAL
+    assert lib.qkv_rank_tiers(fake, fake, fake, 16, fake, 255, fake, None) == L.EINVAL
+
+
+def test_binding_checks_dtype_and_shape():
+    """The binding refuses tensors whose element size or shape the C call
+    would read or write past (checked on host tensors: no GPU needed)."""
+    import torch
+    L, _ = _lib()
+    L._check_tensor(torch.zeros((2, 3), dtype=torch.bfloat16), "x", (2, 3), "16")
+    L._check_tensor(torch.zeros((2, 3), dtype=torch.int16), "x", (2, 3), "16")
+    L._check_tensor(torch.zeros((2, 3), dtype=torch.float32), "x", (2, 3), "f32")
+    for t, shape, kind in ((torch.zeros((2, 3), dtype=torch.float32), (2, 3), "16"),
+                           (torch.zeros((2, 3), dtype=torch.bfloat16), (2, 3), "f32"),
+                           (torch.zeros((2, 4), dtype=torch.int16), (2, 3), "16"),
+                           (torch.zeros((3, 2), dtype=torch.float32), (2, 3), "f32")):
+        with pytest.raises(ValueError):
+            L._check_tensor(t, "x", shape, kind)

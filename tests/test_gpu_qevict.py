@@ -135,7 +135,7 @@ def test_rank_tiers_examples(torch_cuda):
     assert pos[t == 1].tolist() == [h["evicted"]]
 
 
-@pytest.mark.parametrize("n", [1, 7, 100, 1000, 4096])
+@pytest.mark.parametrize("n", [1, 7, 100, 1000, 4096, 8192])
 def test_rank_tiers_random_with_ties(torch_cuda, n):
     from tiered_quantization_eviction_amd import _lib as L
     log(f"rank tiers random n={n}")

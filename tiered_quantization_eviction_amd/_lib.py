@@ -18,8 +18,13 @@ KIND_K_PER_CHANNEL, KIND_PER_TOKEN, KIND_INT1_NORMAL = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 TIER_EMPTY, TIER_SINK, TIER_RECENT, TIER_FULL, TIER_QUANT, TIER_EVICTED = range(6)
 EXPORT = {"tiers": 0, "scores": 1, "ledger": 2, "kcodes": 3, "vcodes": 4, "kparams": 5, "vparams": 6,
-          "keys": 7, "values": 8}
-INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5}
+          "keys": 7, "values": 8, "routed": 9, "state": 10}
+INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5, "list_capacity": 6}
+# what each policy's session snapshot holds (qkv_import restores them all)
+SNAPSHOT = {0: ("state", "tiers", "scores", "ledger", "routed", "kcodes", "vcodes", "kparams", "vparams",
+                "keys", "values"),
+            1: ("state", "tiers", "scores", "routed", "keys", "values"),
+            2: ("state", "tiers", "scores", "routed", "keys", "values", "kcodes", "vcodes", "kparams", "vparams")}
 
 
 class QkvError(RuntimeError):
@@ -66,6 +71,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_quantize_status.argtypes = [_vp]
         L.qkv_rank_tiers.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp]
         L.qkv_export.argtypes = [_vp, _i32, _vp, _sz, _vp]
+        L.qkv_import.argtypes = [_vp, _i32, _vp, _sz, _vp]
         L.qkv_export_bytes.restype = _sz
         L.qkv_export_bytes.argtypes = [_vp, _i32]
         L.qkv_info.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_int64)]
@@ -99,6 +105,21 @@ def _ptr(t) -> int:
     if not t.is_contiguous():
         raise ValueError("contiguous tensor required")
     return t.data_ptr()
+
+
+def _check_tensor(t, what: str, shape, kind: str) -> None:
+    """The C calls take raw pointers: a tensor of the wrong element size or
+    shape would be read or written past its end, so both are checked here.
+    kind '16': 2-byte elements (bfloat16 bits as bfloat16, int16 or uint16);
+    'f32': float32."""
+    import torch
+    ok16 = (torch.bfloat16, torch.int16, torch.float16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
+    if kind == "16" and t.dtype not in ok16:
+        raise ValueError(f"{what}: 2-byte (bfloat16 bits) tensor required, got {t.dtype}")
+    if kind == "f32" and t.dtype != torch.float32:
+        raise ValueError(f"{what}: float32 tensor required, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(shape)} required, got {tuple(t.shape)}")
 
 
 def make_config(cfg=None, *, n_splits: int = 0, max_ctx: int | None = None, **kw) -> QkvConfig:
@@ -176,10 +197,22 @@ class Cache:
 
     def append(self, k, v, stream=None):
         """k, v: bf16 [B, Hkv, n, d] device tensors."""
+        c = self.c
+        if k.dim() != 4:
+            raise ValueError("k: [B, Hkv, n, d] required")
         n = int(k.shape[2])
+        _check_tensor(k, "k", (c.batch, c.n_kv_heads, n, c.head_dim), "16")
+        _check_tensor(v, "v", (c.batch, c.n_kv_heads, n, c.head_dim), "16")
         _check(_lib().qkv_append(self.h, _ptr(k), _ptr(v), n, _stream(stream)), "qkv_append")
 
     def decode_attend(self, q, out, mass_out=None, stream=None):
+        """q: bf16 [B, Hq, d]; out: float32 [B, Hq, d]; mass_out: optional
+        float32 [B, Hkv, units]."""
+        c = self.c
+        _check_tensor(q, "q", (c.batch, c.n_q_heads, c.head_dim), "16")
+        _check_tensor(out, "out", (c.batch, c.n_q_heads, c.head_dim), "f32")
+        if mass_out is not None:
+            _check_tensor(mass_out, "mass_out", (c.batch, c.n_kv_heads, self.info("units")), "f32")
         _check(_lib().qkv_decode_attend(self.h, _ptr(q), _ptr(out), _ptr(mass_out), _stream(stream)),
                "qkv_decode_attend")
 
@@ -188,15 +221,38 @@ class Cache:
 
     def prefill_score(self, q, stream=None):
         """q: bf16 [B, n_queries, Hq, d] queries of the last appended positions."""
+        c = self.c
+        if q.dim() != 4:
+            raise ValueError("q: [B, n_queries, Hq, d] required")
+        _check_tensor(q, "q", (c.batch, int(q.shape[1]), c.n_q_heads, c.head_dim), "16")
         _check(_lib().qkv_prefill_score(self.h, _ptr(q), int(q.shape[1]), _stream(stream)), "qkv_prefill_score")
 
     def export(self, what: str, stream=None):
         import torch
         code = EXPORT[what]
         nbytes = int(_lib().qkv_export_bytes(self.h, code))
+        if nbytes == 0:
+            raise QkvError(EINVAL, f"qkv_export({what})")
         dst = torch.empty(nbytes, dtype=torch.uint8, device=self.workspace.device)
         _check(_lib().qkv_export(self.h, code, _ptr(dst), nbytes, _stream(stream)), "qkv_export")
         return dst
+
+    def import_(self, what: str, src, stream=None):
+        """Restore one kind of state from a uint8 device tensor that export()
+        returned for a cache of the same configuration."""
+        import torch
+        if src.dtype != torch.uint8 or src.dim() != 1:
+            raise ValueError("src: 1-D uint8 tensor (as export returns) required")
+        _check(_lib().qkv_import(self.h, EXPORT[what], _ptr(src), int(src.numel()), _stream(stream)),
+               f"qkv_import({what})")
+
+    def snapshot(self, stream=None) -> dict:
+        """Every kind of state this policy holds, as export() tensors."""
+        return {w: self.export(w, stream) for w in SNAPSHOT[self.c.policy]}
+
+    def restore(self, snap: dict, stream=None) -> None:
+        for w, t in snap.items():
+            self.import_(w, t, stream)
 
     def info(self, what: str) -> int:
         v = ctypes.c_int64()
@@ -220,7 +276,11 @@ def quantize_window(x, kind: int, bits: int, group: int = 32, stream=None):
     """x: [n_blocks, tokens, d] bf16 (as int16/uint16/bfloat16) or float32 device tensor.
     Returns (codes uint8 [n_blocks, code_bytes], params uint16 [n_blocks, ...])."""
     import torch
+    if x.dim() != 3:
+        raise ValueError("x: [n_blocks, tokens, d] required")
     n_blocks, tokens, d = (int(s) for s in x.shape)
+    if x.dtype != torch.float32:
+        _check_tensor(x, "x", (n_blocks, tokens, d), "16")
     dtype = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
     code_bytes = (tokens * d * bits + 7) // 8
     if kind == KIND_K_PER_CHANNEL:
@@ -243,6 +303,11 @@ def quantize_status(stream=None) -> int:
 def rank_tiers(score, pos, eligible, counts, stream=None):
     import torch
     n = int(score.numel())
+    if score.dtype != torch.float32 or pos.dtype != torch.int32 or eligible.dtype != torch.uint8 \
+            or counts.dtype != torch.int32:
+        raise ValueError("rank_tiers: score float32, pos int32, eligible uint8, counts int32 required")
+    if int(pos.numel()) != n or int(eligible.numel()) != n:
+        raise ValueError("rank_tiers: score, pos and eligible must have the same length")
     out = torch.empty(n, dtype=torch.uint8, device=score.device)
     _check(_lib().qkv_rank_tiers(_ptr(score), _ptr(pos), _ptr(eligible), n, _ptr(counts), int(counts.numel()),
                                  _ptr(out), _stream(stream)), "qkv_rank_tiers")

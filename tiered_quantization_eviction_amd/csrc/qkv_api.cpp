@@ -32,6 +32,9 @@ struct qkv_cache {
   int routed;     // ranked windows held (same for every sequence)
   long long steps;
   long long routes;
+  // after an import: derived structures (list-order scores, compact tiles,
+  // value ranges) are rebuilt before the next call that reads them
+  bool rebuild_pending;
   // kernel timing
   hipEvent_t *ev;   // 2 * ev_n events
   int ev_n, ev_next, ev_stride, ev_calls;
@@ -195,7 +198,6 @@ size_t carve(const Geom &g, char *base, State &st) {
   st.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
   st.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
   st.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
-  st.tail_next = (int32_t *)take((size_t)g.B * g.Hkv * 4);
   st.slist = (float *)take(BU * 4);
   st.status = (int32_t *)take(16);
   return off;
@@ -211,6 +213,56 @@ StepInfo step_info(const qkv_cache *c) {
   si.r1 = c->N > c->g.n_sink ? unit_of(c->g, c->N - 1) : 0;
   si.n_routed = c->routed;
   return si;
+}
+
+// rebuild what an import left pending, on the stream of the call that needs it
+int settle(qkv_cache *c, hipStream_t s) {
+  if (!c->rebuild_pending) return QKV_OK;
+  const int rc = c->tok ? hip_err(tok_launch_rebuild(c->tg, c->ts, c->n_cmp, s))
+                        : hip_err(launch_rebuild(c->g, c->st, step_info(c), s));
+  if (rc == QKV_OK) c->rebuild_pending = false;
+  return rc;
+}
+
+Snapshot make_snapshot(const qkv_cache *c) {
+  Snapshot sn;
+  memset(&sn, 0, sizeof sn);
+  sn.v[SNAP_TAG] = SNAP_TAG_VALUE;
+  sn.v[SNAP_POLICY] = c->cfg.policy;
+  sn.v[SNAP_BATCH] = c->cfg.batch;
+  sn.v[SNAP_HQ] = c->cfg.n_q_heads;
+  sn.v[SNAP_HKV] = c->cfg.n_kv_heads;
+  sn.v[SNAP_D] = c->cfg.head_dim;
+  sn.v[SNAP_WINDOW] = c->cfg.window;
+  sn.v[SNAP_MAXCTX] = c->cfg.max_ctx;
+  sn.v[SNAP_N] = c->N;
+  sn.v[SNAP_R] = c->tok ? c->r_tok : c->r0;
+  sn.v[SNAP_RANKED] = c->tok ? c->n_cmp : c->routed;
+  sn.v[SNAP_STEPS] = c->steps;
+  sn.v[SNAP_ROUTES] = c->routes;
+  sn.v[SNAP_SINCE_ROUTE] = c->steps_since_route;
+  sn.v[SNAP_LAST_EVENT] = c->last_event_N;
+  return sn;
+}
+
+// a snapshot's step scalars are usable by this cache (same policy and
+// geometry, values in range)
+bool snapshot_fits(const qkv_cache *c, const Snapshot &sn) {
+  const long long *v = sn.v;
+  if (v[SNAP_TAG] != SNAP_TAG_VALUE || v[SNAP_POLICY] != c->cfg.policy || v[SNAP_BATCH] != c->cfg.batch ||
+      v[SNAP_HQ] != c->cfg.n_q_heads || v[SNAP_HKV] != c->cfg.n_kv_heads || v[SNAP_D] != c->cfg.head_dim ||
+      v[SNAP_WINDOW] != c->cfg.window || v[SNAP_MAXCTX] != c->cfg.max_ctx)
+    return false;
+  const long long N = v[SNAP_N];
+  if (N < 0 || N > c->cfg.max_ctx || v[SNAP_STEPS] < 0 || v[SNAP_ROUTES] < 0 || v[SNAP_SINCE_ROUTE] < 0) return false;
+  if (v[SNAP_LAST_EVENT] < 0 || v[SNAP_LAST_EVENT] > N) return false;
+  if (c->tok) {
+    const long long cap = c->cfg.policy == QKV_POLICY_H2O ? c->cfg.k_full : 0;
+    return v[SNAP_R] >= 0 && v[SNAP_R] <= N && v[SNAP_RANKED] >= 0 && v[SNAP_RANKED] <= cap;
+  }
+  const long long kfq = (long long)c->g.k_full + c->g.k_quant;
+  return v[SNAP_R] >= 1 && v[SNAP_R] <= c->g.U && v[SNAP_RANKED] >= 0 && v[SNAP_RANKED] <= kfq &&
+         v[SNAP_RANKED] <= c->g.U;
 }
 
 }  // namespace
@@ -361,7 +413,9 @@ int qkv_profile_read(qkv_cache *c, float *ms, int32_t n) {
 int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv_stream stream) {
   if (!c || !k || !v || n_tokens < 1) return QKV_EINVAL;
   if ((long long)c->N + n_tokens > c->cfg.max_ctx) return QKV_ECAPACITY;
-  int rc = c->tok ? hip_err(tok_launch_append(c->tg, c->ts, (const uint16_t *)k, (const uint16_t *)v, n_tokens,
+  int rc = settle(c, (hipStream_t)stream);
+  if (rc != QKV_OK) return rc;
+  rc = c->tok ? hip_err(tok_launch_append(c->tg, c->ts, (const uint16_t *)k, (const uint16_t *)v, n_tokens,
                                               c->N, (hipStream_t)stream))
                   : hip_err(launch_append(c->g, c->st, (const uint16_t *)k, (const uint16_t *)v, n_tokens, c->N,
                                           (hipStream_t)stream));
@@ -373,6 +427,7 @@ int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv
 int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, qkv_stream stream) {
   if (!c || !q || !out) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
+  if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->ev && c->ev_next < c->ev_n && c->ev_calls++ % c->ev_stride == 0) {
     e0 = c->ev[2 * c->ev_next];
@@ -404,6 +459,7 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
   if (n_queries > c->N) return QKV_EINVAL;
   // a scored position must not be older than a kept ranked token (it would see it)
   if (c->n_cmp > 0 && c->N - n_queries < c->r_tok) return QKV_ESTATE;
+  if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
   const TokGeom &g = c->tg;
   const size_t row = (size_t)g.Hq * g.d;
   for (int i = 0; i < n_queries; ++i) {
@@ -419,6 +475,7 @@ int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream
 int qkv_route(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
   if (c->N < 1) return QKV_ESTATE;
+  if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
   if (c->tok && c->tacc_dirty) {
     // masses accumulated in list order reach the per-token scores first
     const TokStep ts = {c->N, c->r_tok, c->n_cmp};
@@ -513,17 +570,21 @@ int qkv_quantize_status(qkv_stream stream) {
 int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligible, int32_t n,
                    const int32_t *tier_counts, int32_t n_tiers, uint8_t *tier_out, qkv_stream stream) {
   if (!score || !pos || !eligible || !tier_counts || !tier_out) return QKV_EINVAL;
-  if (n < 1 || n > 4096 || n_tiers < 0 || n_tiers > 254) return QKV_EINVAL;
+  if (n < 1 || n > SORT_MAX || n_tiers < 0 || n_tiers > 254) return QKV_EINVAL;
   return hip_err(launch_rank_tiers(score, pos, eligible, n, tier_counts, n_tiers, tier_out, (hipStream_t)stream));
 }
 
 size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
   if (!c) return 0;
+  if (what == QKV_EXPORT_STATE) return sizeof(Snapshot);
   if (c->tok) {
     const size_t n = (size_t)c->tg.B * c->tg.Hkv * c->tg.T;
     switch (what) {
       case QKV_EXPORT_TIERS: return n;
       case QKV_EXPORT_SCORES: return n * 4;
+      case QKV_EXPORT_KEYS:
+      case QKV_EXPORT_VALUES: return n * c->tg.d * 2;
+      case QKV_EXPORT_ROUTED: return (size_t)c->tg.B * c->tg.Hkv * (4 + 4 * (size_t)tok_list_cap(c->tg)) * 4;
       case QKV_EXPORT_KCODES:
       case QKV_EXPORT_VCODES: return c->tg.policy == QKV_POLICY_HQEKV ? n * (c->tg.d / 2) : 0;
       case QKV_EXPORT_KPARAMS:
@@ -543,14 +604,22 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
     case QKV_EXPORT_VPARAMS: return BU * g.Hkv * (size_t)g.window * (g.d / g.group) * 2 * 2;
     case QKV_EXPORT_KEYS:
     case QKV_EXPORT_VALUES: return (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2;
+    case QKV_EXPORT_ROUTED: return BU * 4;
     default: return 0;
   }
 }
 
-int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_stream stream) {
-  if (!c || !dst) return QKV_EINVAL;
-  const size_t need = qkv_export_bytes(c, what);
+int qkv_export(const qkv_cache *cc, int32_t what, void *dst, size_t bytes, qkv_stream stream) {
+  if (!cc || !dst) return QKV_EINVAL;
+  const size_t need = qkv_export_bytes(cc, what);
   if (need == 0 || bytes != need) return QKV_EINVAL;
+  // an export reads derived structures only once they are rebuilt (the
+  // handle is const to the caller; its pending rebuild is not caller state)
+  qkv_cache *c = const_cast<qkv_cache *>(cc);
+  if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
+  if (what == QKV_EXPORT_STATE) return hip_err(launch_write_snapshot(make_snapshot(c), dst, (hipStream_t)stream));
+  if (c->tok && what == QKV_EXPORT_ROUTED)
+    return hip_err(tok_launch_export_routed(c->tg, c->ts, c->n_cmp, dst, (hipStream_t)stream));
   if (c->tok) {
     if (what == QKV_EXPORT_SCORES && c->tacc_dirty) {
       const TokStep ts = {c->N, c->r_tok, c->n_cmp};
@@ -563,6 +632,40 @@ int qkv_export(const qkv_cache *c, int32_t what, void *dst, size_t bytes, qkv_st
   return hip_err(launch_export(c->g, c->st, step_info(c), what, dst, (hipStream_t)stream));
 }
 
+int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_stream stream) {
+  if (!c || !src) return QKV_EINVAL;
+  const size_t need = qkv_export_bytes(c, what);
+  if (need == 0 || bytes != need) return QKV_EINVAL;
+  const hipStream_t s = (hipStream_t)stream;
+  if (what == QKV_EXPORT_STATE) {
+    Snapshot sn;
+    if (hipMemcpyAsync(&sn, src, sizeof sn, hipMemcpyDeviceToHost, s) != hipSuccess) return QKV_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;
+    if (!snapshot_fits(c, sn)) return QKV_EINVAL;
+    c->N = (int)sn.v[SNAP_N];
+    c->steps = sn.v[SNAP_STEPS];
+    c->routes = sn.v[SNAP_ROUTES];
+    c->steps_since_route = (int)sn.v[SNAP_SINCE_ROUTE];
+    c->last_event_N = (int)sn.v[SNAP_LAST_EVENT];
+    if (c->tok) {
+      c->r_tok = (int)sn.v[SNAP_R];
+      c->n_cmp = (int)sn.v[SNAP_RANKED];
+      c->tacc_dirty = false;   // the imported scores hold every pending mass
+    } else {
+      c->r0 = (int)sn.v[SNAP_R];
+      c->routed = (int)sn.v[SNAP_RANKED];
+    }
+    c->rebuild_pending = true;
+    return QKV_OK;
+  }
+  const int rc = c->tok ? hip_err(tok_launch_import(c->tg, c->ts, what, src, s))
+                        : hip_err(launch_import(c->g, c->st, what, src, s));
+  if (rc != QKV_OK) return rc;
+  if (c->tok && what == QKV_EXPORT_SCORES) c->tacc_dirty = false;
+  c->rebuild_pending = true;
+  return QKV_OK;
+}
+
 int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
   if (!c || !value) return QKV_EINVAL;
   switch (what) {
@@ -572,6 +675,7 @@ int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
     case QKV_INFO_ROUTES: *value = c->routes; return QKV_OK;
     case QKV_INFO_SPLITS: *value = c->tok ? c->tg.n_splits : c->g.n_splits; return QKV_OK;
     case QKV_INFO_WORKSPACE: *value = (int64_t)c->ws_bytes; return QKV_OK;
+    case QKV_INFO_LIST_CAPACITY: *value = c->tok ? tok_list_cap(c->tg) : 0; return QKV_OK;
     default: return QKV_EINVAL;
   }
 }

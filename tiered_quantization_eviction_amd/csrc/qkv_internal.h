@@ -66,8 +66,6 @@ struct State {
   float *part_o;     // [B][Hkv][S][G][d]
   float *part_ml;    // [B][Hkv][S][G][2]  (max in log2 units, sum)
   float *mass_part;  // [B][Hkv][U+1][G][2] (partial mass, reference max)
-  int32_t *tail_next;   // [B][Hkv] next full-precision tail chunk of the attention launch
-                        // in flight; back to zero once the merge has run
   float *slist;         // [B][U] scores of the live entries in list order (sink, ranked,
                         // recent): the per-step merge updates these; score[] is brought up
                         // to date from them by each routing event and before an export
@@ -237,7 +235,21 @@ __host__ __device__ inline size_t tok_cpage_offset(const TokGeom &g, int b, int 
   return (((size_t)b * g.Hkv + h) * g.NCT + tile) * (size_t)(2 * TS * g.d);
 }
 
+// Step scalars and geometry of a session snapshot (QKV_EXPORT_STATE): written
+// to device memory by a kernel from its arguments, read back by an import.
+struct Snapshot {
+  long long v[16];
+};
+enum : int {
+  SNAP_TAG = 0, SNAP_POLICY, SNAP_BATCH, SNAP_HQ, SNAP_HKV, SNAP_D, SNAP_WINDOW, SNAP_MAXCTX,
+  SNAP_N, SNAP_R, SNAP_RANKED, SNAP_STEPS, SNAP_ROUTES, SNAP_SINCE_ROUTE, SNAP_LAST_EVENT, SNAP_SPARE
+};
+constexpr long long SNAP_TAG_VALUE = 0x514B5631;   // "QKV1"
+
 // ---- launchers (defined in qkv_kernels.hip) ----
+hipError_t launch_write_snapshot(const Snapshot &snap, void *dst, hipStream_t s);
+hipError_t launch_import(const Geom &g, const State &st, int what, const void *src, hipStream_t s);
+hipError_t launch_rebuild(const Geom &g, const State &st, const StepInfo &si, hipStream_t s);
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
                          int pos0, hipStream_t s);
@@ -267,5 +279,10 @@ hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, voi
 hipError_t tok_launch_flush(const TokGeom &g, const TokState &st, const TokStep &ts, hipStream_t s);
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
                            hipStream_t s);
+hipError_t tok_launch_import(const TokGeom &g, const TokState &st, int what, const void *src, hipStream_t s);
+hipError_t tok_launch_rebuild(const TokGeom &g, const TokState &st, int n_cmp, hipStream_t s);
+hipError_t tok_launch_export_routed(const TokGeom &g, const TokState &st, int n_cmp, void *dst, hipStream_t s);
+// entries per list of a token-mode ROUTED snapshot
+__host__ __device__ inline int tok_list_cap(const TokGeom &g) { return g.NCT * TS; }
 
 }  // namespace qkv

@@ -652,12 +652,6 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   }
 }
 
-// Tail of the attention work taken dynamically when every entry is full
-// precision: 1/TAIL_DIV of the entries, in about TAIL_CHUNKS chunks (at least
-// 8 entries each) per (sequence, KV head)
-constexpr int TAIL_DIV = 3;
-constexpr int TAIL_CHUNKS = 32;
-
 // Waves per attention workgroup: one 8-wave workgroup per compute unit
 // holds two waves on each SIMD.
 constexpr int QW = 8;
@@ -700,17 +694,11 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const EntryList L = make_list(g, st, si, b);
   const int A = L.s0 + L.nF, AQ = A + L.nQ, E = L.count();
   const int nB = A + (E - AQ);
-  // With no quantized windows (every entry streams in full precision), all
-  // but 1/TAIL_DIV of the entries are dealt out statically; the rest is a
-  // tail of chunks that the waves of this (sequence, KV head) take in turn
-  // once their static share is done, so that waves which stream slower finish
-  // with less work (wave times differ by tens of percent within a launch).
-  // With quantized windows the static deal stays whole: there, the pairing
-  // of streaming and arithmetic work on each SIMD matters more.
-  const int nBs = L.nQ == 0 ? nB - nB / TAIL_DIV : nB, nQs = L.nQ;
+  // The deal is static and fixed by (split, wave) alone, so every partial
+  // sum, and with it every output and mass bit, is the same from run to run.
   const int NS = QW * S, gi = split * QW + wave;
-  const int vb0 = (int)((long long)nBs * gi / NS), vb1 = (int)((long long)nBs * (gi + 1) / NS);
-  const int q0 = A + (int)((long long)nQs * gi / NS), q1 = A + (int)((long long)nQs * (gi + 1) / NS);
+  const int vb0 = (int)((long long)nB * gi / NS), vb1 = (int)((long long)nB * (gi + 1) / NS);
+  const int q0 = A + (int)((long long)L.nQ * gi / NS), q1 = A + (int)((long long)L.nQ * (gi + 1) / NS);
 
   WaveState<D> ws;
 #pragma unroll
@@ -750,9 +738,6 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // workgroup's waves are dealt to the SIMDs round-robin (w, w+4) or in
   // pairs (2k, 2k+1): one streams full-precision tiles while the other
   // unpacks quantized ones.
-  // tail chunks of full-precision virtual entries [nBs, nB)
-  int32_t *tail = st.tail_next + (b * g.Hkv + h);
-  const int fch = max(8, (nB - nBs + TAIL_CHUNKS - 1) / TAIL_CHUNKS);
   const int f0 = min(vb0, A), f1 = min(vb1, A);
   const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
   if (((wave & 1) ^ (wave >> 2)) & 1) {
@@ -763,18 +748,6 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
     run_quant<D, GP>(ws, c, q0, q1);
-  }
-  // full-precision tail, chunk by chunk until taken (launches without one
-  // issue no atomic)
-  for (; nBs < nB;) {
-    int k = 0;
-    if (lane == 0) k = atomicAdd(tail, 1);
-    k = __builtin_amdgcn_readfirstlane(k);
-    const int lo = nBs + k * fch;
-    if (lo >= nB) break;
-    const int hi = min(lo + fch, nB);
-    run_full<D>(ws, c, min(lo, A), min(hi, A));
-    run_full<D>(ws, c, AQ + max(lo - A, 0), AQ + max(hi - A, 0));
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -865,7 +838,6 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     // outputs of one (sequence, KV head): each thread folds the split
     // partials of its outputs with the LSE rule on its own
     const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
-    if (threadIdx.x == 0) st.tail_next[blockIdx.x] = 0;   // for the next launch
     const float2 *ml = (const float2 *)st.part_ml + (size_t)(b * g.Hkv + h) * S * G;
     const float *po = st.part_o + (size_t)(b * g.Hkv + h) * S * G * D;
     for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
@@ -1626,6 +1598,8 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
 }
 
 hipError_t launch_export(const Geom &g, const State &st, const StepInfo &si, int what, void *dst, hipStream_t s) {
+  if (what == QKV_EXPORT_ROUTED)
+    return hipMemcpyAsync(dst, st.routed, (size_t)g.B * g.U * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
   if (what == QKV_EXPORT_TIERS)
     return hipMemcpyAsync(dst, st.tier, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
   if (what == QKV_EXPORT_SCORES) {
@@ -1637,6 +1611,121 @@ hipError_t launch_export(const Geom &g, const State &st, const StepInfo &si, int
   if (what == QKV_EXPORT_LEDGER)
     return hipMemcpyAsync(dst, st.has_ledger, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
   hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, s, g, st, what, dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// session snapshot: step scalars, canonical -> internal layouts, derived lists
+// ---------------------------------------------------------------------------
+
+__global__ void write_snapshot_kernel(Snapshot snap, long long *dst) {
+  const int i = threadIdx.x;
+  if (i < 16) dst[i] = snap.v[i];
+}
+
+hipError_t launch_write_snapshot(const Snapshot &snap, void *dst, hipStream_t s) {
+  hipLaunchKernelGGL(write_snapshot_kernel, dim3(1), dim3(64), 0, s, snap, (long long *)dst);
+  return hipGetLastError();
+}
+
+// The inverse of export_kernel: every internal element is written by one
+// thread from the canonical copy (a code dword gathers its 16 slots, so no
+// two threads write the same word).
+__global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what, const void *__restrict__ src) {
+  const int W = g.window, D = g.d, nkd = D / 64;
+  const size_t n_units = (size_t)g.B * g.U * g.Hkv;   // (b, u, h) blocks, in canonical order
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) {
+    const bool keys = what == QKV_EXPORT_KCODES;
+    const int per_unit = g.tpw * 64 * nkd;   // this kind's code dwords per block
+    const int cbytes = W * D / 4;            // canonical bytes per block
+    for (size_t it = i0; it < n_units * per_unit; it += stride) {
+      const size_t blk = it / per_unit;
+      const int r = (int)(it % per_unit);
+      const int tile = r / (64 * nkd), l = (r % (64 * nkd)) / nkd, j = r % nkd;
+      const uint8_t *cs = (const uint8_t *)src + blk * cbytes;
+      uint32_t word = 0u;
+      for (int p = 0; p < 16; ++p) {
+        const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
+        const int c = keys ? (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi : (4 * j + m) * 16 + l % 16;
+        const int tt = tile * TS + (keys ? l % 16 : 4 * (l / 16) + 2 * par + hi);
+        if (tt >= W) continue;
+        const int e = keys ? c * W + tt : tt * D + c;
+        word |= (uint32_t)((cs[e >> 2] >> (2 * (e & 3))) & 3) << (2 * p);
+      }
+      uint32_t *tc = (uint32_t *)(st.ledger + blk * g.ledger_unit_bytes + g.kparam_bytes +
+                                  (size_t)tile * g.tile_block_bytes);
+      tc[l * 2 * nkd + (keys ? 0 : nkd) + j] = word;
+    }
+  } else if (what == QKV_EXPORT_KPARAMS) {
+    const uint16_t *ps = (const uint16_t *)src;   // [blk][D][1][2]
+    for (size_t it = i0; it < n_units * D * 2; it += stride) {
+      const size_t blk = it / (D * 2);
+      const int k = (int)(it % (D * 2)), c = k / 2, which = k % 2;
+      ((uint16_t *)(st.ledger + blk * g.ledger_unit_bytes))[which * D + c] = ps[it];
+    }
+  } else if (what == QKV_EXPORT_VPARAMS) {
+    const uint16_t *ps = (const uint16_t *)src;   // [blk][W][D/32][2]
+    const int per = W * (D / 32) * 2;
+    for (size_t it = i0; it < n_units * per; it += stride) {
+      const size_t blk = it / per;
+      const int k = (int)(it % per), which = k % 2, grp = (k / 2) % (D / 32), t = k / 2 / (D / 32);
+      uint16_t *vp = (uint16_t *)(st.ledger + blk * g.ledger_unit_bytes + g.kparam_bytes +
+                                  (size_t)(t / TS) * g.tile_block_bytes + g.tile_kcode_bytes + g.tile_vcode_bytes);
+      vp[vparam_index(g, t % TS, grp, which)] = ps[it];
+    }
+  } else {   // KEYS / VALUES: [B][Hkv][max_ctx][D]
+    const uint16_t *xs = (const uint16_t *)src;
+    const size_t total = (size_t)g.B * g.Hkv * g.max_ctx * D;
+    for (size_t it = i0; it < total; it += stride) {
+      const int c = (int)(it % D);
+      const int pos = (int)((it / D) % g.max_ctx);
+      const int h = (int)((it / ((size_t)D * g.max_ctx)) % g.Hkv);
+      const int b = (int)(it / ((size_t)D * g.max_ctx * g.Hkv));
+      const int u = unit_of(g, pos);
+      const int slot = pos - unit_start(g, u);
+      uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)(slot / TS) * 2 * TS * D;
+      const int t = slot % TS;
+      if (what == QKV_EXPORT_KEYS)
+        kt[k_tile_index(t, c)] = xs[it];
+      else
+        kt[TS * D + v_tile_index(t, c)] = xs[it];
+    }
+  }
+}
+
+hipError_t launch_import(const Geom &g, const State &st, int what, const void *src, hipStream_t s) {
+  const size_t BU = (size_t)g.B * g.U;
+  switch (what) {
+    case QKV_EXPORT_TIERS: return hipMemcpyAsync(st.tier, src, BU, hipMemcpyDeviceToDevice, s);
+    case QKV_EXPORT_LEDGER: return hipMemcpyAsync(st.has_ledger, src, BU, hipMemcpyDeviceToDevice, s);
+    case QKV_EXPORT_SCORES: return hipMemcpyAsync(st.score, src, BU * sizeof(float), hipMemcpyDeviceToDevice, s);
+    case QKV_EXPORT_ROUTED: return hipMemcpyAsync(st.routed, src, BU * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    default: break;
+  }
+  hipLaunchKernelGGL(import_kernel, dim3(2048), dim3(256), 0, s, g, st, what, src);
+  return hipGetLastError();
+}
+
+// After an import: the per-sequence full/quantized split of the ranked list
+// and the list-order scores (sink, ranked, recent) from the per-unit scores;
+// slots past the list hold 0, as a routing event leaves them.
+__global__ __launch_bounds__(256) void rebuild_kernel(Geom g, State st, StepInfo si) {
+  const int b = blockIdx.y;
+  const EntryList L = make_list(g, st, si, b);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    st.routed_nf[b] = L.nF;
+    st.routed_nq[b] = L.nQ;
+  }
+  const int E = L.count();
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < g.U; e += gridDim.x * blockDim.x)
+    st.slist[(size_t)b * g.U + e] = e < E ? st.score[(size_t)b * g.U + entry_unit(L, st.routed + (size_t)b * g.U, e)]
+                                          : 0.0f;
+}
+
+hipError_t launch_rebuild(const Geom &g, const State &st, const StepInfo &si, hipStream_t s) {
+  hipLaunchKernelGGL(rebuild_kernel, dim3((g.U + 255) / 256, g.B), dim3(256), 0, s, g, st, si);
   return hipGetLastError();
 }
 

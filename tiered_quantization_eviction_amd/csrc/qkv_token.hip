@@ -1960,6 +1960,20 @@ hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig
 
 __global__ __launch_bounds__(256) void tok_export_kernel(TokGeom g, TokState st, int what, void *dst) {
   const size_t n = (size_t)g.B * g.Hkv * g.T;
+  if (what == QKV_EXPORT_KEYS || what == QKV_EXPORT_VALUES) {
+    // the appended originals from the position pages: [B][Hkv][T][d]
+    const int D = g.d;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * D; i += (size_t)gridDim.x * blockDim.x) {
+      const int c = (int)(i % D);
+      const size_t row = i / D;                       // bh * T + pos
+      const int pos = (int)(row % g.T);
+      const size_t bh = row / g.T;
+      const uint16_t *kt = st.pages + tok_page_offset(g, (int)(bh / g.Hkv), (int)(bh % g.Hkv), pos / TS);
+      ((uint16_t *)dst)[i] = what == QKV_EXPORT_KEYS ? kt[k_tile_index(pos % TS, c)]
+                                                     : kt[TS * D + v_tile_index(pos % TS, c)];
+    }
+    return;
+  }
   if (what == QKV_EXPORT_TIERS || what == QKV_EXPORT_SCORES) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
       if (what == QKV_EXPORT_TIERS)
@@ -1983,6 +1997,156 @@ hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, voi
   int grid = (int)((n + 255) / 256);
   grid = grid > 4096 ? 4096 : (grid < 1 ? 1 : grid);
   hipLaunchKernelGGL(tok_export_kernel, dim3(grid), dim3(256), 0, s, g, st, what, dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// session snapshot: ranked lists, canonical -> internal layouts, compact tiles
+// ---------------------------------------------------------------------------
+
+// ROUTED [B][Hkv][4 + 4 L]: counts of the full-precision, INT4, INT2, INT1
+// lists, then the lists (L entries each; -1 where a policy has no list)
+__global__ __launch_bounds__(256) void tok_routed_kernel(TokGeom g, TokState st, int n_cmp, int32_t *dst,
+                                                         int to_state) {
+  const int bh = blockIdx.x;
+  const int Lc = tok_list_cap(g);
+  int32_t *row = dst + (size_t)bh * (4 + 4 * Lc);
+  const bool hq = g.policy == QKV_POLICY_HQEKV;
+  if (!to_state) {
+    for (int i = threadIdx.x; i < 4 + 4 * Lc; i += blockDim.x) {
+      int32_t v = -1;
+      if (i < 4) {
+        v = hq ? st.cnt[bh * 4 + i] : (i == 0 ? n_cmp : 0);
+      } else {
+        const int k = (i - 4) / Lc, e = (i - 4) % Lc;
+        if (k == 0)
+          v = st.cpos[(size_t)bh * Lc + e];
+        else if (hq)
+          v = st.qpos[k - 1][(size_t)bh * Lc + e];
+      }
+      row[i] = v;
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < 4 + 4 * Lc; i += blockDim.x) {
+    const int32_t v = row[i];
+    if (i < 4) {
+      if (hq) st.cnt[bh * 4 + i] = v;
+    } else {
+      const int k = (i - 4) / Lc, e = (i - 4) % Lc;
+      if (k == 0)
+        st.cpos[(size_t)bh * Lc + e] = v;
+      else if (hq)
+        st.qpos[k - 1][(size_t)bh * Lc + e] = v;
+    }
+  }
+}
+
+hipError_t tok_launch_export_routed(const TokGeom &g, const TokState &st, int n_cmp, void *dst, hipStream_t s) {
+  hipLaunchKernelGGL(tok_routed_kernel, dim3(g.B * g.Hkv), dim3(256), 0, s, g, st, n_cmp, (int32_t *)dst, 0);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void tok_import_kernel(TokGeom g, TokState st, int what, const void *__restrict__ src) {
+  const size_t n = (size_t)g.B * g.Hkv * g.T;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (what == QKV_EXPORT_KEYS || what == QKV_EXPORT_VALUES) {
+    const int D = g.d;
+    const uint16_t *xs = (const uint16_t *)src;
+    for (size_t i = i0; i < n * D; i += stride) {
+      const int c = (int)(i % D);
+      const size_t row = i / D;
+      const int pos = (int)(row % g.T);
+      const size_t bh = row / g.T;
+      uint16_t *kt = st.pages + tok_page_offset(g, (int)(bh / g.Hkv), (int)(bh % g.Hkv), pos / TS);
+      if (what == QKV_EXPORT_KEYS)
+        kt[k_tile_index(pos % TS, c)] = xs[i];
+      else
+        kt[TS * D + v_tile_index(pos % TS, c)] = xs[i];
+    }
+    return;
+  }
+  // per-token records: KCODES / VCODES [.., d/2] bytes, KPARAMS / VPARAMS [.., d/32, 2] fp16
+  const int off = what == QKV_EXPORT_KCODES ? 0 : what == QKV_EXPORT_VCODES ? g.d / 2
+                : what == QKV_EXPORT_KPARAMS ? g.d : g.d + (g.d / 32) * 4;
+  const int len = (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) ? g.d / 2 : (g.d / 32) * 4;
+  for (size_t i = i0; i < n * len; i += stride)
+    st.qrec[(i / len) * g.rec_bytes + off + (i % len)] = ((const uint8_t *)src)[i];
+}
+
+// value range of every position's original value row (as the append kernel
+// forms it: max - min over the row, exact in any order)
+__global__ __launch_bounds__(256) void tok_vrange_kernel(TokGeom g, TokState st) {
+  const size_t n = (size_t)g.B * g.Hkv * g.T;
+  const int D = g.d;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(i % g.T);
+    const size_t bh = i / g.T;
+    const uint16_t *vt = st.pages + tok_page_offset(g, (int)(bh / g.Hkv), (int)(bh % g.Hkv), pos / TS) + TS * D;
+    float mn = bf16_to_f32(vt[v_tile_index(pos % TS, 0)]), mx = mn;
+    for (int c = 1; c < D; ++c) {
+      const float x = bf16_to_f32(vt[v_tile_index(pos % TS, c)]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    st.vrange[i] = mx - mn;
+  }
+}
+
+hipError_t tok_launch_import(const TokGeom &g, const TokState &st, int what, const void *src, hipStream_t s) {
+  const size_t n = (size_t)g.B * g.Hkv * g.T;
+  switch (what) {
+    case QKV_EXPORT_TIERS: return hipMemcpyAsync(st.tier, src, n, hipMemcpyDeviceToDevice, s);
+    case QKV_EXPORT_SCORES: {
+      // the imported scores already hold every pending mass
+      hipError_t e = hipMemcpyAsync(st.score, src, n * sizeof(float), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return e;
+      return launch_clear(st.tacc, (size_t)g.B * g.Hkv * g.TILES * TS * sizeof(float), s);
+    }
+    case QKV_EXPORT_ROUTED:
+      hipLaunchKernelGGL(tok_routed_kernel, dim3(g.B * g.Hkv), dim3(256), 0, s, g, st, 0,
+                         (int32_t *)const_cast<void *>(src), 1);
+      return hipGetLastError();
+    default: break;
+  }
+  hipLaunchKernelGGL(tok_import_kernel, dim3(2048), dim3(256), 0, s, g, st, what, src);
+  return hipGetLastError();
+}
+
+// H2O: the kept heavy hitters of each (sequence, KV head) gathered, in list
+// order, into the compact tiles
+__global__ __launch_bounds__(256) void tok_regather_kernel(TokGeom g, TokState st, int n_cmp) {
+  const int bh = blockIdx.y;
+  const int b = bh / g.Hkv, h = bh % g.Hkv;
+  const int chunks = g.d / 8;
+  const int32_t *cpos = st.cpos + (size_t)bh * g.NCT * TS;
+  const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
+  uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < n_cmp * chunks; it += gridDim.x * blockDim.x)
+    tok_copy_token(g, pages_bh, cpages_bh, cpos[it / chunks], it / chunks, (it % chunks) * 8);
+}
+
+hipError_t tok_launch_rebuild(const TokGeom &g, const TokState &st, int n_cmp, hipStream_t s) {
+  if (g.policy == QKV_POLICY_HQEKV) {
+    const size_t n = (size_t)g.B * g.Hkv * g.T;
+    int grid = (int)((n + 255) / 256);
+    grid = grid > 4096 ? 4096 : (grid < 1 ? 1 : grid);
+    hipLaunchKernelGGL(tok_vrange_kernel, dim3(grid), dim3(256), 0, s, g, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 ggrid(64, g.B * g.Hkv);
+    if (g.d == 128)
+      hipLaunchKernelGGL(hq_gather_kernel<128>, ggrid, dim3(256), 0, s, g, st);
+    else
+      hipLaunchKernelGGL(hq_gather_kernel<64>, ggrid, dim3(256), 0, s, g, st);
+    return hipGetLastError();
+  }
+  if (n_cmp > 0) {
+    const int chunks = g.d / 8;
+    const dim3 grid((n_cmp * chunks + 255) / 256, g.B * g.Hkv);
+    hipLaunchKernelGGL(tok_regather_kernel, grid, dim3(256), 0, s, g, st, n_cmp);
+  }
   return hipGetLastError();
 }
 
