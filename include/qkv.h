@@ -318,8 +318,12 @@ size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);
  * The order is free.  Structures derived from these (list-order scores, the
  * compact tiles of the ranked lists, value ranges) are rebuilt on `stream`
  * before the next append, attention, prompt scoring, routing or export, so a
- * restored cache continues exactly as the exported one does (no pending
- * masses are carried: SCORES already holds them).  STATE is read back to the
+ * restored cache continues exactly as the exported one does.  No pending
+ * masses are carried: with a routing period above 1 the token policies keep
+ * each step's masses in list order until the next routing call, and an
+ * export of SCORES adds them into the scores first (the exported cache then
+ * continues from those scores too; a cache never exported adds a period's
+ * masses at once, which can differ from it in the last float32 bits).  STATE is read back to the
  * host, so importing it waits for `stream`.  Errors: QKV_EINVAL for a kind
  * the policy does not hold, a wrong size, or a STATE whose format tag,
  * policy or geometry differs from the cache's or whose step scalars are out

@@ -87,7 +87,23 @@ def _same_state(torch, a, b, tag):
         assert torch.equal(t, u), f"{tag}: exported {what} differs"
 
 
-def _snapshot_run(cfg, torch, cut, label, oracle_seq=None):
+def _same_state_within(torch, a, b, tag, rtol):
+    """Every kind equal, scores within rtol (exporting the scores of a cache
+    with masses pending in list order adds them in early, so the last bits of
+    its scores can differ from a cache that adds them at its routing call)."""
+    for what, t in a.cache.snapshot().items():
+        u = b.cache.export(what)
+        torch.cuda.synchronize()
+        if what == "scores":
+            x, y = t.view(torch.float32), u.view(torch.float32)
+            assert torch.allclose(x, y, rtol=rtol, atol=1e-12), f"{tag}: scores differ beyond {rtol}"
+            continue
+        if what == "state":
+            continue
+        assert torch.equal(t, u), f"{tag}: exported {what} differs"
+
+
+def _snapshot_run(cfg, torch, cut, label, oracle_seq=None, pending=False):
     wl = W.Workload(cfg)
     K, V, Q = gpu_inputs(cfg, wl)
     QP = _prompt_queries(cfg)
@@ -121,7 +137,10 @@ def _snapshot_run(cfg, torch, cut, label, oracle_seq=None):
         B.step(s)
         C.step(s)
         assert torch.equal(A.out, B.out), f"[{label}] step {s}: restored cache differs from the exported one"
-        assert torch.equal(A.out, C.out), f"[{label}] step {s}: exported cache differs from the uninterrupted one"
+        if pending:
+            assert torch.allclose(A.out, C.out, rtol=0, atol=1e-5), f"[{label}] step {s}: vs the uninterrupted run"
+        else:
+            assert torch.equal(A.out, C.out), f"[{label}] step {s}: exported cache differs from the uninterrupted one"
         if seq is not None:
             o, _ = seq.step(s, qs[s])
             err = float(np.abs(B.out[oracle_seq].cpu().numpy() - o).max())
@@ -132,7 +151,10 @@ def _snapshot_run(cfg, torch, cut, label, oracle_seq=None):
                 tiers = B.cache.export("tiers").cpu().numpy().reshape(cfg.batch, -1)
                 np.testing.assert_array_equal(tiers[oracle_seq], seq.tier, err_msg=f"[{label}] tiers after step {s}")
     _same_state(torch, A, B, f"[{label}] at the end")
-    _same_state(torch, A, C, f"[{label}] at the end (uninterrupted)")
+    if pending:
+        _same_state_within(torch, A, C, f"[{label}] at the end (uninterrupted)", 1e-6)
+    else:
+        _same_state(torch, A, C, f"[{label}] at the end (uninterrupted)")
     log(f"[{label}] restored run bit-identical over {cfg.steps - cut} steps; oracle worst {worst:.2e}")
     return seq
 
@@ -159,11 +181,12 @@ def test_snapshot_restore_h2o(torch_cuda):
 
 @pytest.mark.parametrize("cut", [64, 90])
 def test_snapshot_restore_hqekv(torch_cuda, cut):
-    """Right after an assignment event, and in the middle of a period (the
-    masses pending in list order are folded into the exported scores, in the
-    exported cache too)."""
+    """Right after an assignment event, and in the middle of a period: there
+    the masses pending in list order are folded into the exported scores (in
+    the exported cache too), so the restored cache is bit-identical to the
+    exported one and agrees with a never-exported run to float32 rounding."""
     cfg = W.HQEKV.replace(batch=2, n_q_heads=16, n_kv_heads=4, prefill=1024, steps=160)
-    _snapshot_run(cfg, torch_cuda, cut, f"hqekv-snapshot-{cut}")
+    _snapshot_run(cfg, torch_cuda, cut, f"hqekv-snapshot-{cut}", pending=cut % cfg.omega != 0)
 
 
 def test_import_rejects_wrong_size_and_other_state(torch_cuda):

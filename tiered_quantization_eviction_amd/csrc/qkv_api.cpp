@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <new>
+#include <vector>
 #include <string.h>
 
 #include "qkv_internal.h"
@@ -657,6 +658,28 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
     }
     c->rebuild_pending = true;
     return QKV_OK;
+  }
+  if (what == QKV_EXPORT_ROUTED) {
+    // list entries index pages and records: checked on the host before they
+    // reach a kernel (a restore is not on the decode path, so the read-back
+    // is affordable)
+    std::vector<int32_t> h(need / 4);
+    if (hipMemcpyAsync(h.data(), src, need, hipMemcpyDeviceToHost, s) != hipSuccess) return QKV_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;
+    if (c->tok) {
+      const int Lc = tok_list_cap(c->tg);
+      for (size_t r = 0; r < (size_t)c->tg.B * c->tg.Hkv; ++r) {
+        const int32_t *row = h.data() + r * (4 + 4 * (size_t)Lc);
+        for (int k = 0; k < 4; ++k) {
+          if (row[k] < 0 || row[k] > Lc) return QKV_EINVAL;
+          for (int e = 0; e < row[k]; ++e)
+            if (row[4 + k * Lc + e] < 0 || row[4 + k * Lc + e] >= c->tg.T) return QKV_EINVAL;
+        }
+      }
+    } else {
+      for (int32_t u : h)
+        if (u < 0 || u >= c->g.U) return QKV_EINVAL;
+    }
   }
   const int rc = c->tok ? hip_err(tok_launch_import(c->tg, c->ts, what, src, s))
                         : hip_err(launch_import(c->g, c->st, what, src, s));

@@ -1719,9 +1719,10 @@ __global__ __launch_bounds__(256) void rebuild_kernel(Geom g, State st, StepInfo
     st.routed_nq[b] = L.nQ;
   }
   const int E = L.count();
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < g.U; e += gridDim.x * blockDim.x)
-    st.slist[(size_t)b * g.U + e] = e < E ? st.score[(size_t)b * g.U + entry_unit(L, st.routed + (size_t)b * g.U, e)]
-                                          : 0.0f;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < g.U; e += gridDim.x * blockDim.x) {
+    const int u = min(max(entry_unit(L, st.routed + (size_t)b * g.U, e), 0), g.U - 1);
+    st.slist[(size_t)b * g.U + e] = e < E ? st.score[(size_t)b * g.U + u] : 0.0f;
+  }
 }
 
 hipError_t launch_rebuild(const Geom &g, const State &st, const StepInfo &si, hipStream_t s) {

@@ -2124,7 +2124,7 @@ __global__ __launch_bounds__(256) void tok_regather_kernel(TokGeom g, TokState s
   const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
   uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
   for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < n_cmp * chunks; it += gridDim.x * blockDim.x)
-    tok_copy_token(g, pages_bh, cpages_bh, cpos[it / chunks], it / chunks, (it % chunks) * 8);
+    tok_copy_token(g, pages_bh, cpages_bh, min(max(cpos[it / chunks], 0), g.T - 1), it / chunks, (it % chunks) * 8);
 }
 
 hipError_t tok_launch_rebuild(const TokGeom &g, const TokState &st, int n_cmp, hipStream_t s) {
