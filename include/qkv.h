@@ -130,6 +130,23 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
 int qkv_destroy(qkv_cache *cache);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * cache as qkv_create, with its workspace in a device array inside the
+ * library instead of caller memory.  Each GPU holds its own array of
+ * QKV_STATIC_WORKSPACE_BYTES bytes until the process ends; nothing is
+ * allocated by this call or by later calls on the cache.  The array is
+ * cleared for the new cache on `stream`.
+ * One such cache per device at a time: a second qkv_create_static on the same
+ * device replaces the first (both handles then name the new cache), and calls
+ * on caches that share a device's array race.  qkv_destroy releases the
+ * handle.  Errors: QKV_ECAPACITY when qkv_workspace_bytes(cfg) exceeds
+ * QKV_STATIC_WORKSPACE_BYTES; QKV_EINVAL as qkv_create.
+ */
+#define QKV_STATIC_WORKSPACE_BYTES (64u << 20)
+int qkv_create_static(const qkv_config *cfg, qkv_stream stream, qkv_cache **out);
+
+/*
  * Policies.
  * QKV_POLICY_QEVICT: window units (window = 8, 16 or 32 tokens), one score
  *   per (sequence, window) summed over all query heads, three tiers (full

@@ -62,6 +62,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_plan_capacities.argtypes = [ctypes.POINTER(QkvConfig), ctypes.c_double, ctypes.c_double, _i32,
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.qkv_create.argtypes = [ctypes.POINTER(QkvConfig), _vp, _sz, _vp, ctypes.POINTER(_vp)]
+        L.qkv_create_static.argtypes = [ctypes.POINTER(QkvConfig), _vp, ctypes.POINTER(_vp)]
         L.qkv_destroy.argtypes = [_vp]
         L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
         L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
@@ -168,20 +169,33 @@ def workspace_bytes(c: QkvConfig) -> int:
     return int(_lib().qkv_workspace_bytes(ctypes.byref(c)))
 
 
-class Cache:
-    """One layer's tiered KV cache for a batch of sequences (device state)."""
+STATIC_WORKSPACE_BYTES = 64 << 20
 
-    def __init__(self, c: QkvConfig, device="cuda", stream=None):
+
+class Cache:
+    """One layer's tiered KV cache for a batch of sequences (device state).
+
+    static=True: the cache lives in the library's own per-device array
+    (qkv_create_static, no allocation; one such cache per device)."""
+
+    def __init__(self, c: QkvConfig, device="cuda", stream=None, static: bool = False):
         import torch
         self.c = c
         n = workspace_bytes(c)
         if n == 0:
             raise QkvError(_lib().qkv_check_config(ctypes.byref(c)), "qkv config")
-        self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
-        base = self.workspace.data_ptr()
-        self._base = (base + 255) // 256 * 256
         h = _vp()
-        _check(_lib().qkv_create(ctypes.byref(c), self._base, n, _stream(stream), ctypes.byref(h)), "qkv_create")
+        if static:
+            self.workspace = None
+            self._device = torch.device(device if not isinstance(device, str) or ":" in device
+                                        else f"{device}:{torch.cuda.current_device()}")
+            _check(_lib().qkv_create_static(ctypes.byref(c), _stream(stream), ctypes.byref(h)), "qkv_create_static")
+        else:
+            self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
+            self._device = self.workspace.device
+            base = self.workspace.data_ptr()
+            self._base = (base + 255) // 256 * 256
+            _check(_lib().qkv_create(ctypes.byref(c), self._base, n, _stream(stream), ctypes.byref(h)), "qkv_create")
         self.h = h
 
     def close(self):
@@ -233,7 +247,7 @@ class Cache:
         nbytes = int(_lib().qkv_export_bytes(self.h, code))
         if nbytes == 0:
             raise QkvError(EINVAL, f"qkv_export({what})")
-        dst = torch.empty(nbytes, dtype=torch.uint8, device=self.workspace.device)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=self._device)
         _check(_lib().qkv_export(self.h, code, _ptr(dst), nbytes, _stream(stream)), "qkv_export")
         return dst
 

@@ -318,14 +318,15 @@ size_t qkv_workspace_bytes(const qkv_config *cfg) {
   return carve(g, nullptr, st);
 }
 
-int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream, qkv_cache **out) {
-  if (!out) return QKV_EINVAL;
-  *out = nullptr;
+}  // extern "C"
+
+// Set up handle `c` (cleared here) for a cache over `workspace`; nothing is
+// allocated.  Shared by qkv_create (a handle from the heap) and
+// qkv_create_static (a per-device handle of this file).
+static int create_into(qkv_cache *c, const qkv_config *cfg, void *workspace, size_t bytes, hipStream_t stream) {
   int rc = validate(cfg);
   if (rc != QKV_OK) return rc;
   if (!workspace || ((uintptr_t)workspace % ALIGN)) return QKV_EINVAL;
-  qkv_cache *c = new (std::nothrow) qkv_cache;
-  if (!c) return QKV_ECAPACITY;
   memset(c, 0, sizeof *c);
   c->cfg = *cfg;
   c->tok = cfg->policy == QKV_POLICY_H2O || cfg->policy == QKV_POLICY_HQEKV;
@@ -338,31 +339,16 @@ int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream 
     make_geom(cfg, c->g);
     bool fits = false;
     rc = hip_err(attend_lds_fits(c->g, &fits));
-    if (rc != QKV_OK || !fits) {
-      delete c;
-      return rc != QKV_OK ? rc : QKV_EINVAL;   // (d = 128 with eight heads per KV head needs 32-token windows)
-    }
+    if (rc != QKV_OK || !fits) return rc != QKV_OK ? rc : QKV_EINVAL;   // (d = 128, G = 8 needs 32-token windows)
     rc = hip_err(transitions_shape(c->g));
-    if (rc != QKV_OK) {
-      delete c;
-      return rc;
-    }
+    if (rc != QKV_OK) return rc;
     need = carve(c->g, (char *)workspace, c->st);
   }
-  if (bytes < need) {
-    delete c;
-    return QKV_ECAPACITY;
-  }
+  if (bytes < need) return QKV_ECAPACITY;
   c->ws = workspace;
   c->ws_bytes = need;
   c->r0 = 1;
-  rc = hip_err(launch_clear(workspace, need, (hipStream_t)stream));
-  if (rc != QKV_OK) {
-    delete c;
-    return rc;
-  }
-  *out = c;
-  return QKV_OK;
+  return hip_err(launch_clear(workspace, need, stream));
 }
 
 static void free_events(qkv_cache *c) {
@@ -374,8 +360,60 @@ static void free_events(qkv_cache *c) {
   c->ev_n = c->ev_next = 0;
 }
 
+namespace qkv {
+
+// one handle per device for the caches of qkv_create_static
+constexpr int STATIC_DEVICES = 64;
+static qkv_cache g_static_handle[STATIC_DEVICES];
+static bool g_static_live[STATIC_DEVICES];
+
+int create_static_over(const qkv_config *cfg, void *workspace, size_t bytes, int dev, hipStream_t stream,
+                       qkv_cache **out) {
+  if (!out) return QKV_EINVAL;
+  *out = nullptr;
+  if (dev < 0 || dev >= STATIC_DEVICES) return QKV_EINVAL;
+  qkv_cache *c = &g_static_handle[dev];
+  if (g_static_live[dev]) free_events(c);   // the device's previous static cache ends here
+  g_static_live[dev] = false;
+  const int rc = create_into(c, cfg, workspace, bytes, stream);
+  if (rc != QKV_OK) return rc;
+  g_static_live[dev] = true;
+  *out = c;
+  return QKV_OK;
+}
+
+static bool is_static_handle(const qkv_cache *c) {
+  return c >= g_static_handle && c < g_static_handle + STATIC_DEVICES;
+}
+
+}  // namespace qkv
+
+extern "C" {
+
+int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream, qkv_cache **out) {
+  if (!out) return QKV_EINVAL;
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc != QKV_OK) return rc;
+  qkv_cache *c = new (std::nothrow) qkv_cache;
+  if (!c) return QKV_ECAPACITY;
+  rc = create_into(c, cfg, workspace, bytes, (hipStream_t)stream);
+  if (rc != QKV_OK) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return QKV_OK;
+}
+
+
 int qkv_destroy(qkv_cache *cache) {
-  if (cache) free_events(cache);
+  if (!cache) return QKV_OK;
+  free_events(cache);
+  if (is_static_handle(cache)) {
+    g_static_live[cache - g_static_handle] = false;   // the handle stays with its device
+    return QKV_OK;
+  }
   delete cache;
   return QKV_OK;
 }
