@@ -59,8 +59,18 @@ def _two_tier(c3):
 def _diagnose(cfg, torch, K, V, Q, full_attn, label):
     """Step the GPU path; per step the FMM and tier shares of the full-cache
     attention under the tiers in force at that step; per event the sets."""
+    from oracle import qevict as oe
     run = QEvictGPURun(cfg, K, V, Q)
     B, P = cfg.batch, cfg.prefill
+    wl = W.Workload(cfg)
+    oseq, oq = {}, {}
+    for b in range(B):
+        k, v = wl.kv(b)
+        oseq[b] = oe.QEvictSequence(k, v, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
+                                    n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
+                                    bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads)
+        oseq[b].prefill(P)
+        oq[b] = wl.queries(b)
     pos = np.arange(cfg.total_tokens)
     unit_of_pos = np.where(pos < cfg.n_sink, 0, 1 + (pos - cfg.n_sink) // cfg.window)
     tiers = run.tiers()
@@ -77,9 +87,13 @@ def _diagnose(cfg, torch, K, V, Q, full_attn, label):
             fmm[b].append(dg.future_missed_mass(p, t_pos != EVICTED))
             sh = dg.tier_shares(p, t_pos, (SINK, RECENT, FULL, QUANT, EVICTED))
             shares[b].append((sh[SINK] + sh[RECENT], sh[FULL], sh[QUANT], sh[EVICTED]))
+        for b in range(B):
+            oseq[b].step(s, oq[b][s])
         if run.step(want_mass=False):
             tiers = run.tiers()
             for b in range(B):
+                # the tiers measured here are the oracle's, bit for bit
+                np.testing.assert_array_equal(tiers[b], oseq[b].tier, err_msg=f"[{label}] tiers after step {s}")
                 full_sets[b].append(set(np.flatnonzero(tiers[b] == FULL).tolist()))
                 kept_sets[b].append(set(np.flatnonzero((tiers[b] == FULL) | (tiers[b] == QUANT)).tolist()))
     first = cfg.omega               # steps after the first event

@@ -12,13 +12,19 @@ oracle follows step by step.
   event every 32 tokens: four events).
 
 Bars as in the small parity tests: outputs 2e-3, scores 1e-4 relative,
-tiers exact (codes and parameters are compared bit for bit in the small
-parity tests, which export them).
+tiers exact.  At this launch geometry each pack/promote workgroup walks
+dozens of (window, KV head) items, so the drift test also exports the ledger
+(codes and parameters) and the full-precision contents after the first
+routing event (the big pack) and after every event past the query switch
+(the promotions), and compares the sampled sequences' bytes with the
+oracle's; the HqeKV test compares the sampled groups' per-token records
+(codes, scales, zeros) after every event.
 """
 import numpy as np
 import pytest
 
 import workloads as W
+from oracle import codec as oc
 from oracle import hqekv as oq
 from oracle import qevict as oe
 
@@ -39,7 +45,7 @@ def torch_cuda():
     return torch
 
 
-def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True):
+def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True, bytes_at=()):
     log(f"[{label}] generating {cfg.batch} x {cfg.total_tokens} tokens")
     K, V, Q = gpu_inputs_parallel(cfg) if all_real else gpu_inputs_sampled(cfg, seq_ids)
     run = QEvictGPURun(cfg, K, V, Q)
@@ -73,6 +79,14 @@ def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True):
                 np.testing.assert_array_equal(tiers[b], seqs[b].tier,
                                               err_msg=f"tiers after event {routes} (step {s}) seq {b}, "
                                                       f"margins {seqs[b].events[-1].margins}")
+            if routes in bytes_at or (cfg.switch_step and bytes_at and s > cfg.switch_step):
+                from test_gpu_qevict import _check_content, _check_ledger
+                _check_ledger(run, seqs, cfg)
+                _check_content(run, seqs, cfg)
+                n_led = sum(len(sq.ledger) for sq in seqs.values())
+                n_prom = sum(len(sq.events[-1].promoted) for sq in seqs.values())
+                log(f"[{label}] event {routes}: ledgers ({n_led} windows) and contents bit-exact, "
+                    f"{n_prom} promoted at this event")
         if s % 16 == 15:
             log(f"[{label}] step {s + 1}: worst out err {worst:.2e}, routes {routes}")
     promoted = sum(len(e.promoted) for sq in seqs.values() for e in sq.events)
@@ -81,7 +95,7 @@ def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True):
 
 
 def test_drift_fullsize_sampled(torch_cuda):
-    seqs = _qevict_sampled(W.DRIFT.replace(steps=160), torch_cuda, [0, 11], "drift-full")
+    seqs = _qevict_sampled(W.DRIFT.replace(steps=160), torch_cuda, [0, 11], "drift-full", bytes_at=(1,))
     assert sum(len(e.promoted) for sq in seqs.values() for e in sq.events) > 0, \
         "no INT2 -> BF16 promotion after the query switch"
 
@@ -133,13 +147,37 @@ def test_hqekv_fullsize_sampled(torch_cuda, name):
         torch.cuda.synchronize()
         tiers = cache.export("tiers").cpu().numpy().reshape(B, Hkv, T)
         scores = cache.export("scores").cpu().numpy().view(np.float32).reshape(B, Hkv, T)
+        recs = {w: cache.export(w).cpu().numpy() for w in ("kcodes", "vcodes", "kparams", "vparams")}
+        kc, vc = recs["kcodes"].reshape(B, Hkv, T, d // 2), recs["vcodes"].reshape(B, Hkv, T, d // 2)
+        kp = recs["kparams"].view(np.uint16).reshape(B, Hkv, T, -1)
+        vp = recs["vparams"].view(np.uint16).reshape(B, Hkv, T, -1)
+        n_rec = 0
         for (b, g), grp in groups.items():
             got = np.vectorize(to_o.get)(tiers[b, g]).astype(np.uint8)
             np.testing.assert_array_equal(got, grp.tier, err_msg=f"{tag}: tiers (seq {b}, head {g})")
             live = np.flatnonzero((grp.tier != 255) & (grp.tier != oq.EVICT))
             np.testing.assert_allclose(scores[b, g, live], grp.score[live], rtol=SCORE_RTOL, atol=1e-7,
                                        err_msg=f"{tag}: scores (seq {b}, head {g})")
-        log(f"[{label}] {tag}: tiers and scores agree")
+            for t, rec in grp.codes.items():
+                lvl = rec[0]
+                bits = {oq.INT4: 4, oq.INT2: 2, oq.INT1: 1}[lvl]
+                nb = d * bits // 8
+                np.testing.assert_array_equal(kc[b, g, t, :nb], oc.pack_codes(rec[1].reshape(-1), bits),
+                                              err_msg=f"{tag}: K codes of token {t} (seq {b}, head {g})")
+                np.testing.assert_array_equal(vc[b, g, t, :nb], oc.pack_codes(rec[4].reshape(-1), bits),
+                                              err_msg=f"{tag}: V codes of token {t} (seq {b}, head {g})")
+                if bits == 1:
+                    kpar = np.array([rec[2], rec[3]], np.float16).view(np.uint16)
+                    vpar = np.array([rec[5], rec[6]], np.float16).view(np.uint16)
+                    np.testing.assert_array_equal(kp[b, g, t, :2], kpar, err_msg=f"{tag}: K mean/std {t}")
+                    np.testing.assert_array_equal(vp[b, g, t, :2], vpar, err_msg=f"{tag}: V mean/std {t}")
+                else:
+                    np.testing.assert_array_equal(kp[b, g, t], oc.canonical_params(rec[2], rec[3]).view(np.uint16)
+                                                  .reshape(-1), err_msg=f"{tag}: K params {t}")
+                    np.testing.assert_array_equal(vp[b, g, t], oc.canonical_params(rec[5], rec[6]).view(np.uint16)
+                                                  .reshape(-1), err_msg=f"{tag}: V params {t}")
+                n_rec += 1
+        log(f"[{label}] {tag}: tiers, scores and {n_rec} per-token records agree")
 
     check("first assignment")
     worst = 0.0

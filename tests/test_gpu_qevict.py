@@ -278,3 +278,15 @@ def test_qevict_degenerate_capacities_parity(torch_cuda, kf, kq):
     small two-tier and quantized-only budgets that evict most windows."""
     c = W.TINY.replace(k_full=kf, k_quant=kq, steps=40)
     _run_parity(c, torch_cuda, label=f"degenerate kf={kf} kq={kq}")
+
+
+def test_qevict_large_batch_multi_item_pack_parity(torch_cuda):
+    """128 sequences: the pack/promote launch holds about 6 * CUs / 128
+    workgroups per sequence, fewer than the (window, KV head) items of a
+    routing event (12 windows x 4 KV heads at the first one), so every
+    workgroup walks several items with the next item's window fetched ahead.
+    Ledgers, contents and tiers of sampled sequences are compared bit for bit
+    after every event."""
+    c = W.TINY.replace(batch=128, n_q_heads=16, n_kv_heads=4, head_dim=128, prefill=520, steps=40, window=16,
+                       omega=16, n_sink=5, n_recent=64, k_full=3, k_quant=12)
+    _run_parity(c, torch_cuda, seq_ids=[0, 37, 64, 127], check_ledger_every=1, label="batch128")
