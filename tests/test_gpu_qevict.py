@@ -290,3 +290,29 @@ def test_qevict_large_batch_multi_item_pack_parity(torch_cuda):
     c = W.TINY.replace(batch=128, n_q_heads=16, n_kv_heads=4, head_dim=128, prefill=520, steps=40, window=16,
                        omega=16, n_sink=5, n_recent=64, k_full=3, k_quant=12)
     _run_parity(c, torch_cuda, seq_ids=[0, 37, 64, 127], check_ledger_every=1, label="batch128")
+
+
+def test_quantize_int1_float16_tie_rounds_twice(torch_cuda):
+    """A value row of the HqeKV recipe (sequence 5, KV head 3, position 40690
+    at a 65536-token prompt + 128 steps) whose population deviation rounds to
+    exactly 1.81396484375 in float32: a float16 tie, which rounds to even
+    (16194).  The float64 deviation lies just below the tie, so rounding it to
+    float16 in one step would give 16193; the reading rounds to float32
+    first."""
+    from tiered_quantization_eviction_amd import _lib as L
+    log("quantize int1-normal at a float16 tie")
+    cfg = W.HQEKV.replace(steps=128)
+    _, v = W.Workload(cfg).kv(5)
+    row = v[3, 40690][None, None, :]                         # [1 block, 1 token, 128] bf16 bits
+    x = bf16_to_f64(row).astype(np.float32)
+    c, m, sd = oc.int1_normal_quantize(x[0])
+    assert float(sd[0]) == 1.814453125 and sd.view(np.uint16)[0] == 16194
+    x64 = x[0, 0].astype(np.float64)
+    m32 = np.float32(x64.sum() / 128)
+    s64 = np.sqrt(((x64 - np.float64(m32)) ** 2).sum() / 128)
+    assert float(np.float32(s64)) == 1.81396484375 and np.float16(s64) != np.float16(np.float32(s64))
+    codes, params = L.quantize_window(torch_cuda.from_numpy(row.view(np.int16)).cuda(), L.KIND_INT1_NORMAL, 1)
+    params = params.cpu().numpy().view(np.uint16).reshape(-1)
+    assert params[1] == 16194, params
+    assert params[0] == m.view(np.uint16)[0]
+    np.testing.assert_array_equal(codes.cpu().numpy()[0], oc.pack_codes(c.reshape(-1), 1))

@@ -80,6 +80,16 @@ __device__ __forceinline__ half8 codes8(uint32_t m) {
 
 __device__ inline float neg_inf() { return -__builtin_inff(); }
 
+// float32 rounding of a double that a following float16 conversion must see:
+// without the barrier the compiler folds double -> float -> half into one
+// double -> half rounding, which differs from the two-step rounding whenever
+// the float32 value is a float16 tie
+__device__ __forceinline__ float f64_to_f32_kept(double x) {
+  float f = (float)x;
+  asm volatile("" : "+v"(f));
+  return f;
+}
+
 // Streaming loads of cache tiles: read once per decode step, so they are
 // issued nontemporal (they do not displace reused lines in the caches, and
 // HBM read throughput is measurably higher than with ordinary loads).

@@ -1399,13 +1399,13 @@ __global__ __launch_bounds__(256) void quantize_window_kernel(const void *__rest
       const size_t row = xb + (size_t)t * D;
       double sum = 0.0;
       for (int c = 0; c < D; ++c) sum += (double)load_x(x, dtype, row + c);
-      const float m32 = (float)(sum / D);
+      const float m32 = f64_to_f32_kept(sum / D);
       double ss = 0.0;
       for (int c = 0; c < D; ++c) {
         const double dv = (double)load_x(x, dtype, row + c) - (double)m32;
         ss += dv * dv;
       }
-      const float sd32 = (float)sqrt(ss / D);
+      const float sd32 = f64_to_f32_kept(sqrt(ss / D));
       const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
       if (!isfinite((float)m16) || !isfinite((float)sd16)) g_quant_status = QKV_ERANGE;
       uint16_t *pp = params + ((size_t)blk * tokens + t) * 2;

@@ -1315,7 +1315,7 @@ __global__ __launch_bounds__(256) void hq_requant_kernel(TokGeom g, TokState st,
       for (int e = 0; e < CPL; ++e) sum += (double)x[e];
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
-      const float m32 = (float)(sum / D);
+      const float m32 = f64_to_f32_kept(sum / D);
       double ss = 0.0;
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
@@ -1324,7 +1324,7 @@ __global__ __launch_bounds__(256) void hq_requant_kernel(TokGeom g, TokState st,
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
-      const float sd32 = (float)sqrt(ss / D);
+      const float sd32 = f64_to_f32_kept(sqrt(ss / D));
       const half_t m16 = (half_t)m32, sd16 = (half_t)sd32;
       if (!isfinite((float)m16) || !isfinite((float)sd16)) st.status[0] = QKV_ERANGE;
       uint32_t cb = 0u;   // bit c of the row: x_c > mean
