@@ -63,7 +63,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
-WORKLOADS = {c.name: c for c in (W.DRIFT, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O, W.TINY)}
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O, W.TINY)}
 CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",
@@ -82,7 +82,8 @@ def describe(cfg, steps, first=0):
                 f"Kf=204 BF16 + Kq=612 INT2 windows (group 32); query switch A->B at step {sw} ({inside})")
     if cfg.policy == W.POLICY_QEVICT:
         return (f"QEvict three-tier ({cfg.name}): " + head + f", window={cfg.window} Omega={cfg.omega}, "
-                f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} INT2 windows")
+                f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} "
+                f"INT{cfg.quant_bits} windows")
     if cfg.policy == W.POLICY_H2O:
         return (f"H2O heavy hitters: " + head + f", scored prompt, {cfg.n_sink} sinks + {cfg.k_full} heavy + "
                 f"{cfg.n_recent} recent tokens per KV head, eviction every step")
@@ -562,7 +563,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPES[cfg.policy],
+        "dtype": DTYPES[cfg.policy].replace("int2", f"int{cfg.quant_bits}"),
         "data": "synthetic",
         "config": {"workload": describe(cfg, steps, first), "global_batch": cfg.batch,
                    "seq_len": cfg.total_tokens, "parallelism": "single GPU", "attention_splits": splits},

@@ -159,17 +159,19 @@ def _snapshot_run(cfg, torch, cut, label, oracle_seq=None, pending=False):
     return seq
 
 
-def _small_drift():
+def _small_drift(bits=2):
     c = W.DRIFT.replace(name="drift_small", batch=3, n_q_heads=16, n_kv_heads=4, head_dim=128, prefill=2048,
-                        steps=160, cluster_a=(60, 24), cluster_b=(4, 12), switch_step=64)
+                        steps=160, cluster_a=(60, 24), cluster_b=(4, 12), switch_step=64, quant_bits=bits)
     w0 = W.w0(c)
     return c.replace(k_full=int(0.1 * w0), k_quant=int(0.3 * w0))
 
 
-def test_snapshot_restore_qevict(torch_cuda):
+@pytest.mark.parametrize("bits", [2, 4])
+def test_snapshot_restore_qevict(torch_cuda, bits):
     """Exported mid-window after four routing events (step 70), restored, and
-    continued through the query switch and the promotions that follow."""
-    seq = _snapshot_run(_small_drift(), torch_cuda, 70, "qevict-snapshot", oracle_seq=1)
+    continued through the query switch and the promotions that follow (INT2
+    and INT4 recoverable tiers)."""
+    seq = _snapshot_run(_small_drift(bits), torch_cuda, 70, f"qevict{bits}-snapshot", oracle_seq=1)
     assert any(e.promoted for e in seq.events[5:]), "no promotion after the restore"
 
 

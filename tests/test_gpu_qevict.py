@@ -163,17 +163,17 @@ def _oracle_seq(cfg, wl, b):
 
 
 def _check_ledger(run, seqs, cfg):
-    U, B, H, w, d = run.U, cfg.batch, cfg.n_kv_heads, cfg.window, cfg.head_dim
+    U, B, H, w, d, bits = run.U, cfg.batch, cfg.n_kv_heads, cfg.window, cfg.head_dim, cfg.quant_bits
     flags = run.ledger_flags()
-    kc = run.export_np("kcodes", np.uint8, (B, U, H, w * d // 4))
-    vc = run.export_np("vcodes", np.uint8, (B, U, H, w * d // 4))
+    kc = run.export_np("kcodes", np.uint8, (B, U, H, w * d * bits // 8))
+    vc = run.export_np("vcodes", np.uint8, (B, U, H, w * d * bits // 8))
     kp = run.export_np("kparams", np.uint16, (B, U, H, d, 2))
     vp = run.export_np("vparams", np.uint16, (B, U, H, w, d // 32, 2))
     for b, seq in seqs.items():
         assert set(np.flatnonzero(flags[b])) == set(seq.ledger), "ledger membership differs"
         for u, Lg in seq.ledger.items():
-            np.testing.assert_array_equal(kc[b, u], oc.canonical_k_codes(Lg["kcodes"], 2), err_msg=f"kcodes u={u}")
-            np.testing.assert_array_equal(vc[b, u], oc.canonical_v_codes(Lg["vcodes"], 2), err_msg=f"vcodes u={u}")
+            np.testing.assert_array_equal(kc[b, u], oc.canonical_k_codes(Lg["kcodes"], bits), err_msg=f"kcodes u={u}")
+            np.testing.assert_array_equal(vc[b, u], oc.canonical_v_codes(Lg["vcodes"], bits), err_msg=f"vcodes u={u}")
             np.testing.assert_array_equal(kp[b, u], oc.canonical_params(Lg["kscale"], Lg["kzero"])[:, :, 0]
                                           .view(np.uint16), err_msg=f"kparams u={u}")
             np.testing.assert_array_equal(vp[b, u], oc.canonical_params(Lg["vscale"], Lg["vzero"]).view(np.uint16),
@@ -316,3 +316,36 @@ def test_quantize_int1_float16_tie_rounds_twice(torch_cuda):
     assert params[1] == 16194, params
     assert params[0] == m.view(np.uint16)[0]
     np.testing.assert_array_equal(codes.cpu().numpy()[0], oc.pack_codes(c.reshape(-1), 1))
+
+
+# ---------------------------------------------------------------------------
+# the INT4 recoverable tier (QEvict notes section 6.5: the recoverable tier's
+# precision is one of the swept knobs; INT4 keeps fewer windows at a fixed
+# byte budget, each with less error)
+# ---------------------------------------------------------------------------
+
+def test_qevict_int4_tiny_parity(torch_cuda):
+    _run_parity(W.TINY.replace(quant_bits=4), torch_cuda, label="int4-tiny")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_qevict_int4_small_drift_parity(torch_cuda, splits):
+    """The drift recipe with a 4-bit recoverable tier at the capacities an
+    INT2 tier of the same bytes would have bought half of (K_q halved):
+    codes, parameters, promoted contents bit-exact; promotions after the
+    query switch."""
+    c = _small_drift(quant_bits=4)
+    run, seqs = _run_parity(c.replace(k_quant=c.k_quant // 2), torch_cuda, n_splits=splits, check_ledger_every=2,
+                            label=f"int4-drift s={splits}")
+    assert any(e.promoted for sq in seqs.values() for e in sq.events)
+
+
+def test_qevict_int4_window32_g8_parity(torch_cuda):
+    c = W.STRESS.replace(batch=2, prefill=3000, steps=96, n_q_heads=64, n_kv_heads=8, quant_bits=4)
+    w0 = W.w0(c)
+    _run_parity(c.replace(k_full=w0 // 4, k_quant=w0 // 2), torch_cuda, n_splits=5, label="int4-w32g8")
+
+
+def test_qevict_int4_d64_window8_parity(torch_cuda):
+    c = W.TINY.replace(batch=2, n_q_heads=8, n_kv_heads=2, prefill=515, steps=40, k_full=10, k_quant=20, quant_bits=4)
+    _run_parity(c, torch_cuda, n_splits=4, label="int4-d64w8")

@@ -98,8 +98,45 @@ def test_qevict_int2_lossless_on_four_level_data():
         np.testing.assert_allclose(outs[s], ref, atol=1e-12)
 
 
-def test_qevict_invariants_on_small_drift():
-    cfg = small_drift()
+def _sixteen_level_bits(cfg, rng):
+    """K/V whose KIVI groups sit exactly on 16 levels -1 + k/8, k = 0..15."""
+    hkv, T, d, w = cfg.n_kv_heads, cfg.total_tokens, cfg.head_dim, cfg.window
+    lv = (-1.0 + np.arange(16) / 8.0).astype(np.float32)
+    kc = rng.integers(0, 16, (hkv, T, d))
+    for a in range(cfg.n_sink, T - w + 1, w):
+        kc[:, a, :], kc[:, a + 1, :] = 0, 15
+    vc = rng.integers(0, 16, (hkv, T, d))
+    vc[:, :, 0::32], vc[:, :, 1::32] = 0, 15
+    to_bits = lambda x: (x.view(np.uint32) >> 16).astype(np.uint16)
+    return to_bits(lv[kc]), to_bits(lv[vc])
+
+
+def test_qevict_int4_lossless_on_sixteen_level_data_and_int2_is_not():
+    """QEvict notes section 6.5 (INT4 as the recoverable tier's precision):
+    with every window quantized, data on 16 levels per group passes the
+    4-bit tier exactly (attention equals exact attention); the 2-bit tier on
+    the same data does not."""
+    cfg = W.TINY.replace(k_full=0, k_quant=10 ** 6, quant_bits=4)
+    rng = np.random.default_rng(11)
+    kb, vb = _sixteen_level_bits(cfg, rng)
+    qb = (np.asarray(rng.standard_normal((cfg.steps, cfg.n_q_heads, cfg.head_dim)), np.float32)
+          .view(np.uint32) >> 16).astype(np.uint16)
+    seq, outs, _ = run(cfg, kb, vb, qb)
+    assert seq.ledger and all(L["bits"] == 4 and L["kcodes"].max() <= 15 for L in seq.ledger.values())
+    K, V = bf16_to_f64(kb), bf16_to_f64(vb)
+    worst2 = 0.0
+    seq2, outs2, _ = run(cfg.replace(quant_bits=2), kb, vb, qb)
+    for s in range(cfg.steps):
+        n = cfg.prefill + s + 1
+        ref, _ = attend(bf16_to_f64(qb[s]), K[:, :n], V[:, :n])
+        np.testing.assert_allclose(outs[s], ref, atol=1e-12)
+        worst2 = max(worst2, float(np.abs(outs2[s] - ref).max()))
+    assert worst2 > 1e-3
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_qevict_invariants_on_small_drift(bits):
+    cfg = small_drift(quant_bits=bits)
     wl = W.Workload(cfg)
     kb, vb = wl.kv(0)
     qb = wl.queries(0)
@@ -118,7 +155,7 @@ def test_qevict_invariants_on_small_drift():
     # migration stability: a window's codes never change after its first pack
     seq2 = oe.QEvictSequence(kb, vb, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
                              n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
-                             n_q_heads=cfg.n_q_heads)
+                             bits=cfg.quant_bits, n_q_heads=cfg.n_q_heads)
     seq2.prefill(cfg.prefill)
     cycles = 0
     for s in range(cfg.steps):

@@ -86,7 +86,7 @@ int validate(const qkv_config *c) {
   if (c->omega < 1) return QKV_EINVAL;
   if (c->n_sink < 0 || c->n_sink > TS || c->n_recent < 0) return QKV_EINVAL;
   if (c->k_full < 0 || c->k_quant < 0) return QKV_EINVAL;
-  if (c->quant_bits != 2 || c->group != 32) return QKV_EINVAL;
+  if ((c->quant_bits != 2 && c->quant_bits != 4) || c->group != 32) return QKV_EINVAL;
   // the attention workgroup's LDS (q*s limbs of every window slot of eight
   // waves) exceeds the device's with d = 128, eight heads per KV head and
   // windows of one tile
@@ -117,8 +117,8 @@ void make_geom(const qkv_config *c, Geom &g) {
   g.tpw = (c->window + TS - 1) / TS;
   g.page_unit_elems = g.tpw * 2 * TS * g.d;
   g.kparam_bytes = 4 * g.d;
-  g.tile_kcode_bytes = TS * g.d / 4;
-  g.tile_vcode_bytes = TS * g.d / 4;
+  g.tile_kcode_bytes = TS * g.d * g.bits / 8;
+  g.tile_vcode_bytes = TS * g.d * g.bits / 8;
   g.tile_vparam_bytes = 4 * (g.d / 32) * 16;
   g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
   g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;

@@ -103,30 +103,75 @@ __host__ __device__ inline int v_tile_index(int t, int c) {
   return (((c >> 5) * 64 + (t >> 2) * 16 + (c & 15)) * 2 + ((c >> 4) & 1)) * 4 + (t & 3);
 }
 
-// Ledger code placement (2-bit codes, 16 per dword, slot p at bits [2p, 2p+1]).
-// A tile's codes are 2*nkd dwords per lane (nkd = d/64): the lane's nkd key
-// dwords, then its nkd value dwords, so one 16-byte load (d = 128) fetches all
-// of a lane's codes.  Slots are placed for the unpack in the attention
-// kernel: x & 0x33333333 keeps slots 4k and 4k+2 of byte k in the low bits of
-// its two nibbles, (x >> 2) & 0x33333333 slots 4k+1 and 4k+3, and a scaled
-// FP4 (e2m1) conversion of a byte then yields the two codes as an exact fp16
-// pair (a nibble 00cc is the e2m1 value cc/2).
-// Keys, for the A operand of k-block kb (lane l = ((c%32)/8)*16 + t holds the
-// 8 channels kb*32 + 8*(l/16) ..): dword l*2nkd + kb/2; channel e = c%8 sits
-// in byte e/2 of the kb%2 half: slot 4*(e/2) + kb%2 + 2*(e%2).
-__host__ __device__ inline void kcode_slot(int t, int c, int nkd, int &dword, int &shift) {
-  const int kb = c >> 5, l = ((c & 31) >> 3) * 16 + t, e = c & 7;
-  dword = l * 2 * nkd + (kb >> 1);
-  shift = 2 * (4 * (e >> 1) + (kb & 1) + 2 * (e & 1));
+// Ledger code placement.  A tile's codes are DPL = d*bits/64 dwords per lane
+// (code_dwords): the lane's key dwords, then its value dwords, so one or two
+// 16-byte loads fetch all of a lane's codes.
+//
+// 2-bit codes (16 per dword, slot p at bits [2p, 2p+1]; nkd = d/64 key and
+// nkd value dwords per lane).  Slots are placed for the unpack in the
+// attention kernel: x & 0x33333333 keeps slots 4k and 4k+2 of byte k in the
+// low bits of its two nibbles, (x >> 2) & 0x33333333 slots 4k+1 and 4k+3, and
+// a scaled FP4 (e2m1) conversion of a byte then yields the two codes as an
+// exact fp16 pair (a nibble 00cc is the e2m1 value cc/2).
+//   Keys, for the A operand of k-block kb (lane l = ((c%32)/8)*16 + t holds
+//   the 8 channels kb*32 + 8*(l/16) ..): dword l*DPL + kb/2; channel e = c%8
+//   sits in byte e/2 of the kb%2 half: slot 4*(e/2) + kb%2 + 2*(e%2).
+//   Values, for the B operand of column tile ct (lane l = (t/4)*16 + c%16
+//   holds tokens 4*(l/16) .. +3 of channel ct*16 + l%16): dword l*DPL + nkd +
+//   ct/4; byte ct%4; tokens (0,1) of the quad in the first half, (2,3) in the
+//   second: slot 4*(ct%4) + (t%4)/2 + 2*(t%2).
+// 4-bit codes (8 per dword, nibble p at bits [4p, 4p+3]; d/32 key and d/32
+// value dwords per lane).  x & 0x0F0F0F0F keeps the even nibbles, (x >> 4) &
+// 0x0F0F0F0F the odd ones, each as the low nibble of a byte, which the scaled
+// FP8 conversion turns into an exact fp16 code.
+//   Keys: dword l*DPL + kb; channel e = c%8 at nibble 2e (e < 4) or 2(e-4)+1.
+//   Values: dword l*DPL + d/32 + ct/2; token t%4 of column tile ct at nibble
+//   2*(t%4) + ct%2.
+__host__ __device__ inline int code_dwords(int d, int bits) { return d * bits / 64; }
+__host__ __device__ inline void kcode_slot(int t, int c, int d, int bits, int &dword, int &shift) {
+  const int kb = c >> 5, l = ((c & 31) >> 3) * 16 + t, e = c & 7, dpl = code_dwords(d, bits);
+  if (bits == 2) {
+    dword = l * dpl + (kb >> 1);
+    shift = 2 * (4 * (e >> 1) + (kb & 1) + 2 * (e & 1));
+  } else {
+    dword = l * dpl + kb;
+    shift = 4 * (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+  }
 }
-// Values, for the B operand of column tile ct (lane l = (t/4)*16 + c%16 holds
-// tokens 4*(l/16) .. +3 of channel ct*16 + l%16): dword l*2nkd + nkd + ct/4;
-// byte ct%4; tokens (0,1) of the quad in the first half, (2,3) in the second:
-// slot 4*(ct%4) + (t%4)/2 + 2*(t%2).
-__host__ __device__ inline void vcode_slot(int t, int c, int nkd, int &dword, int &shift) {
-  const int ct = c >> 4, l = (t >> 2) * 16 + (c & 15), tt = t & 3;
-  dword = l * 2 * nkd + nkd + (ct >> 2);
-  shift = 2 * (4 * (ct & 3) + (tt >> 1) + 2 * (tt & 1));
+__host__ __device__ inline void vcode_slot(int t, int c, int d, int bits, int &dword, int &shift) {
+  const int ct = c >> 4, l = (t >> 2) * 16 + (c & 15), tt = t & 3, dpl = code_dwords(d, bits);
+  if (bits == 2) {
+    dword = l * dpl + d / 64 + (ct >> 2);
+    shift = 2 * (4 * (ct & 3) + (tt >> 1) + 2 * (tt & 1));
+  } else {
+    dword = l * dpl + d / 32 + (ct >> 1);
+    shift = 4 * (2 * tt + (ct & 1));
+  }
+}
+// The inverse: code slot p of dword w of lane l (a key dword when w is below
+// the lane's key-dword count) holds the element (token t, channel c).
+__host__ __device__ inline bool code_slot_elem(int l, int w, int p, int d, int bits, int &t, int &c) {
+  if (bits == 2) {
+    const int nkd = d / 64, m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
+    if (w < nkd) {
+      c = (2 * w + par) * 32 + (l / 16) * 8 + 2 * m + hi;
+      t = l % 16;
+      return true;
+    }
+    c = (4 * (w - nkd) + m) * 16 + l % 16;
+    t = 4 * (l / 16) + 2 * par + hi;
+    return false;
+  }
+  const int kbn = d / 32;
+  if (w < kbn) {
+    const int e = (p & 1) ? 4 + (p >> 1) : (p >> 1);
+    c = w * 32 + (l / 16) * 8 + e;
+    t = l % 16;
+    return true;
+  }
+  c = (2 * (w - kbn) + (p & 1)) * 16 + l % 16;
+  t = 4 * (l / 16) + (p >> 1);
+  return false;
 }
 // V params of a tile: [token quad tq][group g][s x4, z x4] fp16
 __host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int which /*0 s,1 z*/) {

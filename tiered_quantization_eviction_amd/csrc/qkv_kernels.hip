@@ -378,9 +378,33 @@ template <int D> constexpr int QSTR = D + 8;       // one q*s row
 
 struct QBuf {
   uint4 code[QT];   // the lane's key code dwords, then value code dwords, of each tile
+  uint4 code2[QT];  // 4-bit codes at d = 128: the lane's value code dwords
   uint2 kp[QT];     // the lane's 8 bytes of each window's key params (window slots)
   uint32_t vp[QT];  // the lane's 4 bytes of each tile's value params
 };
+
+__device__ __forceinline__ uint32_t u4_at(const uint4 &v, int i) {   // i is a constant after unrolling
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// A operand of k-block kb of tile j: the lane's 8 key codes as exact fp16
+template <int D, int BITS>
+__device__ __forceinline__ half8 key_codes(const QBuf &buf, int j, int kb) {
+  if (BITS == 2) return codes8(code_half(u4_at(buf.code[j], kb >> 1), kb & 1));
+  return codes8_int4(u4_at(buf.code[j], kb));
+}
+// B operand half of column tile ct of tile j: the codes of the lane's four
+// tokens (4 lq .. 4 lq + 3) of channel ct*16 + col, as exact fp16
+template <int D, int BITS>
+__device__ __forceinline__ half4 value_codes(const QBuf &buf, int j, int ct) {
+  if (BITS == 2) {
+    const uint32_t v = u4_at(buf.code[j], D == 128 ? 2 + (ct >> 2) : 1);
+    return __builtin_shufflevector(fp4_pair_sel(code_half(v, 0), ct), fp4_pair_sel(code_half(v, 1), ct), 0, 1, 2, 3);
+  }
+  const uint32_t v = D == 128 ? u4_at(buf.code2[j], ct >> 1) : u4_at(buf.code[j], 2 + (ct >> 1));
+  const uint32_t m = ((ct & 1) ? (v >> 4) : v) & 0x0F0F0F0Fu;
+  return __builtin_shufflevector(fp8_pair<false>(m), fp8_pair<true>(m), 0, 1, 2, 3);
+}
 struct QBlock {
   int e, nwin;
   int u[QT];        // window slots; spare slots repeat slot 0
@@ -401,9 +425,9 @@ __device__ __forceinline__ void qblock_make(const Ctx &c, int ea, int eb, int i,
   }
 }
 
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf &buf) {
-  constexpr int NKD = D / 64;
+  constexpr int DPL = D * BITS / 64;   // code dwords per lane per tile
   const Geom &g = *c.g;
   const int tpw = g.tpw;
   const int kl = c.lane & (g.kparam_bytes / 8 - 1);       // lanes past the params repeat them
@@ -416,7 +440,10 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     const int uw = tpw == 1 ? qb.u[j] : qb.u[j >> 1];
     const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, uw, c.h);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
-    if (NKD == 2) {
+    if (DPL == 8) {
+      buf.code[j] = ld_stream16(T + c.lane * 32);
+      buf.code2[j] = ld_stream16(T + c.lane * 32 + 16);
+    } else if (DPL == 4) {
       buf.code[j] = ld_stream16(T + c.lane * 16);
     } else {
       const uint2 cw = ld_stream8(T + c.lane * 8);
@@ -428,11 +455,11 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
   for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
 }
 
-template <int D, int GP>
+template <int D, int GP, int BITS>
 __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&qc)[2],
                                               const half8 (&bz)[D / 32], float sc_quant, const float (&row_bias)[4],
                                               const QBlock &qb, const QBuf &buf) {
-  constexpr int NKD = D / 64, KB = D / 32, NG = D / 32;
+  constexpr int KB = D / 32, NG = D / 32;
   const Geom &g = *c.g;
   const int tpw = g.tpw;
   const int nws = QT / tpw;                                  // window slots per block
@@ -503,8 +530,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     const half8 bq = bqa;
     bqa = bqb;
     if (idx + 2 < KB * QT) bqb = bq_at(idx + 2);
-    const uint32_t kw = (kb >> 1) == 0 ? buf.code[j].x : buf.code[j].y;
-    s[j] = mfma_f16_k32(codes8(code_half(kw, kb & 1)), bq, s[j]);
+    s[j] = mfma_f16_k32(key_codes<D, BITS>(buf, j, kb), bq, s[j]);
   }
 #pragma unroll
   for (int j = 0; j < QT; ++j)
@@ -589,15 +615,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
 #pragma unroll
       for (int c2 = 0; c2 < 2 * GP; ++c2) {
         const int ct = gb * 2 + c2;
-        const uint32_t v0 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j0].z : buf.code[j0].y)
-                                           : buf.code[j0].w;
-        const uint32_t v1 = (ct >> 2) == 0 ? (NKD == 2 ? buf.code[j1].z : buf.code[j1].y)
-                                           : buf.code[j1].w;
-        // tokens (0,1) of the lane's quad from the low half, (2,3) from the high half; byte = ct % 4
-        const half4 b0 = __builtin_shufflevector(fp4_pair_sel(code_half(v0, 0), ct), fp4_pair_sel(code_half(v0, 1), ct),
-                                                 0, 1, 2, 3);
-        const half4 b1 = __builtin_shufflevector(fp4_pair_sel(code_half(v1, 0), ct), fp4_pair_sel(code_half(v1, 1), ct),
-                                                 0, 1, 2, 3);
+        const half4 b0 = value_codes<D, BITS>(buf, j0, ct), b1 = value_codes<D, BITS>(buf, j1, ct);
         const half8 bc = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
         ws.acc[ct] = mfma_f16_k32(ag, bc, ws.acc[ct]);
       }
@@ -609,7 +627,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   wave_lds_sync();
 }
 
-template <int D, int GP>
+template <int D, int GP, int BITS>
 __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
   half8 qc[2], bz[D / 32];
@@ -628,27 +646,27 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   const int ids0 = ids_fetch(c, ea);
   int ids1 = ids_fetch(c, ea + min(1, n_blocks - 1) * per);
   qblock_make(c, ea, eb, 0, ids0, k0);
-  quant_load<D>(c, k0, b0);
+  quant_load<D, BITS>(c, k0, b0);
   // steady state: two blocks per trip, the following block always in flight
   int i = 0;
   for (; i + 2 < n_blocks; i += 2) {
     const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
     qblock_make(c, ea, eb, i + 1, ids1, k1);
-    quant_load<D>(c, k1, b1);
-    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_load<D, BITS>(c, k1, b1);
+    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
     ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
     qblock_make(c, ea, eb, i + 2, ids2, k0);
-    quant_load<D>(c, k0, b0);
-    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+    quant_load<D, BITS>(c, k0, b0);
+    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
   }
   // the last one or two blocks: nothing past the run is read
   if (i + 1 < n_blocks) {
     qblock_make(c, ea, eb, i + 1, ids1, k1);
-    quant_load<D>(c, k1, b1);
-    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
-    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+    quant_load<D, BITS>(c, k1, b1);
+    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
   } else {
-    quant_compute<D, GP>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
   }
 }
 
@@ -656,12 +674,11 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
 // holds two waves on each SIMD.
 constexpr int QW = 8;
 
-template <int D, int GP>
+template <int D, int GP, int BITS>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
   constexpr int CT = D / 16;
-  constexpr int NKD = D / 64;      // code dwords per lane per tile (keys, values)
   const int S = g.n_splits;
   const int split = blockIdx.x % S;
   const int bh = blockIdx.x / S;
@@ -741,13 +758,13 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int f0 = min(vb0, A), f1 = min(vb1, A);
   const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
   if (((wave & 1) ^ (wave >> 2)) & 1) {
-    run_quant<D, GP>(ws, c, q0, q1);
+    run_quant<D, GP, BITS>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
     run_full<D>(ws, c, r0e, r1e);    // windows not yet ranked
   } else {
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
-    run_quant<D, GP>(ws, c, q0, q1);
+    run_quant<D, GP, BITS>(ws, c, q0, q1);
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -923,11 +940,20 @@ static size_t attend_qs_bytes(const Geom &g) {
   return (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
 }
 
+// the attention kernel of a configuration: head dimension, four or eight heads
+// per KV head (paired channel groups with four), 2- or 4-bit quantized tier
+template <int D, int GP>
+static const void *attend_fn_bits(int bits) {
+  return bits == 4 ? (const void *)attend_qevict_kernel<D, GP, 4> : (const void *)attend_qevict_kernel<D, GP, 2>;
+}
+static const void *attend_fn(const Geom &g) {
+  if (g.d == 128) return g.G == 4 ? attend_fn_bits<128, 2>(g.bits) : attend_fn_bits<128, 1>(g.bits);
+  return g.G == 4 ? attend_fn_bits<64, 2>(g.bits) : attend_fn_bits<64, 1>(g.bits);
+}
+
 hipError_t attend_lds_fits(const Geom &g, bool *fits) {
-  const void *f = g.d == 128 ? (g.G == 4 ? (const void *)attend_qevict_kernel<128, 2> : (const void *)attend_qevict_kernel<128, 1>)
-                             : (g.G == 4 ? (const void *)attend_qevict_kernel<64, 2> : (const void *)attend_qevict_kernel<64, 1>);
   hipFuncAttributes a;
-  hipError_t e = hipFuncGetAttributes(&a, f);
+  hipError_t e = hipFuncGetAttributes(&a, attend_fn(g));
   if (e != hipSuccess) return e;
   int dev = 0, max_lds = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -938,27 +964,19 @@ hipError_t attend_lds_fits(const Geom &g, bool *fits) {
 
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
                          float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
+  float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
-  const size_t qs_bytes = attend_qs_bytes(g);
-  // four heads per KV head: value operands shared by channel-group pairs.
+  size_t qs_bytes = attend_qs_bytes(g);
   // The optional events are attached to the dispatch itself, so they time
   // the kernel's execution (no launch gap).
-  const bool pair = g.G == 4;
-  if (g.d == 128 && pair)
-    hipExtLaunchKernelGGL((attend_qevict_kernel<128, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
-                          g, st, si, q, scale_log2);
-  else if (g.d == 128)
-    hipExtLaunchKernelGGL((attend_qevict_kernel<128, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
-                          g, st, si, q, scale_log2);
-  else if (pair)
-    hipExtLaunchKernelGGL((attend_qevict_kernel<64, 2>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
-                          g, st, si, q, scale_log2);
-  else
-    hipExtLaunchKernelGGL((attend_qevict_kernel<64, 1>), dim3(grid), dim3(64 * QW), qs_bytes, s, ev_start, ev_stop, 0,
-                          g, st, si, q, scale_log2);
-  hipError_t e = hipGetLastError();
+  Geom ga = g;
+  State sa = st;
+  StepInfo sia = si;
+  const uint16_t *qa = q;
+  void *args[] = {&ga, &sa, &sia, &qa, &scale_log2};
+  hipError_t e = hipExtLaunchKernel(attend_fn(g), dim3(grid), dim3(64 * QW), args, qs_bytes, s, ev_start, ev_stop, 0);
   if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mass_out) {
     e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.U * sizeof(float), s);
     if (e != hipSuccess) return e;
@@ -1122,10 +1140,11 @@ __global__ __launch_bounds__(256) void slist_sync_kernel(Geom g, State st, StepI
 constexpr int TR_THREADS = 256;
 template <int D> constexpr int TR_ROW = D + 8;   // LDS row (bf16), 16-byte aligned, rows on distinct banks
 
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void transitions_qevict_kernel(
     Geom g, State st, int per_seq) {
-  constexpr int NKD = D / 64;
+  constexpr int DPL = D * BITS / 64;   // code dwords per lane per tile
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
   constexpr int CHUNKS = TS * D / 8;   // 16-byte chunks per K (or V) tile
   static_assert(CHUNKS <= TR_THREADS && D + 32 * (D / 32) <= TR_THREADS, "workgroup too small");
   __shared__ __attribute__((aligned(16))) uint16_t sk[2 * TS][TR_ROW<D>];   // bf16 of the window, [token][channel]
@@ -1138,7 +1157,7 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   const int npr = st.promote_count[b];
   const int items = (npk + npr) * g.Hkv;
   const int W = g.window, tpw = g.tpw;
-  const float levels = 3.0f;
+  const float levels = (float)MASK;
   const int ci = threadIdx.x;
   const bool own = ci < CHUNKS;   // threads with a key and a value chunk of each tile
   // key chunk ci: token kt_t, channels kt_c .. +7; value chunk ci: tokens
@@ -1229,30 +1248,23 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         vp[vparam_index(g, t % TS, grp, 1)] = z16;
       }
       __syncthreads();
-      // 3. codes in the matrix-core operand order: one thread per (tile, code
-      // dword), walking its 16 slots (the inverse of kcode_slot / vcode_slot)
-      for (int dw2 = ci; dw2 < tpw * NKD * 64; dw2 += TR_THREADS) {
-        const int tile = dw2 / (NKD * 64), dw = dw2 % (NKD * 64);
-        uint32_t *tc = (uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes);
-        const int j = dw / 64, l = dw % 64;
-        uint32_t kword = 0u, vword = 0u;
+      // 3. codes in the matrix-core operand order: one thread per (tile, lane,
+      // code dword), walking its slots (the inverse of kcode_slot / vcode_slot)
+      for (int dw2 = ci; dw2 < tpw * 64 * DPL; dw2 += TR_THREADS) {
+        const int tile = dw2 / (64 * DPL), r = dw2 % (64 * DPL), l = r / DPL, w = r % DPL;
+        uint32_t word = 0u;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
-          {  // key slot p: k-block 2j+par, channel pair m, element hi
-            const int c = (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi, t = l % 16;
-            const int tt = tile * TS + t;
-            kword |= (tt < W ? quant_code(bf16_to_f32(sk[tt][c]), s_ks[c], s_kz[c], levels) : 0u) << (2 * p);
-          }
-          {  // value slot p: column tile 4j+m, token pair par of the quad, element hi
-            const int c = (4 * j + m) * 16 + l % 16, t = 4 * (l / 16) + 2 * par + hi;
-            const int tt = tile * TS + t;
-            vword |= (tt < W ? quant_code(bf16_to_f32(sv[tt][c]), s_vs[tt][c / 32], s_vz[tt][c / 32], levels) : 0u)
-                     << (2 * p);
-          }
+        for (int p = 0; p < 32 / BITS; ++p) {
+          int t, c;
+          const bool key = code_slot_elem(l, w, p, D, BITS, t, c);
+          const int tt = tile * TS + t;
+          uint32_t code = 0u;
+          if (tt < W)
+            code = key ? quant_code(bf16_to_f32(sk[tt][c]), s_ks[c], s_kz[c], levels)
+                       : quant_code(bf16_to_f32(sv[tt][c]), s_vs[tt][c / 32], s_vz[tt][c / 32], levels);
+          word |= code << (BITS * p);
         }
-        tc[l * 2 * NKD + j] = kword;
-        tc[l * 2 * NKD + NKD + j] = vword;
+        ((uint32_t *)(Lb + g.kparam_bytes + tile * g.tile_block_bytes))[l * DPL + w] = word;
       }
       __syncthreads();
     } else {
@@ -1267,8 +1279,8 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         uint16_t *kt = pg + (size_t)tile * 2 * TS * D;
         // keys: the chunk's 8 channels share one code dword (kcode_slot)
         int kdw, vdw, sh;
-        kcode_slot(kt_t, kt_c, NKD, kdw, sh);
-        vcode_slot(4 * vt_q, vt_c, NKD, vdw, sh);
+        kcode_slot(kt_t, kt_c, D, BITS, kdw, sh);
+        vcode_slot(4 * vt_q, vt_c, D, BITS, vdw, sh);
         const uint32_t kw = tc[kdw], vw = tc[vdw];
         const uint4 ks4 = *(const uint4 *)(kparam + kt_c), kz4 = *(const uint4 *)(kparam + D + kt_c);
         const uint4 vpar = *(const uint4 *)(vp + vparam_index(g, 4 * vt_q, vt_c / 32, 0));
@@ -1277,16 +1289,16 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         uint16_t *ke = (uint16_t *)&ko, *ve = (uint16_t *)&vo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kcode_slot(kt_t, kt_c + e, NKD, kdw, sh);
-          const float kcode = (float)((kw >> sh) & 3u);
+          kcode_slot(kt_t, kt_c + e, D, BITS, kdw, sh);
+          const float kcode = (float)((kw >> sh) & MASK);
           ke[e] = f32_to_bf16_rne(__builtin_fmaf(kcode, (float)ks[e], (float)kz[e]));
         }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            vcode_slot(4 * vt_q + j, vt_c + 16 * hf, NKD, vdw, sh);
-            const float vcode = (float)((vw >> sh) & 3u);
+            vcode_slot(4 * vt_q + j, vt_c + 16 * hf, D, BITS, vdw, sh);
+            const float vcode = (float)((vw >> sh) & MASK);
             ve[hf * 4 + j] = f32_to_bf16_rne(__builtin_fmaf(vcode, (float)vps[j], (float)vps[4 + j]));
           }
         *(uint4 *)(kt + ci * 8) = ko;
@@ -1303,7 +1315,10 @@ hipError_t transitions_shape(Geom &g) {
   hipError_t e;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  const void *f = g.d == 128 ? (const void *)transitions_qevict_kernel<128> : (const void *)transitions_qevict_kernel<64>;
+  const void *f = g.d == 128 ? (g.bits == 4 ? (const void *)transitions_qevict_kernel<128, 4>
+                                             : (const void *)transitions_qevict_kernel<128, 2>)
+                             : (g.bits == 4 ? (const void *)transitions_qevict_kernel<64, 4>
+                                             : (const void *)transitions_qevict_kernel<64, 2>);
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, TR_THREADS, 0)) != hipSuccess) return e;
   g.tr_per_seq = per_cu * n_cu / g.B > 1 ? per_cu * n_cu / g.B : 1;
   return hipSuccess;
@@ -1320,10 +1335,15 @@ hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int per_seq = g.tr_per_seq > 0 ? g.tr_per_seq : 128;
-  if (g.d == 128)
-    hipLaunchKernelGGL(transitions_qevict_kernel<128>, dim3(g.B * per_seq), dim3(TR_THREADS), 0, s, g, st, per_seq);
+  const dim3 tg(g.B * per_seq), tb(TR_THREADS);
+  if (g.d == 128 && g.bits == 4)
+    hipLaunchKernelGGL((transitions_qevict_kernel<128, 4>), tg, tb, 0, s, g, st, per_seq);
+  else if (g.d == 128)
+    hipLaunchKernelGGL((transitions_qevict_kernel<128, 2>), tg, tb, 0, s, g, st, per_seq);
+  else if (g.bits == 4)
+    hipLaunchKernelGGL((transitions_qevict_kernel<64, 4>), tg, tb, 0, s, g, st, per_seq);
   else
-    hipLaunchKernelGGL(transitions_qevict_kernel<64>, dim3(g.B * per_seq), dim3(TR_THREADS), 0, s, g, st, per_seq);
+    hipLaunchKernelGGL((transitions_qevict_kernel<64, 2>), tg, tb, 0, s, g, st, per_seq);
   return hipGetLastError();
 }
 
@@ -1526,7 +1546,9 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
   const int W = g.window, D = g.d;
   const size_t n_units = (size_t)g.B * g.U * g.Hkv;
   if (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) {
-    const int bytes_per = W * D / 4;
+    const int bits = g.bits, per_byte = 8 / bits;
+    const uint32_t mask = (1u << bits) - 1u;
+    const int bytes_per = W * D * bits / 8;
     const size_t total = n_units * bytes_per;
     for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += (size_t)gridDim.x * blockDim.x) {
       const size_t blk = it / bytes_per;
@@ -1537,22 +1559,20 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
       uint32_t val = 0;
       if (st.has_ledger[b * g.U + u]) {
         const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
-        for (int k = 0; k < 4; ++k) {
-          const int e = byte * 4 + k;
+        for (int k = 0; k < per_byte; ++k) {
+          const int e = byte * per_byte + k;
           int t, c, dw, sh;
           if (what == QKV_EXPORT_KCODES) {
             c = e / W;
             t = e % W;
-            kcode_slot(t % TS, c, D / 64, dw, sh);
-            const uint32_t *kc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
-            val |= ((kc[dw] >> sh) & 3u) << (2 * k);
+            kcode_slot(t % TS, c, D, bits, dw, sh);
           } else {
             t = e / D;
             c = e % D;
-            vcode_slot(t % TS, c, D / 64, dw, sh);
-            const uint32_t *vc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
-            val |= ((vc[dw] >> sh) & 3u) << (2 * k);
+            vcode_slot(t % TS, c, D, bits, dw, sh);
           }
+          const uint32_t *tc = (const uint32_t *)(Lb + g.kparam_bytes + (t / TS) * g.tile_block_bytes);
+          val |= ((tc[dw] >> sh) & mask) << (bits * k);
         }
       }
       ((uint8_t *)dst)[it] = (uint8_t)val;
@@ -1632,31 +1652,35 @@ hipError_t launch_write_snapshot(const Snapshot &snap, void *dst, hipStream_t s)
 // thread from the canonical copy (a code dword gathers its 16 slots, so no
 // two threads write the same word).
 __global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what, const void *__restrict__ src) {
-  const int W = g.window, D = g.d, nkd = D / 64;
+  const int W = g.window, D = g.d;
   const size_t n_units = (size_t)g.B * g.U * g.Hkv;   // (b, u, h) blocks, in canonical order
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES) {
     const bool keys = what == QKV_EXPORT_KCODES;
-    const int per_unit = g.tpw * 64 * nkd;   // this kind's code dwords per block
-    const int cbytes = W * D / 4;            // canonical bytes per block
+    const int bits = g.bits, dpl = code_dwords(D, bits), per_byte = 8 / bits;
+    const int nkw = bits == 2 ? D / 64 : D / 32;     // key dwords per lane
+    const int per_lane = keys ? nkw : dpl - nkw;     // this kind's dwords per lane
+    const int per_unit = g.tpw * 64 * per_lane;      // this kind's code dwords per block
+    const int cbytes = W * D * bits / 8;             // canonical bytes per block
     for (size_t it = i0; it < n_units * per_unit; it += stride) {
       const size_t blk = it / per_unit;
       const int r = (int)(it % per_unit);
-      const int tile = r / (64 * nkd), l = (r % (64 * nkd)) / nkd, j = r % nkd;
+      const int tile = r / (64 * per_lane), l = (r % (64 * per_lane)) / per_lane;
+      const int w = (keys ? 0 : nkw) + r % per_lane;
       const uint8_t *cs = (const uint8_t *)src + blk * cbytes;
       uint32_t word = 0u;
-      for (int p = 0; p < 16; ++p) {
-        const int m = p >> 2, par = p & 1, hi = (p >> 1) & 1;
-        const int c = keys ? (2 * j + par) * 32 + (l / 16) * 8 + 2 * m + hi : (4 * j + m) * 16 + l % 16;
-        const int tt = tile * TS + (keys ? l % 16 : 4 * (l / 16) + 2 * par + hi);
+      for (int p = 0; p < 32 / bits; ++p) {
+        int t, c;
+        (void)code_slot_elem(l, w, p, D, bits, t, c);
+        const int tt = tile * TS + t;
         if (tt >= W) continue;
         const int e = keys ? c * W + tt : tt * D + c;
-        word |= (uint32_t)((cs[e >> 2] >> (2 * (e & 3))) & 3) << (2 * p);
+        word |= (uint32_t)((cs[e / per_byte] >> (bits * (e % per_byte))) & ((1 << bits) - 1)) << (bits * p);
       }
       uint32_t *tc = (uint32_t *)(st.ledger + blk * g.ledger_unit_bytes + g.kparam_bytes +
                                   (size_t)tile * g.tile_block_bytes);
-      tc[l * 2 * nkd + (keys ? 0 : nkd) + j] = word;
+      tc[l * dpl + w] = word;
     }
   } else if (what == QKV_EXPORT_KPARAMS) {
     const uint16_t *ps = (const uint16_t *)src;   // [blk][D][1][2]

@@ -147,6 +147,11 @@ DRIFT = _reg(Config(
     k_full=int(0.10 * _W0_DRIFT), k_quant=int(0.30 * _W0_DRIFT), quant_bits=2,
     cluster_a=(1024, 256), cluster_b=(8, 128), switch_step=100, seed=0))
 
+# 3b: the same layer with a 4-bit recoverable tier at the same bytes: one
+#     window and KV head costs 2816 B in INT4 against 1792 B in INT2, so the
+#     bytes of 612 INT2 windows hold 389 INT4 windows.
+DRIFT_INT4 = _reg(DRIFT.replace(name="drift_int4", quant_bits=4, k_quant=389))
+
 # 4: HqeKV five-tier per-token assignment.
 HQEKV = _reg(Config(
     name="hqekv", policy=POLICY_HQEKV, recipe="hqekv",
