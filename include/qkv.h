@@ -91,6 +91,13 @@ typedef struct qkv_config {
                        * their tokens' metrics, shares counted in chunks, the
                        * two best chunks kept BF16 (HqeKV notes 3.3);
                        * ceil(max_ctx / c) <= 4096.  0 otherwise.            */
+  int32_t n_layers;   /* QEvict: layers held by the cache (0 or 1: one layer;
+                       * at most 128).  Each layer has its own pages, scores,
+                       * tiers and lists and is ranked by its own scores with the
+                       * same capacities k_full / k_quant (QEvict notes 4.2: one
+                       * score per layer and window; 4.3 and 4.5: capacities of
+                       * a budget over all layers, qkv_plan_capacities); the
+                       * ledgers of every layer share one pool.  1 otherwise.  */
 } qkv_config;
 
 /* Bytes of device workspace a cache with this configuration needs, or 0 if
@@ -177,6 +184,18 @@ int qkv_create_static(const qkv_config *cfg, qkv_stream stream, qkv_cache **out)
  * Errors: QKV_ECAPACITY if the total would exceed max_ctx.
  */
 int qkv_append(qkv_cache *cache, const void *k, const void *v, int32_t n_tokens, qkv_stream stream);
+
+/*
+ * Multi-layer caches (n_layers > 1): the same calls for one layer.  Layers are
+ * appended and attended one at a time, in any order within a decode step;
+ * qkv_append and qkv_decode_attend act on layer 0.  qkv_route needs every
+ * layer to hold the same number of tokens (QKV_ESTATE otherwise) and routes
+ * all of them.  QKV_EINVAL for a layer outside [0, n_layers).
+ */
+int qkv_append_layer(qkv_cache *cache, int32_t layer, const void *k, const void *v, int32_t n_tokens,
+                     qkv_stream stream);
+int qkv_decode_attend_layer(qkv_cache *cache, int32_t layer, const void *q, float *out, float *mass_out,
+                            qkv_stream stream);
 
 /*
  * One decode step of single-query attention over the accessible cache, with
@@ -291,7 +310,10 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *                                                  first, then quantized); entries past the
  *                                                  ranked count are unspecified
  *   QKV_EXPORT_STATE   int64   [16]               format tag, policy, geometry and step scalars
- * (units without a ledger export zero codes and parameters).
+ * (units without a ledger export zero codes and parameters).  A cache of
+ * n_layers > 1 exports every per-layer kind as n_layers such arrays, layer
+ * after layer (STATE once; QKV_ESTATE unless every layer holds the same
+ * number of tokens).
  * Token policies (H2O, HqeKV), per (sequence, KV head, position):
  *   TIERS uint8 [batch, n_kv_heads, max_ctx]; SCORES float32 [same] (masses
  *   pending in list order are added first); KEYS / VALUES uint16 [batch,
@@ -332,7 +354,9 @@ size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);
  *           VPARAMS, KEYS, VALUES;
  *   H2O:    STATE, TIERS, SCORES, ROUTED, KEYS, VALUES;
  *   HqeKV:  the H2O kinds plus KCODES, VCODES, KPARAMS, VPARAMS.
- * The order is free.  Structures derived from these (list-order scores, the
+ * The order is free, except that QEvict's LEDGER (which hands out the ledger
+ * pool's slots) comes before KCODES, VCODES, KPARAMS and VPARAMS (QKV_ESTATE
+ * otherwise).  Structures derived from these (list-order scores, the
  * compact tiles of the ranked lists, value ranges) are rebuilt on `stream`
  * before the next append, attention, prompt scoring, routing or export, so a
  * restored cache continues exactly as the exported one does.  No pending
@@ -357,6 +381,7 @@ enum {
   QKV_INFO_SPLITS = 4,      /* attention splits per (sequence, KV head)      */
   QKV_INFO_WORKSPACE = 5,   /* workspace bytes in use                        */
   QKV_INFO_LIST_CAPACITY = 6, /* token policies: entries per list of QKV_EXPORT_ROUTED */
+  QKV_INFO_LAYERS = 7,      /* layers held                                   */
 };
 int qkv_info(const qkv_cache *cache, int32_t what, int64_t *value);
 
@@ -371,7 +396,10 @@ int qkv_info(const qkv_cache *cache, int32_t what, int64_t *value);
 int qkv_profile_start(qkv_cache *cache, int32_t n, int32_t stride);
 int qkv_profile_read(qkv_cache *cache, float *ms, int32_t n);
 
-/* Device-latched status: waits for `stream`, returns QKV_OK or QKV_ERANGE. */
+/* Device-latched status of every layer: waits for `stream`, returns QKV_OK,
+ * QKV_ERANGE (a quantization parameter outside float16 range) or
+ * QKV_ECAPACITY (the ledger pool ran out: cannot happen with the pool sized
+ * as qkv_workspace_bytes sizes it, latched rather than faulting). */
 int qkv_status(qkv_cache *cache, qkv_stream stream);
 /* Status latched by qkv_quantize_window calls since the last query (same rule). */
 int qkv_quantize_status(qkv_stream stream);

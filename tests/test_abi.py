@@ -140,13 +140,25 @@ def test_strerror_and_info_arguments():
 
 
 def test_workspace_holds_payload_of_config3():
-    """Unit-indexed pages and ledger of the 32K x 16 workload."""
+    """Unit-indexed pages of the 32K x 16 workload and a ledger pool of
+    K_f + K_q slots per sequence (only Full and Quantized windows hold codes);
+    a 32-layer cache holds 32 layers' pages and one pool of 32 times the slots."""
     L, _ = _lib()
     c = L.make_config(W.DRIFT)
     U = 1 + -(-(W.DRIFT.total_tokens - 5) // 16)
     pages = 16 * U * 8 * 2 * 16 * 128 * 2
-    ledger = 16 * U * 8 * (512 + 512 + 512 + 256)
+    slot = 8 * (512 + 512 + 512 + 256)
+    ledger = 16 * (W.DRIFT.k_full + W.DRIFT.k_quant) * slot
     assert pages + ledger <= L.workspace_bytes(c) <= pages + ledger + 64 * 2 ** 20
+    c32 = L.make_config(W.DRIFT.replace(prefill=4096, steps=64), n_layers=32)
+    U32 = 1 + -(-(4096 + 64 - 5) // 16)
+    pages32 = 32 * 16 * U32 * 8 * 2 * 16 * 128 * 2
+    ledger32 = 32 * 16 * min(W.DRIFT.k_full + W.DRIFT.k_quant, U32) * slot
+    assert pages32 + ledger32 <= L.workspace_bytes(c32) <= pages32 + ledger32 + 32 * 2 ** 20
+    c.n_layers = 129
+    assert L.workspace_bytes(c) == 0
+    h = L.make_config(W.H2O, n_layers=2)
+    assert L.workspace_bytes(h) == 0                 # layers belong to the window policy
 
 
 def test_snapshot_and_ranking_arguments_checked_on_host():

@@ -19,7 +19,8 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 TIER_EMPTY, TIER_SINK, TIER_RECENT, TIER_FULL, TIER_QUANT, TIER_EVICTED = range(6)
 EXPORT = {"tiers": 0, "scores": 1, "ledger": 2, "kcodes": 3, "vcodes": 4, "kparams": 5, "vparams": 6,
           "keys": 7, "values": 8, "routed": 9, "state": 10}
-INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5, "list_capacity": 6}
+INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5, "list_capacity": 6,
+        "layers": 7}
 # what each policy's session snapshot holds (qkv_import restores them all)
 SNAPSHOT = {0: ("state", "tiers", "scores", "ledger", "routed", "kcodes", "vcodes", "kparams", "vparams",
                 "keys", "values"),
@@ -41,6 +42,7 @@ class QkvConfig(ctypes.Structure):
         ("k_full", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("ratios", ctypes.c_float * 5),
         ("quant_bits", ctypes.c_int32), ("group", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
         ("n_splits", ctypes.c_int32), ("score_window", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
     ]
 
 
@@ -66,6 +68,8 @@ def _lib() -> ctypes.CDLL:
         L.qkv_destroy.argtypes = [_vp]
         L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
         L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
+        L.qkv_append_layer.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp]
+        L.qkv_decode_attend_layer.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp]
         L.qkv_route.argtypes = [_vp, _vp]
         L.qkv_prefill_score.argtypes = [_vp, _vp, _i32, _vp]
         L.qkv_quantize_window.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
@@ -209,26 +213,26 @@ class Cache:
         except Exception:
             pass
 
-    def append(self, k, v, stream=None):
-        """k, v: bf16 [B, Hkv, n, d] device tensors."""
+    def append(self, k, v, stream=None, layer: int = 0):
+        """k, v: bf16 [B, Hkv, n, d] device tensors (of `layer`)."""
         c = self.c
         if k.dim() != 4:
             raise ValueError("k: [B, Hkv, n, d] required")
         n = int(k.shape[2])
         _check_tensor(k, "k", (c.batch, c.n_kv_heads, n, c.head_dim), "16")
         _check_tensor(v, "v", (c.batch, c.n_kv_heads, n, c.head_dim), "16")
-        _check(_lib().qkv_append(self.h, _ptr(k), _ptr(v), n, _stream(stream)), "qkv_append")
+        _check(_lib().qkv_append_layer(self.h, int(layer), _ptr(k), _ptr(v), n, _stream(stream)), "qkv_append")
 
-    def decode_attend(self, q, out, mass_out=None, stream=None):
+    def decode_attend(self, q, out, mass_out=None, stream=None, layer: int = 0):
         """q: bf16 [B, Hq, d]; out: float32 [B, Hq, d]; mass_out: optional
-        float32 [B, Hkv, units]."""
+        float32 [B, Hkv, units] (of `layer`)."""
         c = self.c
         _check_tensor(q, "q", (c.batch, c.n_q_heads, c.head_dim), "16")
         _check_tensor(out, "out", (c.batch, c.n_q_heads, c.head_dim), "f32")
         if mass_out is not None:
             _check_tensor(mass_out, "mass_out", (c.batch, c.n_kv_heads, self.info("units")), "f32")
-        _check(_lib().qkv_decode_attend(self.h, _ptr(q), _ptr(out), _ptr(mass_out), _stream(stream)),
-               "qkv_decode_attend")
+        _check(_lib().qkv_decode_attend_layer(self.h, int(layer), _ptr(q), _ptr(out), _ptr(mass_out),
+                                              _stream(stream)), "qkv_decode_attend")
 
     def route(self, stream=None):
         _check(_lib().qkv_route(self.h, _stream(stream)), "qkv_route")

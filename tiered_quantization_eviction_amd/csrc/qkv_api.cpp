@@ -16,7 +16,12 @@ struct qkv_cache {
   qkv_config cfg;
   bool tok;       // token mode (H2O): per-token units, per-(sequence, KV head) scores
   Geom g;
-  State st;
+  int L;          // layers (window policy; 1 for the token policies)
+  State sts[MAX_LAYERS];   // per layer; the ledger pool, its free-slot stack and the
+                           // attention partials are shared by every layer
+  int Nl[MAX_LAYERS];      // tokens appended per sequence, per layer
+  bool ledger_ready;       // ledger slots assigned (always, except between importing a
+                           // snapshot's state and its ledger flags)
   TokGeom tg;
   TokState ts;
   int r_tok;      // token mode: first position not yet ranked
@@ -56,6 +61,8 @@ int validate(const qkv_config *c) {
   if (c->head_dim != 64 && c->head_dim != 128) return QKV_EINVAL;
   if (c->max_ctx < 1) return QKV_EINVAL;
   if (c->n_splits < 0 || c->n_splits > 256) return QKV_EINVAL;
+  if (c->n_layers < 0 || c->n_layers > MAX_LAYERS) return QKV_EINVAL;
+  if (c->n_layers > 1 && c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;   // layers: the window policy
   // a rolling score window is HqeKV's, at most one routing period long
   if (c->score_window < 0 || (c->score_window > 0 && (c->policy != QKV_POLICY_HQEKV || c->score_window > c->omega)))
     return QKV_EINVAL;
@@ -122,6 +129,13 @@ void make_geom(const qkv_config *c, Geom &g) {
   g.tile_vparam_bytes = 4 * (g.d / 32) * 16;
   g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
   g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;
+  {
+    // a layer's sequence holds at most K_f + K_q ledgers (Full and Quantized
+    // windows only), and never more than it has windows
+    const long long per = (long long)c->k_full + c->k_quant < g.U ? (long long)c->k_full + c->k_quant : g.U;
+    const long long P = (long long)(c->n_layers > 1 ? c->n_layers : 1) * g.B * per;
+    g.pool_slots = P > 0 ? (int)P : 1;
+  }
   int S = c->n_splits;
   if (S == 0) {   // one resident round: 256 workgroups of 8 waves = 1 per compute unit, 2 waves per SIMD
     const int pairs = g.B * g.Hkv;
@@ -175,8 +189,8 @@ void make_tok_geom(const qkv_config *c, TokGeom &g) {
   g.n_splits = S;
 }
 
-// workspace carving; with base == nullptr only sizes are computed
-size_t carve(const Geom &g, char *base, State &st) {
+// workspace carving for L layers; with base == nullptr only sizes are computed
+size_t carve(const Geom &g, int L, char *base, State *sts) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char *p = base ? base + off : nullptr;
@@ -184,43 +198,67 @@ size_t carve(const Geom &g, char *base, State &st) {
     return (void *)p;
   };
   const size_t BU = (size_t)g.B * g.U;
-  st.pages = (uint16_t *)take(BU * g.Hkv * (size_t)g.page_unit_elems * 2);
-  st.ledger = (uint8_t *)take(BU * g.Hkv * (size_t)g.ledger_unit_bytes);
-  st.tier = (uint8_t *)take(BU);
-  st.has_ledger = (uint8_t *)take(BU);
-  st.score = (float *)take(BU * 4);
-  st.routed = (int32_t *)take(BU * 4);
-  st.routed_nf = (int32_t *)take((size_t)g.B * 4);
-  st.routed_nq = (int32_t *)take((size_t)g.B * 4);
-  st.pack_list = (int32_t *)take(BU * 4);
-  st.pack_count = (int32_t *)take((size_t)g.B * 4);
-  st.promote_list = (int32_t *)take(BU * 4);
-  st.promote_count = (int32_t *)take((size_t)g.B * 4);
-  st.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
-  st.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
-  st.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
-  st.slist = (float *)take(BU * 4);
-  st.status = (int32_t *)take(16);
+  State sh;   // shared by every layer
+  memset(&sh, 0, sizeof sh);
+  sh.ledger = (uint8_t *)take((size_t)g.pool_slots * g.Hkv * (size_t)g.ledger_unit_bytes);
+  sh.pool_stack = (int32_t *)take((size_t)g.pool_slots * 4);
+  sh.pool_top = (int32_t *)take(16);
+  sh.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
+  sh.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
+  sh.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
+  for (int l = 0; l < L; ++l) {
+    State st = sh;
+    st.pages = (uint16_t *)take(BU * g.Hkv * (size_t)g.page_unit_elems * 2);
+    st.tier = (uint8_t *)take(BU);
+    st.has_ledger = (uint8_t *)take(BU);
+    st.score = (float *)take(BU * 4);
+    st.routed = (int32_t *)take(BU * 4);
+    st.routed_nf = (int32_t *)take((size_t)g.B * 4);
+    st.routed_nq = (int32_t *)take((size_t)g.B * 4);
+    st.pack_list = (int32_t *)take(BU * 4);
+    st.pack_count = (int32_t *)take((size_t)g.B * 4);
+    st.promote_list = (int32_t *)take(BU * 4);
+    st.promote_count = (int32_t *)take((size_t)g.B * 4);
+    st.free_list = (int32_t *)take(BU * 4);
+    st.free_count = (int32_t *)take((size_t)g.B * 4);
+    st.lslot = (int32_t *)take(BU * 4);
+    st.qslot = (int32_t *)take(BU * 4);
+    st.slist = (float *)take(BU * 4);
+    st.status = (int32_t *)take(16);
+    if (sts) sts[l] = st;
+  }
   return off;
 }
 
 int hip_err(hipError_t e) { return e == hipSuccess ? QKV_OK : QKV_EHIP; }
 
-StepInfo step_info(const qkv_cache *c) {
+StepInfo step_info(const qkv_cache *c, int layer = 0) {
   StepInfo si;
-  si.N = c->N;
-  si.has_sink = (c->g.n_sink > 0 && c->N > 0) ? 1 : 0;
+  const int N = c->Nl[layer];
+  si.N = N;
+  si.has_sink = (c->g.n_sink > 0 && N > 0) ? 1 : 0;
   si.r0 = c->r0;
-  si.r1 = c->N > c->g.n_sink ? unit_of(c->g, c->N - 1) : 0;
+  si.r1 = N > c->g.n_sink ? unit_of(c->g, N - 1) : 0;
   si.n_routed = c->routed;
   return si;
+}
+
+// every layer holds the same number of tokens (routing and snapshots need it)
+bool layers_in_step(const qkv_cache *c) {
+  for (int l = 1; l < c->L; ++l)
+    if (c->Nl[l] != c->Nl[0]) return false;
+  return true;
 }
 
 // rebuild what an import left pending, on the stream of the call that needs it
 int settle(qkv_cache *c, hipStream_t s) {
   if (!c->rebuild_pending) return QKV_OK;
-  const int rc = c->tok ? hip_err(tok_launch_rebuild(c->tg, c->ts, c->n_cmp, s))
-                        : hip_err(launch_rebuild(c->g, c->st, step_info(c), s));
+  int rc = QKV_OK;
+  if (c->tok) {
+    rc = hip_err(tok_launch_rebuild(c->tg, c->ts, c->n_cmp, s));
+  } else {
+    for (int l = 0; l < c->L && rc == QKV_OK; ++l) rc = hip_err(launch_rebuild(c->g, c->sts[l], step_info(c, l), s));
+  }
   if (rc == QKV_OK) c->rebuild_pending = false;
   return rc;
 }
@@ -243,6 +281,7 @@ Snapshot make_snapshot(const qkv_cache *c) {
   sn.v[SNAP_ROUTES] = c->routes;
   sn.v[SNAP_SINCE_ROUTE] = c->steps_since_route;
   sn.v[SNAP_LAST_EVENT] = c->last_event_N;
+  sn.v[SNAP_SPARE] = c->L;
   return sn;
 }
 
@@ -252,7 +291,7 @@ bool snapshot_fits(const qkv_cache *c, const Snapshot &sn) {
   const long long *v = sn.v;
   if (v[SNAP_TAG] != SNAP_TAG_VALUE || v[SNAP_POLICY] != c->cfg.policy || v[SNAP_BATCH] != c->cfg.batch ||
       v[SNAP_HQ] != c->cfg.n_q_heads || v[SNAP_HKV] != c->cfg.n_kv_heads || v[SNAP_D] != c->cfg.head_dim ||
-      v[SNAP_WINDOW] != c->cfg.window || v[SNAP_MAXCTX] != c->cfg.max_ctx)
+      v[SNAP_WINDOW] != c->cfg.window || v[SNAP_MAXCTX] != c->cfg.max_ctx || v[SNAP_SPARE] != c->L)
     return false;
   const long long N = v[SNAP_N];
   if (N < 0 || N > c->cfg.max_ctx || v[SNAP_STEPS] < 0 || v[SNAP_ROUTES] < 0 || v[SNAP_SINCE_ROUTE] < 0) return false;
@@ -314,8 +353,7 @@ size_t qkv_workspace_bytes(const qkv_config *cfg) {
   }
   Geom g;
   make_geom(cfg, g);
-  State st;
-  return carve(g, nullptr, st);
+  return carve(g, cfg->n_layers > 1 ? cfg->n_layers : 1, nullptr, nullptr);
 }
 
 }  // extern "C"
@@ -342,13 +380,18 @@ static int create_into(qkv_cache *c, const qkv_config *cfg, void *workspace, siz
     if (rc != QKV_OK || !fits) return rc != QKV_OK ? rc : QKV_EINVAL;   // (d = 128, G = 8 needs 32-token windows)
     rc = hip_err(transitions_shape(c->g));
     if (rc != QKV_OK) return rc;
-    need = carve(c->g, (char *)workspace, c->st);
+    c->L = cfg->n_layers > 1 ? cfg->n_layers : 1;
+    need = carve(c->g, c->L, (char *)workspace, c->sts);
   }
+  if (c->tok) c->L = 1;
   if (bytes < need) return QKV_ECAPACITY;
   c->ws = workspace;
   c->ws_bytes = need;
   c->r0 = 1;
-  return hip_err(launch_clear(workspace, need, stream));
+  c->ledger_ready = true;
+  rc = hip_err(launch_clear(workspace, need, stream));
+  if (rc != QKV_OK || c->tok) return rc;
+  return hip_err(launch_pool_init(c->g, c->sts[0], stream));
 }
 
 static void free_events(qkv_cache *c) {
@@ -449,23 +492,30 @@ int qkv_profile_read(qkv_cache *c, float *ms, int32_t n) {
   return QKV_OK;
 }
 
-int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv_stream stream) {
-  if (!c || !k || !v || n_tokens < 1) return QKV_EINVAL;
-  if ((long long)c->N + n_tokens > c->cfg.max_ctx) return QKV_ECAPACITY;
+int qkv_append_layer(qkv_cache *c, int32_t layer, const void *k, const void *v, int32_t n_tokens,
+                     qkv_stream stream) {
+  if (!c || !k || !v || n_tokens < 1 || layer < 0 || layer >= c->L) return QKV_EINVAL;
+  if ((long long)c->Nl[layer] + n_tokens > c->cfg.max_ctx) return QKV_ECAPACITY;
   int rc = settle(c, (hipStream_t)stream);
   if (rc != QKV_OK) return rc;
   rc = c->tok ? hip_err(tok_launch_append(c->tg, c->ts, (const uint16_t *)k, (const uint16_t *)v, n_tokens,
-                                              c->N, (hipStream_t)stream))
-                  : hip_err(launch_append(c->g, c->st, (const uint16_t *)k, (const uint16_t *)v, n_tokens, c->N,
-                                          (hipStream_t)stream));
+                                          c->N, (hipStream_t)stream))
+              : hip_err(launch_append(c->g, c->sts[layer], (const uint16_t *)k, (const uint16_t *)v, n_tokens,
+                                      c->Nl[layer], (hipStream_t)stream));
   if (rc != QKV_OK) return rc;
-  c->N += n_tokens;
+  c->Nl[layer] += n_tokens;
+  c->N = c->Nl[0];
   return QKV_OK;
 }
 
-int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, qkv_stream stream) {
-  if (!c || !q || !out) return QKV_EINVAL;
-  if (c->N < 1) return QKV_ESTATE;
+int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv_stream stream) {
+  return qkv_append_layer(c, 0, k, v, n_tokens, stream);
+}
+
+int qkv_decode_attend_layer(qkv_cache *c, int32_t layer, const void *q, float *out, float *mass_out,
+                            qkv_stream stream) {
+  if (!c || !q || !out || layer < 0 || layer >= c->L) return QKV_EINVAL;
+  if (c->Nl[layer] < 1) return QKV_ESTATE;
   if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->ev && c->ev_next < c->ev_n && c->ev_calls++ % c->ev_stride == 0) {
@@ -484,12 +534,16 @@ int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, 
     if (c->tg.omega > 1) c->tacc_dirty = true;
     c->steps_since_route++;
   } else {
-    rc = hip_err(launch_attend(c->g, c->st, step_info(c), (const uint16_t *)q, out, mass_out, (hipStream_t)stream,
-                               e0, e1));
+    rc = hip_err(launch_attend(c->g, c->sts[layer], step_info(c, layer), (const uint16_t *)q, out, mass_out,
+                               (hipStream_t)stream, e0, e1));
   }
   if (rc != QKV_OK) return rc;
-  c->steps++;
+  if (layer == c->L - 1) c->steps++;   // a decode step of the model ends with its last layer
   return QKV_OK;
+}
+
+int qkv_decode_attend(qkv_cache *c, const void *q, float *out, float *mass_out, qkv_stream stream) {
+  return qkv_decode_attend_layer(c, 0, q, out, mass_out, stream);
 }
 
 int qkv_prefill_score(qkv_cache *c, const void *q, int32_t n_queries, qkv_stream stream) {
@@ -564,14 +618,19 @@ int qkv_route(qkv_cache *c, qkv_stream stream) {
     return QKV_OK;
   }
   const Geom &g = c->g;
+  if (!layers_in_step(c)) return QKV_ESTATE;   // every layer must hold the same tokens
   // windows whose last position is older than the newest n_recent positions
   const long long limit = (long long)c->N - g.n_recent;
   const long long aged = limit > g.n_sink ? (limit - g.n_sink) / g.window : 0;
   const int a0 = c->r0;
   const int a1 = (int)(aged + 1 > a0 ? aged + 1 : a0);
   const int n_cand = c->routed + (a1 - a0);
-  int rc = hip_err(launch_route(g, c->st, step_info(c), a0, a1, n_cand, (hipStream_t)stream));
-  if (rc != QKV_OK) return rc;
+  // each layer ranks its own windows by its own scores (QEvict notes 4.2:
+  // one score per layer and window), with the same capacities
+  for (int l = 0; l < c->L; ++l) {
+    int rc = hip_err(launch_route(g, c->sts[l], step_info(c, l), a0, a1, n_cand, (hipStream_t)stream));
+    if (rc != QKV_OK) return rc;
+  }
   c->r0 = a1;
   const int kfq = g.k_full + g.k_quant;
   c->routed = n_cand < kfq ? n_cand : kfq;
@@ -631,21 +690,24 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
       default: return 0;
     }
   }
+  // window policy: one layer's array per layer, layer-major
   const Geom &g = c->g;
   const size_t BU = (size_t)g.B * g.U;
+  size_t per = 0;
   switch (what) {
     case QKV_EXPORT_TIERS:
-    case QKV_EXPORT_LEDGER: return BU;
-    case QKV_EXPORT_SCORES: return BU * 4;
+    case QKV_EXPORT_LEDGER: per = BU; break;
+    case QKV_EXPORT_SCORES: per = BU * 4; break;
     case QKV_EXPORT_KCODES:
-    case QKV_EXPORT_VCODES: return BU * g.Hkv * (size_t)(g.window * g.d * g.bits / 8);
-    case QKV_EXPORT_KPARAMS: return BU * g.Hkv * (size_t)g.d * 2 * 2;
-    case QKV_EXPORT_VPARAMS: return BU * g.Hkv * (size_t)g.window * (g.d / g.group) * 2 * 2;
+    case QKV_EXPORT_VCODES: per = BU * g.Hkv * (size_t)(g.window * g.d * g.bits / 8); break;
+    case QKV_EXPORT_KPARAMS: per = BU * g.Hkv * (size_t)g.d * 2 * 2; break;
+    case QKV_EXPORT_VPARAMS: per = BU * g.Hkv * (size_t)g.window * (g.d / g.group) * 2 * 2; break;
     case QKV_EXPORT_KEYS:
-    case QKV_EXPORT_VALUES: return (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2;
-    case QKV_EXPORT_ROUTED: return BU * 4;
+    case QKV_EXPORT_VALUES: per = (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2; break;
+    case QKV_EXPORT_ROUTED: per = BU * 4; break;
     default: return 0;
   }
+  return per * (size_t)c->L;
 }
 
 int qkv_export(const qkv_cache *cc, int32_t what, void *dst, size_t bytes, qkv_stream stream) {
@@ -656,7 +718,10 @@ int qkv_export(const qkv_cache *cc, int32_t what, void *dst, size_t bytes, qkv_s
   // handle is const to the caller; its pending rebuild is not caller state)
   qkv_cache *c = const_cast<qkv_cache *>(cc);
   if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
-  if (what == QKV_EXPORT_STATE) return hip_err(launch_write_snapshot(make_snapshot(c), dst, (hipStream_t)stream));
+  if (what == QKV_EXPORT_STATE) {
+    if (!layers_in_step(c)) return QKV_ESTATE;
+    return hip_err(launch_write_snapshot(make_snapshot(c), dst, (hipStream_t)stream));
+  }
   if (c->tok && what == QKV_EXPORT_ROUTED)
     return hip_err(tok_launch_export_routed(c->tg, c->ts, c->n_cmp, dst, (hipStream_t)stream));
   if (c->tok) {
@@ -668,7 +733,13 @@ int qkv_export(const qkv_cache *cc, int32_t what, void *dst, size_t bytes, qkv_s
     }
     return hip_err(tok_launch_export(c->tg, c->ts, what, dst, (hipStream_t)stream));
   }
-  return hip_err(launch_export(c->g, c->st, step_info(c), what, dst, (hipStream_t)stream));
+  const size_t per = need / c->L;
+  for (int l = 0; l < c->L; ++l) {
+    const int rc = hip_err(launch_export(c->g, c->sts[l], step_info(c, l), what, (char *)dst + per * l,
+                                         (hipStream_t)stream));
+    if (rc != QKV_OK) return rc;
+  }
+  return QKV_OK;
 }
 
 int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_stream stream) {
@@ -682,6 +753,7 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
     if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;
     if (!snapshot_fits(c, sn)) return QKV_EINVAL;
     c->N = (int)sn.v[SNAP_N];
+    for (int l = 0; l < c->L; ++l) c->Nl[l] = c->N;
     c->steps = sn.v[SNAP_STEPS];
     c->routes = sn.v[SNAP_ROUTES];
     c->steps_since_route = (int)sn.v[SNAP_SINCE_ROUTE];
@@ -719,8 +791,47 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
         if (u < 0 || u >= c->g.U) return QKV_EINVAL;
     }
   }
-  const int rc = c->tok ? hip_err(tok_launch_import(c->tg, c->ts, what, src, s))
-                        : hip_err(launch_import(c->g, c->st, what, src, s));
+  if (!c->tok && what == QKV_EXPORT_LEDGER) {
+    // ledger flags of every layer: windows holding codes get pool slots in
+    // order (layer, sequence, window), the rest of the pool is free
+    std::vector<uint8_t> f(need);
+    if (hipMemcpyAsync(f.data(), src, need, hipMemcpyDeviceToHost, s) != hipSuccess) return QKV_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;
+    const size_t BU = (size_t)c->g.B * c->g.U;
+    std::vector<int32_t> slot(need, 0);
+    int next = 0;
+    for (size_t i = 0; i < need; ++i)
+      if (f[i]) slot[i] = ++next;
+    if (next > c->g.pool_slots) return QKV_EINVAL;   // more ledgers than the pool holds
+    std::vector<int32_t> stack(c->g.pool_slots);
+    for (int i = next; i < c->g.pool_slots; ++i) stack[i - next] = i;
+    const int32_t top = c->g.pool_slots - next;
+    for (int l = 0; l < c->L; ++l) {
+      const State &st = c->sts[l];
+      if (hipMemcpyAsync(st.has_ledger, (const uint8_t *)src + BU * l, BU, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+          hipMemcpyAsync(st.lslot, slot.data() + BU * l, BU * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+        return QKV_EHIP;
+    }
+    const State &st0 = c->sts[0];
+    if (hipMemcpyAsync(st0.pool_stack, stack.data(), stack.size() * 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(st0.pool_top, &top, 4, hipMemcpyHostToDevice, s) != hipSuccess)
+      return QKV_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;   // the host vectors go out of scope
+    c->ledger_ready = true;
+    c->rebuild_pending = true;
+    return QKV_OK;
+  }
+  if (!c->tok && (what == QKV_EXPORT_KCODES || what == QKV_EXPORT_VCODES || what == QKV_EXPORT_KPARAMS ||
+                  what == QKV_EXPORT_VPARAMS) && !c->ledger_ready)
+    return QKV_ESTATE;   // codes go to the slots the ledger flags assign
+  int rc = QKV_OK;
+  if (c->tok) {
+    rc = hip_err(tok_launch_import(c->tg, c->ts, what, src, s));
+  } else {
+    const size_t per = need / c->L;
+    for (int l = 0; l < c->L && rc == QKV_OK; ++l)
+      rc = hip_err(launch_import(c->g, c->sts[l], what, (const char *)src + per * l, s));
+  }
   if (rc != QKV_OK) return rc;
   if (c->tok && what == QKV_EXPORT_SCORES) c->tacc_dirty = false;
   c->rebuild_pending = true;
@@ -731,6 +842,7 @@ int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
   if (!c || !value) return QKV_EINVAL;
   switch (what) {
     case QKV_INFO_TOKENS: *value = c->N; return QKV_OK;
+    case QKV_INFO_LAYERS: *value = c->L; return QKV_OK;
     case QKV_INFO_UNITS: *value = c->tok ? c->tg.T : c->g.U; return QKV_OK;
     case QKV_INFO_STEPS: *value = c->steps; return QKV_OK;
     case QKV_INFO_ROUTES: *value = c->routes; return QKV_OK;
@@ -743,11 +855,15 @@ int qkv_info(const qkv_cache *c, int32_t what, int64_t *value) {
 
 int qkv_status(qkv_cache *c, qkv_stream stream) {
   if (!c) return QKV_EINVAL;
-  int32_t flag = 0;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return QKV_EHIP;
-  if (hipMemcpy(&flag, c->tok ? c->ts.status : c->st.status, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
-    return QKV_EHIP;
-  return flag ? QKV_ERANGE : QKV_OK;
+  for (int l = 0; l < c->L; ++l) {
+    int32_t flag = 0;
+    if (hipMemcpy(&flag, c->tok ? c->ts.status : c->sts[l].status, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
+      return QKV_EHIP;
+    if (flag == QKV_ECAPACITY) return QKV_ECAPACITY;
+    if (flag) return QKV_ERANGE;
+  }
+  return QKV_OK;
 }
 
 }  // extern "C"

@@ -7,9 +7,14 @@
 //                  token slots; K tiles and V tiles are stored in the order
 //                  the matrix-core operands are read (see k_tile_index /
 //                  v_tile_index), so each wavefront load is one contiguous block.
-//   ledger   u8    [B][U][Hkv][ledger_unit_bytes]  persistent quantized codes
-//                  of every window ever demoted (pack-once ledger).
-//   tier, has_ledger u8 [B][U]; score f32 [B][U]
+//   ledger   u8    [P][Hkv][ledger_unit_bytes]  pool of P ledger slots holding the
+//                  persistent quantized codes of every window demoted and not
+//                  evicted since (pack-once ledger); one pool for every layer and
+//                  sequence of the cache, slots handed out and returned at routing
+//                  events through a free-slot stack.  A layer's sequence never holds
+//                  more than K_f + K_q ledgers (only Full and Quantized windows keep
+//                  one), so P = layers * B * min(K_f + K_q, U) never runs out.
+//   tier, has_ledger u8 [B][U]; score f32 [B][U]; lslot i32 [B][U] (pool slot + 1, 0: none)
 //   routed   i32   [B][U]  ranked unit ids: full-precision windows first, then
 //                  quantized windows (rank order); counts in routed_nf/nq.
 //   pack/promote lists i32 [B][U] + counts; attention partials; mass partials.
@@ -48,6 +53,7 @@ struct Geom {
   int tile_vparam_bytes; // 4 token quads * d/32 groups * 16 B
   int tile_block_bytes;
   int tr_per_seq;        // workgroups per sequence of the pack/promote launch (one resident round)
+  int pool_slots;        // ledger-pool slots of the cache (every layer)
 };
 
 struct State {
@@ -70,6 +76,12 @@ struct State {
                         // recent): the per-step merge updates these; score[] is brought up
                         // to date from them by each routing event and before an export
   int32_t *status;   // [4] latched device errors
+  int32_t *lslot;       // [B][U] ledger-pool slot + 1 of each window holding codes (0: none)
+  int32_t *qslot;       // [B][U] pool slot of ranked entry r (its quantized part), set at each event
+  int32_t *free_list;   // [B][U] windows whose ledger the last routing event released
+  int32_t *free_count;  // [B]
+  int32_t *pool_stack;  // [pool_slots] free slots (shared by every layer)
+  int32_t *pool_top;    // [1] free slots on the stack (shared by every layer)
 };
 
 // Per-step scalars the host knows without reading the device.
@@ -181,8 +193,8 @@ __host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int w
 __host__ __device__ inline size_t page_offset(const Geom &g, int b, int u, int h) {
   return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.page_unit_elems;
 }
-__host__ __device__ inline size_t ledger_offset(const Geom &g, int b, int u, int h) {
-  return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.ledger_unit_bytes;
+__host__ __device__ inline size_t ledger_slot_offset(const Geom &g, int slot, int h) {
+  return ((size_t)slot * g.Hkv + h) * (size_t)g.ledger_unit_bytes;
 }
 
 // bf16 helpers
@@ -295,6 +307,8 @@ constexpr long long SNAP_TAG_VALUE = 0x514B5631;   // "QKV1"
 hipError_t launch_write_snapshot(const Snapshot &snap, void *dst, hipStream_t s);
 hipError_t launch_import(const Geom &g, const State &st, int what, const void *src, hipStream_t s);
 hipError_t launch_rebuild(const Geom &g, const State &st, const StepInfo &si, hipStream_t s);
+hipError_t launch_pool_init(const Geom &g, const State &st, hipStream_t s);
+constexpr int MAX_LAYERS = 128;   // layers of one cache
 hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
                          int pos0, hipStream_t s);

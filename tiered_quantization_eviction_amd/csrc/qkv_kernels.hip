@@ -164,6 +164,11 @@ __device__ __forceinline__ int ids_fetch(const Ctx &c, int e0) {
   const int r = min(max(e0 + (c.lane & 3) - c.L->s0, 0), c.g->U - 1);
   return c.st->routed[(size_t)c.b * c.g->U + r];
 }
+// the same for quantized entries: their ledger-pool slots (clamped into the pool)
+__device__ __forceinline__ int slots_fetch(const Ctx &c, int e0) {
+  const int r = min(max(e0 + (c.lane & 3) - c.L->s0, 0), c.g->U - 1);
+  return min(max(c.st->qslot[(size_t)c.b * c.g->U + r], 0), c.g->pool_slots - 1);
+}
 
 // Mass partials of up to 4 units of a block in one store: lanes of row q
 // (lq == q) and column h < G write unit slot q's (rho, m) when ok[q]; all
@@ -407,7 +412,7 @@ __device__ __forceinline__ half4 value_codes(const QBuf &buf, int j, int ct) {
 }
 struct QBlock {
   int e, nwin;
-  int u[QT];        // window slots; spare slots repeat slot 0
+  int u[QT];        // ledger-pool slots of the block's windows; spare slots repeat slot 0
 };
 
 // window slot and tile-in-window of block tile j
@@ -438,7 +443,7 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     const int tj = j - w * tpw;
     // both candidates are fixed indices: a run-time index would put u[] in scratch memory
     const int uw = tpw == 1 ? qb.u[j] : qb.u[j >> 1];
-    const uint8_t *Lb = c.st->ledger + ledger_offset(g, c.b, uw, c.h);
+    const uint8_t *Lb = c.st->ledger + ledger_slot_offset(g, uw, c.h);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
     if (DPL == 8) {
       buf.code[j] = ld_stream16(T + c.lane * 32);
@@ -452,7 +457,7 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     buf.vp[j] = ld_stream4(T + g.tile_kcode_bytes + g.tile_vcode_bytes + 4 * vl);
   }
 #pragma unroll
-  for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_offset(g, c.b, qb.u[w], c.h) + kl * 8);
+  for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_slot_offset(g, qb.u[w], c.h) + kl * 8);
 }
 
 template <int D, int GP, int BITS>
@@ -643,18 +648,18 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   // loads on every trip, and the tail reads nothing past the run
   QBlock k0, k1;
   QBuf b0, b1;
-  const int ids0 = ids_fetch(c, ea);
-  int ids1 = ids_fetch(c, ea + min(1, n_blocks - 1) * per);
+  const int ids0 = slots_fetch(c, ea);
+  int ids1 = slots_fetch(c, ea + min(1, n_blocks - 1) * per);
   qblock_make(c, ea, eb, 0, ids0, k0);
   quant_load<D, BITS>(c, k0, b0);
   // steady state: two blocks per trip, the following block always in flight
   int i = 0;
   for (; i + 2 < n_blocks; i += 2) {
-    const int ids2 = ids_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
+    const int ids2 = slots_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
     qblock_make(c, ea, eb, i + 1, ids1, k1);
     quant_load<D, BITS>(c, k1, b1);
     quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
-    ids1 = ids_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
+    ids1 = slots_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
     qblock_make(c, ea, eb, i + 2, ids2, k0);
     quant_load<D, BITS>(c, k0, b0);
     quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
@@ -1048,7 +1053,7 @@ __device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
 
 __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, StepInfo si, int a0, int a1, int npow) {
   extern __shared__ unsigned long long keys[];
-  __shared__ int n_pack, n_prom;
+  __shared__ int n_pack, n_prom, n_free;
   const int b = blockIdx.x;
   const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
   const int RC = nF + nQ;
@@ -1056,6 +1061,7 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
   if (threadIdx.x == 0) {
     n_pack = 0;
     n_prom = 0;
+    n_free = 0;
   }
   // Candidate i sits at entry s0 + i of the list so far (the ranked windows,
   // then the windows aged since the last event, which lead the recent ones):
@@ -1095,7 +1101,11 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
       const int p = atomicAdd(&n_prom, 1);
       st.promote_list[b * g.U + p] = u;
     }
-    if (nt == T_EVICTED) st.has_ledger[idx] = 0;
+    if (nt == T_EVICTED && st.has_ledger[idx]) {   // its ledger slot goes back to the pool
+      const int p = atomicAdd(&n_free, 1);
+      st.free_list[b * g.U + p] = u;
+      st.has_ledger[idx] = 0;
+    }
     st.tier[idx] = nt;
     if (r < KFQ) st.routed[b * g.U + r] = u;
   }
@@ -1106,6 +1116,7 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     st.routed_nq[b] = nQ2;
     st.pack_count[b] = n_pack;
     st.promote_count[b] = n_prom;
+    st.free_count[b] = n_free;
   }
   // list-order scores of the new list: the sink's is unchanged, the ranked
   // windows' are in their sorted keys, the recent windows' were written back
@@ -1131,6 +1142,59 @@ __global__ __launch_bounds__(256) void slist_sync_kernel(Geom g, State st, StepI
   const EntryList L = make_list(g, st, si, b);
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e < L.count()) st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] = st.slist[b * g.U + e];
+}
+
+// Ledger pool: the slots a routing event released go back on the free-slot
+// stack in one kernel, and the windows packed for the first time take slots
+// in the next, so pushes and pops never overlap.  Every (layer, sequence)
+// holds at most K_f + K_q slots after its event and the pool has that many
+// for each, so a pop always finds a slot (a failed one is latched, never
+// followed by an out-of-range access).
+__global__ __launch_bounds__(256) void pool_free_kernel(Geom g, State st) {
+  const int b = blockIdx.x;
+  const int n = st.free_count[b];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int u = st.free_list[b * g.U + i];
+    const int slot = st.lslot[b * g.U + u] - 1;
+    st.lslot[b * g.U + u] = 0;
+    if (slot < 0) continue;
+    const int pos = atomicAdd(st.pool_top, 1);
+    if (pos >= 0 && pos < g.pool_slots)
+      st.pool_stack[pos] = slot;
+    else
+      st.status[0] = QKV_ECAPACITY;
+  }
+}
+
+// ... and the ranked list's quantized entries get their slots (qslot), which
+// the attention kernel reads instead of the window ids
+__global__ __launch_bounds__(256) void pool_alloc_kernel(Geom g, State st) {
+  const int b = blockIdx.x;
+  const int n = st.pack_count[b];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int u = st.pack_list[b * g.U + i];
+    const int pos = atomicSub(st.pool_top, 1) - 1;
+    int slot = -1;
+    if (pos >= 0 && pos < g.pool_slots)
+      slot = st.pool_stack[pos];
+    else
+      st.status[0] = QKV_ECAPACITY;
+    st.lslot[b * g.U + u] = slot + 1;
+  }
+  __syncthreads();
+  const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
+  for (int r = nF + threadIdx.x; r < nF + nQ; r += blockDim.x)
+    st.qslot[b * g.U + r] = st.lslot[b * g.U + st.routed[b * g.U + r]] - 1;
+}
+
+__global__ void pool_init_kernel(int32_t *stack, int32_t *top, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) stack[i] = i;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *top = n;
+}
+
+hipError_t launch_pool_init(const Geom &g, const State &st, hipStream_t s) {
+  hipLaunchKernelGGL(pool_init_kernel, dim3(64), dim3(256), 0, s, st.pool_stack, st.pool_top, g.pool_slots);
+  return hipGetLastError();
 }
 
 // pack (first demotion) and promote (quantized -> full) of listed windows;
@@ -1176,7 +1240,9 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
     const int u = u_next;
     u_next = item_unit(it + per_seq);
     uint16_t *pg = st.pages + page_offset(g, b, u, h);
-    uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+    const int slot = st.lslot[b * g.U + u] - 1;
+    if (slot < 0) continue;   // no slot (a latched pool error): nothing to pack or promote
+    uint8_t *Lb = st.ledger + ledger_slot_offset(g, slot, h);
     half_t *kparam = (half_t *)Lb;
     if (pack) {
       // 1. tiles -> LDS in logical order (all loads issued before the stores)
@@ -1334,6 +1400,10 @@ hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int 
                      a1, npow);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pool_free_kernel, dim3(g.B), dim3(256), 0, s, g, st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(pool_alloc_kernel, dim3(g.B), dim3(256), 0, s, g, st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int per_seq = g.tr_per_seq > 0 ? g.tr_per_seq : 128;
   const dim3 tg(g.B * per_seq), tb(TR_THREADS);
   if (g.d == 128 && g.bits == 4)
@@ -1557,8 +1627,9 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
       const int u = (int)((blk / g.Hkv) % g.U);
       const int b = (int)(blk / ((size_t)g.Hkv * g.U));
       uint32_t val = 0;
-      if (st.has_ledger[b * g.U + u]) {
-        const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+      const int slot = st.lslot[b * g.U + u] - 1;
+      if (st.has_ledger[b * g.U + u] && slot >= 0) {
+        const uint8_t *Lb = st.ledger + ledger_slot_offset(g, slot, h);
         for (int k = 0; k < per_byte; ++k) {
           const int e = byte * per_byte + k;
           int t, c, dw, sh;
@@ -1587,8 +1658,9 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
       const int u = (int)((blk / g.Hkv) % g.U);
       const int b = (int)(blk / ((size_t)g.Hkv * g.U));
       uint16_t val = 0;
-      if (st.has_ledger[b * g.U + u]) {
-        const uint8_t *Lb = st.ledger + ledger_offset(g, b, u, h);
+      const int slot = st.lslot[b * g.U + u] - 1;
+      if (st.has_ledger[b * g.U + u] && slot >= 0) {
+        const uint8_t *Lb = st.ledger + ledger_slot_offset(g, slot, h);
         if (what == QKV_EXPORT_KPARAMS) {
           const int c = k / 2, which = k % 2;
           val = ((const uint16_t *)Lb)[which * D + c];
@@ -1678,7 +1750,9 @@ __global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what,
         const int e = keys ? c * W + tt : tt * D + c;
         word |= (uint32_t)((cs[e / per_byte] >> (bits * (e % per_byte))) & ((1 << bits) - 1)) << (bits * p);
       }
-      uint32_t *tc = (uint32_t *)(st.ledger + blk * g.ledger_unit_bytes + g.kparam_bytes +
+      const int slot = st.lslot[blk / g.Hkv] - 1;   // blk = (b * U + u) * Hkv + h
+      if (slot < 0) continue;
+      uint32_t *tc = (uint32_t *)(st.ledger + ledger_slot_offset(g, slot, (int)(blk % g.Hkv)) + g.kparam_bytes +
                                   (size_t)tile * g.tile_block_bytes);
       tc[l * dpl + w] = word;
     }
@@ -1687,7 +1761,9 @@ __global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what,
     for (size_t it = i0; it < n_units * D * 2; it += stride) {
       const size_t blk = it / (D * 2);
       const int k = (int)(it % (D * 2)), c = k / 2, which = k % 2;
-      ((uint16_t *)(st.ledger + blk * g.ledger_unit_bytes))[which * D + c] = ps[it];
+      const int slot = st.lslot[blk / g.Hkv] - 1;
+      if (slot < 0) continue;
+      ((uint16_t *)(st.ledger + ledger_slot_offset(g, slot, (int)(blk % g.Hkv))))[which * D + c] = ps[it];
     }
   } else if (what == QKV_EXPORT_VPARAMS) {
     const uint16_t *ps = (const uint16_t *)src;   // [blk][W][D/32][2]
@@ -1695,7 +1771,9 @@ __global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what,
     for (size_t it = i0; it < n_units * per; it += stride) {
       const size_t blk = it / per;
       const int k = (int)(it % per), which = k % 2, grp = (k / 2) % (D / 32), t = k / 2 / (D / 32);
-      uint16_t *vp = (uint16_t *)(st.ledger + blk * g.ledger_unit_bytes + g.kparam_bytes +
+      const int slot = st.lslot[blk / g.Hkv] - 1;
+      if (slot < 0) continue;
+      uint16_t *vp = (uint16_t *)(st.ledger + ledger_slot_offset(g, slot, (int)(blk % g.Hkv)) + g.kparam_bytes +
                                   (size_t)(t / TS) * g.tile_block_bytes + g.tile_kcode_bytes + g.tile_vcode_bytes);
       vp[vparam_index(g, t % TS, grp, which)] = ps[it];
     }
@@ -1723,7 +1801,6 @@ hipError_t launch_import(const Geom &g, const State &st, int what, const void *s
   const size_t BU = (size_t)g.B * g.U;
   switch (what) {
     case QKV_EXPORT_TIERS: return hipMemcpyAsync(st.tier, src, BU, hipMemcpyDeviceToDevice, s);
-    case QKV_EXPORT_LEDGER: return hipMemcpyAsync(st.has_ledger, src, BU, hipMemcpyDeviceToDevice, s);
     case QKV_EXPORT_SCORES: return hipMemcpyAsync(st.score, src, BU * sizeof(float), hipMemcpyDeviceToDevice, s);
     case QKV_EXPORT_ROUTED: return hipMemcpyAsync(st.routed, src, BU * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
     default: break;
@@ -1742,6 +1819,8 @@ __global__ __launch_bounds__(256) void rebuild_kernel(Geom g, State st, StepInfo
     st.routed_nf[b] = L.nF;
     st.routed_nq[b] = L.nQ;
   }
+  for (int r = L.nF + blockIdx.x * blockDim.x + threadIdx.x; r < L.nF + L.nQ; r += gridDim.x * blockDim.x)
+    st.qslot[(size_t)b * g.U + r] = st.lslot[(size_t)b * g.U + min(max(st.routed[(size_t)b * g.U + r], 0), g.U - 1)] - 1;
   const int E = L.count();
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < g.U; e += gridDim.x * blockDim.x) {
     const int u = min(max(entry_unit(L, st.routed + (size_t)b * g.U, e), 0), g.U - 1);
