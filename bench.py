@@ -63,7 +63,8 @@ KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
-WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O, W.TINY)}
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.DRIFT_L32, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O,
+                                  W.TINY)}
 CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",
@@ -80,6 +81,11 @@ def describe(cfg, steps, first=0):
                   "before the timed steps" if sw < first else "after the timed steps")
         return ("QEvict three-tier attention drift: " + head + ", window=Omega=16, 5 sinks + 64 recent, "
                 f"Kf=204 BF16 + Kq=612 INT2 windows (group 32); query switch A->B at step {sw} ({inside})")
+    if cfg.policy == W.POLICY_QEVICT and cfg.layers > 1:
+        return (f"QEvict three-tier, {cfg.layers} layers in one cache ({cfg.name}): " + head +
+                f" per layer, window={cfg.window} Omega={cfg.omega}, {cfg.n_sink} sinks + {cfg.n_recent} recent, "
+                f"Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} INT{cfg.quant_bits} windows per layer from a byte budget "
+                f"over all layers, one ledger pool; inputs of each layer drawn on the GPU")
     if cfg.policy == W.POLICY_QEVICT:
         return (f"QEvict three-tier ({cfg.name}): " + head + f", window={cfg.window} Omega={cfg.omega}, "
                 f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} "
@@ -231,6 +237,90 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
             "wall": wall, "attend_ms": attend_ms, "route_ms": route_ms,
             "firsts": [f[0].cpu().numpy() for f in firsts], "splits": cache.info("splits"),
             "status": cache.status()}
+
+
+def layered_capacities(cfg):
+    """K_f and K_q per layer that a byte budget over all layers buys (the
+    library's planner, QEvict notes 4.3 Eq.(3)): the budget is `layers` times
+    the bytes one layer of the single-layer workload holds, and q is the share
+    its quantized windows take of the history budget."""
+    from tiered_quantization_eviction_amd import make_config, plan_capacities
+    L, d, w, h = cfg.layers, cfg.head_dim, cfg.window, cfg.n_kv_heads
+    per_token = 2 * h * d * 2                                   # one layer, K and V, BF16
+    quant = cfg.k_quant * h * quant_window_bytes(cfg)
+    hist = cfg.k_full * w * per_token + quant
+    budget = L * ((cfg.n_sink + cfg.n_recent) * per_token + hist)
+    kf, kq = plan_capacities(make_config(cfg), budget, quant / hist, L)
+    return kf, kq, budget, quant / hist
+
+
+def run_gpu_layers(cfg, steps, warmup, n_splits):
+    """The drift layer `cfg.layers` times in one cache, inputs drawn on the GPU
+    per layer: per decode step every layer appends its token and attends, and
+    every Omega steps one routing call ranks every layer.  Phases as in
+    run_gpu; attention launches timed with events every PROFILE_STRIDE-th
+    call (calls of all layers counted)."""
+    import torch
+    from tiered_quantization_eviction_amd import Cache, make_config
+    L, P, om = cfg.layers, cfg.prefill, cfg.omega
+    cache = Cache(make_config(cfg, n_splits=n_splits, n_layers=L))
+    dec = []
+    host0 = None
+    for l in range(L):
+        K, V, Q = W.drift_inputs_torch(cfg, l)
+        cache.append(K[:, :, :P].contiguous(), V[:, :, :P].contiguous(), layer=l)
+        k_dec = K[:, :, P:].permute(2, 0, 1, 3).contiguous()[:, :, :, None, :]     # [S, B, Hkv, 1, d]
+        v_dec = V[:, :, P:].permute(2, 0, 1, 3).contiguous()[:, :, :, None, :]
+        q_dec = Q.permute(1, 0, 2, 3).contiguous()                                  # [S, B, Hq, d]
+        dec.append((k_dec, v_dec, q_dec))
+        if l == 0:   # the oracle leg follows sequence 0 of layer 0
+            host0 = (K[:1].cpu().numpy().view(np.uint16), V[:1].cpu().numpy().view(np.uint16),
+                     Q[:1].cpu().numpy().view(np.uint16))
+        del K, V, Q
+        torch.cuda.synchronize()
+    out = torch.zeros((L, cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    ev_route = []
+
+    def loop(s0, n, firsts=None):
+        for s in range(s0, s0 + n):
+            for l, (kd, vd, qd) in enumerate(dec):
+                cache.append(kd[s], vd[s], layer=l)
+                cache.decode_attend(qd[s], out[l], layer=l)
+            if firsts is not None and len(firsts) < 4:
+                firsts.append(out[0].clone())
+            if (s + 1) % om == 0:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                cache.route()
+                e1.record()
+                ev_route.append((s, e0, e1))
+
+    firsts = []
+    cache.profile_start(om * L, 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop(0, om, firsts)
+    torch.cuda.synchronize()
+    pre_wall = time.perf_counter() - t0
+    pre_att = cache.profile_read(om * L)
+    pre_route = [e0.elapsed_time(e1) for _, e0, e1 in ev_route]
+    ev_route.clear()
+    loop(om, warmup)
+    s0 = om + warmup
+    n_prof = (steps * L + PROFILE_STRIDE - 1) // PROFILE_STRIDE
+    cache.profile_start(n_prof, PROFILE_STRIDE)
+    torch.cuda.synchronize()
+    ev_route.clear()
+    t0 = time.perf_counter()
+    loop(s0, steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attend_ms = cache.profile_read(n_prof)
+    route_ms = [e0.elapsed_time(e1) for _, e0, e1 in ev_route]
+    return {"pre_wall": pre_wall, "pre_attend_ms": pre_att, "pre_route_ms": pre_route, "first": s0,
+            "wall": wall, "attend_ms": attend_ms, "route_ms": route_ms,
+            "firsts": [f[0].cpu().numpy() for f in firsts], "splits": cache.info("splits"),
+            "status": cache.status(), "host0": host0}
 
 
 # token modes (H2O, HqeKV): every token is a unit, decisions per (sequence, KV head)
@@ -493,11 +583,20 @@ def main():
     warmup = 0 if token_mode else max(0, min(a.warmup, cfg.steps - cfg.omega - 1))
     lead = 0 if token_mode else cfg.omega + warmup       # decode steps before the timed ones
     steps = max(1, min(a.steps, cfg.steps - lead))
-    log(f"bench: generating inputs ({cfg.batch} x {cfg.total_tokens} tokens)")
-    t = time.perf_counter()
-    K, V, Q = make_inputs(cfg)
-    log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running "
-        f"{'a counting pass' if token_mode else f'{cfg.omega} pre-route + {warmup} warm-up'} + {steps} timed steps")
+    layered = cfg.layers > 1
+    if layered:
+        kf, kq, budget, qshare = layered_capacities(cfg)
+        cfg = cfg.replace(k_full=kf, k_quant=kq)
+        log(f"bench: {cfg.layers} layers; a budget of {budget / 2 ** 30:.2f} GiB per sequence (q = {qshare:.3f}) "
+            f"buys K_f = {kf}, K_q = {kq} per layer; inputs drawn on the GPU per layer")
+        K = V = Q = None
+    else:
+        log(f"bench: generating inputs ({cfg.batch} x {cfg.total_tokens} tokens)")
+        t = time.perf_counter()
+        K, V, Q = make_inputs(cfg)
+        log(f"bench: inputs ready in {time.perf_counter() - t:.1f}s; running "
+            f"{'a counting pass' if token_mode else f'{cfg.omega} pre-route + {warmup} warm-up'} + "
+            f"{steps} timed steps")
     firsts = []
     pre = None
     if token_mode:
@@ -506,13 +605,18 @@ def main():
         wall, attend_ms, abytes, splits, status, route_ms = run_gpu_tok(cfg, K, V, Q, QP, steps, a.splits)
         first = 0
     else:
-        r = run_gpu(cfg, K, V, Q, steps, warmup, a.splits)
+        r = (run_gpu_layers(cfg, steps, warmup, a.splits) if layered else
+             run_gpu(cfg, K, V, Q, steps, warmup, a.splits))
+        if layered:
+            K, V, Q = r["host0"]
         wall, attend_ms, firsts, splits, status, route_ms = (r["wall"], r["attend_ms"], r["firsts"], r["splits"],
                                                              r["status"], r["route_ms"])
         first = r["first"]
+        # per attention launch (one layer); a decode step holds `layers` of them
         sched_bytes = attend_bytes(cfg, live_schedule(cfg, first + steps))
-        abytes = sched_bytes[first:]
-        pre_us, pre_b, pre_gbps = _phase(sched_bytes[:cfg.omega], r["pre_attend_ms"])
+        launch_bytes = [b for b in sched_bytes for _ in range(cfg.layers)]
+        abytes = launch_bytes[first * cfg.layers:]
+        pre_us, pre_b, pre_gbps = _phase(launch_bytes[:cfg.omega * cfg.layers], r["pre_attend_ms"])
         pre = {"steps": cfg.omega, "ms_per_step": r["pre_wall"] * 1e3 / cfg.omega,
                "tokens_per_s": cfg.batch * cfg.omega / r["pre_wall"],
                "attention_us": pre_us, "algorithmic_bytes_per_launch": pre_b, "attention_GBps": pre_gbps,
@@ -535,6 +639,11 @@ def main():
         n_cpu = min(a.cpu_steps, cfg.steps)
         log(f"bench: oracle baseline on {n_cpu} steps of {a.cpu_seqs} sequences")
         cpu, worst = cpu_baseline(cfg, K, V, Q, a.cpu_seqs, n_cpu, firsts)
+    elif not a.no_cpu and layered:
+        log(f"bench: oracle baseline on layer 0, sequence 0, up to {CPU_BUDGET_S:.0f} s of decode steps")
+        cpu, worst = cpu_baseline(cfg, K, V, Q, 1, cfg.steps, firsts, budget_s=CPU_BUDGET_S)
+        cpu["value"] /= cfg.layers     # a decode step of the model is every layer's
+        cpu["sample"] = "layer 0 of " + str(cfg.layers) + ", " + cpu["sample"] + "; tokens/s divided by the layers"
     elif not a.no_cpu and token_mode:
         log(f"bench: oracle baseline on sequence 0, up to {CPU_BUDGET_S:.0f} s of decode steps")
         cpu = cpu_baseline_tok(cfg, K, V, Q, QP, CPU_BUDGET_S)
@@ -553,7 +662,8 @@ def main():
               "whole_loop_kv_GBps": kv_bytes / wall / 1e9}
     res = {
         "metric": "decode tokens/s + KV-read GB/s (% of HBM peak), 32K ctx, batch 16, 1 layer"
-                  if a.workload == "drift" else "decode tokens/s + KV-read GB/s (% of HBM peak), 1 layer",
+                  if a.workload == "drift" else
+                  f"decode tokens/s + KV-read GB/s (% of HBM peak), {cfg.layers} layer{'s' if cfg.layers > 1 else ''}",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,

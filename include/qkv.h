@@ -405,6 +405,9 @@ int qkv_status(qkv_cache *cache, qkv_stream stream);
 int qkv_quantize_status(qkv_stream stream);
 
 const char *qkv_strerror(int code);
+/* The HIP runtime's description of the error behind the calling thread's
+ * most recent QKV_EHIP ("no error" if there was none). */
+const char *qkv_hip_error_detail(void);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,8 @@ SNAPSHOT = {0: ("state", "tiers", "scores", "ledger", "routed", "kcodes", "vcode
 class QkvError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
-        super().__init__(f"{what}: {_lib().qkv_strerror(code).decode()} ({code})")
+        detail = f" [{_lib().qkv_hip_error_detail().decode()}]" if code == EHIP else ""
+        super().__init__(f"{what}: {_lib().qkv_strerror(code).decode()} ({code}){detail}")
 
 
 class QkvConfig(ctypes.Structure):
@@ -55,9 +56,15 @@ def _lib() -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libqkv.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        # torch carries its own HIP runtime under the same soname; loading it
+        # first makes the library bind to that one (a second runtime loaded
+        # beside it would find no device)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.qkv_strerror.restype = ctypes.c_char_p
         L.qkv_strerror.argtypes = [ctypes.c_int]
+        L.qkv_hip_error_detail.restype = ctypes.c_char_p
+        L.qkv_hip_error_detail.argtypes = []
         L.qkv_workspace_bytes.restype = _sz
         L.qkv_workspace_bytes.argtypes = [ctypes.POINTER(QkvConfig)]
         L.qkv_check_config.argtypes = [ctypes.POINTER(QkvConfig)]

@@ -230,7 +230,13 @@ size_t carve(const Geom &g, int L, char *base, State *sts) {
   return off;
 }
 
-int hip_err(hipError_t e) { return e == hipSuccess ? QKV_OK : QKV_EHIP; }
+thread_local hipError_t g_last_hip = hipSuccess;   // the HIP error behind this thread's last QKV_EHIP
+
+int hip_err(hipError_t e) {
+  if (e == hipSuccess) return QKV_OK;
+  g_last_hip = e;
+  return QKV_EHIP;
+}
 
 StepInfo step_info(const qkv_cache *c, int layer = 0) {
   StepInfo si;
@@ -322,6 +328,8 @@ const char *qkv_strerror(int code) {
 }
 
 int qkv_check_config(const qkv_config *cfg) { return validate(cfg); }
+
+const char *qkv_hip_error_detail(void) { return hipGetErrorString(g_last_hip); }
 
 int qkv_plan_capacities(const qkv_config *cfg, double budget_bytes, double q, int32_t layers, int32_t *k_full,
                         int32_t *k_quant) {

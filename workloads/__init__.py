@@ -94,6 +94,7 @@ class Config:
     side_gain: float = 4.7
     n_clusters: int = 64
     switch_period: int = 200
+    layers: int = 1          # layers of one cache (each with its own inputs)
 
     @property
     def group_size(self) -> int:
@@ -151,6 +152,10 @@ DRIFT = _reg(Config(
 #     window and KV head costs 2816 B in INT4 against 1792 B in INT2, so the
 #     bytes of 612 INT2 windows hold 389 INT4 windows.
 DRIFT_INT4 = _reg(DRIFT.replace(name="drift_int4", quant_bits=4, k_quant=389))
+
+# 3c: 32 layers of the drift layer in one cache (Llama-3.1-8B depth), the
+#     per-layer capacities those of a byte budget of 32 times the layer's.
+DRIFT_L32 = _reg(DRIFT.replace(name="drift_l32", layers=32))
 
 # 4: HqeKV five-tier per-token assignment.
 HQEKV = _reg(Config(
@@ -309,3 +314,44 @@ class Workload:
 
     def queries_all(self) -> np.ndarray:
         return np.stack([self.queries(b) for b in range(self.cfg.batch)])
+
+
+# ---------------------------------------------------------------------------
+# the drift recipe drawn on the GPU (for many-layer runs, where drawing every
+# layer on the host would take minutes): the same structure -- N(0,1) keys and
+# values, two key clusters along per-(sequence, KV head) unit vectors, queries
+# aimed at one cluster with the other as a side target, roles swapped at the
+# switch step -- from torch's generator seeded by (seed, layer); not the same
+# numbers as the host recipe
+# ---------------------------------------------------------------------------
+
+def drift_inputs_torch(cfg: Config, layer: int, device="cuda"):
+    """K, V [B, Hkv, T, d] and Q [B, steps, Hq, d] as int16 (bf16 bits) on `device`."""
+    import torch
+    if cfg.recipe != "drift":
+        raise ValueError("drift_inputs_torch draws the drift recipe")
+    B, Hkv, T, d, S, Hq, G = (cfg.batch, cfg.n_kv_heads, cfg.total_tokens, cfg.head_dim, cfg.steps,
+                              cfg.n_q_heads, cfg.group_size)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000003 * cfg.seed + 7919 * layer + 17)
+    unit = lambda: torch.nn.functional.normalize(torch.randn((B, Hkv, d), generator=gen, device=device), dim=-1)
+    u_a, u_b = unit(), unit()
+    K = torch.empty((B, Hkv, T, d), dtype=torch.bfloat16, device=device)
+    V = torch.empty_like(K)
+    for b in range(B):                       # one sequence at a time (float32 draws)
+        k = torch.randn((Hkv, T, d), generator=gen, device=device)
+        for (w0_, nw), u in ((cfg.cluster_a, u_a[b]), (cfg.cluster_b, u_b[b])):
+            lo = cfg.n_sink + w0_ * cfg.window
+            hi = min(cfg.n_sink + (w0_ + nw) * cfg.window, cfg.prefill)
+            if hi > lo:
+                k[:, lo:hi, :] += cfg.key_gain * u[:, None, :]
+        K[b] = k.to(torch.bfloat16)
+        V[b] = torch.randn((Hkv, T, d), generator=gen, device=device).to(torch.bfloat16)
+    g = torch.arange(Hq, device=device) // G
+    ua, ub = u_a[:, g], u_b[:, g]                       # [B, Hq, d]
+    before = cfg.key_gain * ua + cfg.side_gain * ub
+    after = cfg.key_gain * ub + cfg.side_gain * ua
+    s = torch.arange(S, device=device)[None, :, None, None]
+    noise = torch.randn((B, S, Hq, d), generator=gen, device=device)
+    Q = (torch.where(s < cfg.switch_step, before[:, None], after[:, None]) + noise).to(torch.bfloat16)
+    return K.view(torch.int16), V.view(torch.int16), Q.view(torch.int16)
