@@ -684,8 +684,8 @@ def main():
                      "kernel": kernel,
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": att_us,
-                     "timed_launches": f"{len(attend_ms)} of the {steps} timed steps (every "
-                                       f"{PROFILE_STRIDE}th, from decode step {first})"},
+                     "timed_launches": f"{len(attend_ms)} of the {steps * cfg.layers} attention launches of the "
+                                       f"timed steps (every {PROFILE_STRIDE}th, from decode step {first})"},
         "phases": {"pre_route": pre, "steady": steady, "events": events},
         "cpu_baseline": cpu,
         "parity_spot_check_max_abs": worst,
