@@ -38,7 +38,13 @@ Readings where the pages are silent (each also listed in the design notes):
   ledger is kept while the window is Full again.
 * Routing is per sequence (one score per window, summed over KV heads), so
   all KV heads of a window share its tier.
-* Positional rotation is not modelled (the synthetic keys carry none).
+* Rotary embedding (``rope``, a table given with the inputs): keys arrive
+  before the rotation; the full-precision content read by attention is the
+  rotated key (``oracle.rope``), a window's ledger quantizes its original
+  unrotated keys, the quantized tier is read as the rotation of the
+  dequantized keys at their positions, and a promoted window's content is
+  that rotation rounded like a stored key.  Without a table no rotation is
+  applied (the synthetic keys of the other workloads carry none).
 """
 from __future__ import annotations
 
@@ -47,6 +53,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from . import rope as rp
 from .attention import attend
 from .codec import kivi_dequantize_window, kivi_quantize_window
 from .numerics import FLT_MIN, bf16_to_f64, round_to_bf16
@@ -74,9 +81,10 @@ class QEvictSequence:
 
     def __init__(self, k_bits: np.ndarray, v_bits: np.ndarray, *, window: int, omega: int,
                  n_sink: int, n_recent: int, k_full: int, k_quant: int, bits: int = 2,
-                 group: int = 32, n_q_heads: int):
-        self.korig = bf16_to_f64(k_bits)              # [Hkv, T, d]
+                 group: int = 32, n_q_heads: int, rope_table=None):
+        self.korig = bf16_to_f64(k_bits)              # [Hkv, T, d] (before any rotation)
         self.vorig = bf16_to_f64(v_bits)
+        self.rope = None if rope_table is None else np.asarray(rope_table, np.float32)
         self.hkv, self.T, self.d = self.korig.shape
         self.hq = n_q_heads
         self.G = n_q_heads // self.hkv
@@ -89,7 +97,11 @@ class QEvictSequence:
         self.score = np.zeros(self.n_units, np.float64)
         self.ledger: dict[int, dict] = {}
         # content currently read by attention, per position (float64 values)
-        self.kcur = self.korig.copy()
+        if self.rope is None:
+            self.kcur = self.korig.copy()
+        else:
+            pos = np.arange(self.korig.shape[1])
+            self.kcur = np.stack([rp.rotate_stored(self.korig[g], self.rope, pos) for g in range(self.korig.shape[0])])
         self.vcur = self.vorig.copy()
         self.N = 0
         self.P = 0
@@ -155,9 +167,21 @@ class QEvictSequence:
 
     # -- routing event (Eq. 4-6, Algorithm 1) ------------------------------
     def _quantize_unit(self, u: int) -> dict:
+        # a window is packed on its first demotion only, so its content is
+        # still the original (keys before the rotation)
         a, b = self.span(u)
-        return kivi_quantize_window(self.kcur[:, a:b].astype(np.float32),
+        keys = self.korig if self.rope is not None else self.kcur
+        return kivi_quantize_window(keys[:, a:b].astype(np.float32),
                                     self.vcur[:, a:b].astype(np.float32), self.bits, self.group)
+
+    def _rotated(self, kh: np.ndarray, a: int, b: int, stored: bool) -> np.ndarray:
+        """Dequantized keys [Hkv, w, d] of positions a..b-1 as attention reads
+        them: rotated at their positions when there is a table."""
+        if self.rope is None:
+            return round_to_bf16(kh) if stored else kh
+        pos = np.arange(a, b)
+        f = rp.rotate_stored if stored else rp.rotate
+        return np.stack([f(kh[g], self.rope, pos) for g in range(kh.shape[0])])
 
     def route(self, s: int) -> RouteEvent:
         N = self.N
@@ -183,14 +207,14 @@ class QEvictSequence:
                 ev.reused.append(u)
             a, b = self.span(u)
             kh, vh = kivi_dequantize_window(self.ledger[u])
-            self.kcur[:, a:b] = kh
+            self.kcur[:, a:b] = self._rotated(kh, a, b, stored=False)
             self.vcur[:, a:b] = vh
             self.tier[u] = QUANT
         for u in F.tolist():
             if self.tier[u] == QUANT:
                 kh, vh = kivi_dequantize_window(self.ledger[u])
                 a, b = self.span(u)
-                self.kcur[:, a:b] = round_to_bf16(kh)
+                self.kcur[:, a:b] = self._rotated(kh, a, b, stored=True)   # rotated again at its positions
                 self.vcur[:, a:b] = round_to_bf16(vh)
                 ev.promoted.append(u)
             self.tier[u] = FULL
@@ -201,14 +225,14 @@ class QEvictSequence:
         return ev
 
 
-def run_sequence(cfg, k_bits, v_bits, q_bits, steps: int | None = None, record=False):
+def run_sequence(cfg, k_bits, v_bits, q_bits, steps: int | None = None, record=False, rope_table=None):
     """Drive one sequence through prefill and ``steps`` decode steps.
 
     Returns (seq, outs [steps, Hq, d], masses list) -- masses only when
     ``record`` is true."""
     seq = QEvictSequence(k_bits, v_bits, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
                          n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
-                         bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads)
+                         bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads, rope_table=rope_table)
     seq.prefill(cfg.prefill)
     steps = cfg.steps if steps is None else steps
     outs = np.zeros((steps, cfg.n_q_heads, cfg.head_dim))

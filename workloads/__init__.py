@@ -95,6 +95,7 @@ class Config:
     n_clusters: int = 64
     switch_period: int = 200
     layers: int = 1          # layers of one cache (each with its own inputs)
+    rope_base: float = 0.0   # rotary embedding of the keys (0: none): table base, queries rotated
 
     @property
     def group_size(self) -> int:
@@ -184,6 +185,26 @@ def w0(cfg: Config) -> int:
 
 
 # ---------------------------------------------------------------------------
+# rotary embedding table (a model input): frequency i of d/2 is base^(-2i/d),
+# the angle of position p is p times it, cos and sin taken in float64 and
+# rounded to float32; [n_pos, d/2, 2]
+# ---------------------------------------------------------------------------
+
+def rope_table(n_pos: int, d: int, base: float) -> np.ndarray:
+    inv = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def _rope_rows_f32(rows: np.ndarray, table: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Model-side rotation of query targets (float32; rotate-half pairing)."""
+    h = rows.shape[-1] // 2
+    c, s = table[pos, :, 0], table[pos, :, 1]
+    lo, hi = rows[..., :h], rows[..., h:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # generators
 # ---------------------------------------------------------------------------
 
@@ -262,18 +283,29 @@ class Workload:
         return out
 
     # -- queries ------------------------------------------------------------
-    def _aimed(self, b: int, positions: np.ndarray, tensor) -> np.ndarray:
-        """q_h = 2 k_j + N(0,1), j uniform over positions <= the query's own."""
+    def _aimed(self, b: int, positions: np.ndarray, tensor, lo=None, hi=None) -> np.ndarray:
+        """q_h = 2 k_j + N(0,1), j uniform over positions <= the query's own
+        (or over [lo, hi) when given).  With a rotary table the target is the
+        rotated key k_j at its position: queries are given already rotated."""
         cfg = self.cfg
         kb, _ = self.kv(b)
         rng = _rng(cfg, b, tensor)
         n = len(positions)
         hq, d, G = cfg.n_q_heads, cfg.head_dim, cfg.group_size
-        j = np.floor(rng.random((n, hq)) * (positions[:, None] + 1)).astype(np.int64)
+        if lo is None:
+            j = np.floor(rng.random((n, hq)) * (positions[:, None] + 1)).astype(np.int64)
+        else:
+            j = (lo[:, None] + np.floor(rng.random((n, hq)) * (hi - lo)[:, None])).astype(np.int64)
         noise = rng.standard_normal((n, hq, d), dtype=np.float32)
         g = np.arange(hq) // G
-        q = np.float32(2.0) * bf16_bits_to_f32(kb[g[None, :], j, :]) + noise   # only the target keys
-        return f32_to_bf16_bits(q)
+        tgt = bf16_bits_to_f32(kb[g[None, :], j, :])                            # only the target keys
+        if cfg.rope_base:
+            tgt = _rope_rows_f32(tgt, self.rope(), j)
+        return f32_to_bf16_bits(np.float32(2.0) * tgt + noise)
+
+    def rope(self) -> np.ndarray:
+        """The rotary table of this workload ([total_tokens, d/2, 2] float32)."""
+        return rope_table(self.cfg.total_tokens, self.cfg.head_dim, self.cfg.rope_base)
 
     def queries(self, b: int) -> np.ndarray:
         """bf16 bits of the decode-step queries: uint16 [steps, Hq, d]."""
@@ -281,6 +313,16 @@ class Workload:
         hq, d, G = cfg.n_q_heads, cfg.head_dim, cfg.group_size
         if cfg.recipe in ("aimed", "hqekv"):
             return self._aimed(b, cfg.prefill + np.arange(cfg.steps), _T_Q)
+        if cfg.recipe == "drift" and cfg.rope_base:
+            # rotated keys no longer line up across positions, so the queries
+            # aim at single keys of the attended cluster (A, then B after the
+            # switch): their windows gather the mass
+            s = np.arange(cfg.steps)
+            span = lambda c: (cfg.n_sink + c[0] * cfg.window, cfg.n_sink + (c[0] + c[1]) * cfg.window)
+            (a0, a1), (b0, b1) = span(cfg.cluster_a), span(cfg.cluster_b)
+            lo = np.where(s < cfg.switch_step, a0, b0)
+            hi = np.where(s < cfg.switch_step, a1, b1)
+            return self._aimed(b, cfg.prefill + s, _T_Q, lo=lo, hi=hi)
         aux = self._aux(b)
         rng = _rng(cfg, b, _T_Q)
         noise = rng.standard_normal((cfg.steps, hq, d), dtype=np.float32)
