@@ -98,6 +98,15 @@ typedef struct qkv_config {
                        * score per layer and window; 4.3 and 4.5: capacities of
                        * a budget over all layers, qkv_plan_capacities); the
                        * ledgers of every layer share one pool.  1 otherwise.  */
+  int32_t rope;       /* QEvict: 1 = keys arrive before the rotary embedding
+                       * (QEvict notes 4.4, Algorithm 1's promotion step and the
+                       * paragraph on promoted keys' positions): qkv_set_rope
+                       * gives the table; full-precision pages hold the keys
+                       * rotated once at their positions, the ledger quantizes
+                       * the keys before rotation, the quantized tier is read
+                       * rotated at the tokens' positions and a promoted window
+                       * is rotated again at them.  Queries are given rotated.
+                       * Windows of at most 16 tokens.  0 otherwise.          */
 } qkv_config;
 
 /* Bytes of device workspace a cache with this configuration needs, or 0 if
@@ -132,6 +141,18 @@ int qkv_check_config(const qkv_config *cfg);
  * not fit the current device's LDS. */
 int qkv_create(const qkv_config *cfg, void *workspace, size_t bytes, qkv_stream stream,
                qkv_cache **out);
+
+/* The rotary table of a cache created with rope = 1: device float32
+ * [n_positions][head_dim/2][2] holding (cos, sin) of position p and frequency
+ * i, which rotates the channel pair (i, i + head_dim/2):
+ *   r_i = x_i cos - x_{i+d/2} sin,   r_{i+d/2} = x_{i+d/2} cos + x_i sin.
+ * The quantized tier composes the row of a window's first position with the
+ * row of the token's offset in it, so row p must be the rotation by p times
+ * fixed angles (what a model's table is).  n_positions >= max_ctx; the table
+ * is the caller's and must stay valid while the cache is used.  Required
+ * before the first append (QKV_ESTATE otherwise); QKV_EINVAL for a cache
+ * without rope. */
+int qkv_set_rope(qkv_cache *cache, const float *table, int32_t n_positions);
 
 /* Release the host-side handle (the workspace stays the caller's). */
 int qkv_destroy(qkv_cache *cache);

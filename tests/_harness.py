@@ -96,6 +96,9 @@ class QEvictGPURun:
         self.cfg = cfg
         self.K, self.V, self.Q = K, V, Q
         self.cache = Cache(make_config(cfg, n_splits=n_splits))
+        if cfg.rope_base:
+            self.rope = torch.from_numpy(W.Workload(cfg).rope()).cuda()
+            self.cache.set_rope(self.rope)
         self.U = self.cache.info("units")
         self.out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
         self.mass = torch.zeros((cfg.batch, cfg.n_kv_heads, self.U), dtype=torch.float32, device="cuda")

@@ -190,3 +190,26 @@ def test_binding_checks_dtype_and_shape():
                            (torch.zeros((3, 2), dtype=torch.float32), (2, 3), "f32")):
         with pytest.raises(ValueError):
             L._check_tensor(t, "x", shape, kind)
+
+
+def test_rope_config_checks_on_host():
+    """Keys before the rotary embedding: the window policy with windows of at
+    most one 16-token tile; the workspace adds the keys as appended (the
+    pages' key half) and the table is set through qkv_set_rope."""
+    L, lib = _lib()
+    c = L.make_config(W.TINY.replace(rope_base=10000.0))
+    assert c.rope == 1 and lib.qkv_check_config(ctypes.byref(c)) == 0
+    plain = L.make_config(W.TINY)
+    assert plain.rope == 0
+    U = 1 + -(-(W.TINY.total_tokens - W.TINY.n_sink) // W.TINY.window)
+    assert L.workspace_bytes(c) - L.workspace_bytes(plain) >= U * W.TINY.n_kv_heads * 16 * W.TINY.head_dim * 2
+    d = L.make_config(W.DRIFT.replace(rope_base=500000.0))
+    assert lib.qkv_check_config(ctypes.byref(d)) == 0
+    for bad in (dict(window=32), dict(rope=2), dict(rope=-1)):
+        e = L.make_config(W.STRESS if "window" in bad else W.TINY, rope=1)
+        for k, v in bad.items():
+            setattr(e, k, v)
+        assert lib.qkv_check_config(ctypes.byref(e)) == L.EINVAL, bad
+    h = L.make_config(W.H2O, rope=1)
+    assert lib.qkv_check_config(ctypes.byref(h)) == L.EINVAL       # the window policy only
+    assert lib.qkv_set_rope(None, ctypes.c_void_p(256), 1 << 20) == L.EINVAL

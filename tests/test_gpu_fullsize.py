@@ -56,7 +56,8 @@ def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True, bytes_at=()):
         k, v = wl.kv(b)
         seqs[b] = oe.QEvictSequence(k, v, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
                                     n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
-                                    bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads)
+                                    bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads,
+                                    rope_table=wl.rope() if cfg.rope_base else None)
         seqs[b].prefill(cfg.prefill)
         qs[b] = wl.queries(b)
     worst, routes = 0.0, 0

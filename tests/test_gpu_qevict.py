@@ -157,7 +157,7 @@ def _oracle_seq(cfg, wl, b):
     k, v = wl.kv(b)
     seq = oe.QEvictSequence(k, v, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
                             k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits, group=cfg.group,
-                            n_q_heads=cfg.n_q_heads)
+                            n_q_heads=cfg.n_q_heads, rope_table=wl.rope() if cfg.rope_base else None)
     seq.prefill(cfg.prefill)
     return seq, wl.queries(b)
 

@@ -43,7 +43,7 @@ class QkvConfig(ctypes.Structure):
         ("k_full", ctypes.c_int32), ("k_quant", ctypes.c_int32), ("ratios", ctypes.c_float * 5),
         ("quant_bits", ctypes.c_int32), ("group", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
         ("n_splits", ctypes.c_int32), ("score_window", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("n_layers", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32), ("rope", ctypes.c_int32),
     ]
 
 
@@ -76,6 +76,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_append.argtypes = [_vp, _vp, _vp, _i32, _vp]
         L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.qkv_append_layer.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp]
+        L.qkv_set_rope.argtypes = [_vp, _vp, _i32]
         L.qkv_decode_attend_layer.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp]
         L.qkv_route.argtypes = [_vp, _vp]
         L.qkv_prefill_score.argtypes = [_vp, _vp, _i32, _vp]
@@ -159,6 +160,9 @@ def make_config(cfg=None, *, n_splits: int = 0, max_ctx: int | None = None, **kw
         elif f == "policy":
             p = src.get("policy", 0)
             c.policy = POLICY[p] if isinstance(p, str) else int(p)
+        elif f == "rope":
+            # a workload with a rotary table base has keys before the rotation
+            c.rope = int(src.get("rope", 1 if getattr(cfg, "rope_base", 0) else 0))
         else:
             setattr(c, f, int(src.get(f, 32 if f == "group" else (2 if f == "quant_bits" else 0))))
     return c
@@ -240,6 +244,15 @@ class Cache:
             _check_tensor(mass_out, "mass_out", (c.batch, c.n_kv_heads, self.info("units")), "f32")
         _check(_lib().qkv_decode_attend_layer(self.h, int(layer), _ptr(q), _ptr(out), _ptr(mass_out),
                                               _stream(stream)), "qkv_decode_attend")
+
+    def set_rope(self, table):
+        """table: float32 [n_positions, d/2, 2] device tensor (kept by the caller)."""
+        import torch
+        if table.dtype != torch.float32 or table.dim() != 3 or int(table.shape[1]) * 2 != self.c.head_dim \
+                or int(table.shape[2]) != 2:
+            raise ValueError("rope table: float32 [n_positions, d/2, 2] required")
+        self._rope = table
+        _check(_lib().qkv_set_rope(self.h, _ptr(table), int(table.shape[0])), "qkv_set_rope")
 
     def route(self, stream=None):
         _check(_lib().qkv_route(self.h, _stream(stream)), "qkv_route")

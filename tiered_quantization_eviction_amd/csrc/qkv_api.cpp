@@ -63,6 +63,9 @@ int validate(const qkv_config *c) {
   if (c->n_splits < 0 || c->n_splits > 256) return QKV_EINVAL;
   if (c->n_layers < 0 || c->n_layers > MAX_LAYERS) return QKV_EINVAL;
   if (c->n_layers > 1 && c->policy != QKV_POLICY_QEVICT) return QKV_EINVAL;   // layers: the window policy
+  // rotary keys: the window policy, windows of at most one 16-token tile (the
+  // attention kernel keeps a tile's offset rotations in registers)
+  if (c->rope < 0 || c->rope > 1 || (c->rope && (c->policy != QKV_POLICY_QEVICT || c->window > TS))) return QKV_EINVAL;
   // a rolling score window is HqeKV's, at most one routing period long
   if (c->score_window < 0 || (c->score_window > 0 && (c->policy != QKV_POLICY_HQEKV || c->score_window > c->omega)))
     return QKV_EINVAL;
@@ -129,6 +132,7 @@ void make_geom(const qkv_config *c, Geom &g) {
   g.tile_vparam_bytes = 4 * (g.d / 32) * 16;
   g.tile_block_bytes = g.tile_kcode_bytes + g.tile_vcode_bytes + g.tile_vparam_bytes;
   g.ledger_unit_bytes = g.kparam_bytes + g.tpw * g.tile_block_bytes;
+  g.rope = c->rope;
   {
     // a layer's sequence holds at most K_f + K_q ledgers (Full and Quantized
     // windows only), and never more than it has windows
@@ -225,6 +229,9 @@ size_t carve(const Geom &g, int L, char *base, State *sts) {
     st.qslot = (int32_t *)take(BU * 4);
     st.slist = (float *)take(BU * 4);
     st.status = (int32_t *)take(16);
+    st.kraw = g.rope ? (uint16_t *)take(BU * g.Hkv * (size_t)(g.tpw * TS * g.d) * 2) : nullptr;
+    st.rope = nullptr;
+    st.rope_n = 0;
     if (sts) sts[l] = st;
   }
   return off;
@@ -404,7 +411,7 @@ static int create_into(qkv_cache *c, const qkv_config *cfg, void *workspace, siz
 
 static void free_events(qkv_cache *c) {
   if (c->ev) {
-    for (int i = 0; i < 2 * c->ev_n; ++i) hipEventDestroy(c->ev[i]);
+    for (int i = 0; i < 2 * c->ev_n; ++i) (void)hipEventDestroy(c->ev[i]);
     delete[] c->ev;
   }
   c->ev = nullptr;
@@ -478,7 +485,7 @@ int qkv_profile_start(qkv_cache *c, int32_t n, int32_t stride) {
   for (int i = 0; i < 2 * n; ++i) {
     // timing only: no system-scope fence (cache writeback) when recorded
     if (hipEventCreateWithFlags(&c->ev[i], hipEventDisableSystemFence) != hipSuccess) {
-      for (int j = 0; j < i; ++j) hipEventDestroy(c->ev[j]);
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(c->ev[j]);
       delete[] c->ev;
       c->ev = nullptr;
       return QKV_EHIP;
@@ -500,9 +507,20 @@ int qkv_profile_read(qkv_cache *c, float *ms, int32_t n) {
   return QKV_OK;
 }
 
+int qkv_set_rope(qkv_cache *c, const float *table, int32_t n_positions) {
+  if (!c || !table || c->tok || !c->g.rope) return QKV_EINVAL;
+  if (n_positions < c->cfg.max_ctx || n_positions < 16 || ((uintptr_t)table & 15)) return QKV_EINVAL;
+  for (int l = 0; l < c->L; ++l) {
+    c->sts[l].rope = table;
+    c->sts[l].rope_n = n_positions;
+  }
+  return QKV_OK;
+}
+
 int qkv_append_layer(qkv_cache *c, int32_t layer, const void *k, const void *v, int32_t n_tokens,
                      qkv_stream stream) {
   if (!c || !k || !v || n_tokens < 1 || layer < 0 || layer >= c->L) return QKV_EINVAL;
+  if (!c->tok && c->g.rope && !c->sts[0].rope) return QKV_ESTATE;   // qkv_set_rope first
   if ((long long)c->Nl[layer] + n_tokens > c->cfg.max_ctx) return QKV_ECAPACITY;
   int rc = settle(c, (hipStream_t)stream);
   if (rc != QKV_OK) return rc;

@@ -90,6 +90,15 @@ __device__ __forceinline__ float f64_to_f32_kept(double x) {
   return f;
 }
 
+// Rotary embedding of one channel pair (x_i, x_{i+d/2}) by a table entry
+// (cos, sin): float64 products of the float32 operands (exact), one rounding
+// of each difference or sum, then float32.
+__device__ __forceinline__ void rope_pair(float lo, float hi, float c, float s, float &rlo, float &rhi) {
+  const double l = lo, h = hi, cd = c, sd = s;
+  rlo = f64_to_f32_kept(l * cd - h * sd);
+  rhi = f64_to_f32_kept(h * cd + l * sd);
+}
+
 // Streaming loads of cache tiles: read once per decode step, so they are
 // issued nontemporal (they do not displace reused lines in the caches, and
 // HBM read throughput is measurably higher than with ordinary loads).

@@ -54,6 +54,7 @@ struct Geom {
   int tile_block_bytes;
   int tr_per_seq;        // workgroups per sequence of the pack/promote launch (one resident round)
   int pool_slots;        // ledger-pool slots of the cache (every layer)
+  int rope;              // keys arrive before the rotary embedding (table in State::rope)
 };
 
 struct State {
@@ -82,6 +83,12 @@ struct State {
   int32_t *free_count;  // [B]
   int32_t *pool_stack;  // [pool_slots] free slots (shared by every layer)
   int32_t *pool_top;    // [1] free slots on the stack (shared by every layer)
+  // rotary embedding (Geom::rope): the caller's table [positions][d/2][cos, sin]
+  // and the keys as appended, before the rotation, [B][U][Hkv][tpw*TS][d]
+  // (packing reads them; the pages hold the rotated keys)
+  const float *rope;
+  int rope_n;           // rows of the table
+  uint16_t *kraw;
 };
 
 // Per-step scalars the host knows without reading the device.
@@ -192,6 +199,9 @@ __host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int w
 
 __host__ __device__ inline size_t page_offset(const Geom &g, int b, int u, int h) {
   return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.page_unit_elems;
+}
+__host__ __device__ inline size_t kraw_offset(const Geom &g, int b, int u, int h) {
+  return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)(g.tpw * TS * g.d);
 }
 __host__ __device__ inline size_t ledger_slot_offset(const Geom &g, int slot, int h) {
   return ((size_t)slot * g.Hkv + h) * (size_t)g.ledger_unit_bytes;

@@ -43,8 +43,12 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s) {
 // ---------------------------------------------------------------------------
 
 // one block row per (sequence, KV head); thread it of the row copies 16-byte
-// chunk it % (D/8) of token it / (D/8) (32-bit indices: a prompt is far below 2^31 chunks)
-template <int D>
+// chunk it % (D/8) of token it / (D/8) (32-bit indices: a prompt is far below 2^31 chunks).
+// ROPE: the key arrives before the rotary embedding; it is kept as given (the
+// quantized tier is packed from it) and the page takes its rotation at the
+// token's position, so the thread of chunk c0 < D/2 also handles the key
+// chunk c0 + D/2 that pairs with it.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(Geom g, State st, const uint16_t *__restrict__ k,
                                                      const uint16_t *__restrict__ v, int n_tokens, int pos0) {
   constexpr int CH = D / 8;
@@ -60,7 +64,31 @@ __global__ __launch_bounds__(256) void append_kernel(Geom g, State st, const uin
     uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)tile * 2 * TS * D;
     uint16_t *vt = kt + TS * D;
     const size_t src = ((size_t)bh * n_tokens + tok) * D + c0;
-    *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + src);
+    if (!ROPE) {
+      *(uint4 *)(kt + k_tile_index(t, c0)) = *(const uint4 *)(k + src);
+    } else if (c0 < D / 2) {
+      const uint4 klo = *(const uint4 *)(k + src), khi = *(const uint4 *)(k + src + D / 2);
+      uint16_t *kr = st.kraw + kraw_offset(g, b, u, h) + (size_t)tile * TS * D;
+      *(uint4 *)(kr + k_tile_index(t, c0)) = klo;
+      *(uint4 *)(kr + k_tile_index(t, c0 + D / 2)) = khi;
+      const float4 *row = (const float4 *)(st.rope + ((size_t)pos * (D / 2) + c0) * 2);   // 8 (cos, sin) pairs
+      float4 cs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs[j] = row[j];
+      const uint16_t *el = (const uint16_t *)&klo, *eh = (const uint16_t *)&khi;
+      uint4 olo, ohi;
+      uint16_t *ol = (uint16_t *)&olo, *oh = (uint16_t *)&ohi;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float cj = (j & 1) ? cs[j >> 1].z : cs[j >> 1].x, sj = (j & 1) ? cs[j >> 1].w : cs[j >> 1].y;
+        float rl, rh;
+        rope_pair(bf16_to_f32(el[j]), bf16_to_f32(eh[j]), cj, sj, rl, rh);
+        ol[j] = f32_to_bf16_rne(rl);
+        oh[j] = f32_to_bf16_rne(rh);
+      }
+      *(uint4 *)(kt + k_tile_index(t, c0)) = olo;
+      *(uint4 *)(kt + k_tile_index(t, c0 + D / 2)) = ohi;
+    }
     const uint4 vq = *(const uint4 *)(v + src);
     const uint16_t *vs = (const uint16_t *)&vq;
 #pragma unroll
@@ -77,10 +105,15 @@ hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, cons
   int rows = (total + threads - 1) / threads;
   if (rows > 65535) rows = 65535;
   const dim3 grid(g.B * g.Hkv, rows);
-  if (g.d == 128)
-    hipLaunchKernelGGL(append_kernel<128>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+  if (g.rope && (!st.rope || !st.kraw || pos0 + n_tokens > st.rope_n)) return hipErrorInvalidValue;
+  if (g.d == 128 && g.rope)
+    hipLaunchKernelGGL((append_kernel<128, true>), grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+  else if (g.d == 128)
+    hipLaunchKernelGGL((append_kernel<128, false>), grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+  else if (g.rope)
+    hipLaunchKernelGGL((append_kernel<64, true>), grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
   else
-    hipLaunchKernelGGL(append_kernel<64>, grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
+    hipLaunchKernelGGL((append_kernel<64, false>), grid, dim3(threads), 0, s, g, st, k, v, n_tokens, pos0);
   return hipGetLastError();
 }
 
@@ -140,6 +173,8 @@ struct Ctx {
   half_t *kp_lds;
   half_t *vp_lds;
   half_t *qs_lds;         // per window slot: q*s limbs [2][G][d] (fp16)
+  float *rw_lds;          // rotary keys: table rows of the block's window starts [QT][d/2][2]
+  const float *rd_lds;    // rotary keys: table rows 0..15 (token offsets in a window) [16][RD_STR]
 };
 
 // unit id of entry e; `raw` is the routed-list value fetched for it (used
@@ -386,7 +421,10 @@ struct QBuf {
   uint4 code2[QT];  // 4-bit codes at d = 128: the lane's value code dwords
   uint2 kp[QT];     // the lane's 8 bytes of each window's key params (window slots)
   uint32_t vp[QT];  // the lane's 4 bytes of each tile's value params
+  uint4 tr[2];      // rotary keys: the lane's 16-byte chunks of window (lane / 16)'s start row
 };
+// row stride (floats) of the offset rows of the rotary table in LDS
+template <int D> constexpr int RD_STR = D + 4;
 
 __device__ __forceinline__ uint32_t u4_at(const uint4 &v, int i) {   // i is a constant after unrolling
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -413,12 +451,14 @@ __device__ __forceinline__ half4 value_codes(const QBuf &buf, int j, int ct) {
 struct QBlock {
   int e, nwin;
   int u[QT];        // ledger-pool slots of the block's windows; spare slots repeat slot 0
+  int p0;           // rotary keys: first position of window slot lane / 16 (per lane)
 };
 
 // window slot and tile-in-window of block tile j
 __device__ __forceinline__ int qt_win(int j, int tpw) { return tpw == 1 ? j : j >> 1; }
 
-__device__ __forceinline__ void qblock_make(const Ctx &c, int ea, int eb, int i, int ids, QBlock &qb) {
+template <bool ROPE>
+__device__ __forceinline__ void qblock_make(const Ctx &c, int ea, int eb, int i, int ids, int units, QBlock &qb) {
   const int per = QT / c.g->tpw;
   const int e0 = ea + i * per;
   qb.e = e0;
@@ -428,9 +468,15 @@ __device__ __forceinline__ void qblock_make(const Ctx &c, int ea, int eb, int i,
     const int ww = w < qb.nwin ? w : 0;
     qb.u[w] = entry_id(c, e0 + ww, __builtin_amdgcn_readlane(ids, ww));
   }
+  qb.p0 = 0;
+  if (ROPE) {
+    // lane ww of `units` holds the routed value of entry e0 + ww
+    const int wl = c.lane >> 4, ww = wl < qb.nwin ? wl : 0;
+    qb.p0 = min(max(unit_start(*c.g, entry_id(c, e0 + ww, __shfl(units, ww))), 0), c.st->rope_n - 1);
+  }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool ROPE>
 __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf &buf) {
   constexpr int DPL = D * BITS / 64;   // code dwords per lane per tile
   const Geom &g = *c.g;
@@ -458,15 +504,23 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
   }
 #pragma unroll
   for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + ledger_slot_offset(g, qb.u[w], c.h) + kl * 8);
+  if (ROPE) {
+    // lanes 16w .. 16w+15 fetch the table row of window slot w's first
+    // position (D/2 (cos, sin) pairs, D/64 chunks of 16 bytes per lane); the
+    // rows are shared by every KV head, so these are ordinary cached loads
+    const float *row = c.st->rope + (size_t)qb.p0 * D;
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) buf.tr[r] = *(const uint4 *)(row + ((c.lane & 15) * (D / 64) + r) * 4);
+  }
 }
 
-template <int D, int GP, int BITS>
+template <int D, int GP, int BITS, bool ROPE>
 __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, const half8 (&qc)[2],
-                                              const half8 (&bz)[D / 32], float sc_quant, const float (&row_bias)[4],
-                                              const QBlock &qb, const QBuf &buf) {
+                                              const half8 (&qp)[2], const half8 (&bz)[D / 32], float sc_quant,
+                                              const float (&row_bias)[4], const QBlock &qb, const QBuf &buf) {
   constexpr int KB = D / 32, NG = D / 32;
   const Geom &g = *c.g;
-  const int tpw = g.tpw;
+  const int tpw = ROPE ? 1 : g.tpw;                          // rotary keys: one tile per window
   const int nws = QT / tpw;                                  // window slots per block
   constexpr int G = GP == 2 ? 4 : 8;   // query heads per KV head (the launcher pairs groups for four)
   const int kl = c.lane & (g.kparam_bytes / 8 - 1);
@@ -477,7 +531,48 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     *(uint2 *)(c.kp_lds + j * PSTR<D> + kl * 4) = buf.kp[j];
     ((uint32_t *)(c.vp_lds + j * PSTR<D>))[vl] = buf.vp[j];
   }
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r)
+      *(uint4 *)(c.rw_lds + (c.lane >> 4) * D + ((c.lane & 15) * (D / 64) + r) * 4) = buf.tr[r];
+  }
   wave_lds_sync();
+  if constexpr (ROPE) {
+    // Rotary keys.  A key of the window starting at p0 sits at p0 + t and
+    // reads as R(p0 + t) k = R(p0) R(t) k, so q . R(p0 + t) k equals
+    // (R(p0)^T q) . (R(t) k): the query is turned back by the window's start
+    // once per (head, channel), and each dequantized key element is turned by
+    // its offset t (the tile row, a lane constant).  q' = R(p0)^T q in two
+    // fp16 limbs [limb][head][c]; the lane's channels pair with the lane
+    // D/16 away (qp).
+    const int c0 = 8 * ((c.lane & 15) % (D / 8));
+    const int i0 = c0 & (D / 2 - 1);
+    const bool lower = c0 < D / 2;
+#pragma unroll
+    for (int w = 0; w < QT; ++w) {
+      float4 cs[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cs[k] = *(const float4 *)(c.rw_lds + w * D + (i0 + 2 * k) * 2);
+      half_t *qs = c.qs_lds + w * 2 * G * QSTR<D>;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (4 * r < G) {
+          const int hh = (c.lane >> 4) + 4 * r;
+          half8 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float cj = (j & 1) ? cs[j >> 1].z : cs[j >> 1].x, sj = (j & 1) ? cs[j >> 1].w : cs[j >> 1].y;
+            const float o = (float)qp[r][j];
+            const float v = __builtin_fmaf((float)qc[r][j], cj, (lower ? o : -o) * sj);
+            hi[j] = (half_t)v;
+            lo[j] = (half_t)(v - (float)hi[j]);
+          }
+          *(half8 *)(qs + hh * QSTR<D> + c0) = hi;
+          *(half8 *)(qs + (G + hh) * QSTR<D> + c0) = lo;
+        }
+      }
+    }
+  } else {
   // q*s of each window as two fp16 limbs (high, exact remainder), computed
   // once per (head, channel) in the compact layout and stored [limb][head][c]
   {
@@ -502,7 +597,56 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
       }
     }
   }
+  }
   wave_lds_sync();
+  floatx4 s[QT];
+  const int qrow = (c.is_lo ? G : 0) + c.hc;
+  if constexpr (ROPE) {
+    // A operand: the lane's 8 channels of k-block kb and their partners in
+    // kb + KB/2, dequantized in float32 (code * s + z, one rounding), turned
+    // by the row's offset and split into two fp16 limbs; each limb takes one
+    // MFMA against the q' limbs (the key-zero term is inside the dequantized
+    // values)
+#pragma unroll
+    for (int j = 0; j < QT; ++j) s[j] = floatx4{row_bias[0], row_bias[1], row_bias[2], row_bias[3]};
+    const int t = c.lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < KB / 2; ++kb) {
+      const int ch = kb * 32 + c.lq * 8;
+      float4 cs[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cs[k] = *(const float4 *)(c.rd_lds + t * RD_STR<D> + (ch + 2 * k) * 2);
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        const half_t *kp = c.kp_lds + j * PSTR<D>;
+        const half8 sl = *(const half8 *)(kp + ch), sh = *(const half8 *)(kp + ch + D / 2);
+        const half8 zl = *(const half8 *)(kp + D + ch), zh = *(const half8 *)(kp + D + ch + D / 2);
+        const half8 cl = key_codes<D, BITS>(buf, j, kb), chh = key_codes<D, BITS>(buf, j, kb + KB / 2);
+        half8 al, all, ah, ahl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xl = __builtin_fmaf((float)cl[e], (float)sl[e], (float)zl[e]);
+          const float xh = __builtin_fmaf((float)chh[e], (float)sh[e], (float)zh[e]);
+          const float ce = (e & 1) ? cs[e >> 1].z : cs[e >> 1].x, se = (e & 1) ? cs[e >> 1].w : cs[e >> 1].y;
+          const float rl = __builtin_fmaf(xl, ce, -xh * se);
+          const float rh = __builtin_fmaf(xh, ce, xl * se);
+          al[e] = (half_t)rl;
+          all[e] = (half_t)(rl - (float)al[e]);
+          ah[e] = (half_t)rh;
+          ahl[e] = (half_t)(rh - (float)ah[e]);
+        }
+        const half_t *qs = c.qs_lds + (j * 2 * G + qrow) * QSTR<D>;
+        const half8 bl = *(const half8 *)(qs + ch), bh = *(const half8 *)(qs + ch + D / 2);
+        s[j] = mfma_f16_k32(al, bl, s[j]);
+        s[j] = mfma_f16_k32(all, bl, s[j]);
+        s[j] = mfma_f16_k32(ah, bh, s[j]);
+        s[j] = mfma_f16_k32(ahl, bh, s[j]);
+        // one tile's operands at a time: letting the scheduler hoist the
+        // next tiles' reads and arithmetic runs out of registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
   // key-zero term sum_c q_c z_c of every window at once: A rows r are the
   // zero vectors of window slot r % nws, so register i of every lane holds
   // the term of window slot i % nws for the lane's column (high columns only)
@@ -515,13 +659,11 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   for (int kb = 0; kb < KB; ++kb) zb = mfma_f16_k32(z8[kb], bz[kb], zb);
   // scores of the QT tiles: column h takes the high limb, column 8+h the low
   // limb, one MFMA per k-block; the two are folded after the last k-block
-  floatx4 s[QT];
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const float z = tpw == 1 ? zb[j & 3] : zb[(j >> 1) & 3];
     s[j] = floatx4{z + row_bias[0], z + row_bias[1], z + row_bias[2], z + row_bias[3]};
   }
-  const int qrow = (c.is_lo ? G : 0) + c.hc;
   // the q*s operands are read two steps ahead of their MFMA, so that LDS
   // latency overlaps the matrix-core work instead of preceding every op
   auto bq_at = [&](int idx) {
@@ -536,6 +678,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
     bqa = bqb;
     if (idx + 2 < KB * QT) bqb = bq_at(idx + 2);
     s[j] = mfma_f16_k32(key_codes<D, BITS>(buf, j, kb), bq, s[j]);
+  }
   }
 #pragma unroll
   for (int j = 0; j < QT; ++j)
@@ -632,11 +775,24 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   wave_lds_sync();
 }
 
-template <int D, int GP, int BITS>
-__device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
+template <int D, int GP, int BITS, bool ROPE>
+__device__ __forceinline__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   if (ea >= eb) return;
-  half8 qc[2], bz[D / 32];
+  half8 qc[2], qp[2], bz[D / 32];
   const float sc_quant = query_f16<D>(c, qc, bz);
+  // rotary keys: the compact query's pair partners (channel c +- D/2 sits
+  // D/16 lanes away in the same head row)
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    uint4 w = __builtin_bit_cast(uint4, qc[r]);
+    if (ROPE) {
+      w.x = __shfl_xor(w.x, D / 16);
+      w.y = __shfl_xor(w.y, D / 16);
+      w.z = __shfl_xor(w.z, D / 16);
+      w.w = __shfl_xor(w.w, D / 16);
+    }
+    qp[r] = __builtin_bit_cast(half8, w);
+  }
   // rows of a tile past a window shorter than the tile hold no token
   float row_bias[4];
 #pragma unroll
@@ -648,30 +804,32 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
   // loads on every trip, and the tail reads nothing past the run
   QBlock k0, k1;
   QBuf b0, b1;
-  const int ids0 = slots_fetch(c, ea);
-  int ids1 = slots_fetch(c, ea + min(1, n_blocks - 1) * per);
-  qblock_make(c, ea, eb, 0, ids0, k0);
-  quant_load<D, BITS>(c, k0, b0);
+  auto units = [&](int e0) { return ROPE ? ids_fetch(c, e0) : 0; };
+  const int ids0 = slots_fetch(c, ea), un0 = units(ea);
+  int ids1 = slots_fetch(c, ea + min(1, n_blocks - 1) * per), un1 = units(ea + min(1, n_blocks - 1) * per);
+  qblock_make<ROPE>(c, ea, eb, 0, ids0, un0, k0);
+  quant_load<D, BITS, ROPE>(c, k0, b0);
   // steady state: two blocks per trip, the following block always in flight
   int i = 0;
   for (; i + 2 < n_blocks; i += 2) {
-    const int ids2 = slots_fetch(c, ea + min(i + 2, n_blocks - 1) * per);
-    qblock_make(c, ea, eb, i + 1, ids1, k1);
-    quant_load<D, BITS>(c, k1, b1);
-    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    const int ids2 = slots_fetch(c, ea + min(i + 2, n_blocks - 1) * per), un2 = units(ea + min(i + 2, n_blocks - 1) * per);
+    qblock_make<ROPE>(c, ea, eb, i + 1, ids1, un1, k1);
+    quant_load<D, BITS, ROPE>(c, k1, b1);
+    quant_compute<D, GP, BITS, ROPE>(ws, c, qc, qp, bz, sc_quant, row_bias, k0, b0);
     ids1 = slots_fetch(c, ea + min(i + 3, n_blocks - 1) * per);
-    qblock_make(c, ea, eb, i + 2, ids2, k0);
-    quant_load<D, BITS>(c, k0, b0);
-    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+    un1 = units(ea + min(i + 3, n_blocks - 1) * per);
+    qblock_make<ROPE>(c, ea, eb, i + 2, ids2, un2, k0);
+    quant_load<D, BITS, ROPE>(c, k0, b0);
+    quant_compute<D, GP, BITS, ROPE>(ws, c, qc, qp, bz, sc_quant, row_bias, k1, b1);
   }
   // the last one or two blocks: nothing past the run is read
   if (i + 1 < n_blocks) {
-    qblock_make(c, ea, eb, i + 1, ids1, k1);
-    quant_load<D, BITS>(c, k1, b1);
-    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
-    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k1, b1);
+    qblock_make<ROPE>(c, ea, eb, i + 1, ids1, un1, k1);
+    quant_load<D, BITS, ROPE>(c, k1, b1);
+    quant_compute<D, GP, BITS, ROPE>(ws, c, qc, qp, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP, BITS, ROPE>(ws, c, qc, qp, bz, sc_quant, row_bias, k1, b1);
   } else {
-    quant_compute<D, GP, BITS>(ws, c, qc, bz, sc_quant, row_bias, k0, b0);
+    quant_compute<D, GP, BITS, ROPE>(ws, c, qc, qp, bz, sc_quant, row_bias, k0, b0);
   }
 }
 
@@ -679,7 +837,7 @@ __device__ void run_quant(WaveState<D> &ws, const Ctx &c, int ea, int eb) {
 // holds two waves on each SIMD.
 constexpr int QW = 8;
 
-template <int D, int GP, int BITS>
+template <int D, int GP, int BITS, bool ROPE>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
                                                             const uint16_t *__restrict__ q, float scale_log2) {
   constexpr int KB = D / 32;
@@ -707,7 +865,9 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ float sm_m[QW][8];
   __shared__ float sm_l[QW][8];
   __shared__ float sm_o[QW][8][D];
-  extern __shared__ __attribute__((aligned(16))) half_t s_qs[];   // [QW][window slots][2][G][D+8]
+  // [QW][window slots][2][G][D+8] halfs; rotary keys: then [QW][QT][D] and
+  // [16][RD_STR] floats (window-start rows, offset rows of the table)
+  extern __shared__ __attribute__((aligned(16))) half_t s_qs[];
 
   // ---- this wave's share: slice gi of QW*S of the full-precision entries
   // (sink, ranked full, recent) and the same slice of the quantized windows,
@@ -756,6 +916,18 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
   c.qs_lds = s_qs + (size_t)wave * (QT / g.tpw) * 2 * G * QSTR<D>;
+  if (ROPE) {
+    float *rw = (float *)(s_qs + (size_t)QW * QT * 2 * G * QSTR<D>);
+    float *rd = rw + QW * QT * D;
+    c.rw_lds = rw + wave * QT * D;
+    c.rd_lds = rd;
+    // table rows 0..15 (the offsets of a window's tokens), D floats each
+    for (int it = threadIdx.x; it < 16 * (D / 4); it += 64 * QW) {
+      const int t = it / (D / 4), k = it % (D / 4);
+      *(float4 *)(rd + t * RD_STR<D> + 4 * k) = *(const float4 *)(st.rope + (size_t)t * D + 4 * k);
+    }
+    __syncthreads();
+  }
   // Opposite orders for the two waves that share a SIMD, whether the
   // workgroup's waves are dealt to the SIMDs round-robin (w, w+4) or in
   // pairs (2k, 2k+1): one streams full-precision tiles while the other
@@ -763,13 +935,13 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int f0 = min(vb0, A), f1 = min(vb1, A);
   const int r0e = AQ + max(vb0 - A, 0), r1e = AQ + max(vb1 - A, 0);
   if (((wave & 1) ^ (wave >> 2)) & 1) {
-    run_quant<D, GP, BITS>(ws, c, q0, q1);
+    run_quant<D, GP, BITS, ROPE>(ws, c, q0, q1);
     run_full<D>(ws, c, f0, f1);      // sink and ranked full-precision windows
     run_full<D>(ws, c, r0e, r1e);    // windows not yet ranked
   } else {
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
-    run_quant<D, GP, BITS>(ws, c, q0, q1);
+    run_quant<D, GP, BITS, ROPE>(ws, c, q0, q1);
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -942,19 +1114,25 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
 // LDS of one attention workgroup beyond its static arrays: the q*s limbs of
 // every window slot of every wave
 static size_t attend_qs_bytes(const Geom &g) {
-  return (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+  size_t n = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+  if (g.rope) n += ((size_t)QW * QT * g.d + 16 * (size_t)(g.d + 4)) * sizeof(float);   // RD_STR
+  return n;
 }
 
 // the attention kernel of a configuration: head dimension, four or eight heads
-// per KV head (paired channel groups with four), 2- or 4-bit quantized tier
-template <int D, int GP>
+// per KV head (paired channel groups with four), 2- or 4-bit quantized tier,
+// keys with or without the rotary embedding around the quantized tier
+template <int D, int GP, bool ROPE>
 static const void *attend_fn_bits(int bits) {
-  return bits == 4 ? (const void *)attend_qevict_kernel<D, GP, 4> : (const void *)attend_qevict_kernel<D, GP, 2>;
+  return bits == 4 ? (const void *)attend_qevict_kernel<D, GP, 4, ROPE>
+                   : (const void *)attend_qevict_kernel<D, GP, 2, ROPE>;
 }
-static const void *attend_fn(const Geom &g) {
-  if (g.d == 128) return g.G == 4 ? attend_fn_bits<128, 2>(g.bits) : attend_fn_bits<128, 1>(g.bits);
-  return g.G == 4 ? attend_fn_bits<64, 2>(g.bits) : attend_fn_bits<64, 1>(g.bits);
+template <bool ROPE>
+static const void *attend_fn_rope(const Geom &g) {
+  if (g.d == 128) return g.G == 4 ? attend_fn_bits<128, 2, ROPE>(g.bits) : attend_fn_bits<128, 1, ROPE>(g.bits);
+  return g.G == 4 ? attend_fn_bits<64, 2, ROPE>(g.bits) : attend_fn_bits<64, 1, ROPE>(g.bits);
 }
+static const void *attend_fn(const Geom &g) { return g.rope ? attend_fn_rope<true>(g) : attend_fn_rope<false>(g); }
 
 hipError_t attend_lds_fits(const Geom &g, bool *fits) {
   hipFuncAttributes a;
@@ -1248,10 +1426,13 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
       // 1. tiles -> LDS in logical order (all loads issued before the stores)
       if (own) {
         uint4 kch[2], vch[2];
+        // with the rotary embedding the ledger quantizes the keys as appended
+        const uint16_t *kraw = g.rope ? st.kraw + kraw_offset(g, b, u, h) : nullptr;
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
           const uint16_t *kt = pg + (size_t)min(tile, tpw - 1) * 2 * TS * D;
-          kch[tile] = *(const uint4 *)(kt + ci * 8);
+          const uint16_t *ks = g.rope ? kraw + (size_t)min(tile, tpw - 1) * TS * D : kt;
+          kch[tile] = *(const uint4 *)(ks + ci * 8);
           vch[tile] = *(const uint4 *)(kt + TS * D + ci * 8);
         }
 #pragma unroll
@@ -1353,11 +1534,44 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         const half_t *ks = (const half_t *)&ks4, *kz = (const half_t *)&kz4, *vps = (const half_t *)&vpar;
         uint4 ko, vo;
         uint16_t *ke = (uint16_t *)&ko, *ve = (uint16_t *)&vo;
+        if (!g.rope) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kcode_slot(kt_t, kt_c + e, D, BITS, kdw, sh);
-          const float kcode = (float)((kw >> sh) & MASK);
-          ke[e] = f32_to_bf16_rne(__builtin_fmaf(kcode, (float)ks[e], (float)kz[e]));
+          for (int e = 0; e < 8; ++e) {
+            kcode_slot(kt_t, kt_c + e, D, BITS, kdw, sh);
+            const float kcode = (float)((kw >> sh) & MASK);
+            ke[e] = f32_to_bf16_rne(__builtin_fmaf(kcode, (float)ks[e], (float)kz[e]));
+          }
+          *(uint4 *)(kt + ci * 8) = ko;
+        } else if (ci < CHUNKS / 2) {
+          // rotary keys: the dequantized pair (kt_c + e, kt_c + e + D/2) is
+          // rotated again at the token's position (chunk ci + CHUNKS/2 holds
+          // the upper channels)
+          int kdw2;
+          kcode_slot(kt_t, kt_c + D / 2, D, BITS, kdw2, sh);
+          const uint32_t kw2 = tc[kdw2];
+          const uint4 ks24 = *(const uint4 *)(kparam + kt_c + D / 2), kz24 = *(const uint4 *)(kparam + D + kt_c + D / 2);
+          const half_t *ks2 = (const half_t *)&ks24, *kz2 = (const half_t *)&kz24;
+          const int row = min(unit_start(g, u) + tile * TS + kt_t, st.rope_n - 1);   // rows past the window hold no token
+          const float4 *cs4 = (const float4 *)(st.rope + ((size_t)row * (D / 2) + kt_c) * 2);
+          float4 cs[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cs[j] = cs4[j];
+          uint4 ko2;
+          uint16_t *ke2 = (uint16_t *)&ko2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kcode_slot(kt_t, kt_c + e, D, BITS, kdw, sh);
+            const float xl = __builtin_fmaf((float)((kw >> sh) & MASK), (float)ks[e], (float)kz[e]);
+            kcode_slot(kt_t, kt_c + D / 2 + e, D, BITS, kdw2, sh);
+            const float xh = __builtin_fmaf((float)((kw2 >> sh) & MASK), (float)ks2[e], (float)kz2[e]);
+            const float ce = (e & 1) ? cs[e >> 1].z : cs[e >> 1].x, se = (e & 1) ? cs[e >> 1].w : cs[e >> 1].y;
+            float rl, rh;
+            rope_pair(xl, xh, ce, se, rl, rh);
+            ke[e] = f32_to_bf16_rne(rl);
+            ke2[e] = f32_to_bf16_rne(rh);
+          }
+          *(uint4 *)(kt + ci * 8) = ko;
+          *(uint4 *)(kt + (ci + CHUNKS / 2) * 8) = ko2;
         }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -1367,7 +1581,6 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
             const float vcode = (float)((vw >> sh) & MASK);
             ve[hf * 4 + j] = f32_to_bf16_rne(__builtin_fmaf(vcode, (float)vps[j], (float)vps[4 + j]));
           }
-        *(uint4 *)(kt + ci * 8) = ko;
         *(uint4 *)(kt + TS * D + ci * 8) = vo;
       }
     }
