@@ -63,8 +63,8 @@ KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
-WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.DRIFT_L32, W.STRESS, W.HQEKV, W.HQEKV_PAGE, W.H2O,
-                                  W.TINY)}
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.DRIFT_L32, W.DRIFT_ROPE, W.STRESS, W.HQEKV,
+                                  W.HQEKV_PAGE, W.H2O, W.TINY)}
 CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",
@@ -87,9 +87,11 @@ def describe(cfg, steps, first=0):
                 f"Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} INT{cfg.quant_bits} windows per layer from a byte budget "
                 f"over all layers, one ledger pool; inputs of each layer drawn on the GPU")
     if cfg.policy == W.POLICY_QEVICT:
+        rope = (f"; keys before the rotary embedding (table base {cfg.rope_base:g}): pages rotated, ledger packed "
+                f"before rotation, quantized tier read rotated" if cfg.rope_base else "")
         return (f"QEvict three-tier ({cfg.name}): " + head + f", window={cfg.window} Omega={cfg.omega}, "
                 f"{cfg.n_sink} sinks + {cfg.n_recent} recent, Kf={cfg.k_full} BF16 + Kq={cfg.k_quant} "
-                f"INT{cfg.quant_bits} windows")
+                f"INT{cfg.quant_bits} windows" + rope)
     if cfg.policy == W.POLICY_H2O:
         return (f"H2O heavy hitters: " + head + f", scored prompt, {cfg.n_sink} sinks + {cfg.k_full} heavy + "
                 f"{cfg.n_recent} recent tokens per KV head, eviction every step")
@@ -164,10 +166,14 @@ def quant_window_bytes(cfg):
 def attend_bytes(cfg, sched):
     """Algorithmic bytes per attention launch: every live BF16 token (K and V,
     2 bytes each) and every quantized window's codes + parameters, per KV head,
-    plus the bf16 queries."""
+    plus the bf16 queries.  With rotary keys, also the table row of each
+    quantized window's first position (d/2 float32 (cos, sin) pairs, shared
+    by the KV heads of a sequence) and the 16 offset rows."""
     per = []
+    rope_row = cfg.head_dim * 4 if cfg.rope_base else 0
     for bf_tok, nq in sched:
         kv = cfg.batch * cfg.n_kv_heads * (bf_tok * cfg.head_dim * 4 + nq * quant_window_bytes(cfg))
+        kv += cfg.batch * nq * rope_row + (16 * rope_row if nq else 0)
         per.append(kv + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2)
     return per
 
@@ -193,6 +199,9 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
     q_dec = dev(np.ascontiguousarray(Q.transpose(1, 0, 2, 3)))                             # [S, B, Hq, d]
     out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
     cache = Cache(make_config(cfg, n_splits=n_splits))
+    if cfg.rope_base:
+        rope = torch.from_numpy(W.Workload(cfg).rope()).cuda()   # the layer's rotary table (a model input)
+        cache.set_rope(rope)
     cache.append(k_pre, v_pre)
     ev_route = []
 
@@ -444,10 +453,11 @@ def cpu_baseline(cfg, K, V, Q, n_seqs, sample_steps, firsts, budget_s=None):
     worst = 0.0
     dt = 0.0
     done = 0
+    table = W.Workload(cfg).rope() if cfg.rope_base else None
     for b in range(n_seqs):
         seq = oe.QEvictSequence(K[b], V[b], window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
                                 n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant, bits=cfg.quant_bits,
-                                group=cfg.group, n_q_heads=cfg.n_q_heads)
+                                group=cfg.group, n_q_heads=cfg.n_q_heads, rope_table=table)
         seq.prefill(cfg.prefill)
         outs = []
         t0 = time.perf_counter()
@@ -651,7 +661,8 @@ def main():
         log(f"bench: oracle baseline on sequence 0, up to {CPU_BUDGET_S:.0f} s of decode steps")
         cpu, worst = cpu_baseline(cfg, K, V, Q, 1, cfg.steps, firsts, budget_s=CPU_BUDGET_S)
     kernel = ("tok_attend_kernel<%d>" % cfg.head_dim if token_mode else
-              "attend_qevict_kernel<%d, %d>" % (cfg.head_dim, 2 if cfg.group_size == 4 else 1))
+              "attend_qevict_kernel<%d, %d, %d, %s>" % (cfg.head_dim, 2 if cfg.group_size == 4 else 1,
+                                                       cfg.quant_bits, "true" if cfg.rope_base else "false"))
     events = {"count": len(route_ms),
               "avg_us": float(np.mean(route_ms)) * 1e3 if route_ms else None,
               "max_us": float(np.max(route_ms)) * 1e3 if route_ms else None,

@@ -101,6 +101,16 @@ def test_drift_fullsize_sampled(torch_cuda):
         "no INT2 -> BF16 promotion after the query switch"
 
 
+def test_drift_rope_fullsize_sampled(torch_cuda):
+    """The drift layer with keys before the rotary embedding (table base
+    500000) at 16 x 32768: ledgers packed from the keys before rotation and
+    rotated contents (promotions after the query switch) bit-exact on the
+    sampled sequences."""
+    seqs = _qevict_sampled(W.DRIFT_ROPE.replace(steps=160), torch_cuda, [0, 11], "drift-rope-full", bytes_at=(1,))
+    assert sum(len(e.promoted) for sq in seqs.values() for e in sq.events) > 0, \
+        "no INT2 -> BF16 promotion after the query switch"
+
+
 def test_stress_fullsize_sampled(torch_cuda):
     """Batch 32 at 131072 tokens; sequence 5 follows the clustered recipe and
     the oracle, the other 31 are normal filler of the same shape."""

@@ -158,6 +158,11 @@ DRIFT_INT4 = _reg(DRIFT.replace(name="drift_int4", quant_bits=4, k_quant=389))
 #     per-layer capacities those of a byte budget of 32 times the layer's.
 DRIFT_L32 = _reg(DRIFT.replace(name="drift_l32", layers=32))
 
+# 3d: the drift layer with keys before the rotary embedding (Llama-3 table
+#     base 500000): pages hold rotated keys, the ledger packs the keys before
+#     rotation and the quantized tier is read rotated at its positions.
+DRIFT_ROPE = _reg(DRIFT.replace(name="drift_rope", rope_base=500000.0))
+
 # 4: HqeKV five-tier per-token assignment.
 HQEKV = _reg(Config(
     name="hqekv", policy=POLICY_HQEKV, recipe="hqekv",
@@ -194,6 +199,16 @@ def rope_table(n_pos: int, d: int, base: float) -> np.ndarray:
     inv = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
     ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
     return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def low_frequency_channels(d: int, base: float, span: int, max_angle: float = 0.3) -> np.ndarray:
+    """Channels (i and i + d/2) of the pairs whose angle over `span`
+    positions stays below max_angle radians (at least the four slowest pairs)."""
+    inv = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    pairs = np.flatnonzero(inv * span <= max_angle)
+    if len(pairs) < 4:
+        pairs = np.argsort(inv)[:4]
+    return np.sort(np.concatenate([pairs, pairs + d // 2]))
 
 
 def _rope_rows_f32(rows: np.ndarray, table: np.ndarray, pos: np.ndarray) -> np.ndarray:
@@ -242,6 +257,16 @@ class Workload:
         if cfg.recipe == "drift":
             aux["u_a"] = _unit_vectors(rng, hkv, d)
             aux["u_b"] = _unit_vectors(rng, hkv, d)
+            if cfg.rope_base:
+                # with rotary keys the clusters live in the channel pairs whose
+                # rotation over the whole context stays small (the
+                # lowest-frequency pairs): there a cluster direction lines up
+                # across all its positions, as without the rotation
+                m = np.zeros(d, np.float32)
+                m[low_frequency_channels(d, cfg.rope_base, cfg.total_tokens)] = 1.0
+                for key in ("u_a", "u_b"):
+                    u = aux[key] * m
+                    aux[key] = (u / np.linalg.norm(u, axis=-1, keepdims=True)).astype(np.float32)
         if cfg.recipe == "clusters":
             aux["mu"] = np.stack([_unit_vectors(rng, cfg.n_clusters, d) for _ in range(hkv)])   # [hkv, C, d]
             n_win = (cfg.total_tokens - cfg.n_sink + cfg.window - 1) // cfg.window
@@ -313,16 +338,6 @@ class Workload:
         hq, d, G = cfg.n_q_heads, cfg.head_dim, cfg.group_size
         if cfg.recipe in ("aimed", "hqekv"):
             return self._aimed(b, cfg.prefill + np.arange(cfg.steps), _T_Q)
-        if cfg.recipe == "drift" and cfg.rope_base:
-            # rotated keys no longer line up across positions, so the queries
-            # aim at single keys of the attended cluster (A, then B after the
-            # switch): their windows gather the mass
-            s = np.arange(cfg.steps)
-            span = lambda c: (cfg.n_sink + c[0] * cfg.window, cfg.n_sink + (c[0] + c[1]) * cfg.window)
-            (a0, a1), (b0, b1) = span(cfg.cluster_a), span(cfg.cluster_b)
-            lo = np.where(s < cfg.switch_step, a0, b0)
-            hi = np.where(s < cfg.switch_step, a1, b1)
-            return self._aimed(b, cfg.prefill + s, _T_Q, lo=lo, hi=hi)
         aux = self._aux(b)
         rng = _rng(cfg, b, _T_Q)
         noise = rng.standard_normal((cfg.steps, hq, d), dtype=np.float32)
@@ -331,7 +346,13 @@ class Workload:
             s = np.arange(cfg.steps)[:, None, None]
             ua, ub = aux["u_a"][g][None], aux["u_b"][g][None]
             hi_, lo_ = np.float32(cfg.key_gain), np.float32(cfg.side_gain)
-            q = np.where(s < cfg.switch_step, hi_ * ua + lo_ * ub, hi_ * ub + lo_ * ua) + noise
+            tgt = np.where(s < cfg.switch_step, hi_ * ua + lo_ * ub, hi_ * ub + lo_ * ua)
+            if cfg.rope_base:
+                # queries are given rotated at their own positions
+                pos = cfg.prefill + np.arange(cfg.steps)
+                tgt = _rope_rows_f32(np.broadcast_to(tgt, (cfg.steps, hq, d)),
+                                     self.rope(), np.broadcast_to(pos[:, None], (cfg.steps, hq)))
+            q = tgt + noise
             return f32_to_bf16_bits(q.astype(np.float32))
         if cfg.recipe == "clusters":
             tgt = aux["target"][np.arange(cfg.steps) // cfg.switch_period]       # [steps]
