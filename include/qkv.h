@@ -331,6 +331,10 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *                                                  first, then quantized); entries past the
  *                                                  ranked count are unspecified
  *   QKV_EXPORT_STATE   int64   [16]               format tag, policy, geometry and step scalars
+ *   QKV_EXPORT_KEYS_RAW uint16 [batch, n_kv_heads, max_ctx, head_dim]  caches with rope = 1: the
+ *                                                  keys as appended, before the rotation (the
+ *                                                  ledger packs from them); KEYS holds them
+ *                                                  rotated
  * (units without a ledger export zero codes and parameters).  A cache of
  * n_layers > 1 exports every per-layer kind as n_layers such arrays, layer
  * after layer (STATE once; QKV_ESTATE unless every layer holds the same
@@ -359,6 +363,7 @@ enum {
   QKV_EXPORT_VALUES = 8,
   QKV_EXPORT_ROUTED = 9,
   QKV_EXPORT_STATE = 10,
+  QKV_EXPORT_KEYS_RAW = 11,
 };
 int qkv_export(const qkv_cache *cache, int32_t what, void *dst, size_t bytes, qkv_stream stream);
 size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);

@@ -114,3 +114,48 @@ def test_rope_requires_a_table(torch_cuda):
     plain = Cache(make_config(W.TINY))
     with pytest.raises(QkvError):
         plain.set_rope(torch.zeros((cfg.total_tokens, cfg.head_dim // 2, 2), dtype=torch.float32, device="cuda"))
+
+
+def test_rope_snapshot_restore_continues_bitwise(torch_cuda):
+    """A rotary cache restored from its snapshot (the raw keys included: the
+    ledger packs from them at later demotions) continues exactly like the
+    original: outputs, tiers, scores and ledgers bitwise through the query
+    switch and the promotions after it."""
+    from tiered_quantization_eviction_amd import Cache, make_config
+    from _harness import gpu_inputs
+    torch = torch_cuda
+    cfg = _small_drift(rope_base=500000.0)
+    wl = W.Workload(cfg)
+    K, V, Q = gpu_inputs(cfg, wl)
+    table = torch.from_numpy(wl.rope()).cuda()
+    a = Cache(make_config(cfg))
+    a.set_rope(table)
+    P = cfg.prefill
+    a.append(K[:, :, :P].contiguous(), V[:, :, :P].contiguous())
+    outs = [torch.zeros((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+
+    def step(c, o, s):
+        c.append(K[:, :, P + s:P + s + 1].contiguous(), V[:, :, P + s:P + s + 1].contiguous())
+        c.decode_attend(Q[:, s].contiguous(), o)
+        if (s + 1) % cfg.omega == 0:
+            c.route()
+
+    cut = 40                                        # mid-period, before the query switch
+    for s in range(cut):
+        step(a, outs[0], s)
+    snap = a.snapshot()
+    assert "keys_raw" in snap
+    b = Cache(make_config(cfg))
+    b.set_rope(table)
+    b.restore(snap)
+    for s in range(cut, cfg.steps):
+        step(a, outs[0], s)
+        step(b, outs[1], s)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {s}"
+    for what in ("tiers", "scores", "ledger", "kcodes", "kparams", "keys", "keys_raw"):
+        x, y = a.export(what), b.export(what)
+        torch.cuda.synchronize()
+        assert torch.equal(x, y), what
+    log(f"[rope-snapshot] restored at step {cut}; {cfg.steps - cut} steps bitwise equal")

@@ -18,7 +18,7 @@ KIND_K_PER_CHANNEL, KIND_PER_TOKEN, KIND_INT1_NORMAL = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 TIER_EMPTY, TIER_SINK, TIER_RECENT, TIER_FULL, TIER_QUANT, TIER_EVICTED = range(6)
 EXPORT = {"tiers": 0, "scores": 1, "ledger": 2, "kcodes": 3, "vcodes": 4, "kparams": 5, "vparams": 6,
-          "keys": 7, "values": 8, "routed": 9, "state": 10}
+          "keys": 7, "values": 8, "routed": 9, "state": 10, "keys_raw": 11}
 INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5, "list_capacity": 6,
         "layers": 7}
 # what each policy's session snapshot holds (qkv_import restores them all)
@@ -286,7 +286,8 @@ class Cache:
 
     def snapshot(self, stream=None) -> dict:
         """Every kind of state this policy holds, as export() tensors."""
-        return {w: self.export(w, stream) for w in SNAPSHOT[self.c.policy]}
+        kinds = SNAPSHOT[self.c.policy] + (("keys_raw",) if self.c.rope else ())
+        return {w: self.export(w, stream) for w in kinds}
 
     def restore(self, snap: dict, stream=None) -> None:
         for w, t in snap.items():

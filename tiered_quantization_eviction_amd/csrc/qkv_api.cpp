@@ -730,6 +730,7 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
     case QKV_EXPORT_VPARAMS: per = BU * g.Hkv * (size_t)g.window * (g.d / g.group) * 2 * 2; break;
     case QKV_EXPORT_KEYS:
     case QKV_EXPORT_VALUES: per = (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2; break;
+    case QKV_EXPORT_KEYS_RAW: per = g.rope ? (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2 : 0; break;
     case QKV_EXPORT_ROUTED: per = BU * 4; break;
     default: return 0;
   }

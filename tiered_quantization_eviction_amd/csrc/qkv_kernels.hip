@@ -1897,7 +1897,10 @@ __global__ __launch_bounds__(256) void export_kernel(Geom g, State st, int what,
       const int slot = pos - unit_start(g, u);
       const uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)(slot / TS) * 2 * TS * D;
       const int t = slot % TS;
-      ((uint16_t *)dst)[it] = what == QKV_EXPORT_KEYS ? kt[k_tile_index(t, c)] : kt[TS * D + v_tile_index(t, c)];
+      if (what == QKV_EXPORT_KEYS_RAW)   // the keys as appended (rotary caches), page key-half layout
+        ((uint16_t *)dst)[it] = st.kraw[kraw_offset(g, b, u, h) + (size_t)(slot / TS) * TS * D + k_tile_index(t, c)];
+      else
+        ((uint16_t *)dst)[it] = what == QKV_EXPORT_KEYS ? kt[k_tile_index(t, c)] : kt[TS * D + v_tile_index(t, c)];
     }
   }
 }
@@ -2002,7 +2005,9 @@ __global__ __launch_bounds__(256) void import_kernel(Geom g, State st, int what,
       const int slot = pos - unit_start(g, u);
       uint16_t *kt = st.pages + page_offset(g, b, u, h) + (size_t)(slot / TS) * 2 * TS * D;
       const int t = slot % TS;
-      if (what == QKV_EXPORT_KEYS)
+      if (what == QKV_EXPORT_KEYS_RAW)
+        st.kraw[kraw_offset(g, b, u, h) + (size_t)(slot / TS) * TS * D + k_tile_index(t, c)] = xs[it];
+      else if (what == QKV_EXPORT_KEYS)
         kt[k_tile_index(t, c)] = xs[it];
       else
         kt[TS * D + v_tile_index(t, c)] = xs[it];
