@@ -335,6 +335,22 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *                                                  keys as appended, before the rotation (the
  *                                                  ledger packs from them); KEYS holds them
  *                                                  rotated
+ *   QKV_EXPORT_EVENT   int32   [batch, 16]        the last routing event of each sequence (H2O
+ *                                                  notes section 5.1: log what each eviction
+ *                                                  decided and how close its cut was): tokens
+ *                                                  in the cache, candidates, kept full, kept
+ *                                                  quantized, evicted, promoted, demoted,
+ *                                                  first packs, ledger reuses, ledger slots
+ *                                                  freed (words 0..9); then float32 bits of the
+ *                                                  relative score gap (lowest kept minus highest
+ *                                                  dropped, over the larger) at the K_f cut, at
+ *                                                  the K_f + K_q cut and their minimum (words
+ *                                                  10..12; +inf where the ranking has no such
+ *                                                  cut); zero before the first event
+ *   QKV_EXPORT_VICTIMS int32   [batch, n_units]   windows the last event evicted, best-ranked
+ *                                                  first (their scores: SCORES; their positions:
+ *                                                  the window spans), -1 past them
+ *   (EVENT and VICTIMS are diagnostics: export only)
  * (units without a ledger export zero codes and parameters).  A cache of
  * n_layers > 1 exports every per-layer kind as n_layers such arrays, layer
  * after layer (STATE once; QKV_ESTATE unless every layer holds the same
@@ -364,6 +380,8 @@ enum {
   QKV_EXPORT_ROUTED = 9,
   QKV_EXPORT_STATE = 10,
   QKV_EXPORT_KEYS_RAW = 11,
+  QKV_EXPORT_EVENT = 12,
+  QKV_EXPORT_VICTIMS = 13,
 };
 int qkv_export(const qkv_cache *cache, int32_t what, void *dst, size_t bytes, qkv_stream stream);
 size_t qkv_export_bytes(const qkv_cache *cache, int32_t what);

@@ -80,6 +80,8 @@ def _qevict_sampled(cfg, torch, seq_ids, label, all_real=True, bytes_at=()):
                 np.testing.assert_array_equal(tiers[b], seqs[b].tier,
                                               err_msg=f"tiers after event {routes} (step {s}) seq {b}, "
                                                       f"margins {seqs[b].events[-1].margins}")
+            from test_gpu_qevict import _check_event
+            _check_event(run, seqs, cfg)
             if routes in bytes_at or (cfg.switch_step and bytes_at and s > cfg.switch_step):
                 from test_gpu_qevict import _check_content, _check_ledger
                 _check_ledger(run, seqs, cfg)

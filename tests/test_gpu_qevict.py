@@ -180,6 +180,31 @@ def _check_ledger(run, seqs, cfg):
                                           err_msg=f"vparams u={u}")
 
 
+def _check_event(run, seqs, cfg):
+    """The library's record of the last routing event against the oracle's:
+    counters exactly, the victims as a set (listed in non-increasing score
+    order), the relative cut margins to the score tolerance (the library's
+    come from float32 scores)."""
+    recs = run.cache.last_event()
+    scores = run.scores()
+    for b, seq in seqs.items():
+        ev, r = seq.events[-1], recs[b]
+        exp = dict(tokens=ev.n_tokens, candidates=ev.candidates, full=len(ev.full), quant=len(ev.quant),
+                   evicted=len(ev.evicted), promoted=len(ev.promoted), first_packs=len(ev.first_packed),
+                   reused=len(ev.reused), demoted=len(ev.first_packed) + len(ev.reused))
+        got = {k: r[k] for k in exp}
+        assert got == exp, f"seq {b}: event record {got} != oracle {exp}"
+        assert set(r["victims"]) == set(ev.evicted), f"seq {b}: victims"
+        vs = scores[b][r["victims"]]
+        assert np.all(vs[:-1] >= vs[1:]), f"seq {b}: victims not in rank order"
+        for k, m in zip(("margin_full", "margin_quant"), ev.margins):
+            if np.isinf(m):
+                assert np.isinf(r[k]), (b, k, r[k])
+            else:
+                assert abs(r[k] - m) <= 2 * SCORE_RTOL, f"seq {b}: {k} {r[k]} vs oracle {m}"
+        assert r["margin_min"] == min(r["margin_full"], r["margin_quant"])
+
+
 def _check_content(run, seqs, cfg):
     """Full-precision content of sink/recent/full units, incl. promoted windows."""
     T, B, H, d = cfg.prefill + cfg.steps, cfg.batch, cfg.n_kv_heads, cfg.head_dim
@@ -228,6 +253,7 @@ def _run_parity(cfg, torch_cuda, seq_ids=None, n_splits=0, check_ledger_every=1,
                 exp = seqs[b].tier.copy()
                 np.testing.assert_array_equal(tiers[b], exp, err_msg=f"tiers after event {n_routes} (step {s}) "
                                               f"seq {b}, margins {ev.margins}")
+            _check_event(run, seqs, cfg)
             if n_routes % check_ledger_every == 0:
                 _check_ledger(run, seqs, cfg)
                 _check_content(run, seqs, cfg)

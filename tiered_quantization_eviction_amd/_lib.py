@@ -18,7 +18,11 @@ KIND_K_PER_CHANNEL, KIND_PER_TOKEN, KIND_INT1_NORMAL = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 TIER_EMPTY, TIER_SINK, TIER_RECENT, TIER_FULL, TIER_QUANT, TIER_EVICTED = range(6)
 EXPORT = {"tiers": 0, "scores": 1, "ledger": 2, "kcodes": 3, "vcodes": 4, "kparams": 5, "vparams": 6,
-          "keys": 7, "values": 8, "routed": 9, "state": 10, "keys_raw": 11}
+          "keys": 7, "values": 8, "routed": 9, "state": 10, "keys_raw": 11, "event": 12, "victims": 13}
+# fields of an exported routing-event record (int32 words, then float32 margins)
+EVENT_FIELDS = ("tokens", "candidates", "full", "quant", "evicted", "promoted", "demoted", "first_packs",
+                "reused", "freed")
+EVENT_MARGINS = ("margin_full", "margin_quant", "margin_min")
 INFO = {"tokens": 0, "units": 1, "steps": 2, "routes": 3, "splits": 4, "workspace": 5, "list_capacity": 6,
         "layers": 7}
 # what each policy's session snapshot holds (qkv_import restores them all)
@@ -283,6 +287,23 @@ class Cache:
             raise ValueError("src: 1-D uint8 tensor (as export returns) required")
         _check(_lib().qkv_import(self.h, EXPORT[what], _ptr(src), int(src.numel()), _stream(stream)),
                f"qkv_import({what})")
+
+    def last_event(self, layer: int = 0) -> list[dict]:
+        """The last routing event of each sequence of `layer` (QEvict): its
+        counters, cut margins and victims (window ids, best-ranked first)."""
+        import numpy as np
+        import torch
+        ev = self.export("event").cpu().numpy().view(np.int32).reshape(-1, self.c.batch, 16)[layer]
+        vic = self.export("victims").cpu().numpy().view(np.int32).reshape(-1, self.c.batch,
+                                                                             self.info("units"))[layer]
+        torch.cuda.synchronize()
+        out = []
+        for b in range(self.c.batch):
+            r = {k: int(ev[b, i]) for i, k in enumerate(EVENT_FIELDS)}
+            r.update({k: float(ev[b, 10 + i:11 + i].view(np.float32)[0]) for i, k in enumerate(EVENT_MARGINS)})
+            r["victims"] = [int(u) for u in vic[b, :r["evicted"]]]
+            out.append(r)
+        return out
 
     def snapshot(self, stream=None) -> dict:
         """Every kind of state this policy holds, as export() tensors."""

@@ -225,6 +225,8 @@ size_t carve(const Geom &g, int L, char *base, State *sts) {
     st.promote_count = (int32_t *)take((size_t)g.B * 4);
     st.free_list = (int32_t *)take(BU * 4);
     st.free_count = (int32_t *)take((size_t)g.B * 4);
+    st.event = (int32_t *)take((size_t)g.B * EV_WORDS * 4);
+    st.victims = (int32_t *)take(BU * 4);
     st.lslot = (int32_t *)take(BU * 4);
     st.qslot = (int32_t *)take(BU * 4);
     st.slist = (float *)take(BU * 4);
@@ -732,6 +734,8 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
     case QKV_EXPORT_VALUES: per = (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2; break;
     case QKV_EXPORT_KEYS_RAW: per = g.rope ? (size_t)g.B * g.Hkv * g.max_ctx * g.d * 2 : 0; break;
     case QKV_EXPORT_ROUTED: per = BU * 4; break;
+    case QKV_EXPORT_EVENT: per = (size_t)g.B * EV_WORDS * 4; break;
+    case QKV_EXPORT_VICTIMS: per = BU * 4; break;
     default: return 0;
   }
   return per * (size_t)c->L;
@@ -773,6 +777,7 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
   if (!c || !src) return QKV_EINVAL;
   const size_t need = qkv_export_bytes(c, what);
   if (need == 0 || bytes != need) return QKV_EINVAL;
+  if (what == QKV_EXPORT_EVENT || what == QKV_EXPORT_VICTIMS) return QKV_EINVAL;   // diagnostics, export only
   const hipStream_t s = (hipStream_t)stream;
   if (what == QKV_EXPORT_STATE) {
     Snapshot sn;

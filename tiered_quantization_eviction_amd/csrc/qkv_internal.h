@@ -79,6 +79,8 @@ struct State {
   int32_t *status;   // [4] latched device errors
   int32_t *lslot;       // [B][U] ledger-pool slot + 1 of each window holding codes (0: none)
   int32_t *qslot;       // [B][U] pool slot of ranked entry r (its quantized part), set at each event
+  int32_t *event;       // [B][EV_WORDS] record of the last routing event (EV_* fields)
+  int32_t *victims;     // [B][U] windows the last routing event evicted, in rank order (-1 past them)
   int32_t *free_list;   // [B][U] windows whose ledger the last routing event released
   int32_t *free_count;  // [B]
   int32_t *pool_stack;  // [pool_slots] free slots (shared by every layer)
@@ -200,6 +202,25 @@ __host__ __device__ inline int vparam_index(const Geom &g, int t, int grp, int w
 __host__ __device__ inline size_t page_offset(const Geom &g, int b, int u, int h) {
   return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)g.page_unit_elems;
 }
+// Record of a routing event per (layer, sequence): int32 counters, then the
+// float32 relative score gaps across the two cuts of the ranking.
+enum {
+  EV_TOKENS = 0,      // tokens in the cache at the event
+  EV_CANDIDATES,      // windows ranked
+  EV_FULL,            // windows kept in full precision
+  EV_QUANT,           // windows kept quantized
+  EV_EVICTED,         // windows evicted at this event
+  EV_PROMOTED,        // quantized -> full precision
+  EV_DEMOTED,         // full precision or recent -> quantized
+  EV_FIRST_PACKS,     // demotions that packed the window (no ledger yet)
+  EV_REUSED,          // demotions that reused the window's ledger
+  EV_FREED,           // ledger slots released (evicted windows that held codes)
+  EV_MARGIN_FULL,     // float: (s[Kf-1] - s[Kf]) / max(|s[Kf-1]|, |s[Kf]|), +inf without such a cut
+  EV_MARGIN_QUANT,    // float: the same at Kf + Kq
+  EV_MARGIN_MIN,      // float: the smaller of the two
+  EV_WORDS = 16
+};
+
 __host__ __device__ inline size_t kraw_offset(const Geom &g, int b, int u, int h) {
   return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)(g.tpw * TS * g.d);
 }

@@ -1231,7 +1231,7 @@ __device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
 
 __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, StepInfo si, int a0, int a1, int npow) {
   extern __shared__ unsigned long long keys[];
-  __shared__ int n_pack, n_prom, n_free;
+  __shared__ int n_pack, n_prom, n_free, n_reuse, n_demote;
   const int b = blockIdx.x;
   const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
   const int RC = nF + nQ;
@@ -1240,6 +1240,8 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     n_pack = 0;
     n_prom = 0;
     n_free = 0;
+    n_reuse = 0;
+    n_demote = 0;
   }
   // Candidate i sits at entry s0 + i of the list so far (the ranked windows,
   // then the windows aged since the last event, which lead the recent ones):
@@ -1270,11 +1272,16 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     const int idx = b * g.U + u;
     const uint8_t old = st.tier[idx];
     const uint8_t nt = r < g.k_full ? T_FULL : (r < KFQ ? T_QUANT : T_EVICTED);
+    if (nt == T_QUANT && old != T_QUANT) {
+      atomicAdd(&n_demote, 1);
+      if (st.has_ledger[idx]) atomicAdd(&n_reuse, 1);
+    }
     if (nt == T_QUANT && !st.has_ledger[idx]) {
       const int p = atomicAdd(&n_pack, 1);
       st.pack_list[b * g.U + p] = u;
       st.has_ledger[idx] = 1;
     }
+    if (r >= KFQ) st.victims[b * g.U + (r - KFQ)] = u;
     if (nt == T_FULL && old == T_QUANT) {
       const int p = atomicAdd(&n_prom, 1);
       st.promote_list[b * g.U + p] = u;
@@ -1295,6 +1302,28 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     st.pack_count[b] = n_pack;
     st.promote_count[b] = n_prom;
     st.free_count[b] = n_free;
+    // the event record: counters and the relative score gaps across the cuts
+    // (lowest kept minus highest dropped) of the sorted keys
+    auto margin = [&](int cut) {
+      if (cut <= 0 || cut >= n) return __builtin_inff();
+      const float hi = __uint_as_float((uint32_t)(keys[cut - 1] >> 32)), lo = __uint_as_float((uint32_t)(keys[cut] >> 32));
+      return (hi - lo) / fmaxf(fmaxf(fabsf(hi), fabsf(lo)), 1.17549435e-38f);
+    };
+    int32_t *ev = st.event + (size_t)b * EV_WORDS;
+    const float mf = margin(g.k_full), mq = margin(KFQ);
+    ev[EV_TOKENS] = si.N;
+    ev[EV_CANDIDATES] = n;
+    ev[EV_FULL] = nF2;
+    ev[EV_QUANT] = nQ2;
+    ev[EV_EVICTED] = n - nF2 - nQ2;
+    ev[EV_PROMOTED] = n_prom;
+    ev[EV_DEMOTED] = n_demote;
+    ev[EV_FIRST_PACKS] = n_pack;
+    ev[EV_REUSED] = n_reuse;
+    ev[EV_FREED] = n_free;
+    ev[EV_MARGIN_FULL] = __float_as_int(mf);
+    ev[EV_MARGIN_QUANT] = __float_as_int(mq);
+    ev[EV_MARGIN_MIN] = __float_as_int(fminf(mf, mq));
   }
   // list-order scores of the new list: the sink's is unchanged, the ranked
   // windows' are in their sorted keys, the recent windows' were written back
@@ -1310,6 +1339,7 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
       else if (e < E)
         v = st.score[b * g.U + a1 + (e - s0 - nFQ2)];
       st.slist[b * g.U + e] = v;
+      if (e >= n - nFQ2) st.victims[b * g.U + e] = -1;   // past this event's victims
     }
   }
 }
@@ -1918,6 +1948,10 @@ hipError_t launch_export(const Geom &g, const State &st, const StepInfo &si, int
   }
   if (what == QKV_EXPORT_LEDGER)
     return hipMemcpyAsync(dst, st.has_ledger, (size_t)g.B * g.U, hipMemcpyDeviceToDevice, s);
+  if (what == QKV_EXPORT_EVENT)
+    return hipMemcpyAsync(dst, st.event, (size_t)g.B * EV_WORDS * 4, hipMemcpyDeviceToDevice, s);
+  if (what == QKV_EXPORT_VICTIMS)
+    return hipMemcpyAsync(dst, st.victims, (size_t)g.B * g.U * 4, hipMemcpyDeviceToDevice, s);
   hipLaunchKernelGGL(export_kernel, dim3(2048), dim3(256), 0, s, g, st, what, dst);
   return hipGetLastError();
 }
