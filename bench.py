@@ -166,15 +166,18 @@ def quant_window_bytes(cfg):
 def attend_bytes(cfg, sched):
     """Algorithmic bytes per attention launch: every live BF16 token (K and V,
     2 bytes each) and every quantized window's codes + parameters, per KV head,
-    plus the bf16 queries.  With rotary keys, also the table row of each
+    plus the bf16 queries and the appended token.  With rotary keys, also the table row of each
     quantized window's first position (d/2 float32 (cos, sin) pairs, shared
     by the KV heads of a sequence) and the 16 offset rows."""
     per = []
     rope_row = cfg.head_dim * 4 if cfg.rope_base else 0
+    # without rotary keys the step's append is part of the launch: the new
+    # token's K and V are read from the input and written to their page
+    new_tok = 0 if cfg.rope_base else cfg.batch * cfg.n_kv_heads * cfg.head_dim * 2 * 2 * 2
     for bf_tok, nq in sched:
         kv = cfg.batch * cfg.n_kv_heads * (bf_tok * cfg.head_dim * 4 + nq * quant_window_bytes(cfg))
         kv += cfg.batch * nq * rope_row + (16 * rope_row if nq else 0)
-        per.append(kv + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2)
+        per.append(kv + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2 + new_tok)
     return per
 
 
@@ -207,8 +210,7 @@ def run_gpu(cfg, K, V, Q, steps, warmup, n_splits):
 
     def loop(s0, n, firsts=None):
         for s in range(s0, s0 + n):
-            cache.append(k_dec[s], v_dec[s])
-            cache.decode_attend(q_dec[s], out)
+            cache.decode_step(k_dec[s], v_dec[s], q_dec[s], out)   # append + attend (+ merge)
             if firsts is not None and len(firsts) < 4:
                 firsts.append(out.clone())
             if (s + 1) % om == 0:
@@ -293,8 +295,7 @@ def run_gpu_layers(cfg, steps, warmup, n_splits):
     def loop(s0, n, firsts=None):
         for s in range(s0, s0 + n):
             for l, (kd, vd, qd) in enumerate(dec):
-                cache.append(kd[s], vd[s], layer=l)
-                cache.decode_attend(qd[s], out[l], layer=l)
+                cache.decode_step(kd[s], vd[s], qd[s], out[l], layer=l)
             if firsts is not None and len(firsts) < 4:
                 firsts.append(out[0].clone())
             if (s + 1) % om == 0:

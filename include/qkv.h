@@ -235,6 +235,21 @@ int qkv_decode_attend_layer(qkv_cache *cache, int32_t layer, const void *q, floa
 int qkv_decode_attend(qkv_cache *cache, const void *q, float *out, float *mass_out, qkv_stream stream);
 
 /*
+ * A whole decode step in one call: qkv_append of one token (k, v: bfloat16
+ * [batch, n_kv_heads, 1, head_dim]) followed by qkv_decode_attend, with the
+ * same results bit for bit (QEvict notes section 4.1: the step appends the
+ * token, then attends over the accessible cache including it).  For the
+ * window policy without rotary keys the append is part of the attention
+ * launch (the new token's row is taken from k and v, and stored in its page
+ * for later steps); otherwise the two calls run in turn.  Errors as for the
+ * two calls.  The _layer form acts on one layer of a multi-layer cache.
+ */
+int qkv_decode_step(qkv_cache *cache, const void *k, const void *v, const void *q, float *out, float *mass_out,
+                    qkv_stream stream);
+int qkv_decode_step_layer(qkv_cache *cache, int32_t layer, const void *k, const void *v, const void *q, float *out,
+                          float *mass_out, qkv_stream stream);
+
+/*
  * Routing event (QEvict notes section 4.4, Eq.(4)-(6), Algorithm 1): the
  * previous full and quantized windows and the windows that aged out of the
  * recent region are ranked by score (descending, ties to the later window);

@@ -90,10 +90,11 @@ def gpu_inputs(cfg: W.Config, wl: W.Workload):
 class QEvictGPURun:
     """Drive the QEvict path through the C ABI and keep per-step results."""
 
-    def __init__(self, cfg: W.Config, K, V, Q, n_splits: int = 0):
+    def __init__(self, cfg: W.Config, K, V, Q, n_splits: int = 0, fused: bool = False):
         import torch
         from tiered_quantization_eviction_amd import Cache, make_config
         self.cfg = cfg
+        self.fused = fused   # qkv_decode_step instead of qkv_append + qkv_decode_attend
         self.K, self.V, self.Q = K, V, Q
         self.cache = Cache(make_config(cfg, n_splits=n_splits))
         if cfg.rope_base:
@@ -109,8 +110,12 @@ class QEvictGPURun:
     def step(self, want_mass: bool = True):
         cfg, s = self.cfg, self.s
         P = cfg.prefill
-        self.cache.append(self.K[:, :, P + s:P + s + 1].contiguous(), self.V[:, :, P + s:P + s + 1].contiguous())
-        self.cache.decode_attend(self.Q[:, s].contiguous(), self.out, self.mass if want_mass else None)
+        k, v = self.K[:, :, P + s:P + s + 1].contiguous(), self.V[:, :, P + s:P + s + 1].contiguous()
+        if self.fused:
+            self.cache.decode_step(k, v, self.Q[:, s].contiguous(), self.out, self.mass if want_mass else None)
+        else:
+            self.cache.append(k, v)
+            self.cache.decode_attend(self.Q[:, s].contiguous(), self.out, self.mass if want_mass else None)
         routed = (s + 1) % cfg.omega == 0
         if routed:
             self.cache.route()

@@ -217,12 +217,13 @@ def _check_content(run, seqs, cfg):
         np.testing.assert_array_equal(bf16_to_f64(vals[b][:, idx]), seq.vcur[:, idx], err_msg="values")
 
 
-def _run_parity(cfg, torch_cuda, seq_ids=None, n_splits=0, check_ledger_every=1, mass_every=1, label=""):
+def _run_parity(cfg, torch_cuda, seq_ids=None, n_splits=0, check_ledger_every=1, mass_every=1, label="",
+                fused=False):
     wl = W.Workload(cfg)
     log(f"[{label}] QEvict parity: {cfg.name} B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} "
-        f"d={cfg.head_dim} P={cfg.prefill} steps={cfg.steps} w={cfg.window} splits={n_splits}")
+        f"d={cfg.head_dim} P={cfg.prefill} steps={cfg.steps} w={cfg.window} splits={n_splits} fused={fused}")
     K, V, Q = gpu_inputs(cfg, wl)
-    run = QEvictGPURun(cfg, K, V, Q, n_splits=n_splits)
+    run = QEvictGPURun(cfg, K, V, Q, n_splits=n_splits, fused=fused)
     seq_ids = list(range(cfg.batch)) if seq_ids is None else seq_ids
     seqs, qs = {}, {}
     for b in seq_ids:
@@ -375,3 +376,44 @@ def test_qevict_int4_window32_g8_parity(torch_cuda):
 def test_qevict_int4_d64_window8_parity(torch_cuda):
     c = W.TINY.replace(batch=2, n_q_heads=8, n_kv_heads=2, prefill=515, steps=40, k_full=10, k_quant=20, quant_bits=4)
     _run_parity(c, torch_cuda, n_splits=4, label="int4-d64w8")
+
+
+# ---------------------------------------------------------------------------
+# the decode step in one call (append folded into the attention launch)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "drift_small", "w32g8", "int4"])
+def test_decode_step_parity(torch_cuda, name):
+    """qkv_decode_step against the oracle: tiny (d = 64, 8-token windows,
+    the new token in a new unit every 8 steps), the small drift layer (3
+    splits, promotions), 32-token windows with G = 8 (the token in a
+    window's second tile) and the INT4 tier."""
+    cfgs = {"tiny": (W.TINY, 0),
+            "drift_small": (_small_drift(), 3),
+            "w32g8": (W.STRESS.replace(batch=2, prefill=3000, steps=96, n_q_heads=64, n_kv_heads=8,
+                                       k_full=W.w0(W.STRESS.replace(prefill=3000, steps=96)) // 4,
+                                       k_quant=W.w0(W.STRESS.replace(prefill=3000, steps=96)) // 2), 5),
+            "int4": (_small_drift(quant_bits=4), 2)}
+    cfg, splits = cfgs[name]
+    _run_parity(cfg, torch_cuda, n_splits=splits, check_ledger_every=2, label=f"step-{name}", fused=True)
+
+
+def test_decode_step_equals_append_then_attend(torch_cuda):
+    """The one-call step and the two calls give the same bits: outputs and
+    masses every step, tiers, scores, pages and ledgers at the end; a prompt
+    shorter than the sink unit puts the first new tokens in the sink unit."""
+    torch = torch_cuda
+    for cfg in (_small_drift(steps=64), W.TINY.replace(prefill=2, steps=40)):
+        K, V, Q = gpu_inputs(cfg, W.Workload(cfg))
+        runs = [QEvictGPURun(cfg, K, V, Q, n_splits=3, fused=f) for f in (False, True)]
+        for s in range(cfg.steps):
+            for r in runs:
+                r.step(want_mass=True)
+            torch.cuda.synchronize()
+            assert torch.equal(runs[0].out, runs[1].out), f"{cfg.name} step {s}: outputs"
+            assert torch.equal(runs[0].mass, runs[1].mass), f"{cfg.name} step {s}: masses"
+        for what in ("tiers", "scores", "keys", "values", "kcodes", "vcodes", "kparams", "vparams"):
+            a, b = runs[0].cache.export(what), runs[1].cache.export(what)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), f"{cfg.name}: {what}"
+        log(f"[decode-step] {cfg.name}: {cfg.steps} steps bitwise equal to append + attend")

@@ -81,6 +81,7 @@ def _lib() -> ctypes.CDLL:
         L.qkv_decode_attend.argtypes = [_vp, _vp, _vp, _vp, _vp]
         L.qkv_append_layer.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp]
         L.qkv_set_rope.argtypes = [_vp, _vp, _i32]
+        L.qkv_decode_step_layer.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.qkv_decode_attend_layer.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp]
         L.qkv_route.argtypes = [_vp, _vp]
         L.qkv_prefill_score.argtypes = [_vp, _vp, _i32, _vp]
@@ -248,6 +249,19 @@ class Cache:
             _check_tensor(mass_out, "mass_out", (c.batch, c.n_kv_heads, self.info("units")), "f32")
         _check(_lib().qkv_decode_attend_layer(self.h, int(layer), _ptr(q), _ptr(out), _ptr(mass_out),
                                               _stream(stream)), "qkv_decode_attend")
+
+    def decode_step(self, k, v, q, out, mass_out=None, stream=None, layer: int = 0):
+        """append(k, v) of one token, then decode_attend(q, out, mass_out), in
+        one call (for the window policy one launch): k, v bf16 [B, Hkv, 1, d]."""
+        c = self.c
+        _check_tensor(k, "k", (c.batch, c.n_kv_heads, 1, c.head_dim), "16")
+        _check_tensor(v, "v", (c.batch, c.n_kv_heads, 1, c.head_dim), "16")
+        _check_tensor(q, "q", (c.batch, c.n_q_heads, c.head_dim), "16")
+        _check_tensor(out, "out", (c.batch, c.n_q_heads, c.head_dim), "f32")
+        if mass_out is not None:
+            _check_tensor(mass_out, "mass_out", (c.batch, c.n_kv_heads, self.info("units")), "f32")
+        _check(_lib().qkv_decode_step_layer(self.h, int(layer), _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(mass_out),
+                                            _stream(stream)), "qkv_decode_step")
 
     def set_rope(self, table):
         """table: float32 [n_positions, d/2, 2] device tensor (kept by the caller)."""

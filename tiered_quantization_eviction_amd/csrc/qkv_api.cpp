@@ -540,11 +540,40 @@ int qkv_append(qkv_cache *c, const void *k, const void *v, int32_t n_tokens, qkv
   return qkv_append_layer(c, 0, k, v, n_tokens, stream);
 }
 
+static int decode_attend(qkv_cache *c, int32_t layer, const void *q, float *out, float *mass_out, qkv_stream stream,
+                         const void *k_new = nullptr, const void *v_new = nullptr);
+
 int qkv_decode_attend_layer(qkv_cache *c, int32_t layer, const void *q, float *out, float *mass_out,
                             qkv_stream stream) {
   if (!c || !q || !out || layer < 0 || layer >= c->L) return QKV_EINVAL;
   if (c->Nl[layer] < 1) return QKV_ESTATE;
   if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
+  return decode_attend(c, layer, q, out, mass_out, stream);
+}
+
+int qkv_decode_step_layer(qkv_cache *c, int32_t layer, const void *k, const void *v, const void *q, float *out,
+                          float *mass_out, qkv_stream stream) {
+  if (!c || !k || !v || !q || !out || layer < 0 || layer >= c->L) return QKV_EINVAL;
+  if (c->tok || c->g.rope) {
+    // token policies and rotary keys: the append kernel, then attention
+    const int rc = qkv_append_layer(c, layer, k, v, 1, stream);
+    if (rc != QKV_OK) return rc;
+    return qkv_decode_attend_layer(c, layer, q, out, mass_out, stream);
+  }
+  if ((long long)c->Nl[layer] + 1 > c->cfg.max_ctx) return QKV_ECAPACITY;
+  if (settle(c, (hipStream_t)stream) != QKV_OK) return QKV_EHIP;
+  c->Nl[layer] += 1;   // the launch attends over the new token and stores it in its page
+  c->N = c->Nl[0];
+  return decode_attend(c, layer, q, out, mass_out, stream, k, v);
+}
+
+int qkv_decode_step(qkv_cache *c, const void *k, const void *v, const void *q, float *out, float *mass_out,
+                    qkv_stream stream) {
+  return qkv_decode_step_layer(c, 0, k, v, q, out, mass_out, stream);
+}
+
+static int decode_attend(qkv_cache *c, int32_t layer, const void *q, float *out, float *mass_out, qkv_stream stream,
+                         const void *k_new, const void *v_new) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->ev && c->ev_next < c->ev_n && c->ev_calls++ % c->ev_stride == 0) {
     e0 = c->ev[2 * c->ev_next];
@@ -563,7 +592,7 @@ int qkv_decode_attend_layer(qkv_cache *c, int32_t layer, const void *q, float *o
     c->steps_since_route++;
   } else {
     rc = hip_err(launch_attend(c->g, c->sts[layer], step_info(c, layer), (const uint16_t *)q, out, mass_out,
-                               (hipStream_t)stream, e0, e1));
+                               (hipStream_t)stream, e0, e1, (const uint16_t *)k_new, (const uint16_t *)v_new));
   }
   if (rc != QKV_OK) return rc;
   if (layer == c->L - 1) c->steps++;   // a decode step of the model ends with its last layer

@@ -344,7 +344,8 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const Geom &g, const State &st, const uint16_t *k, const uint16_t *v, int n_tokens,
                          int pos0, hipStream_t s);
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
-                         float *mass_out, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                         float *mass_out, hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                         const uint16_t *k_new = nullptr, const uint16_t *v_new = nullptr);
 hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int a0, int a1, int n_cand,
                         hipStream_t s);
 hipError_t attend_lds_fits(const Geom &g, bool *fits);   // the attention workgroup's LDS fits the device

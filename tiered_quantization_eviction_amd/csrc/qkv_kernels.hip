@@ -175,6 +175,12 @@ struct Ctx {
   half_t *qs_lds;         // per window slot: q*s limbs [2][G][d] (fp16)
   float *rw_lds;          // rotary keys: table rows of the block's window starts [QT][d/2][2]
   const float *rd_lds;    // rotary keys: table rows 0..15 (token offsets in a window) [16][RD_STR]
+  // a token appended by this launch (new_u < 0: none): its unit, tile and row;
+  // lane l < d/4 holds 16-byte chunk l of its K and V rows ([2][d] bf16) in
+  // new_chunk, which the wave that reads the token's tile stages in new_kv
+  int new_u, new_tile, new_row;
+  uint16_t *new_kv;        // LDS [2][d]
+  uint4 new_chunk;
 };
 
 // unit id of entry e; `raw` is the routed-list value fetched for it (used
@@ -313,6 +319,33 @@ __device__ __forceinline__ const uint16_t *ftile_ptr(const Ctx &c, const FBlock 
   return c.st->pages + page_offset(*c.g, c.b, fb.u[s], c.h) + (size_t)fb.tile[s] * 2 * TS * D;
 }
 
+// The tile that holds a token appended by this launch was read before the
+// token reached the page: its row is patched in registers from the LDS copy
+// (K: the lanes of the token's row; V: the lanes of its group of four
+// tokens, element (channel half, token & 3) of each column-tile pair).
+template <int D>
+__device__ __forceinline__ void patch_new_token(const Ctx &c, u32x4v (&kr)[D / 32], u32x4v (&vr)[D / 32]) {
+  if (c.lane < D / 4) *(uint4 *)(c.new_kv + c.lane * 8) = c.new_chunk;
+  wave_lds_sync();
+  const int row = c.new_row;
+  if ((c.lane & 15) == row) {
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) kr[kb] = *(const u32x4v *)(c.new_kv + kb * 32 + c.lq * 8);
+  }
+  if (c.lq == (row >> 2)) {
+#pragma unroll
+    for (int cp = 0; cp < D / 32; ++cp)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int i = hf * 4 + (row & 3);   // the element of the lane's 8
+        const uint32_t v = c.new_kv[D + 32 * cp + c.col + 16 * hf];
+        uint32_t w = vr[cp][i >> 1];
+        w = (i & 1) ? ((w & 0x0000ffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
+        vr[cp][i >> 1] = w;
+      }
+  }
+}
+
 // Attend over block `cur` (tiles in kr, vr); with PF the tiles of block
 // `nxt` are loaded into kr and vr as soon as each has been consumed.
 template <int D, bool PF>
@@ -321,6 +354,11 @@ __device__ __forceinline__ void full_step(WaveState<D> &ws, const Ctx &c, const 
                                           u32x4v (&vr)[2][D / 32]) {
   constexpr int KB = D / 32, CP = D / 32;
   const int tpw = c.g->tpw;
+  if (c.new_u >= 0) {   // wave-uniform; the patch reads LDS only, so no global wait lands here
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (cur.nv[t] > 0 && cur.u[t] == c.new_u && cur.tile[t] == c.new_tile) patch_new_token<D>(c, kr[t], vr[t]);
+  }
   floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -839,7 +877,9 @@ constexpr int QW = 8;
 
 template <int D, int GP, int BITS, bool ROPE>
 __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_qevict_kernel(Geom g, State st, StepInfo si,
-                                                            const uint16_t *__restrict__ q, float scale_log2) {
+                                                            const uint16_t *__restrict__ q, float scale_log2,
+                                                            const uint16_t *__restrict__ k_new,
+                                                            const uint16_t *__restrict__ v_new) {
   constexpr int KB = D / 32;
   constexpr int CT = D / 16;
   const int S = g.n_splits;
@@ -916,6 +956,26 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
   c.qs_lds = s_qs + (size_t)wave * (QT / g.tpw) * 2 * G * QSTR<D>;
+  // Append folded into the launch (k_new, v_new: the step's token of every
+  // (sequence, KV head), [B][Hkv][d]): lane l < d/4 of every wave loads
+  // 16-byte chunk l of its K and V rows now (nothing waits for it here); the
+  // one wave that reads the token's tile stages the chunks in LDS and patches
+  // its row, and wave 0 of the split-0 workgroup stores the rows in the page
+  // at the end (no wave of this launch reads that row from the page).
+  __shared__ __attribute__((aligned(16))) uint16_t s_new[2 * D];
+  const bool fused = !ROPE && k_new != nullptr;
+  const int new_pos = si.N - 1;
+  const int new_u = unit_of(g, new_pos), new_slot = new_pos - unit_start(g, new_u);
+  c.new_u = fused ? new_u : -1;
+  c.new_tile = new_slot / TS;
+  c.new_row = new_slot % TS;
+  c.new_kv = s_new;
+  c.new_chunk = make_uint4(0u, 0u, 0u, 0u);
+  if (!ROPE) {
+    const int l = lane % (D / 4), kv = l / (D / 8), c0 = (l % (D / 8)) * 8;
+    const uint16_t *src = fused ? (kv ? v_new : k_new) + (size_t)bh * D + c0 : q;   // q: any valid address
+    c.new_chunk = *(const uint4 *)src;
+  }
   if (ROPE) {
     float *rw = (float *)(s_qs + (size_t)QW * QT * 2 * G * QSTR<D>);
     float *rd = rw + QW * QT * D;
@@ -942,6 +1002,21 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     run_full<D>(ws, c, f0, f1);
     run_full<D>(ws, c, r0e, r1e);
     run_quant<D, GP, BITS, ROPE>(ws, c, q0, q1);
+  }
+
+  // ---- the appended token into its page (see above) ----
+  if (fused && split == 0 && wave == 0) {
+    uint16_t *kt = st.pages + page_offset(g, b, new_u, h) + (size_t)(new_slot / TS) * 2 * TS * D;
+    const int kv = lane / (D / 8), c0 = (lane % (D / 8)) * 8;
+    if (lane < D / 8) {
+      *(uint4 *)(kt + k_tile_index(new_slot % TS, c0)) = c.new_chunk;
+    } else if (lane < D / 4) {
+      const uint16_t *e = (const uint16_t *)&c.new_chunk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kt[TS * D + v_tile_index(new_slot % TS, c0 + j)] = e[j];
+    }
+    (void)kv;
+    if (h == 0 && lane == 0) st.tier[b * g.U + new_u] = (new_u == 0) ? T_SINK : T_RECENT;
   }
 
   // ---- wave epilogue: fold value-zero term and limbs ----
@@ -1146,7 +1221,8 @@ hipError_t attend_lds_fits(const Geom &g, bool *fits) {
 }
 
 hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, const uint16_t *q, float *out,
-                         float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                         float *mass_out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const uint16_t *k_new, const uint16_t *v_new) {
   float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.d));
   const int grid = g.B * g.Hkv * g.n_splits;
   size_t qs_bytes = attend_qs_bytes(g);
@@ -1155,8 +1231,8 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
   Geom ga = g;
   State sa = st;
   StepInfo sia = si;
-  const uint16_t *qa = q;
-  void *args[] = {&ga, &sa, &sia, &qa, &scale_log2};
+  const uint16_t *qa = q, *ka = k_new, *va = v_new;
+  void *args[] = {&ga, &sa, &sia, &qa, &scale_log2, &ka, &va};
   hipError_t e = hipExtLaunchKernel(attend_fn(g), dim3(grid), dim3(64 * QW), args, qs_bytes, s, ev_start, ev_stop, 0);
   if (e != hipSuccess) return e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
