@@ -1096,13 +1096,17 @@ __device__ inline void split_stats(const Geom &g, const State &st, int b, int h,
   invL = 1.0f / l;
 }
 
+// Entries per mass block of the merge (four lanes per entry).
+constexpr int MERGE_ENTRIES = 64;
+
 template <int G>
 __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, StepInfo si, float *__restrict__ out,
                                                            float *__restrict__ mass_out, int n_chunks) {
-  constexpr int CH = 8;   // splits / KV heads whose loads are issued together
+  constexpr int CH = 4;   // splits whose loads are issued together
   const int S = g.n_splits, D = g.d;
   const int n_out_blocks = g.B * g.Hkv;
   __shared__ float sM[128], sInvL[128];   // Hkv*G = Hq <= 128
+  __shared__ float sPart[4][MERGE_ENTRIES];
   if ((int)blockIdx.x < n_out_blocks) {
     // outputs of one (sequence, KV head): each thread folds the split
     // partials of its outputs with the LSE rule on its own
@@ -1135,55 +1139,62 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     }
     return;
   }
-  // masses of up to 256 live entries of one sequence -> window scores, kept
-  // in list order (the unit of an entry is needed only for mass_out); the
-  // old score and first KV heads' (rho, m) pairs are loaded before the wait
-  // for the split statistics
+  // masses of MERGE_ENTRIES live entries of one sequence -> list-order scores:
+  // lane q of an entry's four sums the KV heads h = q, q + 4, ... (in that
+  // order), and the four partial sums are added in order q = 0..3; the old
+  // score and the lane's (rho, m) pairs are loaded before the wait for the
+  // split statistics
   const int mb = blockIdx.x - n_out_blocks;
   const int b = mb / n_chunks, chunk = mb % n_chunks;
   const EntryList L = make_list(g, st, si, b);
   const int E = L.count();
-  const int e = chunk * blockDim.x + threadIdx.x;
+  const int el = threadIdx.x % MERGE_ENTRIES, q = threadIdx.x / MERGE_ENTRIES;
+  const int e = chunk * MERGE_ENTRIES + el;
   const int ee = min(e, E - 1);
-  const float old = st.slist[b * g.U + ee];
   const int u_out = mass_out ? entry_unit(L, st.routed + b * g.U, ee) : 0;
-  float4 mp[CH][G / 2];   // (rho, m) of the G heads, per KV head
+  constexpr int HPL = 2;   // KV heads per lane whose loads go out together
+  float4 mp[HPL][G / 2];
   auto load_heads = [&](int h0) {
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int h = min(h0 + k, g.Hkv - 1);
+    for (int k = 0; k < HPL; ++k) {
+      const int h = min(h0 + 4 * k, g.Hkv - 1);
       const float4 *src = (const float4 *)(st.mass_part + ((size_t)(b * g.Hkv + h) * (g.U + 1) + ee) * G * 2);
 #pragma unroll
-      for (int q = 0; q < G / 2; ++q) mp[k][q] = src[q];
+      for (int j = 0; j < G / 2; ++j) mp[k][j] = src[j];
     }
   };
-  load_heads(0);
+  load_heads(q);
   for (int it = threadIdx.x; it < g.Hkv * G; it += blockDim.x) split_stats(g, st, b, it / G, it % G, sM[it], sInvL[it]);
   __syncthreads();
-  float total = 0.0f;
-  for (int h0 = 0; h0 < g.Hkv; h0 += CH) {
-    if (h0 > 0) load_heads(h0);
+  float part = 0.0f;
+  for (int h0 = q; h0 < g.Hkv; h0 += 4 * HPL) {
+    if (h0 > q) load_heads(h0);
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int h = h0 + k;
+    for (int k = 0; k < HPL; ++k) {
+      const int h = h0 + 4 * k;
       if (h >= g.Hkv) break;
       float gs = 0.0f;
 #pragma unroll
-      for (int q = 0; q < G / 2; ++q) {
-        const float r2[2] = {mp[k][q].x, mp[k][q].z}, m2[2] = {mp[k][q].y, mp[k][q].w};
+      for (int j = 0; j < G / 2; ++j) {
+        const float r2[2] = {mp[k][j].x, mp[k][j].z}, m2[2] = {mp[k][j].y, mp[k][j].w};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int hh = 2 * q + t;
+          const int hh = 2 * j + t;
           float v = (m2[t] == neg_inf()) ? 0.0f : r2[t] * exp2f(m2[t] - sM[h * G + hh]) * sInvL[h * G + hh];
           if (!(v >= 1.17549435e-38f)) v = 0.0f;   // a head's mass below FLT_MIN counts as 0
           gs += v;
         }
       }
       if (mass_out && e < E) mass_out[((size_t)b * g.Hkv + h) * g.U + u_out] = gs;
-      total += gs;
+      part += gs;
     }
   }
-  if (e < E) st.slist[b * g.U + e] = old + total;
+  sPart[q][el] = part;
+  __syncthreads();
+  if (q == 0 && e < E) {
+    const float total = (sPart[0][el] + sPart[1][el]) + (sPart[2][el] + sPart[3][el]);
+    st.slist[b * g.U + e] += total;
+  }
 }
 
 // LDS of one attention workgroup beyond its static arrays: the q*s limbs of
@@ -1241,7 +1252,7 @@ hipError_t launch_attend(const Geom &g, const State &st, const StepInfo &si, con
     if (e != hipSuccess) return e;
   }
   const int n_live = si.has_sink + si.n_routed + (si.r1 >= si.r0 ? si.r1 - si.r0 + 1 : 0);   // entries this step
-  const int n_chunks = (n_live + 255) / 256;
+  const int n_chunks = (n_live + MERGE_ENTRIES - 1) / MERGE_ENTRIES;
   const dim3 mgrid(g.B * g.Hkv + g.B * n_chunks);
   if (g.G == 4)
     hipLaunchKernelGGL(merge_qevict_kernel<4>, mgrid, dim3(256), 0, s, g, st, si, out, mass_out, n_chunks);
