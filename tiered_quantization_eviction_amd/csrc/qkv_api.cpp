@@ -139,6 +139,7 @@ void make_geom(const qkv_config *c, Geom &g) {
     const long long per = (long long)c->k_full + c->k_quant < g.U ? (long long)c->k_full + c->k_quant : g.U;
     const long long P = (long long)(c->n_layers > 1 ? c->n_layers : 1) * g.B * per;
     g.pool_slots = P > 0 ? (int)P : 1;
+    g.pool_per = (int)per;
   }
   int S = c->n_splits;
   if (S == 0) {   // one resident round: 256 workgroups of 8 waves = 1 per compute unit, 2 waves per SIMD
@@ -206,12 +207,13 @@ size_t carve(const Geom &g, int L, char *base, State *sts) {
   memset(&sh, 0, sizeof sh);
   sh.ledger = (uint8_t *)take((size_t)g.pool_slots * g.Hkv * (size_t)g.ledger_unit_bytes);
   sh.pool_stack = (int32_t *)take((size_t)g.pool_slots * 4);
-  sh.pool_top = (int32_t *)take(16);
+  sh.pool_top = (int32_t *)take((size_t)L * g.B * 4);
   sh.part_o = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * g.d * 4);
   sh.part_ml = (float *)take((size_t)g.B * g.Hkv * g.n_splits * g.G * 2 * 4);
   sh.mass_part = (float *)take((size_t)g.B * g.Hkv * (g.U + 1) * g.G * 2 * 4);
   for (int l = 0; l < L; ++l) {
     State st = sh;
+    st.layer = l;
     st.pages = (uint16_t *)take(BU * g.Hkv * (size_t)g.page_unit_elems * 2);
     st.tier = (uint8_t *)take(BU);
     st.has_ledger = (uint8_t *)take(BU);
@@ -858,15 +860,22 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
     std::vector<uint8_t> f(need);
     if (hipMemcpyAsync(f.data(), src, need, hipMemcpyDeviceToHost, s) != hipSuccess) return QKV_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;
+    // each (layer, sequence) takes the first slots of its range, in window
+    // order; the rest of the range is its free stack
     const size_t BU = (size_t)c->g.B * c->g.U;
-    std::vector<int32_t> slot(need, 0);
-    int next = 0;
-    for (size_t i = 0; i < need; ++i)
-      if (f[i]) slot[i] = ++next;
-    if (next > c->g.pool_slots) return QKV_EINVAL;   // more ledgers than the pool holds
-    std::vector<int32_t> stack(c->g.pool_slots);
-    for (int i = next; i < c->g.pool_slots; ++i) stack[i - next] = i;
-    const int32_t top = c->g.pool_slots - next;
+    const int per = c->g.pool_per, nR = c->L * c->g.B;
+    std::vector<int32_t> slot(need, 0), stack((size_t)nR * per), top(nR);
+    for (int r = 0; r < nR; ++r) {
+      int next = 0;
+      for (int u = 0; u < c->g.U; ++u)
+        if (f[(size_t)r * c->g.U + u]) {
+          if (next >= per) return QKV_EINVAL;   // more ledgers than the range holds
+          slot[(size_t)r * c->g.U + u] = r * per + next + 1;
+          ++next;
+        }
+      for (int i = next; i < per; ++i) stack[(size_t)r * per + (i - next)] = r * per + i;
+      top[r] = per - next;
+    }
     for (int l = 0; l < c->L; ++l) {
       const State &st = c->sts[l];
       if (hipMemcpyAsync(st.has_ledger, (const uint8_t *)src + BU * l, BU, hipMemcpyDeviceToDevice, s) != hipSuccess ||
@@ -875,7 +884,7 @@ int qkv_import(qkv_cache *c, int32_t what, const void *src, size_t bytes, qkv_st
     }
     const State &st0 = c->sts[0];
     if (hipMemcpyAsync(st0.pool_stack, stack.data(), stack.size() * 4, hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipMemcpyAsync(st0.pool_top, &top, 4, hipMemcpyHostToDevice, s) != hipSuccess)
+        hipMemcpyAsync(st0.pool_top, top.data(), top.size() * 4, hipMemcpyHostToDevice, s) != hipSuccess)
       return QKV_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return QKV_EHIP;   // the host vectors go out of scope
     c->ledger_ready = true;

@@ -54,6 +54,7 @@ struct Geom {
   int tile_block_bytes;
   int tr_per_seq;        // workgroups per sequence of the pack/promote launch (one resident round)
   int pool_slots;        // ledger-pool slots of the cache (every layer)
+  int pool_per;          // slots of one (layer, sequence): its range of the pool
   int rope;              // keys arrive before the rotary embedding (table in State::rope)
 };
 
@@ -83,8 +84,9 @@ struct State {
   int32_t *victims;     // [B][U] windows the last routing event evicted, in rank order (-1 past them)
   int32_t *free_list;   // [B][U] windows whose ledger the last routing event released
   int32_t *free_count;  // [B]
-  int32_t *pool_stack;  // [pool_slots] free slots (shared by every layer)
-  int32_t *pool_top;    // [1] free slots on the stack (shared by every layer)
+  int32_t *pool_stack;  // [L*B][pool_per] free slots of each (layer, sequence)'s range of the pool
+  int32_t *pool_top;    // [L*B] free slots on each stack
+  int layer;            // this state's layer (its pool ranges are layer * B + b)
   // rotary embedding (Geom::rope): the caller's table [positions][d/2][cos, sin]
   // and the keys as appended, before the rotation, [B][U][Hkv][tpw*TS][d]
   // (packing reads them; the pages hold the rotated keys)

@@ -1318,7 +1318,7 @@ __device__ inline void bitonic_desc_u64(unsigned long long *keys, int n) {
 
 __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, StepInfo si, int a0, int a1, int npow) {
   extern __shared__ unsigned long long keys[];
-  __shared__ int n_pack, n_prom, n_free, n_reuse, n_demote;
+  __shared__ int n_pack, n_prom, n_free, n_reuse, n_demote, s_top;
   const int b = blockIdx.x;
   const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
   const int RC = nF + nQ;
@@ -1382,7 +1382,44 @@ __global__ __launch_bounds__(1024) void route_qevict_kernel(Geom g, State st, St
     if (r < KFQ) st.routed[b * g.U + r] = u;
   }
   __syncthreads();
+  // ledger slots: the evicted windows' go back on this (layer, sequence)'s
+  // stack, then the windows packed for the first time take theirs (a failed
+  // pop is latched and leaves the window without codes, never an
+  // out-of-range access); then the new list's quantized entries get their
+  // slots (qslot), which the attention kernel reads instead of window ids
+  {
+    const int range = st.layer * g.B + b, per = g.pool_per;
+    int32_t *stack = st.pool_stack + (size_t)range * per;
+    if (threadIdx.x == 0) s_top = st.pool_top[range];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_free; i += blockDim.x) {
+      const int u = st.free_list[b * g.U + i];
+      const int slot = st.lslot[b * g.U + u] - 1;
+      st.lslot[b * g.U + u] = 0;
+      if (slot < 0) continue;
+      const int p = atomicAdd(&s_top, 1);
+      if (p >= 0 && p < per)
+        stack[p] = slot;
+      else
+        st.status[0] = QKV_ECAPACITY;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_pack; i += blockDim.x) {
+      const int u = st.pack_list[b * g.U + i];
+      const int p = atomicSub(&s_top, 1) - 1;
+      int slot = -1;
+      if (p >= 0 && p < per)
+        slot = stack[p];
+      else
+        st.status[0] = QKV_ECAPACITY;
+      st.lslot[b * g.U + u] = slot + 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) st.pool_top[range] = max(s_top, 0);
+  }
   const int nF2 = min(n, g.k_full), nQ2 = max(0, min(n - g.k_full, g.k_quant));
+  for (int r = nF2 + threadIdx.x; r < nF2 + nQ2; r += blockDim.x)
+    st.qslot[b * g.U + r] = st.lslot[b * g.U + st.routed[b * g.U + r]] - 1;
   if (threadIdx.x == 0) {
     st.routed_nf[b] = nF2;
     st.routed_nq[b] = nQ2;
@@ -1439,56 +1476,17 @@ __global__ __launch_bounds__(256) void slist_sync_kernel(Geom g, State st, StepI
   if (e < L.count()) st.score[b * g.U + entry_unit(L, st.routed + b * g.U, e)] = st.slist[b * g.U + e];
 }
 
-// Ledger pool: the slots a routing event released go back on the free-slot
-// stack in one kernel, and the windows packed for the first time take slots
-// in the next, so pushes and pops never overlap.  Every (layer, sequence)
-// holds at most K_f + K_q slots after its event and the pool has that many
-// for each, so a pop always finds a slot (a failed one is latched, never
-// followed by an out-of-range access).
-__global__ __launch_bounds__(256) void pool_free_kernel(Geom g, State st) {
-  const int b = blockIdx.x;
-  const int n = st.free_count[b];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int u = st.free_list[b * g.U + i];
-    const int slot = st.lslot[b * g.U + u] - 1;
-    st.lslot[b * g.U + u] = 0;
-    if (slot < 0) continue;
-    const int pos = atomicAdd(st.pool_top, 1);
-    if (pos >= 0 && pos < g.pool_slots)
-      st.pool_stack[pos] = slot;
-    else
-      st.status[0] = QKV_ECAPACITY;
-  }
-}
-
-// ... and the ranked list's quantized entries get their slots (qslot), which
-// the attention kernel reads instead of the window ids
-__global__ __launch_bounds__(256) void pool_alloc_kernel(Geom g, State st) {
-  const int b = blockIdx.x;
-  const int n = st.pack_count[b];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int u = st.pack_list[b * g.U + i];
-    const int pos = atomicSub(st.pool_top, 1) - 1;
-    int slot = -1;
-    if (pos >= 0 && pos < g.pool_slots)
-      slot = st.pool_stack[pos];
-    else
-      st.status[0] = QKV_ECAPACITY;
-    st.lslot[b * g.U + u] = slot + 1;
-  }
-  __syncthreads();
-  const int nF = st.routed_nf[b], nQ = st.routed_nq[b];
-  for (int r = nF + threadIdx.x; r < nF + nQ; r += blockDim.x)
-    st.qslot[b * g.U + r] = st.lslot[b * g.U + st.routed[b * g.U + r]] - 1;
-}
-
-__global__ void pool_init_kernel(int32_t *stack, int32_t *top, int n) {
+// Ledger pool: one range of pool_per slots per (layer, sequence), enough for
+// the K_f + K_q windows it can hold; its free slots are a stack that only the
+// routing workgroup of that (layer, sequence) touches.
+__global__ void pool_init_kernel(int32_t *stack, int32_t *top, int n, int per) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) stack[i] = i;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *top = n;
+  const int n_ranges = per > 0 ? n / per : 0;
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n_ranges; r += gridDim.x * blockDim.x) top[r] = per;
 }
 
 hipError_t launch_pool_init(const Geom &g, const State &st, hipStream_t s) {
-  hipLaunchKernelGGL(pool_init_kernel, dim3(64), dim3(256), 0, s, st.pool_stack, st.pool_top, g.pool_slots);
+  hipLaunchKernelGGL(pool_init_kernel, dim3(64), dim3(256), 0, s, st.pool_stack, st.pool_top, g.pool_slots, g.pool_per);
   return hipGetLastError();
 }
 
@@ -1730,10 +1728,6 @@ hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int 
                      a1, npow);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pool_free_kernel, dim3(g.B), dim3(256), 0, s, g, st);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(pool_alloc_kernel, dim3(g.B), dim3(256), 0, s, g, st);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int per_seq = g.tr_per_seq > 0 ? g.tr_per_seq : 128;
   const dim3 tg(g.B * per_seq), tb(TR_THREADS);
   if (g.d == 128 && g.bits == 4)
