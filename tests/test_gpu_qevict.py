@@ -417,3 +417,27 @@ def test_decode_step_equals_append_then_attend(torch_cuda):
             torch.cuda.synchronize()
             assert torch.equal(a, b), f"{cfg.name}: {what}"
         log(f"[decode-step] {cfg.name}: {cfg.steps} steps bitwise equal to append + attend")
+
+
+def test_same_inputs_give_the_same_bits(torch_cuda):
+    """Two caches fed the same inputs produce the same bits, launch after
+    launch: the work of every attention launch is dealt to the waves by
+    (split, wave) alone and every reduction runs in a fixed order, also in
+    the all-full-precision launches before the first routing event (16
+    sequences, 8 KV heads, an 8K prompt: 256 workgroups, as at full size)."""
+    torch = torch_cuda
+    cfg = _small_drift(batch=16, n_q_heads=32, n_kv_heads=8, prefill=8192, steps=48,
+                       cluster_a=(200, 64), cluster_b=(8, 32), switch_step=30)
+    K, V, Q = gpu_inputs(cfg, W.Workload(cfg))
+    runs = [QEvictGPURun(cfg, K, V, Q, fused=True) for _ in range(2)]
+    for s in range(cfg.steps):
+        for r in runs:
+            r.step(want_mass=True)
+        torch.cuda.synchronize()
+        assert torch.equal(runs[0].out, runs[1].out), f"step {s}: outputs"
+        assert torch.equal(runs[0].mass, runs[1].mass), f"step {s}: masses"
+    for what in ("tiers", "scores", "kcodes", "kparams", "keys"):
+        a, b = runs[0].cache.export(what), runs[1].cache.export(what)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), what
+    log(f"[same-bits] {cfg.steps} steps of two caches bitwise equal")
