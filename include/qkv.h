@@ -366,6 +366,12 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  *                                                  first (their scores: SCORES; their positions:
  *                                                  the window spans), -1 past them
  *   (EVENT and VICTIMS are diagnostics: export only)
+ * H2O also writes them per (sequence, KV head) at every eviction call that
+ * ranks: EVENT int32 [batch, n_kv_heads, 16] with tokens, candidates, kept
+ * heavy hitters, evicted (words 0..4 with 1 and 3 as above: 2 kept, 3 zero,
+ * 4 evicted), the margin at the heavy-hitter cut (word 10, also word 12;
+ * word 11 +inf); VICTIMS int32 [batch, n_kv_heads, max_ctx] the evicted
+ * positions, best-ranked first (their age is tokens - 1 - position).
  * (units without a ledger export zero codes and parameters).  A cache of
  * n_layers > 1 exports every per-layer kind as n_layers such arrays, layer
  * after layer (STATE once; QKV_ESTATE unless every layer holds the same

@@ -31,7 +31,7 @@ import numpy as np
 
 from .attention import attend
 from .numerics import FLT_MIN, bf16_to_f64
-from .rank import order
+from .rank import cut_margins, order
 
 
 def update_and_evict(positions, scores, weights, *, n_heavy: int, n_recent: int, n_sink: int = 0,
@@ -55,6 +55,22 @@ def update_and_evict(positions, scores, weights, *, n_heavy: int, n_recent: int,
     keep = np.ones(len(positions), bool)
     keep[victim] = False
     return new, int(positions[victim]), positions[keep]
+
+
+def eviction_margin(positions, scores, *, n_heavy: int, n_recent: int, n_sink: int = 0) -> float:
+    """The relative score gap at the heavy-hitter cut of one H2O step (the
+    H2O notes, section 5.1: log how close each eviction was), on the
+    updated scores of the kept set including the new position: the same
+    candidates update_and_evict ranks, the cut after the best n_heavy;
+    +inf when nothing is evicted."""
+    positions = np.asarray(positions, np.int64)
+    scores = np.asarray(scores, np.float64)
+    if len(positions) <= n_sink + n_heavy + n_recent:
+        return float("inf")
+    newest = np.sort(positions)[-n_recent:] if n_recent else np.array([], np.int64)
+    protected = np.isin(positions, newest) | (positions < n_sink)
+    cand = np.flatnonzero(~protected)
+    return cut_margins(scores[cand], positions[cand], np.ones(len(cand), bool), [n_heavy])[0]
 
 
 class H2OGroup:
@@ -110,6 +126,9 @@ class H2OGroup:
         new, victim, kept = update_and_evict(self.pos, self.score, w, n_heavy=self.n_heavy,
                                              n_recent=self.n_recent, n_sink=self.n_sink,
                                              budget=self.budget)
+        self.last_margin = eviction_margin(self.pos, new, n_heavy=self.n_heavy, n_recent=self.n_recent,
+                                           n_sink=self.n_sink)
+        self.last_victim = victim
         keep = np.isin(self.pos, kept)
         self.pos, self.score = self.pos[keep], new[keep]
         return out, w, d_pos, victim

@@ -63,6 +63,21 @@ def _run_h2o(cfg, torch, n_splits=0, label=""):
             np.testing.assert_allclose(scores[b, g, grp.pos[order]], grp.score[order], rtol=SCORE_RTOL, atol=1e-7,
                                        err_msg=f"{tag}: scores of (seq {b}, head {g})")
 
+    def check_log(tag, n_tokens):
+        """The eviction record of the step against the oracle's eviction:
+        the victim exactly, the margin at the heavy-hitter cut to 2e-4."""
+        recs = cache.last_event()
+        for (b, g), grp in groups.items():
+            r = recs[b * Hkv + g]
+            victim = grp.last_victim
+            assert r["tokens"] == n_tokens, (tag, r)
+            assert r["victims"] == ([] if victim is None else [victim]), f"{tag}: victims of (seq {b}, head {g})"
+            m = grp.last_margin
+            if np.isinf(m):
+                assert np.isinf(r["margin_full"]), (tag, b, g, r)
+            else:
+                assert abs(r["margin_full"] - m) <= 2 * SCORE_RTOL, f"{tag}: margin {r['margin_full']} vs {m}"
+
     check_sets("after the trimmed prompt")
     worst = 0.0
     qs = {b: wl.queries(b) for b in range(B)}
@@ -79,6 +94,7 @@ def _run_h2o(cfg, torch, n_splits=0, label=""):
             worst = max(worst, err)
             assert err <= OUT_TOL, f"step {s} (seq {b}, head {g}): out err {err}"
         check_sets(f"step {s}")
+        check_log(f"step {s}", t + 1)
     log(f"[{label}] worst out err {worst:.3e}")
 
 

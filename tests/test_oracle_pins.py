@@ -368,3 +368,34 @@ def test_qevict_flush_applies_to_unit_sums():
     assert mass[0, 1] == pytest.approx(8 * p, rel=1e-12)
     assert mass[0, 2] == 0.0
     assert seq.score[1] == pytest.approx(8 * p, rel=1e-12) and seq.score[2] == 0.0
+
+
+def test_cut_margins_hand_cases():
+    """H2O notes section 5.1 (log the cutoff margin of each eviction): the
+    relative gap lowest kept minus highest dropped, over the larger of the
+    two, at each cut of the (score desc, position desc) ranking; +inf where
+    a cut falls outside the list.  Hand cases, including a tie straddling a
+    cut (margin 0) and a tie broken by position."""
+    from oracle.rank import cut_margins
+    m = cut_margins([5.0, 3.0, 3.0, 1.0], [0, 1, 2, 3], [1, 1, 1, 1], [1, 2, 3, 4, 0])
+    assert m[0] == 0.4 and m[1] == 0.0 and abs(m[2] - 2.0 / 3.0) < 1e-15
+    assert m[3] == float("inf") and m[4] == float("inf")
+    # ineligible entries are left out of the ranking
+    assert cut_margins([9.0, 4.0, 2.0], [0, 1, 2], [0, 1, 1], [1]) == [0.5]
+    # equal scores: the newer position ranks first, the gap is 0
+    assert cut_margins([2.0, 2.0, 1.0], [10, 20, 5], [1, 1, 1], [1, 2]) == [0.0, 0.5]
+
+
+def test_h2o_eviction_margin_hand_case():
+    """One sink, two recent, three heavy hitters, seven kept positions after
+    the append: positions 1..4 compete, scores 0.5, 0.2, 0.9, 0.3; the best
+    three stay (3, 1, 4), position 2 goes, and the gap at the cut is
+    (0.3 - 0.2) / 0.3.  With six positions nothing is evicted (+inf)."""
+    from oracle import h2o as oh
+    pos = np.arange(7)
+    sc = np.array([9.0, 0.5, 0.2, 0.9, 0.3, 0.0, 0.0])
+    m = oh.eviction_margin(pos, sc, n_heavy=3, n_recent=2, n_sink=1)
+    assert abs(m - (0.3 - 0.2) / 0.3) < 1e-15
+    new, victim, kept = oh.update_and_evict(pos, sc, np.zeros(7), n_heavy=3, n_recent=2, n_sink=1)
+    assert victim == 2 and sorted(kept.tolist()) == [0, 1, 3, 4, 5, 6]
+    assert oh.eviction_margin(pos[:6], sc[:6], n_heavy=3, n_recent=2, n_sink=1) == float("inf")

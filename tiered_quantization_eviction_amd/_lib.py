@@ -303,19 +303,24 @@ class Cache:
                f"qkv_import({what})")
 
     def last_event(self, layer: int = 0) -> list[dict]:
-        """The last routing event of each sequence of `layer` (QEvict): its
-        counters, cut margins and victims (window ids, best-ranked first)."""
+        """The last routing event of each sequence of `layer` (QEvict), or the
+        last eviction call of each (sequence, KV head) (H2O, in b * Hkv + h
+        order): its counters, cut margins and victims (window ids or
+        positions, best-ranked first)."""
         import numpy as np
         import torch
-        ev = self.export("event").cpu().numpy().view(np.int32).reshape(-1, self.c.batch, 16)[layer]
-        vic = self.export("victims").cpu().numpy().view(np.int32).reshape(-1, self.c.batch,
-                                                                             self.info("units"))[layer]
+        n_unit = self.c.max_ctx if self.c.policy == POLICY["h2o"] else self.info("units")
+        ev = self.export("event").cpu().numpy().view(np.int32).reshape(-1, 16)
+        vic = self.export("victims").cpu().numpy().view(np.int32).reshape(-1, n_unit)
         torch.cuda.synchronize()
+        if self.c.policy != POLICY["h2o"]:
+            B = self.c.batch
+            ev, vic = ev[layer * B:(layer + 1) * B], vic[layer * B:(layer + 1) * B]
         out = []
-        for b in range(self.c.batch):
-            r = {k: int(ev[b, i]) for i, k in enumerate(EVENT_FIELDS)}
-            r.update({k: float(ev[b, 10 + i:11 + i].view(np.float32)[0]) for i, k in enumerate(EVENT_MARGINS)})
-            r["victims"] = [int(u) for u in vic[b, :r["evicted"]]]
+        for r_ev, r_vic in zip(ev, vic):
+            r = {k: int(r_ev[i]) for i, k in enumerate(EVENT_FIELDS)}
+            r.update({k: float(r_ev[10 + i:11 + i].view(np.float32)[0]) for i, k in enumerate(EVENT_MARGINS)})
+            r["victims"] = [int(u) for u in r_vic[:r["evicted"]]]
             out.append(r)
         return out
 

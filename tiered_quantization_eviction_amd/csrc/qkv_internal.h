@@ -306,6 +306,9 @@ struct TokState {
   int32_t *qpos[3];     // [B][Hkv][NCT*TS] their positions
   int32_t *cnt;         // [B][Hkv][4] tokens per ranked tier (BF16, INT4, INT2, INT1)
   unsigned long long *cuts;   // [B][Hkv][4] cut keys of the last assignment
+  // H2O
+  int32_t *event;       // [B][Hkv][EV_WORDS] record of the last eviction call that ranked
+  int32_t *victims;     // [B][Hkv][T] positions it evicted, best-ranked first (-1 past them)
 };
 
 // Per-call scalars the host knows: tokens so far, first position not yet

@@ -69,6 +69,12 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.cuts = nullptr;
   st.hqold = nullptr;
   st.hqkey = nullptr;
+  st.event = nullptr;
+  st.victims = nullptr;
+  if (g.policy == QKV_POLICY_H2O) {
+    st.event = (int32_t *)take(BH * EV_WORDS * 4);
+    st.victims = (int32_t *)take(BH * g.T * 4);
+  }
   for (int k = 0; k < 3; ++k) {
     st.qtiles[k] = nullptr;
     st.qpos[k] = nullptr;
@@ -1162,7 +1168,7 @@ __device__ __forceinline__ void tok_copy_token(const TokGeom &g, const uint16_t 
 }
 
 __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState st, int n_old, int a0, int a1,
-                                                             int npow) {
+                                                             int npow, int N) {
   extern __shared__ unsigned long long keys[];
   const int bh = blockIdx.x;
   const int b = bh / g.Hkv, h = bh % g.Hkv;
@@ -1181,10 +1187,31 @@ __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState
   __syncthreads();
   tok_bitonic_desc(keys, npow);
   const int keep = n < g.k_heavy ? n : g.k_heavy;
+  int32_t *vic = st.victims + tb;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int pos = (int)(keys[i] & 0xffffffffull) - 1;
     st.tier[tb + pos] = i < keep ? T_FULL : T_EVICTED;
     if (i < keep) cpos[i] = pos;
+    else vic[i - keep] = pos;
+  }
+  for (int i = n - keep + threadIdx.x; i < g.T; i += blockDim.x) vic[i] = -1;
+  if (threadIdx.x == 0) {
+    // the eviction record: candidates, kept, evicted and the relative score
+    // gap across the cut (lowest kept minus highest evicted, over the larger)
+    int32_t *ev = st.event + (size_t)bh * EV_WORDS;
+    float m = __builtin_inff();
+    if (keep > 0 && keep < n) {
+      const float hi = __uint_as_float((uint32_t)(keys[keep - 1] >> 32)), lo = __uint_as_float((uint32_t)(keys[keep] >> 32));
+      m = (hi - lo) / fmaxf(fmaxf(fabsf(hi), fabsf(lo)), 1.17549435e-38f);
+    }
+    for (int k = 0; k < EV_WORDS; ++k) ev[k] = 0;
+    ev[EV_TOKENS] = N;
+    ev[EV_CANDIDATES] = n;
+    ev[EV_FULL] = keep;
+    ev[EV_EVICTED] = n - keep;
+    ev[EV_MARGIN_FULL] = __float_as_int(m);
+    ev[EV_MARGIN_QUANT] = __float_as_int(__builtin_inff());
+    ev[EV_MARGIN_MIN] = __float_as_int(m);
   }
   // gather the kept tokens (rank order) into the compact tiles
   const int chunks = g.d / 8;
@@ -1201,7 +1228,7 @@ hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep 
   int npow = 1;
   while (npow < n_cand) npow <<= 1;
   hipLaunchKernelGGL(tok_route_h2o_kernel, dim3(g.B * g.Hkv), dim3(1024), npow * sizeof(unsigned long long), s, g,
-                     st, ts.n_cmp, a0, a1, npow);
+                     st, ts.n_cmp, a0, a1, npow, ts.N);
   return hipGetLastError();
 }
 
@@ -1994,6 +2021,9 @@ __global__ __launch_bounds__(256) void tok_export_kernel(TokGeom g, TokState st,
 
 hipError_t tok_launch_export(const TokGeom &g, const TokState &st, int what, void *dst, hipStream_t s) {
   const size_t n = (size_t)g.B * g.Hkv * g.T;
+  if (what == QKV_EXPORT_EVENT)
+    return hipMemcpyAsync(dst, st.event, (size_t)g.B * g.Hkv * EV_WORDS * 4, hipMemcpyDeviceToDevice, s);
+  if (what == QKV_EXPORT_VICTIMS) return hipMemcpyAsync(dst, st.victims, n * 4, hipMemcpyDeviceToDevice, s);
   int grid = (int)((n + 255) / 256);
   grid = grid > 4096 ? 4096 : (grid < 1 ? 1 : grid);
   hipLaunchKernelGGL(tok_export_kernel, dim3(grid), dim3(256), 0, s, g, st, what, dst);
