@@ -178,7 +178,9 @@ int qkv_create_static(const qkv_config *cfg, qkv_stream stream, qkv_cache **out)
  * Policies.
  * QKV_POLICY_QEVICT: window units (window = 8, 16 or 32 tokens), one score
  *   per (sequence, window) summed over all query heads, three tiers (full
- *   precision, INT2 ledger, evicted); routing every omega steps.
+ *   precision, INT2 or INT4 ledger, evicted); routing every omega steps.  At
+ *   most 16383 windows per sequence (the routing sort holds 16384 keys in
+ *   LDS): max_ctx up to about 262K tokens at window = 16.
  * QKV_POLICY_H2O (H2O notes, sections 1.1-2.1 and the GQA paragraph): token
  *   units (window = 1, k_quant = 0), one score per (sequence, KV head, token)
  *   summed over the G query heads of that KV head; k_full is the heavy-hitter

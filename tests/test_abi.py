@@ -213,3 +213,13 @@ def test_rope_config_checks_on_host():
     h = L.make_config(W.H2O, rope=1)
     assert lib.qkv_check_config(ctypes.byref(h)) == L.EINVAL       # the window policy only
     assert lib.qkv_set_rope(None, ctypes.c_void_p(256), 1 << 20) == L.EINVAL
+
+
+def test_window_policy_context_limit():
+    """The routing sort holds 16384 candidates: a window-policy cache may
+    have up to 16383 windows per sequence (about 262K tokens at 16-token
+    windows), one more is refused."""
+    L, lib = _lib()
+    for max_ctx, ok in ((5 + 16382 * 16, True), (5 + 16383 * 16, False), (140000, True)):
+        c = L.make_config(W.TINY.replace(window=16, omega=16, n_sink=5), max_ctx=max_ctx)
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, max_ctx

@@ -441,3 +441,13 @@ def test_same_inputs_give_the_same_bits(torch_cuda):
         torch.cuda.synchronize()
         assert torch.equal(a, b), what
     log(f"[same-bits] {cfg.steps} steps of two caches bitwise equal")
+
+
+def test_qevict_long_context_parity(torch_cuda):
+    """More than 8192 candidate windows at the first routing event (a
+    140000-token prompt at 16-token windows: 8744 windows, a 16384-key sort
+    that does not fit one key per thread): tiers, ledgers and contents
+    bit-exact, outputs and scores to the usual bars."""
+    c = W.TINY.replace(prefill=140000, steps=40, window=16, omega=16, n_sink=5, n_recent=32, k_full=100,
+                       k_quant=300)
+    _run_parity(c, torch_cuda, n_splits=4, label="long-context")

@@ -102,7 +102,7 @@ int validate(const qkv_config *c) {
   // windows of one tile
   if (c->head_dim == 128 && G == 8 && c->window <= TS) return QKV_EINVAL;
   const long long U = 1 + ((long long)c->max_ctx - c->n_sink + c->window - 1) / c->window;
-  if (U + 1 > SORT_MAX) return QKV_EINVAL;            // routing candidates are ranked in LDS
+  if (U + 1 > ROUTE_SORT_MAX) return QKV_EINVAL;      // routing candidates are ranked in LDS
   return QKV_OK;
 }
 

@@ -34,7 +34,8 @@ namespace qkv {
 constexpr int TS = 16;           // token slots per tile
 constexpr int WAVE = 64;
 constexpr int ATT_WAVES = 4;     // waves per attention workgroup
-constexpr int SORT_MAX = 8192;   // largest routing candidate set (LDS sort)
+constexpr int SORT_MAX = 8192;          // largest LDS sort of the token policies and the stateless ranking
+constexpr int ROUTE_SORT_MAX = 16384;   // largest window-policy candidate set (8-byte keys, 128 KB of LDS)
 
 enum : uint8_t { T_EMPTY = 0, T_SINK = 1, T_RECENT = 2, T_FULL = 3, T_QUANT = 4, T_EVICTED = 5 };
 

@@ -1723,7 +1723,7 @@ hipError_t launch_route(const Geom &g, const State &st, const StepInfo &si, int 
   int bound = n_cand > 1 ? n_cand : 1;   // ranked windows + newly aged windows (same for every sequence)
   int npow = 1;
   while (npow < bound) npow <<= 1;
-  if (npow > SORT_MAX) return hipErrorInvalidValue;
+  if (npow > ROUTE_SORT_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(route_qevict_kernel, dim3(g.B), dim3(1024), npow * sizeof(unsigned long long), s, g, st, si, a0,
                      a1, npow);
   hipError_t e = hipGetLastError();
