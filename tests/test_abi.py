@@ -61,11 +61,12 @@ def test_config_checks_on_host():
                 setattr(c, k, v)
         assert lib.qkv_check_config(ctypes.byref(c)) == L.EINVAL, kw
         assert L.workspace_bytes(c) == 0
-    # eight heads per KV head at d = 128 need 32-token windows (attention LDS)
-    for window, ok in ((16, False), (32, True)):
-        c = L.make_config(W.STRESS)
-        c.window = window
-        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, window
+    # eight heads per KV head at d = 128: every window size; with rotary keys
+    # the attention LDS does not fit
+    for window, rope, ok in ((8, 0, True), (16, 0, True), (32, 0, True), (16, 1, False)):
+        c = L.make_config(W.STRESS, max_ctx=65536)
+        c.window, c.rope = window, rope
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, (window, rope)
 
 
 def test_score_window_checks_on_host():

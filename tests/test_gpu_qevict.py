@@ -451,3 +451,16 @@ def test_qevict_long_context_parity(torch_cuda):
     c = W.TINY.replace(prefill=140000, steps=40, window=16, omega=16, n_sink=5, n_recent=32, k_full=100,
                        k_quant=300)
     _run_parity(c, torch_cuda, n_splits=4, label="long-context")
+
+
+@pytest.mark.parametrize("window,bits", [(16, 2), (8, 2), (16, 4)])
+def test_qevict_g8_d128_short_windows_parity(torch_cuda, window, bits):
+    """Eight heads per KV head at d = 128 (the Llama-70B head geometry) with
+    windows of one tile: a block's quantized windows take two rounds of
+    query-limb staging (the LDS of eight waves holds the limbs of two
+    windows); ragged prompt, several splits."""
+    c = W.STRESS.replace(batch=2, prefill=3000, steps=64, n_q_heads=64, n_kv_heads=8, window=window, omega=window,
+                         n_recent=32, quant_bits=bits)
+    w0 = W.w0(c)
+    c = c.replace(k_full=w0 // 6, k_quant=w0 // 2)
+    _run_parity(c, torch_cuda, n_splits=5, check_ledger_every=2, label=f"g8-d128-w{window}-int{bits}")

@@ -97,10 +97,10 @@ int validate(const qkv_config *c) {
   if (c->n_sink < 0 || c->n_sink > TS || c->n_recent < 0) return QKV_EINVAL;
   if (c->k_full < 0 || c->k_quant < 0) return QKV_EINVAL;
   if ((c->quant_bits != 2 && c->quant_bits != 4) || c->group != 32) return QKV_EINVAL;
-  // the attention workgroup's LDS (q*s limbs of every window slot of eight
-  // waves) exceeds the device's with d = 128, eight heads per KV head and
-  // windows of one tile
-  if (c->head_dim == 128 && G == 8 && c->window <= TS) return QKV_EINVAL;
+  // rotary keys with eight heads per KV head at d = 128: the attention
+  // workgroup's LDS (rotated query limbs of every window slot of eight
+  // waves, the table rows) exceeds the device's
+  if (c->rope && c->head_dim == 128 && G == 8) return QKV_EINVAL;
   const long long U = 1 + ((long long)c->max_ctx - c->n_sink + c->window - 1) / c->window;
   if (U + 1 > ROUTE_SORT_MAX) return QKV_EINVAL;      // routing candidates are ranked in LDS
   return QKV_OK;

@@ -453,6 +453,10 @@ constexpr int QT = 4;   // quantized tiles per block
 // together fall on different banks
 template <int D> constexpr int PSTR = 2 * D + 8;   // parameter slot: [s(d), z(d)]
 template <int D> constexpr int QSTR = D + 8;       // one q*s row
+// window slots whose q*s limbs are staged in LDS at once: all of a block's,
+// but half of them with eight heads per KV head at d = 128 (the LDS of eight
+// waves holds no more), the block's windows then taking two rounds
+template <int D, int GP> constexpr int QS_SLOTS = (GP == 1 && D == 128) ? QT / 2 : QT;
 
 struct QBuf {
   uint4 code[QT];   // the lane's key code dwords, then value code dwords, of each tile
@@ -575,6 +579,8 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
       *(uint4 *)(c.rw_lds + (c.lane >> 4) * D + ((c.lane & 15) * (D / 64) + r) * 4) = buf.tr[r];
   }
   wave_lds_sync();
+  floatx4 s[QT];
+  bool scored = false;   // the two-round path below forms the scores itself
   if constexpr (ROPE) {
     // Rotary keys.  A key of the window starting at p0 sits at p0 + t and
     // reads as R(p0 + t) k = R(p0) R(t) k, so q . R(p0 + t) k equals
@@ -610,6 +616,57 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
         }
       }
     }
+  } else if (QS_SLOTS<D, GP> < QT && nws > QS_SLOTS<D, GP>) {
+    // the block's windows in two rounds of QS window slots: limbs of windows
+    // w0 .. w0 + QS - 1, then the MFMAs of their tiles
+    constexpr int QS = QS_SLOTS<D, GP>;
+    const int c0 = 8 * ((c.lane & 15) % (D / 8));
+    const int qrow = (c.is_lo ? G : 0) + c.hc;
+    {
+      // key-zero term of every window at once (reads the parameters only)
+      floatx4 zb = {0.f, 0.f, 0.f, 0.f};
+      const int zr = (c.lane & 15) % nws;
+      half8 z8[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) z8[kb] = *(const half8 *)(c.kp_lds + zr * PSTR<D> + D + kb * 32 + c.lq * 8);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) zb = mfma_f16_k32(z8[kb], bz[kb], zb);
+#pragma unroll
+      for (int j = 0; j < QT; ++j) s[j] = floatx4{zb[j & 3] + row_bias[0], zb[j & 3] + row_bias[1],
+                                                  zb[j & 3] + row_bias[2], zb[j & 3] + row_bias[3]};
+    }
+#pragma unroll
+    for (int rd = 0; rd < QT / QS; ++rd) {
+      if (rd > 0) {
+        wave_lds_sync();   // the previous round's limbs have been read
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int w = 0; w < QS; ++w) {
+        const half8 sw = *(const half8 *)(c.kp_lds + (rd * QS + w) * PSTR<D> + c0);
+        half_t *qs = c.qs_lds + w * 2 * G * QSTR<D>;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (4 * r < G) {
+            const int hh = (c.lane >> 4) + 4 * r;
+            const half8 hi = qc[r] * sw;
+            const half8 lo = __builtin_elementwise_fma(qc[r], sw, -hi);
+            *(half8 *)(qs + hh * QSTR<D> + c0) = hi;
+            *(half8 *)(qs + (G + hh) * QSTR<D> + c0) = lo;
+          }
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int w = 0; w < QS; ++w) {
+          const int j = rd * QS + w;   // one tile per window
+          const half8 bq = *(const half8 *)(c.qs_lds + (w * 2 * G + qrow) * QSTR<D> + kb * 32 + c.lq * 8);
+          s[j] = mfma_f16_k32(key_codes<D, BITS>(buf, j, kb), bq, s[j]);
+        }
+    }
+    scored = true;
   } else {
   // q*s of each window as two fp16 limbs (high, exact remainder), computed
   // once per (head, channel) in the compact layout and stored [limb][head][c]
@@ -637,7 +694,6 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   }
   }
   wave_lds_sync();
-  floatx4 s[QT];
   const int qrow = (c.is_lo ? G : 0) + c.hc;
   if constexpr (ROPE) {
     // A operand: the lane's 8 channels of k-block kb and their partners in
@@ -684,7 +740,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  } else {
+  } else if (!scored) {
   // key-zero term sum_c q_c z_c of every window at once: A rows r are the
   // zero vectors of window slot r % nws, so register i of every lane holds
   // the term of window slot i % nws for the lane's column (high columns only)
@@ -955,7 +1011,8 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   c.mass_row = mass_row;
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
-  c.qs_lds = s_qs + (size_t)wave * (QT / g.tpw) * 2 * G * QSTR<D>;
+  const int qs_slots = ROPE ? QT : min(QT / g.tpw, QS_SLOTS<D, GP>);   // window slots of q*s limbs per wave
+  c.qs_lds = s_qs + (size_t)wave * qs_slots * 2 * G * QSTR<D>;
   // Append folded into the launch (k_new, v_new: the step's token of every
   // (sequence, KV head), [B][Hkv][d]): lane l < d/4 of every wave loads
   // 16-byte chunk l of its K and V rows now (nothing waits for it here); the
@@ -1200,7 +1257,8 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
 // LDS of one attention workgroup beyond its static arrays: the q*s limbs of
 // every window slot of every wave
 static size_t attend_qs_bytes(const Geom &g) {
-  size_t n = (size_t)QW * (QT / g.tpw) * 2 * g.G * (g.d + 8) * sizeof(half_t);
+  const int slots = g.rope ? QT : min(QT / g.tpw, (g.G == 8 && g.d == 128) ? QT / 2 : QT);   // QS_SLOTS
+  size_t n = (size_t)QW * slots * 2 * g.G * (g.d + 8) * sizeof(half_t);
   if (g.rope) n += ((size_t)QW * QT * g.d + 16 * (size_t)(g.d + 4)) * sizeof(float);   // RD_STR
   return n;
 }
