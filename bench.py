@@ -63,8 +63,8 @@ KERNEL_SRCS = [os.path.join(ROOT, "tiered_quantization_eviction_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_drift_traffic.md")
 
 
-WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.DRIFT_L32, W.DRIFT_ROPE, W.STRESS, W.HQEKV,
-                                  W.HQEKV_PAGE, W.H2O, W.TINY)}
+WORKLOADS = {c.name: c for c in (W.DRIFT, W.DRIFT_INT4, W.DRIFT_L32, W.DRIFT_ROPE, W.DRIFT_G8, W.STRESS,
+                                  W.HQEKV, W.HQEKV_PAGE, W.H2O, W.TINY)}
 CPU_BUDGET_S = 15.0   # oracle time of the other workloads' bounded samples
 DTYPES = {W.POLICY_QEVICT: "bf16+int2 (fp32 accumulate)",
           W.POLICY_H2O: "bf16 (fp32 accumulate)",

@@ -163,6 +163,10 @@ DRIFT_L32 = _reg(DRIFT.replace(name="drift_l32", layers=32))
 #     rotation and the quantized tier is read rotated at its positions.
 DRIFT_ROPE = _reg(DRIFT.replace(name="drift_rope", rope_base=500000.0))
 
+# 3e: the drift layer with eight query heads per KV head (Hq = 64, the
+#     Llama-70B head geometry) at the same 16-token windows.
+DRIFT_G8 = _reg(DRIFT.replace(name="drift_g8", n_q_heads=64))
+
 # 4: HqeKV five-tier per-token assignment.
 HQEKV = _reg(Config(
     name="hqekv", policy=POLICY_HQEKV, recipe="hqekv",
