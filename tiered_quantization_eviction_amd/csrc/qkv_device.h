@@ -271,4 +271,52 @@ __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float s
   for (int t = 0; t < NT; ++t) ts[t] = sum_x32(sum_x16(ts[t]));
 }
 
+// Outputs of one (sequence, KV head) from its split partials: thread t folds
+// outputs t, t + 256, ... (G*D of them, [head][channel]) with the LSE rule in
+// split order; the loads of two outputs and CH splits go out together.
+template <int G, int CH>
+__device__ inline void merge_outputs(const float2 *ml, const float *po, int S, int D, float *out) {
+  constexpr int PT = 2;
+  const int n = G * D;
+  for (int it0 = threadIdx.x; it0 < n; it0 += PT * blockDim.x) {
+    float m[PT], l[PT], o[PT];
+    int hh[PT], c[PT];
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int it = min(it0 + p * (int)blockDim.x, n - 1);
+      hh[p] = it / D;
+      c[p] = it % D;
+      m[p] = neg_inf();
+      l[p] = 0.0f;
+      o[p] = 0.0f;
+    }
+    for (int s0 = 0; s0 < S; s0 += CH) {
+      float2 mls[PT][CH];
+      float os[PT][CH];
+#pragma unroll
+      for (int p = 0; p < PT; ++p)
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const int sp = min(s0 + k, S - 1);
+          mls[p][k] = ml[sp * G + hh[p]];
+          os[p][k] = po[(size_t)(sp * G + hh[p]) * D + c[p]];
+        }
+#pragma unroll
+      for (int p = 0; p < PT; ++p)
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          if (s0 + k >= S || mls[p][k].x == neg_inf()) continue;
+          const float mn = fmaxf(m[p], mls[p][k].x);
+          const float a = m[p] == neg_inf() ? 0.0f : exp2f(m[p] - mn), w = exp2f(mls[p][k].x - mn);
+          l[p] = l[p] * a + mls[p][k].y * w;
+          o[p] = o[p] * a + os[p][k] * w;
+          m[p] = mn;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PT; ++p)
+      if (it0 + p * (int)blockDim.x < n) out[hh[p] * D + c[p]] = o[p] / l[p];
+  }
+}
+
 }  // namespace qkv

@@ -1176,30 +1176,7 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
     const int b = blockIdx.x / g.Hkv, h = blockIdx.x % g.Hkv;
     const float2 *ml = (const float2 *)st.part_ml + (size_t)(b * g.Hkv + h) * S * G;
     const float *po = st.part_o + (size_t)(b * g.Hkv + h) * S * G * D;
-    for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
-      const int hh = it / D, c = it % D;
-      float m = neg_inf(), l = 0.0f, o = 0.0f;
-      for (int s0 = 0; s0 < S; s0 += CH) {
-        float2 mls[CH];
-        float os[CH];
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-          const int sp = min(s0 + k, S - 1);
-          mls[k] = ml[sp * G + hh];
-          os[k] = po[(size_t)(sp * G + hh) * D + c];
-        }
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-          if (s0 + k >= S || mls[k].x == neg_inf()) continue;
-          const float mn = fmaxf(m, mls[k].x);
-          const float a = m == neg_inf() ? 0.0f : exp2f(m - mn), w = exp2f(mls[k].x - mn);
-          l = l * a + mls[k].y * w;
-          o = o * a + os[k] * w;
-          m = mn;
-        }
-      }
-      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + c] = o / l;
-    }
+    merge_outputs<G, CH>(ml, po, S, D, out + ((size_t)b * g.Hq + (size_t)h * G) * D);
     return;
   }
   // masses of MERGE_ENTRIES live entries of one sequence -> list-order scores:
@@ -1215,6 +1192,8 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   const int e = chunk * MERGE_ENTRIES + el;
   const int ee = min(e, E - 1);
   const int u_out = mass_out ? entry_unit(L, st.routed + b * g.U, ee) : 0;
+  // the entry's list-order score: no other thread of the launch touches it
+  const float old_score = q == 0 ? st.slist[b * g.U + ee] : 0.0f;
   constexpr int HPL = 2;   // KV heads per lane whose loads go out together
   float4 mp[HPL][G / 2];
   auto load_heads = [&](int h0) {
@@ -1256,7 +1235,7 @@ __global__ __launch_bounds__(256) void merge_qevict_kernel(Geom g, State st, Ste
   __syncthreads();
   if (q == 0 && e < E) {
     const float total = (sPart[0][el] + sPart[1][el]) + (sPart[2][el] + sPart[3][el]);
-    st.slist[b * g.U + e] += total;
+    st.slist[b * g.U + e] = old_score + total;
   }
 }
 

@@ -969,30 +969,7 @@ __global__ __launch_bounds__(256) void tok_merge_kernel(TokGeom g, TokState st, 
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const float2 *ml = (const float2 *)st.part_ml + (size_t)bh * S * G;
     const float *po = st.part_o + (size_t)bh * S * G * D;
-    for (int it = threadIdx.x; it < G * D; it += blockDim.x) {
-      const int hh = it / D, cc = it % D;
-      float m = neg_inf(), l = 0.0f, o = 0.0f;
-      for (int s0 = 0; s0 < S; s0 += CH) {
-        float2 mls[CH];
-        float os[CH];
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-          const int sp = min(s0 + k, S - 1);
-          mls[k] = ml[sp * G + hh];
-          os[k] = po[(size_t)(sp * G + hh) * D + cc];
-        }
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-          if (s0 + k >= S || mls[k].x == neg_inf()) continue;
-          const float mn = fmaxf(m, mls[k].x);
-          const float a = m == neg_inf() ? 0.0f : exp2f(m - mn), w = exp2f(mls[k].x - mn);
-          l = l * a + mls[k].y * w;
-          o = o * a + os[k] * w;
-          m = mn;
-        }
-      }
-      out[((size_t)b * g.Hq + (size_t)h * G + hh) * D + cc] = o / l;
-    }
+    merge_outputs<G, CH>(ml, po, S, D, out + ((size_t)b * g.Hq + (size_t)h * G) * D);
     return;
   }
   // masses: block `part` of n_parts per (sequence, KV head) strides over its
