@@ -170,7 +170,7 @@ struct Ctx {
   int slot;               // channel-group slot of this lane's A row in the paired value product
   float scale_log2;
   float *mass_row;        // [(U+1)][G][2] of this (sequence, KV head); slot U is the spare
-  const uint8_t *ledger_h;  // this KV head's entry of ledger pool slot 0
+  size_t ledger_h;          // byte offset of this KV head's entry of ledger pool slot 0
   size_t ledger_stride;     // bytes from one pool slot to the next
   half_t *kp_lds;
   half_t *vp_lds;
@@ -526,8 +526,11 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
   const int tpw = g.tpw;
   const int kl = c.lane & (g.kparam_bytes / 8 - 1);       // lanes past the params repeat them
   const int vl = c.lane & (g.tile_vparam_bytes / 4 - 1);
-  // the windows' ledger slots, one scalar product each
-  const uint8_t *Lw[QT];
+  // the windows' ledger offsets, one scalar product each; every address is
+  // formed from the ledger base itself, so the loads stay global ones (a
+  // pointer chosen among several would become a generic one, and generic
+  // loads make every LDS wait wait for them as well)
+  size_t Lw[QT];
 #pragma unroll
   for (int w = 0; w < QT; ++w) Lw[w] = c.ledger_h + (size_t)(uint32_t)qb.u[w] * c.ledger_stride;
 #pragma unroll
@@ -535,7 +538,7 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     const int w = qt_win(j, tpw);
     const int tj = j - w * tpw;
     // both candidates are fixed indices: a run-time index would put Lw[] in scratch memory
-    const uint8_t *Lb = tpw == 1 ? Lw[j] : Lw[j >> 1];
+    const uint8_t *Lb = c.st->ledger + (tpw == 1 ? Lw[j] : Lw[j >> 1]);
     const uint8_t *T = Lb + g.kparam_bytes + (size_t)tj * g.tile_block_bytes;
     if (DPL == 8) {
       buf.code[j] = ld_stream16(T + c.lane * 32);
@@ -549,7 +552,7 @@ __device__ __forceinline__ void quant_load(const Ctx &c, const QBlock &qb, QBuf 
     buf.vp[j] = ld_stream4(T + g.tile_kcode_bytes + g.tile_vcode_bytes + 4 * vl);
   }
 #pragma unroll
-  for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(Lw[w] + kl * 8);
+  for (int w = 0; w < QT; ++w) buf.kp[w] = ld_stream8(c.st->ledger + Lw[w] + kl * 8);
   if (ROPE) {
     // lanes 16w .. 16w+15 fetch the table row of window slot w's first
     // position (D/2 (cos, sin) pairs, D/64 chunks of 16 bytes per lane); the
@@ -1013,7 +1016,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   c.slot = min((col & 7) / G, GP - 1);
   c.scale_log2 = scale_log2;
   c.mass_row = mass_row;
-  c.ledger_h = st.ledger + (size_t)h * g.ledger_unit_bytes;
+  c.ledger_h = (size_t)h * g.ledger_unit_bytes;
   c.ledger_stride = (size_t)g.Hkv * g.ledger_unit_bytes;
   c.kp_lds = kp_lds;
   c.vp_lds = vp_lds;
