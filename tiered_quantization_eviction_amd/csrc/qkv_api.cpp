@@ -183,11 +183,16 @@ void make_tok_geom(const qkv_config *c, TokGeom &g) {
   g.k_heavy = c->k_full;
   g.omega = c->omega;
   g.chunk = c->policy == QKV_POLICY_HQEKV ? c->chunk : 0;
+  // HqeKV: 8-wave workgroups, whose two waves on a SIMD take the
+  // full-precision and quantized tiers in opposite orders; H2O (a short
+  // compact list and the recent tiles): 4-wave workgroups, twice as many
+  g.att_waves = c->policy == QKV_POLICY_HQEKV ? ATT_WAVES : ATT_WAVES / 2;
   int S = c->n_splits;
-  if (S == 0) {   // one resident round of workgroups, at least two tiles per wave
+  if (S == 0) {   // one resident round (two waves per SIMD), at least two tiles per wave
     const int pairs = g.B * g.Hkv;
-    S = (512 + pairs - 1) / pairs;
-    const int cap = g.TILES / 8 > 1 ? g.TILES / 8 : 1;
+    const int wgs = 256 * ATT_WAVES / g.att_waves;
+    S = (wgs + pairs - 1) / pairs;
+    const int cap = g.TILES / (2 * g.att_waves) > 1 ? g.TILES / (2 * g.att_waves) : 1;
     if (S > cap) S = cap;
     if (S > 64) S = 64;
   }

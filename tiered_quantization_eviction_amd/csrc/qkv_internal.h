@@ -33,7 +33,7 @@ namespace qkv {
 
 constexpr int TS = 16;           // token slots per tile
 constexpr int WAVE = 64;
-constexpr int ATT_WAVES = 4;     // waves per attention workgroup
+constexpr int ATT_WAVES = 8;     // most waves per token-mode attention workgroup
 constexpr int SORT_MAX = 8192;          // largest LDS sort of the token policies and the stateless ranking
 constexpr int ROUTE_SORT_MAX = 16384;   // largest window-policy candidate set (8-byte keys, 128 KB of LDS)
 
@@ -275,6 +275,7 @@ struct TokGeom {
   int TILES;        // live tiles per (sequence, KV head), upper bound
   int n_sink, n_recent, k_heavy, omega;
   int n_splits;
+  int att_waves;    // waves per attention workgroup: 8 (HqeKV) or 4 (H2O)
   // HqeKV: per-position record of a quantized token (canonical per-token
   // packing): K codes [d/2 B], V codes [d/2 B], K params [d/32][2] fp16,
   // V params [d/32][2] fp16 (INT1: [mean, std] in the first pair)

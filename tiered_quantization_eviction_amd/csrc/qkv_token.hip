@@ -279,7 +279,7 @@ __device__ __forceinline__ void tok_store_mass(const TokCtx &c, int e, const flo
 // full-precision tiles (sink, compact, recent) of virtual range [ea, eb);
 // virtual index v < s0 + nC is list tile v, above it list tile v + (quantized tiles)
 template <int D, int GP>
-__device__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&bq)[D / 32], float sc, int ea,
+__device__ __forceinline__ void tok_run_bf16(WaveState<D> &ws, const TokCtx &c, const bf16x8 (&bq)[D / 32], float sc, int ea,
                              int eb) {
   if (ea >= eb) return;
   constexpr int KB = D / 32, CP = D / 32;
@@ -429,7 +429,7 @@ __device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_
 // on low rows), against the exact integer codes; the value-zero term is one
 // MFMA per block.
 template <int D, int F, int GP>
-__device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], half4 bQ, float sc,
+__device__ __forceinline__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], half4 bQ, float sc,
                            int ea, int eb) {
   if (ea >= eb) return;
   using Q = QL<D, F>;
@@ -622,7 +622,7 @@ __device__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
 //           fp16 limbs (high rows, low rows) against the 0/1 codes, and the
 //           zero term as two MFMAs over the fp16 limbs of c.
 template <int D, int GP>
-__device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], float qall, float sc,
+__device__ __forceinline__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)[D / 32], float qall, float sc,
                            int ea, int eb) {
   if (ea >= eb) return;
   using Q = Q1<D>;
@@ -745,8 +745,10 @@ __device__ void tok_run_q1(WaveState<D> &ws, const TokCtx &c, const half8 (&bqk)
   if (i < n_blocks) step(i, buf0, buf1);
 }
 
-template <int D, int GP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tok_attend_kernel(
+// NW waves per workgroup (8: the two waves on a SIMD belong to one
+// workgroup; 4: two workgroups per compute unit)
+template <int D, int GP, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void tok_attend_kernel(
     TokGeom g, TokState st, TokStep ts, const uint16_t *__restrict__ q, size_t q_bstride, float scale_log2) {
   constexpr int KB = D / 32, CT = D / 16, NG = D / 32;
   const int S = g.n_splits;
@@ -765,11 +767,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool is_lo = col >= 8;
   const int hc = (col & 7) & (G - 1);
 
-  __shared__ float sm_m[ATT_WAVES][8];
-  __shared__ float sm_l[ATT_WAVES][8];
-  __shared__ float sm_o[ATT_WAVES][8][D];
-  __shared__ __attribute__((aligned(16))) uint32_t s_par[ATT_WAVES][2 * 32 * NG];
-  __shared__ __attribute__((aligned(16))) float s_ks[ATT_WAVES][2 * 16 * NG];
+  __shared__ float sm_m[NW][8];
+  __shared__ float sm_l[NW][8];
+  __shared__ float sm_o[NW][8][D];
+  __shared__ __attribute__((aligned(16))) uint32_t s_par[NW][2 * 32 * NG];
+  __shared__ __attribute__((aligned(16))) float s_ks[NW][2 * 16 * NG];
 
   const TokList L = tok_list(g, st, ts, bh);
   TokCtx c;
@@ -854,8 +856,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     scq = ldexpf(scale_log2, qexp);
   }
 
-  // this wave's share: slice gi of 4*S of every part of the list
-  const int NS = 4 * S, gi = split * 4 + wave;
+  // this wave's share: slice gi of NW*S of every part of the list
+  const int NS = NW * S, gi = split * NW + wave;
   auto slice = [&](int n, int &a, int &z) {
     a = (int)((long long)n * gi / NS);
     z = (int)((long long)n * (gi + 1) / NS);
@@ -865,11 +867,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int qa[3], qz[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) slice(L.nQ[k], qa[k], qz[k]);
-  tok_run_bf16<D, GP>(ws, c, bq, scale_log2, fa, fz);
-  if (g.policy == QKV_POLICY_HQEKV) {
-    tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
-    tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
-    tok_run_q1<D, GP>(ws, c, bqk, qall, scq, qa[2], qz[2]);
+  auto quantized = [&]() {
+    if (g.policy == QKV_POLICY_HQEKV) {
+      tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
+      tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
+      tok_run_q1<D, GP>(ws, c, bqk, qall, scq, qa[2], qz[2]);
+    }
+  };
+  // Opposite orders for the two waves that share a SIMD (w and w + 4 when
+  // the waves are dealt round-robin, 2k and 2k + 1 when dealt in pairs): one
+  // streams full-precision tiles while the other unpacks quantized ones.
+  if (((wave & 1) ^ (wave >> 2)) & 1) {
+    quantized();
+    tok_run_bf16<D, GP>(ws, c, bq, scale_log2, fa, fz);
+  } else {
+    tok_run_bf16<D, GP>(ws, c, bq, scale_log2, fa, fz);
+    quantized();
   }
 
   // ---- wave epilogue: value-zero term, then the low-limb rows 8+h onto rows h ----
@@ -905,16 +918,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int hh = it / D, cc = it % D;
     float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
     float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w)
+    for (int w = 0; w < NW; ++w)
       if (sm_m[w][hh] != neg_inf()) o += sm_o[w][hh][cc] * exp2f(sm_m[w][hh] - M);
     st.part_o[(pbase + hh) * D + cc] = o;
     if (cc == 0) {
       float l = 0.0f;
 #pragma unroll
-      for (int w = 0; w < ATT_WAVES; ++w)
+      for (int w = 0; w < NW; ++w)
         if (sm_m[w][hh] != neg_inf()) l += sm_l[w][hh] * exp2f(sm_m[w][hh] - M);
       st.part_ml[(pbase + hh) * 2 + 0] = M;
       st.part_ml[(pbase + hh) * 2 + 1] = l;
@@ -1078,18 +1091,22 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
   // the optional events are attached to the dispatch (kernel execution time);
   // four heads per KV head: value operands shared by channel-group pairs
   const bool pair = g.G == 4;
-  if (g.d == 128 && pair)
-    hipExtLaunchKernelGGL((tok_attend_kernel<128, 2>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
-                          q, q_bstride, scale_log2);
-  else if (g.d == 128)
-    hipExtLaunchKernelGGL((tok_attend_kernel<128, 1>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
-                          q, q_bstride, scale_log2);
-  else if (pair)
-    hipExtLaunchKernelGGL((tok_attend_kernel<64, 2>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
-                          q, q_bstride, scale_log2);
+  const void *fn;
+  if (g.att_waves == ATT_WAVES)
+    fn = g.d == 128 ? (pair ? (const void *)tok_attend_kernel<128, 2, ATT_WAVES> : (const void *)tok_attend_kernel<128, 1, ATT_WAVES>)
+                    : (pair ? (const void *)tok_attend_kernel<64, 2, ATT_WAVES> : (const void *)tok_attend_kernel<64, 1, ATT_WAVES>);
   else
-    hipExtLaunchKernelGGL((tok_attend_kernel<64, 1>), dim3(grid), dim3(256), 0, s, ev_start, ev_stop, 0, g, st, ts,
-                          q, q_bstride, scale_log2);
+    fn = g.d == 128 ? (pair ? (const void *)tok_attend_kernel<128, 2, ATT_WAVES / 2> : (const void *)tok_attend_kernel<128, 1, ATT_WAVES / 2>)
+                    : (pair ? (const void *)tok_attend_kernel<64, 2, ATT_WAVES / 2> : (const void *)tok_attend_kernel<64, 1, ATT_WAVES / 2>);
+  TokGeom ga = g;
+  TokState sa = st;
+  TokStep tsa = ts;
+  const uint16_t *qa = q;
+  size_t qb = q_bstride;
+  float sl = scale_log2;
+  void *args[] = {&ga, &sa, &tsa, &qa, &qb, &sl};
+  e = hipExtLaunchKernel(fn, dim3(grid), dim3(64 * g.att_waves), args, 0, s, ev_start, ev_stop, 0);
+  if (e != hipSuccess) return e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mass_out && (e = launch_clear(mass_out, (size_t)g.B * g.Hkv * g.T * sizeof(float), s)) != hipSuccess) return e;
   // mass blocks: about 2048 in all (a few per CU), at most one per 64 live tiles
