@@ -867,7 +867,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int qa[3], qz[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) slice(L.nQ[k], qa[k], qz[k]);
-  auto quantized = [&]() {
+  auto quantized = [&]() __attribute__((always_inline)) {
     if (g.policy == QKV_POLICY_HQEKV) {
       tok_run_ql<D, 0, GP>(ws, c, bqk, bQ, scq, qa[0], qz[0]);
       tok_run_ql<D, 1, GP>(ws, c, bqk, bQ, scq, qa[1], qz[1]);
