@@ -17,6 +17,15 @@
  * the cache and reported by qkv_status().  No call throws.  A cache is not
  * thread-safe: use one cache per stream.
  *
+ * Non-finite inputs: K, V and q must be finite.  The attention path does not
+ * check them (a check would cost a pass over the data): a NaN or infinity
+ * reaches the outputs, masses and scores of its (sequence, KV head), and a
+ * NaN score takes part in the ranking by its bit pattern.  Every quantizer
+ * (the routing pack, HqeKV re-quantization, qkv_quantize_window) does check
+ * its groups: a NaN or infinity in a group makes its scale or zero
+ * non-finite, which latches QKV_ERANGE as an out-of-range value does; the
+ * group's codes are then not meaningful.
+ *
  * Notation follows the pages: H_q query heads, H_kv KV heads, G = H_q/H_kv,
  * d = head dim, window = tokens per window (omega_w), omega = routing period
  * (Omega), K_f / K_q = windows kept in full precision / quantized.
@@ -304,7 +313,8 @@ int qkv_prefill_score(qkv_cache *cache, const void *q, int32_t n_queries, qkv_st
  *           INT1_NORMAL:   [tokens][mean, std]
  * bits: 2 or 4 for the uniform kinds, 1 for INT1_NORMAL.  Groups are `group`
  * tokens (K_PER_CHANNEL) or channels (PER_TOKEN).  A parameter outside float16
- * range latches QKV_ERANGE, reported by qkv_quantize_status().
+ * range, or a group holding a NaN or infinity, latches QKV_ERANGE, reported
+ * by qkv_quantize_status().
  */
 int qkv_quantize_window(const void *x, int32_t x_dtype, int32_t n_blocks, int32_t tokens, int32_t head_dim,
                         int32_t bits, int32_t group, int32_t kind, uint8_t *codes, uint16_t *params,
@@ -464,7 +474,8 @@ int qkv_profile_start(qkv_cache *cache, int32_t n, int32_t stride);
 int qkv_profile_read(qkv_cache *cache, float *ms, int32_t n);
 
 /* Device-latched status of every layer: waits for `stream`, returns QKV_OK,
- * QKV_ERANGE (a quantization parameter outside float16 range) or
+ * QKV_ERANGE (a quantization parameter outside float16 range, or a quantized
+ * group holding a NaN or infinity) or
  * QKV_ECAPACITY (the ledger pool ran out: cannot happen with the pool sized
  * as qkv_workspace_bytes sizes it, latched rather than faulting). */
 int qkv_status(qkv_cache *cache, qkv_stream stream);

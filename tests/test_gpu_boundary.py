@@ -268,18 +268,22 @@ def test_call_order_and_capacity_errors(torch_cuda):
                         torch.zeros((1, 4, 32), dtype=torch.float32, device="cuda"))
 
 
-def test_range_error_in_a_routing_pack_is_latched(torch_cuda):
-    """Sequence 0 holds one value of -1e5 in window 2 (positions 20..27):
-    its per-token float16 zero (the group minimum) overflows when the first
-    routing event packs the window (every aged window is quantized here).
-    The status reports QKV_ERANGE from then on; sequence 1 keeps matching the
-    oracle, and the oracle refuses sequence 0's window the same way."""
+@pytest.mark.parametrize("bad", ["-1e5", "nan", "inf"])
+def test_range_error_in_a_routing_pack_is_latched(torch_cuda, bad):
+    """Sequence 0 holds one bad value in window 2 (positions 20..27): -1e5,
+    whose per-token float16 zero (the group minimum) overflows, or a NaN or
+    an infinity (non-finite inputs are refused by every quantizer) when the
+    first routing event packs the window (every aged window is quantized
+    here).  The status reports QKV_ERANGE from then on; sequence 1 keeps
+    matching the oracle, and the oracle refuses sequence 0's window the same
+    way."""
     import torch
     from tiered_quantization_eviction_amd import _lib as L
     cfg = W.TINY.replace(batch=2, k_full=0, k_quant=100, steps=24)
     wl = W.Workload(cfg)
     K, V, Q = gpu_inputs(cfg, wl)
-    big = int(round_to_bf16_bits(np.array([-1e5], np.float32))[0])
+    # bfloat16 bits: -1e5 rounded, the quiet NaN 0x7fc0, +infinity 0x7f80
+    big = {"-1e5": int(round_to_bf16_bits(np.array([-1e5], np.float32))[0]), "nan": 0x7FC0, "inf": 0x7F80}[bad]
     V[0, 0, 22, 5] = big - 65536 if big > 32767 else big
     d = Driver(cfg, K, V, Q)
     k1, v1 = wl.kv(1)

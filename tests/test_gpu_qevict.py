@@ -104,14 +104,24 @@ def test_quantize_int1_normal_codes_bitexact(torch_cuda):
         np.testing.assert_array_equal(params[blk].reshape(-1, 2)[:, 1].view(np.uint16), sd.view(np.uint16))
 
 
-def test_quantize_range_error_latched(torch_cuda):
+@pytest.mark.parametrize("bad", [1e6, np.nan, np.inf, -np.inf])
+def test_quantize_range_error_latched(torch_cuda, bad):
+    """A step above the float16 maximum, and a NaN or infinity in a group
+    (refused like an out-of-range value, as the oracle's quantizer refuses
+    it), latch QKV_ERANGE for either uniform kind; finite inputs leave the
+    latch clear."""
     from tiered_quantization_eviction_amd import _lib as L
-    log("quantize range error")
-    x = np.zeros((1, 8, 64), np.float32)
-    x[0, 0, 0] = 1e6                                   # step > float16 max
-    L.quantize_window(torch_cuda.from_numpy(x).cuda(), L.KIND_PER_TOKEN, 2)
-    assert L.quantize_status() == L.ERANGE
-    assert L.quantize_status() == 0                    # the latch clears when read
+    log(f"quantize range error ({bad})")
+    for kind in (L.KIND_PER_TOKEN, L.KIND_K_PER_CHANNEL):
+        x = np.zeros((1, 8, 64), np.float32)
+        L.quantize_window(torch_cuda.from_numpy(x).cuda(), kind, 2)
+        assert L.quantize_status() == 0
+        x[0, 3, 5] = bad
+        L.quantize_window(torch_cuda.from_numpy(x).cuda(), kind, 2)
+        assert L.quantize_status() == L.ERANGE, (kind, bad)
+        assert L.quantize_status() == 0                # the latch clears when read
+        with pytest.raises(oc.ParamRangeError):
+            oc.uniform_quantize(x[0] if kind == L.KIND_PER_TOKEN else x[0].T, 2)
 
 
 def test_rank_tiers_examples(torch_cuda):

@@ -170,6 +170,26 @@ def test_uniform_quantizer_degenerate_and_lossless_levels():
     np.testing.assert_array_equal(codec.uniform_dequantize(c, s, z), x)
 
 
+@pytest.mark.parametrize("bad", [2.5e5, -7.0e4, np.nan, np.inf, -np.inf])
+def test_quantizers_refuse_parameters_outside_float16(bad):
+    """The float16 parameters the pages store cannot hold a step or zero past
+    65504, nor a NaN: a 2-bit group of [-1, 1] with 2.5e5 in it (step
+    ~83000) or -7e4 (zero -7e4) is refused (ParamRangeError), and so is one
+    holding a NaN or an infinity, by the one-bit normalized quantizer too;
+    the same group without the value is accepted."""
+    x = np.linspace(-1.0, 1.0, 32, dtype=np.float32)[None, :].repeat(2, axis=0)
+    codec.uniform_quantize(x, 2)
+    codec.int1_normal_quantize(x)
+    y = x.copy()
+    y[1, 7] = bad
+    with np.errstate(invalid="ignore", over="ignore"):
+        with pytest.raises(codec.ParamRangeError):
+            codec.uniform_quantize(y, 2)
+        if not np.isfinite(bad):
+            with pytest.raises(codec.ParamRangeError):
+                codec.int1_normal_quantize(y)
+
+
 def test_kivi_groups_keys_per_channel_values_per_token():
     """KV-cache evolution page, section 5: per-channel key groups keep an
     outlier channel from inflating the other channels' steps; values are

@@ -271,6 +271,13 @@ __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float s
   for (int t = 0; t < NT; ++t) ts[t] = sum_x32(sum_x16(ts[t]));
 }
 
+// Minimum and maximum that return NaN when either operand is NaN, as a
+// float reduction over the values does: a quantizer's group that holds a NaN
+// then gets a NaN step, which latches the range error, instead of the NaN
+// being skipped and coded as if it were in range.
+__device__ __forceinline__ float min_nan(float a, float b) { return a != a ? a : (b != b ? b : fminf(a, b)); }
+__device__ __forceinline__ float max_nan(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
+
 // Outputs of one (sequence, KV head) from its split partials: thread t folds
 // outputs t, t + 256, ... (G*D of them, [head][channel]) with the LSE rule in
 // split order; the loads of two outputs and CH splits go out together.

@@ -1618,8 +1618,8 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float x = bf16_to_f32(sk[t0 + k][c]);
-            mn = fminf(mn, x);
-            mx = fmaxf(mx, x);
+            mn = min_nan(mn, x);
+            mx = max_nan(mx, x);
           }
         const half_t s16 = (half_t)((mx - mn) / levels);
         const half_t z16 = (half_t)mn;
@@ -1641,8 +1641,8 @@ __global__ __launch_bounds__(TR_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = bf16_to_f32(e[j]);
-            mn = fminf(mn, x);
-            mx = fmaxf(mx, x);
+            mn = min_nan(mn, x);
+            mx = max_nan(mx, x);
           }
         }
         const half_t s16 = (half_t)((mx - mn) / levels);
@@ -1821,8 +1821,8 @@ __global__ __launch_bounds__(256) void quantize_window_kernel(const void *__rest
       float mn = load_x(x, dtype, xb + (size_t)t0 * D + c), mx = mn;
       for (int t = t0 + 1; t < t1; ++t) {
         const float v = load_x(x, dtype, xb + (size_t)t * D + c);
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+        mn = min_nan(mn, v);
+        mx = max_nan(mx, v);
       }
       const half_t s16 = (half_t)((mx - mn) / levels), z16 = (half_t)mn;
       if (!isfinite((float)s16) || !isfinite((float)z16)) g_quant_status = QKV_ERANGE;
@@ -1841,8 +1841,8 @@ __global__ __launch_bounds__(256) void quantize_window_kernel(const void *__rest
       float mn = load_x(x, dtype, row), mx = mn;
       for (int c = 1; c < group; ++c) {
         const float v = load_x(x, dtype, row + c);
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+        mn = min_nan(mn, v);
+        mx = max_nan(mx, v);
       }
       const half_t s16 = (half_t)((mx - mn) / levels), z16 = (half_t)mn;
       if (!isfinite((float)s16) || !isfinite((float)z16)) g_quant_status = QKV_ERANGE;

@@ -1367,13 +1367,13 @@ __global__ __launch_bounds__(256) void hq_requant_kernel(TokGeom g, TokState st,
       float mn = x[0], mx = x[0];
 #pragma unroll
       for (int e = 1; e < CPL; ++e) {
-        mn = fminf(mn, x[e]);
-        mx = fmaxf(mx, x[e]);
+        mn = min_nan(mn, x[e]);
+        mx = max_nan(mx, x[e]);
       }
 #pragma unroll
       for (int off = 1; off < LPG; off <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, off));
-        mx = fmaxf(mx, __shfl_xor(mx, off));
+        mn = min_nan(mn, __shfl_xor(mn, off));
+        mx = max_nan(mx, __shfl_xor(mx, off));
       }
       const half_t s16 = (half_t)((mx - mn) / levels);
       const half_t z16 = (half_t)mn;
