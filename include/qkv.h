@@ -197,7 +197,8 @@ int qkv_create_static(const qkv_config *cfg, qkv_stream stream, qkv_cache **out)
  *   qkv_route after every decode step (omega = 1) to evict down to the budget.
  *   The scored prompt (section 1.2, each position accumulates from its own
  *   causal row): append it, qkv_prefill_score with its
- *   queries, then one qkv_route trims it.  max_ctx <= 8192.
+ *   queries, then one qkv_route trims it.  max_ctx <= 16384 (a routing
+ *   event ranks its candidates in LDS).
  * QKV_POLICY_HQEKV (HqeKV notes, sections 3.2-3.5 and 3.8): token units
  *   (window = 1, n_sink = 0), one score per (sequence, KV head, token) summed
  *   over the G query heads; ratios[0..4] are the shares of full precision,

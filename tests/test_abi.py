@@ -224,3 +224,13 @@ def test_window_policy_context_limit():
     for max_ctx, ok in ((5 + 16382 * 16, True), (5 + 16383 * 16, False), (140000, True)):
         c = L.make_config(W.TINY.replace(window=16, omega=16, n_sink=5), max_ctx=max_ctx)
         assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, max_ctx
+
+
+def test_h2o_context_limit():
+    """The H2O routing sort holds 16384 candidates (8-byte keys, 128 KB of
+    LDS): a per-token heavy-hitter cache may hold up to 16384 positions, one
+    more is refused."""
+    L, lib = _lib()
+    for max_ctx, ok in ((8192, True), (16384, True), (16385, False)):
+        c = L.make_config(W.H2O, max_ctx=max_ctx)
+        assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, max_ctx

@@ -117,3 +117,14 @@ def test_h2o_no_heavy_hitters_parity(torch_cuda):
     window only (StreamingLLM)."""
     cfg = W.H2O.replace(batch=1, prefill=200, steps=64, k_full=0)
     _run_h2o(cfg, torch_cuda, label="h2o-kheavy0")
+
+
+def test_h2o_long_prompt_parity(torch_cuda):
+    """A 9000-token scored prompt (one KV head, four query heads; past the
+    8192 positions one LDS sort of 8192 keys would hold): the first routing
+    call ranks 8867 candidates in one sort of 16384 keys (128 KB of LDS),
+    then 12 steps evict one token each; kept sets, scores, outputs and every
+    eviction record match the oracle."""
+    cfg = W.H2O.replace(batch=1, n_q_heads=4, n_kv_heads=1, prefill=9000, steps=12, n_sink=5, k_full=256,
+                        n_recent=128)
+    _run_h2o(cfg, torch_cuda, label="h2o-9k")

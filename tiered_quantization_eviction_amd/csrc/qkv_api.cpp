@@ -77,7 +77,7 @@ int validate(const qkv_config *c) {
     // per-token heavy hitters: window 1, no quantized tier, scores per KV head
     if (c->window != 1 || c->omega < 1 || c->k_quant != 0 || c->k_full < 0 || c->n_recent < 0) return QKV_EINVAL;
     if (c->n_sink < 0 || c->n_sink > TS) return QKV_EINVAL;
-    if (c->max_ctx > SORT_MAX) return QKV_EINVAL;    // routing candidates are ranked in LDS
+    if (c->max_ctx > ROUTE_SORT_MAX) return QKV_EINVAL;   // routing candidates are ranked in LDS
     return QKV_OK;
   }
   if (c->policy == QKV_POLICY_HQEKV) {

@@ -1221,6 +1221,7 @@ hipError_t tok_launch_route(const TokGeom &g, const TokState &st, const TokStep 
                             hipStream_t s) {
   int npow = 1;
   while (npow < n_cand) npow <<= 1;
+  if (npow > ROUTE_SORT_MAX) return hipErrorInvalidValue;   // 8-byte keys, at most 128 KB of LDS
   hipLaunchKernelGGL(tok_route_h2o_kernel, dim3(g.B * g.Hkv), dim3(1024), npow * sizeof(unsigned long long), s, g,
                      st, ts.n_cmp, a0, a1, npow, ts.N);
   return hipGetLastError();
