@@ -385,6 +385,16 @@ int qkv_rank_tiers(const float *score, const int32_t *pos, const uint8_t *eligib
  * 4 evicted), the margin at the heavy-hitter cut (word 10, also word 12;
  * word 11 +inf); VICTIMS int32 [batch, n_kv_heads, max_ctx] the evicted
  * positions, best-ranked first (their age is tokens - 1 - position).
+ * HqeKV writes them per (sequence, KV head) at every assignment event:
+ * EVENT words 0 tokens, 1 tokens ranked, 2 BF16, 3 INT2, 8 INT4 and 9 INT1
+ * tokens of the ranked positions after the event, 4 tokens it evicted, 6
+ * tokens it moved to a lower tier, 7 of them re-quantized (6 minus 4), 5
+ * zero (downgrade only); float32 margins (the metric score x value range,
+ * relative gap across the cut) at the BF16|INT4 (10), INT4|INT2 (11),
+ * INT2|INT1 (13) and INT1|evict (14) cuts and their minimum (12), +inf where
+ * a cut falls outside the ranking and with chunk ranking; VICTIMS int32
+ * [batch, n_kv_heads, max_ctx] the positions the event evicted, in position
+ * order, -1 past them.
  * (units without a ledger export zero codes and parameters).  A cache of
  * n_layers > 1 exports every per-layer kind as n_layers such arrays, layer
  * after layer (STATE once; QKV_ESTATE unless every layer holds the same

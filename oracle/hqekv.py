@@ -44,7 +44,7 @@ from .attention import attend
 from .codec import (int1_normal_dequantize, int1_normal_quantize, per_token_dequantize,
                     per_token_quantize)
 from .numerics import FLT_MIN, bf16_to_f64
-from .rank import order, rank_tiers
+from .rank import cut_margins, order, rank_tiers
 
 BF16, INT4, INT2, INT1, EVICT = 0, 1, 2, 3, 4
 
@@ -127,14 +127,33 @@ class HqeKVGroup:
         else:                                      # tokens appended before the previous event
             eligible[live[live < self.last_event_N]] = True
         metric = joint_metric(self.score, self.range)
+        counts = share_counts(self.ratios, N)
         if self.chunk:
             target = self._chunk_targets(metric, eligible, N)
         else:
-            target = assign(metric, np.arange(self.T), eligible, share_counts(self.ratios, N))
+            target = assign(metric, np.arange(self.T), eligible, counts)
+        end = N if self.last_event_N == 0 else self.last_event_N   # the ranked range of positions
+        moved, gone = 0, []
         for t in np.flatnonzero(eligible):
             new = max(int(self.tier[t]), int(target[t]))
             if new > self.tier[t]:
                 self._requantize(t, new)
+                moved += 1
+                if new == EVICT:
+                    gone.append(int(t))
+        # the event's record (H2O notes section 5.1: what each eviction
+        # decided and how close its cuts were): tokens per tier of the
+        # ranked range after it, tokens moved down and evicted, and the
+        # relative metric gap at each of the four cuts of the token ranking
+        cum = np.cumsum(counts).tolist()
+        tiers = self.tier[:end]
+        self.last_record = {
+            "tokens": N, "candidates": int(eligible.sum()),
+            "full": int((tiers == BF16).sum()), "int4": int((tiers == INT4).sum()),
+            "int2": int((tiers == INT2).sum()), "int1": int((tiers == INT1).sum()),
+            "moved": moved, "evicted": len(gone), "requantized": moved - len(gone), "victims": sorted(gone),
+            "margins": [float("inf")] * 4 if self.chunk else cut_margins(metric, np.arange(self.T), eligible, cum),
+        }
         self.last_event_N = N
         self.last_metric = metric
         if self.window:

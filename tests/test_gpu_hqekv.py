@@ -4,7 +4,9 @@ Per (sequence, KV head): tiers after the first assignment (scored prompt
 tail) and after every event must equal the oracle's; the codes and float16
 parameters of every quantized token must be bit-identical (canonical per-token
 packing); scores of live tokens agree to 1e-4 relative, attention outputs to
-2e-3 max-abs.
+2e-3 max-abs; each event's record (tokens per tier, tokens moved, evicted and
+re-quantized, the evicted positions) equals the oracle's, and its margins at
+the four cuts agree to 2e-4.
 
 The shares reach the library as float32, so the oracle is given the same
 float32 values (floor(r * N) is taken of them in both).  The ranking key is
@@ -107,6 +109,7 @@ def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
         vc = cache.export("vcodes").cpu().numpy().reshape(B, Hkv, T, d // 2)
         kp = cache.export("kparams").cpu().numpy().view(np.uint16).reshape(B, Hkv, T, -1)
         vp = cache.export("vparams").cpu().numpy().view(np.uint16).reshape(B, Hkv, T, -1)
+        recs = cache.last_event()
         for (b, g), grp in groups.items():
             exp = grp.tier.copy()
             bad = np.flatnonzero(tiers[b, g] != exp)
@@ -133,6 +136,16 @@ def _run_hqekv(cfg, torch, n_splits=0, label="", wrap=None):
             live = np.flatnonzero((exp != 255) & (exp != oq.EVICT))
             np.testing.assert_allclose(scores[b, g, live], grp.score[live], rtol=SCORE_RTOL, atol=1e-7,
                                        err_msg=f"{tag}: scores of (seq {b}, head {g})")
+            # the event record: counts and victims exactly, cut margins to 2e-4
+            r, o = recs[b * Hkv + g], grp.last_record
+            for k in ("tokens", "candidates", "full", "int4", "int2", "int1", "moved", "evicted", "requantized"):
+                assert r[k] == o[k], f"{tag}: record {k} of (seq {b}, head {g}): {r[k]} vs {o[k]}"
+            assert r["victims"] == o["victims"], f"{tag}: victims of (seq {b}, head {g})"
+            for j, (mg, mo) in enumerate(zip(r["margins"], o["margins"])):
+                assert (np.isinf(mg) and np.isinf(mo)) or abs(mg - mo) <= 2 * SCORE_RTOL, \
+                    f"{tag}: margin at cut {j} of (seq {b}, head {g}): {mg} vs {mo}"
+            assert (np.isinf(r["margin_min"]) and np.isinf(min(o["margins"]))) or \
+                abs(r["margin_min"] - min(o["margins"])) <= 2 * SCORE_RTOL
             for t, rec in grp.codes.items():
                 lvl = rec[0]
                 if lvl in (oq.INT4, oq.INT2):

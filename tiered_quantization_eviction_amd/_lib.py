@@ -304,22 +304,30 @@ class Cache:
 
     def last_event(self, layer: int = 0) -> list[dict]:
         """The last routing event of each sequence of `layer` (QEvict), or the
-        last eviction call of each (sequence, KV head) (H2O, in b * Hkv + h
-        order): its counters, cut margins and victims (window ids or
-        positions, best-ranked first)."""
+        last eviction call / assignment event of each (sequence, KV head)
+        (H2O, HqeKV, in b * Hkv + h order): its counters, cut margins and
+        victims (window ids or positions; best-ranked first, HqeKV in
+        position order).  HqeKV records also name the INT4 and INT1 counts,
+        the re-quantized tokens and the margins at all four cuts."""
         import numpy as np
         import torch
-        n_unit = self.c.max_ctx if self.c.policy == POLICY["h2o"] else self.info("units")
+        tok = self.c.policy != POLICY["qevict"]
+        n_unit = self.c.max_ctx if tok else self.info("units")
         ev = self.export("event").cpu().numpy().view(np.int32).reshape(-1, 16)
         vic = self.export("victims").cpu().numpy().view(np.int32).reshape(-1, n_unit)
         torch.cuda.synchronize()
-        if self.c.policy != POLICY["h2o"]:
+        if not tok:
             B = self.c.batch
             ev, vic = ev[layer * B:(layer + 1) * B], vic[layer * B:(layer + 1) * B]
+        f32 = lambda w: float(w.view(np.float32)[0])
         out = []
         for r_ev, r_vic in zip(ev, vic):
             r = {k: int(r_ev[i]) for i, k in enumerate(EVENT_FIELDS)}
-            r.update({k: float(r_ev[10 + i:11 + i].view(np.float32)[0]) for i, k in enumerate(EVENT_MARGINS)})
+            r.update({k: f32(r_ev[10 + i:11 + i]) for i, k in enumerate(EVENT_MARGINS)})
+            if self.c.policy == POLICY["hqekv"]:
+                r.update({"requantized": r["first_packs"], "int4": r["reused"], "int1": r["freed"],
+                          "int2": r["quant"], "moved": r["demoted"],
+                          "margins": [r["margin_full"], r["margin_quant"], f32(r_ev[13:14]), f32(r_ev[14:15])]})
             r["victims"] = [int(u) for u in r_vic[:r["evicted"]]]
             out.append(r)
         return out

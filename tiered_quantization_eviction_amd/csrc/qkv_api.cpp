@@ -751,8 +751,8 @@ size_t qkv_export_bytes(const qkv_cache *c, int32_t what) {
       case QKV_EXPORT_VCODES: return c->tg.policy == QKV_POLICY_HQEKV ? n * (c->tg.d / 2) : 0;
       case QKV_EXPORT_KPARAMS:
       case QKV_EXPORT_VPARAMS: return c->tg.policy == QKV_POLICY_HQEKV ? n * (c->tg.d / 32) * 4 : 0;
-      case QKV_EXPORT_EVENT: return c->tg.policy == QKV_POLICY_H2O ? (size_t)c->tg.B * c->tg.Hkv * EV_WORDS * 4 : 0;
-      case QKV_EXPORT_VICTIMS: return c->tg.policy == QKV_POLICY_H2O ? n * 4 : 0;
+      case QKV_EXPORT_EVENT: return c->tg.policy != QKV_POLICY_QEVICT ? (size_t)c->tg.B * c->tg.Hkv * EV_WORDS * 4 : 0;
+      case QKV_EXPORT_VICTIMS: return c->tg.policy != QKV_POLICY_QEVICT ? n * 4 : 0;
       default: return 0;
     }
   }

@@ -223,6 +223,16 @@ enum {
   EV_MARGIN_MIN,      // float: the smaller of the two
   EV_WORDS = 16
 };
+// HqeKV's assignment event in the same record: EV_FULL, EV_QUANT = BF16 and
+// INT2 tokens of the ranked range after it, EV_EVICTED / EV_DEMOTED = tokens
+// it evicted / moved to a lower tier, margins at its four cuts
+enum {
+  EV_HQ_REQUANTIZED = EV_FIRST_PACKS,   // tokens moved to INT4, INT2 or INT1
+  EV_HQ_INT4 = EV_REUSED,
+  EV_HQ_INT1 = EV_FREED,
+  EV_HQ_MARGIN_INT1 = 13,               // float: margin at the INT2 | INT1 cut
+  EV_HQ_MARGIN_EVICT = 14,              // float: margin at the INT1 | evict cut
+};
 
 __host__ __device__ inline size_t kraw_offset(const Geom &g, int b, int u, int h) {
   return ((size_t)(b * g.U + u) * g.Hkv + h) * (size_t)(g.tpw * TS * g.d);

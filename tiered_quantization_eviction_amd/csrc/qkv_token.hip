@@ -71,7 +71,7 @@ size_t tok_carve(const TokGeom &g, char *base, TokState &st) {
   st.hqkey = nullptr;
   st.event = nullptr;
   st.victims = nullptr;
-  if (g.policy == QKV_POLICY_H2O) {
+  if (g.policy == QKV_POLICY_H2O || g.policy == QKV_POLICY_HQEKV) {
     st.event = (int32_t *)take(BH * EV_WORDS * 4);
     st.victims = (int32_t *)take(BH * g.T * 4);
   }
@@ -1518,8 +1518,8 @@ __device__ void hq_rank_chunks(const TokGeom &g, const uint32_t *keys, int elig_
 // target tier if that is lower (a token that moves to a quantized tier
 // keeps its previous level in hqold until hq_requant_kernel has rebuilt its
 // record), and the per-tier position lists are rebuilt in position order.
-__global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, int elig_end, int c0, int c1, int c2,
-                                                        int c3) {
+__global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, int N, int elig_end, int c0, int c1,
+                                                        int c2, int c3) {
   const int bh = blockIdx.x;
   const size_t tb = (size_t)bh * g.T;
   uint32_t *keys = st.hqkey + (size_t)bh * hq_key_stride(g);
@@ -1533,7 +1533,9 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
   __shared__ int s_E;
   __shared__ unsigned long long thr[4];
   __shared__ int tie_pos[4][HQ_TIE_CAP];
-  __shared__ int run[4];
+  __shared__ int run[5];                   // list lengths: BF16, INT4, INT2, INT1, evicted at this event
+  __shared__ unsigned long long below[4];
+  __shared__ int n_moved, n_evicted;
 
   // ---- keys: metric bits of every eligible token, four positions per thread ----
   if (tid == 0) s_E = 0;
@@ -1683,13 +1685,45 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
              : (c <= 0 ? ~0ull : (((unsigned long long)pref[tid] << 32) | (unsigned)(pcut[tid] + 1)));
     st.cuts[bh * 4 + tid] = thr[tid];
     run[tid] = 0;
+    below[tid] = 0ull;
+  }
+  if (tid == 0) {
+    run[4] = 0;
+    n_moved = 0;
+    n_evicted = 0;
+  }
+  __syncthreads();
+  // ---- the key just below each cut (the best-ranked one the cut drops), for
+  // the event record's margins (per-token ranking only) ----
+  if (g.chunk == 0) {
+    unsigned long long lb[4] = {0ull, 0ull, 0ull, 0ull};
+    for_keys([&](uint32_t k, int pos) {
+      if (k == HQ_KEY_NONE) return;
+      const unsigned long long key = ((unsigned long long)k << 32) | (unsigned)(pos + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (key < thr[j] && key > lb[j]) lb[j] = key;
+    });
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned long long v = lb[j];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = ((unsigned long long)(uint32_t)__shfl_xor((int)(v >> 32), off) << 32) |
+                                     (uint32_t)__shfl_xor((int)(uint32_t)v, off);
+        v = o > v ? o : v;
+      }
+      if (lane == 0 && v != 0ull) atomicMax(&below[j], v);
+    }
   }
   __syncthreads();
   // ---- targets (downgrade only) and the per-tier position lists, in position order ----
-  __shared__ int wsum[16][4];
+  __shared__ int wsum[16][5];
+  int my_moved = 0, my_evicted = 0;
   for (int base = 0; base < elig_end; base += 4 * nthr) {
     const int p0 = base + 4 * tid;
-    int lv[4], cnt[4] = {0, 0, 0, 0};
+    int lv[4], cnt[5] = {0, 0, 0, 0, 0};
+    bool gone[4] = {false, false, false, false};   // evicted at this event
     const u32x4v k4 = p0 < elig_end ? *(const u32x4v *)(keys + p0)
                                     : u32x4v{HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE, HQ_KEY_NONE};
 #pragma unroll
@@ -1713,15 +1747,22 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
           st.tier[tb + pos] = hq_code(target);
           if (target != HQ_EVICT) st.hqold[tb + pos] = (uint8_t)(old + 1);
           lv[e] = target;
+          ++my_moved;
+          if (target == HQ_EVICT) {
+            ++my_evicted;
+            gone[e] = true;
+          }
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
       if (lv[e] < 4) ++cnt[lv[e]];
-    int incl[4];
+      if (gone[e]) ++cnt[4];
+    }
+    int incl[5];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 5; ++k) {
       int v = cnt[k];
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -1732,14 +1773,15 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
       if (lane == 63) wsum[wave][k] = v;
     }
     __syncthreads();
-    int off[4];
+    int off[5];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 5; ++k) {
       off[k] = run[k] + incl[k] - cnt[k];
       for (int w2 = 0; w2 < wave; ++w2) off[k] += wsum[w2][k];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      if (gone[e]) st.victims[tb + off[4]++] = p0 + e;   // position order
       const int l = lv[e];
       if (l >= 4) continue;
       const int o = l == 0 ? off[0]++ : l == 1 ? off[1]++ : l == 2 ? off[2]++ : off[3]++;
@@ -1749,7 +1791,7 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
         st.qpos[l - 1][(size_t)bh * g.NCT * TS + o] = p0 + e;
     }
     __syncthreads();
-    if (tid < 4) {
+    if (tid < 5) {
       int t = 0;
       for (int w2 = 0; w2 < n_waves; ++w2) t += wsum[w2][tid];
       run[tid] += t;
@@ -1757,6 +1799,45 @@ __global__ __launch_bounds__(1024) void hq_event_kernel(TokGeom g, TokState st, 
     __syncthreads();
   }
   if (tid < 4) st.cnt[bh * 4 + tid] = run[tid];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    my_moved += __shfl_xor(my_moved, off);
+    my_evicted += __shfl_xor(my_evicted, off);
+  }
+  if (lane == 0) {
+    atomicAdd(&n_moved, my_moved);
+    atomicAdd(&n_evicted, my_evicted);
+  }
+  __syncthreads();
+  // the victims list ends at -1; the event record (layout in the header)
+  for (int i = run[4] + tid; i < g.T; i += nthr) st.victims[tb + i] = -1;
+  if (tid == 0) {
+    int32_t *ev = st.event + (size_t)bh * EV_WORDS;
+    float m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = __builtin_inff();
+      if (g.chunk == 0 && cum[j] > 0 && cum[j] < E) {
+        const float hi = __uint_as_float((uint32_t)(thr[j] >> 32)), lo = __uint_as_float((uint32_t)(below[j] >> 32));
+        m[j] = (hi - lo) / fmaxf(fmaxf(fabsf(hi), fabsf(lo)), 1.17549435e-38f);
+      }
+    }
+    for (int k = 0; k < EV_WORDS; ++k) ev[k] = 0;
+    ev[EV_TOKENS] = N;
+    ev[EV_CANDIDATES] = (int)E;
+    ev[EV_FULL] = run[0];
+    ev[EV_QUANT] = run[2];
+    ev[EV_EVICTED] = n_evicted;
+    ev[EV_DEMOTED] = n_moved;
+    ev[EV_HQ_REQUANTIZED] = n_moved - n_evicted;
+    ev[EV_HQ_INT4] = run[1];
+    ev[EV_HQ_INT1] = run[3];
+    ev[EV_MARGIN_FULL] = __float_as_int(m[0]);
+    ev[EV_MARGIN_QUANT] = __float_as_int(m[1]);
+    ev[EV_HQ_MARGIN_INT1] = __float_as_int(m[2]);
+    ev[EV_HQ_MARGIN_EVICT] = __float_as_int(m[3]);
+    ev[EV_MARGIN_MIN] = __float_as_int(fminf(fminf(m[0], m[1]), fminf(m[2], m[3])));
+  }
 }
 
 __device__ __forceinline__ size_t tb_of(const TokGeom &g, int bh) { return (size_t)bh * g.T; }
@@ -1956,7 +2037,7 @@ __global__ __launch_bounds__(256) void hq_gather_kernel(TokGeom g, TokState st) 
 
 hipError_t hq_launch_event(const TokGeom &g, const TokState &st, int N, int elig_end, const int *counts,
                            hipStream_t s) {
-  hipLaunchKernelGGL(hq_event_kernel, dim3(g.B * g.Hkv), dim3(1024), 0, s, g, st, elig_end, counts[0], counts[1],
+  hipLaunchKernelGGL(hq_event_kernel, dim3(g.B * g.Hkv), dim3(1024), 0, s, g, st, N, elig_end, counts[0], counts[1],
                      counts[2], counts[3]);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
