@@ -123,7 +123,9 @@ def test_stress_fullsize_sampled(torch_cuda):
 def test_hqekv_fullsize_sampled(torch_cuda, name):
     """The HqeKV layer at full size (per-token ranking with accumulated
     scores, and the page variant: 32-position chunks, scores from the last 20
-    queries, an event every 32 tokens), two KV heads followed by the oracle."""
+    queries, an event every 32 tokens), two KV heads followed by the oracle;
+    after every event their per-token records and their event records (tokens
+    per tier, moved and evicted, the evicted positions, cut margins) agree."""
     from tiered_quantization_eviction_amd import Cache, make_config
     torch = torch_cuda
     cfg = W.CONFIGS[name].replace(steps=128)
@@ -164,6 +166,7 @@ def test_hqekv_fullsize_sampled(torch_cuda, name):
         kc, vc = recs["kcodes"].reshape(B, Hkv, T, d // 2), recs["vcodes"].reshape(B, Hkv, T, d // 2)
         kp = recs["kparams"].view(np.uint16).reshape(B, Hkv, T, -1)
         vp = recs["vparams"].view(np.uint16).reshape(B, Hkv, T, -1)
+        events = cache.last_event()
         n_rec = 0
         for (b, g), grp in groups.items():
             got = np.vectorize(to_o.get)(tiers[b, g]).astype(np.uint8)
@@ -171,6 +174,14 @@ def test_hqekv_fullsize_sampled(torch_cuda, name):
             live = np.flatnonzero((grp.tier != 255) & (grp.tier != oq.EVICT))
             np.testing.assert_allclose(scores[b, g, live], grp.score[live], rtol=SCORE_RTOL, atol=1e-7,
                                        err_msg=f"{tag}: scores (seq {b}, head {g})")
+            # the event record: counts and evicted positions exactly, margins to 2e-4
+            r, o = events[b * Hkv + g], grp.last_record
+            for k in ("tokens", "candidates", "full", "int4", "int2", "int1", "moved", "evicted", "requantized"):
+                assert r[k] == o[k], f"{tag}: record {k} (seq {b}, head {g}): {r[k]} vs {o[k]}"
+            assert r["victims"] == o["victims"], f"{tag}: victims (seq {b}, head {g})"
+            for j, (mg, mo) in enumerate(zip(r["margins"], o["margins"])):
+                assert (np.isinf(mg) and np.isinf(mo)) or abs(mg - mo) <= 2 * SCORE_RTOL, \
+                    f"{tag}: margin at cut {j} (seq {b}, head {g}): {mg} vs {mo}"
             for t, rec in grp.codes.items():
                 lvl = rec[0]
                 bits = {oq.INT4: 4, oq.INT2: 2, oq.INT1: 1}[lvl]
