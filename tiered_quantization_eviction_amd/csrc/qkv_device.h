@@ -271,6 +271,24 @@ __device__ inline void softmax_block(WaveState<D> &ws, const floatx4 *s, float s
   for (int t = 0; t < NT; ++t) ts[t] = sum_x32(sum_x16(ts[t]));
 }
 
+// fp16 limbs.  opaque_neg1() is -1.0 that the compiler cannot see, so that
+// lo_limb's fma(hi, -1, x) stays one mixed-precision FMA with an fp16
+// result (v_fma_mixlo_f16) instead of being folded into a conversion of hi
+// and a subtraction; x - hi is exact in float32 when hi is x rounded to
+// fp16, so the result is that remainder rounded once.
+__device__ __forceinline__ float opaque_neg1() {
+  float v = -1.0f;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ half_t lo_limb(half_t hi, float x, float neg1) {
+  return (half_t)__builtin_fmaf((float)hi, neg1, x);
+}
+// two floats cut toward zero to fp16 (one packed conversion)
+__device__ __forceinline__ half2v rtz_pair(float a, float b) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // Minimum and maximum that return NaN when either operand is NaN, as a
 // float reduction over the values does: a quantizer's group that holds a NaN
 // then gets a NaN step, which latches the range error, instead of the NaN

@@ -568,6 +568,7 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
                                               const half8 (&qp)[2], const half8 (&bz)[D / 32], float sc_quant,
                                               const float (&row_bias)[4], const QBlock &qb, const QBuf &buf) {
   constexpr int KB = D / 32, NG = D / 32;
+  const float neg1 = opaque_neg1();
   const Geom &g = *c.g;
   const int tpw = ROPE ? 1 : g.tpw;                          // rotary keys: one tile per window
   const int nws = QT / tpw;                                  // window slots per block
@@ -732,9 +733,9 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
           const float rl = __builtin_fmaf(xl, ce, -xh * se);
           const float rh = __builtin_fmaf(xh, ce, xl * se);
           al[e] = (half_t)rl;
-          all[e] = (half_t)(rl - (float)al[e]);
+          all[e] = lo_limb(al[e], rl, neg1);
           ah[e] = (half_t)rh;
-          ahl[e] = (half_t)(rh - (float)ah[e]);
+          ahl[e] = lo_limb(ah[e], rh, neg1);
         }
         const half_t *qs = c.qs_lds + (j * 2 * G + qrow) * QSTR<D>;
         const half8 bl = *(const half8 *)(qs + ch), bh = *(const half8 *)(qs + ch + D / 2);
@@ -833,14 +834,16 @@ __device__ __forceinline__ void quant_compute(WaveState<D> &ws, const Ctx &c, co
   const uint32_t lo_keep = c.is_lo ? 0xffffffffu : 0u;
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
-    // phi: p cut to 11 significant bits (exact in fp16 for p >= 2^-14);
+    // phi: p cut toward zero to fp16 (11 significant bits for p >= 2^-14);
     // plo: the exact fp32 remainder, rounded to fp16
     half4 phi, plo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ph = __uint_as_float(__float_as_uint(p[j][i]) & 0xffffe000u);
-      phi[i] = (half_t)ph;
-      plo[i] = (half_t)(p[j][i] - ph);
+    for (int i = 0; i < 4; i += 2) {
+      const half2v h = rtz_pair(p[j][i], p[j][i + 1]);
+      phi[i] = h[0];
+      phi[i + 1] = h[1];
+      plo[i] = lo_limb(h[0], p[j][i], neg1);
+      plo[i + 1] = lo_limb(h[1], p[j][i + 1], neg1);
     }
     const uint2 ph = __builtin_bit_cast(uint2, phi), pl = __builtin_bit_cast(uint2, plo);
     P1[j] = __builtin_bit_cast(half4, make_uint2(ph.x & lo_keep, ph.y & lo_keep));

@@ -434,6 +434,7 @@ __device__ __forceinline__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, co
   if (ea >= eb) return;
   using Q = QL<D, F>;
   constexpr int KB = Q::KB, NG = Q::NG, CW = Q::CW;
+  const float neg1 = opaque_neg1();
   const TokList &L = *c.L;
   const int base = L.base_q(F);
   const int ntok = L.nQtok[F];
@@ -538,18 +539,20 @@ __device__ __forceinline__ void tok_run_ql(WaveState<D> &ws, const TokCtx &c, co
 #pragma unroll
     for (int t = 0; t < 2; ++t) tok_store_mass<GP>(c, ce[t], p[t], ws.m);
     // ---- values ----
-    // fp16 limbs of p (p cut to 11 bits, exact remainder); (P1, P2) = (0, phi)
-    // on high rows, (phi, plo) on low rows
+    // fp16 limbs of p (p cut toward zero to fp16, exact remainder); (P1, P2)
+    // = (0, phi) on high rows, (phi, plo) on low rows
     half4 P1[2], P2[2];
     const uint32_t lo_keep = c.is_lo ? 0xffffffffu : 0u;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       half4 phi, plo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ph = __uint_as_float(__float_as_uint(p[t][r]) & 0xffffe000u);
-        phi[r] = (half_t)ph;
-        plo[r] = (half_t)(p[t][r] - ph);
+      for (int r = 0; r < 4; r += 2) {
+        const half2v h = rtz_pair(p[t][r], p[t][r + 1]);
+        phi[r] = h[0];
+        phi[r + 1] = h[1];
+        plo[r] = lo_limb(h[0], p[t][r], neg1);
+        plo[r + 1] = lo_limb(h[1], p[t][r + 1], neg1);
       }
       const uint2 hb = __builtin_bit_cast(uint2, phi), lb = __builtin_bit_cast(uint2, plo);
       P1[t] = __builtin_bit_cast(half4, make_uint2(hb.x & lo_keep, hb.y & lo_keep));
