@@ -19,8 +19,8 @@ Phases (each timed on its own and reported under "phases"):
   `roofline` is taken on its attention launches.
 * events -- the routing calls inside the timed steps (rank + pack/promote).
 
-Prints one JSON line.  --gpus N with N > 1 is refused: this build measures
-one GPU.
+Prints one JSON line.  --gpus N with N > 1 is refused: the benchmark
+measures one GPU (how the path would shard is a design, not a measured path).
 
 --workload selects another layer of the same path (the default is the one
 above): `stress` (QEvict, batch 32, 128K prompt, G = 8, 32-token windows),
@@ -595,8 +595,8 @@ def main():
         copy_probe(a.copy_probe)
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
-              f"(the multi-GPU sharding is a design note, not a measured path)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
+              f"(how the path would shard across GPUs is a design, not a measured path)", file=sys.stderr)
         sys.exit(2)
     cfg = WORKLOADS[a.workload]
     token_mode = cfg.policy != W.POLICY_QEVICT

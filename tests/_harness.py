@@ -1,4 +1,4 @@
-"""Drivers shared by the GPU parity tests and the benchmark's checks.
+"""Runners shared by the GPU parity tests and the benchmark's checks.
 
 The GPU side only goes through the C ABI binding; the oracle side only through
 ``oracle``.  Both read the same seeded inputs from ``workloads``.

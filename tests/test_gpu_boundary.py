@@ -39,7 +39,7 @@ def torch_cuda():
     return torch
 
 
-class Driver:
+class CacheRun:
     """One cache driven through the C ABI the way the benchmark drives it."""
 
     def __init__(self, cfg, K, V, Q, QP=None, prompt=True):
@@ -108,8 +108,8 @@ def _snapshot_run(cfg, torch, cut, label, oracle_seq=None, pending=False):
     K, V, Q = gpu_inputs(cfg, wl)
     QP = _prompt_queries(cfg)
     log(f"[{label}] snapshot at step {cut} of {cfg.steps}: {cfg.policy} B={cfg.batch} P={cfg.prefill}")
-    A = Driver(cfg, K, V, Q, QP)          # exported mid-run, then continues
-    C = Driver(cfg, K, V, Q, QP)          # never exported
+    A = CacheRun(cfg, K, V, Q, QP)          # exported mid-run, then continues
+    C = CacheRun(cfg, K, V, Q, QP)          # never exported
     seq = qs = None
     if oracle_seq is not None:
         k, v = wl.kv(oracle_seq)
@@ -126,7 +126,7 @@ def _snapshot_run(cfg, torch, cut, label, oracle_seq=None, pending=False):
             seq.step(s, qs[s])
     snap = A.cache.snapshot()
     torch.cuda.synchronize()
-    B = Driver(cfg, K, V, Q, QP, prompt=False)
+    B = CacheRun(cfg, K, V, Q, QP, prompt=False)
     B.cache.restore(snap)
     for what in ("tokens", "steps", "routes"):
         assert B.cache.info(what) == A.cache.info(what), what
@@ -285,7 +285,7 @@ def test_range_error_in_a_routing_pack_is_latched(torch_cuda, bad):
     # bfloat16 bits: -1e5 rounded, the quiet NaN 0x7fc0, +infinity 0x7f80
     big = {"-1e5": int(round_to_bf16_bits(np.array([-1e5], np.float32))[0]), "nan": 0x7FC0, "inf": 0x7F80}[bad]
     V[0, 0, 22, 5] = big - 65536 if big > 32767 else big
-    d = Driver(cfg, K, V, Q)
+    d = CacheRun(cfg, K, V, Q)
     k1, v1 = wl.kv(1)
     seq = oe.QEvictSequence(k1, v1, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
                             k_full=cfg.k_full, k_quant=cfg.k_quant, n_q_heads=cfg.n_q_heads)
