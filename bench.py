@@ -533,25 +533,32 @@ def kernel_source_hash():
 def read_traffic(src_hash, workload, first, steps):
     """HBM bytes per attention launch from the committed counter summary,
     only if it was taken on the current kernel source, on this workload and
-    on the same launches the events time (the routed steps from `first`)."""
+    on the same launches the events time (the routed steps from `first`,
+    every PROFILE_STRIDE-th of `steps`).  The summary holds one record per
+    launch mix; each record starts at its kernel_source_sha256 field."""
     if workload != "drift":
         return None
     try:
         txt = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    f = {}
+    records = []
     for ln in txt.splitlines():
         if ":" in ln and not ln.startswith(("|", "#", " ")):
-            k, v = ln.split(":", 1)
-            f[k.strip()] = v.strip()
-    try:
-        ok = (f.get("kernel_source_sha256") == src_hash and f.get("launch_mix") == "routed" and
-              int(f.get("first_step", -1)) == first and int(f.get("stride", -1)) == PROFILE_STRIDE and
-              int(f.get("steps", -1)) >= steps)
-        return float(f["traffic_bytes_per_launch"]) if ok else None
-    except (KeyError, ValueError):
-        return None
+            k, v = (x.strip() for x in ln.split(":", 1))
+            if k == "kernel_source_sha256":
+                records.append({})
+            if records:
+                records[-1][k] = v
+    for f in records:
+        try:
+            if (f.get("kernel_source_sha256") == src_hash and f.get("launch_mix") == "routed" and
+                    int(f.get("first_step", -1)) == first and int(f.get("stride", -1)) == PROFILE_STRIDE and
+                    int(f.get("steps", -1)) == steps):
+                return float(f["traffic_bytes_per_launch"])
+        except (KeyError, ValueError):
+            continue
+    return None
 
 
 def copy_probe(mib):
