@@ -34,7 +34,7 @@ def rotate(x: np.ndarray, table: np.ndarray, positions: np.ndarray) -> np.ndarra
     x = np.asarray(x, np.float64)
     d = x.shape[-1]
     h = d // 2
-    tb = np.asarray(table, np.float32).astype(np.float64)[np.asarray(positions)]   # [t, h, 2]
+    tb = np.asarray(table, np.float32)[np.asarray(positions)].astype(np.float64)   # [t, h, 2]
     c, s = tb[..., 0], tb[..., 1]
     lo, hi = x[..., :h], x[..., h:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
