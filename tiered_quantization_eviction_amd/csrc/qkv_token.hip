@@ -1119,7 +1119,9 @@ hipError_t tok_launch_attend(const TokGeom &g, const TokState &st, const TokStep
   const int want = (2048 + BH - 1) / BH;
   if (n_parts > want) n_parts = want;
   if (n_parts < 1) n_parts = 1;
-  const dim3 mgrid(BH + BH * n_parts);
+  // a step outside the rolling score window adds nothing to the scores:
+  // without a mass output its mass blocks are left out
+  const dim3 mgrid(mass_out || !ts.skip ? BH + BH * n_parts : BH);
   if (g.G == 4)
     hipLaunchKernelGGL(tok_merge_kernel<4>, mgrid, dim3(256), 0, s, g, st, ts, out, mass_out, n_parts);
   else
