@@ -129,7 +129,10 @@ class QEvictSequence:
         that has aged out of the recent region, which is the pool Eq.(4) gives
         when the aged prompt windows are counted as the previous Full set."""
         self.P = self.N = P
-        self.tier[0] = SINK
+        # a unit takes a tier once it holds a position: with no sink tokens
+        # the sink unit stays empty
+        if self.n_sink > 0:
+            self.tier[0] = SINK
         for u in range(1, self.unit_of_pos[P - 1] + 1):
             self.tier[u] = RECENT
 

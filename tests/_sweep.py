@@ -1,0 +1,35 @@
+"""Seeded random window-policy configurations (drift recipe) for the sweep
+parity test: every knob the library accepts for the window policy drawn per
+case, at sizes the oracle follows step by step."""
+import numpy as np
+
+import workloads as W
+
+N_CASES = 10
+
+
+def draw(case: int) -> tuple:
+    """(workload config, attention splits) of sweep case `case`."""
+    r = np.random.default_rng(7100 + case)
+    G = int(r.choice([4, 8]))
+    hkv = int(r.choice([1, 2, 4]))
+    d = int(r.choice([64, 128]))
+    window = int(r.choice([8, 16, 32]))
+    bits = int(r.choice([2, 4]))
+    # rotary keys: windows of at most one tile, and not at d = 128 with G = 8
+    rope = bool(window <= 16 and not (d == 128 and G == 8) and r.random() < 0.4)
+    prefill = int(r.integers(150, 1600))
+    steps = int(r.integers(40, 97))
+    omega = int(r.choice([4, 8, 12, 16, 20, 32]))
+    n_sink = int(r.integers(0, 17))
+    n_recent = int(r.integers(0, 97))
+    batch = int(r.integers(1, 4))
+    splits = int(r.choice([0, 1, 2, 5]))
+    base = W.DRIFT.replace(name=f"sweep{case}", batch=batch, n_q_heads=G * hkv, n_kv_heads=hkv, head_dim=d,
+                           prefill=prefill, steps=steps, window=window, omega=omega, n_sink=n_sink,
+                           n_recent=n_recent, quant_bits=bits, rope_base=10000.0 if rope else 0.0,
+                           seed=case, switch_step=steps // 2)
+    w0 = W.w0(base)
+    cfg = base.replace(k_full=int(r.uniform(0.0, 0.4) * w0), k_quant=int(r.uniform(0.0, 0.5) * w0),
+                       cluster_a=(w0 // 2, max(1, w0 // 6)), cluster_b=(1, max(1, w0 // 8)))
+    return cfg, splits

@@ -234,3 +234,17 @@ def test_h2o_context_limit():
     for max_ctx, ok in ((8192, True), (16384, True), (16385, False)):
         c = L.make_config(W.H2O, max_ctx=max_ctx)
         assert (lib.qkv_check_config(ctypes.byref(c)) == 0) == ok, max_ctx
+
+
+def test_sweep_configs_are_accepted_on_host():
+    """Every configuration of the random parity sweep is one the library
+    accepts (checked on the host, no GPU)."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _sweep import N_CASES, draw
+    L, lib = _lib()
+    for case in range(N_CASES):
+        cfg, splits = draw(case)
+        c = L.make_config(cfg, n_splits=splits)
+        assert lib.qkv_check_config(ctypes.byref(c)) == 0, (case, cfg)
+        assert L.workspace_bytes(c) > 0

@@ -1,0 +1,31 @@
+"""Seeded random window-policy configurations on the GPU against the oracle.
+
+QEvict notes, section 4 (Eq. (1)-(6), Algorithm 1): each case draws the
+batch, query heads per KV head, head size, window length, routing period
+(also one that is not a multiple of the window), sinks, recent tokens,
+capacities, code width, rotary keys and attention splits, then runs prefill
+and a few routing events with the per-step checks of the parity runner:
+outputs within 2e-3, masses and scores within 1e-4 relative, tiers, event
+records, ledgers and full-precision contents exactly.
+"""
+import pytest
+
+from _sweep import N_CASES, draw
+from test_gpu_qevict import _run_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiered_quantization_eviction_amd  # noqa: F401  (raises if the library is missing)
+    return torch
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_config_parity(torch_cuda, case):
+    cfg, splits = draw(case)
+    _run_parity(cfg, torch_cuda, n_splits=splits, check_ledger_every=1, label=f"sweep{case}")

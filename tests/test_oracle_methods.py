@@ -48,12 +48,18 @@ def test_qevict_full_capacity_is_exact_attention():
     assert not seq.ledger and not np.any(seq.tier == oe.EVICTED)
 
 
-def test_qevict_zero_capacity_is_sinks_plus_recent():
-    cfg = W.TINY.replace(k_full=0, k_quant=0)
+@pytest.mark.parametrize("n_sink", [W.TINY.n_sink, 0])
+def test_qevict_zero_capacity_is_sinks_plus_recent(n_sink):
+    """With no ranked capacity attention reads the sinks and the recent
+    windows only; with no sink tokens the sink unit holds no position and
+    keeps no tier."""
+    cfg = W.TINY.replace(k_full=0, k_quant=0, n_sink=n_sink)
     wl = W.Workload(cfg)
     kb, vb = wl.kv(0)
     qb = wl.queries(0)
-    _, outs, _ = run(cfg, kb, vb, qb)
+    seq, outs, _ = run(cfg, kb, vb, qb)
+    if n_sink == 0:
+        assert seq.tier[0] == oe.EMPTY and not np.any(seq.unit_of_pos == 0)
     K, V = bf16_to_f64(kb), bf16_to_f64(vb)
     P, w, ns, nr, om = cfg.prefill, cfg.window, cfg.n_sink, cfg.n_recent, cfg.omega
     for s in range(cfg.steps):
