@@ -5,7 +5,7 @@ import numpy as np
 
 import workloads as W
 
-N_CASES = 10
+N_CASES = 24
 
 
 def draw(case: int) -> tuple:
@@ -33,3 +33,41 @@ def draw(case: int) -> tuple:
     cfg = base.replace(k_full=int(r.uniform(0.0, 0.4) * w0), k_quant=int(r.uniform(0.0, 0.5) * w0),
                        cluster_a=(w0 // 2, max(1, w0 // 6)), cluster_b=(1, max(1, w0 // 8)))
     return cfg, splits
+
+
+N_TOKEN_CASES = 12
+
+
+def draw_hqekv(case: int) -> tuple:
+    """(HqeKV config, splits): heads, head size, prompt, routing period,
+    tier shares (multiples of 1/20, some of them zero), prompt queries,
+    rolling score window and chunk ranking drawn per case."""
+    r = np.random.default_rng(7300 + case)
+    G = int(r.choice([4, 8]))
+    hkv = int(r.choice([1, 2, 4]))
+    d = int(r.choice([64, 128]))
+    prefill = int(r.integers(200, 2500))
+    steps = int(r.integers(40, 131))
+    omega = int(r.choice([16, 24, 32, 64]))
+    parts = r.multinomial(20, r.dirichlet(np.full(5, 0.7)))
+    ratios = tuple(float(k) / 20.0 for k in parts)
+    score_window = int(r.choice([0, 0, int(r.integers(1, omega + 1))]))
+    chunk = int(r.choice([0, 0, 8, 16, 32, 64]))
+    cfg = W.HQEKV.replace(name=f"hq_sweep{case}", batch=int(r.integers(1, 3)), n_q_heads=G * hkv, n_kv_heads=hkv,
+                          head_dim=d, prefill=prefill, steps=steps, omega=omega, ratios=ratios,
+                          init_queries=int(r.integers(1, 33)), score_window=score_window, chunk=chunk, seed=case)
+    return cfg, int(r.choice([0, 1, 3]))
+
+
+def draw_h2o(case: int) -> tuple:
+    """(H2O config, splits): heads, head size, prompt, sinks (also none),
+    heavy-hitter and recent budgets drawn per case."""
+    r = np.random.default_rng(7500 + case)
+    G = int(r.choice([4, 8]))
+    hkv = int(r.choice([1, 2]))
+    d = int(r.choice([64, 128]))
+    cfg = W.H2O.replace(name=f"h2o_sweep{case}", batch=int(r.integers(1, 3)), n_q_heads=G * hkv, n_kv_heads=hkv,
+                        head_dim=d, prefill=int(r.integers(60, 600)), steps=int(r.integers(30, 81)),
+                        n_sink=int(r.integers(0, 17)), k_full=int(r.integers(0, 65)),
+                        n_recent=int(r.integers(0, 65)), seed=case)
+    return cfg, int(r.choice([0, 1, 3]))

@@ -1,4 +1,4 @@
-"""Seeded random window-policy configurations on the GPU against the oracle.
+"""Seeded random configurations on the GPU against the oracle.
 
 QEvict notes, section 4 (Eq. (1)-(6), Algorithm 1): each case draws the
 batch, query heads per KV head, head size, window length, routing period
@@ -6,11 +6,17 @@ batch, query heads per KV head, head size, window length, routing period
 capacities, code width, rotary keys and attention splits, then runs prefill
 and a few routing events with the per-step checks of the parity runner:
 outputs within 2e-3, masses and scores within 1e-4 relative, tiers, event
-records, ledgers and full-precision contents exactly.
+records, ledgers and full-precision contents exactly.  The token policies
+get the same treatment with their own knobs (HqeKV notes sections 3.2-3.10:
+tier shares, routing period, prompt queries, rolling score window, chunk
+ranking; H2O notes section 2: sinks, heavy-hitter and recent budgets) and
+the checks of their parity runners.
 """
 import pytest
 
-from _sweep import N_CASES, draw
+from _sweep import N_CASES, N_TOKEN_CASES, draw, draw_h2o, draw_hqekv
+from test_gpu_h2o import _run_h2o
+from test_gpu_hqekv import _run_hqekv
 from test_gpu_qevict import _run_parity
 
 pytestmark = pytest.mark.gpu
@@ -29,3 +35,15 @@ def torch_cuda():
 def test_random_config_parity(torch_cuda, case):
     cfg, splits = draw(case)
     _run_parity(cfg, torch_cuda, n_splits=splits, check_ledger_every=1, label=f"sweep{case}")
+
+
+@pytest.mark.parametrize("case", range(N_TOKEN_CASES))
+def test_random_hqekv_config_parity(torch_cuda, case):
+    cfg, splits = draw_hqekv(case)
+    _run_hqekv(cfg, torch_cuda, n_splits=splits, label=f"hq_sweep{case}")
+
+
+@pytest.mark.parametrize("case", range(N_TOKEN_CASES))
+def test_random_h2o_config_parity(torch_cuda, case):
+    cfg, splits = draw_h2o(case)
+    _run_h2o(cfg, torch_cuda, n_splits=splits, label=f"h2o_sweep{case}")
