@@ -10,6 +10,13 @@ N_CASES = 24
 
 def draw(case: int) -> tuple:
     """(workload config, attention splits) of sweep case `case`."""
+    return draw_run(case)[:2]
+
+
+def draw_run(case: int) -> tuple:
+    """(workload config, attention splits, runner options) of sweep case
+    `case`: the one-call decode step instead of append + attend, and how
+    often the per-window masses are asked for."""
     r = np.random.default_rng(7100 + case)
     G = int(r.choice([4, 8]))
     hkv = int(r.choice([1, 2, 4]))
@@ -32,7 +39,8 @@ def draw(case: int) -> tuple:
     w0 = W.w0(base)
     cfg = base.replace(k_full=int(r.uniform(0.0, 0.4) * w0), k_quant=int(r.uniform(0.0, 0.5) * w0),
                        cluster_a=(w0 // 2, max(1, w0 // 6)), cluster_b=(1, max(1, w0 // 8)))
-    return cfg, splits
+    opts = dict(fused=bool(r.random() < 0.4), mass_every=int(r.choice([1, 1, 3])))
+    return cfg, splits, opts
 
 
 N_TOKEN_CASES = 12

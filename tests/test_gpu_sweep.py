@@ -14,7 +14,7 @@ the checks of their parity runners.
 """
 import pytest
 
-from _sweep import N_CASES, N_TOKEN_CASES, draw, draw_h2o, draw_hqekv
+from _sweep import N_CASES, N_TOKEN_CASES, draw_h2o, draw_hqekv, draw_run
 from test_gpu_h2o import _run_h2o
 from test_gpu_hqekv import _run_hqekv
 from test_gpu_qevict import _run_parity
@@ -33,8 +33,8 @@ def torch_cuda():
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_config_parity(torch_cuda, case):
-    cfg, splits = draw(case)
-    _run_parity(cfg, torch_cuda, n_splits=splits, check_ledger_every=1, label=f"sweep{case}")
+    cfg, splits, opts = draw_run(case)
+    _run_parity(cfg, torch_cuda, n_splits=splits, check_ledger_every=1, label=f"sweep{case}", **opts)
 
 
 @pytest.mark.parametrize("case", range(N_TOKEN_CASES))
