@@ -78,3 +78,49 @@ def test_random_token_config_snapshot_restore(torch_cuda, case):
     cut = 1 + (cfg.steps - 2) * (case + 1) // (SNAP_CASES + 1)
     pending = cfg.policy == W.POLICY_HQEKV and cut % cfg.omega != 0
     _snapshot_run(cfg, torch_cuda, cut, f"{cfg.name}-snapshot", pending=pending)
+
+
+LAYER_CASES = 4
+
+
+@pytest.mark.parametrize("case", range(LAYER_CASES))
+def test_random_layered_config_parity(torch_cuda, case):
+    """Random window-policy cases as caches of 2 to 5 layers over one ledger
+    pool (QEvict notes section 4.2: each layer ranked by its own scores):
+    every layer and sequence against the oracle, outputs each step, tiers
+    and scores after each routing event."""
+    import numpy as np
+    from oracle import qevict as oe
+    from test_gpu_layers import Layered, _layer_inputs
+    torch = torch_cuda
+    plain = [i for i in range(N_CASES) if draw_run(i)[0].rope_base == 0.0]
+    cfg = draw_run(plain[-1 - case])[0]
+    L = 2 + case
+    run = Layered(cfg, L, _layer_inputs(cfg, L))
+    U = run.cache.info("units")
+    seqs, qs = {}, {}
+    for l in range(L):
+        wl = W.Workload(cfg.replace(seed=l))
+        for b in range(cfg.batch):
+            k, v = wl.kv(b)
+            seqs[l, b] = oe.QEvictSequence(k, v, window=cfg.window, omega=cfg.omega, n_sink=cfg.n_sink,
+                                           n_recent=cfg.n_recent, k_full=cfg.k_full, k_quant=cfg.k_quant,
+                                           bits=cfg.quant_bits, group=cfg.group, n_q_heads=cfg.n_q_heads)
+            seqs[l, b].prefill(cfg.prefill)
+            qs[l, b] = wl.queries(b)
+    for s in range(cfg.steps):
+        routed = run.step(s)
+        torch.cuda.synchronize()
+        out = run.out.cpu().numpy()
+        for (l, b), sq in seqs.items():
+            o, _ = sq.step(s, qs[l, b][s])
+            err = float(np.abs(out[l, b] - o).max())
+            assert err <= 2e-3, f"step {s} layer {l} seq {b}: out err {err}"
+        if routed:
+            tiers = run.cache.export("tiers").cpu().numpy().reshape(L, cfg.batch, U)
+            scores = run.cache.export("scores").cpu().numpy().view(np.float32).reshape(L, cfg.batch, U)
+            for (l, b), sq in seqs.items():
+                np.testing.assert_array_equal(tiers[l, b], sq.tier, err_msg=f"tiers after step {s}, layer {l} seq {b}")
+                np.testing.assert_allclose(scores[l, b], sq.score, rtol=1e-4, atol=1e-7,
+                                           err_msg=f"scores after step {s}, layer {l} seq {b}")
+    assert run.cache.status() == 0
