@@ -5,7 +5,7 @@ import numpy as np
 
 import workloads as W
 
-N_CASES = 24
+N_CASES = 48
 
 
 def draw(case: int) -> tuple:
@@ -43,7 +43,7 @@ def draw_run(case: int) -> tuple:
     return cfg, splits, opts
 
 
-N_TOKEN_CASES = 12
+N_TOKEN_CASES = 20
 
 
 def draw_hqekv(case: int) -> tuple:
