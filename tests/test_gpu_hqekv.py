@@ -223,6 +223,14 @@ def test_hqekv_chunk_ranking_parity(torch_cuda, chunk, window):
     _run_hqekv(cfg, torch_cuda, label=f"hqekv-chunk{chunk}-w{window}")
 
 
+def test_hqekv_chunk_count_limit_parity(torch_cuda):
+    """The most ranked chunks a cache holds (4096: 8-position chunks over a
+    32768-token capacity, sorted in LDS at each event), two events."""
+    cfg = W.HQEKV.replace(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, prefill=32768 - 72, steps=72, omega=32,
+                          chunk=8)
+    _run_hqekv(cfg, torch_cuda, label="hqekv-chunk-limit")
+
+
 @pytest.mark.parametrize("prefill", [1024, 4096])
 def test_hqekv_equal_metrics_parity(torch_cuda, prefill):
     """Thousands of tokens with metric 0 at three of the four cuts: about 700
