@@ -79,3 +79,19 @@ def draw_h2o(case: int) -> tuple:
                         n_sink=int(r.integers(0, 17)), k_full=int(r.integers(0, 65)),
                         n_recent=int(r.integers(0, 65)), seed=case)
     return cfg, int(r.choice([0, 1, 3]))
+
+
+def head_limit_cases() -> dict:
+    """The most query heads a cache takes (128), with eight and with four
+    query heads per KV head."""
+    drift = W.DRIFT.replace(name="heads128", batch=1, prefill=1500, steps=48, cluster_a=(40, 12), cluster_b=(2, 8),
+                            switch_step=24)
+    return {
+        "qevict-g8": drift.replace(n_q_heads=128, n_kv_heads=16, head_dim=128, window=32, omega=32, k_full=6,
+                                   k_quant=18),
+        "qevict-g4": drift.replace(n_q_heads=128, n_kv_heads=32, head_dim=64, window=16, omega=16, k_full=12,
+                                   k_quant=36),
+        "hqekv-g4": W.HQEKV.replace(batch=1, n_q_heads=128, n_kv_heads=32, head_dim=64, prefill=800, steps=70,
+                                    omega=32),
+        "h2o-g8": W.H2O.replace(batch=1, n_q_heads=128, n_kv_heads=16, head_dim=128, prefill=200, steps=40),
+    }

@@ -241,10 +241,10 @@ def test_sweep_configs_are_accepted_on_host():
     accepts (checked on the host, no GPU)."""
     import sys
     sys.path.insert(0, os.path.dirname(__file__))
-    from _sweep import N_CASES, N_TOKEN_CASES, draw, draw_h2o, draw_hqekv
+    from _sweep import N_CASES, N_TOKEN_CASES, draw, draw_h2o, draw_hqekv, head_limit_cases
     L, lib = _lib()
     cases = ([draw(i) for i in range(N_CASES)] + [draw_hqekv(i) for i in range(N_TOKEN_CASES)] +
-             [draw_h2o(i) for i in range(N_TOKEN_CASES)])
+             [draw_h2o(i) for i in range(N_TOKEN_CASES)] + [(c, 0) for c in head_limit_cases().values()])
     for cfg, splits in cases:
         c = L.make_config(cfg, n_splits=splits)
         assert lib.qkv_check_config(ctypes.byref(c)) == 0, cfg

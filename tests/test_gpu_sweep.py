@@ -10,13 +10,14 @@ records, ledgers and full-precision contents exactly.  The token policies
 get the same treatment with their own knobs (HqeKV notes sections 3.2-3.10:
 tier shares, routing period, prompt queries, rolling score window, chunk
 ranking; H2O notes section 2: sinks, heavy-hitter and recent budgets) and
-the checks of their parity runners.
+the checks of their parity runners.  Each policy also runs at the most
+query heads a cache takes (128).
 """
 import pytest
 
 import workloads as W
 
-from _sweep import N_CASES, N_TOKEN_CASES, draw_h2o, draw_hqekv, draw_run
+from _sweep import N_CASES, N_TOKEN_CASES, draw_h2o, draw_hqekv, draw_run, head_limit_cases
 from test_gpu_h2o import _run_h2o
 from test_gpu_hqekv import _run_hqekv
 from test_gpu_qevict import _run_parity
@@ -124,3 +125,14 @@ def test_random_layered_config_parity(torch_cuda, case):
                 np.testing.assert_allclose(scores[l, b], sq.score, rtol=1e-4, atol=1e-7,
                                            err_msg=f"scores after step {s}, layer {l} seq {b}")
     assert run.cache.status() == 0
+
+
+@pytest.mark.parametrize("name", sorted(head_limit_cases()))
+def test_head_count_limit_parity(torch_cuda, name):
+    cfg = head_limit_cases()[name]
+    if cfg.policy == W.POLICY_QEVICT:
+        _run_parity(cfg, torch_cuda, label=name)
+    elif cfg.policy == W.POLICY_HQEKV:
+        _run_hqekv(cfg, torch_cuda, label=name)
+    else:
+        _run_h2o(cfg, torch_cuda, label=name)
