@@ -110,9 +110,16 @@ def _check(rc: int, what: str) -> None:
 
 
 def _stream(stream=None) -> int:
+    """The raw HIP stream of `stream`, or of the current device's current
+    stream (read without building a Stream object: that costs a few
+    microseconds per call, which a decode step of a small batch notices)."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is None:
+        return torch.cuda.current_stream().cuda_stream
+    return raw(torch.cuda.current_device())
 
 
 def _ptr(t) -> int:

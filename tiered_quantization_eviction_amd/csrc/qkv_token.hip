@@ -1166,12 +1166,36 @@ __device__ __forceinline__ void tok_copy_token(const TokGeom &g, const uint16_t 
   for (int j = 0; j < 8; ++j) dv[v_tile_index(td, c0 + j)] = sv[v_tile_index(ts_, c0 + j)];
 }
 
+// exclusive prefix of v over the threads of a workgroup of whole waves (in
+// thread order), and the workgroup's total; wsum holds one int per wave
+__device__ inline int block_excl_scan(int v, int *wsum, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int k = 0; k < nw; ++k) {
+    const int x = wsum[k];
+    if (k < w) base += x;
+    tot += x;
+  }
+  __syncthreads();   // wsum may be reused
+  total = tot;
+  return base + inc - v;
+}
+
 __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState st, int n_old, int a0, int a1,
                                                              int npow, int N) {
   extern __shared__ unsigned long long keys[];
+  __shared__ int wsum[16];
   const int bh = blockIdx.x;
   const int b = bh / g.Hkv, h = bh % g.Hkv;
-  const int n = n_old + (a1 - a0);
+  const int n_new = a1 > a0 ? a1 - a0 : 0;
+  const int n = n_old + n_new;
   const size_t tb = (size_t)bh * g.T;
   int32_t *cpos = st.cpos + (size_t)bh * g.NCT * TS;
   // key: score bits (non-negative floats order like their bits), then position + 1
@@ -1190,8 +1214,7 @@ __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int pos = (int)(keys[i] & 0xffffffffull) - 1;
     st.tier[tb + pos] = i < keep ? T_FULL : T_EVICTED;
-    if (i < keep) cpos[i] = pos;
-    else vic[i - keep] = pos;
+    if (i >= keep) vic[i - keep] = pos;
   }
   for (int i = n - keep + threadIdx.x; i < g.T; i += blockDim.x) vic[i] = -1;
   if (threadIdx.x == 0) {
@@ -1212,13 +1235,47 @@ __global__ __launch_bounds__(1024) void tok_route_h2o_kernel(TokGeom g, TokState
     ev[EV_MARGIN_QUANT] = __float_as_int(__builtin_inff());
     ev[EV_MARGIN_MIN] = __float_as_int(m);
   }
-  // gather the kept tokens (rank order) into the compact tiles
+  __syncthreads();   // tiers written; the sorted keys are not read below, their LDS is reused
+  // The compact list keeps its slots: a kept token stays where it is, the
+  // slot of an evicted one (and, while the list grows, slots n_old .. keep-1)
+  // takes a kept newcomer, the k-th free slot in slot order the k-th
+  // newcomer in position order, and only the newcomers are copied into the
+  // compact tiles.
+  int *freeslot = (int *)keys;   // keep <= npow entries
+  int n_free = 0;
+  {
+    const int per = (keep + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int j0 = (int)threadIdx.x * per, j1 = min(keep, j0 + per);
+    auto is_free = [&](int j) { return j >= n_old || st.tier[tb + cpos[j]] == T_EVICTED; };
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) cnt += is_free(j) ? 1 : 0;
+    int r = block_excl_scan(cnt, wsum, n_free);
+    for (int j = j0; j < j1; ++j)
+      if (is_free(j)) freeslot[r++] = j;
+  }
+  __syncthreads();
+  {
+    const int per = (n_new + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int e0 = (int)threadIdx.x * per, e1 = min(n_new, e0 + per);
+    auto kept_new = [&](int e) { return st.tier[tb + a0 + e] == T_FULL; };
+    int cnt = 0;
+    for (int e = e0; e < e1; ++e) cnt += kept_new(e) ? 1 : 0;
+    int total;
+    int r = block_excl_scan(cnt, wsum, total);
+    for (int e = e0; e < e1; ++e) {
+      if (!kept_new(e)) continue;
+      if (r < n_free) cpos[freeslot[r]] = a0 + e;
+      else st.status[0] = QKV_ECAPACITY;   // more newcomers than free slots: cannot happen
+      ++r;
+    }
+  }
+  __syncthreads();
   const int chunks = g.d / 8;
   const uint16_t *pages_bh = st.pages + tok_page_offset(g, b, h, 0);
   uint16_t *cpages_bh = st.cpages + tok_cpage_offset(g, b, h, 0);
-  for (int it = threadIdx.x; it < keep * chunks; it += blockDim.x) {
-    const int i = it / chunks;
-    tok_copy_token(g, pages_bh, cpages_bh, (int)(keys[i] & 0xffffffffull) - 1, i, (it % chunks) * 8);
+  for (int it = threadIdx.x; it < n_free * chunks; it += blockDim.x) {
+    const int slot = freeslot[it / chunks];
+    tok_copy_token(g, pages_bh, cpages_bh, cpos[slot], slot, (it % chunks) * 8);
   }
 }
 
