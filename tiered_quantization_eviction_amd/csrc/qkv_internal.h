@@ -261,7 +261,8 @@ __host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 //   pages   bf16 [B][Hkv][NPT][2][TS*d]  every appended token at its position
 //                (tile pos/16, slot pos%16; same swizzle as the window pages)
 //   cpages  bf16 [B][Hkv][NCT][2][TS*d]  compact full-precision tiles: kept
-//                tokens in rank order; cpos [B][Hkv][NCT*TS] their positions
+//                tokens (HqeKV: in rank order; H2O: each in the slot it keeps
+//                until evicted); cpos [B][Hkv][NCT*TS] their positions
 //   tier u8, score f32 [B][Hkv][T]       per token
 //   mrho f32 [B][Hkv][TILES+1][G][TS]    per live tile and head: p of each slot
 //   mref f32 [B][Hkv][TILES+1][G]        ... and the running max it is relative
